@@ -135,8 +135,8 @@ def ref_summarize(k, lm, S, scale=None, mode="surrogate", store="bf16"):
     Returns (ks [B,Hq,nC,d] rounded to `store`, bs [B,Hq,nC] rounded to fp32;
     with store='f64' neither is rounded).
     """
-    k = np.asarray(k, np.float64)
-    lm = np.asarray(lm, np.float64)
+    k = np.asarray(k)
+    lm = np.asarray(lm)
     B, Hkv, N, d = k.shape
     Hq, nC = lm.shape[1], lm.shape[2]
     G = Hq // Hkv
@@ -144,13 +144,13 @@ def ref_summarize(k, lm, S, scale=None, mode="surrogate", store="bf16"):
     ks = np.zeros((B, Hq, nC, d))
     bs = np.zeros((B, Hq, nC))
     if mode == "landmark_key":
-        return store_round(lm, store), bs
+        return store_round(lm.astype(np.float64), store), bs
     if mode != "surrogate":
         raise ValueError(mode)
     for b in range(B):
         for h in range(Hq):
-            kc = k[b, h // G, : nC * S].reshape(nC, S, d)
-            t = tau * np.einsum("cd,csd->cs", lm[b, h], kc)
+            kc = k[b, h // G, : nC * S].reshape(nC, S, d).astype(np.float64)
+            t = tau * np.einsum("cd,csd->cs", lm[b, h].astype(np.float64), kc)
             t = t - t.max(axis=1, keepdims=True)
             e = np.exp(t)
             z = e.sum(axis=1, keepdims=True)
@@ -178,7 +178,7 @@ def ref_exact_logz(q_rows, kg, n, S, scale):
     """Exact chunk log-masses log Z_{i,c} = log sum_{j in T_c} exp(s_ij), c < n (section 2.1)."""
     if n == 0:
         return np.zeros((q_rows.shape[0], 0))
-    s = scale * np.einsum("hd,jd->hj", q_rows, kg[: n * S])
+    s = scale * np.einsum("hd,jd->hj", q_rows, kg[: n * S].astype(np.float64))
     return _lse(s.reshape(q_rows.shape[0], n, S), axis=2)
 
 
@@ -188,7 +188,7 @@ def ref_group_scores(s_hat):
     G == 1: the raw score.  G > 1: per head, the log of the softmax over the
     candidate chunks (s_hat - LSE_c s_hat), then the maximum over the heads.
     """
-    if s_hat.shape[0] == 1:
+    if s_hat.shape[0] == 1 or s_hat.shape[1] == 0:
         return s_hat[0].copy()
     L = _lse(s_hat, axis=1)
     return np.max(s_hat - L[:, None], axis=0)
@@ -237,7 +237,7 @@ def ref_row(q, k, v, i, S, W, K, scale, s_hat_fn, forced_sel=None, want_weights=
     out = np.zeros((G, d))
     logz_swa = np.zeros(G)
     weights = np.zeros((G, i + 1)) if want_weights else None
-    kw, vw = k[w0: i + 1], v[w0: i + 1]
+    kw, vw = k[w0: i + 1].astype(np.float64), v[w0: i + 1].astype(np.float64)
     for r in range(G):
         sw = scale * (kw @ q[r])
         m = sw.max()
@@ -253,7 +253,8 @@ def ref_row(q, k, v, i, S, W, K, scale, s_hat_fn, forced_sel=None, want_weights=
         if want_weights:
             weights[r, w0: i + 1] = a[-1] * ew / zw
         for t, c in enumerate(sel):
-            kc, vc = k[c * S:(c + 1) * S], v[c * S:(c + 1) * S]
+            kc = k[c * S:(c + 1) * S].astype(np.float64)
+            vc = v[c * S:(c + 1) * S].astype(np.float64)
             sc = scale * (kc @ q[r])
             ec = np.exp(sc - sc.max())
             zc = ec.sum()
@@ -271,6 +272,12 @@ def _as64(x):
     return None if x is None else np.asarray(x, dtype=np.float64)
 
 
+def _arr(x):
+    """Keep float32/float64 input arrays as they are (bf16 and fp32 values are exact
+    in float32); every slice is upcast to float64 before any arithmetic."""
+    return None if x is None else np.asarray(x)
+
+
 def ref_prefill_rows(q, k, v, lm, rows, S, W, K, q_route=None, scale=None,
                      mode="surrogate", store="bf16", summaries=None,
                      forced_sel=None, want_weights=False):
@@ -282,7 +289,7 @@ def ref_prefill_rows(q, k, v, lm, rows, S, W, K, q_route=None, scale=None,
     forced_sel: optional dict {(b, g, i): sel} to evaluate a given selection.
     Returns dict keyed by (b, i) -> dict(out [Hq,d], sel {g: ids}, gap {g: gap}, ...).
     """
-    q, k, v, lm, q_route = map(_as64, (q, k, v, lm, q_route))
+    q, k, v, lm, q_route = map(_arr, (q, k, v, lm, q_route))
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
@@ -297,14 +304,15 @@ def ref_prefill_rows(q, k, v, lm, rows, S, W, K, q_route=None, scale=None,
         for g in range(Hkv):
             hs = slice(g * G, (g + 1) * G)
             kg, vg = k[b, g], v[b, g]
+            qrow = q[b, hs, i].astype(np.float64)
             if mode == "exact":
-                fn = (lambda n, qq=q[b, hs, i], kk=kg: ref_exact_logz(qq, kk, n, S, tau))
+                fn = (lambda n, qq=qrow, kk=kg: ref_exact_logz(qq, kk, n, S, tau))
             else:
                 ks, bs = summaries
-                fn = (lambda n, qq=qr[b, hs, i], kk=ks[b, hs], bb=bs[b, hs]:
+                fn = (lambda n, qq=qr[b, hs, i].astype(np.float64), kk=ks[b, hs], bb=bs[b, hs]:
                       ref_chunk_scores(qq, kk, bb, n, tau))
             fs = None if forced_sel is None else forced_sel.get((b, g, i))
-            r = ref_row(q[b, hs, i], kg, vg, i, S, W, K, tau, fn, forced_sel=fs,
+            r = ref_row(qrow, kg, vg, i, S, W, K, tau, fn, forced_sel=fs,
                         want_weights=want_weights)
             out[hs] = r["out"]
             sels[g], gaps[g], shats[g], lzs[g] = r["sel"], r["gap"], r["s_hat"], r["logz_swa"]
@@ -331,8 +339,8 @@ def ref_decode(q, k_cache, v_cache, seqlen, lm, S, W, K, q_route=None, scale=Non
     if q.ndim == 4:
         q = q[:, :, 0]
     qr = q if q_route is None else np.asarray(q_route, np.float64).reshape(q.shape)
-    k_cache, v_cache = _as64(k_cache), _as64(v_cache)
-    lm = _as64(lm)
+    k_cache, v_cache = _arr(k_cache), _arr(v_cache)
+    lm = _arr(lm)
     B, Hq, d = q.shape
     Hkv = k_cache.shape[1]
     G = Hq // Hkv

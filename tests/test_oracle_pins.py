@@ -268,6 +268,17 @@ def test_gqa_max_over_heads_hand_case():
     assert sorted(mean_sel.tolist()) != sel.tolist()
 
 
+def test_gqa_rows_without_candidates_are_window_attention():
+    w, x = _tiny()
+    q2 = np.concatenate([x["q"], x["q"][:, ::-1]], axis=1)       # 4 q heads, 2 KV heads
+    lm2 = np.concatenate([x["lm"], x["lm"][:, ::-1]], axis=1)
+    res = O.ref_prefill_rows(q2, x["k"], x["v"], lm2, [(0, 10), (0, 94)], w.S, w.W, w.K)
+    full = O.ref_full_causal(q2, x["k"], x["v"])
+    for i in (10, 94):
+        assert res[(0, i)]["n"] == 0 and all(len(s) == 0 for s in res[(0, i)]["sel"].values())
+        np.testing.assert_allclose(res[(0, i)]["out"], full[0, :, i], atol=1e-12)
+
+
 def test_select_ties_and_short_candidate_lists():
     sel, gap = O.ref_select(np.array([1.0, 2.0, 2.0, 0.5, 2.0]), 2)
     assert sel.tolist() == [1, 2] and gap == 0.0
