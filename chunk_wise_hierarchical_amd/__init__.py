@@ -1,0 +1,9 @@
+"""HiLS (Hierarchical Landmark Sparse) attention forward pass for AMD MI355X (gfx950).
+
+The computation lives in libhils.so (hand-written HIP kernels behind the C ABI
+of include/hils.h); this package only marshals torch tensors into that ABI.
+"""
+from .api import decode, make_cfg, prefill, summarize, workspace_bytes  # noqa: F401
+from ._lib import HilsError, LIB_PATH  # noqa: F401
+
+__all__ = ["prefill", "decode", "summarize", "workspace_bytes", "make_cfg", "HilsError", "LIB_PATH"]

@@ -1,0 +1,133 @@
+"""Torch-facing wrappers of the HiLS C ABI: prefill, decode, summarize.
+
+Torch provides device memory and the current stream; every step of the
+computation runs in the HIP kernels of libhils.so.  Tensors must be contiguous
+CUDA (HIP) tensors of dtype bfloat16 or float32 with the layouts documented in
+include/hils.h.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import HilsCfg, check
+
+_DT = {torch.bfloat16: _lib.HILS_BF16, torch.float32: _lib.HILS_F32}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_tensor(t, name, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def make_cfg(B, N, Hq, Hkv, d, S, W, K, dtype, mode="surrogate", scale=0.0, generic=False):
+    return HilsCfg(B=B, N=N, Hq=Hq, Hkv=Hkv, d=d, S=S, W=W, K=K, dtype=_DT[dtype],
+                   mode=_lib.MODES[mode], scale=float(scale),
+                   flags=_lib.HILS_FLAG_GENERIC if generic else 0)
+
+
+def workspace_bytes(cfg: HilsCfg, decode: bool) -> int:
+    return int(_lib.lib().hils_workspace_bytes(ctypes.byref(cfg), 1 if decode else 0))
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(cfg, decode, device, ws):
+    need = workspace_bytes(cfg, decode)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return ws, need
+
+
+def prefill(q, k, v, lm, S, W, K, q_route=None, mode="surrogate", scale=0.0, out=None,
+            sel=None, summaries=None, ws=None, generic=False):
+    """HiLS prefill. q [B,Hq,N,d]; k,v [B,Hkv,N,d]; lm [B,Hq,N//S,d].
+
+    sel (optional) [B,Hkv,N,K] int32 receives the selected chunk ids;
+    summaries (optional) (k_sum [B,Hq,N//S,d], b_sum [B,Hq,N//S] fp32) receive the
+    chunk summaries.  Returns out [B,Hq,N,d].
+    """
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("lm", lm), ("q_route", q_route)):
+        _check_tensor(t, name, q.dtype, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor(out, "out", q.dtype, dev)
+    _check_tensor(sel, "sel", torch.int32, dev)
+    ks = bs = None
+    if summaries is not None:
+        ks, bs = summaries
+        _check_tensor(ks, "k_sum", q.dtype, dev)
+        _check_tensor(bs, "b_sum", torch.float32, dev)
+    cfg = make_cfg(B, N, Hq, Hkv, d, S, W, K, q.dtype, mode, scale, generic)
+    ws, need = _workspace(cfg, False, dev, ws)
+    st = _lib.lib().hils_prefill(ctypes.byref(cfg), _ptr(q), _ptr(q_route), _ptr(k), _ptr(v),
+                                 _ptr(lm), _ptr(out), _ptr(sel), _ptr(ks), _ptr(bs), _ptr(ws),
+                                 ctypes.c_size_t(ws.numel()), _stream(dev))
+    check(st, "hils_prefill")
+    return out
+
+
+def summarize(k, lm, S, c0=0, c1=None, out=None, mode="surrogate", scale=0.0, Hq=None):
+    """Chunk summaries for chunks [c0, c1): returns (k_sum [B,Hq,N//S,d], b_sum [B,Hq,N//S])."""
+    B, Hkv, N, d = k.shape
+    Hq = lm.shape[1] if Hq is None else Hq
+    nC = N // S
+    c1 = nC if c1 is None else c1
+    dev = k.device
+    _check_tensor(k, "k", None, dev)
+    _check_tensor(lm, "lm", k.dtype, dev)
+    if out is None:
+        out = (torch.empty((B, Hq, nC, d), dtype=k.dtype, device=dev),
+               torch.empty((B, Hq, nC), dtype=torch.float32, device=dev))
+    ks, bs = out
+    _check_tensor(ks, "k_sum", k.dtype, dev)
+    _check_tensor(bs, "b_sum", torch.float32, dev)
+    cfg = make_cfg(B, N, Hq, Hkv, d, S, 1, 1, k.dtype, mode, scale)
+    st = _lib.lib().hils_summarize(ctypes.byref(cfg), _ptr(k), _ptr(lm), int(c0), int(c1),
+                                   _ptr(ks), _ptr(bs), _stream(dev))
+    check(st, "hils_summarize")
+    return ks, bs
+
+
+def decode(q, k_cache, v_cache, seqlen, k_sum, b_sum, S, W, K, q_route=None, mode="surrogate",
+           scale=0.0, out=None, sel=None, ws=None):
+    """HiLS single-step decode. q [B,Hq,1,d]; caches [B,Hkv,T,d]; seqlen [B] int32 (device);
+    k_sum [B,Hq,T//S,d], b_sum [B,Hq,T//S].  Returns out [B,Hq,1,d]."""
+    B, Hq, _, d = q.shape
+    Hkv, T = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_sum", k_sum),
+                    ("q_route", q_route)):
+        _check_tensor(t, name, q.dtype, dev)
+    _check_tensor(seqlen, "seqlen", torch.int32, dev)
+    _check_tensor(b_sum, "b_sum", torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor(out, "out", q.dtype, dev)
+    _check_tensor(sel, "sel", torch.int32, dev)
+    cfg = make_cfg(B, T, Hq, Hkv, d, S, W, K, q.dtype, mode, scale)
+    ws, need = _workspace(cfg, True, dev, ws)
+    st = _lib.lib().hils_decode(ctypes.byref(cfg), _ptr(q), _ptr(q_route), _ptr(k_cache),
+                                _ptr(v_cache), _ptr(seqlen), _ptr(k_sum), _ptr(b_sum), _ptr(out),
+                                _ptr(sel), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+    check(st, "hils_decode")
+    return out

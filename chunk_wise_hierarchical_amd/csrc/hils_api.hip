@@ -1,0 +1,175 @@
+// C ABI of libhils: argument validation, workspace layout and kernel dispatch.
+// See include/hils.h for the contract of every entry point.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/hils.h"
+#include "hils_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int n_cand_host(long long i, int W, int S) {
+  long long t = i - W + 1;
+  long long q = (t >= 0) ? t / S : -((-t + S - 1) / S);
+  long long l = q * S;
+  return l > 0 ? (int)(l / S) : 0;
+}
+
+// Validates a configuration and fills the shape record.
+hils_status make_shape(const hils_cfg* c, HilsShape& s) {
+  if (!c) return HILS_E_ARG;
+  if (c->B < 1 || c->N < 1 || c->Hq < 1 || c->Hkv < 1 || c->d < 1 || c->S < 1 || c->W < 1 ||
+      c->K < 1)
+    return HILS_E_ARG;
+  if (c->Hq % c->Hkv != 0) return HILS_E_ARG;
+  if (c->dtype != HILS_BF16 && c->dtype != HILS_F32) return HILS_E_ARG;
+  if (c->mode < HILS_SCORE_SURROGATE || c->mode > HILS_SCORE_EXACT) return HILS_E_ARG;
+  if (!(c->scale >= 0.0f) || isinf(c->scale)) return HILS_E_ARG;
+  if (c->d > 256 || c->S > 64 || c->K > 128 || c->Hq / c->Hkv > 8) return HILS_E_UNSUPPORTED;
+  const long long elems = (long long)c->B * c->Hq * c->N * c->d;
+  if (elems <= 0 || elems > (1LL << 40)) return HILS_E_UNSUPPORTED;
+  s.B = c->B; s.N = c->N; s.Hq = c->Hq; s.Hkv = c->Hkv; s.G = c->Hq / c->Hkv;
+  s.d = c->d; s.S = c->S; s.W = c->W; s.K = c->K;
+  s.dtype = c->dtype; s.mode = c->mode;
+  s.nC = c->N / c->S;
+  s.nCc = (c->N + c->S - 1) / c->S;
+  s.nmax = n_cand_host((long long)c->N - 1, c->W, c->S);
+  s.nwin = (c->W + c->S - 1 + c->S - 1) / c->S;   // ceil((W + S - 1) / S)
+  s.tau = (c->scale == 0.0f) ? 1.0 / sqrt((double)c->d) : (double)c->scale;
+  return HILS_OK;
+}
+
+inline size_t esize(const HilsShape& s) { return s.dtype == HILS_BF16 ? 2 : 4; }
+
+struct PrefillLayout {
+  size_t ks, bs, sel, slog, total;
+};
+PrefillLayout prefill_layout(const HilsShape& s) {
+  PrefillLayout L{};
+  size_t off = 0;
+  L.ks = off;   off += align_up((size_t)s.B * s.Hq * s.nC * s.d * esize(s));
+  L.bs = off;   off += align_up((size_t)s.B * s.Hq * s.nC * 4);
+  L.sel = off;  off += align_up((size_t)s.B * s.Hkv * s.N * s.K * 4);
+  L.slog = off; off += align_up((size_t)s.B * s.Hq * s.N * s.K * 4);
+  L.total = off;
+  return L;
+}
+
+struct DecodeLayout {
+  size_t scores, keys, slog, sel, part, total;
+};
+DecodeLayout decode_layout(const HilsShape& s) {
+  DecodeLayout L{};
+  const size_t nm = (size_t)(s.nmax > 0 ? s.nmax : 1);
+  size_t off = 0;
+  L.scores = off; off += align_up((size_t)s.B * s.Hq * nm * 4);
+  L.keys = off;   off += align_up((size_t)s.B * s.Hkv * nm * 4);
+  L.slog = off;   off += align_up((size_t)s.B * s.Hq * s.K * 4);
+  L.sel = off;    off += align_up((size_t)s.B * s.Hkv * s.K * 4);
+  L.part = off;   off += align_up((size_t)s.B * s.Hq * (s.K + s.nwin) * (s.d + 2) * 4);
+  L.total = off;
+  return L;
+}
+
+inline hils_status hip_status(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* hils_strerror(hils_status st) {
+  switch (st) {
+    case HILS_OK: return "ok";
+    case HILS_E_ARG: return "invalid argument";
+    case HILS_E_UNSUPPORTED: return "unsupported configuration";
+    case HILS_E_WORKSPACE: return "workspace too small";
+    case HILS_E_HIP: return "HIP runtime or launch error";
+  }
+  return "unknown status";
+}
+
+int hils_abi_version(void) { return HILS_ABI_VERSION; }
+
+size_t hils_workspace_bytes(const hils_cfg* cfg, int is_decode) {
+  HilsShape s;
+  if (make_shape(cfg, s) != HILS_OK) return 0;
+  return is_decode ? decode_layout(s).total : prefill_layout(s).total;
+}
+
+hils_status hils_summarize(const hils_cfg* cfg, const void* k, const void* lm_q, int32_t c0,
+                           int32_t c1, void* k_sum, float* b_sum, void* stream) {
+  HilsShape s;
+  hils_status r = make_shape(cfg, s);
+  if (r != HILS_OK) return r;
+  if (s.mode == HILS_SCORE_EXACT) return HILS_E_ARG;   // exact mode has no summaries
+  if (c0 < 0 || c1 < c0 || c1 > s.nC) return HILS_E_ARG;
+  if (c1 == c0) return HILS_OK;
+  if (!k || !lm_q || !k_sum || !b_sum) return HILS_E_ARG;
+  if (!aligned16(k) || !aligned16(lm_q) || !aligned16(k_sum) || !aligned16(b_sum)) return HILS_E_ARG;
+  if ((long long)s.B * s.Hq * (c1 - c0) >= (1LL << 31)) return HILS_E_UNSUPPORTED;
+  return hip_status(hils_launch_summarize(s, k, lm_q, c0, c1, k_sum, b_sum, (hipStream_t)stream));
+}
+
+hils_status hils_prefill(const hils_cfg* cfg, const void* q, const void* q_route, const void* k,
+                         const void* v, const void* lm_q, void* out, int32_t* sel, void* k_sum,
+                         float* b_sum, void* ws, size_t ws_bytes, void* stream) {
+  HilsShape s;
+  hils_status r = make_shape(cfg, s);
+  if (r != HILS_OK) return r;
+  if (s.mode == HILS_SCORE_EXACT) return HILS_E_UNSUPPORTED;
+  if (!q || !k || !v || !out) return HILS_E_ARG;
+  if (s.nC > 0 && !lm_q) return HILS_E_ARG;
+  if ((k_sum == nullptr) != (b_sum == nullptr)) return HILS_E_ARG;
+  const void* ptrs[] = {q, q_route, k, v, lm_q, out, sel, k_sum, b_sum, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return HILS_E_ARG;
+  if (s.nmax > HILS_GENERIC_NMAX) return HILS_E_UNSUPPORTED;
+  if ((long long)s.B * s.Hkv * s.N >= (1LL << 31)) return HILS_E_UNSUPPORTED;
+  const PrefillLayout L = prefill_layout(s);
+  if (ws_bytes < L.total || (L.total > 0 && !ws)) return HILS_E_WORKSPACE;
+  char* w = static_cast<char*>(ws);
+  void* ks = k_sum ? k_sum : (void*)(w + L.ks);
+  float* bs = b_sum ? b_sum : (float*)(w + L.bs);
+  int32_t* sl = sel ? sel : (int32_t*)(w + L.sel);
+  float* slog = (float*)(w + L.slog);
+  const void* qr = q_route ? q_route : q;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hils_launch_summarize(s, k, lm_q, 0, s.nC, ks, bs, st);
+  if (e != hipSuccess) return HILS_E_HIP;
+  e = hils_launch_select_generic(s, qr, ks, bs, sl, slog, st);
+  if (e != hipSuccess) return HILS_E_HIP;
+  e = hils_launch_attn_generic(s, q, k, v, sl, slog, out, st);
+  return hip_status(e);
+}
+
+hils_status hils_decode(const hils_cfg* cfg, const void* q, const void* q_route,
+                        const void* k_cache, const void* v_cache, const int32_t* seqlen,
+                        const void* k_sum, const float* b_sum, void* out, int32_t* sel, void* ws,
+                        size_t ws_bytes, void* stream) {
+  HilsShape s;
+  hils_status r = make_shape(cfg, s);
+  if (r != HILS_OK) return r;
+  if (s.mode == HILS_SCORE_EXACT) return HILS_E_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !seqlen || !out) return HILS_E_ARG;
+  if (s.nmax > 0 && (!k_sum || !b_sum)) return HILS_E_ARG;
+  const void* ptrs[] = {q, q_route, k_cache, v_cache, seqlen, k_sum, b_sum, out, sel, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return HILS_E_ARG;
+  if (s.d % (s.dtype == HILS_BF16 ? 8 : 4) != 0) return HILS_E_UNSUPPORTED;
+  const DecodeLayout L = decode_layout(s);
+  if (ws_bytes < L.total || (L.total > 0 && !ws)) return HILS_E_WORKSPACE;
+  char* w = static_cast<char*>(ws);
+  int32_t* sl = sel ? sel : (int32_t*)(w + L.sel);
+  const void* qr = q_route ? q_route : q;
+  return hip_status(hils_launch_decode(s, q, qr, k_cache, v_cache, seqlen, k_sum, b_sum, out, sl,
+                                       (float*)(w + L.scores), (uint32_t*)(w + L.keys),
+                                       (float*)(w + L.slog), (float*)(w + L.part),
+                                       (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// Host-side shape record and kernel launchers (internal to libhils).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+struct HilsShape {
+  int B, N, Hq, Hkv, G, d, S, W, K;
+  int dtype;   // 0 bf16, 1 fp32
+  int mode;    // 0 surrogate, 1 landmark key, 2 exact
+  int nC;      // floor(N/S): chunks with a landmark / summary
+  int nCc;     // ceil(N/S): chunks holding tokens
+  int nmax;    // |C_{N-1}|: most candidate chunks of any position
+  int nwin;    // max number of S-token tiles a window spans
+  double tau;  // logit scale
+};
+
+// summarize.hip
+hipError_t hils_launch_summarize(const HilsShape& s, const void* k, const void* lm, int c0, int c1,
+                                 void* ksum, float* bsum, hipStream_t st);
+
+// prefill_generic.hip: vector-ALU score/select and attention, any supported shape
+hipError_t hils_launch_select_generic(const HilsShape& s, const void* qr, const void* ksum,
+                                      const float* bsum, int32_t* sel, float* slog, hipStream_t st);
+hipError_t hils_launch_attn_generic(const HilsShape& s, const void* q, const void* k, const void* v,
+                                    const int32_t* sel, const float* slog, void* out, hipStream_t st);
+
+// decode.hip
+hipError_t hils_launch_decode(const HilsShape& s, const void* q, const void* qr, const void* k,
+                              const void* v, const int32_t* seqlen, const void* ksum,
+                              const float* bsum, void* out, int32_t* sel, float* scores,
+                              uint32_t* keys, float* slog, float* part, hipStream_t st);
+
+// maximum candidates the generic select kernel keeps in LDS
+constexpr int HILS_GENERIC_NMAX = 8192;

@@ -1,0 +1,83 @@
+// Landmark chunk summaries (k'_c, b'_c).
+//
+// "Hierarchical Sparse Attention Done Right", section 3 (Proposition 3.1 and
+// the landmark-token text): the landmark query q'_c attends over the S keys of
+// chunk c; k'_c is the attention-weighted key sum and b'_c the entropy of the
+// attention weights, i.e. Attn(q'_c, K_c, K_c).  One wavefront per
+// (batch, query head, chunk); lane j owns token j of the chunk.  The math is
+// done in double precision and rounded once to the storage type, so the
+// bf16/fp32 summary is the correctly rounded value of the exact summary.
+#include "hils_device.h"
+#include "hils_internal.h"
+
+namespace {
+
+template <typename T>
+__global__ void __launch_bounds__(64)
+k_summarize(const T* __restrict__ k, const T* __restrict__ lm, T* __restrict__ ksum,
+            float* __restrict__ bsum, int Hq, int Hkv, int N, int d, int S, int nC,
+            int c0, int ncs, double tau, int landmark_key) {
+  extern __shared__ double sm_sum[];
+  double* qd = sm_sum;        // [d]
+  double* pj = sm_sum + d;    // [S]
+  const int lane = threadIdx.x;
+  const long long item = blockIdx.x;
+  const int c = c0 + (int)(item % ncs);
+  const long long bh = item / ncs;
+  const int h = (int)(bh % Hq);
+  const long long b = bh / Hq;
+  const int g = h / (Hq / Hkv);
+  const T* kc = k + (((b * Hkv + g) * (long long)N) + (long long)c * S) * d;
+  const T* qc = lm + ((b * Hq + h) * (long long)nC + c) * d;
+  T* ko = ksum + ((b * Hq + h) * (long long)nC + c) * d;
+  float* bo = bsum + (b * Hq + h) * (long long)nC + c;
+
+  if (landmark_key) {            // ablation: the landmark row is the routing key
+    for (int e = lane; e < d; e += 64) ko[e] = qc[e];
+    if (lane == 0) *bo = 0.0f;
+    return;
+  }
+  for (int e = lane; e < d; e += 64) qd[e] = (double)Elt<T>::ld(qc + e);
+  __syncthreads();
+  double t = -INFINITY;
+  if (lane < S) {
+    const T* kr = kc + (long long)lane * d;
+    double acc = 0.0;
+    for (int e = 0; e < d; ++e) acc = fma(qd[e], (double)Elt<T>::ld(kr + e), acc);
+    t = tau * acc;
+  }
+  const double m = wave_max_d(t);
+  const double ex = (lane < S) ? exp(t - m) : 0.0;
+  const double z = wave_sum_d(ex);
+  const double p = ex / z;
+  const double logp = (t - m) - log(z);
+  const double ent = wave_sum_d((lane < S) ? -p * logp : 0.0);
+  if (lane < S) pj[lane] = p;
+  __syncthreads();
+  for (int e = lane; e < d; e += 64) {
+    double acc = 0.0;
+    for (int j = 0; j < S; ++j) acc = fma(pj[j], (double)Elt<T>::ld(kc + (long long)j * d + e), acc);
+    Elt<T>::st64(ko + e, acc);
+  }
+  if (lane == 0) *bo = (float)ent;
+}
+
+}  // namespace
+
+hipError_t hils_launch_summarize(const HilsShape& s, const void* k, const void* lm, int c0, int c1,
+                                 void* ksum, float* bsum, hipStream_t st) {
+  const int ncs = c1 - c0;
+  if (ncs <= 0) return hipSuccess;
+  const long long nblk = (long long)s.B * s.Hq * ncs;
+  const size_t shm = sizeof(double) * (s.d + 64);
+  const int lk = (s.mode == 1);
+  if (s.dtype == 0)
+    hipLaunchKernelGGL(k_summarize<bf16_t>, dim3((unsigned)nblk), dim3(64), shm, st,
+                       (const bf16_t*)k, (const bf16_t*)lm, (bf16_t*)ksum, bsum, s.Hq, s.Hkv, s.N,
+                       s.d, s.S, s.nC, c0, ncs, (double)s.tau, lk);
+  else
+    hipLaunchKernelGGL(k_summarize<float>, dim3((unsigned)nblk), dim3(64), shm, st,
+                       (const float*)k, (const float*)lm, (float*)ksum, bsum, s.Hq, s.Hkv, s.N,
+                       s.d, s.S, s.nC, c0, ncs, (double)s.tau, lk);
+  return hipGetLastError();
+}

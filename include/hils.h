@@ -1,0 +1,133 @@
+/*
+ * hils.h — C ABI of the HiLS (Hierarchical Landmark Sparse) attention forward
+ * pass for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is defined in "Hierarchical Sparse Attention Done Right:
+ * Toward Infinite Context Modeling" (Hu et al., arXiv 2607.02980):
+ *   - section 2.1: chunks c(j) = floor(j/S); aligned window boundary
+ *     l(i) = floor((i-W+1)/S)*S; candidate chunks C_i = {0..l(i)/S-1};
+ *     token logits s_ij = q_i.k_j/sqrt(d); window mass Z_{i,swa};
+ *   - section 3, Proposition 3.1 and the landmark text: per-chunk summary
+ *     (k'_c, b'_c) from Attn(q'_c, K_c, K_c), b'_c the entropy of the
+ *     landmark query's attention over the chunk;
+ *   - section 3, routing equation: s_hat_ic = q_i.k'_c/sqrt(d) + b'_c, the
+ *     top-K chunks of C_i, and the fused mass Z_hat_i;
+ *   - section 3, hierarchical-softmax equation: independent softmax inside
+ *     every selected chunk and inside the window, fused by a softmax over the
+ *     chunk scores (the window's logit is log Z_{i,swa});
+ *   - section 4.1: low-rank query calibration (a routing query q_hat used only
+ *     in s_hat) and GQA shared selection (per-head normalised chunk weights,
+ *     maximum over the heads of a group, one top-K per group).
+ *
+ * Conventions for every entry point
+ *   - All tensors are caller-owned DEVICE memory, contiguous, head-major:
+ *       q, q_route, out : [B][Hq][N][d]         (decode: [B][Hq][1][d])
+ *       k, v            : [B][Hkv][N][d]        (decode: the KV cache, N = capacity)
+ *       lm_q            : [B][Hq][floor(N/S)][d]  one landmark query per chunk per q head
+ *       k_sum           : [B][Hq][floor(N/S)][d]  summary keys, element type = dtype
+ *       b_sum           : [B][Hq][floor(N/S)]     entropy biases, fp32
+ *       sel             : [B][Hkv][N][K] int32   (decode: [B][Hkv][K]) selected chunk
+ *                         ids of each query, ascending, -1 padded when |C_i| < K
+ *     Element type of q/q_route/k/v/lm_q/k_sum/out is cfg->dtype (bf16 or fp32).
+ *     Query head h uses KV head h / (Hq/Hkv).  Tokens and chunks are 0-based.
+ *   - The library allocates no device memory.  Scratch comes from the caller's
+ *     workspace `ws` of at least hils_workspace_bytes() bytes (256-byte aligned).
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *     No entry point synchronises the host.  Outputs are valid once the stream
+ *     reaches the enqueued work.  The library keeps no global mutable state:
+ *     calls on different streams with different buffers are independent.
+ *   - Errors: arguments are validated before anything is enqueued; on a
+ *     non-OK return nothing has been enqueued (except HILS_E_HIP, which reports
+ *     a launch failure), and outputs are undefined.  No C++ exception crosses
+ *     this boundary.
+ */
+#ifndef HILS_H
+#define HILS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HILS_ABI_VERSION 1
+
+typedef enum {
+  HILS_OK = 0,
+  HILS_E_ARG = 1,          /* invalid argument (shape, null pointer, misalignment) */
+  HILS_E_UNSUPPORTED = 2,  /* valid but not implemented (e.g. d > 256, S > 64) */
+  HILS_E_WORKSPACE = 3,    /* workspace too small */
+  HILS_E_HIP = 4           /* HIP runtime / launch error */
+} hils_status;
+
+typedef enum { HILS_BF16 = 0, HILS_F32 = 1 } hils_dtype;
+
+typedef enum {
+  HILS_SCORE_SURROGATE = 0,     /* Proposition 3.1 summary (k'_c, b'_c) — the method */
+  HILS_SCORE_LANDMARK_KEY = 1,  /* ablation "w/o Prop. 3.1" (Table 5): lm row is k'_c, b'_c = 0 */
+  HILS_SCORE_EXACT = 2          /* naive-BSA exact chunk log-mass (section 2.1); not yet implemented */
+} hils_score_mode;
+
+/* flags */
+#define HILS_FLAG_GENERIC 1u   /* prefill: force the generic (vector-ALU) kernels */
+
+typedef struct hils_cfg {
+  int32_t B;      /* batch */
+  int32_t N;      /* prefill: sequence length; decode: KV-cache capacity */
+  int32_t Hq;     /* query heads */
+  int32_t Hkv;    /* key/value heads; Hq % Hkv == 0 */
+  int32_t d;      /* head dim, 1..256 */
+  int32_t S;      /* chunk size, 1..64 */
+  int32_t W;      /* window size >= 1 */
+  int32_t K;      /* top-K chunks, 1..128 */
+  int32_t dtype;  /* hils_dtype */
+  int32_t mode;   /* hils_score_mode */
+  float scale;    /* logit scale; 0 selects 1/sqrt(d) */
+  uint32_t flags; /* HILS_FLAG_* */
+} hils_cfg;
+
+/* Bytes of workspace hils_prefill (is_decode = 0) or hils_decode (is_decode = 1)
+ * needs for this configuration; 0 when the configuration is invalid. */
+size_t hils_workspace_bytes(const hils_cfg* cfg, int is_decode);
+
+/* Chunk summaries for chunks c0 <= c < c1 (section 3, Proposition 3.1):
+ *   p_j = softmax_{j in chunk c}(scale * lm_q[b,h,c] . k[b,h/G,j]),
+ *   k_sum[b,h,c] = sum_j p_j k_j (rounded once, to nearest-even, to dtype),
+ *   b_sum[b,h,c] = -sum_j p_j log p_j (rounded once to fp32).
+ * Computed in double precision.  Mode LANDMARK_KEY copies lm_q into k_sum and
+ * writes b_sum = 0.  Requires 0 <= c0 <= c1 <= floor(N/S).  Used to build or
+ * extend a decode summary cache as chunks complete. */
+hils_status hils_summarize(const hils_cfg* cfg, const void* k, const void* lm_q,
+                           int32_t c0, int32_t c1, void* k_sum, float* b_sum, void* stream);
+
+/* Prefill: HiLS output for every position of every sequence.
+ *   q_route  : routing query (low-rank query calibration, section 4.1) used only
+ *              in the chunk scores; NULL means q.
+ *   out      : [B][Hq][N][d], dtype.
+ *   sel      : optional output of the selected chunk ids (NULL: kept in workspace).
+ *   k_sum, b_sum : optional outputs of the summaries of all floor(N/S) chunks
+ *              (both NULL or both non-NULL).
+ * Requires 1 <= K, 1 <= W, N >= 1. */
+hils_status hils_prefill(const hils_cfg* cfg, const void* q, const void* q_route,
+                         const void* k, const void* v, const void* lm_q, void* out,
+                         int32_t* sel, void* k_sum, float* b_sum,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Single-step decode: for each sequence b the new token is already in the
+ * cache at position T_b - 1 (T_b = seqlen[b], 1 <= T_b <= N, device int32[B]),
+ * and the query q[b,:,0,:] is that token's query.  k_sum/b_sum hold the
+ * summaries of every complete chunk (from hils_summarize); only chunks
+ * c < |C_{T_b-1}| are read.  out: [B][Hq][1][d]; sel optional [B][Hkv][K]. */
+hils_status hils_decode(const hils_cfg* cfg, const void* q, const void* q_route,
+                        const void* k_cache, const void* v_cache, const int32_t* seqlen,
+                        const void* k_sum, const float* b_sum, void* out, int32_t* sel,
+                        void* ws, size_t ws_bytes, void* stream);
+
+const char* hils_strerror(hils_status status);
+int hils_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HILS_H */

@@ -1,0 +1,96 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every symbol
+include/hils.h declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunk_wise_hierarchical_amd import _lib
+from chunk_wise_hierarchical_amd._lib import HilsCfg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hils.h")
+PKG = os.path.join(ROOT, "chunk_wise_hierarchical_amd")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(hils_[a-z_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libhils.so is not built (run python -m chunk_wise_hierarchical_amd.build)")
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) >= set(_lib.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in hils.h but not exported"
+
+
+def test_version_and_strerror(L):
+    assert L.hils_abi_version() == 1
+    assert L.hils_strerror(0) == b"ok"
+    assert b"workspace" in L.hils_strerror(3)
+
+
+def _cfg(**kw):
+    base = dict(B=1, N=1024, Hq=8, Hkv=2, d=128, S=64, W=256, K=8, dtype=0, mode=0, scale=0.0,
+                flags=0)
+    base.update(kw)
+    return HilsCfg(**base)
+
+
+def test_workspace_bytes(L):
+    c = _cfg()
+    n = L.hils_workspace_bytes(ctypes.byref(c), 0)
+    # summaries + selection ids + fusion logits, each rounded up to 256 bytes
+    want = (1 * 8 * 16 * 128 * 2) + (1 * 8 * 16 * 4) + (1 * 2 * 1024 * 8 * 4) + (1 * 8 * 1024 * 8 * 4)
+    assert want <= n <= want + 4 * 256
+    assert L.hils_workspace_bytes(ctypes.byref(c), 1) > 0
+    for bad in (dict(Hq=7), dict(d=0), dict(K=0), dict(dtype=5), dict(mode=9), dict(N=0)):
+        assert L.hils_workspace_bytes(ctypes.byref(_cfg(**bad)), 0) == 0, bad
+
+
+def _prefill(L, c, ws_bytes=1 << 30, null_q=False, misalign=False):
+    p = ctypes.c_void_p(0x10000)
+    q = None if null_q else ctypes.c_void_p(0x10000 + (8 if misalign else 0))
+    return L.hils_prefill(ctypes.byref(c), q, None, p, p, p, p, None, None, None, p,
+                          ctypes.c_size_t(ws_bytes), None)
+
+
+def test_argument_errors_return_before_launch(L):
+    assert _prefill(L, _cfg(Hq=6, Hkv=4)) == _lib.HILS_E_ARG
+    assert _prefill(L, _cfg(), null_q=True) == _lib.HILS_E_ARG
+    assert _prefill(L, _cfg(), misalign=True) == _lib.HILS_E_ARG
+    assert _prefill(L, _cfg(d=512)) == _lib.HILS_E_UNSUPPORTED
+    assert _prefill(L, _cfg(S=128)) == _lib.HILS_E_UNSUPPORTED
+    assert _prefill(L, _cfg(mode=2)) == _lib.HILS_E_UNSUPPORTED
+    assert _prefill(L, _cfg(), ws_bytes=16) == _lib.HILS_E_WORKSPACE
+    p = ctypes.c_void_p(0x10000)
+    # k_sum without b_sum
+    assert L.hils_prefill(ctypes.byref(_cfg()), p, None, p, p, p, p, None, p, None, p,
+                          ctypes.c_size_t(1 << 30), None) == _lib.HILS_E_ARG
+    # summarize: chunk range outside [0, N/S]
+    assert L.hils_summarize(ctypes.byref(_cfg()), p, p, 0, 17, p, p, None) == _lib.HILS_E_ARG
+    assert L.hils_summarize(ctypes.byref(_cfg()), p, p, 3, 2, p, p, None) == _lib.HILS_E_ARG
+    assert L.hils_summarize(ctypes.byref(_cfg()), p, p, 2, 2, p, p, None) == _lib.HILS_OK
+    # decode: missing seqlen, head dim not a multiple of the vector width
+    assert L.hils_decode(ctypes.byref(_cfg()), p, None, p, p, None, p, p, p, None, p,
+                         ctypes.c_size_t(1 << 30), None) == _lib.HILS_E_ARG
+    assert L.hils_decode(ctypes.byref(_cfg(d=12)), p, None, p, p, p, p, p, p, None, p,
+                         ctypes.c_size_t(1 << 30), None) == _lib.HILS_E_UNSUPPORTED
+
+
+def test_product_path_does_not_touch_the_oracle():
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                txt = open(os.path.join(dirpath, f), errors="ignore").read()
+                assert "oracle" not in txt.lower(), f"{f} mentions the oracle"

@@ -1,0 +1,194 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Inputs come from the seeded generators in synth/; expected values come only
+from oracle/.  Every test prints what it covered (selection exact / tie-band
+counts and the largest output error).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import hils_oracle as O
+from tests.parity_util import (Tally, check_selection, compare_prefill_rows, np32, out_error,
+                               sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import chunk_wise_hierarchical_amd as hils
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _gpu_inputs(w, device="cuda", **kw):
+    gen_dev = "cpu" if w.B * w.Hq * w.N * w.d <= (1 << 26) else device
+    x = synth.make_prefill_inputs(w, device=gen_dev, **kw)
+    return {k: v.to(device) for k, v in x.items()}
+
+
+def _run_prefill(w, x, mode="surrogate", generic=False):
+    B, Hq, N, d = x["q"].shape
+    nC = N // w.S
+    ks = torch.empty((B, Hq, nC, d), dtype=x["q"].dtype, device="cuda")
+    bs = torch.empty((B, Hq, nC), dtype=torch.float32, device="cuda")
+    sel = torch.empty((B, w.Hkv, N, w.K), dtype=torch.int32, device="cuda")
+    out = hils.prefill(x["q"], x["k"], x["v"], x["lm"], w.S, w.W, w.K, q_route=x.get("q_route"),
+                       mode=mode, sel=sel, summaries=(ks, bs), generic=generic)
+    torch.cuda.synchronize()
+    return out, sel, ks, bs
+
+
+def _oracle_summaries(w, xn, mode="surrogate"):
+    return O.ref_summarize(xn["k"], xn["lm"], w.S, mode=mode, store=w.dtype)
+
+
+def _check_summaries(w, ks, bs, ref):
+    rks, rbs = ref
+    gks = np32(ks).astype(np.float64)
+    gbs = np32(bs).astype(np.float64)
+    nbad = int((gks != rks).sum())
+    # k' is the correctly rounded exact summary on both sides: expect identity
+    assert nbad <= max(1, gks.size // 10**6), f"{nbad} summary-key elements differ"
+    rel = np.abs(gbs - rbs) / np.maximum(np.abs(rbs), 1e-30)
+    assert rel.max() <= 1e-6, f"b' rel err {rel.max()}"
+    return nbad
+
+
+def _prefill_case(w, rows=None, mode="surrogate", generic=False, q_route=False, label=""):
+    _say(f"[prefill] {label} {w.name} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} d={w.d} S={w.S} "
+         f"W={w.W} K={w.K} dtype={w.dtype} mode={mode} generic={generic}")
+    x = _gpu_inputs(w, with_q_route=q_route)
+    out, sel, ks, bs = _run_prefill(w, x, mode=mode, generic=generic)
+    xn = {k: np32(v) for k, v in x.items()}
+    summ = _oracle_summaries(w, xn, mode)
+    nbad = _check_summaries(w, ks, bs, summ)
+    if rows is None:
+        rows = [(b, i) for b in range(w.B) for i in range(w.N)]
+    res = O.ref_prefill_rows(xn["q"], xn["k"], xn["v"], xn["lm"], rows, w.S, w.W, w.K,
+                             q_route=xn.get("q_route"), mode=mode, store=w.dtype, summaries=summ)
+    t = compare_prefill_rows(res, np32(out), sel.cpu().numpy(), rows, w)
+    _say(f"   summaries: {nbad} k' elements differ; {t}")
+    assert t.exact >= 0.9 * (t.exact + t.tie)
+    return t
+
+
+# ---------------------------------------------------------------------------
+# prefill, generic kernels
+# ---------------------------------------------------------------------------
+
+def test_prefill_tiny_fp32_all_rows():
+    w = synth.get_workload("tiny_fp32")
+    _prefill_case(w, label="tiny fp32 all rows")
+
+
+def test_prefill_bf16_mha_peaked_all_rows():
+    w = synth.get_workload("prefill_8k", N=2048, B=2)
+    _prefill_case(w, label="8K-geometry MHA, N=2048")
+
+
+def test_prefill_bf16_gqa_sampled():
+    w = synth.get_workload("prefill_64k", N=8192, W=1024, K=32)
+    _prefill_case(w, rows=sample_rows(w, 160), label="64K-geometry GQA 4:1, N=8192")
+
+
+def test_prefill_ragged_and_degenerate():
+    # N not a multiple of S, K larger than some candidate sets, GQA 2:1
+    w = synth.get_workload("prefill_64k", N=1000, Hq=4, Hkv=2, d=64, S=32, W=100, K=8,
+                           regime="iid")
+    _prefill_case(w, label="ragged N=1000 S=32")
+    # window covering the whole sequence: no candidates anywhere
+    w2 = w.with_(N=300, W=400)
+    _prefill_case(w2, label="W > N")
+    # one token, one chunk
+    w3 = w.with_(N=1, W=1, S=1, K=1)
+    _prefill_case(w3, label="N=1")
+
+
+def test_prefill_q_route_and_landmark_key():
+    w = synth.get_workload("prefill_64k", N=2048, Hq=8, Hkv=2, W=256, K=8)
+    _prefill_case(w, rows=sample_rows(w, 120), q_route=True, label="q_route")
+    _prefill_case(w, rows=sample_rows(w, 120), mode="landmark_key", label="landmark_key")
+
+
+def test_prefill_deterministic():
+    w = synth.get_workload("prefill_64k", N=4096, W=512, K=16)
+    x = _gpu_inputs(w)
+    o1, s1, _, _ = _run_prefill(w, x)
+    o2, s2, _, _ = _run_prefill(w, x)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def _decode_case(w, seqlen, label="", q_route=False, seqs=None):
+    _say(f"[decode] {label} {w.name} B={w.B} T={w.N} Hq={w.Hq} Hkv={w.Hkv} d={w.d} S={w.S} "
+         f"W={w.W} K={w.K} seqlen={seqlen[:4]}...")
+    gen_dev = "cpu" if w.B * w.Hkv * w.N * w.d <= (1 << 26) else "cuda"
+    x = synth.make_decode_inputs(w, device=gen_dev, seqlen=seqlen, with_q_route=q_route)
+    x = {k: v.cuda() for k, v in x.items()}
+    ks, bs = hils.summarize(x["k"], x["lm"], w.S)
+    sel = torch.empty((w.B, w.Hkv, w.K), dtype=torch.int32, device="cuda")
+    out = hils.decode(x["q"], x["k"], x["v"], x["seqlen"], ks, bs, w.S, w.W, w.K,
+                      q_route=x.get("q_route"), sel=sel)
+    torch.cuda.synchronize()
+    seqs = range(w.B) if seqs is None else seqs
+    t = Tally()
+    gsel = sel.cpu().numpy()
+    gout = np32(out)
+    for b in seqs:
+        _say(f"   checking sequence {b}")
+        T = int(seqlen[b])
+        n = O.n_candidates(T - 1, w.W, w.S)
+        kb = np32(x["k"][b:b + 1, :, :T])
+        vb = np32(x["v"][b:b + 1, :, :T])
+        lb = np32(x["lm"][b:b + 1, :, :max(n, 1)])
+        qb = np32(x["q"][b:b + 1])
+        qrb = np32(x["q_route"][b:b + 1]) if q_route else None
+        summ = O.ref_summarize(kb[:, :, :n * w.S], lb[:, :, :n], w.S, store=w.dtype) if n else None
+        # the decode query stands at position T-1 (a zero-copy broadcast view over positions)
+        qq = np.broadcast_to(qb, (1, w.Hq, T, w.d))
+        qr = np.broadcast_to(qrb, (1, w.Hq, T, w.d)) if q_route else None
+        # decode is the prefill row i = T-1 (same definition)
+        res = O.ref_prefill_rows(qq, kb, vb, lb, [(0, T - 1)], w.S, w.W, w.K, q_route=qr,
+                                 store=w.dtype, summaries=summ if n else
+                                 (np.zeros((1, w.Hq, 0, w.d)), np.zeros((1, w.Hq, 0))))
+        r = res[(0, T - 1)]
+        t.rows += 1
+        G = w.G
+        for g in range(w.Hkv):
+            kind = check_selection(gsel[b, g], dict(sel=r["sel"][g], gap=r["gap"][g],
+                                                    s_hat=r["s_hat"][g]), w.K)
+            if kind == "exact":
+                t.exact += 1
+                hs = slice(g * G, (g + 1) * G)
+                err, tol = out_error(gout[b, hs, 0], r["out"][hs], w.dtype)
+                t.tol, t.max_err = tol, max(t.max_err, err)
+                assert err <= tol, f"decode output error {err} > {tol} (b={b}, g={g})"
+            else:
+                t.tie += 1
+    _say(f"   {t}")
+    return t
+
+
+def test_decode_small_ragged():
+    w = synth.get_workload("decode_512k", N=8192, B=4)
+    _decode_case(w, [8192, 5000, 700, 1], label="ragged seqlen")
+
+
+def test_decode_fp32_and_q_route():
+    w = synth.get_workload("decode_512k", N=4096, B=2, dtype="f32", Hq=4, Hkv=2, d=64, K=8,
+                           W=256)
+    _decode_case(w, [4096, 3001], label="fp32", q_route=True)
+
+
+def test_decode_full_512k_sampled_sequences():
+    w = synth.get_workload("decode_512k")
+    _decode_case(w, [w.N] * w.B, label="full size, 2 sequences checked", seqs=[0, 15])
