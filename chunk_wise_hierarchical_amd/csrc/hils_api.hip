@@ -46,16 +46,34 @@ hils_status make_shape(const hils_cfg* c, HilsShape& s) {
 
 inline size_t esize(const HilsShape& s) { return s.dtype == HILS_BF16 ? 2 : 4; }
 
+// The MFMA fast path covers bf16, d = 128, S = 64, G in {1, 2, 4}, K <= 64.
+bool fast_eligible(const HilsShape& s, uint32_t flags) {
+  if (flags & HILS_FLAG_GENERIC) return false;
+  if (s.dtype != HILS_BF16 || s.d != 128 || s.S != 64 || s.K > 64) return false;
+  if (!(s.G == 1 || s.G == 2 || s.G == 4)) return false;
+  if (s.nC > HILS_FAST_NCMAX) return false;
+  return true;
+}
+
 struct PrefillLayout {
-  size_t ks, bs, sel, slog, total;
+  size_t ks, bs, sel, slog, vt, total;
 };
-PrefillLayout prefill_layout(const HilsShape& s) {
+// generic path: summaries, selection, fusion logits; fast path: summaries,
+// selection and the per-chunk transposed V (fusion logits are recomputed in
+// the attention kernel)
+PrefillLayout prefill_layout(const HilsShape& s, bool fast) {
   PrefillLayout L{};
   size_t off = 0;
   L.ks = off;   off += align_up((size_t)s.B * s.Hq * s.nC * s.d * esize(s));
   L.bs = off;   off += align_up((size_t)s.B * s.Hq * s.nC * 4);
   L.sel = off;  off += align_up((size_t)s.B * s.Hkv * s.N * s.K * 4);
-  L.slog = off; off += align_up((size_t)s.B * s.Hq * s.N * s.K * 4);
+  if (fast) {
+    L.slog = 0;
+    L.vt = off; off += align_up((size_t)s.B * s.Hkv * s.nCc * s.d * s.S * 2);
+  } else {
+    L.slog = off; off += align_up((size_t)s.B * s.Hq * s.N * s.K * 4);
+    L.vt = 0;
+  }
   L.total = off;
   return L;
 }
@@ -98,7 +116,7 @@ int hils_abi_version(void) { return HILS_ABI_VERSION; }
 size_t hils_workspace_bytes(const hils_cfg* cfg, int is_decode) {
   HilsShape s;
   if (make_shape(cfg, s) != HILS_OK) return 0;
-  return is_decode ? decode_layout(s).total : prefill_layout(s).total;
+  return is_decode ? decode_layout(s).total : prefill_layout(s, fast_eligible(s, cfg->flags)).total;
 }
 
 hils_status hils_summarize(const hils_cfg* cfg, const void* k, const void* lm_q, int32_t c0,
@@ -128,19 +146,28 @@ hils_status hils_prefill(const hils_cfg* cfg, const void* q, const void* q_route
   const void* ptrs[] = {q, q_route, k, v, lm_q, out, sel, k_sum, b_sum, ws};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return HILS_E_ARG;
-  if (s.nmax > HILS_GENERIC_NMAX) return HILS_E_UNSUPPORTED;
+  const bool fast = fast_eligible(s, cfg->flags);
+  if (!fast && s.nmax > HILS_GENERIC_NMAX) return HILS_E_UNSUPPORTED;
   if ((long long)s.B * s.Hkv * s.N >= (1LL << 31)) return HILS_E_UNSUPPORTED;
-  const PrefillLayout L = prefill_layout(s);
+  const PrefillLayout L = prefill_layout(s, fast);
   if (ws_bytes < L.total || (L.total > 0 && !ws)) return HILS_E_WORKSPACE;
   char* w = static_cast<char*>(ws);
   void* ks = k_sum ? k_sum : (void*)(w + L.ks);
   float* bs = b_sum ? b_sum : (float*)(w + L.bs);
   int32_t* sl = sel ? sel : (int32_t*)(w + L.sel);
-  float* slog = (float*)(w + L.slog);
   const void* qr = q_route ? q_route : q;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = hils_launch_summarize(s, k, lm_q, 0, s.nC, ks, bs, st);
   if (e != hipSuccess) return HILS_E_HIP;
+  if (fast) {
+    void* vt = (void*)(w + L.vt);
+    e = hils_launch_vt(s, v, vt, st);
+    if (e != hipSuccess) return HILS_E_HIP;
+    e = hils_launch_score_fast(s, qr, ks, bs, sl, st);
+    if (e != hipSuccess) return HILS_E_HIP;
+    return hip_status(hils_launch_attn_fast(s, q, qr, k, vt, ks, bs, sl, out, st));
+  }
+  float* slog = (float*)(w + L.slog);
   e = hils_launch_select_generic(s, qr, ks, bs, sl, slog, st);
   if (e != hipSuccess) return HILS_E_HIP;
   e = hils_launch_attn_generic(s, q, k, v, sl, slog, out, st);

@@ -24,6 +24,17 @@ hipError_t hils_launch_select_generic(const HilsShape& s, const void* qr, const 
 hipError_t hils_launch_attn_generic(const HilsShape& s, const void* q, const void* k, const void* v,
                                     const int32_t* sel, const float* slog, void* out, hipStream_t st);
 
+// fast path (bf16, d = 128, S = 64, G in {1,2,4}, K <= 64): fast_score.hip, fast_attn.hip
+hipError_t hils_launch_vt(const HilsShape& s, const void* v, void* vt, hipStream_t st);
+hipError_t hils_launch_score_fast(const HilsShape& s, const void* qr, const void* ksum,
+                                  const float* bsum, int32_t* sel, hipStream_t st);
+hipError_t hils_launch_attn_fast(const HilsShape& s, const void* q, const void* qr, const void* k,
+                                 const void* vt, const void* ksum, const float* bsum,
+                                 const int32_t* sel, void* out, hipStream_t st);
+size_t hils_fast_score_lds(int G, int K);
+size_t hils_fast_attn_lds(int G, int K);
+constexpr int HILS_FAST_NCMAX = 16384;   // chunk ids the fast attention bitmap covers
+
 // decode.hip
 hipError_t hils_launch_decode(const HilsShape& s, const void* q, const void* qr, const void* k,
                               const void* v, const int32_t* seqlen, const void* ksum,

@@ -116,6 +116,79 @@ def test_prefill_q_route_and_landmark_key():
     _prefill_case(w, rows=sample_rows(w, 120), mode="landmark_key", label="landmark_key")
 
 
+def test_prefill_generic_kernels_bf16():
+    # the same geometries through the vector-ALU kernels (HILS_FLAG_GENERIC)
+    w = synth.get_workload("prefill_8k", N=1024, B=1)
+    _prefill_case(w, generic=True, label="generic MHA")
+    w = synth.get_workload("prefill_64k", N=4096, W=512, K=16)
+    _prefill_case(w, rows=sample_rows(w, 100), generic=True, label="generic GQA")
+
+
+def test_prefill_fast_ragged():
+    # fast path (bf16, d=128, S=64) with N not a multiple of 64 and of the query block
+    for G, N in ((2, 3001), (4, 2049), (1, 1500)):
+        w = synth.get_workload("prefill_64k", N=N, Hq=2 * G, Hkv=2, W=200, K=8, regime="mod3")
+        _prefill_case(w, label=f"fast ragged G={G}")
+
+
+def test_fast_and_generic_agree():
+    w = synth.get_workload("prefill_64k", N=4096, W=512, K=16)
+    x = _gpu_inputs(w)
+    o1, s1, _, _ = _run_prefill(w, x, generic=False)
+    o2, s2, _, _ = _run_prefill(w, x, generic=True)
+    same = (s1 == s2).all(dim=-1).cpu().numpy()           # [B, Hkv, N]
+    frac = float(same.mean())
+    err = np.abs(np32(o1) - np32(o2))[same.repeat(w.G, axis=1)]
+    _say(f"   fast/generic identical selections: {frac:.5f}; max |out diff| {err.max():.3g}")
+    assert frac > 0.999
+    assert err.max() < 2e-2
+
+
+def _group_slice(x, w, g):
+    G = w.G
+    return dict(q=x["q"][:, g * G:(g + 1) * G], k=x["k"][:, g:g + 1], v=x["v"][:, g:g + 1],
+                lm=x["lm"][:, g * G:(g + 1) * G])
+
+
+def _large_sampled(w, groups, nrows, label):
+    _say(f"[prefill] {label} {w.name} N={w.N} Hq={w.Hq} Hkv={w.Hkv} K={w.K} W={w.W} groups={groups}")
+    x = {k2: v2 for k2, v2 in synth.make_prefill_inputs(w, device="cuda").items()}
+    _run_prefill(w, x)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    out, sel, ks, bs = _run_prefill(w, x)
+    t1.record()
+    torch.cuda.synchronize()
+    _say(f"   prefill time {t0.elapsed_time(t1):.2f} ms")
+    rows = sample_rows(w, nrows, include=[w.N - 2, w.N - 65])
+    t = Tally()
+    wg = w.with_(Hq=w.G, Hkv=1)
+    for g in groups:
+        _say(f"   group {g}: oracle summaries")
+        xg = {k2: np32(v2) for k2, v2 in _group_slice(x, w, g).items()}
+        summ = O.ref_summarize(xg["k"], xg["lm"], w.S, store=w.dtype)
+        gk = np32(ks[:, g * w.G:(g + 1) * w.G]).astype(np.float64)
+        assert int((gk != summ[0]).sum()) <= max(1, gk.size // 10**6)
+        _say(f"   group {g}: oracle rows")
+        res = O.ref_prefill_rows(xg["q"], xg["k"], xg["v"], xg["lm"], rows, w.S, w.W, w.K,
+                                 store=w.dtype, summaries=summ)
+        compare_prefill_rows(res, np32(out[:, g * w.G:(g + 1) * w.G]),
+                             sel[:, g:g + 1].cpu().numpy(), rows, wg, tally=t)
+    _say(f"   {t}")
+    assert t.exact >= 0.9 * (t.exact + t.tie)
+
+
+def test_prefill_full_64k_sampled():
+    w = synth.get_workload("prefill_64k")
+    _large_sampled(w, groups=[0, 5], nrows=96, label="full 64K")
+
+
+def test_prefill_full_512k_sampled():
+    w = synth.get_workload("prefill_512k")
+    _large_sampled(w, groups=[0, 7], nrows=48, label="full 512K")
+
+
 def test_prefill_deterministic():
     w = synth.get_workload("prefill_64k", N=4096, W=512, K=16)
     x = _gpu_inputs(w)
