@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""HiLS attention forward on one MI355X: prefill tokens/s and decode steps/s at 512K context.
+
+A step is one HiLS prefill of the prefill workload (summaries, scoring and
+top-K, window + selected-chunk attention, fusion); the decode workload's
+single-step decode is timed in the same run and reported under "decode".
+Inputs are seeded synthetic tensors (synth/) already resident in HBM when the
+timed region starts.  Per-kernel durations come from HIP events the library
+records on its own stream (hils_profile_enable) inside the timed region.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_512k]
+                    [--decode-workload decode_512k] [--decode-steps 50] [--no-cpu]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def _geometry(N, W, S):
+    i = np.arange(N, dtype=np.int64)
+    left = np.floor_divide(i - W + 1, S) * S
+    n = np.maximum(0, left // S)
+    win = i - np.maximum(0, left) + 1
+    return n, win
+
+
+def prefill_work(w):
+    """Algorithmic FLOPs: (scoring, summaries, attention) for one prefill."""
+    n, win = _geometry(w.N, w.W, w.S)
+    score = 2.0 * w.d * float(n.sum()) * w.Hq * w.B
+    summ = 4.0 * w.B * w.Hq * (w.N // w.S) * w.S * w.d
+    attn = 4.0 * w.d * float((np.minimum(w.K, n) * w.S + win).sum()) * w.Hq * w.B
+    return score, summ, attn
+
+
+def decode_work(w, T):
+    """Algorithmic HBM bytes of one decode step (all sequences at length T), and the
+    bytes of the summary-scoring kernel alone (k', b' read, scores written)."""
+    n, win = _geometry(T, w.W, w.S)
+    n, win = int(n[-1]), int(win[-1])
+    e = 2 if w.dtype == "bf16" else 4
+    per_seq = (w.Hq * n * (w.d * e + 4) + w.Hkv * min(w.K, n) * w.S * w.d * e * 2
+               + w.Hkv * win * w.d * e * 2 + 2 * w.Hq * w.d * e)
+    score_bytes = w.B * w.Hq * n * (w.d * e + 4 + 4)
+    return per_seq * w.B, score_bytes
+
+
+def _kernel_table(records, steps):
+    agg = {}
+    for name, ms in records:
+        a = agg.setdefault(name, [0.0, 0])
+        a[0] += ms
+        a[1] += 1
+    return {k: {"ms_per_step": v[0] / steps, "calls": v[1], "avg_ms": v[0] / v[1]} for k, v in agg.items()}
+
+
+def _overlap(sel, K, M=16, blocks=64):
+    """Normalised chunk overlap of M adjacent queries (section 7.2) over the
+    last `blocks` full blocks of KV group 0 (rows with at least K candidates)."""
+    s = sel[0, 0].cpu().numpy()
+    N = s.shape[0]
+    vals = []
+    for bidx in range(blocks):
+        hi = N - bidx * M
+        blk = s[hi - M:hi]
+        if (blk < 0).any():
+            break
+        u = len(set(blk.ravel().tolist()))
+        vals.append((M * K - u) / ((M - 1) * K))
+    return float(np.mean(vals)) if vals else None
+
+
+def cpu_baseline_prefill(x, w, rows=32):
+    """Oracle on one KV group: summaries of every chunk + `rows` query rows;
+    full-prefill time extrapolated to all groups and positions."""
+    from threadpoolctl import threadpool_limits
+    from oracle import hils_oracle as O
+    G = w.G
+    with threadpool_limits(1):
+        qg = x["q"][:, :G].float().cpu().numpy()
+        kg = x["k"][:, :1].float().cpu().numpy()
+        vg = x["v"][:, :1].float().cpu().numpy()
+        lg = x["lm"][:, :G].float().cpu().numpy()
+        t0 = time.perf_counter()
+        summ = O.ref_summarize(kg, lg, w.S, store=w.dtype)
+        t1 = time.perf_counter()
+        idx = np.linspace(w.W + w.S, w.N - 1, rows).astype(int)
+        O.ref_prefill_rows(qg, kg, vg, lg, [(0, int(i)) for i in idx], w.S, w.W, w.K,
+                           store=w.dtype, summaries=summ)
+        t2 = time.perf_counter()
+    t_full = w.Hkv * w.B * ((t1 - t0) + (t2 - t1) * w.N / rows)
+    return {"value": w.B * w.N / t_full, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": (f"KV group 0 of {w.Hkv}: summaries of all {w.N // w.S} chunks "
+                       f"({t1 - t0:.1f} s) + {rows} query rows spread over the sequence "
+                       f"({t2 - t1:.1f} s); full prefill extrapolated = {w.Hkv * w.B} groups x "
+                       f"(summaries + rows x {w.N}/{rows}) = {t_full:.0f} s; NumPy float64, 1 BLAS thread")}
+
+
+def cpu_baseline_decode(xd, wd):
+    """Oracle decode of one sequence and one KV group; step time extrapolated."""
+    from threadpoolctl import threadpool_limits
+    from oracle import hils_oracle as O
+    G = wd.G
+    T = wd.N
+    with threadpool_limits(1):
+        q = xd["q"][:1, :G].float().cpu().numpy()
+        k = xd["k"][:1, :1].float().cpu().numpy()
+        v = xd["v"][:1, :1].float().cpu().numpy()
+        lm = xd["lm"][:1, :G].float().cpu().numpy()
+        t0 = time.perf_counter()
+        O.ref_decode(q, k, v, [T], lm, wd.S, wd.W, wd.K, store=wd.dtype)
+        t1 = time.perf_counter()
+    t_step = (t1 - t0) * wd.Hkv * wd.B
+    return {"value": 1.0 / t_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": (f"sequence 0, KV group 0 ({t1 - t0:.1f} s incl. summaries of its "
+                       f"{T // wd.S} chunks); step time extrapolated x {wd.Hkv} groups x "
+                       f"{wd.B} sequences = {t_step:.0f} s; NumPy float64, 1 BLAS thread")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="prefill_512k")
+    ap.add_argument("--decode-workload", default="decode_512k")
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import chunk_wise_hierarchical_amd as hils
+    from chunk_wise_hierarchical_amd import _lib
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---------------- prefill ----------------
+    w = synth.get_workload(args.workload)
+    log(f"prefill inputs {w.name}: B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} d={w.d} S={w.S} W={w.W} K={w.K}")
+    x = synth.make_prefill_inputs(w, device=dev)
+    out = torch.empty_like(x["q"])
+    sel = torch.empty((w.B, w.Hkv, w.N, w.K), dtype=torch.int32, device=dev)
+    cfg = hils.make_cfg(w.B, w.N, w.Hq, w.Hkv, w.d, w.S, w.W, w.K, x["q"].dtype)
+    ws = torch.empty(max(1, hils.workspace_bytes(cfg, False)), dtype=torch.uint8, device=dev)
+
+    def step():
+        hils.prefill(x["q"], x["k"], x["v"], x["lm"], w.S, w.W, w.K, out=out, sel=sel, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("prefill warm")
+    _lib.profile_enable(True)
+    _lib.profile_read()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1) / args.steps
+    kern = _kernel_table(_lib.profile_read(), args.steps)
+    _lib.profile_enable(False)
+    log(f"prefill {prefill_ms:.2f} ms/step; kernels {json.dumps(kern)}")
+    overlap = _overlap(sel, w.K)
+
+    score_f, summ_f, attn_f = prefill_work(w)
+    dom = max(kern, key=lambda k2: kern[k2]["ms_per_step"])
+    dom_flops = {"k_attn_fast": attn_f, "k_attn_generic": attn_f, "k_score_fast": score_f,
+                 "k_select_generic": score_f, "k_summarize": summ_f}.get(dom, attn_f)
+    achieved = dom_flops / (kern[dom]["avg_ms"] * 1e-3) / 1e12
+    roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+            "algorithmic_flops_per_launch": dom_flops}
+    total_tflops = (score_f + summ_f + attn_f) / (prefill_ms * 1e-3) / 1e12
+
+    cpu_pre = None
+    if not args.no_cpu:
+        log("oracle baseline (prefill sample)")
+        cpu_pre = cpu_baseline_prefill(x, w)
+    del x, out, ws
+    sel_cpu_overlap = overlap
+    del sel
+    torch.cuda.empty_cache()
+
+    # ---------------- decode ----------------
+    dec = None
+    if not args.no_decode:
+        wd = synth.get_workload(args.decode_workload)
+        log(f"decode inputs {wd.name}: B={wd.B} T={wd.N} Hq={wd.Hq} Hkv={wd.Hkv} W={wd.W} K={wd.K}")
+        xd = synth.make_decode_inputs(wd, device=dev)
+        ks, bs = hils.summarize(xd["k"], xd["lm"], wd.S)
+        outd = torch.empty_like(xd["q"])
+        cfgd = hils.make_cfg(wd.B, wd.N, wd.Hq, wd.Hkv, wd.d, wd.S, wd.W, wd.K, xd["q"].dtype)
+        wsd = torch.empty(max(1, hils.workspace_bytes(cfgd, True)), dtype=torch.uint8, device=dev)
+
+        def dstep():
+            hils.decode(xd["q"], xd["k"], xd["v"], xd["seqlen"], ks, bs, wd.S, wd.W, wd.K,
+                        out=outd, ws=wsd)
+
+        for _ in range(max(3, args.warmup)):
+            dstep()
+        torch.cuda.synchronize()
+        _lib.profile_enable(True)
+        _lib.profile_read()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.decode_steps):
+            dstep()
+        e1.record()
+        torch.cuda.synchronize()
+        dec_ms = e0.elapsed_time(e1) / args.decode_steps
+        dk = _kernel_table(_lib.profile_read(), args.decode_steps)
+        _lib.profile_enable(False)
+        log(f"decode {dec_ms:.3f} ms/step; kernels {json.dumps(dk)}")
+        step_bytes, score_bytes = decode_work(wd, wd.N)
+        sc = dk.get("k_dec_score")
+        dach = score_bytes / (sc["avg_ms"] * 1e-3) / 1e9 if sc else None
+        dec = {"workload": wd.name, "metric": "decode steps/s", "value": 1000.0 / dec_ms,
+               "unit": "steps/s", "ms_per_step": dec_ms, "tokens_per_s": wd.B * 1000.0 / dec_ms,
+               "config": {"workload": wd.name, "B": wd.B, "T": wd.N, "Hq": wd.Hq, "Hkv": wd.Hkv,
+                          "d": wd.d, "S": wd.S, "W": wd.W, "K": wd.K},
+               "step_hbm_gbs": step_bytes / (dec_ms * 1e-3) / 1e9,
+               "step_frac_hbm": step_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+               "algorithmic_bytes_per_step": step_bytes,
+               "roofline": {"kernel": "k_dec_score", "bound": "hbm", "achieved": dach,
+                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": (dach / PEAK_HBM_GBS) if dach else None, "traffic": None,
+                            "algorithmic_bytes_per_launch": score_bytes},
+               "kernels": dk}
+        if not args.no_cpu:
+            log("oracle baseline (decode sample)")
+            dec["cpu_baseline"] = cpu_baseline_decode(xd, wd)
+        del xd, ks, bs, outd, wsd
+
+    line = {
+        "metric": "prefill tokens/s and decode steps/s at 512K ctx; % of MFMA/HBM roofline",
+        "value": w.B * w.N / (prefill_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": prefill_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
+                   "S": w.S, "W": w.W, "K": w.K, "regime": w.regime,
+                   "chunk_overlap_M16": sel_cpu_overlap},
+        "useful_tflops_total": total_tflops,
+        "algorithmic_tflop": {"scoring": score_f / 1e12, "summaries": summ_f / 1e12,
+                              "attention": attn_f / 1e12},
+        "roofline": roof,
+        "cpu_baseline": cpu_pre,
+        "kernels": kern,
+        "decode": dec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

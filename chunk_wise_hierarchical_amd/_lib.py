@@ -17,7 +17,7 @@ MODES = {"surrogate": 0, "landmark_key": 1, "exact": 2}
 HILS_FLAG_GENERIC = 1
 
 EXPORTED = ("hils_workspace_bytes", "hils_summarize", "hils_prefill", "hils_decode",
-            "hils_strerror", "hils_abi_version")
+            "hils_strerror", "hils_abi_version", "hils_profile_enable", "hils_profile_read")
 
 
 class HilsCfg(ctypes.Structure):
@@ -59,12 +59,29 @@ def lib() -> ctypes.CDLL:
         L.hils_strerror.restype = ctypes.c_char_p
         L.hils_abi_version.argtypes = []
         L.hils_abi_version.restype = ctypes.c_int
+        L.hils_profile_enable.argtypes = [ctypes.c_int]
+        L.hils_profile_enable.restype = None
+        L.hils_profile_read.argtypes = [ctypes.POINTER(ctypes.c_char_p),
+                                        ctypes.POINTER(ctypes.c_float), ctypes.c_int]
+        L.hils_profile_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
 
 def strerror(status: int) -> str:
     return lib().hils_strerror(status).decode()
+
+
+def profile_enable(on: bool) -> None:
+    lib().hils_profile_enable(1 if on else 0)
+
+
+def profile_read(cap: int = 4096):
+    """[(kernel name, ms)] of the kernels enqueued since the last read (streams synchronised)."""
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_float * cap)()
+    n = lib().hils_profile_read(names, ms, cap)
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n, cap))]
 
 
 def check(status: int, what: str) -> None:

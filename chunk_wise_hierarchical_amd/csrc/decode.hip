@@ -363,29 +363,29 @@ hipError_t hils_launch_decode(const HilsShape& s, const void* q, const void* qr,
   const size_t ashm = (size_t)s.G * s.d * 4;
   if (s.dtype == 0) {
     if (nsb > 0)
-      hipLaunchKernelGGL(k_dec_score<bf16_t>, dim3(s.B * s.Hq, nsb), dim3(256), 0, st,
+      { HilsProfScope ps_("k_dec_score", st); hipLaunchKernelGGL(k_dec_score<bf16_t>, dim3(s.B * s.Hq, nsb), dim3(256), 0, st,
                          (const bf16_t*)qr, (const bf16_t*)ksum, bsum, seqlen, scores, s.Hq, s.nC,
-                         s.nmax, s.N, s.d, s.S, s.W, tau);
+                         s.nmax, s.N, s.d, s.S, s.W, tau); }
   } else {
     if (nsb > 0)
-      hipLaunchKernelGGL(k_dec_score<float>, dim3(s.B * s.Hq, nsb), dim3(256), 0, st,
+      { HilsProfScope ps_("k_dec_score", st); hipLaunchKernelGGL(k_dec_score<float>, dim3(s.B * s.Hq, nsb), dim3(256), 0, st,
                          (const float*)qr, (const float*)ksum, bsum, seqlen, scores, s.Hq, s.nC,
-                         s.nmax, s.N, s.d, s.S, s.W, tau);
+                         s.nmax, s.N, s.d, s.S, s.W, tau); }
   }
-  hipLaunchKernelGGL(k_dec_select, dim3(s.B * s.Hkv), dim3(SEL_NT), 0, st, scores, seqlen, keys,
-                     sel, slog, s.Hq, s.Hkv, s.G, s.nmax > 0 ? s.nmax : 1, s.N, s.S, s.W, s.K);
+  { HilsProfScope ps_("k_dec_select", st); hipLaunchKernelGGL(k_dec_select, dim3(s.B * s.Hkv), dim3(SEL_NT), 0, st, scores, seqlen, keys,
+                     sel, slog, s.Hq, s.Hkv, s.G, s.nmax > 0 ? s.nmax : 1, s.N, s.S, s.W, s.K); }
   if (s.dtype == 0) {
-    hipLaunchKernelGGL(k_dec_attn<bf16_t>, dim3(s.B * s.Hkv, NS), dim3(AT_NT), ashm, st,
+    { HilsProfScope ps_("k_dec_attn", st); hipLaunchKernelGGL(k_dec_attn<bf16_t>, dim3(s.B * s.Hkv, NS), dim3(AT_NT), ashm, st,
                        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, seqlen, sel, part,
-                       s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, NS, tau);
-    hipLaunchKernelGGL(k_dec_combine<bf16_t>, dim3(s.B * s.Hq), dim3(64), 0, st, part, slog,
-                       seqlen, (bf16_t*)out, s.Hq, s.G, s.N, s.d, s.S, s.W, s.K, NS, s.nwin);
+                       s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, NS, tau); }
+    { HilsProfScope ps_("k_dec_combine", st); hipLaunchKernelGGL(k_dec_combine<bf16_t>, dim3(s.B * s.Hq), dim3(64), 0, st, part, slog,
+                       seqlen, (bf16_t*)out, s.Hq, s.G, s.N, s.d, s.S, s.W, s.K, NS, s.nwin); }
   } else {
-    hipLaunchKernelGGL(k_dec_attn<float>, dim3(s.B * s.Hkv, NS), dim3(AT_NT), ashm, st,
+    { HilsProfScope ps_("k_dec_attn", st); hipLaunchKernelGGL(k_dec_attn<float>, dim3(s.B * s.Hkv, NS), dim3(AT_NT), ashm, st,
                        (const float*)q, (const float*)k, (const float*)v, seqlen, sel, part,
-                       s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, NS, tau);
-    hipLaunchKernelGGL(k_dec_combine<float>, dim3(s.B * s.Hq), dim3(64), 0, st, part, slog,
-                       seqlen, (float*)out, s.Hq, s.G, s.N, s.d, s.S, s.W, s.K, NS, s.nwin);
+                       s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, NS, tau); }
+    { HilsProfScope ps_("k_dec_combine", st); hipLaunchKernelGGL(k_dec_combine<float>, dim3(s.B * s.Hq), dim3(64), 0, st, part, slog,
+                       seqlen, (float*)out, s.Hq, s.G, s.N, s.d, s.S, s.W, s.K, NS, s.nwin); }
   }
   return hipGetLastError();
 }

@@ -382,18 +382,18 @@ hipError_t launch_attn(const HilsShape& s, const void* q, const void* qr, const 
   auto f = k_attn_fast<G>;
   hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
   const float tau2 = (float)(s.tau * 1.4426950408889634);
-  hipLaunchKernelGGL(f, dim3((unsigned)((long long)s.B * s.Hkv * nqb)), dim3(NT), L.total, st,
+  { HilsProfScope ps_("k_attn_fast", st); hipLaunchKernelGGL(f, dim3((unsigned)((long long)s.B * s.Hkv * nqb)), dim3(NT), L.total, st,
                      (const bf16_t*)q, (const bf16_t*)qr, (const bf16_t*)k, (const bf16_t*)vt,
                      (const bf16_t*)ksum, bsum, sel, (bf16_t*)out, s.Hq, s.Hkv, s.N, s.W, s.K, s.nC,
-                     s.nCc, tau2, nqb);
+                     s.nCc, tau2, nqb); }
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t hils_launch_vt(const HilsShape& s, const void* v, void* vt, hipStream_t st) {
-  hipLaunchKernelGGL(k_vt, dim3((unsigned)((long long)s.B * s.Hkv * s.nCc)), dim3(NT), 0, st,
-                     (const bf16_t*)v, (bf16_t*)vt, s.N, s.nCc);
+  { HilsProfScope ps_("k_vt", st); hipLaunchKernelGGL(k_vt, dim3((unsigned)((long long)s.B * s.Hkv * s.nCc)), dim3(NT), 0, st,
+                     (const bf16_t*)v, (bf16_t*)vt, s.N, s.nCc); }
   return hipGetLastError();
 }
 

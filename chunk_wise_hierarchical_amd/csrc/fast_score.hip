@@ -308,9 +308,9 @@ hipError_t launch_score(const HilsShape& s, const void* qr, const void* ksum, co
   auto f = k_score_fast<G>;
   hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
   const float tau2 = (float)(s.tau * 1.4426950408889634);
-  hipLaunchKernelGGL(f, dim3((unsigned)((long long)s.B * s.Hkv * nqb)), dim3(NT), L.total, st,
+  { HilsProfScope ps_("k_score_fast", st); hipLaunchKernelGGL(f, dim3((unsigned)((long long)s.B * s.Hkv * nqb)), dim3(NT), L.total, st,
                      (const bf16_t*)qr, (const bf16_t*)ksum, bsum, sel, s.Hq, s.Hkv, s.N, s.W, s.K,
-                     s.nC, tau2, nqb);
+                     s.nC, tau2, nqb); }
   return hipGetLastError();
 }
 

@@ -3,6 +3,10 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+#include <vector>
+
 #include "../../include/hils.h"
 #include "hils_internal.h"
 
@@ -96,7 +100,44 @@ DecodeLayout decode_layout(const HilsShape& s) {
 
 inline hils_status hip_status(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_E_HIP; }
 
+// ---- kernel timing record ------------------------------------------------
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+std::atomic<int> g_prof_on{0};
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_prof;        // recorded this period
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
 }  // namespace
+
+HilsProfScope::HilsProfScope(const char* name, hipStream_t s) : slot(-1), st(s) {
+  if (!g_prof_on.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRec r{name, prof_event(), prof_event()};
+  if (!r.a || !r.b) return;
+  hipEventRecord(r.a, st);
+  slot = (int)g_prof.size();
+  g_prof.push_back(r);
+}
+
+HilsProfScope::~HilsProfScope() {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (slot < (int)g_prof.size()) hipEventRecord(g_prof[slot].b, st);
+}
 
 extern "C" {
 
@@ -112,6 +153,34 @@ const char* hils_strerror(hils_status st) {
 }
 
 int hils_abi_version(void) { return HILS_ABI_VERSION; }
+
+void hils_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on.store(on ? 1 : 0);
+  if (!on) {
+    for (auto& r : g_prof) { hipEventDestroy(r.a); hipEventDestroy(r.b); }
+    g_prof.clear();
+    for (auto e : g_prof_pool) hipEventDestroy(e);
+    g_prof_pool.clear();
+  }
+}
+
+int hils_profile_read(const char** names, float* ms, int cap) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  const int n = (int)g_prof.size();
+  for (int i = 0; i < n; ++i) {
+    if (i < cap) {
+      float t = 0.0f;
+      if (hipEventElapsedTime(&t, g_prof[i].a, g_prof[i].b) != hipSuccess) t = -1.0f;
+      if (names) names[i] = g_prof[i].name;
+      if (ms) ms[i] = t;
+    }
+    g_prof_pool.push_back(g_prof[i].a);
+    g_prof_pool.push_back(g_prof[i].b);
+  }
+  g_prof.clear();
+  return n;
+}
 
 size_t hils_workspace_bytes(const hils_cfg* cfg, int is_decode) {
   HilsShape s;

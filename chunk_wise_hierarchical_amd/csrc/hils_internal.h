@@ -14,6 +14,14 @@ struct HilsShape {
   double tau;  // logit scale
 };
 
+// Kernel timing (hils_profile_enable): records a HIP event pair around each launch.
+struct HilsProfScope {
+  HilsProfScope(const char* name, hipStream_t st);
+  ~HilsProfScope();
+  int slot;
+  hipStream_t st;
+};
+
 // summarize.hip
 hipError_t hils_launch_summarize(const HilsShape& s, const void* k, const void* lm, int c0, int c1,
                                  void* ksum, float* bsum, hipStream_t st);

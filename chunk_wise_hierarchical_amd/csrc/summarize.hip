@@ -72,12 +72,12 @@ hipError_t hils_launch_summarize(const HilsShape& s, const void* k, const void* 
   const size_t shm = sizeof(double) * (s.d + 64);
   const int lk = (s.mode == 1);
   if (s.dtype == 0)
-    hipLaunchKernelGGL(k_summarize<bf16_t>, dim3((unsigned)nblk), dim3(64), shm, st,
+    { HilsProfScope ps_("k_summarize", st); hipLaunchKernelGGL(k_summarize<bf16_t>, dim3((unsigned)nblk), dim3(64), shm, st,
                        (const bf16_t*)k, (const bf16_t*)lm, (bf16_t*)ksum, bsum, s.Hq, s.Hkv, s.N,
-                       s.d, s.S, s.nC, c0, ncs, (double)s.tau, lk);
+                       s.d, s.S, s.nC, c0, ncs, (double)s.tau, lk); }
   else
-    hipLaunchKernelGGL(k_summarize<float>, dim3((unsigned)nblk), dim3(64), shm, st,
+    { HilsProfScope ps_("k_summarize", st); hipLaunchKernelGGL(k_summarize<float>, dim3((unsigned)nblk), dim3(64), shm, st,
                        (const float*)k, (const float*)lm, (float*)ksum, bsum, s.Hq, s.Hkv, s.N,
-                       s.d, s.S, s.nC, c0, ncs, (double)s.tau, lk);
+                       s.d, s.S, s.nC, c0, ncs, (double)s.tau, lk); }
   return hipGetLastError();
 }

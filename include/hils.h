@@ -34,8 +34,9 @@
  *     workspace `ws` of at least hils_workspace_bytes() bytes (256-byte aligned).
  *   - All work is enqueued on `stream` (a hipStream_t; NULL = default stream).
  *     No entry point synchronises the host.  Outputs are valid once the stream
- *     reaches the enqueued work.  The library keeps no global mutable state:
- *     calls on different streams with different buffers are independent.
+ *     reaches the enqueued work.  The library keeps no global mutable state
+ *     (apart from the opt-in kernel-timing record below): calls on different
+ *     streams with different buffers are independent.
  *   - Errors: arguments are validated before anything is enqueued; on a
  *     non-OK return nothing has been enqueued (except HILS_E_HIP, which reports
  *     a launch failure), and outputs are undefined.  No C++ exception crosses
@@ -126,6 +127,18 @@ hils_status hils_decode(const hils_cfg* cfg, const void* q, const void* q_route,
 
 const char* hils_strerror(hils_status status);
 int hils_abi_version(void);
+
+/* Kernel timing for measurement tools (not part of the method).
+ * hils_profile_enable(1): from then on every kernel the library enqueues is
+ * bracketed by two HIP events recorded on its stream.  hils_profile_read()
+ * copies the names (static strings) and durations in milliseconds of the
+ * kernels enqueued since the previous read into names[]/ms[] (at most cap
+ * entries), returns how many kernels were recorded (which may exceed cap),
+ * and forgets them; the caller must have synchronised the streams first.
+ * While enabled the library keeps this process-wide record (guarded by a
+ * mutex); hils_profile_enable(0) turns it off and releases the events. */
+void hils_profile_enable(int on);
+int hils_profile_read(const char** names, float* ms, int cap);
 
 #ifdef __cplusplus
 }

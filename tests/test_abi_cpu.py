@@ -48,12 +48,15 @@ def _cfg(**kw):
 
 
 def test_workspace_bytes(L):
-    c = _cfg()
-    n = L.hils_workspace_bytes(ctypes.byref(c), 0)
-    # summaries + selection ids + fusion logits, each rounded up to 256 bytes
+    # generic kernels: summaries + selection ids + fusion logits (each 256-byte aligned)
+    n = L.hils_workspace_bytes(ctypes.byref(_cfg(flags=_lib.HILS_FLAG_GENERIC)), 0)
     want = (1 * 8 * 16 * 128 * 2) + (1 * 8 * 16 * 4) + (1 * 2 * 1024 * 8 * 4) + (1 * 8 * 1024 * 8 * 4)
     assert want <= n <= want + 4 * 256
-    assert L.hils_workspace_bytes(ctypes.byref(c), 1) > 0
+    # MFMA fast path (bf16, d=128, S=64): summaries + selection ids + per-chunk V^T
+    n = L.hils_workspace_bytes(ctypes.byref(_cfg()), 0)
+    want = (1 * 8 * 16 * 128 * 2) + (1 * 8 * 16 * 4) + (1 * 2 * 1024 * 8 * 4) + (1 * 2 * 16 * 128 * 64 * 2)
+    assert want <= n <= want + 4 * 256
+    assert L.hils_workspace_bytes(ctypes.byref(_cfg()), 1) > 0
     for bad in (dict(Hq=7), dict(d=0), dict(K=0), dict(dtype=5), dict(mode=9), dict(N=0)):
         assert L.hils_workspace_bytes(ctypes.byref(_cfg(**bad)), 0) == 0, bad
 
