@@ -27,7 +27,11 @@ using namespace fastp;
 namespace {
 
 constexpr int NT = 256;
-constexpr int KSTR = D + 8;   // K tile row stride (elements)
+constexpr int KSTR = D;       // K tile row stride (elements); 16-byte parts XOR-swizzled per row
+
+// physical 16-byte part of logical part p in K-tile row r: the rows read by one
+// 16-lane group (see the key order in qk) land in 16 distinct bank groups
+__device__ __forceinline__ int kswz(int r, int p) { return p ^ (((r >> 1) & 12) | (r & 3)); }
 constexpr int VSTR = S + 8;   // V^T tile row stride (elements)
 constexpr int MAXW = 512;     // bitmap words: chunk ids < 16384
 
@@ -43,7 +47,7 @@ struct ALds {
     ul = o;  o += (size_t)QA * K * 4;
     o = (o + 15) & ~(size_t)15;
     um = o;  o += (size_t)QA * K * 8;
-    lam = o; o += (size_t)64 * K * 4;
+    lam = o; o += (size_t)64 * (K + 1) * 4;   // rows padded to K+1 floats
     total = o;
   }
 };
@@ -163,6 +167,7 @@ k_attn_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
   // ---- fusion logits s_hat (base 2) of every (row, selected chunk) ----------
   for (int idx = tid; idx < 64 * K; idx += NT) {
     const int r = idx / K, kx = idx % K, qa = r / G, h = r % G;
+    const int li = r * (K + 1) + kx;
     const int c = (qa < qcount) ? sel_s[qa * K + kx] : -1;
     float val = -INFINITY;
     if (c >= 0) {
@@ -181,7 +186,7 @@ k_attn_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
       }
       val = fmaf(acc, tau2, bsum[(hb + h) * nC + c] * LOG2E);
     }
-    lam[idx] = val;
+    lam[li] = val;
   }
   __syncthreads();
 
@@ -199,19 +204,30 @@ k_attn_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
   }
   const long long wlo = vcol ? window_start(iq, W, S) : 0;
 
-  auto stage = [&](int c) {
+  // chunk staging through registers (two chunks in flight) into one LDS tile
+  auto load_chunk = [&](uint4* r, int c) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int piece = tid + NT * p, row = piece / 16, part = piece % 16;
       const long long t = (long long)c * S + row;
-      const uint4 val = (t < N) ? ld_u4(k + (kvbase * N + t) * D + part * 8) : make_uint4(0, 0, 0, 0);
-      st_u4(ktile + row * KSTR + part * 8, val);
+      r[p] = (t < N) ? ld_u4(k + (kvbase * N + t) * D + part * 8) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int piece = tid + NT * p, row = piece / 8, part = piece % 8;
-      st_u4(vtile + row * VSTR + part * 8,
-            ld_u4(vt + ((kvbase * nCc + c) * D + row) * (long long)S + part * 8));
+      r[4 + p] = ld_u4(vt + ((kvbase * nCc + c) * D + row) * (long long)S + part * 8);
+    }
+  };
+  auto store_chunk = [&](const uint4* r) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int piece = tid + NT * p, row = piece / 16, part = piece % 16;
+      st_u4(ktile + row * KSTR + kswz(row, part) * 8, r[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int piece = tid + NT * p, row = piece / 8, part = piece % 8;
+      st_u4(vtile + row * VSTR + part * 8, r[4 + p]);
     }
   };
   // S^T tile: s[kt][e] <-> key 32*(kt>>1) + 8*lq + 4*(kt&1) + e
@@ -223,7 +239,7 @@ k_attn_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
       f32x4_t a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        a4 = mfma16(ld_bf16x8(ktile + key * KSTR + 32 * ks + 8 * lq), bq[ks], a4);
+        a4 = mfma16(ld_bf16x8(ktile + key * KSTR + kswz(key, 4 * ks + lq) * 8), bq[ks], a4);
       s[kt] = a4;
     }
   };
@@ -249,13 +265,19 @@ k_attn_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
     }
   };
 
-  // ---- window: online softmax over the block's window tiles ----------------
+  // ---- one pipelined pass over the block's window tiles, then its union ------
   float m = -INFINITY, l = 0.0f;
+  float M2 = 0.0f, invZ = 0.0f;
   const int cw_lo = (int)(window_start(i0, W, S) / S);
   const int cw_hi = (i0 + qcount - 1) / S;
-  for (int c = cw_lo; c <= cw_hi; ++c) {
-    stage(c);
-    __syncthreads();
+  const int nw = cw_hi - cw_lo + 1;
+  const int total = nw + nunion;
+  unsigned long long wq = 0ull;   // queries with a row in this wavefront
+  for (int r = 16 * w; r < 16 * w + 16; ++r) wq |= 1ull << (r / G);
+  int kptr = 0;
+  auto chunk_of = [&](int idx) { return idx < nw ? cw_lo + idx : ulist[idx - nw]; };
+
+  auto window_tile = [&](int c) {
     f32x4_t s[4];
     qk(s);
     float x[16];
@@ -280,9 +302,9 @@ k_attn_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
 #pragma unroll
       for (int t = 0; t < 16; ++t) p[t] = 0.0f;
     } else {
-      scale = exp2f(m - mnew);       // 0 when m = -inf
+      scale = fast_exp2(m - mnew);       // 0 when m = -inf
 #pragma unroll
-      for (int t = 0; t < 16; ++t) { p[t] = exp2f(x[t] - mnew); ps += p[t]; }
+      for (int t = 0; t < 16; ++t) { p[t] = fast_exp2(x[t] - mnew); ps += p[t]; }
     }
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
@@ -290,75 +312,91 @@ k_attn_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
     m = mnew;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[dt] *= scale;
-    // reorder p to key order 32kb + 8lq + t: t<4 -> kt=2kb, t>=4 -> kt=2kb+1
     float pk[16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int t = 0; t < 8; ++t) pk[8 * kb + t] = p[(2 * kb + (t >> 2)) * 4 + (t & 3)];
     pv(pk);
-    __syncthreads();
-  }
+  };
 
-  // ---- chunk-level fusion weights -----------------------------------------
-  const float logz2 = m + log2f(l);
-  int kk = 0;
-  float M2 = logz2;
-  for (int kx = 0; kx < K; ++kx) {
-    const float lv = lam[colr * K + kx];
-    if (lv != -INFINITY) { M2 = fmaxf(M2, lv); ++kk; }
-  }
-  float Z = exp2f(logz2 - M2);
-  for (int kx = 0; kx < kk; ++kx) Z += exp2f(lam[colr * K + kx] - M2);
-  const float invZ = 1.0f / Z;
-  const float a_swa = vcol ? exp2f(logz2 - M2) * invZ / l : 0.0f;
+  // chunk-level fusion weights once the window is done: softmax over
+  // {s_hat_c : c selected} U {log Z_swa}
+  auto fusion_setup = [&]() {
+    const float logz2 = m + log2f(l);
+    int kk = 0;
+    M2 = logz2;
+    for (int kx = 0; kx < K; ++kx) {
+      const float lv = lam[colr * (K + 1) + kx];
+      if (lv != -INFINITY) { M2 = fmaxf(M2, lv); ++kk; }
+    }
+    float Z = fast_exp2(logz2 - M2);
+    for (int kx = 0; kx < kk; ++kx) Z += fast_exp2(lam[colr * (K + 1) + kx] - M2);
+    invZ = 1.0f / Z;
+    const float a_swa = vcol ? fast_exp2(logz2 - M2) * invZ / l : 0.0f;
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) acc[dt] *= a_swa;
+    for (int dt = 0; dt < 8; ++dt) acc[dt] *= a_swa;
+  };
 
-  // ---- union of selected chunks -------------------------------------------
-  unsigned long long wq = 0ull;   // queries with a row in this wavefront
-  for (int r = 16 * w; r < 16 * w + 16; ++r) wq |= 1ull << (r / G);
-  int kptr = 0;
-  for (int u = 0; u < nunion; ++u) {
-    const int c = ulist[u];
-    stage(c);
-    __syncthreads();
+  auto selected_chunk = [&](int u) {
     const unsigned long long mk = umask[u];
-    if (mk & wq) {
-      f32x4_t s[4];
-      qk(s);
-      const bool here = vcol && ((mk >> qa) & 1ull);
-      float x[16];
-      float mt = -INFINITY;
+    if (!(mk & wq)) return;
+    f32x4_t s[4];
+    qk(s);
+    const bool here = vcol && ((mk >> qa) & 1ull);
+    float x[16];
+    float mt = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v2 = here ? s[kt][e] * tau2 : -INFINITY;
-          x[kt * 4 + e] = v2;
-          mt = fmaxf(mt, v2);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      float p[16];
-      float ps = 0.0f;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) { p[t] = here ? exp2f(x[t] - mt) : 0.0f; ps += p[t]; }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
-      float coef = 0.0f;
-      if (here) {
-        coef = exp2f(lam[colr * K + kptr] - M2) * invZ / ps;
-        ++kptr;
+      for (int e = 0; e < 4; ++e) {
+        const float v2 = here ? s[kt][e] * tau2 : -INFINITY;
+        x[kt * 4 + e] = v2;
+        mt = fmaxf(mt, v2);
       }
-      float pk[16];
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    float p[16];
+    float ps = 0.0f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int t = 0; t < 16; ++t) { p[t] = here ? fast_exp2(x[t] - mt) : 0.0f; ps += p[t]; }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    float coef = 0.0f;
+    if (here) {
+      coef = fast_exp2(lam[colr * (K + 1) + kptr] - M2) * invZ / ps;
+      ++kptr;
+    }
+    float pk[16];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) pk[8 * kb + t] = p[(2 * kb + (t >> 2)) * 4 + (t & 3)] * coef;
-      pv(pk);
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) pk[8 * kb + t] = p[(2 * kb + (t >> 2)) * 4 + (t & 3)] * coef;
+    pv(pk);
+  };
+
+  // invariant at step idx: LDS holds chunk idx, `nxt` holds chunk idx+1 (loads
+  // in flight), `far` is free and receives chunk idx+2
+  uint4 ra[8], rb[8];
+  auto step = [&](int idx, uint4* nxt, uint4* far) {
+    if (idx + 2 < total) load_chunk(far, chunk_of(idx + 2));
+    if (idx < nw) {
+      window_tile(cw_lo + idx);
+      if (idx == nw - 1) fusion_setup();
+    } else {
+      selected_chunk(idx - nw);
     }
     __syncthreads();
+    if (idx + 1 < total) store_chunk(nxt);
+    __syncthreads();
+  };
+  load_chunk(ra, chunk_of(0));
+  if (total > 1) load_chunk(rb, chunk_of(1));
+  store_chunk(ra);
+  __syncthreads();
+  for (int idx = 0; idx < total; idx += 2) {
+    step(idx, rb, ra);
+    if (idx + 1 < total) step(idx + 1, ra, rb);
   }
 
   // ---- store ------------------------------------------------------------

@@ -6,15 +6,21 @@
 // of a group, one shared top-K).
 //
 // One workgroup (4 wavefronts) owns QB = 128/G query positions of one
-// (batch, KV group).  k' tiles of 32 chunks x G heads stream through LDS
-// (double-buffered); each wavefront computes a 32-chunk x 32-query score tile
-// of one head with v_mfma_f32_32x32x16_bf16 (A = k' rows, B = q_hat).  Scores
-// are kept in base-2 units (scaled by log2 e), which preserves their order.
-//   pass 0 (G > 1 only): per (query, head) online log-sum-exp over C_i;
-//   pass 1: group score g = max_h (s_h - L_h) (cross-head max through LDS),
-//           filtered against the query's current K-th best key and appended to
-//           an LDS staging list; a staging list past half full is merged into
-//           the query's sorted top-K list by a wavefront-wide bitonic sort.
+// (batch, KV group).  k' tiles of 32 chunks x G heads stream through LDS; each
+// wavefront computes a 32-chunk x 32-query score tile of one head with
+// v_mfma_f32_32x32x16_bf16 (A = k' rows, B = q_hat).  Scores are kept in
+// base-2 units (scaled by log2 e), which preserves their order.
+//   pass 0: per (query, head) online log-sum-exp over C_i (G > 1), and the two
+//           largest scores seen in each of the lane's 16 register slots.  The
+//           smallest of a (query, head)'s 64 tracked scores is a lower bound on
+//           its 64th (hence K-th) best score; T = max_h (bound_h - L_h) is then
+//           a lower bound on the K-th best group score, because the >= K
+//           chunks reaching bound_h all have a group score >= bound_h - L_h.
+//   pass 1: group score g = max_h (s_h - L_h) (cross-head max through LDS);
+//           chunks scoring above the query's current K-th best key (initially
+//           T) go to an LDS staging list, which is merged into the query's
+//           sorted top-K list (wavefront bitonic sort of the staged keys and
+//           one bitonic merge) once it holds more than 16 keys.
 // Keys are 64-bit: (order-preserving bits of g) << 32 | (~chunk id), so ties
 // rank the lower chunk id first and every key is unique.  The selected ids
 // are written ascending, -1 padded.
@@ -27,9 +33,9 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int CT = 32;         // chunks per tile
-constexpr int KROW = D + 8;    // padded k' row in LDS (elements)
-constexpr int XROW = CT + 4;   // padded row of the cross-head exchange buffer (floats)
-constexpr int STG = 64;        // staging slots per query
+constexpr int XROW = CT + 1;   // row of the cross-head exchange buffer (floats)
+constexpr int STG = 48;        // staging slots per query
+constexpr int STG_MERGE = 16;  // merge when more than this many keys are staged
 
 template <int G>
 struct Geo {
@@ -39,17 +45,21 @@ struct Geo {
   static constexpr int CL = CT / LQ;      // chunks per lane per tile (selection layout)
 };
 
+// ktile..stg is also the scratch of the tracked scores between the passes
+// (G*QB = 128 (query, head) pairs x 64 floats = 32 KB, which always fits).
 template <int G>
 struct Lds {
-  size_t ktile, btile, xb, lst, stg, cnt, thr, total;
+  size_t ktile, btile, xb, lst, stg, tq, tk, cnt, thr, total;
   __host__ __device__ Lds(int K) {
     size_t o = 0;
-    ktile = o; o += (size_t)2 * G * CT * KROW * 2;
-    btile = o; o += (size_t)2 * G * CT * 4;
+    ktile = o; o += (size_t)G * CT * D * 2;            // swizzled, no padding
+    btile = o; o += (size_t)G * CT * 4;
     xb = o;    o += (G > 1) ? (size_t)G * Geo<G>::QB * XROW * 4 : 0;
     o = (o + 15) & ~(size_t)15;
     lst = o;   o += (size_t)Geo<G>::QB * K * 8;
     stg = o;   o += (size_t)Geo<G>::QB * STG * 8;
+    tq = o;    o += (size_t)G * Geo<G>::QB * 4;
+    tk = o;    o += (size_t)G * Geo<G>::QB * 4;
     cnt = o;   o += (size_t)Geo<G>::QB * 2 * 4;
     o = (o + 15) & ~(size_t)15;
     thr = o;   o += (size_t)Geo<G>::QB * 8;
@@ -57,26 +67,51 @@ struct Lds {
   }
 };
 
-// wavefront-wide bitonic sort of 128 keys (2 per lane: index lane and lane+64), descending
-__device__ __forceinline__ void sort128_desc(uint64_t& e0, uint64_t& e1, int lane) {
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a > b ? b : a; }
+
+// wavefront-wide bitonic sort of 64 keys (1 per lane), descending
+__device__ __forceinline__ uint64_t sort64_desc(uint64_t v, int lane) {
 #pragma unroll
-  for (int size = 2; size <= 128; size <<= 1) {
+  for (int size = 2; size <= 64; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride == 64) {
-        const uint64_t mx = e0 > e1 ? e0 : e1, mn = e0 > e1 ? e1 : e0;
-        e0 = mx; e1 = mn;
-      } else {
-        const uint64_t p0 = shfl_xor_u64(e0, stride), p1 = shfl_xor_u64(e1, stride);
-        const bool lower = (lane & stride) == 0;
-        const bool desc0 = ((lane & size) == 0);
-        const bool desc1 = (((lane + 64) & size) == 0);
-        const bool km0 = (lower == desc0), km1 = (lower == desc1);
-        e0 = km0 ? (e0 > p0 ? e0 : p0) : (e0 < p0 ? e0 : p0);
-        e1 = km1 ? (e1 > p1 ? e1 : p1) : (e1 < p1 ? e1 : p1);
-      }
+      const uint64_t p = shfl_xor_u64(v, stride);
+      const bool lower = (lane & stride) == 0;
+      const bool desc = (lane & size) == 0 || size == 64;
+      v = (lower == desc) ? umax64(v, p) : umin64(v, p);
     }
   }
+  return v;
+}
+
+// a, b descending across the wavefront -> the 64 largest of a U b, descending
+__device__ __forceinline__ uint64_t merge_top64(uint64_t a, uint64_t b, int lane) {
+  const uint32_t lo = __shfl((uint32_t)b, 63 - lane, 64);
+  const uint32_t hi = __shfl((uint32_t)(b >> 32), 63 - lane, 64);
+  const uint64_t br = ((uint64_t)hi << 32) | lo;          // b reversed: ascending
+  uint64_t v = umax64(a, br);                              // top half of the bitonic sequence
+#pragma unroll
+  for (int stride = 32; stride > 0; stride >>= 1) {
+    const uint64_t p = shfl_xor_u64(v, stride);
+    v = ((lane & stride) == 0) ? umax64(v, p) : umin64(v, p);
+  }
+  return v;
+}
+
+// wavefront-wide bitonic sort of 64 floats (1 per lane), descending
+__device__ __forceinline__ float sort64_desc_f(float v, int lane) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const float p = __shfl_xor(v, stride, 64);
+      const bool lower = (lane & stride) == 0;
+      const bool desc = (lane & size) == 0 || size == 64;
+      v = (lower == desc) ? fmaxf(v, p) : fminf(v, p);
+    }
+  }
+  return v;
 }
 
 // wavefront-wide bitonic sort of 64 ints (1 per lane), ascending
@@ -95,7 +130,7 @@ __device__ __forceinline__ int sort64_asc(int v, int lane) {
 }
 
 template <int G>
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(NT, 2)
 k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
              const float* __restrict__ bsum, int32_t* __restrict__ sel, int Hq, int Hkv, int N,
              int W, int K, int nC, float tau2, int nqb) {
@@ -103,9 +138,12 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   constexpr int QB = GE::QB, QW = GE::QW, LQ = GE::LQ, CL = GE::CL;
   extern __shared__ __align__(16) unsigned char sm[];
   const Lds<G> L(K);
-  bf16_t* ktile = reinterpret_cast<bf16_t*>(sm + L.ktile);   // [2][G][CT][KROW]
-  float* btile = reinterpret_cast<float*>(sm + L.btile);     // [2][G][CT]  (b' * log2 e)
+  bf16_t* ktile = reinterpret_cast<bf16_t*>(sm + L.ktile);   // [G][CT][16 parts], part ^= c & 15
+  float* btile = reinterpret_cast<float*>(sm + L.btile);     // [G][CT]  (b' * log2 e)
   float* xb = reinterpret_cast<float*>(sm + L.xb);           // [G][QB][XROW]
+  float* tq = reinterpret_cast<float*>(sm + L.tq);           // [G][QB] log-sum-exp (base 2)
+  float* tk = reinterpret_cast<float*>(sm + L.tk);           // [G][QB] K-th tracked score
+  float* trk = reinterpret_cast<float*>(sm + L.ktile);       // [G*QB][64] between the passes
   uint64_t* lst = reinterpret_cast<uint64_t*>(sm + L.lst);   // [QB][K]
   uint64_t* stg = reinterpret_cast<uint64_t*>(sm + L.stg);   // [QB][STG]
   uint32_t* cnt_stg = reinterpret_cast<uint32_t*>(sm + L.cnt);
@@ -129,7 +167,7 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     for (int t = tid; t < (i_last - i0 + 1) * K; t += NT) selg[(long long)i0 * K + t] = -1;
     return;
   }
-  for (int t = tid; t < QB; t += NT) { cnt_stg[t] = 0; cnt_lst[t] = 0; thr[t] = 0; }
+  for (int t = tid; t < QB; t += NT) { cnt_stg[t] = 0; cnt_lst[t] = 0; }
 
   // MFMA layout: wavefront -> (head hw, 32-query column block qw); lane -> query column
   const int hw = w % G, qw = w / G;
@@ -147,7 +185,7 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   const int qsel = (G == 1) ? (32 * w + col) : (w * QW + lane / LQ);
   const int cbase = (G == 1) ? 0 : CL * (lane % LQ);
 
-  // tile staging through registers (double-buffered LDS)
+  // tile staging through registers into a single XOR-swizzled LDS tile
   constexpr int PPT = 2 * G;               // 16-byte pieces per thread per tile
   uint4 pre[PPT];
   float bpre = 0.0f;
@@ -165,48 +203,52 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
       bpre = (cg < nC) ? bsum[(hb + h) * nC + cg] * LOG2E : 0.0f;
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&]() {
 #pragma unroll
     for (int p = 0; p < PPT; ++p) {
       const int piece = tid + NT * p;
       const int h = piece / (CT * 16), c = (piece / 16) % CT, part = piece % 16;
-      st_u4(ktile + (((size_t)buf * G + h) * CT + c) * KROW + part * 8, pre[p]);
+      st_u4(ktile + ((size_t)h * CT + c) * D + ((part ^ (c & 15)) * 8), pre[p]);
     }
-    if (tid < G * CT) btile[buf * G * CT + tid] = bpre;
+    if (tid < G * CT) btile[tid] = bpre;
   };
 
   // merge query q's staging list into its sorted top-K list (whole wavefront)
   auto merge = [&](int q) {
     const int ns = (int)cnt_stg[q], nl = (int)cnt_lst[q];
-    uint64_t e0 = (lane < nl) ? lst[(size_t)q * K + lane] : 0ull;
-    uint64_t e1 = (lane < ns) ? stg[(size_t)q * STG + lane] : 0ull;
-    sort128_desc(e0, e1, lane);
+    const uint64_t a = (lane < nl) ? lst[(size_t)q * K + lane] : 0ull;
+    uint64_t sb = (lane < ns) ? stg[(size_t)q * STG + lane] : 0ull;
+    sb = sort64_desc(sb, lane);
+    const uint64_t v = merge_top64(a, sb, lane);
     const int tot = min(K, nl + ns);
-    const uint32_t klo = __shfl((uint32_t)e0, K - 1, 64);
-    const uint32_t khi = __shfl((uint32_t)(e0 >> 32), K - 1, 64);
-    if (lane < K) lst[(size_t)q * K + lane] = (lane < tot) ? e0 : 0ull;
+    const uint32_t klo = __shfl((uint32_t)v, K - 1, 64);
+    const uint32_t khi = __shfl((uint32_t)(v >> 32), K - 1, 64);
+    if (lane < K) lst[(size_t)q * K + lane] = (lane < tot) ? v : 0ull;
     if (lane == 0) {
       cnt_lst[q] = tot;
       cnt_stg[q] = 0;
-      thr[q] = (tot >= K) ? (((uint64_t)khi << 32) | klo) : 0ull;
+      if (tot >= K) thr[q] = umax64(thr[q], ((uint64_t)khi << 32) | klo);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   };
 
   float L2 = 0.0f;
-  for (int pass = (G > 1 ? 0 : 1); pass < 2; ++pass) {
+  for (int pass = 0; pass < 2; ++pass) {
     float m = -INFINITY, ssum = 0.0f;
+    float ta[16], tb[16];                  // top-2 per register slot (pass 0)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { ta[i] = -INFINITY; tb[i] = -INFINITY; }
     load_tile(0);
-    store_tile(0);
+    store_tile();
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
-      const int buf = t & 1;
       if (t + 1 < ntiles) load_tile(t + 1);
       f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      const bf16_t* kb = ktile + (((size_t)buf * G + hw) * CT + col) * KROW + 8 * half;
+      const bf16_t* kb = ktile + ((size_t)hw * CT + col) * D;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) acc = mfma32(ld_bf16x8(kb + 16 * ks), bq[ks], acc);
-      const float* bt = btile + ((size_t)buf * G + hw) * CT;
+      for (int ks = 0; ks < 8; ++ks)
+        acc = mfma32(ld_bf16x8(kb + (((2 * ks + half) ^ (col & 15)) * 8)), bq[ks], acc);
+      const float* bt = btile + (size_t)hw * CT;
       float x[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -214,37 +256,37 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
         x[i] = (CT * t + cl < nq) ? fmaf(acc[i], tau2, bt[cl]) : -INFINITY;
       }
       if (pass == 0) {
-        float mt = x[0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mt = fmaxf(mt, x[i]);
-        if (mt > m) { ssum = (m == -INFINITY) ? 0.0f : ssum * exp2f(m - mt); m = mt; }
-        if (m != -INFINITY) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) ssum += exp2f(x[i] - m);
+        for (int i = 0; i < 16; ++i) {
+          tb[i] = fmaxf(tb[i], fminf(ta[i], x[i]));
+          ta[i] = fmaxf(ta[i], x[i]);
         }
+        if (G > 1) {
+          float mt = x[0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) mt = fmaxf(mt, x[i]);
+          if (mt > m) { ssum = (m == -INFINITY) ? 0.0f : ssum * fast_exp2(m - mt); m = mt; }
+          if (m != -INFINITY) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ssum += fast_exp2(x[i] - m);
+          }
+        }
+        __syncthreads();
       } else {
         float gs[CL];
         int cid0;
         if (G > 1) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) x[i] = (x[i] == -INFINITY) ? -INFINITY : x[i] - L2;
           float* xr = xb + ((size_t)hw * QB + 32 * qw + col) * XROW;
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            float4 v4 = make_float4(x[4 * gq], x[4 * gq + 1], x[4 * gq + 2], x[4 * gq + 3]);
-            *reinterpret_cast<float4*>(xr + 8 * gq + 4 * half) = v4;
-          }
+          for (int i = 0; i < 16; ++i)
+            xr[8 * (i >> 2) + 4 * half + (i & 3)] = (x[i] == -INFINITY) ? -INFINITY : x[i] - L2;
           __syncthreads();
 #pragma unroll
-          for (int j = 0; j < CL; j += 4) {
-            float4 mx = *reinterpret_cast<const float4*>(xb + ((size_t)0 * QB + qsel) * XROW + cbase + j);
+          for (int j = 0; j < CL; ++j) {
+            float mx = xb[((size_t)0 * QB + qsel) * XROW + cbase + j];
 #pragma unroll
-            for (int h = 1; h < G; ++h) {
-              const float4 v = *reinterpret_cast<const float4*>(xb + ((size_t)h * QB + qsel) * XROW + cbase + j);
-              mx.x = fmaxf(mx.x, v.x); mx.y = fmaxf(mx.y, v.y);
-              mx.z = fmaxf(mx.z, v.z); mx.w = fmaxf(mx.w, v.w);
-            }
-            gs[j] = mx.x; gs[j + 1] = mx.y; gs[j + 2] = mx.z; gs[j + 3] = mx.w;
+            for (int h = 1; h < G; ++h) mx = fmaxf(mx, xb[((size_t)h * QB + qsel) * XROW + cbase + j]);
+            gs[j] = mx;
           }
           cid0 = CT * t + cbase;
         } else {
@@ -267,22 +309,55 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
           }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        for (int qq = 0; qq < QW; ++qq) {
-          const int q = w * QW + qq;
-          if (cnt_stg[q] > (uint32_t)(STG / 2)) merge(q);
+        {
+          const bool leader = (G == 1) ? (half == 0) : (lane % LQ == 0);
+          unsigned long long need = __ballot(leader && cnt_stg[qsel] > (uint32_t)STG_MERGE);
+          while (need) {
+            const int l = __ffsll((long long)need) - 1;
+            need &= need - 1;
+            merge((G == 1) ? (32 * w + l) : (w * QW + l / LQ));
+          }
         }
+        __syncthreads();
       }
-      if (t + 1 < ntiles) store_tile(buf ^ 1);
+      if (t + 1 < ntiles) store_tile();
       __syncthreads();
     }
     if (pass == 0) {
-      const float m2 = __shfl_xor(m, 32, 64), s2 = __shfl_xor(ssum, 32, 64);
-      const float M = fmaxf(m, m2);
-      float s = 0.0f;
-      if (M != -INFINITY) {
-        s = (m == -INFINITY ? 0.0f : ssum * exp2f(m - M)) + (m2 == -INFINITY ? 0.0f : s2 * exp2f(m2 - M));
+      // per (query, head): log-sum-exp, and the K-th largest of the 64 tracked
+      // scores (a lower bound on the head's K-th best score)
+      const int pr = hw * QB + 32 * qw + col;        // (head, query) pair of this lane
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        trk[(size_t)pr * 64 + half * 32 + i] = ta[i];
+        trk[(size_t)pr * 64 + half * 32 + 16 + i] = tb[i];
       }
-      L2 = M + log2f(s);
+      if (G > 1) {
+        const float m2 = __shfl_xor(m, 32, 64), s2 = __shfl_xor(ssum, 32, 64);
+        const float M = fmaxf(m, m2);
+        float s = 0.0f;
+        if (M != -INFINITY)
+          s = (m == -INFINITY ? 0.0f : ssum * fast_exp2(m - M)) + (m2 == -INFINITY ? 0.0f : s2 * fast_exp2(m2 - M));
+        L2 = M + log2f(s);
+      }
+      if (half == 0) tq[pr] = L2;
+      __syncthreads();
+      for (int j = 0; j < (G * QB) / 4; ++j) {
+        const int p = w * ((G * QB) / 4) + j;
+        const float v = sort64_desc_f(trk[(size_t)p * 64 + lane], lane);
+        const float kth = __shfl(v, K - 1, 64);
+        if (lane == 0) tk[p] = kth;
+      }
+      __syncthreads();
+      for (int t = tid; t < QB; t += NT) {
+        float T = -INFINITY;
+        for (int h = 0; h < G; ++h) {
+          const float kh = tk[(size_t)h * QB + t];
+          if (kh != -INFINITY) T = fmaxf(T, (G > 1) ? kh - tq[(size_t)h * QB + t] : kh);
+        }
+        thr[t] = (T == -INFINITY) ? 0ull : ((uint64_t)f32_order_key(T) << 32);
+      }
+      __syncthreads();
     }
   }
 
