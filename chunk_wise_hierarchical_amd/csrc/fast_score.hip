@@ -195,12 +195,13 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
       const int piece = tid + NT * p;
       const int h = piece / (CT * 16), c = (piece / 16) % CT, part = piece % 16;
       const int cg = CT * t + c;
-      pre[p] = (cg < nC) ? ld_u4(ksum + ((hb + h) * nC + cg) * (long long)D + part * 8)
-                         : make_uint4(0, 0, 0, 0);
+      const uint4 v = ld_u4(ksum + ((hb + h) * nC + min(cg, nC - 1)) * (long long)D + part * 8);
+      pre[p] = (cg < nC) ? v : make_uint4(0, 0, 0, 0);
     }
     if (tid < G * CT) {
       const int h = tid / CT, cg = CT * t + tid % CT;
-      bpre = (cg < nC) ? bsum[(hb + h) * nC + cg] * LOG2E : 0.0f;
+      const float bv = bsum[(hb + h) * nC + min(cg, nC - 1)];
+      bpre = (cg < nC) ? bv * LOG2E : 0.0f;
     }
   };
   auto store_tile = [&]() {
@@ -232,6 +233,34 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   };
 
+  // scores of tile t for this lane (base 2): x[i] <-> chunk 32t + 8(i>>2) + 4*half + (i&3)
+  const int n_lo = n_cand(i0, W, S);                 // every query of the block has >= n_lo
+  auto tile_scores = [&](int t, float* x) {
+    const bf16_t* kb = ktile + ((size_t)hw * CT + col) * D;
+    bf16x8_t a[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) a[ks] = ld_bf16x8(kb + (((2 * ks + half) ^ (col & 15)) * 8));
+    f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) acc = mfma32(a[ks], bq[ks], acc);
+    const float* bt = btile + (size_t)hw * CT;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const float4 b4 = *reinterpret_cast<const float4*>(bt + 8 * gq + 4 * half);
+      x[4 * gq + 0] = fmaf(acc[4 * gq + 0], tau2, b4.x);
+      x[4 * gq + 1] = fmaf(acc[4 * gq + 1], tau2, b4.y);
+      x[4 * gq + 2] = fmaf(acc[4 * gq + 2], tau2, b4.z);
+      x[4 * gq + 3] = fmaf(acc[4 * gq + 3], tau2, b4.w);
+    }
+    if (CT * t + CT > n_lo) {                        // tile crosses some query's candidate range
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int cl = 8 * (i >> 2) + 4 * half + (i & 3);
+        x[i] = (CT * t + cl < nq) ? x[i] : -INFINITY;
+      }
+    }
+  };
+
   float L2 = 0.0f;
   for (int pass = 0; pass < 2; ++pass) {
     float m = -INFINITY, ssum = 0.0f;
@@ -243,18 +272,8 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
       if (t + 1 < ntiles) load_tile(t + 1);
-      f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      const bf16_t* kb = ktile + ((size_t)hw * CT + col) * D;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        acc = mfma32(ld_bf16x8(kb + (((2 * ks + half) ^ (col & 15)) * 8)), bq[ks], acc);
-      const float* bt = btile + (size_t)hw * CT;
       float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int cl = 8 * (i >> 2) + 4 * half + (i & 3);
-        x[i] = (CT * t + cl < nq) ? fmaf(acc[i], tau2, bt[cl]) : -INFINITY;
-      }
+      tile_scores(t, x);
       if (pass == 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -299,13 +318,11 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
 #pragma unroll
         for (int j = 0; j < CL; ++j) {
           const int cid = (G == 1) ? (cid0 + 8 * (j >> 2) + 4 * half + (j & 3)) : (cid0 + j);
-          if (gs[j] != -INFINITY) {
-            const uint64_t key = ((uint64_t)f32_order_key(gs[j]) << 32) |
-                                 (uint64_t)(0xffffffffu - (uint32_t)cid);
-            if (key > th) {
-              const uint32_t slot = atomicAdd(&cnt_stg[qsel], 1u);
-              stg[(size_t)qsel * STG + slot] = key;
-            }
+          const uint64_t key = ((uint64_t)f32_order_key(gs[j]) << 32) |
+                               (uint64_t)(0xffffffffu - (uint32_t)cid);
+          if (gs[j] != -INFINITY && key > th) {
+            const uint32_t slot = atomicAdd(&cnt_stg[qsel], 1u);
+            stg[(size_t)qsel * STG + slot] = key;
           }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
