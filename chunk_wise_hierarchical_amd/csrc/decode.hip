@@ -36,51 +36,86 @@ template <> struct Vec<float> {
   }
 };
 
-constexpr int SC_CPB = 256;   // chunks per scoring workgroup
+constexpr int SC_CPB = HILS_DEC_SCORE_ROWS;   // chunks per scoring workgroup: 16 groups x 16 rows
 
-// one 16-lane group per chunk row; d % Vec::N == 0 (checked on the host)
+// Scores of 256 consecutive chunk rows of one (sequence, query head): a
+// 16-lane group owns 16 consecutive rows and reads each row with 16-byte loads
+// (all 16 rows in flight), the 16 row sums are reduce-scattered across the
+// group so lane u ends with row u, and the workgroup also emits the
+// (max, sum exp) partial of its scores for the per-head log-sum-exp.
+// Requires d % Vec::N == 0 (checked on the host).
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_dec_score(const T* __restrict__ qr, const T* __restrict__ ksum, const float* __restrict__ bsum,
-            const int32_t* __restrict__ seqlen, float* __restrict__ scores, int Hq, int nC, int nmax,
-            int N, int d, int S, int W, float tau) {
+            const int32_t* __restrict__ seqlen, float* __restrict__ scores, float* __restrict__ lsep,
+            int Hq, int nC, int nmax, int nsb, int N, int d, int S, int W, float tau) {
   constexpr int V = Vec<T>::N;
   constexpr int MAXT = 256 / (16 * V) > 0 ? 256 / (16 * V) : 1;
+  constexpr int R = 16;
+  __shared__ float red_m[4], red_s[4];
   const long long bh = blockIdx.x;
   const int b = (int)(bh / Hq);
   const int n = n_cand(clamp_len(seqlen[b], N) - 1, W, S);
   const int c0 = blockIdx.y * SC_CPB;
-  if (c0 >= n) return;
-  const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
-  float qv[MAXT][V];
+  const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15, lane = tid & 63, wv = tid >> 6;
+  float* lp = lsep + (bh * nsb + blockIdx.y) * 2;
+  if (c0 >= n) {
+    if (tid == 0) { lp[0] = -INFINITY; lp[1] = 0.0f; }
+    return;
+  }
+  const int r0 = c0 + grp * R;
+  float acc[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) acc[u] = 0.0f;
 #pragma unroll
   for (int t = 0; t < MAXT; ++t) {
     const int e = (t * 16 + l16) * V;
-    if (e < d) Vec<T>::load(qr + bh * d + e, qv[t]);
-    else {
+    if (e < d) {
+      float qv[V];
+      Vec<T>::load(qr + bh * d + e, qv);
+      uint4 raw[R];
 #pragma unroll
-      for (int u = 0; u < V; ++u) qv[t][u] = 0.0f;
-    }
-  }
-  const int c1 = min(n, c0 + SC_CPB);
-  for (int c = c0 + grp; c < c1; c += 16) {
-    const T* kp = ksum + (bh * nC + c) * (long long)d;
-    float acc = 0.0f;
+      for (int u = 0; u < R; ++u) {
+        const int c = min(r0 + u, n - 1);
+        raw[u] = *reinterpret_cast<const uint4*>(ksum + (bh * nC + c) * (long long)d + e);
+      }
 #pragma unroll
-    for (int t = 0; t < MAXT; ++t) {
-      const int e = (t * 16 + l16) * V;
-      if (e < d) {
+      for (int u = 0; u < R; ++u) {
         float kv[V];
-        Vec<T>::load(kp + e, kv);
+        Vec<T>::load(reinterpret_cast<const T*>(&raw[u]), kv);
 #pragma unroll
-        for (int u = 0; u < V; ++u) acc = fmaf(qv[t][u], kv[u], acc);
+        for (int x = 0; x < V; ++x) acc[u] = fmaf(qv[x], kv[x], acc[u]);
       }
     }
-    acc += __shfl_xor(acc, 8, 64);
-    acc += __shfl_xor(acc, 4, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    acc += __shfl_xor(acc, 1, 64);
-    if (l16 == 0) scores[bh * nmax + c] = fmaf(tau, acc, bsum[bh * nC + c]);
+  }
+  // reduce-scatter over the 16 lanes: after the step with mask m a lane keeps
+  // the half of its rows whose index bit m matches its own lane bit m
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) {
+    const bool hi = (l16 & m) != 0;
+#pragma unroll
+    for (int u = 0; u < m; ++u) {
+      const float keep = hi ? acc[u + m] : acc[u];
+      const float send = hi ? acc[u] : acc[u + m];
+      acc[u] = keep + __shfl_xor(send, m, 64);
+    }
+  }
+  const int c = r0 + l16;
+  const bool ok = c < n;
+  const float x = ok ? fmaf(tau, acc[0], bsum[bh * nC + c]) : -INFINITY;
+  if (ok) scores[bh * nmax + c] = x;
+  const float m = wave_max_f(x);
+  const float ex = ok ? __expf(x - m) : 0.0f;
+  const float sw = wave_sum_f(ex);
+  if (lane == 0) { red_m[wv] = m; red_s[wv] = sw; }
+  __syncthreads();
+  if (tid == 0) {
+    float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+    float L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) L += (red_s[w] > 0.0f) ? red_s[w] * __expf(red_m[w] - M) : 0.0f;
+    lp[0] = M;
+    lp[1] = L;
   }
 }
 
@@ -110,12 +145,15 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = M;
 }
 
+constexpr int SEL_LDS_KEYS = 24576;   // keys kept in LDS (96 KB) when the candidate set fits
+
 __global__ void __launch_bounds__(SEL_NT)
-k_dec_select(const float* __restrict__ scores, const int32_t* __restrict__ seqlen,
-             uint32_t* __restrict__ keys, int32_t* __restrict__ sel, float* __restrict__ slog,
-             int Hq, int Hkv, int G, int nmax, int N, int S, int W, int K) {
+k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
+             const int32_t* __restrict__ seqlen, uint32_t* __restrict__ keys,
+             int32_t* __restrict__ sel, float* __restrict__ slog, int Hq, int Hkv, int G, int nmax,
+             int nsb, int N, int S, int W, int K) {
+  extern __shared__ uint32_t sel_keys_lds[];
   __shared__ uint32_t hist[256];
-  __shared__ float red_m[SEL_NW][8], red_s[SEL_NW][8];
   __shared__ float Lh[8];
   __shared__ int wsum[SEL_NW];
   __shared__ int sh_digit, sh_need;
@@ -133,40 +171,45 @@ k_dec_select(const float* __restrict__ scores, const int32_t* __restrict__ seqle
     if (kx >= kk) slog[(hbase + r) * K + kx] = 0.0f;
   }
   if (n == 0) return;
-  uint32_t* ky = keys + (long long)bg * nmax;
+  uint32_t* ky = (n <= SEL_LDS_KEYS) ? sel_keys_lds : keys + (long long)bg * nmax;
 
   if (G > 1) {
-    for (int r = 0; r < G; ++r) {
-      const float* sr = scores + (hbase + r) * nmax;
+    // per-head log-sum-exp from the scoring workgroups' (max, sum exp) partials
+    for (int r = wv; r < G; r += SEL_NW) {
+      const float* lp = lsep + (hbase + r) * nsb * 2;
       float m = -INFINITY, s = 0.0f;
-      for (int c = tid; c < n; c += SEL_NT) {
-        const float x = sr[c];
-        if (x > m) { s = s * __expf(m - x) + 1.0f; m = x; } else { s += __expf(x - m); }
-      }
+      for (int t = lane; t < nsb; t += 64) lse_merge(m, s, lp[2 * t], lp[2 * t + 1]);
 #pragma unroll
       for (int msk = 32; msk >= 1; msk >>= 1) {
         const float m2 = __shfl_xor(m, msk, 64), s2 = __shfl_xor(s, msk, 64);
         lse_merge(m, s, m2, s2);
       }
-      if (lane == 0) { red_m[wv][r] = m; red_s[wv][r] = s; }
-    }
-    __syncthreads();
-    if (tid < G) {
-      float m = red_m[0][tid], s = red_s[0][tid];
-      for (int u = 1; u < SEL_NW; ++u) lse_merge(m, s, red_m[u][tid], red_s[u][tid]);
-      Lh[tid] = m + __logf(s);
+      if (lane == 0) Lh[r] = m + __logf(s);
     }
     __syncthreads();
   }
-  for (int c = tid; c < n; c += SEL_NT) {
-    float gs;
-    if (G == 1) {
-      gs = scores[hbase * nmax + c];
-    } else {
-      gs = -INFINITY;
-      for (int r = 0; r < G; ++r) gs = fmaxf(gs, scores[(hbase + r) * nmax + c] - Lh[r]);
+  constexpr int KU = 4;
+  for (int base = 0; base < n; base += KU * SEL_NT) {
+    float gs[KU];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) gs[u] = -INFINITY;
+    for (int r = 0; r < G; ++r) {
+      const float* sr = scores + (hbase + r) * nmax;
+      const float lr = (G == 1) ? 0.0f : Lh[r];
+      float x[KU];
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const int c = base + u * SEL_NT + tid;
+        x[u] = (c < n) ? sr[c] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < KU; ++u) gs[u] = fmaxf(gs[u], x[u] - lr);
     }
-    ky[c] = f32_order_key(gs);
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int c = base + u * SEL_NT + tid;
+      if (c < n) ky[c] = f32_order_key(gs[u]);
+    }
   }
   if (tid == 0) sh_need = kk;
   __syncthreads();
@@ -232,13 +275,25 @@ k_dec_select(const float* __restrict__ scores, const int32_t* __restrict__ seqle
 
 constexpr int AT_NT = 256;
 
+// One workgroup per (sequence, KV group, split): a split is one selected chunk
+// or one S-token window tile (S <= 64, G <= 8, checked on the host).  The K and
+// V rows of the split are staged in LDS with 16-byte loads; thread (head, key)
+// forms a logit, wave h takes head h's softmax over the split (lane = key),
+// thread (head, element) forms the unnormalised output from the LDS V tile.
 template <typename T>
 __global__ void __launch_bounds__(AT_NT)
 k_dec_attn(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
            const int32_t* __restrict__ seqlen, const int32_t* __restrict__ sel, float* __restrict__ part,
            int Hq, int Hkv, int G, int N, int d, int S, int W, int K, int NS, float tau) {
+  constexpr int V = Vec<T>::N;
   extern __shared__ __align__(16) unsigned char sm_raw[];
-  float* qs = reinterpret_cast<float*>(sm_raw);   // [G][d]
+  const int kstr = d + V;                                     // padded row (elements), 16-byte multiple
+  T* ks = reinterpret_cast<T*>(sm_raw);                       // [S][kstr]
+  T* vs = ks + S * kstr;                                      // [S][kstr]
+  float* qs = reinterpret_cast<float*>(vs + S * kstr);        // [G][d]
+  const int SP = (S + 3) & ~3;                                // padded softmax row
+  float* ps = qs + G * d;                                     // [G][SP], zero past the split
+  __shared__ float hm[8], hl[8];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bg = blockIdx.x, s = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
@@ -255,99 +310,131 @@ k_dec_attn(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
     j0 = w0 + (long long)(s - K) * S;
     if (j0 <= i) jn = (int)min((long long)S, i - j0 + 1);
   }
-  if (jn == 0) {
-    for (int t = tid; t < G; t += AT_NT) {
-      float* pp = part + ((hbase + t) * NS + s) * (long long)(d + 2);
-      pp[0] = -INFINITY;
-      pp[1] = 0.0f;
+  if (jn == 0) {               // empty split: weight 0 in the combine, zero partial
+    for (int t = tid; t < G * (d + 2); t += AT_NT) {
+      const int r = t / (d + 2), e = t - r * (d + 2);
+      part[((hbase + r) * NS + s) * (long long)(d + 2) + e] = (e == 0) ? -INFINITY : 0.0f;
     }
     return;
   }
-  for (int t = tid; t < G * d; t += AT_NT) qs[t] = Elt<T>::ld(q + (hbase + t / d) * d + t % d);
+  const T* kg = k + ((b * (long long)Hkv + g) * N + j0) * d;
+  const T* vg = v + ((b * (long long)Hkv + g) * N + j0) * d;
+  const int vpr = d / V;                                      // 16-byte vectors per row
+  for (int t = tid; t < jn * vpr; t += AT_NT) {
+    const int j = t / vpr, e = (t - j * vpr) * V;
+    const uint4 kx = *reinterpret_cast<const uint4*>(kg + (long long)j * d + e);
+    const uint4 vx = *reinterpret_cast<const uint4*>(vg + (long long)j * d + e);
+    *reinterpret_cast<uint4*>(ks + j * kstr + e) = kx;
+    *reinterpret_cast<uint4*>(vs + j * kstr + e) = vx;
+  }
+  for (int t = tid; t < G * d; t += AT_NT) qs[t] = Elt<T>::ld(q + hbase * d + t);
   __syncthreads();
-  const T* kg = k + (b * (long long)Hkv + g) * N * d;
-  const T* vg = v + (b * (long long)Hkv + g) * N * d;
-  for (int r = wv; r < G; r += AT_NT / 64) {
+  for (int t = tid; t < G * SP; t += AT_NT) {
+    const int r = t / SP, j = t - r * SP;
     float x = -INFINITY;
-    if (lane < jn) {
-      const T* kr = kg + (j0 + lane) * d;
+    if (j < jn) {
       const float* qq = qs + r * d;
+      const T* kr = ks + j * kstr;
       float acc = 0.0f;
-      for (int e = 0; e < d; ++e) acc = fmaf(qq[e], Elt<T>::ld(kr + e), acc);
+      for (int e = 0; e < d; e += V) {
+        float kv[V];
+        Vec<T>::load(kr + e, kv);
+#pragma unroll
+        for (int u = 0; u < V; u += 4) {
+          const float4 qv = *reinterpret_cast<const float4*>(qq + e + u);
+          acc = fmaf(qv.x, kv[u], acc);
+          acc = fmaf(qv.y, kv[u + 1], acc);
+          acc = fmaf(qv.z, kv[u + 2], acc);
+          acc = fmaf(qv.w, kv[u + 3], acc);
+        }
+      }
       x = tau * acc;
     }
+    ps[t] = x;
+  }
+  __syncthreads();
+  for (int r = wv; r < G; r += AT_NT / 64) {
+    const float x = (lane < SP) ? ps[r * SP + lane] : -INFINITY;
     const float m = wave_max_f(x);
     const float p = (lane < jn) ? __expf(x - m) : 0.0f;
     const float l = wave_sum_f(p);
-    float* pp = part + ((hbase + r) * NS + s) * (long long)(d + 2);
-    for (int e0 = 0; e0 < d; e0 += 64) {      // uniform trip count across lanes
-      const int e = e0 + lane;
-      float acc = 0.0f;
-      for (int j = 0; j < jn; ++j) {
-        const float pj = __shfl(p, j, 64);   // every lane runs the same j loop
-        if (e < d) acc = fmaf(pj, Elt<T>::ld(vg + (j0 + j) * d + e), acc);
+    if (lane < SP) ps[r * SP + lane] = p;
+    if (lane == 0) { hm[r] = m; hl[r] = l; }
+  }
+  __syncthreads();
+  const int dh = d / 2;                                       // element pairs per row
+  for (int t = tid; t < G * dh; t += AT_NT) {
+    const int r = t / dh, e = 2 * (t - r * dh);
+    const float* pr = ps + r * SP;
+    float a0 = 0.0f, a1 = 0.0f;
+    for (int j = 0; j < jn; j += 4) {                         // ps is zero past jn
+      const float4 p4 = *reinterpret_cast<const float4*>(pr + j);
+      const float pj[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (j + u < jn) {
+          a0 = fmaf(pj[u], Elt<T>::ld(vs + (j + u) * kstr + e), a0);
+          a1 = fmaf(pj[u], Elt<T>::ld(vs + (j + u) * kstr + e + 1), a1);
+        }
       }
-      if (e < d) pp[2 + e] = acc;
     }
-    if (lane == 0) { pp[0] = m; pp[1] = l; }
+    float* pp = part + ((hbase + r) * NS + s) * (long long)(d + 2);
+    pp[2 + e] = a0;
+    pp[3 + e] = a1;
+    if (e == 0) { pp[0] = hm[r]; pp[1] = hl[r]; }
   }
 }
 
+// Per (sequence, query head): merge the window tiles in the log domain, take
+// the chunk-level softmax over {s_hat_c} U {log Z_swa}, and form the output as
+// one weighted sum of the split partials.  Wave 0 computes the split weights.
 template <typename T>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(256)
 k_dec_combine(const float* __restrict__ part, const float* __restrict__ slog,
               const int32_t* __restrict__ seqlen, T* __restrict__ out, int Hq, int G, int N, int d,
               int S, int W, int K, int NS, int nwin) {
-  const int bh = blockIdx.x, lane = threadIdx.x;
+  extern __shared__ float wsplit[];          // [NS] weight of each split's unnormalised o
+  const int bh = blockIdx.x, tid = threadIdx.x;
   const int b = bh / Hq;
   const long long i = clamp_len(seqlen[b], N) - 1;
   const int n = n_cand(i, W, S);
   const int kk = min(K, n);
   const float* pb = part + (long long)bh * NS * (d + 2);
-  // window: log-domain merge of the tile partials
-  float M = -INFINITY;
-  for (int t = 0; t < nwin; ++t) {
-    const float* pp = pb + (long long)(K + t) * (d + 2);
-    if (pp[1] > 0.0f) M = fmaxf(M, pp[0]);
-  }
-  float L = 0.0f;
-  constexpr int MAXE = 4;   // d <= 256
-  float ow[MAXE], acc[MAXE];
-#pragma unroll
-  for (int u = 0; u < MAXE; ++u) { ow[u] = 0.0f; acc[u] = 0.0f; }
-  for (int t = 0; t < nwin; ++t) {
-    const float* pp = pb + (long long)(K + t) * (d + 2);
-    if (!(pp[1] > 0.0f)) continue;
-    const float sc = __expf(pp[0] - M);
-    L += pp[1] * sc;
-#pragma unroll
-    for (int u = 0; u < MAXE; ++u) {
-      const int e = lane + 64 * u;
-      if (e < d) ow[u] = fmaf(pp[2 + e], sc, ow[u]);
-    }
-  }
-  const float logz = M + __logf(L);
   const float* sl = slog + (long long)bh * K;
-  float Mx = logz;
-  for (int kx = 0; kx < kk; ++kx) Mx = fmaxf(Mx, sl[kx]);
-  float Z = __expf(logz - Mx);
-  for (int kx = 0; kx < kk; ++kx) Z += __expf(sl[kx] - Mx);
-  const float aw = __expf(logz - Mx) / Z / L;
-#pragma unroll
-  for (int u = 0; u < MAXE; ++u) acc[u] = ow[u] * aw;
-  for (int kx = 0; kx < kk; ++kx) {
-    const float* pp = pb + (long long)kx * (d + 2);
-    const float a = __expf(sl[kx] - Mx) / Z / pp[1];
-#pragma unroll
-    for (int u = 0; u < MAXE; ++u) {
-      const int e = lane + 64 * u;
-      if (e < d) acc[u] = fmaf(a, pp[2 + e], acc[u]);
+  if (tid < 64) {
+    float M = -INFINITY;
+    for (int t = tid; t < nwin; t += 64) {
+      const float* pp = pb + (long long)(K + t) * (d + 2);
+      if (pp[1] > 0.0f) M = fmaxf(M, pp[0]);
+    }
+    M = wave_max_f(M);
+    float L = 0.0f;
+    for (int t = tid; t < nwin; t += 64) {
+      const float* pp = pb + (long long)(K + t) * (d + 2);
+      if (pp[1] > 0.0f) L += pp[1] * __expf(pp[0] - M);
+    }
+    L = wave_sum_f(L);
+    const float logz = M + __logf(L);
+    float Mx = logz;
+    for (int kx = tid; kx < kk; kx += 64) Mx = fmaxf(Mx, sl[kx]);
+    Mx = wave_max_f(Mx);
+    float Z = 0.0f;
+    for (int kx = tid; kx < kk; kx += 64) Z += __expf(sl[kx] - Mx);
+    Z = wave_sum_f(Z) + __expf(logz - Mx);
+    const float aw = __expf(logz - Mx) / Z / L;
+    for (int kx = tid; kx < K; kx += 64)
+      wsplit[kx] = (kx < kk) ? __expf(sl[kx] - Mx) / Z / pb[(long long)kx * (d + 2) + 1] : 0.0f;
+    for (int t = tid; t < nwin; t += 64) {
+      const float* pp = pb + (long long)(K + t) * (d + 2);
+      wsplit[K + t] = (pp[1] > 0.0f) ? aw * __expf(pp[0] - M) : 0.0f;
     }
   }
-#pragma unroll
-  for (int u = 0; u < MAXE; ++u) {
-    const int e = lane + 64 * u;
-    if (e < d) Elt<T>::st(out + (long long)bh * d + e, acc[u]);
+  __syncthreads();
+  for (int e = tid; e < d; e += 256) {      // every split holds a finite partial (zero if empty)
+    float acc = 0.0f;
+#pragma unroll 8
+    for (int t = 0; t < NS; ++t) acc = fmaf(wsplit[t], pb[(long long)t * (d + 2) + 2 + e], acc);
+    Elt<T>::st(out + (long long)bh * d + e, acc);
   }
 }
 
@@ -356,35 +443,44 @@ k_dec_combine(const float* __restrict__ part, const float* __restrict__ slog,
 hipError_t hils_launch_decode(const HilsShape& s, const void* q, const void* qr, const void* k,
                               const void* v, const int32_t* seqlen, const void* ksum,
                               const float* bsum, void* out, int32_t* sel, float* scores,
-                              uint32_t* keys, float* slog, float* part, hipStream_t st) {
+                              uint32_t* keys, float* slog, float* part, float* lsep,
+                              hipStream_t st) {
   const int NS = s.K + s.nwin;
   const float tau = (float)s.tau;
   const unsigned nsb = (unsigned)((s.nmax + SC_CPB - 1) / SC_CPB);
-  const size_t ashm = (size_t)s.G * s.d * 4;
+  const size_t esz = s.dtype == 0 ? 2 : 4;
+  const size_t ashm = 2 * (size_t)s.S * (s.d + 16 / esz) * esz + (size_t)s.G * s.d * 4 +
+                      (size_t)s.G * ((s.S + 3) & ~3) * 4;
+  const size_t cshm = (size_t)NS * 4;
   if (s.dtype == 0) {
     if (nsb > 0)
       { HilsProfScope ps_("k_dec_score", st); hipLaunchKernelGGL(k_dec_score<bf16_t>, dim3(s.B * s.Hq, nsb), dim3(256), 0, st,
-                         (const bf16_t*)qr, (const bf16_t*)ksum, bsum, seqlen, scores, s.Hq, s.nC,
-                         s.nmax, s.N, s.d, s.S, s.W, tau); }
+                         (const bf16_t*)qr, (const bf16_t*)ksum, bsum, seqlen, scores, lsep, s.Hq,
+                         s.nC, s.nmax, (int)nsb, s.N, s.d, s.S, s.W, tau); }
   } else {
     if (nsb > 0)
       { HilsProfScope ps_("k_dec_score", st); hipLaunchKernelGGL(k_dec_score<float>, dim3(s.B * s.Hq, nsb), dim3(256), 0, st,
-                         (const float*)qr, (const float*)ksum, bsum, seqlen, scores, s.Hq, s.nC,
-                         s.nmax, s.N, s.d, s.S, s.W, tau); }
+                         (const float*)qr, (const float*)ksum, bsum, seqlen, scores, lsep, s.Hq,
+                         s.nC, s.nmax, (int)nsb, s.N, s.d, s.S, s.W, tau); }
   }
-  { HilsProfScope ps_("k_dec_select", st); hipLaunchKernelGGL(k_dec_select, dim3(s.B * s.Hkv), dim3(SEL_NT), 0, st, scores, seqlen, keys,
-                     sel, slog, s.Hq, s.Hkv, s.G, s.nmax > 0 ? s.nmax : 1, s.N, s.S, s.W, s.K); }
+  const size_t sshm = (size_t)4 * (size_t)min(s.nmax > 0 ? s.nmax : 1, SEL_LDS_KEYS);
+  hipFuncSetAttribute((const void*)k_dec_select, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sshm);
+  { HilsProfScope ps_("k_dec_select", st); hipLaunchKernelGGL(k_dec_select, dim3(s.B * s.Hkv), dim3(SEL_NT), sshm, st, scores, lsep, seqlen,
+                     keys, sel, slog, s.Hq, s.Hkv, s.G, s.nmax > 0 ? s.nmax : 1, (int)nsb, s.N, s.S,
+                     s.W, s.K); }
   if (s.dtype == 0) {
+    hipFuncSetAttribute((const void*)k_dec_attn<bf16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
     { HilsProfScope ps_("k_dec_attn", st); hipLaunchKernelGGL(k_dec_attn<bf16_t>, dim3(s.B * s.Hkv, NS), dim3(AT_NT), ashm, st,
                        (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, seqlen, sel, part,
                        s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, NS, tau); }
-    { HilsProfScope ps_("k_dec_combine", st); hipLaunchKernelGGL(k_dec_combine<bf16_t>, dim3(s.B * s.Hq), dim3(64), 0, st, part, slog,
+    { HilsProfScope ps_("k_dec_combine", st); hipLaunchKernelGGL(k_dec_combine<bf16_t>, dim3(s.B * s.Hq), dim3(256), cshm, st, part, slog,
                        seqlen, (bf16_t*)out, s.Hq, s.G, s.N, s.d, s.S, s.W, s.K, NS, s.nwin); }
   } else {
+    hipFuncSetAttribute((const void*)k_dec_attn<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
     { HilsProfScope ps_("k_dec_attn", st); hipLaunchKernelGGL(k_dec_attn<float>, dim3(s.B * s.Hkv, NS), dim3(AT_NT), ashm, st,
                        (const float*)q, (const float*)k, (const float*)v, seqlen, sel, part,
                        s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, NS, tau); }
-    { HilsProfScope ps_("k_dec_combine", st); hipLaunchKernelGGL(k_dec_combine<float>, dim3(s.B * s.Hq), dim3(64), 0, st, part, slog,
+    { HilsProfScope ps_("k_dec_combine", st); hipLaunchKernelGGL(k_dec_combine<float>, dim3(s.B * s.Hq), dim3(256), cshm, st, part, slog,
                        seqlen, (float*)out, s.Hq, s.G, s.N, s.d, s.S, s.W, s.K, NS, s.nwin); }
   }
   return hipGetLastError();

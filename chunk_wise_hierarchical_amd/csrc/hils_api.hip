@@ -83,7 +83,7 @@ PrefillLayout prefill_layout(const HilsShape& s, bool fast) {
 }
 
 struct DecodeLayout {
-  size_t scores, keys, slog, sel, part, total;
+  size_t scores, keys, slog, sel, part, lsep, total;
 };
 DecodeLayout decode_layout(const HilsShape& s) {
   DecodeLayout L{};
@@ -94,6 +94,7 @@ DecodeLayout decode_layout(const HilsShape& s) {
   L.slog = off;   off += align_up((size_t)s.B * s.Hq * s.K * 4);
   L.sel = off;    off += align_up((size_t)s.B * s.Hkv * s.K * 4);
   L.part = off;   off += align_up((size_t)s.B * s.Hq * (s.K + s.nwin) * (s.d + 2) * 4);
+  L.lsep = off;   off += align_up((size_t)s.B * s.Hq * ((nm + HILS_DEC_SCORE_ROWS - 1) / HILS_DEC_SCORE_ROWS) * 8);
   L.total = off;
   return L;
 }
@@ -265,7 +266,7 @@ hils_status hils_decode(const hils_cfg* cfg, const void* q, const void* q_route,
   return hip_status(hils_launch_decode(s, q, qr, k_cache, v_cache, seqlen, k_sum, b_sum, out, sl,
                                        (float*)(w + L.scores), (uint32_t*)(w + L.keys),
                                        (float*)(w + L.slog), (float*)(w + L.part),
-                                       (hipStream_t)stream));
+                                       (float*)(w + L.lsep), (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -47,7 +47,11 @@ constexpr int HILS_FAST_NCMAX = 16384;   // chunk ids the fast attention bitmap 
 hipError_t hils_launch_decode(const HilsShape& s, const void* q, const void* qr, const void* k,
                               const void* v, const int32_t* seqlen, const void* ksum,
                               const float* bsum, void* out, int32_t* sel, float* scores,
-                              uint32_t* keys, float* slog, float* part, hipStream_t st);
+                              uint32_t* keys, float* slog, float* part, float* lsep,
+                              hipStream_t st);
+
+// chunk rows per decode scoring workgroup (one (max, sum exp) partial each)
+constexpr int HILS_DEC_SCORE_ROWS = 256;
 
 // maximum candidates the generic select kernel keeps in LDS
 constexpr int HILS_GENERIC_NMAX = 8192;

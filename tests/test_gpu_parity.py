@@ -265,3 +265,20 @@ def test_decode_fp32_and_q_route():
 def test_decode_full_512k_sampled_sequences():
     w = synth.get_workload("decode_512k")
     _decode_case(w, [w.N] * w.B, label="full size, 2 sequences checked", seqs=[0, 15])
+
+
+def test_decode_mha_and_wide_groups():
+    # G = 1 ranks raw scores; G = 8 is the widest group the kernels take
+    w = synth.get_workload("decode_512k", N=8192, B=2, Hq=8, Hkv=8, K=16, W=512)
+    _decode_case(w, [8192, 4097], label="G=1")
+    w = synth.get_workload("decode_512k", N=8192, B=2, Hq=16, Hkv=2, K=16, W=512)
+    _decode_case(w, [8192, 6001], label="G=8")
+    # chunk size that is not a multiple of 4, window not a multiple of the chunk
+    w = synth.get_workload("decode_512k", N=4400, B=2, Hq=4, Hkv=2, S=22, W=100, K=6)
+    _decode_case(w, [4400, 3333], label="S=22")
+
+
+def test_decode_candidates_beyond_lds():
+    # more candidate chunks than the selection kernel keeps in LDS (24576)
+    w = synth.get_workload("decode_512k", N=409600, B=1, Hq=2, Hkv=1, d=64, S=16, W=256, K=8)
+    _decode_case(w, [409600], label="n > 24576")
