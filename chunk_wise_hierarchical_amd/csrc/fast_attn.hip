@@ -205,12 +205,15 @@ k_attn_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
   const long long wlo = vcol ? window_start(iq, W, S) : 0;
 
   // chunk staging through registers (two chunks in flight) into one LDS tile
+  // Unconditional loads (rows past N read row N-1: such keys are always masked,
+  // and V^T is zero there), so no load result is ever merged or copied while
+  // it is still in flight.
   auto load_chunk = [&](uint4* r, int c) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int piece = tid + NT * p, row = piece / 16, part = piece % 16;
-      const long long t = (long long)c * S + row;
-      r[p] = (t < N) ? ld_u4(k + (kvbase * N + t) * D + part * 8) : make_uint4(0, 0, 0, 0);
+      const long long t = min((long long)c * S + row, (long long)N - 1);
+      r[p] = ld_u4(k + (kvbase * N + t) * D + part * 8);
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -292,8 +295,7 @@ k_attn_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
         x[kt * 4 + e] = v2;
         mt = fmaxf(mt, v2);
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = max_x32(max_x16(mt));
     const float mnew = fmaxf(m, mt);
     float p[16];
     float ps = 0.0f;
@@ -306,8 +308,7 @@ k_attn_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
 #pragma unroll
       for (int t = 0; t < 16; ++t) { p[t] = fast_exp2(x[t] - mnew); ps += p[t]; }
     }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
+    ps = sum_x32(sum_x16(ps));
     l = l * scale + ps;
     m = mnew;
 #pragma unroll
@@ -354,14 +355,12 @@ k_attn_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
         x[kt * 4 + e] = v2;
         mt = fmaxf(mt, v2);
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = max_x32(max_x16(mt));
     float p[16];
     float ps = 0.0f;
 #pragma unroll
     for (int t = 0; t < 16; ++t) { p[t] = here ? fast_exp2(x[t] - mt) : 0.0f; ps += p[t]; }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
+    ps = sum_x32(sum_x16(ps));
     float coef = 0.0f;
     if (here) {
       coef = fast_exp2(lam[colr * (K + 1) + kptr] - M2) * invZ / ps;
@@ -377,9 +376,10 @@ k_attn_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
 
   // invariant at step idx: LDS holds chunk idx, `nxt` holds chunk idx+1 (loads
   // in flight), `far` is free and receives chunk idx+2
+  // (past the end, loads repeat the last chunk and the final store is unused)
   uint4 ra[8], rb[8];
   auto step = [&](int idx, uint4* nxt, uint4* far) {
-    if (idx + 2 < total) load_chunk(far, chunk_of(idx + 2));
+    load_chunk(far, chunk_of(min(idx + 2, total - 1)));
     if (idx < nw) {
       window_tile(cw_lo + idx);
       if (idx == nw - 1) fusion_setup();
@@ -387,17 +387,19 @@ k_attn_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
       selected_chunk(idx - nw);
     }
     __syncthreads();
-    if (idx + 1 < total) store_chunk(nxt);
+    store_chunk(nxt);
     __syncthreads();
   };
   load_chunk(ra, chunk_of(0));
-  if (total > 1) load_chunk(rb, chunk_of(1));
+  load_chunk(rb, chunk_of(min(1, total - 1)));
   store_chunk(ra);
   __syncthreads();
-  for (int idx = 0; idx < total; idx += 2) {
+  int idx = 0;
+  for (; idx + 1 < total; idx += 2) {
     step(idx, rb, ra);
-    if (idx + 1 < total) step(idx + 1, ra, rb);
+    step(idx + 1, ra, rb);
   }
+  if (idx < total) step(idx, rb, ra);
 
   // ---- store ------------------------------------------------------------
   if (vcol) {

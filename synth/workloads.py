@@ -57,6 +57,11 @@ WORKLOADS = {
     # K=64; needles at 10 evenly spaced depths; half the heads peaked
     "prefill_512k": Workload("prefill_512k", "prefill", 1, 524288, 32, 8, 128, 64, 2048, 64,
                              "bf16", False, "depth10"),
+    # the same prefill with adjacent queries sharing most of their direction
+    # (90% of the variance shared within 512-token segments), so that the
+    # M=16 chunk overlap of adjacent queries is in the range trained models show
+    "prefill_512k_corr": Workload("prefill_512k_corr", "prefill", 1, 524288, 32, 8, 128, 64,
+                                  2048, 64, "bf16", False, "depth10", q_share=0.9, q_seg=512),
     # bf16 extreme context decode: B=1, 4M-token KV cache, same heads/S/W/K
     "decode_4m": Workload("decode_4m", "decode", 1, 4194304, 32, 8, 128, 64, 2048, 64,
                           "bf16", False, "depth10"),
