@@ -10,7 +10,16 @@ records on its own stream (hils_profile_enable) inside the timed region.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_512k]
                     [--decode-workload decode_512k] [--decode-steps 50] [--no-cpu]
+                    [--calibrate-copy]
+
+`roofline.traffic` is the dominant kernel's HBM bytes per launch measured with
+rocprofv3 FETCH_SIZE and WRITE_SIZE counters (profiles/*_pmc.md), scaled by
+what the same counters read for a plain 1 GiB copy kernel (--calibrate-copy
+runs that copy first so one profiled command holds both).  It is reported
+only while the kernel's sources still hash to the value recorded with the
+counters, and is null otherwise.
 """
+import hashlib
 import argparse
 import json
 import math
@@ -55,6 +64,55 @@ def decode_work(w, T):
                + w.Hkv * win * w.d * e * 2 + 2 * w.Hq * w.d * e)
     score_bytes = w.B * w.Hq * n * (w.d * e + 4 + 4)
     return per_seq * w.B, score_bytes
+
+
+# sources whose text decides each kernel's code (for the counter staleness check)
+KERNEL_SOURCES = {
+    "k_attn_fast": ["fast_attn.hip", "fast_common.h", "hils_device.h"],
+    "k_score_fast": ["fast_score.hip", "fast_common.h", "hils_device.h"],
+    "k_dec_score": ["decode.hip", "hils_device.h", "hils_internal.h"],
+}
+
+
+def kernel_source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, "chunk_wise_hierarchical_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel, workload):
+    """HBM bytes per launch from profiles/<kernel>_<workload>_pmc.md, or None
+    when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for ln in fh:
+            if ln.startswith("- ") and ":" in ln:
+                k, v = ln[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256_16") != kernel_source_hash(kernel):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(torch, dev, log):
+    """A plain device copy of 1 GiB (fp32 elementwise kernel), three times, so a
+    rocprofv3 counter run can scale FETCH_SIZE / WRITE_SIZE to bytes."""
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 x {n * 4} bytes read and written")
+    del a, b
 
 
 def _kernel_table(records, steps):
@@ -139,6 +197,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 1 GiB copy first (counter scale for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; this build has no multi-GPU path "
@@ -156,6 +216,9 @@ def main():
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.calibrate_copy:
+        calibrate_copy(torch, dev, log)
 
     # ---------------- prefill ----------------
     w = synth.get_workload(args.workload)
@@ -194,7 +257,8 @@ def main():
                  "k_select_generic": score_f, "k_summarize": summ_f}.get(dom, attn_f)
     achieved = dom_flops / (kern[dom]["avg_ms"] * 1e-3) / 1e12
     roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": counter_traffic(dom, w.name),
             "algorithmic_flops_per_launch": dom_flops}
     total_tflops = (score_f + summ_f + attn_f) / (prefill_ms * 1e-3) / 1e12
 
@@ -249,7 +313,8 @@ def main():
                "algorithmic_bytes_per_step": step_bytes,
                "roofline": {"kernel": "k_dec_score", "bound": "hbm", "achieved": dach,
                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": (dach / PEAK_HBM_GBS) if dach else None, "traffic": None,
+                            "frac": (dach / PEAK_HBM_GBS) if dach else None,
+                            "traffic": counter_traffic("k_dec_score", wd.name),
                             "algorithmic_bytes_per_launch": score_bytes},
                "kernels": dk}
         if not args.no_cpu:

@@ -15,6 +15,7 @@ HILS_OK, HILS_E_ARG, HILS_E_UNSUPPORTED, HILS_E_WORKSPACE, HILS_E_HIP = range(5)
 HILS_BF16, HILS_F32 = 0, 1
 MODES = {"surrogate": 0, "landmark_key": 1, "exact": 2}
 HILS_FLAG_GENERIC = 1
+HILS_FLAG_UNION = 2
 
 EXPORTED = ("hils_workspace_bytes", "hils_summarize", "hils_prefill", "hils_decode",
             "hils_strerror", "hils_abi_version", "hils_profile_enable", "hils_profile_read")

@@ -34,10 +34,11 @@ def _check_tensor(t, name, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def make_cfg(B, N, Hq, Hkv, d, S, W, K, dtype, mode="surrogate", scale=0.0, generic=False):
+def make_cfg(B, N, Hq, Hkv, d, S, W, K, dtype, mode="surrogate", scale=0.0, generic=False,
+             union=False):
+    flags = (_lib.HILS_FLAG_GENERIC if generic else 0) | (_lib.HILS_FLAG_UNION if union else 0)
     return HilsCfg(B=B, N=N, Hq=Hq, Hkv=Hkv, d=d, S=S, W=W, K=K, dtype=_DT[dtype],
-                   mode=_lib.MODES[mode], scale=float(scale),
-                   flags=_lib.HILS_FLAG_GENERIC if generic else 0)
+                   mode=_lib.MODES[mode], scale=float(scale), flags=flags)
 
 
 def workspace_bytes(cfg: HilsCfg, decode: bool) -> int:
@@ -56,9 +57,12 @@ def _workspace(cfg, decode, device, ws):
 
 
 def prefill(q, k, v, lm, S, W, K, q_route=None, mode="surrogate", scale=0.0, out=None,
-            sel=None, summaries=None, ws=None, generic=False):
+            sel=None, summaries=None, ws=None, generic=False, union=False):
     """HiLS prefill. q [B,Hq,N,d]; k,v [B,Hkv,N,d]; lm [B,Hq,N//S,d].
 
+    generic forces the vector-ALU kernels; union selects the MFMA attention by
+    query block over the union of the block's chunks instead of the default
+    per-chunk buckets.
     sel (optional) [B,Hkv,N,K] int32 receives the selected chunk ids;
     summaries (optional) (k_sum [B,Hq,N//S,d], b_sum [B,Hq,N//S] fp32) receive the
     chunk summaries.  Returns out [B,Hq,N,d].
@@ -77,7 +81,7 @@ def prefill(q, k, v, lm, S, W, K, q_route=None, mode="surrogate", scale=0.0, out
         ks, bs = summaries
         _check_tensor(ks, "k_sum", q.dtype, dev)
         _check_tensor(bs, "b_sum", torch.float32, dev)
-    cfg = make_cfg(B, N, Hq, Hkv, d, S, W, K, q.dtype, mode, scale, generic)
+    cfg = make_cfg(B, N, Hq, Hkv, d, S, W, K, q.dtype, mode, scale, generic, union)
     ws, need = _workspace(cfg, False, dev, ws)
     st = _lib.lib().hils_prefill(ctypes.byref(cfg), _ptr(q), _ptr(q_route), _ptr(k), _ptr(v),
                                  _ptr(lm), _ptr(out), _ptr(sel), _ptr(ks), _ptr(bs), _ptr(ws),

@@ -1,0 +1,677 @@
+// Fast-path prefill attention, organised by selected chunk ("pair-sorted"),
+// bf16, d = 128, S = 64.
+//
+// "Hierarchical Sparse Attention Done Right", section 3 (hierarchical
+// softmax): a query's output is the window attention plus, for each selected
+// chunk c, an attention over that chunk's S keys alone, mixed by a softmax
+// over {s_hat_c} U {log Z_swa}.  Once the window pass has fixed log Z_swa and
+// the fusion weights alpha_c, every (query, selected chunk) pair is an
+// independent S-key attention scaled by alpha_c.
+//
+// Section 4.2 of the pages packs adjacent queries and loads the union of their
+// chunks; when adjacent queries route to different chunks that re-reads every
+// chunk's K/V for almost every query.  Here the pairs of a slice of queries are
+// bucketed by chunk instead, so each chunk's K/V is staged in LDS once per
+// slice and every pair that selected it is computed against it:
+//   1. k_pair_count / k_pair_scan / k_pair_tiles / k_pair_scatter: counting
+//      sort of the slice's (query, slot) pairs by (KV group, chunk), cut into
+//      tiles of 64/G pairs (64 MFMA rows with the G heads of a group);
+//   2. k_win_fast: window attention (online softmax over the window tiles);
+//      writes o_swa (normalised, fp32) and log Z_swa;
+//   3. k_pair_attn: per tile, gather the 64 query rows, form the fusion logit
+//      s_hat = scale q_hat.k'_c + b'_c of each row, S^T = K Q^T and
+//      O^T = V^T P^T on MFMA; writes o_c (normalised, bf16) and s_hat per pair;
+//   4. k_pair_reduce: alpha = softmax over {s_hat_c} U {log Z_swa} and
+//      out = alpha_swa o_swa + sum_c alpha_c o_c, in slot order (deterministic;
+//      the order of pairs inside a bucket never changes a result, since MFMA
+//      rows are independent).
+#include "fast_common.h"
+#include "hils_internal.h"
+
+using namespace fastp;
+
+namespace {
+
+constexpr int NT = 256;
+constexpr int KSTR = D;       // K tile row stride (elements); 16-byte parts XOR-swizzled per row
+constexpr int VSTR = S + 8;   // V^T tile row stride (elements)
+constexpr int PQ = 512;       // queries per list-building workgroup
+constexpr int RQ = 16;        // queries per reduce workgroup
+constexpr int PTPW = HILS_PAIR_TPW;   // tiles per pair-attention workgroup
+
+__device__ __forceinline__ int kswz(int r, int p) { return p ^ (((r >> 1) & 12) | (r & 3)); }
+
+constexpr size_t KT_BYTES = (size_t)S * KSTR * 2;
+constexpr size_t VT_BYTES = (size_t)D * VSTR * 2;
+
+// ---------------------------------------------------------------------------
+// pair lists
+
+__global__ void __launch_bounds__(NT)
+k_fill_u32(uint32_t* __restrict__ p, long long n, uint32_t v) {
+  for (long long t = (long long)blockIdx.x * NT + threadIdx.x; t < n; t += (long long)gridDim.x * NT)
+    p[t] = v;
+}
+
+// per (KV group, chunk): number of pairs of the slice that selected it
+__global__ void __launch_bounds__(NT)
+k_pair_count(const int32_t* __restrict__ sel, uint32_t* __restrict__ cnt, int N, int K, int nC,
+             int i0, int qs) {
+  extern __shared__ uint32_t hist[];   // [nC]
+  const int bg = blockIdx.x;
+  const int q0 = blockIdx.y * PQ;
+  const int qn = min(PQ, qs - q0);
+  for (int c = threadIdx.x; c < nC; c += NT) hist[c] = 0;
+  __syncthreads();
+  const int32_t* sb = sel + ((long long)bg * N + i0 + q0) * K;
+  for (int t = threadIdx.x; t < qn * K; t += NT) {
+    const int c = sb[t];
+    if (c >= 0 && c < nC) atomicAdd(&hist[c], 1u);
+  }
+  __syncthreads();
+  uint32_t* cg = cnt + (long long)bg * nC;
+  for (int c = threadIdx.x; c < nC; c += NT)
+    if (hist[c]) atomicAdd(&cg[c], hist[c]);
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+// one workgroup: exclusive prefix sums over f = bg*nC + c of the bucket sizes
+// (list offsets, also the scatter cursors) and of their tile counts;
+// tot[0] = pairs, tot[1] = tiles
+__global__ void __launch_bounds__(1024)
+k_pair_scan(const uint32_t* __restrict__ cnt, uint32_t* __restrict__ loff,
+            uint32_t* __restrict__ toff, uint32_t* __restrict__ cur, uint32_t* __restrict__ tot,
+            int F, int TQ) {
+  __shared__ uint32_t wa[16], wb[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint32_t run_a = 0, run_b = 0;
+  for (int base = 0; base < F; base += 1024) {
+    const int f = base + tid;
+    const uint32_t a = (f < F) ? cnt[f] : 0u;
+    const uint32_t b = (a + (uint32_t)TQ - 1u) / (uint32_t)TQ;
+    const uint32_t ia = wave_incl_scan_u32(a, lane), ib = wave_incl_scan_u32(b, lane);
+    if (lane == 63) { wa[w] = ia; wb[w] = ib; }
+    __syncthreads();
+    uint32_t pa = 0, pb = 0, ta = 0, tb = 0;
+    for (int u = 0; u < 16; ++u) {
+      const uint32_t x = wa[u], y = wb[u];
+      if (u < w) { pa += x; pb += y; }
+      ta += x;
+      tb += y;
+    }
+    if (f < F) {
+      const uint32_t la = run_a + pa + ia - a;
+      loff[f] = la;
+      cur[f] = la;
+      toff[f] = run_b + pb + ib - b;
+    }
+    run_a += ta;
+    run_b += tb;
+    __syncthreads();
+  }
+  if (tid == 0) { tot[0] = run_a; tot[1] = run_b; }
+}
+
+// tile t of bucket f: {f << 7 | pairs in the tile, first list position}
+__global__ void __launch_bounds__(NT)
+k_pair_tiles(const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ loff,
+             const uint32_t* __restrict__ toff, uint2* __restrict__ tinfo, int F, int TQ) {
+  const int f = blockIdx.x * NT + threadIdx.x;
+  if (f >= F) return;
+  const uint32_t n = cnt[f], t0 = toff[f], l0 = loff[f];
+  const uint32_t nt = (n + (uint32_t)TQ - 1u) / (uint32_t)TQ;
+  for (uint32_t u = 0; u < nt; ++u) {
+    const uint32_t m = min((uint32_t)TQ, n - u * (uint32_t)TQ);
+    tinfo[t0 + u] = make_uint2(((uint32_t)f << 7) | m, l0 + u * (uint32_t)TQ);
+  }
+}
+
+// list entries (local query << 7 | slot), bucketed by chunk; the order inside
+// a bucket depends on atomics and does not affect any result
+__global__ void __launch_bounds__(NT)
+k_pair_scatter(const int32_t* __restrict__ sel, uint32_t* __restrict__ cur,
+               uint32_t* __restrict__ list, int N, int K, int nC, int i0, int qs) {
+  extern __shared__ uint32_t lc[];   // [nC]: local count, then next global position
+  const int bg = blockIdx.x;
+  const int q0 = blockIdx.y * PQ;
+  const int qn = min(PQ, qs - q0);
+  for (int c = threadIdx.x; c < nC; c += NT) lc[c] = 0;
+  __syncthreads();
+  const int32_t* sb = sel + ((long long)bg * N + i0 + q0) * K;
+  for (int t = threadIdx.x; t < qn * K; t += NT) {
+    const int c = sb[t];
+    if (c >= 0 && c < nC) atomicAdd(&lc[c], 1u);
+  }
+  __syncthreads();
+  uint32_t* cg = cur + (long long)bg * nC;
+  for (int c = threadIdx.x; c < nC; c += NT) {
+    const uint32_t n = lc[c];
+    if (n) lc[c] = atomicAdd(&cg[c], n);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < qn * K; t += NT) {
+    const int c = sb[t];
+    if (c >= 0 && c < nC) {
+      const uint32_t pos = atomicAdd(&lc[c], 1u);
+      list[pos] = ((uint32_t)(q0 + t / K) << 7) | (uint32_t)(t % K);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// window attention + fusion weights
+
+template <int G>
+__global__ void __launch_bounds__(NT, 2)
+k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+           const bf16_t* __restrict__ vt, float* __restrict__ swa, float* __restrict__ lz,
+           int Hq, int Hkv, int N, int W, int nCc, float tau2, int i0, int qs, int nqb) {
+  constexpr int QA = 64 / G;
+  extern __shared__ __align__(16) unsigned char sm[];
+  bf16_t* ktile = reinterpret_cast<bf16_t*>(sm);
+  bf16_t* vtile = reinterpret_cast<bf16_t*>(sm + KT_BYTES);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int blk = blockIdx.x;
+  const int qb = nqb - 1 - (blk % nqb);
+  const int bg = blk / nqb;
+  const int g = bg % Hkv;
+  const long long b = bg / Hkv;
+  const int ib0 = i0 + qb * QA;
+  const int qcount = min(QA, i0 + qs - ib0);
+  const long long hb = b * Hq + (long long)g * G;
+  const long long kvbase = bg;
+
+  const int colr = 16 * w + (lane & 15);
+  const int qa = colr / G, h = colr % G;
+  const int lq = lane >> 4;
+  const bool vcol = qa < qcount;
+  const int iq = ib0 + qa;
+  bf16x8_t bq[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (vcol) bq[ks] = ld_bf16x8(q + ((hb + h) * N + iq) * (long long)D + 32 * ks + 8 * lq);
+    else bq[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+  }
+  const long long wlo = vcol ? window_start(iq, W, S) : 0;
+
+  // rows past N read row N-1 (masked); V^T is zero there
+  auto load_chunk = [&](uint4* r, int c) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int piece = tid + NT * p, row = piece / 16, part = piece % 16;
+      const long long t = min((long long)c * S + row, (long long)N - 1);
+      r[p] = ld_u4(k + (kvbase * N + t) * D + part * 8);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int piece = tid + NT * p, row = piece / 8, part = piece % 8;
+      r[4 + p] = ld_u4(vt + ((kvbase * nCc + c) * D + row) * (long long)S + part * 8);
+    }
+  };
+  auto store_chunk = [&](const uint4* r) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int piece = tid + NT * p, row = piece / 16, part = piece % 16;
+      st_u4(ktile + row * KSTR + kswz(row, part) * 8, r[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int piece = tid + NT * p, row = piece / 8, part = piece % 8;
+      st_u4(vtile + row * VSTR + part * 8, r[4 + p]);
+    }
+  };
+  f32x4_t acc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.0f;
+
+  auto window_tile = [&](int c) {
+    f32x4_t s[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int mm = lane & 15;
+      const int key = 32 * (kt >> 1) + 8 * (mm >> 2) + 4 * (kt & 1) + (mm & 3);
+      f32x4_t a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        a4 = mfma16(ld_bf16x8(ktile + key * KSTR + kswz(key, 4 * ks + lq) * 8), bq[ks], a4);
+      s[kt] = a4;
+    }
+    float x[16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const long long j = (long long)c * S + 32 * (kt >> 1) + 8 * lq + 4 * (kt & 1) + e;
+        const bool ok = vcol && j >= wlo && j <= iq;
+        const float v2 = ok ? s[kt][e] * tau2 : -INFINITY;
+        x[kt * 4 + e] = v2;
+        mt = fmaxf(mt, v2);
+      }
+    mt = max_x32(max_x16(mt));
+    const float mnew = fmaxf(m, mt);
+    float p[16];
+    float ps = 0.0f;
+    float scale = 1.0f;
+    if (mnew == -INFINITY) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) p[t] = 0.0f;
+    } else {
+      scale = fast_exp2(m - mnew);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) { p[t] = fast_exp2(x[t] - mnew); ps += p[t]; }
+    }
+    ps = sum_x32(sum_x16(ps));
+    l = l * scale + ps;
+    m = mnew;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[dt] *= scale;
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const float* pp = p + 8 * kb;
+      const uint4 u = make_uint4(pack_bf16x2(pp[0], pp[1]), pack_bf16x2(pp[2], pp[3]),
+                                 pack_bf16x2(pp[4], pp[5]), pack_bf16x2(pp[6], pp[7]));
+      pb[kb] = __builtin_bit_cast(bf16x8_t, u);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        acc[dt] = mfma16(ld_bf16x8(vtile + (16 * dt + (lane & 15)) * VSTR + 32 * kb + 8 * lq),
+                         pb[kb], acc[dt]);
+  };
+
+  const int cw_lo = (int)(window_start(ib0, W, S) / S);
+  const int cw_hi = (ib0 + qcount - 1) / S;
+  const int nw = cw_hi - cw_lo + 1;
+  uint4 ra[8], rb[8];
+  auto step = [&](int idx, uint4* nxt, uint4* far) {
+    load_chunk(far, cw_lo + min(idx + 2, nw - 1));
+    window_tile(cw_lo + idx);
+    __syncthreads();
+    store_chunk(nxt);
+    __syncthreads();
+  };
+  load_chunk(ra, cw_lo);
+  load_chunk(rb, cw_lo + min(1, nw - 1));
+  store_chunk(ra);
+  __syncthreads();
+  int idx = 0;
+  for (; idx + 1 < nw; idx += 2) {
+    step(idx, rb, ra);
+    step(idx + 1, ra, rb);
+  }
+  if (idx < nw) step(idx, rb, ra);
+
+  // normalised window output and its log-mass (base 2)
+  if (vcol) {
+    const long long row = (long long)bg * qs + (iq - i0);
+    const float il = 1.0f / l;
+    float* sp = swa + (row * G + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const float4 o = make_float4(acc[dt][0] * il, acc[dt][1] * il, acc[dt][2] * il,
+                                   acc[dt][3] * il);
+      *reinterpret_cast<float4*>(sp + 16 * dt + 4 * lq) = o;
+    }
+    if (lq == 0) lz[row * G + h] = m + log2f(l);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// per-chunk attention of the bucketed pairs
+
+template <int G>
+__global__ void __launch_bounds__(NT, 2)
+k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
+            const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
+            const bf16_t* __restrict__ ksum, const float* __restrict__ bsum,
+            const uint32_t* __restrict__ list, const uint2* __restrict__ tinfo,
+            const uint32_t* __restrict__ tot, float* __restrict__ lamb, bf16_t* __restrict__ part,
+            int Hq, int Hkv, int N, int K, int nC, int nCc, float tau2, int i0, int qs) {
+  extern __shared__ __align__(16) unsigned char sm[];
+  bf16_t* ktile = reinterpret_cast<bf16_t*>(sm);
+  bf16_t* vtile = reinterpret_cast<bf16_t*>(sm + KT_BYTES);
+  bf16_t* kstile = reinterpret_cast<bf16_t*>(sm + KT_BYTES + VT_BYTES);   // [G][D] k'_c
+  __shared__ float bst[G];
+  __shared__ uint2 tl[PTPW];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint32_t T = tot[1];
+  const uint32_t t0 = (uint32_t)blockIdx.x * PTPW;
+  if (t0 >= T) return;
+  const int nt = (int)min((uint32_t)PTPW, T - t0);
+  if (tid < nt) tl[tid] = tinfo[t0 + tid];
+  __syncthreads();
+  const int colr = 16 * w + (lane & 15);
+  const int jr = colr / G, h = colr % G;
+  const int lq = lane >> 4;
+  const bool has_qr = qr != nullptr;
+
+  // list entry of this lane's row in tile u (rows past the tile's pairs repeat
+  // its last pair: loads stay valid, results are not stored)
+  auto entry = [&](int u) {
+    const uint2 ti = tl[u];
+    const int mcount = (int)(ti.x & 127u);
+    return list[ti.y + min(jr, mcount - 1)];
+  };
+  auto qrow = [&](uint32_t ent, int f) {
+    const int bg = f / nC;
+    const int b = bg / Hkv, g = bg - b * Hkv;
+    return (((long long)b * Hq + (long long)g * G + h) * N + i0 + (int)(ent >> 7)) * D;
+  };
+  auto load_q = [&](const bf16_t* src, long long off, bf16x8_t* r) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) r[ks] = ld_bf16x8(src + off + 32 * ks + 8 * lq);
+  };
+
+  // two-deep prefetch: entries of tile u+2 and query rows of tile u+1 are in
+  // flight while tile u is computed
+  uint32_t ent_c = entry(0);
+  uint32_t ent_n = entry(min(1, nt - 1));
+  bf16x8_t bq_c[4], bq_n[4], br_c[4], br_n[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    br_c[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+    br_n[ks] = br_c[ks];
+  }
+  load_q(q, qrow(ent_c, (int)(tl[0].x >> 7)), bq_c);
+  if (has_qr) load_q(qr, qrow(ent_c, (int)(tl[0].x >> 7)), br_c);
+  int cur = -1;
+  for (int u = 0; u < nt; ++u) {
+    const uint2 ti = tl[u];
+    const int f = (int)(ti.x >> 7), mcount = (int)(ti.x & 127u);
+    const int bg = f / nC, c = f - bg * nC;
+    const uint32_t ent_nn = entry(min(u + 2, nt - 1));
+    {
+      const int un = min(u + 1, nt - 1);
+      const long long off = qrow(ent_n, (int)(tl[un].x >> 7));
+      load_q(q, off, bq_n);
+      if (has_qr) load_q(qr, off, br_n);
+    }
+    if (f != cur) {            // stage the chunk's K (swizzled), V^T and the group's k'_c, b'_c
+      __syncthreads();
+      uint4 r[8];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int piece = tid + NT * p, row = piece / 16, pt = piece % 16;
+        r[p] = ld_u4(k + ((long long)bg * N + (long long)c * S + row) * D + pt * 8);
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int piece = tid + NT * p, row = piece / 8, pt = piece % 8;
+        r[4 + p] = ld_u4(vt + (((long long)bg * nCc + c) * D + row) * (long long)S + pt * 8);
+      }
+      const int b = bg / Hkv, g = bg - b * Hkv;
+      const long long hs = (long long)b * Hq + (long long)g * G;
+      uint4 rk = make_uint4(0, 0, 0, 0);
+      if (tid < G * 16) rk = ld_u4(ksum + ((hs + tid / 16) * nC + c) * (long long)D + (tid % 16) * 8);
+      float rb = 0.0f;
+      if (tid < G) rb = bsum[(hs + tid) * nC + c];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int piece = tid + NT * p, row = piece / 16, pt = piece % 16;
+        st_u4(ktile + row * KSTR + kswz(row, pt) * 8, r[p]);
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int piece = tid + NT * p, row = piece / 8, pt = piece % 8;
+        st_u4(vtile + row * VSTR + pt * 8, r[4 + p]);
+      }
+      if (tid < G * 16) st_u4(kstile + tid * 8, rk);
+      if (tid < G) bst[tid] = rb;
+      __syncthreads();
+      cur = f;
+    }
+    const bool valid = jr < mcount;
+    const int qi = (int)(ent_c >> 7), kx = (int)(ent_c & 127u);
+    const long long prow = ((long long)bg * qs + qi) * K + kx;   // pair index
+
+    // fusion logit of the row (base 2): the 4 lanes of a row each hold 32 of
+    // its 128 query elements
+    float lam;
+    {
+      const bf16x8_t* src = has_qr ? br_c : bq_c;
+      float dp = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 a = __builtin_bit_cast(uint4, src[ks]);
+        const uint4 kb = ld_u4(kstile + h * D + 32 * ks + 8 * lq);
+        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {kb.x, kb.y, kb.z, kb.w};
+#pragma unroll
+        for (int t2 = 0; t2 < 4; ++t2) {
+          dp = fmaf(__uint_as_float(av[t2] << 16), __uint_as_float(bv[t2] << 16), dp);
+          dp = fmaf(__uint_as_float(av[t2] & 0xffff0000u), __uint_as_float(bv[t2] & 0xffff0000u), dp);
+        }
+      }
+      dp = sum_x32(sum_x16(dp));
+      lam = fmaf(dp, tau2, bst[h] * LOG2E);
+    }
+
+    f32x4_t s4[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int mm = lane & 15;
+      const int key = 32 * (kt >> 1) + 8 * (mm >> 2) + 4 * (kt & 1) + (mm & 3);
+      f32x4_t a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        a4 = mfma16(ld_bf16x8(ktile + key * KSTR + kswz(key, 4 * ks + lq) * 8), bq_c[ks], a4);
+      s4[kt] = a4;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s4[kt][e] * tau2);
+    mt = max_x32(max_x16(mt));
+    float p[16];
+    float ps = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[kt * 4 + e] = fast_exp2(s4[kt][e] * tau2 - mt);
+        ps += p[kt * 4 + e];
+      }
+    ps = sum_x32(sum_x16(ps));
+    const float coef = 1.0f / ps;
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float pk[8];
+#pragma unroll
+      for (int t2 = 0; t2 < 8; ++t2) pk[t2] = p[(2 * kb + (t2 >> 2)) * 4 + (t2 & 3)] * coef;
+      const uint4 uu = make_uint4(pack_bf16x2(pk[0], pk[1]), pack_bf16x2(pk[2], pk[3]),
+                                  pack_bf16x2(pk[4], pk[5]), pack_bf16x2(pk[6], pk[7]));
+      pb[kb] = __builtin_bit_cast(bf16x8_t, uu);
+    }
+    f32x4_t acc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      acc[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        acc[dt] = mfma16(ld_bf16x8(vtile + (16 * dt + (lane & 15)) * VSTR + 32 * kb + 8 * lq),
+                         pb[kb], acc[dt]);
+    }
+    if (valid) {
+      bf16_t* op = part + (prow * G + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint2 uu = make_uint2(pack_bf16x2(acc[dt][0], acc[dt][1]),
+                                    pack_bf16x2(acc[dt][2], acc[dt][3]));
+        *reinterpret_cast<uint2*>(op + 16 * dt + 4 * lq) = uu;
+      }
+      if (lq == 0) lamb[prow * G + h] = lam;
+    }
+    ent_c = ent_n;
+    ent_n = ent_nn;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bq_c[ks] = bq_n[ks];
+      br_c[ks] = br_n[ks];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// out = alpha_swa o_swa + sum_k alpha_k o_k, slot order
+
+template <int G>
+__global__ void __launch_bounds__(NT)
+k_pair_reduce(const float* __restrict__ swa, const float* __restrict__ lz,
+              const float* __restrict__ lamb, const bf16_t* __restrict__ part,
+              bf16_t* __restrict__ out, int Hq, int Hkv, int N, int W, int K, int i0, int qs) {
+  constexpr int EP = G * D / 2;                 // element pairs of one query
+  constexpr int QPP = NT / EP;                  // queries per pass
+  extern __shared__ float wk[];                 // [RQ*G][K+1]: alpha_c per slot, alpha_swa last
+  const int bg = blockIdx.x;
+  const int b = bg / Hkv, g = bg - b * Hkv;
+  const int tid = threadIdx.x;
+  const int q0 = blockIdx.y * RQ;
+  // fusion weights: softmax over {s_hat_c} U {log Z_swa}, one thread per (query, head)
+  for (int it = tid; it < RQ * G; it += NT) {
+    const int qq = it / G, h = it - qq * G;
+    const int qi = q0 + qq;
+    if (qi >= qs) continue;
+    const long long i = (long long)i0 + qi;
+    const int kk = min(K, n_cand(i, W, S));
+    const long long row = (long long)bg * qs + qi;
+    float* wr = wk + it * (K + 1);
+    const float lzv = lz[row * G + h];
+    float M2 = lzv;
+    for (int kx = 0; kx < kk; ++kx) {
+      const float lv = lamb[(row * K + kx) * G + h];
+      wr[kx] = lv;
+      M2 = fmaxf(M2, lv);
+    }
+    float Z = fast_exp2(lzv - M2);
+    for (int kx = 0; kx < kk; ++kx) {
+      const float e = fast_exp2(wr[kx] - M2);
+      wr[kx] = e;
+      Z += e;
+    }
+    const float invZ = 1.0f / Z;
+    for (int kx = 0; kx < kk; ++kx) wr[kx] *= invZ;
+    wr[K] = fast_exp2(lzv - M2) * invZ;
+  }
+  __syncthreads();
+  const int sub = tid / EP, e2 = tid - sub * EP;
+  const int h = e2 / (D / 2), d = 2 * (e2 - h * (D / 2));
+  for (int qq = sub; qq < RQ; qq += QPP) {
+    const int qi = q0 + qq;
+    if (qi >= qs) break;
+    const long long i = (long long)i0 + qi;
+    const int kk = min(K, n_cand(i, W, S));
+    const long long row = (long long)bg * qs + qi;
+    const float* wr = wk + (qq * G + h) * (K + 1);
+    const float2 sv = *reinterpret_cast<const float2*>(swa + (row * G + h) * D + d);
+    float a0 = wr[K] * sv.x, a1 = wr[K] * sv.y;
+    const bf16_t* pp = part + (row * K * G + h) * D + d;
+    int kx = 0;
+    for (; kx + 8 <= kk; kx += 8) {
+      uint32_t uv[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) uv[t] = *reinterpret_cast<const uint32_t*>(pp + (long long)(kx + t) * G * D);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        a0 = fmaf(wr[kx + t], __uint_as_float(uv[t] << 16), a0);
+        a1 = fmaf(wr[kx + t], __uint_as_float(uv[t] & 0xffff0000u), a1);
+      }
+    }
+    for (; kx < kk; ++kx) {
+      const uint32_t uv = *reinterpret_cast<const uint32_t*>(pp + (long long)kx * G * D);
+      a0 = fmaf(wr[kx], __uint_as_float(uv << 16), a0);
+      a1 = fmaf(wr[kx], __uint_as_float(uv & 0xffff0000u), a1);
+    }
+    *reinterpret_cast<uint32_t*>(out + (((long long)b * Hq + (long long)g * G + h) * N + i) * D + d) =
+        pack_bf16x2(a0, a1);
+  }
+}
+
+template <int G>
+hipError_t launch_pairs(const HilsShape& s, const void* q, const void* qr, const void* k,
+                        const void* vt, const void* ksum, const float* bsum, const int32_t* sel,
+                        void* out, const HilsPairBufs& pb, hipStream_t st) {
+  constexpr int QA = 64 / G;
+  constexpr int TQ = 64 / G;
+  const int F = s.B * s.Hkv * s.nC;
+  const float tau2 = (float)(s.tau * 1.4426950408889634);
+  const size_t hshm = (size_t)(s.nC > 0 ? s.nC : 1) * 4;
+  const size_t wshm = KT_BYTES + VT_BYTES;
+  const size_t ashm = KT_BYTES + VT_BYTES + (size_t)G * D * 2;
+  const size_t rshm = (size_t)RQ * G * (s.K + 1) * 4;
+  hipFuncSetAttribute((const void*)k_pair_count, hipFuncAttributeMaxDynamicSharedMemorySize, (int)hshm);
+  hipFuncSetAttribute((const void*)k_pair_scatter, hipFuncAttributeMaxDynamicSharedMemorySize, (int)hshm);
+  hipFuncSetAttribute((const void*)k_win_fast<G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)wshm);
+  hipFuncSetAttribute((const void*)k_pair_attn<G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
+  hipFuncSetAttribute((const void*)k_pair_reduce<G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rshm);
+  const bf16_t* qb = (const bf16_t*)q;
+  const bf16_t* qrb = (qr == q) ? nullptr : (const bf16_t*)qr;
+  for (int i0 = 0; i0 < s.N; i0 += pb.qs_max) {
+    const int qs = min(pb.qs_max, s.N - i0);
+    const int nqb = (qs + QA - 1) / QA;
+    if (F > 0) {
+      { HilsProfScope ps_("k_pair_lists", st);
+        hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)min(1024, (F + NT - 1) / NT)), dim3(NT), 0, st,
+                           pb.cnt, (long long)F, 0u);
+        hipLaunchKernelGGL(k_pair_count, dim3(s.B * s.Hkv, (qs + PQ - 1) / PQ), dim3(NT), hshm, st,
+                           sel, pb.cnt, s.N, s.K, s.nC, i0, qs);
+        hipLaunchKernelGGL(k_pair_scan, dim3(1), dim3(1024), 0, st, pb.cnt, pb.loff, pb.toff, pb.cur,
+                           pb.tot, F, TQ);
+        hipLaunchKernelGGL(k_pair_tiles, dim3((F + NT - 1) / NT), dim3(NT), 0, st, pb.cnt, pb.loff,
+                           pb.toff, pb.tinfo, F, TQ);
+        hipLaunchKernelGGL(k_pair_scatter, dim3(s.B * s.Hkv, (qs + PQ - 1) / PQ), dim3(NT), hshm, st,
+                           sel, pb.cur, pb.list, s.N, s.K, s.nC, i0, qs); }
+    }
+    { HilsProfScope ps_("k_win_fast", st);
+      hipLaunchKernelGGL(k_win_fast<G>, dim3((unsigned)(s.B * s.Hkv * nqb)), dim3(NT), wshm, st, qb,
+                         (const bf16_t*)k, (const bf16_t*)vt, pb.swa, pb.lz, s.Hq, s.Hkv, s.N, s.W,
+                         s.nCc, tau2, i0, qs, nqb); }
+    if (F > 0) {
+      const long long tmax = hils_pair_tiles_max(s, qs);
+      const unsigned grid = (unsigned)((tmax + PTPW - 1) / PTPW);
+      { HilsProfScope ps_("k_pair_attn", st);
+        hipLaunchKernelGGL(k_pair_attn<G>, dim3(grid), dim3(NT), ashm, st, qb, qrb,
+                           (const bf16_t*)k, (const bf16_t*)vt, (const bf16_t*)ksum, bsum, pb.list,
+                           pb.tinfo, pb.tot, pb.lam, (bf16_t*)pb.part, s.Hq, s.Hkv, s.N, s.K, s.nC,
+                           s.nCc, tau2, i0, qs); }
+    }
+    { HilsProfScope ps_("k_pair_reduce", st);
+      hipLaunchKernelGGL(k_pair_reduce<G>, dim3(s.B * s.Hkv, (qs + RQ - 1) / RQ), dim3(NT), rshm, st,
+                         pb.swa, pb.lz, pb.lam, (const bf16_t*)pb.part, (bf16_t*)out, s.Hq, s.Hkv,
+                         s.N, s.W, s.K, i0, qs); }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+long long hils_pair_tiles_max(const HilsShape& s, int qs) {
+  const long long TQ = 64 / s.G;
+  const long long pairs = (long long)s.B * s.Hkv * qs * s.K;
+  return (pairs + TQ - 1) / TQ + (long long)s.B * s.Hkv * s.nC;
+}
+
+hipError_t hils_launch_attn_pairs(const HilsShape& s, const void* q, const void* qr, const void* k,
+                                  const void* vt, const void* ksum, const float* bsum,
+                                  const int32_t* sel, void* out, const HilsPairBufs& pb,
+                                  hipStream_t st) {
+  switch (s.G) {
+    case 1: return launch_pairs<1>(s, q, qr, k, vt, ksum, bsum, sel, out, pb, st);
+    case 2: return launch_pairs<2>(s, q, qr, k, vt, ksum, bsum, sel, out, pb, st);
+    case 4: return launch_pairs<4>(s, q, qr, k, vt, ksum, bsum, sel, out, pb, st);
+  }
+  return hipErrorInvalidValue;
+}

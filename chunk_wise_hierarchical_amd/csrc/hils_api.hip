@@ -56,16 +56,24 @@ bool fast_eligible(const HilsShape& s, uint32_t flags) {
   if (s.dtype != HILS_BF16 || s.d != 128 || s.S != 64 || s.K > 64) return false;
   if (!(s.G == 1 || s.G == 2 || s.G == 4)) return false;
   if (s.nC > HILS_FAST_NCMAX) return false;
+  if ((long long)s.B * s.Hkv * s.nC >= (1LL << 25)) return false;   // bucket id in 25 bits
   return true;
+}
+
+inline bool pair_path(const HilsShape& s, uint32_t flags, bool fast) {
+  return fast && !(flags & HILS_FLAG_UNION);
 }
 
 struct PrefillLayout {
   size_t ks, bs, sel, slog, vt, total;
+  // per-chunk bucket path
+  size_t cnt, loff, toff, cur, tot, tinfo, list, lam, swa, lz, part;
+  int qs_max;
 };
 // generic path: summaries, selection, fusion logits; fast path: summaries,
 // selection and the per-chunk transposed V (fusion logits are recomputed in
 // the attention kernel)
-PrefillLayout prefill_layout(const HilsShape& s, bool fast) {
+PrefillLayout prefill_layout(const HilsShape& s, bool fast, bool pairs) {
   PrefillLayout L{};
   size_t off = 0;
   L.ks = off;   off += align_up((size_t)s.B * s.Hq * s.nC * s.d * esize(s));
@@ -74,6 +82,23 @@ PrefillLayout prefill_layout(const HilsShape& s, bool fast) {
   if (fast) {
     L.slog = 0;
     L.vt = off; off += align_up((size_t)s.B * s.Hkv * s.nCc * s.d * s.S * 2);
+    if (pairs) {
+      const int qs = s.N < HILS_PAIR_SLICE ? s.N : HILS_PAIR_SLICE;
+      const size_t F = (size_t)s.B * s.Hkv * s.nC;
+      const size_t P = (size_t)s.B * s.Hkv * qs * s.K;   // pair slots of a slice
+      L.qs_max = qs;
+      L.cnt = off;   off += align_up(F * 4);
+      L.loff = off;  off += align_up(F * 4);
+      L.toff = off;  off += align_up(F * 4);
+      L.cur = off;   off += align_up(F * 4);
+      L.tot = off;   off += align_up(16);
+      L.tinfo = off; off += align_up((size_t)hils_pair_tiles_max(s, qs) * 8);
+      L.list = off;  off += align_up(P * 4);
+      L.lam = off;   off += align_up(P * s.G * 4);
+      L.swa = off;   off += align_up((size_t)s.B * s.Hkv * qs * s.G * s.d * 4);
+      L.lz = off;    off += align_up((size_t)s.B * s.Hkv * qs * s.G * 4);
+      L.part = off;  off += align_up(P * s.G * s.d * 2);
+    }
   } else {
     L.slog = off; off += align_up((size_t)s.B * s.Hq * s.N * s.K * 4);
     L.vt = 0;
@@ -186,7 +211,8 @@ int hils_profile_read(const char** names, float* ms, int cap) {
 size_t hils_workspace_bytes(const hils_cfg* cfg, int is_decode) {
   HilsShape s;
   if (make_shape(cfg, s) != HILS_OK) return 0;
-  return is_decode ? decode_layout(s).total : prefill_layout(s, fast_eligible(s, cfg->flags)).total;
+  return is_decode ? decode_layout(s).total : prefill_layout(s, fast_eligible(s, cfg->flags),
+                                    pair_path(s, cfg->flags, fast_eligible(s, cfg->flags))).total;
 }
 
 hils_status hils_summarize(const hils_cfg* cfg, const void* k, const void* lm_q, int32_t c0,
@@ -219,7 +245,8 @@ hils_status hils_prefill(const hils_cfg* cfg, const void* q, const void* q_route
   const bool fast = fast_eligible(s, cfg->flags);
   if (!fast && s.nmax > HILS_GENERIC_NMAX) return HILS_E_UNSUPPORTED;
   if ((long long)s.B * s.Hkv * s.N >= (1LL << 31)) return HILS_E_UNSUPPORTED;
-  const PrefillLayout L = prefill_layout(s, fast);
+  const bool pairs = pair_path(s, cfg->flags, fast);
+  const PrefillLayout L = prefill_layout(s, fast, pairs);
   if (ws_bytes < L.total || (L.total > 0 && !ws)) return HILS_E_WORKSPACE;
   char* w = static_cast<char*>(ws);
   void* ks = k_sum ? k_sum : (void*)(w + L.ks);
@@ -235,7 +262,21 @@ hils_status hils_prefill(const hils_cfg* cfg, const void* q, const void* q_route
     if (e != hipSuccess) return HILS_E_HIP;
     e = hils_launch_score_fast(s, qr, ks, bs, sl, st);
     if (e != hipSuccess) return HILS_E_HIP;
-    return hip_status(hils_launch_attn_fast(s, q, qr, k, vt, ks, bs, sl, out, st));
+    if (!pairs) return hip_status(hils_launch_attn_fast(s, q, qr, k, vt, ks, bs, sl, out, st));
+    HilsPairBufs pb{};
+    pb.cnt = (uint32_t*)(w + L.cnt);
+    pb.loff = (uint32_t*)(w + L.loff);
+    pb.toff = (uint32_t*)(w + L.toff);
+    pb.cur = (uint32_t*)(w + L.cur);
+    pb.tot = (uint32_t*)(w + L.tot);
+    pb.tinfo = (uint2*)(w + L.tinfo);
+    pb.list = (uint32_t*)(w + L.list);
+    pb.lam = (float*)(w + L.lam);
+    pb.swa = (float*)(w + L.swa);
+    pb.lz = (float*)(w + L.lz);
+    pb.part = (uint16_t*)(w + L.part);
+    pb.qs_max = L.qs_max;
+    return hip_status(hils_launch_attn_pairs(s, q, qr, k, vt, ks, bs, sl, out, pb, st));
   }
   float* slog = (float*)(w + L.slog);
   e = hils_launch_select_generic(s, qr, ks, bs, sl, slog, st);

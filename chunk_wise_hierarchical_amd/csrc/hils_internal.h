@@ -40,6 +40,26 @@ hipError_t hils_launch_attn_fast(const HilsShape& s, const void* q, const void* 
                                  const void* vt, const void* ksum, const float* bsum,
                                  const int32_t* sel, void* out, hipStream_t st);
 size_t hils_fast_score_lds(int G, int K);
+
+// fast_pairs.hip: prefill attention organised by selected chunk.  Buffers of
+// one slice of at most qs_max queries (workspace):
+struct HilsPairBufs {
+  uint32_t *cnt, *loff, *toff, *cur, *tot;  // [B*Hkv*nC] x4, [4]
+  uint2* tinfo;                             // [hils_pair_tiles_max]
+  uint32_t* list;                           // [B*Hkv*qs_max*K]
+  float* lam;                               // [B*Hkv*qs_max*K*G] fusion logits (base 2)
+  float* swa;                               // [B*Hkv*qs_max*G*d] normalised window output
+  float* lz;                                // [B*Hkv*qs_max*G] window log-mass (base 2)
+  uint16_t* part;                           // [B*Hkv*qs_max*K*G*d] bf16 per-chunk outputs
+  int qs_max;
+};
+constexpr int HILS_PAIR_SLICE = 32768;      // queries per slice
+constexpr int HILS_PAIR_TPW = 16;           // tiles per attention workgroup
+long long hils_pair_tiles_max(const HilsShape& s, int qs);
+hipError_t hils_launch_attn_pairs(const HilsShape& s, const void* q, const void* qr, const void* k,
+                                  const void* vt, const void* ksum, const float* bsum,
+                                  const int32_t* sel, void* out, const HilsPairBufs& pb,
+                                  hipStream_t st);
 size_t hils_fast_attn_lds(int G, int K);
 constexpr int HILS_FAST_NCMAX = 16384;   // chunk ids the fast attention bitmap covers
 

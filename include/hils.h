@@ -72,6 +72,9 @@ typedef enum {
 
 /* flags */
 #define HILS_FLAG_GENERIC 1u   /* prefill: force the generic (vector-ALU) kernels */
+#define HILS_FLAG_UNION 2u     /* prefill, MFMA path: attention by query block over the
+                                  union of the block's chunks (section 4.2 of the
+                                  pages) instead of the default per-chunk buckets */
 
 typedef struct hils_cfg {
   int32_t B;      /* batch */

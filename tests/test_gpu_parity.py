@@ -32,14 +32,14 @@ def _gpu_inputs(w, device="cuda", **kw):
     return {k: v.to(device) for k, v in x.items()}
 
 
-def _run_prefill(w, x, mode="surrogate", generic=False):
+def _run_prefill(w, x, mode="surrogate", generic=False, union=False):
     B, Hq, N, d = x["q"].shape
     nC = N // w.S
     ks = torch.empty((B, Hq, nC, d), dtype=x["q"].dtype, device="cuda")
     bs = torch.empty((B, Hq, nC), dtype=torch.float32, device="cuda")
     sel = torch.empty((B, w.Hkv, N, w.K), dtype=torch.int32, device="cuda")
     out = hils.prefill(x["q"], x["k"], x["v"], x["lm"], w.S, w.W, w.K, q_route=x.get("q_route"),
-                       mode=mode, sel=sel, summaries=(ks, bs), generic=generic)
+                       mode=mode, sel=sel, summaries=(ks, bs), generic=generic, union=union)
     torch.cuda.synchronize()
     return out, sel, ks, bs
 
@@ -60,11 +60,12 @@ def _check_summaries(w, ks, bs, ref):
     return nbad
 
 
-def _prefill_case(w, rows=None, mode="surrogate", generic=False, q_route=False, label=""):
+def _prefill_case(w, rows=None, mode="surrogate", generic=False, q_route=False, label="",
+                  union=False):
     _say(f"[prefill] {label} {w.name} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} d={w.d} S={w.S} "
-         f"W={w.W} K={w.K} dtype={w.dtype} mode={mode} generic={generic}")
+         f"W={w.W} K={w.K} dtype={w.dtype} mode={mode} generic={generic} union={union}")
     x = _gpu_inputs(w, with_q_route=q_route)
-    out, sel, ks, bs = _run_prefill(w, x, mode=mode, generic=generic)
+    out, sel, ks, bs = _run_prefill(w, x, mode=mode, generic=generic, union=union)
     xn = {k: np32(v) for k, v in x.items()}
     summ = _oracle_summaries(w, xn, mode)
     nbad = _check_summaries(w, ks, bs, summ)
@@ -125,10 +126,30 @@ def test_prefill_generic_kernels_bf16():
 
 
 def test_prefill_fast_ragged():
-    # fast path (bf16, d=128, S=64) with N not a multiple of 64 and of the query block
-    for G, N in ((2, 3001), (4, 2049), (1, 1500)):
-        w = synth.get_workload("prefill_64k", N=N, Hq=2 * G, Hkv=2, W=200, K=8, regime="mod3")
-        _prefill_case(w, label=f"fast ragged G={G}")
+    # fast path (bf16, d=128, S=64) with N not a multiple of 64 and of the query block,
+    # both attention organisations (per-chunk buckets, query-block unions)
+    for union in (False, True):
+        for G, N in ((2, 3001), (4, 2049), (1, 1500)):
+            w = synth.get_workload("prefill_64k", N=N, Hq=2 * G, Hkv=2, W=200, K=8, regime="mod3")
+            _prefill_case(w, label=f"fast ragged G={G}", union=union)
+
+
+def test_prefill_pairs_across_slices():
+    # more queries than one bucket slice (32768), ragged last slice, q_route
+    w = synth.get_workload("prefill_64k", N=40000, Hq=4, Hkv=1, W=1024, K=32)
+    _prefill_case(w, rows=sample_rows(w, 300, include=[32767, 32768, 39999]), q_route=True,
+                  label="two slices")
+
+
+def test_union_and_pairs_agree():
+    w = synth.get_workload("prefill_64k", N=4096, W=512, K=16)
+    x = _gpu_inputs(w)
+    o1, s1, _, _ = _run_prefill(w, x)
+    o2, s2, _, _ = _run_prefill(w, x, union=True)
+    assert torch.equal(s1, s2)
+    err = (o1.float() - o2.float()).abs().max().item()
+    _say(f"   union/pairs max |out diff| {err:.3g}")
+    assert err < 2e-2
 
 
 def test_fast_and_generic_agree():
