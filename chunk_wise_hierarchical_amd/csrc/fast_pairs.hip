@@ -332,7 +332,7 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 // ---------------------------------------------------------------------------
 // per-chunk attention of the bucketed pairs
 
-template <int G>
+template <int G, bool QR>
 __global__ void __launch_bounds__(NT, 2)
 k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
             const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
@@ -356,16 +356,16 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
   const int colr = 16 * w + (lane & 15);
   const int jr = colr / G, h = colr % G;
   const int lq = lane >> 4;
-  const bool has_qr = qr != nullptr;
 
   // list entry of this lane's row in tile u (rows past the tile's pairs repeat
   // its last pair: loads stay valid, results are not stored)
   auto entry = [&](int u) {
-    const uint2 ti = tl[u];
+    const uint2 ti = tl[min(u, nt - 1)];
     const int mcount = (int)(ti.x & 127u);
     return list[ti.y + min(jr, mcount - 1)];
   };
-  auto qrow = [&](uint32_t ent, int f) {
+  auto qrow = [&](uint32_t ent, int u) {
+    const int f = (int)(tl[min(u, nt - 1)].x >> 7);
     const int bg = f / nC;
     const int b = bg / Hkv, g = bg - b * Hkv;
     return (((long long)b * Hq + (long long)g * G + h) * N + i0 + (int)(ent >> 7)) * D;
@@ -375,29 +375,25 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
     for (int ks = 0; ks < 4; ++ks) r[ks] = ld_bf16x8(src + off + 32 * ks + 8 * lq);
   };
 
-  // two-deep prefetch: entries of tile u+2 and query rows of tile u+1 are in
-  // flight while tile u is computed
-  uint32_t ent_c = entry(0);
-  uint32_t ent_n = entry(min(1, nt - 1));
-  bf16x8_t bq_c[4], bq_n[4], br_c[4], br_n[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    br_c[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
-    br_n[ks] = br_c[ks];
+  // prefetch: list entries three tiles ahead, query rows two tiles ahead
+  uint32_t e0 = entry(0), e1 = entry(1), e2 = entry(2);
+  bf16x8_t bq0[4], bq1[4], bq2[4], br0[4], br1[4], br2[4];
+  load_q(q, qrow(e0, 0), bq0);
+  load_q(q, qrow(e1, 1), bq1);
+  if (QR) {
+    load_q(qr, qrow(e0, 0), br0);
+    load_q(qr, qrow(e1, 1), br1);
   }
-  load_q(q, qrow(ent_c, (int)(tl[0].x >> 7)), bq_c);
-  if (has_qr) load_q(qr, qrow(ent_c, (int)(tl[0].x >> 7)), br_c);
   int cur = -1;
   for (int u = 0; u < nt; ++u) {
     const uint2 ti = tl[u];
     const int f = (int)(ti.x >> 7), mcount = (int)(ti.x & 127u);
     const int bg = f / nC, c = f - bg * nC;
-    const uint32_t ent_nn = entry(min(u + 2, nt - 1));
+    const uint32_t e3 = entry(u + 3);
     {
-      const int un = min(u + 1, nt - 1);
-      const long long off = qrow(ent_n, (int)(tl[un].x >> 7));
-      load_q(q, off, bq_n);
-      if (has_qr) load_q(qr, off, br_n);
+      const long long off = qrow(e2, u + 2);
+      load_q(q, off, bq2);
+      if (QR) load_q(qr, off, br2);
     }
     if (f != cur) {            // stage the chunk's K (swizzled), V^T and the group's k'_c, b'_c
       __syncthreads();
@@ -434,14 +430,14 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
       cur = f;
     }
     const bool valid = jr < mcount;
-    const int qi = (int)(ent_c >> 7), kx = (int)(ent_c & 127u);
+    const int qi = (int)(e0 >> 7), kx = (int)(e0 & 127u);
     const long long prow = ((long long)bg * qs + qi) * K + kx;   // pair index
 
     // fusion logit of the row (base 2): the 4 lanes of a row each hold 32 of
     // its 128 query elements
     float lam;
     {
-      const bf16x8_t* src = has_qr ? br_c : bq_c;
+      const bf16x8_t* src = QR ? br0 : bq0;
       float dp = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -466,7 +462,7 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
       f32x4_t a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        a4 = mfma16(ld_bf16x8(ktile + key * KSTR + kswz(key, 4 * ks + lq) * 8), bq_c[ks], a4);
+        a4 = mfma16(ld_bf16x8(ktile + key * KSTR + kswz(key, 4 * ks + lq) * 8), bq0[ks], a4);
       s4[kt] = a4;
     }
     float mt = -INFINITY;
@@ -515,12 +511,17 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
       }
       if (lq == 0) lamb[prow * G + h] = lam;
     }
-    ent_c = ent_n;
-    ent_n = ent_nn;
+    e0 = e1;
+    e1 = e2;
+    e2 = e3;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bq_c[ks] = bq_n[ks];
-      br_c[ks] = br_n[ks];
+      bq0[ks] = bq1[ks];
+      bq1[ks] = bq2[ks];
+      if (QR) {
+        br0[ks] = br1[ks];
+        br1[ks] = br2[ks];
+      }
     }
   }
 }
@@ -533,29 +534,37 @@ __global__ void __launch_bounds__(NT)
 k_pair_reduce(const float* __restrict__ swa, const float* __restrict__ lz,
               const float* __restrict__ lamb, const bf16_t* __restrict__ part,
               bf16_t* __restrict__ out, int Hq, int Hkv, int N, int W, int K, int i0, int qs) {
-  constexpr int EP = G * D / 2;                 // element pairs of one query
-  constexpr int QPP = NT / EP;                  // queries per pass
+  constexpr int EV = D / 8;                     // 16-byte vectors of a head row
+  constexpr int TPQ = G * EV;                   // threads of one query
+  constexpr int QPP = NT / TPQ;                 // queries per pass
   extern __shared__ float wk[];                 // [RQ*G][K+1]: alpha_c per slot, alpha_swa last
   const int bg = blockIdx.x;
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int tid = threadIdx.x;
   const int q0 = blockIdx.y * RQ;
-  // fusion weights: softmax over {s_hat_c} U {log Z_swa}, one thread per (query, head)
+  // fusion logits of the workgroup's queries into LDS (independent loads)
+  for (int it = tid; it < RQ * G * K; it += NT) {
+    const int kx = it % K, qh = it / K, qq = qh / G, h = qh - qq * G;
+    const int qi = q0 + qq;
+    if (qi < qs && kx < min(K, n_cand((long long)i0 + qi, W, S)))
+      wk[qh * (K + 1) + kx] = lamb[((((long long)bg * qs + qi) * K + kx) * G) + h];
+  }
   for (int it = tid; it < RQ * G; it += NT) {
     const int qq = it / G, h = it - qq * G;
     const int qi = q0 + qq;
+    if (qi < qs) wk[it * (K + 1) + K] = lz[((long long)bg * qs + qi) * G + h];
+  }
+  __syncthreads();
+  // alpha = softmax over {s_hat_c} U {log Z_swa}, one thread per (query, head)
+  for (int it = tid; it < RQ * G; it += NT) {
+    const int qq = it / G;
+    const int qi = q0 + qq;
     if (qi >= qs) continue;
-    const long long i = (long long)i0 + qi;
-    const int kk = min(K, n_cand(i, W, S));
-    const long long row = (long long)bg * qs + qi;
+    const int kk = min(K, n_cand((long long)i0 + qi, W, S));
     float* wr = wk + it * (K + 1);
-    const float lzv = lz[row * G + h];
+    const float lzv = wr[K];
     float M2 = lzv;
-    for (int kx = 0; kx < kk; ++kx) {
-      const float lv = lamb[(row * K + kx) * G + h];
-      wr[kx] = lv;
-      M2 = fmaxf(M2, lv);
-    }
+    for (int kx = 0; kx < kk; ++kx) M2 = fmaxf(M2, wr[kx]);
     float Z = fast_exp2(lzv - M2);
     for (int kx = 0; kx < kk; ++kx) {
       const float e = fast_exp2(wr[kx] - M2);
@@ -567,8 +576,8 @@ k_pair_reduce(const float* __restrict__ swa, const float* __restrict__ lz,
     wr[K] = fast_exp2(lzv - M2) * invZ;
   }
   __syncthreads();
-  const int sub = tid / EP, e2 = tid - sub * EP;
-  const int h = e2 / (D / 2), d = 2 * (e2 - h * (D / 2));
+  const int sub = tid / TPQ, e2 = tid - sub * TPQ;
+  const int h = e2 / EV, d = 8 * (e2 - h * EV);
   for (int qq = sub; qq < RQ; qq += QPP) {
     const int qi = q0 + qq;
     if (qi >= qs) break;
@@ -576,27 +585,32 @@ k_pair_reduce(const float* __restrict__ swa, const float* __restrict__ lz,
     const int kk = min(K, n_cand(i, W, S));
     const long long row = (long long)bg * qs + qi;
     const float* wr = wk + (qq * G + h) * (K + 1);
-    const float2 sv = *reinterpret_cast<const float2*>(swa + (row * G + h) * D + d);
-    float a0 = wr[K] * sv.x, a1 = wr[K] * sv.y;
+    const float* sp = swa + (row * G + h) * D + d;
+    const float4 s0 = *reinterpret_cast<const float4*>(sp);
+    const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
+    const float ws = wr[K];
+    float a[8] = {ws * s0.x, ws * s0.y, ws * s0.z, ws * s0.w, ws * s1.x, ws * s1.y, ws * s1.z, ws * s1.w};
     const bf16_t* pp = part + (row * K * G + h) * D + d;
+    auto add = [&](float wt, uint4 u) {
+      const uint32_t uv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        a[2 * t] = fmaf(wt, __uint_as_float(uv[t] << 16), a[2 * t]);
+        a[2 * t + 1] = fmaf(wt, __uint_as_float(uv[t] & 0xffff0000u), a[2 * t + 1]);
+      }
+    };
     int kx = 0;
     for (; kx + 8 <= kk; kx += 8) {
-      uint32_t uv[8];
+      uint4 uv[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) uv[t] = *reinterpret_cast<const uint32_t*>(pp + (long long)(kx + t) * G * D);
+      for (int t = 0; t < 8; ++t) uv[t] = ld_u4(pp + (long long)(kx + t) * G * D);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        a0 = fmaf(wr[kx + t], __uint_as_float(uv[t] << 16), a0);
-        a1 = fmaf(wr[kx + t], __uint_as_float(uv[t] & 0xffff0000u), a1);
-      }
+      for (int t = 0; t < 8; ++t) add(wr[kx + t], uv[t]);
     }
-    for (; kx < kk; ++kx) {
-      const uint32_t uv = *reinterpret_cast<const uint32_t*>(pp + (long long)kx * G * D);
-      a0 = fmaf(wr[kx], __uint_as_float(uv << 16), a0);
-      a1 = fmaf(wr[kx], __uint_as_float(uv & 0xffff0000u), a1);
-    }
-    *reinterpret_cast<uint32_t*>(out + (((long long)b * Hq + (long long)g * G + h) * N + i) * D + d) =
-        pack_bf16x2(a0, a1);
+    for (; kx < kk; ++kx) add(wr[kx], ld_u4(pp + (long long)kx * G * D));
+    const uint4 o = make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                               pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7]));
+    st_u4(out + (((long long)b * Hq + (long long)g * G + h) * N + i) * D + d, o);
   }
 }
 
@@ -615,7 +629,8 @@ hipError_t launch_pairs(const HilsShape& s, const void* q, const void* qr, const
   hipFuncSetAttribute((const void*)k_pair_count, hipFuncAttributeMaxDynamicSharedMemorySize, (int)hshm);
   hipFuncSetAttribute((const void*)k_pair_scatter, hipFuncAttributeMaxDynamicSharedMemorySize, (int)hshm);
   hipFuncSetAttribute((const void*)k_win_fast<G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)wshm);
-  hipFuncSetAttribute((const void*)k_pair_attn<G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
+  hipFuncSetAttribute((const void*)k_pair_attn<G, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
+  hipFuncSetAttribute((const void*)k_pair_attn<G, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
   hipFuncSetAttribute((const void*)k_pair_reduce<G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rshm);
   const bf16_t* qb = (const bf16_t*)q;
   const bf16_t* qrb = (qr == q) ? nullptr : (const bf16_t*)qr;
@@ -643,7 +658,8 @@ hipError_t launch_pairs(const HilsShape& s, const void* q, const void* qr, const
       const long long tmax = hils_pair_tiles_max(s, qs);
       const unsigned grid = (unsigned)((tmax + PTPW - 1) / PTPW);
       { HilsProfScope ps_("k_pair_attn", st);
-        hipLaunchKernelGGL(k_pair_attn<G>, dim3(grid), dim3(NT), ashm, st, qb, qrb,
+        auto kf = qrb ? k_pair_attn<G, true> : k_pair_attn<G, false>;
+        hipLaunchKernelGGL(kf, dim3(grid), dim3(NT), ashm, st, qb, qrb,
                            (const bf16_t*)k, (const bf16_t*)vt, (const bf16_t*)ksum, bsum, pb.list,
                            pb.tinfo, pb.tot, pb.lam, (bf16_t*)pb.part, s.Hq, s.Hkv, s.N, s.K, s.nC,
                            s.nCc, tau2, i0, qs); }

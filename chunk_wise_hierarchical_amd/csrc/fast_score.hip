@@ -185,7 +185,10 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   const int qsel = (G == 1) ? (32 * w + col) : (w * QW + lane / LQ);
   const int cbase = (G == 1) ? 0 : CL * (lane % LQ);
 
-  // tile staging through registers into a single XOR-swizzled LDS tile
+  // tile staging through registers into a single XOR-swizzled LDS tile.  The
+  // loads are unconditional and kept raw until the store (chunk ids past nC
+  // read chunk nC-1; their scores are masked by the candidate range), so the
+  // next tile's loads stay in flight while the current tile is scored.
   constexpr int PPT = 2 * G;               // 16-byte pieces per thread per tile
   uint4 pre[PPT];
   float bpre = 0.0f;
@@ -194,14 +197,12 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     for (int p = 0; p < PPT; ++p) {
       const int piece = tid + NT * p;
       const int h = piece / (CT * 16), c = (piece / 16) % CT, part = piece % 16;
-      const int cg = CT * t + c;
-      const uint4 v = ld_u4(ksum + ((hb + h) * nC + min(cg, nC - 1)) * (long long)D + part * 8);
-      pre[p] = (cg < nC) ? v : make_uint4(0, 0, 0, 0);
+      const int cg = min(CT * t + c, nC - 1);
+      pre[p] = ld_u4(ksum + ((hb + h) * nC + cg) * (long long)D + part * 8);
     }
-    if (tid < G * CT) {
-      const int h = tid / CT, cg = CT * t + tid % CT;
-      const float bv = bsum[(hb + h) * nC + min(cg, nC - 1)];
-      bpre = (cg < nC) ? bv * LOG2E : 0.0f;
+    {
+      const int h = (tid / CT) % G, cg = min(CT * t + tid % CT, nC - 1);
+      bpre = bsum[(hb + h) * nC + cg];
     }
   };
   auto store_tile = [&]() {
@@ -211,7 +212,7 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
       const int h = piece / (CT * 16), c = (piece / 16) % CT, part = piece % 16;
       st_u4(ktile + ((size_t)h * CT + c) * D + ((part ^ (c & 15)) * 8), pre[p]);
     }
-    if (tid < G * CT) btile[tid] = bpre;
+    if (tid < G * CT) btile[tid] = bpre * LOG2E;
   };
 
   // merge query q's staging list into its sorted top-K list (whole wavefront)
@@ -271,7 +272,7 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     store_tile();
     __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
-      if (t + 1 < ntiles) load_tile(t + 1);
+      load_tile(min(t + 1, ntiles - 1));
       float x[16];
       tile_scores(t, x);
       if (pass == 0) {
@@ -337,7 +338,7 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
         }
         __syncthreads();
       }
-      if (t + 1 < ntiles) store_tile();
+      store_tile();            // past the last tile: rewrites the last tile, unused
       __syncthreads();
     }
     if (pass == 0) {
