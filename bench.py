@@ -54,6 +54,14 @@ def prefill_work(w):
     return score, summ, attn
 
 
+def window_work(w):
+    """Algorithmic FLOPs of the attention split into (window part, selected-chunk part)."""
+    n, win = _geometry(w.N, w.W, w.S)
+    win_f = 4.0 * w.d * float(win.sum()) * w.Hq * w.B
+    sel_f = 4.0 * w.d * float((np.minimum(w.K, n) * w.S).sum()) * w.Hq * w.B
+    return win_f, sel_f
+
+
 def decode_work(w, T):
     """Algorithmic HBM bytes of one decode step (all sequences at length T), and the
     bytes of the summary-scoring kernel alone (k', b' read, scores written)."""
@@ -70,6 +78,9 @@ def decode_work(w, T):
 KERNEL_SOURCES = {
     "k_attn_fast": ["fast_attn.hip", "fast_common.h", "hils_device.h"],
     "k_score_fast": ["fast_score.hip", "fast_common.h", "hils_device.h"],
+    "k_pair_attn": ["fast_pairs.hip", "fast_common.h", "hils_device.h", "hils_internal.h"],
+    "k_pair_reduce": ["fast_pairs.hip", "fast_common.h", "hils_device.h", "hils_internal.h"],
+    "k_win_fast": ["fast_pairs.hip", "fast_common.h", "hils_device.h", "hils_internal.h"],
     "k_dec_score": ["decode.hip", "hils_device.h", "hils_internal.h"],
 }
 
@@ -201,7 +212,7 @@ def main():
                     help="run a plain 1 GiB copy first (counter scale for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only; the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
         sys.exit(2)
 
@@ -253,8 +264,10 @@ def main():
 
     score_f, summ_f, attn_f = prefill_work(w)
     dom = max(kern, key=lambda k2: kern[k2]["ms_per_step"])
+    win_f, sel_f = window_work(w)
     dom_flops = {"k_attn_fast": attn_f, "k_attn_generic": attn_f, "k_score_fast": score_f,
-                 "k_select_generic": score_f, "k_summarize": summ_f}.get(dom, attn_f)
+                 "k_select_generic": score_f, "k_summarize": summ_f, "k_win_fast": win_f,
+                 "k_pair_attn": sel_f}.get(dom, attn_f)
     achieved = dom_flops / (kern[dom]["avg_ms"] * 1e-3) / 1e12
     roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,

@@ -17,7 +17,7 @@ Notation (0-based tokens and chunks):
   window = [max(0,l(i)), i].
 GQA: q heads h = g*G + r share KV head g (G = Hq/Hkv).
 
-Readings of points the paper leaves open (each is listed in the design doc):
+Readings of points the paper leaves open:
   * chunks/tokens are 0-based; l(i) uses floor division (negative numerators
     round toward -inf); C_i is empty when l(i) <= 0 and the window starts at 0;
   * |C_i| < K selects all of C_i; equal scores rank the lower chunk id first;
