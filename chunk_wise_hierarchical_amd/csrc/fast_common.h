@@ -60,6 +60,40 @@ __device__ __forceinline__ float sum_x32(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Value of lane l ^ stride within the wavefront, for stride in {1,...,32}
+// (a compile-time constant after unrolling).  Strides 1-8 use DPP row
+// patterns (quad_perm, row_half_mirror, row_mirror), 16 and 32 the row-swap
+// instructions: VALU only, no LDS round trip.
+__device__ __forceinline__ uint32_t xshfl(uint32_t v, int stride) {
+  if (stride == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+  if (stride == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+  if (stride == 4) {
+    const int t = __builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp(t, 0x1B, 0xF, 0xF, false);
+  }
+  if (stride == 8) {
+    const int t = __builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp(t, 0x141, 0xF, 0xF, false);
+  }
+  if (stride == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ float xshfl_f(float v, int stride) {
+  return __uint_as_float(xshfl(__float_as_uint(v), stride));
+}
+__device__ __forceinline__ uint64_t xshfl_u64(uint64_t v, int stride) {
+  return ((uint64_t)xshfl((uint32_t)(v >> 32), stride) << 32) | xshfl((uint32_t)v, stride);
+}
+// value of lane 63 - l (= l ^ 63)
+__device__ __forceinline__ uint32_t lane_reverse(uint32_t v) {
+  const uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);   // l ^ 15
+  return xshfl(xshfl(t, 16), 32);
+}
+
 // 64-bit shuffle
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   const uint32_t lo = __shfl_xor((uint32_t)v, m, 64);

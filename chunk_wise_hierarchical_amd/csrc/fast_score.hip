@@ -33,7 +33,7 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int CT = 32;         // chunks per tile
-constexpr int XROW = CT + 1;   // row of the cross-head exchange buffer (floats)
+constexpr int XROW = CT + 4;   // row of the cross-head exchange buffer (floats, 16-byte rows)
 constexpr int STG = 48;        // staging slots per query
 constexpr int STG_MERGE = 16;  // merge when more than this many keys are staged
 
@@ -45,11 +45,13 @@ struct Geo {
   static constexpr int CL = CT / LQ;      // chunks per lane per tile (selection layout)
 };
 
-// ktile..stg is also the scratch of the tracked scores between the passes
-// (G*QB = 128 (query, head) pairs x 64 floats = 32 KB, which always fits).
+// [0, 32 KB) is also the scratch of the tracked scores between the passes
+// (G*QB = 128 (query, head) pairs x 64 floats); it covers ktile and, for small
+// layouts, lst and stg, which are idle then.  tq and everything after it
+// always start past 32 KB.
 template <int G>
 struct Lds {
-  size_t ktile, btile, xb, lst, stg, tq, tk, cnt, thr, total;
+  size_t ktile, btile, xb, lst, stg, tq, thf, tk, cnt, thr, total;
   __host__ __device__ Lds(int K) {
     size_t o = 0;
     ktile = o; o += (size_t)G * CT * D * 2;            // swizzled, no padding
@@ -59,7 +61,15 @@ struct Lds {
     lst = o;   o += (size_t)Geo<G>::QB * K * 8;
     stg = o;   o += (size_t)Geo<G>::QB * STG * 8;
     tq = o;    o += (size_t)G * Geo<G>::QB * 4;
-    tk = o;    o += (size_t)G * Geo<G>::QB * 4;
+    thf = o;   o += (size_t)Geo<G>::QB * 4;
+    // tk lives between the passes only: it may share the idle staging array
+    // when that starts past the tracked-score scratch [0, 32 KB); otherwise
+    // (G = 1 with a small K) it needs room of its own
+    if (stg >= (size_t)G * Geo<G>::QB * 64 * 4) {
+      tk = stg;
+    } else {
+      tk = o;  o += (size_t)G * Geo<G>::QB * 4;
+    }
     cnt = o;   o += (size_t)Geo<G>::QB * 2 * 4;
     o = (o + 15) & ~(size_t)15;
     thr = o;   o += (size_t)Geo<G>::QB * 8;
@@ -76,7 +86,7 @@ __device__ __forceinline__ uint64_t sort64_desc(uint64_t v, int lane) {
   for (int size = 2; size <= 64; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint64_t p = shfl_xor_u64(v, stride);
+      const uint64_t p = xshfl_u64(v, stride);
       const bool lower = (lane & stride) == 0;
       const bool desc = (lane & size) == 0 || size == 64;
       v = (lower == desc) ? umax64(v, p) : umin64(v, p);
@@ -87,13 +97,13 @@ __device__ __forceinline__ uint64_t sort64_desc(uint64_t v, int lane) {
 
 // a, b descending across the wavefront -> the 64 largest of a U b, descending
 __device__ __forceinline__ uint64_t merge_top64(uint64_t a, uint64_t b, int lane) {
-  const uint32_t lo = __shfl((uint32_t)b, 63 - lane, 64);
-  const uint32_t hi = __shfl((uint32_t)(b >> 32), 63 - lane, 64);
+  const uint32_t lo = lane_reverse((uint32_t)b);
+  const uint32_t hi = lane_reverse((uint32_t)(b >> 32));
   const uint64_t br = ((uint64_t)hi << 32) | lo;          // b reversed: ascending
   uint64_t v = umax64(a, br);                              // top half of the bitonic sequence
 #pragma unroll
   for (int stride = 32; stride > 0; stride >>= 1) {
-    const uint64_t p = shfl_xor_u64(v, stride);
+    const uint64_t p = xshfl_u64(v, stride);
     v = ((lane & stride) == 0) ? umax64(v, p) : umin64(v, p);
   }
   return v;
@@ -105,7 +115,7 @@ __device__ __forceinline__ float sort64_desc_f(float v, int lane) {
   for (int size = 2; size <= 64; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const float p = __shfl_xor(v, stride, 64);
+      const float p = xshfl_f(v, stride);
       const bool lower = (lane & stride) == 0;
       const bool desc = (lane & size) == 0 || size == 64;
       v = (lower == desc) ? fmaxf(v, p) : fminf(v, p);
@@ -120,7 +130,7 @@ __device__ __forceinline__ int sort64_asc(int v, int lane) {
   for (int size = 2; size <= 64; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int p = __shfl_xor(v, stride, 64);
+      const int p = (int)xshfl((uint32_t)v, stride);
       const bool lower = (lane & stride) == 0;
       const bool asc = (lane & size) == 0;
       v = (lower == asc) ? min(v, p) : max(v, p);
@@ -149,6 +159,7 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   uint32_t* cnt_stg = reinterpret_cast<uint32_t*>(sm + L.cnt);
   uint32_t* cnt_lst = cnt_stg + QB;
   uint64_t* thr = reinterpret_cast<uint64_t*>(sm + L.thr);
+  float* thf = reinterpret_cast<float*>(sm + L.thf);        // [QB] thr as a float (prefilter)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int blk = blockIdx.x;
@@ -223,25 +234,34 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     sb = sort64_desc(sb, lane);
     const uint64_t v = merge_top64(a, sb, lane);
     const int tot = min(K, nl + ns);
-    const uint32_t klo = __shfl((uint32_t)v, K - 1, 64);
-    const uint32_t khi = __shfl((uint32_t)(v >> 32), K - 1, 64);
+    const uint32_t klo = __builtin_amdgcn_readlane((uint32_t)v, K - 1);
+    const uint32_t khi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), K - 1);
     if (lane < K) lst[(size_t)q * K + lane] = (lane < tot) ? v : 0ull;
     if (lane == 0) {
       cnt_lst[q] = tot;
       cnt_stg[q] = 0;
-      if (tot >= K) thr[q] = umax64(thr[q], ((uint64_t)khi << 32) | klo);
+      if (tot >= K) {
+        const uint64_t nt = umax64(thr[q], ((uint64_t)khi << 32) | klo);
+        thr[q] = nt;
+        thf[q] = order_key_f32((uint32_t)(nt >> 32));
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   };
 
   // scores of tile t for this lane (base 2): x[i] <-> chunk 32t + 8(i>>2) + 4*half + (i&3)
   const int n_lo = n_cand(i0, W, S);                 // every query of the block has >= n_lo
-  auto tile_scores = [&](int t, float* x) {
+  // ainit seeds the accumulator (every value of a lane belongs to one query):
+  // pass 1 starts it at -L / scale, which folds the head's log-sum-exp into
+  // the score without a separate subtraction
+  auto tile_scores = [&](int t, float* x, float ainit) {
     const bf16_t* kb = ktile + ((size_t)hw * CT + col) * D;
     bf16x8_t a[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) a[ks] = ld_bf16x8(kb + (((2 * ks + half) ^ (col & 15)) * 8));
-    f32x16_t acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    f32x16_t acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = ainit;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) acc = mfma32(a[ks], bq[ks], acc);
     const float* bt = btile + (size_t)hw * CT;
@@ -271,10 +291,13 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     load_tile(0);
     store_tile();
     __syncthreads();
+    // pass 1 accumulator seed: -L / scale (L = +inf/-inf only for rows without
+    // candidates, whose scores are all masked)
+    const float ainit = (pass == 1 && G > 1) ? -L2 / tau2 : 0.0f;
     for (int t = 0; t < ntiles; ++t) {
       load_tile(min(t + 1, ntiles - 1));
       float x[16];
-      tile_scores(t, x);
+      tile_scores(t, x, ainit);
       if (pass == 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -292,21 +315,31 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
           }
         }
         __syncthreads();
+        store_tile();            // past the last tile: rewrites the last tile, unused
+        __syncthreads();
       } else {
+        // group scores: x already holds s_h - L_h; the heads of a group meet in LDS
+        if (G > 1) {
+          float* xr = xb + ((size_t)hw * QB + 32 * qw + col) * XROW + 4 * half;
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq)
+            *reinterpret_cast<float4*>(xr + 8 * gq) =
+                make_float4(x[4 * gq], x[4 * gq + 1], x[4 * gq + 2], x[4 * gq + 3]);
+        }
+        __syncthreads();         // exchange written; every wave is done reading the k' tile
+        store_tile();            // next tile (past the last: rewrites the last, unused)
         float gs[CL];
         int cid0;
         if (G > 1) {
-          float* xr = xb + ((size_t)hw * QB + 32 * qw + col) * XROW;
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            xr[8 * (i >> 2) + 4 * half + (i & 3)] = (x[i] == -INFINITY) ? -INFINITY : x[i] - L2;
-          __syncthreads();
+          for (int j4 = 0; j4 < CL; j4 += 4) {
+            float4 mx = *reinterpret_cast<const float4*>(xb + (size_t)qsel * XROW + cbase + j4);
 #pragma unroll
-          for (int j = 0; j < CL; ++j) {
-            float mx = xb[((size_t)0 * QB + qsel) * XROW + cbase + j];
-#pragma unroll
-            for (int h = 1; h < G; ++h) mx = fmaxf(mx, xb[((size_t)h * QB + qsel) * XROW + cbase + j]);
-            gs[j] = mx;
+            for (int h = 1; h < G; ++h) {
+              const float4 y = *reinterpret_cast<const float4*>(xb + ((size_t)h * QB + qsel) * XROW + cbase + j4);
+              mx = make_float4(fmaxf(mx.x, y.x), fmaxf(mx.y, y.y), fmaxf(mx.z, y.z), fmaxf(mx.w, y.w));
+            }
+            gs[j4] = mx.x; gs[j4 + 1] = mx.y; gs[j4 + 2] = mx.z; gs[j4 + 3] = mx.w;
           }
           cid0 = CT * t + cbase;
         } else {
@@ -314,16 +347,20 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
           for (int i = 0; i < CL; ++i) gs[i] = x[i];
           cid0 = CT * t;
         }
-        // filter against the query's current K-th best key and stage the survivors
+        // filter against the query's current K-th best key (float prefilter, then
+        // the exact 64-bit key) and stage the survivors
+        const float tf = thf[qsel];
         const uint64_t th = thr[qsel];
 #pragma unroll
         for (int j = 0; j < CL; ++j) {
-          const int cid = (G == 1) ? (cid0 + 8 * (j >> 2) + 4 * half + (j & 3)) : (cid0 + j);
-          const uint64_t key = ((uint64_t)f32_order_key(gs[j]) << 32) |
-                               (uint64_t)(0xffffffffu - (uint32_t)cid);
-          if (gs[j] != -INFINITY && key > th) {
-            const uint32_t slot = atomicAdd(&cnt_stg[qsel], 1u);
-            stg[(size_t)qsel * STG + slot] = key;
+          if (gs[j] != -INFINITY && gs[j] >= tf) {
+            const int cid = (G == 1) ? (cid0 + 8 * (j >> 2) + 4 * half + (j & 3)) : (cid0 + j);
+            const uint64_t key = ((uint64_t)f32_order_key(gs[j]) << 32) |
+                                 (uint64_t)(0xffffffffu - (uint32_t)cid);
+            if (key > th) {
+              const uint32_t slot = atomicAdd(&cnt_stg[qsel], 1u);
+              stg[(size_t)qsel * STG + slot] = key;
+            }
           }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -336,10 +373,8 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
             merge((G == 1) ? (32 * w + l) : (w * QW + l / LQ));
           }
         }
-        __syncthreads();
+        __syncthreads();         // next k' tile visible; exchange reads done
       }
-      store_tile();            // past the last tile: rewrites the last tile, unused
-      __syncthreads();
     }
     if (pass == 0) {
       // per (query, head): log-sum-exp, and the K-th largest of the 64 tracked
@@ -373,7 +408,12 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
           const float kh = tk[(size_t)h * QB + t];
           if (kh != -INFINITY) T = fmaxf(T, (G > 1) ? kh - tq[(size_t)h * QB + t] : kh);
         }
-        thr[t] = (T == -INFINITY) ? 0ull : ((uint64_t)f32_order_key(T) << 32);
+        // pass 1 computes s_h - L_h with L folded into the accumulator, which
+        // rounds differently from pass 0: lower the bound by a margin far
+        // above that rounding so no chunk at the bound is lost
+        const float Tm = (T == -INFINITY) ? -INFINITY : T - (1e-3f + 1e-6f * fabsf(T));
+        thr[t] = (Tm == -INFINITY) ? 0ull : ((uint64_t)f32_order_key(Tm) << 32);
+        thf[t] = Tm;
       }
       __syncthreads();
     }

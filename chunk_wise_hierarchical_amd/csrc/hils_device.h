@@ -95,6 +95,11 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// inverse of f32_order_key
+__device__ __forceinline__ float order_key_f32(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // float -> uint32 key whose unsigned order is the float order (-0 mapped to +0).
 __device__ __forceinline__ uint32_t f32_order_key(float f) {
   if (f == 0.0f) f = 0.0f;
