@@ -24,6 +24,8 @@
 // Keys are 64-bit: (order-preserving bits of g) << 32 | (~chunk id), so ties
 // rank the lower chunk id first and every key is unique.  The selected ids
 // are written ascending, -1 padded.
+#include <type_traits>
+
 #include "fast_common.h"
 #include "hils_internal.h"
 
@@ -254,16 +256,14 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   // ainit seeds the accumulator (every value of a lane belongs to one query):
   // pass 1 starts it at -L / scale, which folds the head's log-sum-exp into
   // the score without a separate subtraction
-  auto tile_scores = [&](int t, float* x, float ainit) {
+  auto tile_scores = [&](int t, float* x, const f32x16_t& aseed) {
     const bf16_t* kb = ktile + ((size_t)hw * CT + col) * D;
     bf16x8_t a[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) a[ks] = ld_bf16x8(kb + (((2 * ks + half) ^ (col & 15)) * 8));
-    f32x16_t acc;
+    f32x16_t acc = mfma32(a[0], bq[0], aseed);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = ainit;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) acc = mfma32(a[ks], bq[ks], acc);
+    for (int ks = 1; ks < 8; ++ks) acc = mfma32(a[ks], bq[ks], acc);
     const float* bt = btile + (size_t)hw * CT;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
@@ -283,7 +283,10 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   };
 
   float L2 = 0.0f;
-  for (int pass = 0; pass < 2; ++pass) {
+  // the two passes are separate instantiations, so pass 1 does not keep
+  // pass 0's trackers live
+  auto run_pass = [&](auto pass_tag) {
+    constexpr int pass = decltype(pass_tag)::value;
     float m = -INFINITY, ssum = 0.0f;
     float ta[16], tb[16];                  // top-2 per register slot (pass 0)
 #pragma unroll
@@ -294,11 +297,14 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     // pass 1 accumulator seed: -L / scale (L = +inf/-inf only for rows without
     // candidates, whose scores are all masked)
     const float ainit = (pass == 1 && G > 1) ? -L2 / tau2 : 0.0f;
+    f32x16_t aseed;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) aseed[i] = ainit;
     for (int t = 0; t < ntiles; ++t) {
       load_tile(min(t + 1, ntiles - 1));
       float x[16];
-      tile_scores(t, x, ainit);
-      if (pass == 0) {
+      tile_scores(t, x, aseed);
+      if constexpr (pass == 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           tb[i] = fmaxf(tb[i], fminf(ta[i], x[i]));
@@ -376,7 +382,7 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
         __syncthreads();         // next k' tile visible; exchange reads done
       }
     }
-    if (pass == 0) {
+    if constexpr (pass == 0) {
       // per (query, head): log-sum-exp, and the K-th largest of the 64 tracked
       // scores (a lower bound on the head's K-th best score)
       const int pr = hw * QB + 32 * qw + col;        // (head, query) pair of this lane
@@ -417,7 +423,9 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
       }
       __syncthreads();
     }
-  }
+  };
+  run_pass(std::integral_constant<int, 0>{});
+  run_pass(std::integral_constant<int, 1>{});
 
   // final merge, ascending ids, write the selection
   for (int qq = 0; qq < QW; ++qq) {
