@@ -502,12 +502,17 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
                          pb[kb], acc[dt]);
     }
     if (valid) {
+      // stored in the MFMA output order: 16-byte piece 4j + lq holds elements
+      // 32j + 4lq + {0..3} and 32j + 16 + 4lq + {0..3}, so each lane writes
+      // 16 bytes and the 4 lanes of a row write 64 contiguous bytes
       bf16_t* op = part + (prow * G + h) * D;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const uint2 uu = make_uint2(pack_bf16x2(acc[dt][0], acc[dt][1]),
-                                    pack_bf16x2(acc[dt][2], acc[dt][3]));
-        *reinterpret_cast<uint2*>(op + 16 * dt + 4 * lq) = uu;
+      for (int j = 0; j < 4; ++j) {
+        const uint4 uu = make_uint4(pack_bf16x2(acc[2 * j][0], acc[2 * j][1]),
+                                    pack_bf16x2(acc[2 * j][2], acc[2 * j][3]),
+                                    pack_bf16x2(acc[2 * j + 1][0], acc[2 * j + 1][1]),
+                                    pack_bf16x2(acc[2 * j + 1][2], acc[2 * j + 1][3]));
+        st_u4(op + 8 * (4 * j + lq), uu);
       }
       if (lq == 0) lamb[prow * G + h] = lam;
     }
@@ -577,7 +582,8 @@ k_pair_reduce(const float* __restrict__ swa, const float* __restrict__ lz,
   }
   __syncthreads();
   const int sub = tid / TPQ, e2 = tid - sub * TPQ;
-  const int h = e2 / EV, d = 8 * (e2 - h * EV);
+  const int h = e2 / EV, pv = e2 - h * EV;            // 16-byte piece of the stored order
+  const int d0 = 32 * (pv >> 2) + 4 * (pv & 3);       // its elements: d0 + {0..3}, d0 + 16 + {0..3}
   for (int qq = sub; qq < RQ; qq += QPP) {
     const int qi = q0 + qq;
     if (qi >= qs) break;
@@ -585,12 +591,12 @@ k_pair_reduce(const float* __restrict__ swa, const float* __restrict__ lz,
     const int kk = min(K, n_cand(i, W, S));
     const long long row = (long long)bg * qs + qi;
     const float* wr = wk + (qq * G + h) * (K + 1);
-    const float* sp = swa + (row * G + h) * D + d;
-    const float4 s0 = *reinterpret_cast<const float4*>(sp);
-    const float4 s1 = *reinterpret_cast<const float4*>(sp + 4);
+    const float* sp = swa + (row * G + h) * D;
+    const float4 s0 = *reinterpret_cast<const float4*>(sp + d0);
+    const float4 s1 = *reinterpret_cast<const float4*>(sp + d0 + 16);
     const float ws = wr[K];
     float a[8] = {ws * s0.x, ws * s0.y, ws * s0.z, ws * s0.w, ws * s1.x, ws * s1.y, ws * s1.z, ws * s1.w};
-    const bf16_t* pp = part + (row * K * G + h) * D + d;
+    const bf16_t* pp = part + (row * K * G + h) * D + 8 * pv;
     auto add = [&](float wt, uint4 u) {
       const uint32_t uv[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -608,9 +614,9 @@ k_pair_reduce(const float* __restrict__ swa, const float* __restrict__ lz,
       for (int t = 0; t < 8; ++t) add(wr[kx + t], uv[t]);
     }
     for (; kx < kk; ++kx) add(wr[kx], ld_u4(pp + (long long)kx * G * D));
-    const uint4 o = make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
-                               pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7]));
-    st_u4(out + (((long long)b * Hq + (long long)g * G + h) * N + i) * D + d, o);
+    bf16_t* op = out + (((long long)b * Hq + (long long)g * G + h) * N + i) * D;
+    *reinterpret_cast<uint2*>(op + d0) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+    *reinterpret_cast<uint2*>(op + d0 + 16) = make_uint2(pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7]));
   }
 }
 
