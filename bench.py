@@ -210,6 +210,73 @@ def cpu_baseline_decode(xd, wd, nseq=16):
                        f"{t_step:.2f} s; NumPy float64, 1 BLAS thread")}
 
 
+def paged_decode_bench(torch, hils, _lib, xd, wd, ks, bs, steps, log):
+    """Decode over a paged copy of the cache: pages hold one chunk each and are
+    placed by a random permutation; the page summaries are built with
+    hils_summarize_paged.  Times the step eagerly and as a replayed graph."""
+    B, Hkv, T, d = xd["k"].shape
+    S = wd.S
+    maxp = T // S
+    P = B * maxp
+    dev = xd["k"].device
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(5)).to(dev)
+    table = perm.view(B, maxp).to(torch.int32).contiguous()
+
+    def paged(t, heads):                       # [B,H,T,d] -> [P,H,S,d] at the permuted slots
+        lg = t.view(B, heads, maxp, S, d).permute(0, 2, 1, 3, 4).reshape(P, heads, S, d)
+        out = torch.empty_like(lg)
+        out[perm] = lg
+        return out
+
+    kp, vp = paged(xd["k"], Hkv), paged(xd["v"], Hkv)
+    lmp = torch.empty((P, wd.Hq, d), dtype=xd["lm"].dtype, device=dev)
+    lmp[perm] = xd["lm"].permute(0, 2, 1, 3).reshape(P, wd.Hq, d)
+    ksp, bsp = hils.summarize_paged(kp, lmp, perm.to(torch.int32), S, T)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ksp[perm].view(B, maxp, wd.Hq, d).permute(0, 2, 1, 3), ks))
+    out = torch.empty_like(xd["q"])
+    sel = torch.empty((B, Hkv, wd.K), dtype=torch.int32, device=dev)
+    cfg = hils.make_cfg(B, T, wd.Hq, Hkv, d, S, wd.W, wd.K, xd["q"].dtype)
+    ws = torch.empty(max(1, hils.workspace_bytes(cfg, True)), dtype=torch.uint8, device=dev)
+
+    def step():
+        hils.decode_paged(xd["q"], kp, vp, table, xd["seqlen"], ksp, bsp, S, wd.W, wd.K,
+                          out=out, sel=sel, ws=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / steps
+    log(f"paged decode {eager_ms:.3f} ms/step eager, {graph_ms:.3f} ms/step graph replay "
+        f"({P} pages; page summaries identical to contiguous: {same})")
+    del kp, vp, lmp, ksp, bsp, ws, graph
+    return {"pages": P, "page_tokens": S, "ms_per_step": eager_ms, "steps_per_s": 1000.0 / eager_ms,
+            "graph_ms_per_step": graph_ms, "graph_steps_per_s": 1000.0 / graph_ms,
+            "page_summaries_identical": same}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -342,6 +409,9 @@ def main():
                             "traffic": counter_traffic("k_dec_score", wd.name),
                             "algorithmic_bytes_per_launch": score_bytes},
                "kernels": dk}
+        # the same step over a paged cache (one chunk per page, pages randomly
+        # placed), eagerly and replayed from a captured HIP graph
+        dec["paged"] = paged_decode_bench(torch, hils, _lib, xd, wd, ks, bs, args.decode_steps, log)
         if not args.no_cpu:
             log("oracle baseline (decode sample)")
             dec["cpu_baseline"] = cpu_baseline_decode(xd, wd)

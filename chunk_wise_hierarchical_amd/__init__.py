@@ -3,7 +3,9 @@
 The computation lives in libhils.so (hand-written HIP kernels behind the C ABI
 of include/hils.h); this package only marshals torch tensors into that ABI.
 """
-from .api import decode, make_cfg, prefill, summarize, workspace_bytes  # noqa: F401
+from .api import (decode, decode_paged, make_cfg, prefill, summarize, summarize_paged,  # noqa: F401
+                  workspace_bytes)
 from ._lib import HilsError, LIB_PATH  # noqa: F401
 
-__all__ = ["prefill", "decode", "summarize", "workspace_bytes", "make_cfg", "HilsError", "LIB_PATH"]
+__all__ = ["prefill", "decode", "decode_paged", "summarize", "summarize_paged", "workspace_bytes",
+           "make_cfg", "HilsError", "LIB_PATH"]

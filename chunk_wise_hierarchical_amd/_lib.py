@@ -18,6 +18,7 @@ HILS_FLAG_GENERIC = 1
 HILS_FLAG_UNION = 2
 
 EXPORTED = ("hils_workspace_bytes", "hils_summarize", "hils_prefill", "hils_decode",
+            "hils_summarize_paged", "hils_decode_paged",
             "hils_strerror", "hils_abi_version", "hils_profile_enable", "hils_profile_read")
 
 
@@ -56,6 +57,11 @@ def lib() -> ctypes.CDLL:
         L.hils_prefill.restype = ctypes.c_int
         L.hils_decode.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.hils_decode.restype = ctypes.c_int
+        L.hils_summarize_paged.argtypes = [cfgp, vp, vp, vp, i32, i32, vp, vp, vp]
+        L.hils_summarize_paged.restype = ctypes.c_int
+        L.hils_decode_paged.argtypes = [cfgp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp,
+                                        sz, vp]
+        L.hils_decode_paged.restype = ctypes.c_int
         L.hils_strerror.argtypes = [ctypes.c_int]
         L.hils_strerror.restype = ctypes.c_char_p
         L.hils_abi_version.argtypes = []

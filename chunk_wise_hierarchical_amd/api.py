@@ -135,3 +135,58 @@ def decode(q, k_cache, v_cache, seqlen, k_sum, b_sum, S, W, K, q_route=None, mod
                                 _ptr(sel), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
     check(st, "hils_decode")
     return out
+
+
+def summarize_paged(k_pages, lm_pages, pages, S, N, out=None, mode="surrogate", scale=0.0):
+    """Summaries of the pages listed in `pages` (int32 device tensor) of a paged
+    cache: k_pages [P,Hkv,S,d], lm_pages [P,Hq,d].  Returns (k_sum_pages [P,Hq,d],
+    b_sum_pages [P,Hq]); `out` reuses existing page-summary tensors."""
+    P, Hkv, S_, d = k_pages.shape
+    Hq = lm_pages.shape[1]
+    if S_ != S:
+        raise ValueError(f"k_pages page size {S_} != S={S}")
+    dev = k_pages.device
+    _check_tensor(k_pages, "k_pages", None, dev)
+    _check_tensor(lm_pages, "lm_pages", k_pages.dtype, dev)
+    _check_tensor(pages, "pages", torch.int32, dev)
+    if out is None:
+        out = (torch.empty((P, Hq, d), dtype=k_pages.dtype, device=dev),
+               torch.empty((P, Hq), dtype=torch.float32, device=dev))
+    ks, bs = out
+    _check_tensor(ks, "k_sum_pages", k_pages.dtype, dev)
+    _check_tensor(bs, "b_sum_pages", torch.float32, dev)
+    cfg = make_cfg(1, N, Hq, Hkv, d, S, 1, 1, k_pages.dtype, mode, scale)
+    st = _lib.lib().hils_summarize_paged(ctypes.byref(cfg), _ptr(k_pages), _ptr(lm_pages),
+                                         _ptr(pages), int(pages.numel()), P, _ptr(ks), _ptr(bs),
+                                         _stream(dev))
+    check(st, "hils_summarize_paged")
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, page_table, seqlen, k_sum_pages, b_sum_pages, S, W, K,
+                 q_route=None, mode="surrogate", scale=0.0, out=None, sel=None, ws=None):
+    """HiLS single-step decode over a paged cache (one chunk per page).
+    q [B,Hq,1,d]; k_pages/v_pages [P,Hkv,S,d]; page_table [B,max_pages] int32;
+    seqlen [B] int32; k_sum_pages [P,Hq,d]; b_sum_pages [P,Hq].  Returns out."""
+    B, Hq, _, d = q.shape
+    P, Hkv = k_pages.shape[0], k_pages.shape[1]
+    maxp = page_table.shape[1]
+    dev = q.device
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
+                    ("k_sum_pages", k_sum_pages), ("q_route", q_route)):
+        _check_tensor(t, name, q.dtype, dev)
+    _check_tensor(page_table, "page_table", torch.int32, dev)
+    _check_tensor(seqlen, "seqlen", torch.int32, dev)
+    _check_tensor(b_sum_pages, "b_sum_pages", torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor(out, "out", q.dtype, dev)
+    _check_tensor(sel, "sel", torch.int32, dev)
+    cfg = make_cfg(B, maxp * S, Hq, Hkv, d, S, W, K, q.dtype, mode, scale)
+    ws, need = _workspace(cfg, True, dev, ws)
+    st = _lib.lib().hils_decode_paged(ctypes.byref(cfg), _ptr(q), _ptr(q_route), _ptr(k_pages),
+                                      _ptr(v_pages), P, _ptr(page_table), maxp, _ptr(seqlen),
+                                      _ptr(k_sum_pages), _ptr(b_sum_pages), _ptr(out), _ptr(sel),
+                                      _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+    check(st, "hils_decode_paged")
+    return out

@@ -44,26 +44,54 @@ constexpr int SC_CPB = HILS_DEC_SCORE_ROWS;   // chunks per scoring workgroup: 1
 // group so lane u ends with row u, and the workgroup also emits the
 // (max, sum exp) partial of its scores for the per-head log-sum-exp.
 // Requires d % Vec::N == 0 (checked on the host).
-template <typename T>
+// Paged summary cache (PAGED): row (b, h, c) lives at physical page
+// table[b * maxp + c] ([page][Hq][d] and [page][Hq]); page ids are clamped into
+// [0, npages) so any table content stays in bounds.
+struct PageMap {
+  const int32_t* table;
+  int maxp, npages;
+  __device__ __forceinline__ long long page(int b, long long c) const {
+    const int p = table[(long long)b * maxp + c];
+    return (long long)min(max(p, 0), npages - 1);
+  }
+};
+
+template <typename T, bool PAGED>
 __global__ void __launch_bounds__(256)
 k_dec_score(const T* __restrict__ qr, const T* __restrict__ ksum, const float* __restrict__ bsum,
             const int32_t* __restrict__ seqlen, float* __restrict__ scores, float* __restrict__ lsep,
-            int Hq, int nC, int nmax, int nsb, int N, int d, int S, int W, float tau) {
+            int Hq, int nC, int nmax, int nsb, int N, int d, int S, int W, float tau, PageMap pm) {
   constexpr int V = Vec<T>::N;
   constexpr int MAXT = 256 / (16 * V) > 0 ? 256 / (16 * V) : 1;
   constexpr int R = 16;
   __shared__ float red_m[4], red_s[4];
   const long long bh = blockIdx.x;
   const int b = (int)(bh / Hq);
-  const int n = n_cand(clamp_len(seqlen[b], N) - 1, W, S);
   const int c0 = blockIdx.y * SC_CPB;
   const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15, lane = tid & 63, wv = tid >> 6;
   float* lp = lsep + (bh * nsb + blockIdx.y) * 2;
-  if (c0 >= n) {
-    if (tid == 0) { lp[0] = -INFINITY; lp[1] = 0.0f; }
-    return;
-  }
+  // Contiguous cache: the summary rows are read before the sequence length is
+  // known (rows are clamped to the batch's longest candidate range, which the
+  // cache always holds), so the loads overlap the length lookup; rows past
+  // this sequence's candidates are discarded below.  Paged cache: the page
+  // table is only defined for the sequence's own chunks, so the length comes
+  // first.
   const int r0 = c0 + grp * R;
+  const int h = (int)(bh - (long long)b * Hq);
+  int cmax = nmax - 1;
+  if (PAGED) {
+    const int nb = n_cand(clamp_len(seqlen[b], N) - 1, W, S);
+    if (c0 >= nb) {
+      if (tid == 0) { lp[0] = -INFINITY; lp[1] = 0.0f; }
+      return;
+    }
+    cmax = nb - 1;
+  }
+  auto krow = [&](int c) -> long long {
+    return PAGED ? (pm.page(b, c) * Hq + h) * (long long)d : (bh * nC + c) * (long long)d;
+  };
+  const int cb = min(r0 + l16, cmax);
+  const float bv = PAGED ? bsum[pm.page(b, cb) * Hq + h] : bsum[bh * nC + cb];
   float acc[R];
 #pragma unroll
   for (int u = 0; u < R; ++u) acc[u] = 0.0f;
@@ -76,8 +104,8 @@ k_dec_score(const T* __restrict__ qr, const T* __restrict__ ksum, const float* _
       uint4 raw[R];
 #pragma unroll
       for (int u = 0; u < R; ++u) {
-        const int c = min(r0 + u, n - 1);
-        raw[u] = *reinterpret_cast<const uint4*>(ksum + (bh * nC + c) * (long long)d + e);
+        const int c = min(r0 + u, cmax);
+        raw[u] = *reinterpret_cast<const uint4*>(ksum + krow(c) + e);
       }
 #pragma unroll
       for (int u = 0; u < R; ++u) {
@@ -87,6 +115,11 @@ k_dec_score(const T* __restrict__ qr, const T* __restrict__ ksum, const float* _
         for (int x = 0; x < V; ++x) acc[u] = fmaf(qv[x], kv[x], acc[u]);
       }
     }
+  }
+  const int n = n_cand(clamp_len(seqlen[b], N) - 1, W, S);
+  if (c0 >= n) {
+    if (tid == 0) { lp[0] = -INFINITY; lp[1] = 0.0f; }
+    return;
   }
   // reduce-scatter over the 16 lanes: after the step with mask m a lane keeps
   // the half of its rows whose index bit m matches its own lane bit m
@@ -102,7 +135,7 @@ k_dec_score(const T* __restrict__ qr, const T* __restrict__ ksum, const float* _
   }
   const int c = r0 + l16;
   const bool ok = c < n;
-  const float x = ok ? fmaf(tau, acc[0], bsum[bh * nC + c]) : -INFINITY;
+  const float x = ok ? fmaf(tau, acc[0], bv) : -INFINITY;
   if (ok) scores[bh * nmax + c] = x;
   const float m = wave_max_f(x);
   const float ex = ok ? __expf(x - m) : 0.0f;
@@ -280,11 +313,11 @@ constexpr int AT_NT = 256;
 // V rows of the split are staged in LDS with 16-byte loads; thread (head, key)
 // forms a logit, wave h takes head h's softmax over the split (lane = key),
 // thread (head, element) forms the unnormalised output from the LDS V tile.
-template <typename T>
+template <typename T, bool PAGED>
 __global__ void __launch_bounds__(AT_NT)
 k_dec_attn(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
            const int32_t* __restrict__ seqlen, const int32_t* __restrict__ sel, float* __restrict__ part,
-           int Hq, int Hkv, int G, int N, int d, int S, int W, int K, int NS, float tau) {
+           int Hq, int Hkv, int G, int N, int d, int S, int W, int K, int NS, float tau, PageMap pm) {
   constexpr int V = Vec<T>::N;
   extern __shared__ __align__(16) unsigned char sm_raw[];
   const int kstr = d + V;                                     // padded row (elements), 16-byte multiple
@@ -297,17 +330,18 @@ k_dec_attn(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bg = blockIdx.x, s = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
-  const long long i = clamp_len(seqlen[b], N) - 1;
-  const int n = n_cand(i, W, S);
-  const int kk = min(K, n);
-  const long long w0 = window_start(i, W, S);
   const long long hbase = (long long)b * Hq + (long long)g * G;
+  // loads that do not need the sequence length go first: the query rows and,
+  // for a chunk split, its chunk id (slots past the selection hold -1)
+  for (int t = tid; t < G * d; t += AT_NT) qs[t] = Elt<T>::ld(q + hbase * d + t);
+  const int csel = (s < K) ? sel[(long long)bg * K + s] : -1;
+  const long long i = clamp_len(seqlen[b], N) - 1;
   long long j0 = 0;
   int jn = 0;
   if (s < K) {
-    if (s < kk) { j0 = (long long)sel[(long long)bg * K + s] * S; jn = S; }
+    if (csel >= 0) { j0 = (long long)csel * S; jn = S; }
   } else {
-    j0 = w0 + (long long)(s - K) * S;
+    j0 = window_start(i, W, S) + (long long)(s - K) * S;
     if (j0 <= i) jn = (int)min((long long)S, i - j0 + 1);
   }
   if (jn == 0) {               // empty split: weight 0 in the combine, zero partial
@@ -317,17 +351,32 @@ k_dec_attn(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
     }
     return;
   }
-  const T* kg = k + ((b * (long long)Hkv + g) * N + j0) * d;
-  const T* vg = v + ((b * (long long)Hkv + g) * N + j0) * d;
+  // every split is one chunk-aligned S-token tile: one page of a paged cache
+  const long long kvoff = PAGED ? (pm.page(b, j0 / S) * Hkv + g) * (long long)S * d
+                                : ((b * (long long)Hkv + g) * N + j0) * d;
+  const T* kg = k + kvoff;
+  const T* vg = v + kvoff;
   const int vpr = d / V;                                      // 16-byte vectors per row
-  for (int t = tid; t < jn * vpr; t += AT_NT) {
-    const int j = t / vpr, e = (t - j * vpr) * V;
-    const uint4 kx = *reinterpret_cast<const uint4*>(kg + (long long)j * d + e);
-    const uint4 vx = *reinterpret_cast<const uint4*>(vg + (long long)j * d + e);
-    *reinterpret_cast<uint4*>(ks + j * kstr + e) = kx;
-    *reinterpret_cast<uint4*>(vs + j * kstr + e) = vx;
+  const int nvec = jn * vpr;
+  for (int base = 0; base < nvec; base += 4 * AT_NT) {        // 8 loads in flight per thread
+    uint4 kx[4], vx[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = min(base + u * AT_NT + tid, nvec - 1);
+      const int j = t / vpr, e = (t - j * vpr) * V;
+      kx[u] = *reinterpret_cast<const uint4*>(kg + (long long)j * d + e);
+      vx[u] = *reinterpret_cast<const uint4*>(vg + (long long)j * d + e);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = base + u * AT_NT + tid;
+      if (t < nvec) {
+        const int j = t / vpr, e = (t - j * vpr) * V;
+        *reinterpret_cast<uint4*>(ks + j * kstr + e) = kx[u];
+        *reinterpret_cast<uint4*>(vs + j * kstr + e) = vx[u];
+      }
+    }
   }
-  for (int t = tid; t < G * d; t += AT_NT) qs[t] = Elt<T>::ld(q + hbase * d + t);
   __syncthreads();
   for (int t = tid; t < G * SP; t += AT_NT) {
     const int r = t / SP, j = t - r * SP;
@@ -438,50 +487,51 @@ k_dec_combine(const float* __restrict__ part, const float* __restrict__ slog,
   }
 }
 
+template <typename T, bool PAGED>
+void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const void* k, const void* v,
+                     const int32_t* seqlen, const void* ksum, const float* bsum, void* out,
+                     int32_t* sel, float* scores, uint32_t* keys, float* slog, float* part,
+                     float* lsep, PageMap pm, hipStream_t st) {
+  const int NS = s.K + s.nwin;
+  const float tau = (float)s.tau;
+  const unsigned nsb = (unsigned)((s.nmax + SC_CPB - 1) / SC_CPB);
+  const size_t esz = sizeof(T);
+  const size_t ashm = 2 * (size_t)s.S * (s.d + 16 / esz) * esz + (size_t)s.G * s.d * 4 +
+                      (size_t)s.G * ((s.S + 3) & ~3) * 4;
+  const size_t cshm = (size_t)NS * 4;
+  if (nsb > 0)
+    { HilsProfScope ps_("k_dec_score", st); hipLaunchKernelGGL((k_dec_score<T, PAGED>), dim3(s.B * s.Hq, nsb), dim3(256), 0, st,
+                       (const T*)qr, (const T*)ksum, bsum, seqlen, scores, lsep, s.Hq,
+                       s.nC, s.nmax, (int)nsb, s.N, s.d, s.S, s.W, tau, pm); }
+  const size_t sshm = (size_t)4 * (size_t)min(s.nmax > 0 ? s.nmax : 1, SEL_LDS_KEYS);
+  hipFuncSetAttribute((const void*)k_dec_select, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sshm);
+  { HilsProfScope ps_("k_dec_select", st); hipLaunchKernelGGL(k_dec_select, dim3(s.B * s.Hkv), dim3(SEL_NT), sshm, st, scores, lsep, seqlen,
+                     keys, sel, slog, s.Hq, s.Hkv, s.G, s.nmax > 0 ? s.nmax : 1, (int)nsb, s.N, s.S,
+                     s.W, s.K); }
+  hipFuncSetAttribute((const void*)k_dec_attn<T, PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
+  { HilsProfScope ps_("k_dec_attn", st); hipLaunchKernelGGL((k_dec_attn<T, PAGED>), dim3(s.B * s.Hkv, NS), dim3(AT_NT), ashm, st,
+                     (const T*)q, (const T*)k, (const T*)v, seqlen, sel, part,
+                     s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, NS, tau, pm); }
+  { HilsProfScope ps_("k_dec_combine", st); hipLaunchKernelGGL(k_dec_combine<T>, dim3(s.B * s.Hq), dim3(256), cshm, st, part, slog,
+                     seqlen, (T*)out, s.Hq, s.G, s.N, s.d, s.S, s.W, s.K, NS, s.nwin); }
+}
+
 }  // namespace
 
 hipError_t hils_launch_decode(const HilsShape& s, const void* q, const void* qr, const void* k,
                               const void* v, const int32_t* seqlen, const void* ksum,
                               const float* bsum, void* out, int32_t* sel, float* scores,
                               uint32_t* keys, float* slog, float* part, float* lsep,
+                              const int32_t* page_table, int max_pages, int num_pages,
                               hipStream_t st) {
-  const int NS = s.K + s.nwin;
-  const float tau = (float)s.tau;
-  const unsigned nsb = (unsigned)((s.nmax + SC_CPB - 1) / SC_CPB);
-  const size_t esz = s.dtype == 0 ? 2 : 4;
-  const size_t ashm = 2 * (size_t)s.S * (s.d + 16 / esz) * esz + (size_t)s.G * s.d * 4 +
-                      (size_t)s.G * ((s.S + 3) & ~3) * 4;
-  const size_t cshm = (size_t)NS * 4;
+  const PageMap pm{page_table, max_pages, num_pages};
+  const bool paged = page_table != nullptr;
   if (s.dtype == 0) {
-    if (nsb > 0)
-      { HilsProfScope ps_("k_dec_score", st); hipLaunchKernelGGL(k_dec_score<bf16_t>, dim3(s.B * s.Hq, nsb), dim3(256), 0, st,
-                         (const bf16_t*)qr, (const bf16_t*)ksum, bsum, seqlen, scores, lsep, s.Hq,
-                         s.nC, s.nmax, (int)nsb, s.N, s.d, s.S, s.W, tau); }
+    if (paged) launch_decode_t<bf16_t, true>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, slog, part, lsep, pm, st);
+    else launch_decode_t<bf16_t, false>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, slog, part, lsep, pm, st);
   } else {
-    if (nsb > 0)
-      { HilsProfScope ps_("k_dec_score", st); hipLaunchKernelGGL(k_dec_score<float>, dim3(s.B * s.Hq, nsb), dim3(256), 0, st,
-                         (const float*)qr, (const float*)ksum, bsum, seqlen, scores, lsep, s.Hq,
-                         s.nC, s.nmax, (int)nsb, s.N, s.d, s.S, s.W, tau); }
-  }
-  const size_t sshm = (size_t)4 * (size_t)min(s.nmax > 0 ? s.nmax : 1, SEL_LDS_KEYS);
-  hipFuncSetAttribute((const void*)k_dec_select, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sshm);
-  { HilsProfScope ps_("k_dec_select", st); hipLaunchKernelGGL(k_dec_select, dim3(s.B * s.Hkv), dim3(SEL_NT), sshm, st, scores, lsep, seqlen,
-                     keys, sel, slog, s.Hq, s.Hkv, s.G, s.nmax > 0 ? s.nmax : 1, (int)nsb, s.N, s.S,
-                     s.W, s.K); }
-  if (s.dtype == 0) {
-    hipFuncSetAttribute((const void*)k_dec_attn<bf16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
-    { HilsProfScope ps_("k_dec_attn", st); hipLaunchKernelGGL(k_dec_attn<bf16_t>, dim3(s.B * s.Hkv, NS), dim3(AT_NT), ashm, st,
-                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, seqlen, sel, part,
-                       s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, NS, tau); }
-    { HilsProfScope ps_("k_dec_combine", st); hipLaunchKernelGGL(k_dec_combine<bf16_t>, dim3(s.B * s.Hq), dim3(256), cshm, st, part, slog,
-                       seqlen, (bf16_t*)out, s.Hq, s.G, s.N, s.d, s.S, s.W, s.K, NS, s.nwin); }
-  } else {
-    hipFuncSetAttribute((const void*)k_dec_attn<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
-    { HilsProfScope ps_("k_dec_attn", st); hipLaunchKernelGGL(k_dec_attn<float>, dim3(s.B * s.Hkv, NS), dim3(AT_NT), ashm, st,
-                       (const float*)q, (const float*)k, (const float*)v, seqlen, sel, part,
-                       s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, NS, tau); }
-    { HilsProfScope ps_("k_dec_combine", st); hipLaunchKernelGGL(k_dec_combine<float>, dim3(s.B * s.Hq), dim3(256), cshm, st, part, slog,
-                       seqlen, (float*)out, s.Hq, s.G, s.N, s.d, s.S, s.W, s.K, NS, s.nwin); }
+    if (paged) launch_decode_t<float, true>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, slog, part, lsep, pm, st);
+    else launch_decode_t<float, false>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, slog, part, lsep, pm, st);
   }
   return hipGetLastError();
 }

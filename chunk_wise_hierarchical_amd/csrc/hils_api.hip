@@ -307,7 +307,55 @@ hils_status hils_decode(const hils_cfg* cfg, const void* q, const void* q_route,
   return hip_status(hils_launch_decode(s, q, qr, k_cache, v_cache, seqlen, k_sum, b_sum, out, sl,
                                        (float*)(w + L.scores), (uint32_t*)(w + L.keys),
                                        (float*)(w + L.slog), (float*)(w + L.part),
-                                       (float*)(w + L.lsep), (hipStream_t)stream));
+                                       (float*)(w + L.lsep), nullptr, 0, 0, (hipStream_t)stream));
+}
+
+hils_status hils_summarize_paged(const hils_cfg* cfg, const void* k_pages, const void* lm_pages,
+                                 const int32_t* pages, int32_t npages, int32_t num_pages,
+                                 void* k_sum_pages, float* b_sum_pages, void* stream) {
+  HilsShape s;
+  hils_status r = make_shape(cfg, s);
+  if (r != HILS_OK) return r;
+  if (s.mode == HILS_SCORE_EXACT) return HILS_E_ARG;
+  if (npages < 0 || num_pages < 1) return HILS_E_ARG;
+  if (npages == 0) return HILS_OK;
+  if (!k_pages || !lm_pages || !pages || !k_sum_pages || !b_sum_pages) return HILS_E_ARG;
+  const void* ptrs[] = {k_pages, lm_pages, pages, k_sum_pages, b_sum_pages};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return HILS_E_ARG;
+  if ((long long)npages * s.Hq >= (1LL << 31)) return HILS_E_UNSUPPORTED;
+  return hip_status(hils_launch_summarize_paged(s, k_pages, lm_pages, pages, npages, num_pages,
+                                                k_sum_pages, b_sum_pages, (hipStream_t)stream));
+}
+
+hils_status hils_decode_paged(const hils_cfg* cfg, const void* q, const void* q_route,
+                              const void* k_pages, const void* v_pages, int32_t num_pages,
+                              const int32_t* page_table, int32_t max_pages, const int32_t* seqlen,
+                              const void* k_sum_pages, const float* b_sum_pages, void* out,
+                              int32_t* sel, void* ws, size_t ws_bytes, void* stream) {
+  HilsShape s;
+  hils_status r = make_shape(cfg, s);
+  if (r != HILS_OK) return r;
+  if (s.mode == HILS_SCORE_EXACT) return HILS_E_UNSUPPORTED;
+  if (num_pages < 1 || max_pages < 1 || (long long)max_pages * s.S < s.N) return HILS_E_ARG;
+  if (!q || !k_pages || !v_pages || !page_table || !seqlen || !out) return HILS_E_ARG;
+  if (s.nmax > 0 && (!k_sum_pages || !b_sum_pages)) return HILS_E_ARG;
+  const void* ptrs[] = {q, q_route, k_pages, v_pages, page_table, seqlen, k_sum_pages, b_sum_pages,
+                        out, sel, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return HILS_E_ARG;
+  if (s.d % (s.dtype == HILS_BF16 ? 8 : 4) != 0) return HILS_E_UNSUPPORTED;
+  if ((long long)num_pages * s.Hq * s.d >= (1LL << 40)) return HILS_E_UNSUPPORTED;
+  const DecodeLayout L = decode_layout(s);
+  if (ws_bytes < L.total || (L.total > 0 && !ws)) return HILS_E_WORKSPACE;
+  char* w = static_cast<char*>(ws);
+  int32_t* sl = sel ? sel : (int32_t*)(w + L.sel);
+  const void* qr = q_route ? q_route : q;
+  return hip_status(hils_launch_decode(s, q, qr, k_pages, v_pages, seqlen, k_sum_pages, b_sum_pages,
+                                       out, sl, (float*)(w + L.scores), (uint32_t*)(w + L.keys),
+                                       (float*)(w + L.slog), (float*)(w + L.part),
+                                       (float*)(w + L.lsep), page_table, max_pages, num_pages,
+                                       (hipStream_t)stream));
 }
 
 }  // extern "C"

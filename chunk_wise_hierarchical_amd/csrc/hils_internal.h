@@ -68,7 +68,11 @@ hipError_t hils_launch_decode(const HilsShape& s, const void* q, const void* qr,
                               const void* v, const int32_t* seqlen, const void* ksum,
                               const float* bsum, void* out, int32_t* sel, float* scores,
                               uint32_t* keys, float* slog, float* part, float* lsep,
+                              const int32_t* page_table, int max_pages, int num_pages,
                               hipStream_t st);
+hipError_t hils_launch_summarize_paged(const HilsShape& s, const void* k_pages, const void* lm_pages,
+                                       const int32_t* pages, int npages_listed, int num_pages,
+                                       void* ksum_pages, float* bsum_pages, hipStream_t st);
 
 // chunk rows per decode scoring workgroup (one (max, sum exp) partial each)
 constexpr int HILS_DEC_SCORE_ROWS = 256;

@@ -12,25 +12,44 @@
 
 namespace {
 
+// Paged cache (pages != nullptr): item = listed page x query head; the page's
+// S keys are k[p][g][0..S), its landmark query lm[p][h], and the summary goes
+// to ksum[p][h], bsum[p][h].  Page ids are clamped into [0, npages).
 template <typename T>
 __global__ void __launch_bounds__(64)
 k_summarize(const T* __restrict__ k, const T* __restrict__ lm, T* __restrict__ ksum,
             float* __restrict__ bsum, int Hq, int Hkv, int N, int d, int S, int nC,
-            int c0, int ncs, double tau, int landmark_key) {
+            int c0, int ncs, double tau, int landmark_key, const int32_t* __restrict__ pages,
+            int npages) {
   extern __shared__ double sm_sum[];
   double* qd = sm_sum;        // [d]
   double* pj = sm_sum + d;    // [S]
   const int lane = threadIdx.x;
   const long long item = blockIdx.x;
-  const int c = c0 + (int)(item % ncs);
-  const long long bh = item / ncs;
-  const int h = (int)(bh % Hq);
-  const long long b = bh / Hq;
-  const int g = h / (Hq / Hkv);
-  const T* kc = k + (((b * Hkv + g) * (long long)N) + (long long)c * S) * d;
-  const T* qc = lm + ((b * Hq + h) * (long long)nC + c) * d;
-  T* ko = ksum + ((b * Hq + h) * (long long)nC + c) * d;
-  float* bo = bsum + (b * Hq + h) * (long long)nC + c;
+  const T* kc;
+  const T* qc;
+  T* ko;
+  float* bo;
+  int h;
+  if (pages) {
+    h = (int)(item % Hq);
+    const long long p = min(max(pages[item / Hq], 0), npages - 1);
+    const int g = h / (Hq / Hkv);
+    kc = k + ((p * Hkv + g) * (long long)S) * d;
+    qc = lm + (p * Hq + h) * (long long)d;
+    ko = ksum + (p * Hq + h) * (long long)d;
+    bo = bsum + p * Hq + h;
+  } else {
+    const int c = c0 + (int)(item % ncs);
+    const long long bh = item / ncs;
+    h = (int)(bh % Hq);
+    const long long b = bh / Hq;
+    const int g = h / (Hq / Hkv);
+    kc = k + (((b * Hkv + g) * (long long)N) + (long long)c * S) * d;
+    qc = lm + ((b * Hq + h) * (long long)nC + c) * d;
+    ko = ksum + ((b * Hq + h) * (long long)nC + c) * d;
+    bo = bsum + (b * Hq + h) * (long long)nC + c;
+  }
 
   if (landmark_key) {            // ablation: the landmark row is the routing key
     for (int e = lane; e < d; e += 64) ko[e] = qc[e];
@@ -74,10 +93,28 @@ hipError_t hils_launch_summarize(const HilsShape& s, const void* k, const void* 
   if (s.dtype == 0)
     { HilsProfScope ps_("k_summarize", st); hipLaunchKernelGGL(k_summarize<bf16_t>, dim3((unsigned)nblk), dim3(64), shm, st,
                        (const bf16_t*)k, (const bf16_t*)lm, (bf16_t*)ksum, bsum, s.Hq, s.Hkv, s.N,
-                       s.d, s.S, s.nC, c0, ncs, (double)s.tau, lk); }
+                       s.d, s.S, s.nC, c0, ncs, (double)s.tau, lk, nullptr, 0); }
   else
     { HilsProfScope ps_("k_summarize", st); hipLaunchKernelGGL(k_summarize<float>, dim3((unsigned)nblk), dim3(64), shm, st,
                        (const float*)k, (const float*)lm, (float*)ksum, bsum, s.Hq, s.Hkv, s.N,
-                       s.d, s.S, s.nC, c0, ncs, (double)s.tau, lk); }
+                       s.d, s.S, s.nC, c0, ncs, (double)s.tau, lk, nullptr, 0); }
+  return hipGetLastError();
+}
+
+hipError_t hils_launch_summarize_paged(const HilsShape& s, const void* k_pages, const void* lm_pages,
+                                       const int32_t* pages, int npages_listed, int num_pages,
+                                       void* ksum_pages, float* bsum_pages, hipStream_t st) {
+  if (npages_listed <= 0) return hipSuccess;
+  const long long nblk = (long long)npages_listed * s.Hq;
+  const size_t shm = sizeof(double) * (s.d + 64);
+  const int lk = (s.mode == 1);
+  if (s.dtype == 0)
+    { HilsProfScope ps_("k_summarize", st); hipLaunchKernelGGL(k_summarize<bf16_t>, dim3((unsigned)nblk), dim3(64), shm, st,
+                       (const bf16_t*)k_pages, (const bf16_t*)lm_pages, (bf16_t*)ksum_pages, bsum_pages,
+                       s.Hq, s.Hkv, s.N, s.d, s.S, s.nC, 0, 1, (double)s.tau, lk, pages, num_pages); }
+  else
+    { HilsProfScope ps_("k_summarize", st); hipLaunchKernelGGL(k_summarize<float>, dim3((unsigned)nblk), dim3(64), shm, st,
+                       (const float*)k_pages, (const float*)lm_pages, (float*)ksum_pages, bsum_pages,
+                       s.Hq, s.Hkv, s.N, s.d, s.S, s.nC, 0, 1, (double)s.tau, lk, pages, num_pages); }
   return hipGetLastError();
 }

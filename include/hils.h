@@ -128,6 +128,33 @@ hils_status hils_decode(const hils_cfg* cfg, const void* q, const void* q_route,
                         const void* k_sum, const float* b_sum, void* out, int32_t* sel,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Paged KV cache with one chunk per page (the pages' serving setup, section
+ * 7.1: KV page size equal to the chunk size S).  Physical page p holds
+ *   k_pages, v_pages : [num_pages][Hkv][S][d]   the S tokens of one chunk,
+ *   lm_pages         : [num_pages][Hq][d]       that chunk's landmark queries,
+ *   k_sum_pages      : [num_pages][Hq][d]       its summary keys (dtype),
+ *   b_sum_pages      : [num_pages][Hq]          its entropy biases (fp32).
+ * page_table [B][max_pages] int32 maps chunk c of sequence b to its page; only
+ * the entries of chunks that hold tokens of the sequence are read, and page
+ * ids are clamped into [0, num_pages) on the device, so any table content
+ * stays in bounds (a wrong id gives a wrong result, never a fault).
+ * cfg->N is the per-sequence token capacity (N <= max_pages * S).
+ *
+ * hils_summarize_paged: summaries (as hils_summarize) of the npages pages
+ * listed in pages[] (device int32), written into their own page slots.
+ * hils_decode_paged: as hils_decode, with every KV, summary and window access
+ * going through the page table; the workspace is hils_workspace_bytes(cfg, 1).
+ * Both enqueue kernels only (no allocation, no memset, no host sync), so a
+ * decode step can be captured into a HIP graph and replayed. */
+hils_status hils_summarize_paged(const hils_cfg* cfg, const void* k_pages, const void* lm_pages,
+                                 const int32_t* pages, int32_t npages, int32_t num_pages,
+                                 void* k_sum_pages, float* b_sum_pages, void* stream);
+hils_status hils_decode_paged(const hils_cfg* cfg, const void* q, const void* q_route,
+                              const void* k_pages, const void* v_pages, int32_t num_pages,
+                              const int32_t* page_table, int32_t max_pages, const int32_t* seqlen,
+                              const void* k_sum_pages, const float* b_sum_pages, void* out,
+                              int32_t* sel, void* ws, size_t ws_bytes, void* stream);
+
 const char* hils_strerror(hils_status status);
 int hils_abi_version(void);
 

@@ -100,6 +100,25 @@ def test_argument_errors_return_before_launch(L):
                          ctypes.c_size_t(1 << 30), None) == _lib.HILS_E_UNSUPPORTED
 
 
+def test_paged_entry_points_reject_bad_arguments(L):
+    p = ctypes.c_void_p(0x10000)
+    c = _cfg(N=1024)                      # 16 chunks of 64
+    ws = ctypes.c_size_t(1 << 30)
+    # decode: table narrower than the capacity, no pages, missing table
+    assert L.hils_decode_paged(ctypes.byref(c), p, None, p, p, 40, p, 15, p, p, p, p, None, p, ws,
+                               None) == _lib.HILS_E_ARG
+    assert L.hils_decode_paged(ctypes.byref(c), p, None, p, p, 0, p, 16, p, p, p, p, None, p, ws,
+                               None) == _lib.HILS_E_ARG
+    assert L.hils_decode_paged(ctypes.byref(c), p, None, p, p, 40, None, 16, p, p, p, p, None, p,
+                               ws, None) == _lib.HILS_E_ARG
+    assert L.hils_decode_paged(ctypes.byref(c), p, None, p, p, 40, p, 16, p, p, p, p, None, p,
+                               ctypes.c_size_t(16), None) == _lib.HILS_E_WORKSPACE
+    # summaries: negative count, no pages; zero listed pages is a no-op
+    assert L.hils_summarize_paged(ctypes.byref(c), p, p, p, -1, 40, p, p, None) == _lib.HILS_E_ARG
+    assert L.hils_summarize_paged(ctypes.byref(c), p, p, p, 3, 0, p, p, None) == _lib.HILS_E_ARG
+    assert L.hils_summarize_paged(ctypes.byref(c), p, p, p, 0, 40, p, p, None) == _lib.HILS_OK
+
+
 def test_product_path_does_not_touch_the_oracle():
     for dirpath, _, files in os.walk(PKG):
         for f in files:
