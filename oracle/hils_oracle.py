@@ -132,6 +132,10 @@ def ref_summarize(k, lm, S, scale=None, mode="surrogate", store="bf16"):
         b'_c  = -sum_j p_j log p_j         (entropy of p, natural log)
     For mode 'landmark_key' (ablation "w/o Prop. 3.1", Table 5): the landmark
         row itself is the routing key and b'_c = 0.
+    For mode 'mean_pool' (section 2.2 mean-pooled key; ablation "w/ mean
+        pooling", Table 5): k'_c = (1/S) sum_j k_j and b'_c = ln S, i.e. the
+        Proposition 3.1 summary of a landmark query equal to zero (uniform p),
+        so s_hat is the mean logit plus the log-mass of a uniform chunk.
     Returns (ks [B,Hq,nC,d] rounded to `store`, bs [B,Hq,nC] rounded to fp32;
     with store='f64' neither is rounded).
     """
@@ -145,6 +149,13 @@ def ref_summarize(k, lm, S, scale=None, mode="surrogate", store="bf16"):
     bs = np.zeros((B, Hq, nC))
     if mode == "landmark_key":
         return store_round(lm.astype(np.float64), store), bs
+    if mode == "mean_pool":
+        for b in range(B):
+            for h in range(Hq):
+                kc = k[b, h // G, : nC * S].reshape(nC, S, d).astype(np.float64)
+                ks[b, h] = kc.sum(axis=1) / S
+        bs[:] = math.log(S)
+        return store_round(ks, store), (bs if store == "f64" else f32_round(bs))
     if mode != "surrogate":
         raise ValueError(mode)
     for b in range(B):
@@ -284,7 +295,7 @@ def ref_prefill_rows(q, k, v, lm, rows, S, W, K, q_route=None, scale=None,
     """HiLS prefill outputs for a subset of query rows.
 
     q [B,Hq,N,d], k/v [B,Hkv,N,d], lm [B,Hq,nC,d] (unused in 'exact' mode),
-    rows: iterable of (b, i).  mode: 'surrogate' | 'landmark_key' | 'exact'.
+    rows: iterable of (b, i).  mode: 'surrogate' | 'landmark_key' | 'mean_pool' | 'exact'.
     summaries: optional precomputed (ks, bs) from ref_summarize.
     forced_sel: optional dict {(b, g, i): sel} to evaluate a given selection.
     Returns dict keyed by (b, i) -> dict(out [Hq,d], sel {g: ids}, gap {g: gap}, ...).

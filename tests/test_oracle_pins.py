@@ -330,3 +330,18 @@ def test_decode_equals_last_prefill_row():
         np.testing.assert_allclose(dec[b]["out"], pre["out"], atol=1e-12)
         for g in range(w.Hkv):
             assert dec[b]["sel"][g].tolist() == pre["sel"][g].tolist()
+
+
+def test_mean_pool_is_surrogate_at_zero_landmark_query():
+    """Mean pooling (section 2.2 equation) equals the Proposition 3.1 summary of
+    a zero landmark query: uniform weights give the mean key and entropy ln S."""
+    rng = np.random.default_rng(7)
+    k = rng.standard_normal((1, 2, 96, 8))
+    lm0 = np.zeros((1, 4, 6, 8))
+    ks_m, bs_m = O.ref_summarize(k, lm0, 16, mode="mean_pool", store="f64")
+    ks_s, bs_s = O.ref_summarize(k, lm0, 16, mode="surrogate", store="f64")
+    np.testing.assert_allclose(ks_m, ks_s, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(bs_m, bs_s, rtol=0, atol=1e-14)
+    # the mean key, chunk by chunk, written out directly
+    assert abs(ks_m[0, 3, 2, 5] - k[0, 1, 32:48, 5].mean()) < 1e-15
+    assert np.all(bs_m == math.log(16))
