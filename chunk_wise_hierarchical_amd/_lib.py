@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(_PKG, "libhils.so")
 
 HILS_OK, HILS_E_ARG, HILS_E_UNSUPPORTED, HILS_E_WORKSPACE, HILS_E_HIP = range(5)
 HILS_BF16, HILS_F32 = 0, 1
-MODES = {"surrogate": 0, "landmark_key": 1, "exact": 2}
+MODES = {"surrogate": 0, "landmark_key": 1, "exact": 2, "mean_pool": 3}
 HILS_FLAG_GENERIC = 1
 HILS_FLAG_UNION = 2
 

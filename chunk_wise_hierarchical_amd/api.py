@@ -60,6 +60,8 @@ def prefill(q, k, v, lm, S, W, K, q_route=None, mode="surrogate", scale=0.0, out
             sel=None, summaries=None, ws=None, generic=False, union=False):
     """HiLS prefill. q [B,Hq,N,d]; k,v [B,Hkv,N,d]; lm [B,Hq,N//S,d].
 
+    mode: "surrogate" (the method), "landmark_key", "mean_pool" (lm may be None) or
+    "exact" (token-query chunk log-mass; generic kernels, lm may be None).
     generic forces the vector-ALU kernels; union selects the MFMA attention by
     query block over the union of the block's chunks instead of the default
     per-chunk buckets.
@@ -91,9 +93,13 @@ def prefill(q, k, v, lm, S, W, K, q_route=None, mode="surrogate", scale=0.0, out
 
 
 def summarize(k, lm, S, c0=0, c1=None, out=None, mode="surrogate", scale=0.0, Hq=None):
-    """Chunk summaries for chunks [c0, c1): returns (k_sum [B,Hq,N//S,d], b_sum [B,Hq,N//S])."""
+    """Chunk summaries for chunks [c0, c1): returns (k_sum [B,Hq,N//S,d], b_sum [B,Hq,N//S]).
+    In "mean_pool" mode lm may be None (then pass Hq)."""
     B, Hkv, N, d = k.shape
-    Hq = lm.shape[1] if Hq is None else Hq
+    if Hq is None:
+        if lm is None:
+            raise ValueError("summarize: Hq is required when lm is None")
+        Hq = lm.shape[1]
     nC = N // S
     c1 = nC if c1 is None else c1
     dev = k.device
@@ -142,6 +148,8 @@ def summarize_paged(k_pages, lm_pages, pages, S, N, out=None, mode="surrogate", 
     cache: k_pages [P,Hkv,S,d], lm_pages [P,Hq,d].  Returns (k_sum_pages [P,Hq,d],
     b_sum_pages [P,Hq]); `out` reuses existing page-summary tensors."""
     P, Hkv, S_, d = k_pages.shape
+    if lm_pages is None:
+        raise ValueError("summarize_paged: lm_pages is required (it sets Hq)")
     Hq = lm_pages.shape[1]
     if S_ != S:
         raise ValueError(f"k_pages page size {S_} != S={S}")

@@ -32,7 +32,7 @@ hils_status make_shape(const hils_cfg* c, HilsShape& s) {
     return HILS_E_ARG;
   if (c->Hq % c->Hkv != 0) return HILS_E_ARG;
   if (c->dtype != HILS_BF16 && c->dtype != HILS_F32) return HILS_E_ARG;
-  if (c->mode < HILS_SCORE_SURROGATE || c->mode > HILS_SCORE_EXACT) return HILS_E_ARG;
+  if (c->mode < HILS_SCORE_SURROGATE || c->mode > HILS_SCORE_MEAN_POOL) return HILS_E_ARG;
   if (!(c->scale >= 0.0f) || isinf(c->scale)) return HILS_E_ARG;
   if (c->d > 256 || c->S > 64 || c->K > 128 || c->Hq / c->Hkv > 8) return HILS_E_UNSUPPORTED;
   const long long elems = (long long)c->B * c->Hq * c->N * c->d;
@@ -53,6 +53,7 @@ inline size_t esize(const HilsShape& s) { return s.dtype == HILS_BF16 ? 2 : 4; }
 // The MFMA fast path covers bf16, d = 128, S = 64, G in {1, 2, 4}, K <= 64.
 bool fast_eligible(const HilsShape& s, uint32_t flags) {
   if (flags & HILS_FLAG_GENERIC) return false;
+  if (s.mode == HILS_SCORE_EXACT) return false;   // test mode: generic kernels only
   if (s.dtype != HILS_BF16 || s.d != 128 || s.S != 64 || s.K > 64) return false;
   if (!(s.G == 1 || s.G == 2 || s.G == 4)) return false;
   if (s.nC > HILS_FAST_NCMAX) return false;
@@ -223,8 +224,10 @@ hils_status hils_summarize(const hils_cfg* cfg, const void* k, const void* lm_q,
   if (s.mode == HILS_SCORE_EXACT) return HILS_E_ARG;   // exact mode has no summaries
   if (c0 < 0 || c1 < c0 || c1 > s.nC) return HILS_E_ARG;
   if (c1 == c0) return HILS_OK;
-  if (!k || !lm_q || !k_sum || !b_sum) return HILS_E_ARG;
-  if (!aligned16(k) || !aligned16(lm_q) || !aligned16(k_sum) || !aligned16(b_sum)) return HILS_E_ARG;
+  const bool need_lm = s.mode != HILS_SCORE_MEAN_POOL;
+  if (!k || (need_lm && !lm_q) || !k_sum || !b_sum) return HILS_E_ARG;
+  if (!aligned16(k) || (lm_q && !aligned16(lm_q)) || !aligned16(k_sum) || !aligned16(b_sum))
+    return HILS_E_ARG;
   if ((long long)s.B * s.Hq * (c1 - c0) >= (1LL << 31)) return HILS_E_UNSUPPORTED;
   return hip_status(hils_launch_summarize(s, k, lm_q, c0, c1, k_sum, b_sum, (hipStream_t)stream));
 }
@@ -235,9 +238,9 @@ hils_status hils_prefill(const hils_cfg* cfg, const void* q, const void* q_route
   HilsShape s;
   hils_status r = make_shape(cfg, s);
   if (r != HILS_OK) return r;
-  if (s.mode == HILS_SCORE_EXACT) return HILS_E_UNSUPPORTED;
+  const bool exact = s.mode == HILS_SCORE_EXACT;
   if (!q || !k || !v || !out) return HILS_E_ARG;
-  if (s.nC > 0 && !lm_q) return HILS_E_ARG;
+  if (s.nC > 0 && !lm_q && s.mode != HILS_SCORE_MEAN_POOL && !exact) return HILS_E_ARG;
   if ((k_sum == nullptr) != (b_sum == nullptr)) return HILS_E_ARG;
   const void* ptrs[] = {q, q_route, k, v, lm_q, out, sel, k_sum, b_sum, ws};
   for (const void* p : ptrs)
@@ -252,10 +255,14 @@ hils_status hils_prefill(const hils_cfg* cfg, const void* q, const void* q_route
   void* ks = k_sum ? k_sum : (void*)(w + L.ks);
   float* bs = b_sum ? b_sum : (float*)(w + L.bs);
   int32_t* sl = sel ? sel : (int32_t*)(w + L.sel);
-  const void* qr = q_route ? q_route : q;
+  // exact mode scores chunks with the token query and needs no summaries
+  const void* qr = exact ? q : (q_route ? q_route : q);
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = hils_launch_summarize(s, k, lm_q, 0, s.nC, ks, bs, st);
-  if (e != hipSuccess) return HILS_E_HIP;
+  hipError_t e = hipSuccess;
+  if (!exact) {
+    e = hils_launch_summarize(s, k, lm_q, 0, s.nC, ks, bs, st);
+    if (e != hipSuccess) return HILS_E_HIP;
+  }
   if (fast) {
     void* vt = (void*)(w + L.vt);
     e = hils_launch_vt(s, v, vt, st);
@@ -279,7 +286,7 @@ hils_status hils_prefill(const hils_cfg* cfg, const void* q, const void* q_route
     return hip_status(hils_launch_attn_pairs(s, q, qr, k, vt, ks, bs, sl, out, pb, st));
   }
   float* slog = (float*)(w + L.slog);
-  e = hils_launch_select_generic(s, qr, ks, bs, sl, slog, st);
+  e = hils_launch_select_generic(s, qr, k, ks, bs, sl, slog, st);
   if (e != hipSuccess) return HILS_E_HIP;
   e = hils_launch_attn_generic(s, q, k, v, sl, slog, out, st);
   return hip_status(e);
@@ -319,10 +326,12 @@ hils_status hils_summarize_paged(const hils_cfg* cfg, const void* k_pages, const
   if (s.mode == HILS_SCORE_EXACT) return HILS_E_ARG;
   if (npages < 0 || num_pages < 1) return HILS_E_ARG;
   if (npages == 0) return HILS_OK;
-  if (!k_pages || !lm_pages || !pages || !k_sum_pages || !b_sum_pages) return HILS_E_ARG;
+  const bool need_lm = s.mode != HILS_SCORE_MEAN_POOL;
+  if (!k_pages || (need_lm && !lm_pages) || !pages || !k_sum_pages || !b_sum_pages)
+    return HILS_E_ARG;
   const void* ptrs[] = {k_pages, lm_pages, pages, k_sum_pages, b_sum_pages};
   for (const void* p : ptrs)
-    if (!aligned16(p)) return HILS_E_ARG;
+    if (p && !aligned16(p)) return HILS_E_ARG;
   if ((long long)npages * s.Hq >= (1LL << 31)) return HILS_E_UNSUPPORTED;
   return hip_status(hils_launch_summarize_paged(s, k_pages, lm_pages, pages, npages, num_pages,
                                                 k_sum_pages, b_sum_pages, (hipStream_t)stream));

@@ -27,8 +27,9 @@ hipError_t hils_launch_summarize(const HilsShape& s, const void* k, const void* 
                                  void* ksum, float* bsum, hipStream_t st);
 
 // prefill_generic.hip: vector-ALU score/select and attention, any supported shape
-hipError_t hils_launch_select_generic(const HilsShape& s, const void* qr, const void* ksum,
-                                      const float* bsum, int32_t* sel, float* slog, hipStream_t st);
+hipError_t hils_launch_select_generic(const HilsShape& s, const void* qr, const void* k,
+                                      const void* ksum, const float* bsum, int32_t* sel,
+                                      float* slog, hipStream_t st);
 hipError_t hils_launch_attn_generic(const HilsShape& s, const void* q, const void* k, const void* v,
                                     const int32_t* sel, const float* slog, void* out, hipStream_t st);
 

@@ -48,9 +48,10 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 
 template <typename T>
 __global__ void __launch_bounds__(NT)
-k_select_generic(const T* __restrict__ qr, const T* __restrict__ ksum, const float* __restrict__ bsum,
-                 int32_t* __restrict__ sel, float* __restrict__ slog, int Hq, int Hkv, int G,
-                 int N, int d, int S, int W, int K, int nC, float tau) {
+k_select_generic(const T* __restrict__ qr, const T* __restrict__ kk_, const T* __restrict__ ksum,
+                 const float* __restrict__ bsum, int32_t* __restrict__ sel,
+                 float* __restrict__ slog, int Hq, int Hkv, int G, int N, int d, int S, int W,
+                 int K, int nC, float tau, int exact) {
   extern __shared__ __align__(16) unsigned char sm_raw[];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t suf[256];
@@ -87,10 +88,22 @@ k_select_generic(const T* __restrict__ qr, const T* __restrict__ ksum, const flo
   }
   __syncthreads();
 
-  // s_hat for head r of the group and chunk c (fixed fma order => reproducible)
+  // s_hat for head r of the group and chunk c (fixed fma order => reproducible).
+  // Exact mode (section 2.1): log sum_{j in chunk c} exp(scale q.k_j), max-shifted.
   auto score = [&](int r, int c) -> float {
-    const T* kp = ksum + ((hbase + r) * nC + c) * (long long)d;
     const float* qq = qs + r * d;
+    if (exact) {
+      const T* kc = kk_ + ((b * Hkv + g) * (long long)N + (long long)c * S) * d;
+      float m = -INFINITY, s = 0.0f;
+      for (int j = 0; j < S; ++j) {
+        float acc = 0.0f;
+        for (int e = 0; e < d; ++e) acc = fmaf(qq[e], Elt<T>::ld(kc + (long long)j * d + e), acc);
+        const float x = tau * acc;
+        if (x > m) { s = s * expf(m - x) + 1.0f; m = x; } else { s += expf(x - m); }
+      }
+      return m + logf(s);
+    }
+    const T* kp = ksum + ((hbase + r) * nC + c) * (long long)d;
     float acc = 0.0f;
     for (int e = 0; e < d; ++e) acc = fmaf(qq[e], Elt<T>::ld(kp + e), acc);
     return fmaf(tau, acc, bsum[(hbase + r) * nC + c]);
@@ -337,22 +350,24 @@ k_attn_generic(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
 
 }  // namespace
 
-hipError_t hils_launch_select_generic(const HilsShape& s, const void* qr, const void* ksum,
-                                      const float* bsum, int32_t* sel, float* slog, hipStream_t st) {
+hipError_t hils_launch_select_generic(const HilsShape& s, const void* qr, const void* k,
+                                      const void* ksum, const float* bsum, int32_t* sel,
+                                      float* slog, hipStream_t st) {
+  const int exact = (s.mode == 2);
   const long long nblk = (long long)s.B * s.Hkv * s.N;
   const size_t shm = (((size_t)s.G * s.d * 4 + 15) & ~(size_t)15) + (size_t)8 * (s.nmax > 0 ? s.nmax : 1);
   if (s.dtype == 0) {
     auto f = k_select_generic<bf16_t>;
     hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     { HilsProfScope ps_("k_select_generic", st); hipLaunchKernelGGL(f, dim3((unsigned)nblk), dim3(NT), shm, st, (const bf16_t*)qr,
-                       (const bf16_t*)ksum, bsum, sel, slog, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W,
-                       s.K, s.nC, (float)s.tau); }
+                       (const bf16_t*)k, (const bf16_t*)ksum, bsum, sel, slog, s.Hq, s.Hkv, s.G, s.N,
+                       s.d, s.S, s.W, s.K, s.nC, (float)s.tau, exact); }
   } else {
     auto f = k_select_generic<float>;
     hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     { HilsProfScope ps_("k_select_generic", st); hipLaunchKernelGGL(f, dim3((unsigned)nblk), dim3(NT), shm, st, (const float*)qr,
-                       (const float*)ksum, bsum, sel, slog, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W,
-                       s.K, s.nC, (float)s.tau); }
+                       (const float*)k, (const float*)ksum, bsum, sel, slog, s.Hq, s.Hkv, s.G, s.N,
+                       s.d, s.S, s.W, s.K, s.nC, (float)s.tau, exact); }
   }
   return hipGetLastError();
 }

@@ -51,9 +51,18 @@ k_summarize(const T* __restrict__ k, const T* __restrict__ lm, T* __restrict__ k
     bo = bsum + (b * Hq + h) * (long long)nC + c;
   }
 
-  if (landmark_key) {            // ablation: the landmark row is the routing key
+  if (landmark_key == 1) {       // ablation: the landmark row is the routing key
     for (int e = lane; e < d; e += 64) ko[e] = qc[e];
     if (lane == 0) *bo = 0.0f;
+    return;
+  }
+  if (landmark_key == 3) {       // mean-pooled key, b' = ln S (uniform weights)
+    for (int e = lane; e < d; e += 64) {
+      double acc = 0.0;
+      for (int j = 0; j < S; ++j) acc += (double)Elt<T>::ld(kc + (long long)j * d + e);
+      Elt<T>::st64(ko + e, acc / (double)S);
+    }
+    if (lane == 0) *bo = (float)log((double)S);
     return;
   }
   for (int e = lane; e < d; e += 64) qd[e] = (double)Elt<T>::ld(qc + e);
@@ -89,7 +98,7 @@ hipError_t hils_launch_summarize(const HilsShape& s, const void* k, const void* 
   if (ncs <= 0) return hipSuccess;
   const long long nblk = (long long)s.B * s.Hq * ncs;
   const size_t shm = sizeof(double) * (s.d + 64);
-  const int lk = (s.mode == 1);
+  const int lk = s.mode;          // 0 surrogate, 1 landmark key, 3 mean pool
   if (s.dtype == 0)
     { HilsProfScope ps_("k_summarize", st); hipLaunchKernelGGL(k_summarize<bf16_t>, dim3((unsigned)nblk), dim3(64), shm, st,
                        (const bf16_t*)k, (const bf16_t*)lm, (bf16_t*)ksum, bsum, s.Hq, s.Hkv, s.N,
@@ -107,7 +116,7 @@ hipError_t hils_launch_summarize_paged(const HilsShape& s, const void* k_pages, 
   if (npages_listed <= 0) return hipSuccess;
   const long long nblk = (long long)npages_listed * s.Hq;
   const size_t shm = sizeof(double) * (s.d + 64);
-  const int lk = (s.mode == 1);
+  const int lk = s.mode;
   if (s.dtype == 0)
     { HilsProfScope ps_("k_summarize", st); hipLaunchKernelGGL(k_summarize<bf16_t>, dim3((unsigned)nblk), dim3(64), shm, st,
                        (const bf16_t*)k_pages, (const bf16_t*)lm_pages, (bf16_t*)ksum_pages, bsum_pages,

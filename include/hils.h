@@ -67,7 +67,13 @@ typedef enum { HILS_BF16 = 0, HILS_F32 = 1 } hils_dtype;
 typedef enum {
   HILS_SCORE_SURROGATE = 0,     /* Proposition 3.1 summary (k'_c, b'_c) — the method */
   HILS_SCORE_LANDMARK_KEY = 1,  /* ablation "w/o Prop. 3.1" (Table 5): lm row is k'_c, b'_c = 0 */
-  HILS_SCORE_EXACT = 2          /* naive-BSA exact chunk log-mass (section 2.1); not yet implemented */
+  HILS_SCORE_EXACT = 2,         /* naive-BSA exact chunk log-mass log sum_{j in chunk} exp(s_ij)
+                                   (section 2.1), from the token query q: an O(N^2 d) test mode,
+                                   prefill only (generic kernels); no summaries, lm_q unused */
+  HILS_SCORE_MEAN_POOL = 3      /* mean-pooled key (section 2.2 equation; ablation "w/ mean
+                                   pooling", Table 5): k'_c = mean of the chunk's keys,
+                                   b'_c = ln S (Proposition 3.1 at a zero landmark query);
+                                   lm_q unused */
 } hils_score_mode;
 
 /* flags */

@@ -70,10 +70,11 @@ def test_workspace_bytes(L):
         assert L.hils_workspace_bytes(ctypes.byref(_cfg(**bad)), 0) == 0, bad
 
 
-def _prefill(L, c, ws_bytes=1 << 30, null_q=False, misalign=False):
+def _prefill(L, c, ws_bytes=1 << 30, null_q=False, misalign=False, null_lm=False):
     p = ctypes.c_void_p(0x10000)
     q = None if null_q else ctypes.c_void_p(0x10000 + (8 if misalign else 0))
-    return L.hils_prefill(ctypes.byref(c), q, None, p, p, p, p, None, None, None, p,
+    lm = None if null_lm else p
+    return L.hils_prefill(ctypes.byref(c), q, None, p, p, lm, p, None, None, None, p,
                           ctypes.c_size_t(ws_bytes), None)
 
 
@@ -83,7 +84,11 @@ def test_argument_errors_return_before_launch(L):
     assert _prefill(L, _cfg(), misalign=True) == _lib.HILS_E_ARG
     assert _prefill(L, _cfg(d=512)) == _lib.HILS_E_UNSUPPORTED
     assert _prefill(L, _cfg(S=128)) == _lib.HILS_E_UNSUPPORTED
-    assert _prefill(L, _cfg(mode=2)) == _lib.HILS_E_UNSUPPORTED
+    # the landmark queries are needed by the Proposition 3.1 and landmark-key modes only
+    assert _prefill(L, _cfg(mode=0), null_lm=True) == _lib.HILS_E_ARG
+    assert _prefill(L, _cfg(mode=1), null_lm=True) == _lib.HILS_E_ARG
+    for m in (2, 3):
+        assert _prefill(L, _cfg(mode=m), ws_bytes=16, null_lm=True) == _lib.HILS_E_WORKSPACE
     assert _prefill(L, _cfg(), ws_bytes=16) == _lib.HILS_E_WORKSPACE
     p = ctypes.c_void_p(0x10000)
     # k_sum without b_sum
@@ -98,6 +103,11 @@ def test_argument_errors_return_before_launch(L):
                          ctypes.c_size_t(1 << 30), None) == _lib.HILS_E_ARG
     assert L.hils_decode(ctypes.byref(_cfg(d=12)), p, None, p, p, p, p, p, p, None, p,
                          ctypes.c_size_t(1 << 30), None) == _lib.HILS_E_UNSUPPORTED
+    # exact scoring is a prefill test mode; decode and summaries reject it
+    assert L.hils_decode(ctypes.byref(_cfg(mode=2)), p, None, p, p, p, p, p, p, None, p,
+                         ctypes.c_size_t(1 << 30), None) == _lib.HILS_E_UNSUPPORTED
+    assert L.hils_summarize(ctypes.byref(_cfg(mode=2)), p, p, 0, 2, p, p, None) == _lib.HILS_E_ARG
+    assert L.hils_summarize(ctypes.byref(_cfg(mode=4)), p, p, 0, 2, p, p, None) == _lib.HILS_E_ARG
 
 
 def test_paged_entry_points_reject_bad_arguments(L):

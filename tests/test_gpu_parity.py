@@ -67,8 +67,10 @@ def _prefill_case(w, rows=None, mode="surrogate", generic=False, q_route=False, 
     x = _gpu_inputs(w, with_q_route=q_route)
     out, sel, ks, bs = _run_prefill(w, x, mode=mode, generic=generic, union=union)
     xn = {k: np32(v) for k, v in x.items()}
-    summ = _oracle_summaries(w, xn, mode)
-    nbad = _check_summaries(w, ks, bs, summ)
+    summ, nbad = None, 0
+    if mode != "exact":               # exact scoring has no summaries
+        summ = _oracle_summaries(w, xn, mode)
+        nbad = _check_summaries(w, ks, bs, summ)
     if rows is None:
         rows = [(b, i) for b in range(w.B) for i in range(w.N)]
     res = O.ref_prefill_rows(xn["q"], xn["k"], xn["v"], xn["lm"], rows, w.S, w.W, w.K,
@@ -115,6 +117,41 @@ def test_prefill_q_route_and_landmark_key():
     w = synth.get_workload("prefill_64k", N=2048, Hq=8, Hkv=2, W=256, K=8)
     _prefill_case(w, rows=sample_rows(w, 120), q_route=True, label="q_route")
     _prefill_case(w, rows=sample_rows(w, 120), mode="landmark_key", label="landmark_key")
+
+
+def test_prefill_mean_pool_fast_and_generic():
+    # mean-pooled chunk keys with b' = ln S (Table 5 ablation), both kernel families
+    w = synth.get_workload("prefill_64k", N=4096, W=512, K=16)
+    _prefill_case(w, rows=sample_rows(w, 120), mode="mean_pool", label="mean_pool fast")
+    _prefill_case(w, rows=sample_rows(w, 120), mode="mean_pool", generic=True,
+                  label="mean_pool generic")
+    # the landmark queries are not read in this mode
+    x = _gpu_inputs(w)
+    o1 = hils.prefill(x["q"], x["k"], x["v"], x["lm"], w.S, w.W, w.K, mode="mean_pool")
+    o2 = hils.prefill(x["q"], x["k"], x["v"], None, w.S, w.W, w.K, mode="mean_pool")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_prefill_exact_scoring():
+    # exact chunk log-masses from the token query (section 2.1), generic kernels
+    w = synth.get_workload("tiny_fp32")
+    _prefill_case(w, mode="exact", label="exact tiny fp32")
+    w2 = synth.get_workload("prefill_8k", N=1024, B=1, Hq=4, Hkv=2, W=128, K=4)
+    _prefill_case(w2, rows=sample_rows(w2, 80), mode="exact", label="exact bf16 GQA")
+
+
+def test_prefill_exact_all_chunks_is_full_attention():
+    # with every candidate chunk selected, exact fusion weights reproduce dense
+    # causal softmax attention (section 3: the hierarchical softmax is exact then)
+    w = synth.get_workload("tiny_fp32", K=16)           # N/S = 16 chunks
+    x = _gpu_inputs(w)
+    out = hils.prefill(x["q"], x["k"], x["v"], None, w.S, w.W, w.K, mode="exact")
+    torch.cuda.synchronize()
+    ref = O.ref_full_causal(np32(x["q"]), np32(x["k"]), np32(x["v"]))
+    err, tol = out_error(np32(out), ref, "f32")
+    _say(f"   exact K=|C| vs dense causal: rel err {err:.3g} (tol {tol})")
+    assert err <= tol
 
 
 def test_prefill_generic_kernels_bf16():
@@ -222,16 +259,16 @@ def test_prefill_deterministic():
 # decode
 # ---------------------------------------------------------------------------
 
-def _decode_case(w, seqlen, label="", q_route=False, seqs=None):
+def _decode_case(w, seqlen, label="", q_route=False, seqs=None, mode="surrogate"):
     _say(f"[decode] {label} {w.name} B={w.B} T={w.N} Hq={w.Hq} Hkv={w.Hkv} d={w.d} S={w.S} "
          f"W={w.W} K={w.K} seqlen={seqlen[:4]}...")
     gen_dev = "cpu" if w.B * w.Hkv * w.N * w.d <= (1 << 26) else "cuda"
     x = synth.make_decode_inputs(w, device=gen_dev, seqlen=seqlen, with_q_route=q_route)
     x = {k: v.cuda() for k, v in x.items()}
-    ks, bs = hils.summarize(x["k"], x["lm"], w.S)
+    ks, bs = hils.summarize(x["k"], x["lm"], w.S, mode=mode)
     sel = torch.empty((w.B, w.Hkv, w.K), dtype=torch.int32, device="cuda")
     out = hils.decode(x["q"], x["k"], x["v"], x["seqlen"], ks, bs, w.S, w.W, w.K,
-                      q_route=x.get("q_route"), sel=sel)
+                      q_route=x.get("q_route"), sel=sel, mode=mode)
     torch.cuda.synchronize()
     seqs = range(w.B) if seqs is None else seqs
     t = Tally()
@@ -246,13 +283,14 @@ def _decode_case(w, seqlen, label="", q_route=False, seqs=None):
         lb = np32(x["lm"][b:b + 1, :, :max(n, 1)])
         qb = np32(x["q"][b:b + 1])
         qrb = np32(x["q_route"][b:b + 1]) if q_route else None
-        summ = O.ref_summarize(kb[:, :, :n * w.S], lb[:, :, :n], w.S, store=w.dtype) if n else None
+        summ = (O.ref_summarize(kb[:, :, :n * w.S], lb[:, :, :n], w.S, mode=mode, store=w.dtype)
+                if n else None)
         # the decode query stands at position T-1 (a zero-copy broadcast view over positions)
         qq = np.broadcast_to(qb, (1, w.Hq, T, w.d))
         qr = np.broadcast_to(qrb, (1, w.Hq, T, w.d)) if q_route else None
         # decode is the prefill row i = T-1 (same definition)
         res = O.ref_prefill_rows(qq, kb, vb, lb, [(0, T - 1)], w.S, w.W, w.K, q_route=qr,
-                                 store=w.dtype, summaries=summ if n else
+                                 mode=mode, store=w.dtype, summaries=summ if n else
                                  (np.zeros((1, w.Hq, 0, w.d)), np.zeros((1, w.Hq, 0))))
         r = res[(0, T - 1)]
         t.rows += 1
@@ -297,6 +335,12 @@ def test_decode_mha_and_wide_groups():
     # chunk size that is not a multiple of 4, window not a multiple of the chunk
     w = synth.get_workload("decode_512k", N=4400, B=2, Hq=4, Hkv=2, S=22, W=100, K=6)
     _decode_case(w, [4400, 3333], label="S=22")
+
+
+def test_decode_mean_pool_and_landmark_key():
+    w = synth.get_workload("decode_512k", N=8192, B=3)
+    _decode_case(w, [8192, 6000, 129], label="mean_pool", mode="mean_pool")
+    _decode_case(w, [8192, 6000, 129], label="landmark_key", mode="landmark_key")
 
 
 def test_decode_candidates_beyond_lds():
