@@ -10,17 +10,17 @@
 // wavefront computes a 32-chunk x 32-query score tile of one head with
 // v_mfma_f32_32x32x16_bf16 (A = k' rows, B = q_hat).  Scores are kept in
 // base-2 units (scaled by log2 e), which preserves their order.
-//   pass 0: per (query, head) online log-sum-exp over C_i (G > 1), and the two
+//   pass 0: per (query, head) online log-sum-exp over C_i (G > 1), and the four
 //           largest scores seen in each of the lane's 16 register slots.  The
-//           smallest of a (query, head)'s 64 tracked scores is a lower bound on
-//           its 64th (hence K-th) best score; T = max_h (bound_h - L_h) is then
-//           a lower bound on the K-th best group score, because the >= K
+//           K-th largest of a (query, head)'s 128 tracked scores is a lower
+//           bound bound_h on its K-th best score; T = max_h (bound_h - L_h) is
+//           then a lower bound on the K-th best group score, because the >= K
 //           chunks reaching bound_h all have a group score >= bound_h - L_h.
 //   pass 1: group score g = max_h (s_h - L_h) (cross-head max through LDS);
 //           chunks scoring above the query's current K-th best key (initially
 //           T) go to an LDS staging list, which is merged into the query's
 //           sorted top-K list (wavefront bitonic sort of the staged keys and
-//           one bitonic merge) once it holds more than 16 keys.
+//           one bitonic merge) when it could overflow.
 // Keys are 64-bit: (order-preserving bits of g) << 32 | (~chunk id), so ties
 // rank the lower chunk id first and every key is unique.  The selected ids
 // are written ascending, -1 padded.
@@ -35,9 +35,12 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int CT = 32;         // chunks per tile
-constexpr int XROW = CT + 4;   // row of the cross-head exchange buffer (floats, 16-byte rows)
-constexpr int STG = 48;        // staging slots per query
-constexpr int STG_MERGE = 16;  // merge when more than this many keys are staged
+constexpr int TRK = 128;       // pass-0 tracked scores per (query, head): top 4 of 32 slots
+constexpr int XROW = CT;       // row of the cross-head exchange buffer (floats); its 16-byte
+                               // pieces are XOR-swizzled by the row's low 3 bits
+// buffer descriptor word 3 for raw (unformatted, stride 0) loads on gfx9-family
+// parts: 32-bit data format, so num_records counts bytes
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
 
 template <int G>
 struct Geo {
@@ -45,12 +48,16 @@ struct Geo {
   static constexpr int QW = QB / 4;       // queries per wavefront in the selection layout
   static constexpr int LQ = 64 / QW;      // lanes per query
   static constexpr int CL = CT / LQ;      // chunks per lane per tile (selection layout)
+  // staging slots per query; one selection step (one chunk per lane) adds at
+  // most LQ keys, so a query merges once more than STG - LQ are waiting.  G = 1
+  // keeps a smaller area so two workgroups still fit one CU's LDS.
+  static constexpr int STG = (G == 1) ? 48 : 56;
+  static constexpr int STG_MERGE = STG - LQ;
 };
 
-// [0, 32 KB) is also the scratch of the tracked scores between the passes
-// (G*QB = 128 (query, head) pairs x 64 floats); it covers ktile and, for small
-// layouts, lst and stg, which are idle then.  tq and everything after it
-// always start past 32 KB.
+// [0, 64 KB) is also the scratch of the tracked scores between the passes
+// (G*QB = 128 (query, head) pairs x TRK floats); it covers ktile, xb, lst and
+// possibly stg, which are idle then.  tq and everything after it start past it.
 template <int G>
 struct Lds {
   size_t ktile, btile, xb, lst, stg, tq, thf, tk, cnt, thr, total;
@@ -61,13 +68,15 @@ struct Lds {
     xb = o;    o += (G > 1) ? (size_t)G * Geo<G>::QB * XROW * 4 : 0;
     o = (o + 15) & ~(size_t)15;
     lst = o;   o += (size_t)Geo<G>::QB * K * 8;
-    stg = o;   o += (size_t)Geo<G>::QB * STG * 8;
+    stg = o;   o += (size_t)Geo<G>::QB * Geo<G>::STG * 8;
+    const size_t scratch = (size_t)G * Geo<G>::QB * TRK * 4;
+    o = o > scratch ? o : scratch;
     tq = o;    o += (size_t)G * Geo<G>::QB * 4;
     thf = o;   o += (size_t)Geo<G>::QB * 4;
     // tk lives between the passes only: it may share the idle staging array
-    // when that starts past the tracked-score scratch [0, 32 KB); otherwise
-    // (G = 1 with a small K) it needs room of its own
-    if (stg >= (size_t)G * Geo<G>::QB * 64 * 4) {
+    // when that starts past the tracked-score scratch; otherwise it needs room
+    // of its own
+    if (stg >= scratch) {
       tk = stg;
     } else {
       tk = o;  o += (size_t)G * Geo<G>::QB * 4;
@@ -81,6 +90,19 @@ struct Lds {
 
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a > b ? b : a; }
+
+// a wavefront-uniform pointer, held in scalar registers
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+}
+
+// number of set bits of m below this lane
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
 // wavefront-wide bitonic sort of 64 keys (1 per lane), descending
 __device__ __forceinline__ uint64_t sort64_desc(uint64_t v, int lane) {
@@ -126,6 +148,17 @@ __device__ __forceinline__ float sort64_desc_f(float v, int lane) {
   return v;
 }
 
+// a, b descending across the wavefront -> the 64 largest of a U b, descending
+__device__ __forceinline__ float merge_top64_f(float a, float b, int lane) {
+  float v = fmaxf(a, __builtin_bit_cast(float, lane_reverse(__builtin_bit_cast(uint32_t, b))));
+#pragma unroll
+  for (int stride = 32; stride > 0; stride >>= 1) {
+    const float p = xshfl_f(v, stride);
+    v = ((lane & stride) == 0) ? fmaxf(v, p) : fminf(v, p);
+  }
+  return v;
+}
+
 // wavefront-wide bitonic sort of 64 ints (1 per lane), ascending
 __device__ __forceinline__ int sort64_asc(int v, int lane) {
 #pragma unroll
@@ -148,6 +181,7 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
              int W, int K, int nC, float tau2, int nqb) {
   using GE = Geo<G>;
   constexpr int QB = GE::QB, QW = GE::QW, LQ = GE::LQ, CL = GE::CL;
+  constexpr int STG = GE::STG, STG_MERGE = GE::STG_MERGE;
   extern __shared__ __align__(16) unsigned char sm[];
   const Lds<G> L(K);
   bf16_t* ktile = reinterpret_cast<bf16_t*>(sm + L.ktile);   // [G][CT][16 parts], part ^= c & 15
@@ -155,11 +189,10 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   float* xb = reinterpret_cast<float*>(sm + L.xb);           // [G][QB][XROW]
   float* tq = reinterpret_cast<float*>(sm + L.tq);           // [G][QB] log-sum-exp (base 2)
   float* tk = reinterpret_cast<float*>(sm + L.tk);           // [G][QB] K-th tracked score
-  float* trk = reinterpret_cast<float*>(sm + L.ktile);       // [G*QB][64] between the passes
+  float* trk = reinterpret_cast<float*>(sm + L.ktile);       // [G*QB][TRK] between the passes
   uint64_t* lst = reinterpret_cast<uint64_t*>(sm + L.lst);   // [QB][K]
   uint64_t* stg = reinterpret_cast<uint64_t*>(sm + L.stg);   // [QB][STG]
-  uint32_t* cnt_stg = reinterpret_cast<uint32_t*>(sm + L.cnt);
-  uint32_t* cnt_lst = cnt_stg + QB;
+  uint32_t* cnt_lst = reinterpret_cast<uint32_t*>(sm + L.cnt);
   uint64_t* thr = reinterpret_cast<uint64_t*>(sm + L.thr);
   float* thf = reinterpret_cast<float*>(sm + L.thf);        // [QB] thr as a float (prefilter)
 
@@ -180,7 +213,7 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     for (int t = tid; t < (i_last - i0 + 1) * K; t += NT) selg[(long long)i0 * K + t] = -1;
     return;
   }
-  for (int t = tid; t < QB; t += NT) { cnt_stg[t] = 0; cnt_lst[t] = 0; }
+  for (int t = tid; t < QB; t += NT) cnt_lst[t] = 0;
 
   // MFMA layout: wavefront -> (head hw, 32-query column block qw); lane -> query column
   const int hw = w % G, qw = w / G;
@@ -194,31 +227,53 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     else bq[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
   }
 
-  // selection layout: lane -> (query qsel, CL chunks of the tile)
+  // selection layout: lane -> (query qsel, CL chunks of the tile); gmask is
+  // the lane group of qsel and nstg that query's staged-key count
   const int qsel = (G == 1) ? (32 * w + col) : (w * QW + lane / LQ);
   const int cbase = (G == 1) ? 0 : CL * (lane % LQ);
+  const uint64_t gmask = (G == 1) ? ((1ull << col) | (1ull << (col + 32)))
+                                  : (((1ull << LQ) - 1) << (LQ * (lane / LQ)));
+  int nstg = 0;
 
   // tile staging through registers into a single XOR-swizzled LDS tile.  The
-  // loads are unconditional and kept raw until the store (chunk ids past nC
-  // read chunk nC-1; their scores are masked by the candidate range), so the
-  // next tile's loads stay in flight while the current tile is scored.
+  // loads are unconditional and kept raw until the store, so they stay in
+  // flight while earlier tiles are scored.
   constexpr int PPT = 2 * G;               // 16-byte pieces per thread per tile
-  uint4 pre[PPT];
-  float bpre = 0.0f;
-  auto load_tile = [&](int t) {
+  // piece p of this thread: head p/2, chunk c0 (+16 for odd p) of the tile,
+  // 16-byte part tid % 16.  The loads go through buffer descriptors whose base
+  // is the tile's first row and whose range ends at the group's last k' row:
+  // the per-thread offsets never change, and rows past the range read zero
+  // (past chunk nC - 1 a row reads another head's chunk or zero; those scores
+  // are masked by the candidate range).
+  static_assert(NT == 256 && CT == 32, "piece layout assumes 256 threads and 32-chunk tiles");
+  const int c0 = tid >> 4;
+  const char* kgrp = reinterpret_cast<const char*>(ksum + hb * nC * (long long)D);
+  const char* bgrp = reinterpret_cast<const char*>(bsum + hb * nC);
+  uint32_t voff[PPT];
 #pragma unroll
-    for (int p = 0; p < PPT; ++p) {
-      const int piece = tid + NT * p;
-      const int h = piece / (CT * 16), c = (piece / 16) % CT, part = piece % 16;
-      const int cg = min(CT * t + c, nC - 1);
-      pre[p] = ld_u4(ksum + ((hb + h) * nC + cg) * (long long)D + part * 8);
-    }
-    {
-      const int h = (tid / CT) % G, cg = min(CT * t + tid % CT, nC - 1);
-      bpre = bsum[(hb + h) * nC + cg];
-    }
+  for (int p = 0; p < PPT; ++p)
+    voff[p] = ((uint32_t)(p >> 1) * (uint32_t)nC + (uint32_t)(c0 + 16 * (p & 1))) * (uint32_t)(D * 2) +
+              (uint32_t)(tid & 15) * 16u;
+  const uint32_t boff = ((uint32_t)((tid / CT) % G) * (uint32_t)nC + (uint32_t)(tid % CT)) * 4u;
+  const int grows = G * nC;                // k' rows of the group
+  // two register buffers: the loads of tile t + 2 are issued while tile t is
+  // scored and tile t + 1 waits in the other buffer for its LDS store, so each
+  // load has two tile steps to arrive
+  uint4 preA[PPT], preB[PPT];
+  float bpreA = 0.0f, bpreB = 0.0f;
+  auto load_tile = [&](int t, uint4 (&pre)[PPT], float& bpre) {
+    const int r0 = __builtin_amdgcn_readfirstlane(CT * t);
+    const int left = max(grows - r0, 0);
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(kgrp + (size_t)r0 * (D * 2)), 0, left * (D * 2), BUF_RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(bgrp + (size_t)r0 * 4), 0, left * 4, BUF_RSRC_WORD3);
+#pragma unroll
+    for (int p = 0; p < PPT; ++p)
+      pre[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)voff[p], 0, 0));
+    bpre = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, (int)boff, 0, 0));
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](const uint4 (&pre)[PPT], float bpre) {
 #pragma unroll
     for (int p = 0; p < PPT; ++p) {
       const int piece = tid + NT * p;
@@ -228,9 +283,9 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     if (tid < G * CT) btile[tid] = bpre * LOG2E;
   };
 
-  // merge query q's staging list into its sorted top-K list (whole wavefront)
-  auto merge = [&](int q) {
-    const int ns = (int)cnt_stg[q], nl = (int)cnt_lst[q];
+  // merge query q's ns staged keys into its sorted top-K list (whole wavefront)
+  auto merge = [&](int q, int ns) {
+    const int nl = (int)cnt_lst[q];
     const uint64_t a = (lane < nl) ? lst[(size_t)q * K + lane] : 0ull;
     uint64_t sb = (lane < ns) ? stg[(size_t)q * STG + lane] : 0ull;
     sb = sort64_desc(sb, lane);
@@ -241,14 +296,16 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     if (lane < K) lst[(size_t)q * K + lane] = (lane < tot) ? v : 0ull;
     if (lane == 0) {
       cnt_lst[q] = tot;
-      cnt_stg[q] = 0;
       if (tot >= K) {
         const uint64_t nt = umax64(thr[q], ((uint64_t)khi << 32) | klo);
         thr[q] = nt;
         thf[q] = order_key_f32((uint32_t)(nt >> 32));
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // other lanes of this wavefront read the list, the counts and the
+    // threshold next: acquire-release keeps the compiler from answering those
+    // reads with values it holds from before lane 0's writes
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   };
 
   // scores of tile t for this lane (base 2): x[i] <-> chunk 32t + 8(i>>2) + 4*half + (i&3)
@@ -288,27 +345,34 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   auto run_pass = [&](auto pass_tag) {
     constexpr int pass = decltype(pass_tag)::value;
     float m = -INFINITY, ssum = 0.0f;
-    float ta[16], tb[16];                  // top-2 per register slot (pass 0)
+    float t0[16], t1[16], t2[16], t3[16];  // top 4 per register slot, descending (pass 0)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { ta[i] = -INFINITY; tb[i] = -INFINITY; }
-    load_tile(0);
-    store_tile();
+    for (int i = 0; i < 16; ++i) { t0[i] = -INFINITY; t1[i] = -INFINITY; t2[i] = -INFINITY; t3[i] = -INFINITY; }
+    load_tile(0, preA, bpreA);
+    store_tile(preA, bpreA);
     __syncthreads();
+    load_tile(min(1, ntiles - 1), preA, bpreA);
     // pass 1 accumulator seed: -L / scale (L = +inf/-inf only for rows without
     // candidates, whose scores are all masked)
     const float ainit = (pass == 1 && G > 1) ? -L2 / tau2 : 0.0f;
     f32x16_t aseed;
 #pragma unroll
     for (int i = 0; i < 16; ++i) aseed[i] = ainit;
-    for (int t = 0; t < ntiles; ++t) {
-      load_tile(min(t + 1, ntiles - 1));
+    // one tile step: cur holds tile t + 1 (stored to LDS during the step), nxt
+    // receives tile t + 2
+    auto step = [&](int t, const uint4 (&cur)[PPT], float bcur, uint4 (&nxt)[PPT], float& bnxt) {
+      load_tile(min(t + 2, ntiles - 1), nxt, bnxt);
       float x[16];
       tile_scores(t, x, aseed);
       if constexpr (pass == 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          tb[i] = fmaxf(tb[i], fminf(ta[i], x[i]));
-          ta[i] = fmaxf(ta[i], x[i]);
+          // insert x into t0 >= t1 >= t2 >= t3: each new entry is the median of
+          // its old neighbours above and below and x
+          t3[i] = __builtin_amdgcn_fmed3f(t2[i], t3[i], x[i]);
+          t2[i] = __builtin_amdgcn_fmed3f(t1[i], t2[i], x[i]);
+          t1[i] = __builtin_amdgcn_fmed3f(t0[i], t1[i], x[i]);
+          t0[i] = fmaxf(t0[i], x[i]);
         }
         if (G > 1) {
           float mt = x[0];
@@ -321,28 +385,31 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
           }
         }
         __syncthreads();
-        store_tile();            // past the last tile: rewrites the last tile, unused
+        store_tile(cur, bcur);   // past the last tile: rewrites the last tile, unused
         __syncthreads();
       } else {
         // group scores: x already holds s_h - L_h; the heads of a group meet in LDS
         if (G > 1) {
-          float* xr = xb + ((size_t)hw * QB + 32 * qw + col) * XROW + 4 * half;
+          const int xrow = hw * QB + 32 * qw + col;
+          float* xr = xb + (size_t)xrow * XROW;
 #pragma unroll
           for (int gq = 0; gq < 4; ++gq)
-            *reinterpret_cast<float4*>(xr + 8 * gq) =
+            *reinterpret_cast<float4*>(xr + 4 * ((2 * gq + half) ^ (xrow & 7))) =
                 make_float4(x[4 * gq], x[4 * gq + 1], x[4 * gq + 2], x[4 * gq + 3]);
         }
         __syncthreads();         // exchange written; every wave is done reading the k' tile
-        store_tile();            // next tile (past the last: rewrites the last, unused)
+        store_tile(cur, bcur);   // next tile (past the last: rewrites the last, unused)
         float gs[CL];
         int cid0;
         if (G > 1) {
 #pragma unroll
           for (int j4 = 0; j4 < CL; j4 += 4) {
-            float4 mx = *reinterpret_cast<const float4*>(xb + (size_t)qsel * XROW + cbase + j4);
+            const int piece = (cbase + j4) >> 2;
+            float4 mx = *reinterpret_cast<const float4*>(xb + (size_t)qsel * XROW + 4 * (piece ^ (qsel & 7)));
 #pragma unroll
             for (int h = 1; h < G; ++h) {
-              const float4 y = *reinterpret_cast<const float4*>(xb + ((size_t)h * QB + qsel) * XROW + cbase + j4);
+              const int xrow = h * QB + qsel;
+              const float4 y = *reinterpret_cast<const float4*>(xb + (size_t)xrow * XROW + 4 * (piece ^ (xrow & 7)));
               mx = make_float4(fmaxf(mx.x, y.x), fmaxf(mx.y, y.y), fmaxf(mx.z, y.z), fmaxf(mx.w, y.w));
             }
             gs[j4] = mx.x; gs[j4 + 1] = mx.y; gs[j4 + 2] = mx.z; gs[j4 + 3] = mx.w;
@@ -354,42 +421,52 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
           cid0 = CT * t;
         }
         // filter against the query's current K-th best key (float prefilter, then
-        // the exact 64-bit key) and stage the survivors
+        // the exact 64-bit key) and stage the survivors.  A query's staging
+        // slots are handed out within its lane group by ballot ranks, and its
+        // count lives in a register of every lane of the group.
         const float tf = thf[qsel];
         const uint64_t th = thr[qsel];
+        int off = nstg;
+        const bool leader = (G == 1) ? (half == 0) : (lane % LQ == 0);
 #pragma unroll
         for (int j = 0; j < CL; ++j) {
-          if (gs[j] != -INFINITY && gs[j] >= tf) {
-            const int cid = (G == 1) ? (cid0 + 8 * (j >> 2) + 4 * half + (j & 3)) : (cid0 + j);
-            const uint64_t key = ((uint64_t)f32_order_key(gs[j]) << 32) |
-                                 (uint64_t)(0xffffffffu - (uint32_t)cid);
-            if (key > th) {
-              const uint32_t slot = atomicAdd(&cnt_stg[qsel], 1u);
-              stg[(size_t)qsel * STG + slot] = key;
-            }
-          }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        {
-          const bool leader = (G == 1) ? (half == 0) : (lane % LQ == 0);
-          unsigned long long need = __ballot(leader && cnt_stg[qsel] > (uint32_t)STG_MERGE);
+          const int cid = (G == 1) ? (cid0 + 8 * (j >> 2) + 4 * half + (j & 3)) : (cid0 + j);
+          const uint64_t key = ((uint64_t)f32_order_key(gs[j]) << 32) |
+                               (uint64_t)(0xffffffffu - (uint32_t)cid);
+          const bool pass_j = gs[j] != -INFINITY && gs[j] >= tf && key > th;
+          const uint64_t m = __ballot(pass_j) & gmask;
+          if (pass_j)
+            stg[(size_t)qsel * STG + off + lanes_below(m)] = key;
+          off += __popcll(m);
+          // merge the queries whose next step could overflow their staging
+          unsigned long long need = __ballot(leader && off > STG_MERGE);
           while (need) {
             const int l = __ffsll((long long)need) - 1;
             need &= need - 1;
-            merge((G == 1) ? (32 * w + l) : (w * QW + l / LQ));
+            const int q = (G == 1) ? (32 * w + l) : (w * QW + l / LQ);
+            merge(q, __builtin_amdgcn_readlane(off, l));
+            if (qsel == q) off = 0;
           }
         }
+        nstg = off;
         __syncthreads();         // next k' tile visible; exchange reads done
       }
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, preA, bpreA, preB, bpreB);
+      if (t + 1 < ntiles) step(t + 1, preB, bpreB, preA, bpreA);
     }
     if constexpr (pass == 0) {
-      // per (query, head): log-sum-exp, and the K-th largest of the 64 tracked
+      // per (query, head): log-sum-exp, and the K-th largest of the 128 tracked
       // scores (a lower bound on the head's K-th best score)
       const int pr = hw * QB + 32 * qw + col;        // (head, query) pair of this lane
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        trk[(size_t)pr * 64 + half * 32 + i] = ta[i];
-        trk[(size_t)pr * 64 + half * 32 + 16 + i] = tb[i];
+        float* tr = trk + (size_t)pr * TRK + half * 64 + i;
+        tr[0] = t0[i];
+        tr[16] = t1[i];
+        tr[32] = t2[i];
+        tr[48] = t3[i];
       }
       if (G > 1) {
         const float m2 = __shfl_xor(m, 32, 64), s2 = __shfl_xor(ssum, 32, 64);
@@ -403,7 +480,9 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
       __syncthreads();
       for (int j = 0; j < (G * QB) / 4; ++j) {
         const int p = w * ((G * QB) / 4) + j;
-        const float v = sort64_desc_f(trk[(size_t)p * 64 + lane], lane);
+        const float va = sort64_desc_f(trk[(size_t)p * TRK + lane], lane);
+        const float vb = sort64_desc_f(trk[(size_t)p * TRK + 64 + lane], lane);
+        const float v = merge_top64_f(va, vb, lane);
         const float kth = __shfl(v, K - 1, 64);
         if (lane == 0) tk[p] = kth;
       }
@@ -430,7 +509,8 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   // final merge, ascending ids, write the selection
   for (int qq = 0; qq < QW; ++qq) {
     const int q = w * QW + qq;
-    if (cnt_stg[q] > 0) merge(q);
+    const int ns = __builtin_amdgcn_readlane(nstg, (G == 1) ? qq : qq * LQ);
+    if (ns > 0) merge(q, ns);
     const int tot = (int)cnt_lst[q];
     const uint64_t e = (lane < tot) ? lst[(size_t)q * K + lane] : 0ull;
     int id = (lane < tot) ? (int)(0xffffffffu - (uint32_t)e) : 0x7fffffff;
