@@ -343,6 +343,48 @@ def test_decode_mean_pool_and_landmark_key():
     _decode_case(w, [8192, 6000, 129], label="landmark_key", mode="landmark_key")
 
 
+def test_decode_4m_context_sampled_groups():
+    # 4M-token cache, batch 1, W=2048, K=64: 65504 candidate chunks per query;
+    # the oracle checks two KV groups (their own summaries, selection, output)
+    w = synth.get_workload("decode_4m")
+    T = w.N
+    _say(f"[decode] 4M {w.name} B={w.B} T={T} Hq={w.Hq} Hkv={w.Hkv} W={w.W} K={w.K}")
+    x = synth.make_decode_inputs(w, device="cuda")
+    ks, bs = hils.summarize(x["k"], x["lm"], w.S)
+    sel = torch.empty((w.B, w.Hkv, w.K), dtype=torch.int32, device="cuda")
+    out = hils.decode(x["q"], x["k"], x["v"], x["seqlen"], ks, bs, w.S, w.W, w.K, sel=sel)
+    torch.cuda.synchronize()
+    n = O.n_candidates(T - 1, w.W, w.S)
+    G = w.G
+    t = Tally()
+    t.rows = 1
+    gsel, gout = sel.cpu().numpy(), np32(out)
+    for g in (0, w.Hkv - 1):
+        _say(f"   group {g}: oracle summaries over {n} chunks")
+        hs = slice(g * G, (g + 1) * G)
+        kg = np32(x["k"][:, g:g + 1])
+        vg = np32(x["v"][:, g:g + 1])
+        lg = np32(x["lm"][:, hs, :n])
+        summ = O.ref_summarize(kg[:, :, :n * w.S], lg, w.S, store=w.dtype)
+        gk = np32(ks[:, hs, :n]).astype(np.float64)
+        assert int((gk != summ[0]).sum()) <= max(1, gk.size // 10**6)
+        _say(f"   group {g}: oracle row {T - 1}")
+        qq = np.broadcast_to(np32(x["q"][:, hs]), (1, G, T, w.d))
+        r = O.ref_prefill_rows(qq, kg, vg, lg, [(0, T - 1)], w.S, w.W, w.K, store=w.dtype,
+                               summaries=summ)[(0, T - 1)]
+        kind = check_selection(gsel[0, g], dict(sel=r["sel"][0], gap=r["gap"][0],
+                                                s_hat=r["s_hat"][0]), w.K)
+        if kind == "exact":
+            t.exact += 1
+            err, tol = out_error(gout[0, hs, 0], r["out"], w.dtype)
+            t.tol, t.max_err = tol, max(t.max_err, err)
+            assert err <= tol, f"decode output error {err} > {tol} (group {g})"
+        else:
+            t.tie += 1
+    _say(f"   {t}")
+    assert t.exact >= 1
+
+
 def test_decode_candidates_beyond_lds():
     # more candidate chunks than the selection kernel keeps in LDS (24576)
     w = synth.get_workload("decode_512k", N=409600, B=1, Hq=2, Hkv=1, d=64, S=16, W=256, K=8)
