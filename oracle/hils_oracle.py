@@ -41,7 +41,7 @@ import numpy as np
 
 __all__ = [
     "bf16_round", "f32_round", "store_round", "window_left", "n_candidates",
-    "ref_summarize", "ref_chunk_scores", "ref_exact_logz", "ref_group_scores",
+    "ref_summarize", "ref_chunk_scores", "ref_exact_logz", "ref_group_scores", "ref_decode_multi",
     "ref_select", "ref_row", "ref_prefill_rows", "ref_decode",
     "ref_full_causal", "ref_naive_bsa", "ref_overlap", "ref_brute_force_mass_topk",
 ]
@@ -383,6 +383,56 @@ def ref_decode(q, k_cache, v_cache, seqlen, lm, S, W, K, q_route=None, scale=Non
             out[hs] = r["out"]
             sels[g], gaps[g] = r["sel"], r["gap"]
         results[b] = dict(out=out, sel=sels, gap=gaps, n=n)
+    return results
+
+
+def ref_decode_multi(q, k_cache, v_cache, seqlen, lm, S, W, K, q_route=None, scale=None,
+                     mode="surrogate", store="bf16"):
+    """Decode of a block of M new tokens per sequence, all already in the cache.
+
+    Token m of sequence b sits at position i = T_b - M + m (evaluated at 0 if
+    that is negative) and is computed exactly as the prefill row i (section 3:
+    its own window [max(0, l(i)), i], its own candidates C_i, so the block is
+    causal among its tokens).  q [B,Hq,M,d]; k_cache/v_cache [B,Hkv,T,d];
+    seqlen [B]; lm [B,Hq,>=floor(max T/S),d].  Summaries come from the cache as
+    in ref_decode.  Returns dict (b, m) -> dict(out [Hq,d], sel {g: ids},
+    gap {g: gap}, s_hat {g: [G,n]}, n).
+    """
+    q = np.asarray(q, np.float64)
+    B, Hq, M, d = q.shape
+    qr = q if q_route is None else np.asarray(q_route, np.float64).reshape(q.shape)
+    k_cache, v_cache, lm = _arr(k_cache), _arr(v_cache), _arr(lm)
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    tau = (1.0 / math.sqrt(d)) if scale is None else float(scale)
+    results = {}
+    for b in range(B):
+        T = int(seqlen[b])
+        pos = [max(T - M + m, 0) for m in range(M)]
+        n_top = max(n_candidates(i, W, S) for i in pos)
+        summ = None
+        if mode != "exact" and n_top > 0:
+            summ = ref_summarize(k_cache[b:b + 1, :, : n_top * S], lm[b:b + 1, :, :n_top], S, tau,
+                                 mode=mode, store=store)
+        for m, i in enumerate(pos):
+            n = n_candidates(i, W, S)
+            out = np.zeros((Hq, d))
+            sels, gaps, shats = {}, {}, {}
+            for g in range(Hkv):
+                hs = slice(g * G, (g + 1) * G)
+                kg, vg = k_cache[b, g, : i + 1], v_cache[b, g, : i + 1]
+                if mode == "exact":
+                    fn = (lambda nn, qq=q[b, hs, m], kk=kg: ref_exact_logz(qq, kk, nn, S, tau))
+                elif n == 0:
+                    fn = (lambda nn: np.zeros((G, 0)))
+                else:
+                    ks, bs = summ
+                    fn = (lambda nn, qq=qr[b, hs, m], kk=ks[0, hs], bb=bs[0, hs]:
+                          ref_chunk_scores(qq, kk, bb, nn, tau))
+                r = ref_row(q[b, hs, m], kg, vg, i, S, W, K, tau, fn)
+                out[hs] = r["out"]
+                sels[g], gaps[g], shats[g] = r["sel"], r["gap"], r["s_hat"]
+            results[(b, m)] = dict(out=out, sel=sels, gap=gaps, s_hat=shats, n=n)
     return results
 
 

@@ -332,6 +332,43 @@ def test_decode_equals_last_prefill_row():
             assert dec[b]["sel"][g].tolist() == pre["sel"][g].tolist()
 
 
+def test_decode_multi_rows_are_causal_prefill_rows():
+    """Each token of a multi-token decode block is the prefill row at its own
+    position (section 3), M = 1 is the single-step decode, and a token's output
+    does not change when later tokens of the block change (causality)."""
+    w = synth.get_workload("decode_512k", N=2048, B=3, Hq=4, Hkv=2, W=256, K=4)
+    M = 3
+    T = [2048, 1500, 2]                                  # the last one is shorter than M
+    x = synth.make_decode_inputs(w, seqlen=T)
+    k, v, lm = (_np(x[n]) for n in ("k", "v", "lm"))
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((w.B, w.Hq, M, w.d))
+    dec = O.ref_decode_multi(q, k, v, T, lm, w.S, w.W, w.K)
+    for b in range(w.B):
+        for m in range(M):
+            i = max(T[b] - M + m, 0)
+            qq = np.zeros((1, w.Hq, i + 1, w.d))
+            qq[0, :, i] = q[b, :, m]
+            nck = (i + 1) // w.S
+            pre = O.ref_prefill_rows(qq, k[b:b + 1, :, : i + 1], v[b:b + 1, :, : i + 1],
+                                     lm[b:b + 1, :, :nck], [(0, i)], w.S, w.W, w.K)[(0, i)]
+            np.testing.assert_allclose(dec[(b, m)]["out"], pre["out"], atol=1e-12)
+            for g in range(w.Hkv):
+                assert dec[(b, m)]["sel"][g].tolist() == pre["sel"][g].tolist()
+    one = O.ref_decode_multi(q[:, :, -1:], k, v, T, lm, w.S, w.W, w.K)
+    ref1 = O.ref_decode(q[:, :, -1], k, v, T, lm, w.S, w.W, w.K)
+    for b in range(w.B):
+        np.testing.assert_allclose(one[(b, 0)]["out"], ref1[b]["out"], atol=1e-12)
+    # changing the last token of the block leaves the earlier tokens' outputs alone
+    k2, v2 = k.copy(), v.copy()
+    k2[0, :, T[0] - 1] += 3.0
+    v2[0, :, T[0] - 1] -= 2.0
+    dec2 = O.ref_decode_multi(q, k2, v2, T, lm, w.S, w.W, w.K)
+    for m in range(M - 1):
+        np.testing.assert_allclose(dec2[(0, m)]["out"], dec[(0, m)]["out"], atol=1e-12)
+    assert np.abs(dec2[(0, M - 1)]["out"] - dec[(0, M - 1)]["out"]).max() > 1e-3
+
+
 def test_mean_pool_is_surrogate_at_zero_landmark_query():
     """Mean pooling (section 2.2 equation) equals the Proposition 3.1 summary of
     a zero landmark query: uniform weights give the mean key and entropy ln S."""
