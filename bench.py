@@ -21,6 +21,7 @@ counters, and is null otherwise.
 """
 import hashlib
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -277,6 +278,46 @@ def paged_decode_bench(torch, hils, _lib, xd, wd, ks, bs, steps, log):
             "page_summaries_identical": same}
 
 
+def multi_decode_bench(torch, hils, _lib, xd, wd, ks, bs, M, steps, log):
+    """Decode of a block of M new tokens per sequence (the cache already holds
+    them; token m at position T - M + m).  The per-step summary read is shared
+    by the block's tokens, so tokens/s should grow with M at nearly the
+    single-step cost."""
+    B, Hq, _, d = xd["q"].shape
+    g = torch.Generator(device="cpu").manual_seed(17)
+    qm = (torch.randn((B, Hq, M, d), generator=g)).to(xd["q"].dtype).to(xd["q"].device)
+    qm[:, :, M - 1] = xd["q"][:, :, 0]
+    qm = qm.contiguous()
+    out = torch.empty_like(qm)
+    sel = torch.empty((B, wd.Hkv, M, wd.K), dtype=torch.int32, device=qm.device)
+    cfg = hils.make_cfg(B, wd.N, wd.Hq, wd.Hkv, d, wd.S, wd.W, wd.K, qm.dtype)
+    ws = torch.empty(max(1, _lib.lib().hils_decode_multi_workspace_bytes(ctypes.byref(cfg), M)),
+                     dtype=torch.uint8, device=qm.device)
+
+    def step():
+        hils.decode_multi(qm, xd["k"], xd["v"], xd["seqlen"], ks, bs, wd.S, wd.W, wd.K, out=out,
+                          sel=sel, ws=ws)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    _lib.profile_enable(True)
+    _lib.profile_read()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kt = _kernel_table(_lib.profile_read(), steps)
+    _lib.profile_enable(False)
+    log(f"decode block of {M} tokens {ms:.3f} ms/step; kernels {json.dumps(kt)}")
+    del ws, out, sel, qm
+    return {"M": M, "ms_per_step": ms, "steps_per_s": 1000.0 / ms,
+            "tokens_per_s": B * M * 1000.0 / ms, "kernels": kt}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,6 +453,9 @@ def main():
         # the same step over a paged cache (one chunk per page, pages randomly
         # placed), eagerly and replayed from a captured HIP graph
         dec["paged"] = paged_decode_bench(torch, hils, _lib, xd, wd, ks, bs, args.decode_steps, log)
+        # a block of 4 new tokens per sequence (draft / verification tokens)
+        dec["multi_token"] = multi_decode_bench(torch, hils, _lib, xd, wd, ks, bs, 4,
+                                                args.decode_steps, log)
         if not args.no_cpu:
             log("oracle baseline (decode sample)")
             dec["cpu_baseline"] = cpu_baseline_decode(xd, wd)

@@ -16,10 +16,11 @@ HILS_BF16, HILS_F32 = 0, 1
 MODES = {"surrogate": 0, "landmark_key": 1, "exact": 2, "mean_pool": 3}
 HILS_FLAG_GENERIC = 1
 HILS_FLAG_UNION = 2
+HILS_MAX_DECODE_QUERIES = 16
 
 EXPORTED = ("hils_workspace_bytes", "hils_summarize", "hils_prefill", "hils_decode",
-            "hils_summarize_paged", "hils_decode_paged",
-            "hils_strerror", "hils_abi_version", "hils_profile_enable", "hils_profile_read")
+            "hils_summarize_paged", "hils_decode_paged", "hils_decode_multi_workspace_bytes",
+            "hils_decode_multi", "hils_strerror", "hils_abi_version", "hils_profile_enable", "hils_profile_read")
 
 
 class HilsCfg(ctypes.Structure):
@@ -62,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.hils_decode_paged.argtypes = [cfgp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp,
                                         sz, vp]
         L.hils_decode_paged.restype = ctypes.c_int
+        L.hils_decode_multi_workspace_bytes.argtypes = [cfgp, i32]
+        L.hils_decode_multi_workspace_bytes.restype = sz
+        L.hils_decode_multi.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.hils_decode_multi.restype = ctypes.c_int
         L.hils_strerror.argtypes = [ctypes.c_int]
         L.hils_strerror.restype = ctypes.c_char_p
         L.hils_abi_version.argtypes = []

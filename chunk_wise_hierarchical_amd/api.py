@@ -143,6 +143,38 @@ def decode(q, k_cache, v_cache, seqlen, k_sum, b_sum, S, W, K, q_route=None, mod
     return out
 
 
+def decode_multi(q, k_cache, v_cache, seqlen, k_sum, b_sum, S, W, K, q_route=None,
+                 mode="surrogate", scale=0.0, out=None, sel=None, ws=None):
+    """HiLS decode of M new tokens per sequence. q [B,Hq,M,d] (token m at position
+    seqlen[b] - M + m); caches [B,Hkv,T,d]; seqlen [B] int32 (device);
+    k_sum [B,Hq,T//S,d], b_sum [B,Hq,T//S].  Returns out [B,Hq,M,d]; sel, if
+    given, [B,Hkv,M,K] int32 receives the selected chunk ids."""
+    B, Hq, M, d = q.shape
+    Hkv, T = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_sum", k_sum),
+                    ("q_route", q_route)):
+        _check_tensor(t, name, q.dtype, dev)
+    _check_tensor(seqlen, "seqlen", torch.int32, dev)
+    _check_tensor(b_sum, "b_sum", torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor(out, "out", q.dtype, dev)
+    _check_tensor(sel, "sel", torch.int32, dev)
+    cfg = make_cfg(B, T, Hq, Hkv, d, S, W, K, q.dtype, mode, scale)
+    need = _lib.lib().hils_decode_multi_workspace_bytes(ctypes.byref(cfg), int(M))
+    if need == 0:
+        raise ValueError(f"decode_multi: unsupported configuration (M={M})")
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    st = _lib.lib().hils_decode_multi(ctypes.byref(cfg), int(M), _ptr(q), _ptr(q_route),
+                                      _ptr(k_cache), _ptr(v_cache), _ptr(seqlen), _ptr(k_sum),
+                                      _ptr(b_sum), _ptr(out), _ptr(sel), _ptr(ws),
+                                      ctypes.c_size_t(ws.numel()), _stream(dev))
+    check(st, "hils_decode_multi")
+    return out
+
+
 def summarize_paged(k_pages, lm_pages, pages, S, N, out=None, mode="surrogate", scale=0.0):
     """Summaries of the pages listed in `pages` (int32 device tensor) of a paged
     cache: k_pages [P,Hkv,S,d], lm_pages [P,Hq,d].  Returns (k_sum_pages [P,Hq,d],

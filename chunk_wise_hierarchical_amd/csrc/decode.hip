@@ -1,9 +1,12 @@
-// Single-step HiLS decode: the prefill definition evaluated at i = T_b - 1
-// ("Hierarchical Sparse Attention Done Right", sections 3 and 4.1; serving
-// setup of section 7.1), split for bandwidth:
+// HiLS decode: the prefill definition evaluated at the M newest positions
+// i = T_b - M + m (M = 1: single-step decode; M > 1: a block of draft or
+// verification tokens, each attending causally) ("Hierarchical Sparse
+// Attention Done Right", sections 3 and 4.1; serving setup of section 7.1),
+// split for bandwidth:
 //   1. k_dec_score   — surrogate scores s_hat = scale*q_hat.k'_c + b'_c of every
 //                      candidate chunk (a streaming read of the summary cache,
-//                      the dominant HBM traffic);
+//                      the dominant HBM traffic, shared by up to 4 queries of a
+//                      sequence);
 //   2. k_dec_select  — per KV group: per-head log-sum-exp, max over heads, exact
 //                      top-K by 32-bit radix select, ties to the lower chunk id;
 //   3. k_dec_attn    — split-K attention: one workgroup per selected chunk or
@@ -14,6 +17,13 @@
 #include "hils_internal.h"
 
 namespace {
+
+// position of query m of a block of M new tokens of a sequence whose length is
+// seqlen (clamped into the cache; a position below 0 is evaluated at 0)
+__device__ __forceinline__ long long dec_pos(int32_t seqlen, int cap, int M, int m) {
+  const long long i = clamp_len(seqlen, cap) - M + m;
+  return i < 0 ? 0 : i;
+}
 
 template <typename T> struct Vec;
 template <> struct Vec<bf16_t> {
@@ -56,33 +66,36 @@ struct PageMap {
   }
 };
 
-template <typename T, bool PAGED>
+template <typename T, bool PAGED, int MT>
 __global__ void __launch_bounds__(256)
 k_dec_score(const T* __restrict__ qr, const T* __restrict__ ksum, const float* __restrict__ bsum,
             const int32_t* __restrict__ seqlen, float* __restrict__ scores, float* __restrict__ lsep,
-            int Hq, int nC, int nmax, int nsb, int N, int d, int S, int W, float tau, PageMap pm) {
+            int Hq, int nC, int nmax, int nsb, int N, int d, int S, int W, float tau, int M,
+            PageMap pm) {
   constexpr int V = Vec<T>::N;
   constexpr int MAXT = 256 / (16 * V) > 0 ? 256 / (16 * V) : 1;
   constexpr int R = 16;
-  __shared__ float red_m[4], red_s[4];
+  __shared__ float red_m[4][MT], red_s[4][MT];
   const long long bh = blockIdx.x;
   const int b = (int)(bh / Hq);
   const int c0 = blockIdx.y * SC_CPB;
+  // queries m0 .. m0 + mc - 1 of the sequence share every summary row read
+  const int m0 = blockIdx.z * MT, mc = min(MT, M - m0);
   const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15, lane = tid & 63, wv = tid >> 6;
-  float* lp = lsep + (bh * nsb + blockIdx.y) * 2;
+  auto lpart = [&](int mm) { return lsep + ((bh * M + m0 + mm) * nsb + blockIdx.y) * 2; };
   // Contiguous cache: the summary rows are read before the sequence length is
   // known (rows are clamped to the batch's longest candidate range, which the
   // cache always holds), so the loads overlap the length lookup; rows past
-  // this sequence's candidates are discarded below.  Paged cache: the page
+  // each query's candidates are discarded below.  Paged cache: the page
   // table is only defined for the sequence's own chunks, so the length comes
-  // first.
+  // first.  The last query of the group has the most candidates.
   const int r0 = c0 + grp * R;
   const int h = (int)(bh - (long long)b * Hq);
   int cmax = nmax - 1;
   if (PAGED) {
-    const int nb = n_cand(clamp_len(seqlen[b], N) - 1, W, S);
+    const int nb = n_cand(dec_pos(seqlen[b], N, M, m0 + mc - 1), W, S);
     if (c0 >= nb) {
-      if (tid == 0) { lp[0] = -INFINITY; lp[1] = 0.0f; }
+      if (tid < mc) { lpart(tid)[0] = -INFINITY; lpart(tid)[1] = 0.0f; }
       return;
     }
     cmax = nb - 1;
@@ -92,15 +105,19 @@ k_dec_score(const T* __restrict__ qr, const T* __restrict__ ksum, const float* _
   };
   const int cb = min(r0 + l16, cmax);
   const float bv = PAGED ? bsum[pm.page(b, cb) * Hq + h] : bsum[bh * nC + cb];
-  float acc[R];
+  float acc[MT][R];
 #pragma unroll
-  for (int u = 0; u < R; ++u) acc[u] = 0.0f;
+  for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+    for (int u = 0; u < R; ++u) acc[mm][u] = 0.0f;
 #pragma unroll
   for (int t = 0; t < MAXT; ++t) {
     const int e = (t * 16 + l16) * V;
     if (e < d) {
-      float qv[V];
-      Vec<T>::load(qr + bh * d + e, qv);
+      float qv[MT][V];
+#pragma unroll
+      for (int mm = 0; mm < MT; ++mm)      // past the group: a valid row, result unused
+        Vec<T>::load(qr + (bh * M + m0 + min(mm, mc - 1)) * d + e, qv[mm]);
       uint4 raw[R];
 #pragma unroll
       for (int u = 0; u < R; ++u) {
@@ -112,43 +129,53 @@ k_dec_score(const T* __restrict__ qr, const T* __restrict__ ksum, const float* _
         float kv[V];
         Vec<T>::load(reinterpret_cast<const T*>(&raw[u]), kv);
 #pragma unroll
-        for (int x = 0; x < V; ++x) acc[u] = fmaf(qv[x], kv[x], acc[u]);
+        for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+          for (int x = 0; x < V; ++x) acc[mm][u] = fmaf(qv[mm][x], kv[x], acc[mm][u]);
       }
     }
   }
-  const int n = n_cand(clamp_len(seqlen[b], N) - 1, W, S);
-  if (c0 >= n) {
-    if (tid == 0) { lp[0] = -INFINITY; lp[1] = 0.0f; }
+  const int nhi = n_cand(dec_pos(seqlen[b], N, M, m0 + mc - 1), W, S);
+  if (c0 >= nhi) {
+    if (tid < mc) { lpart(tid)[0] = -INFINITY; lpart(tid)[1] = 0.0f; }
     return;
   }
-  // reduce-scatter over the 16 lanes: after the step with mask m a lane keeps
-  // the half of its rows whose index bit m matches its own lane bit m
+  const int c = r0 + l16;
 #pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) {
-    const bool hi = (l16 & m) != 0;
+  for (int mm = 0; mm < MT; ++mm) {
+    if (mm < mc) {
+      // reduce-scatter over the 16 lanes: after the step with mask k a lane
+      // keeps the half of its rows whose index bit k matches its lane bit k
 #pragma unroll
-    for (int u = 0; u < m; ++u) {
-      const float keep = hi ? acc[u + m] : acc[u];
-      const float send = hi ? acc[u] : acc[u + m];
-      acc[u] = keep + __shfl_xor(send, m, 64);
+      for (int k2 = 8; k2 >= 1; k2 >>= 1) {
+        const bool hi = (l16 & k2) != 0;
+#pragma unroll
+        for (int u = 0; u < k2; ++u) {
+          const float keep = hi ? acc[mm][u + k2] : acc[mm][u];
+          const float send = hi ? acc[mm][u] : acc[mm][u + k2];
+          acc[mm][u] = keep + __shfl_xor(send, k2, 64);
+        }
+      }
+      const int n = n_cand(dec_pos(seqlen[b], N, M, m0 + mm), W, S);
+      const bool ok = c < n;
+      const float x = ok ? fmaf(tau, acc[mm][0], bv) : -INFINITY;
+      if (ok) scores[(bh * M + m0 + mm) * nmax + c] = x;
+      const float m = wave_max_f(x);
+      const float ex = ok ? __expf(x - m) : 0.0f;
+      const float sw = wave_sum_f(ex);
+      if (lane == 0) { red_m[wv][mm] = m; red_s[wv][mm] = sw; }
     }
   }
-  const int c = r0 + l16;
-  const bool ok = c < n;
-  const float x = ok ? fmaf(tau, acc[0], bv) : -INFINITY;
-  if (ok) scores[bh * nmax + c] = x;
-  const float m = wave_max_f(x);
-  const float ex = ok ? __expf(x - m) : 0.0f;
-  const float sw = wave_sum_f(ex);
-  if (lane == 0) { red_m[wv] = m; red_s[wv] = sw; }
   __syncthreads();
-  if (tid == 0) {
-    float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  if (tid < mc) {
+    const int mm = tid;
+    float Mx = fmaxf(fmaxf(red_m[0][mm], red_m[1][mm]), fmaxf(red_m[2][mm], red_m[3][mm]));
     float L = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) L += (red_s[w] > 0.0f) ? red_s[w] * __expf(red_m[w] - M) : 0.0f;
-    lp[0] = M;
-    lp[1] = L;
+    for (int w = 0; w < 4; ++w)
+      L += (red_s[w][mm] > 0.0f) ? red_s[w][mm] * __expf(red_m[w][mm] - Mx) : 0.0f;
+    lpart(mm)[0] = Mx;
+    lpart(mm)[1] = L;
   }
 }
 
@@ -184,7 +211,7 @@ __global__ void __launch_bounds__(SEL_NT)
 k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
              const int32_t* __restrict__ seqlen, uint32_t* __restrict__ keys,
              int32_t* __restrict__ sel, float* __restrict__ slog, int Hq, int Hkv, int G, int nmax,
-             int nsb, int N, int S, int W, int K) {
+             int nsb, int N, int S, int W, int K, int M) {
   extern __shared__ uint32_t sel_keys_lds[];
   __shared__ uint32_t hist[256];
   __shared__ float Lh[8];
@@ -192,24 +219,26 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
   __shared__ int sh_digit, sh_need;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int bg = blockIdx.x;
+  const int bgm = blockIdx.x;                 // (sequence, KV group, query)
+  const int m = bgm % M, bg = bgm / M;
   const int b = bg / Hkv, g = bg % Hkv;
-  const int n = n_cand(clamp_len(seqlen[b], N) - 1, W, S);
+  const int n = n_cand(dec_pos(seqlen[b], N, M, m), W, S);
   const int kk = min(K, n);
-  const long long hbase = (long long)b * Hq + (long long)g * G;
-  int32_t* so = sel + (long long)bg * K;
+  // per-head rows of this query: ((b * Hq + g * G + r) * M + m)
+  auto hrow = [&](int r) { return ((long long)b * Hq + (long long)g * G + r) * M + m; };
+  int32_t* so = sel + (long long)bgm * K;
   for (int t = tid; t < K; t += SEL_NT) if (t >= kk) so[t] = -1;
   for (int t = tid; t < G * K; t += SEL_NT) {
     const int r = t / K, kx = t % K;
-    if (kx >= kk) slog[(hbase + r) * K + kx] = 0.0f;
+    if (kx >= kk) slog[hrow(r) * K + kx] = 0.0f;
   }
   if (n == 0) return;
-  uint32_t* ky = (n <= SEL_LDS_KEYS) ? sel_keys_lds : keys + (long long)bg * nmax;
+  uint32_t* ky = (n <= SEL_LDS_KEYS) ? sel_keys_lds : keys + (long long)bgm * nmax;
 
   if (G > 1) {
     // per-head log-sum-exp from the scoring workgroups' (max, sum exp) partials
     for (int r = wv; r < G; r += SEL_NW) {
-      const float* lp = lsep + (hbase + r) * nsb * 2;
+      const float* lp = lsep + hrow(r) * nsb * 2;
       float m = -INFINITY, s = 0.0f;
       for (int t = lane; t < nsb; t += 64) lse_merge(m, s, lp[2 * t], lp[2 * t + 1]);
 #pragma unroll
@@ -227,7 +256,7 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
 #pragma unroll
     for (int u = 0; u < KU; ++u) gs[u] = -INFINITY;
     for (int r = 0; r < G; ++r) {
-      const float* sr = scores + (hbase + r) * nmax;
+      const float* sr = scores + hrow(r) * nmax;
       const float lr = (G == 1) ? 0.0f : Lh[r];
       float x[KU];
 #pragma unroll
@@ -299,7 +328,7 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
     const int tot = sel_excl_scan(f, wsum, pos);
     if (f) {
       so[running + pos] = c;
-      for (int r = 0; r < G; ++r) slog[(hbase + r) * K + running + pos] = scores[(hbase + r) * nmax + c];
+      for (int r = 0; r < G; ++r) slog[hrow(r) * K + running + pos] = scores[hrow(r) * nmax + c];
     }
     running += tot;
     eq_seen += eqtot;
@@ -317,7 +346,8 @@ template <typename T, bool PAGED>
 __global__ void __launch_bounds__(AT_NT)
 k_dec_attn(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
            const int32_t* __restrict__ seqlen, const int32_t* __restrict__ sel, float* __restrict__ part,
-           int Hq, int Hkv, int G, int N, int d, int S, int W, int K, int NS, float tau, PageMap pm) {
+           int Hq, int Hkv, int G, int N, int d, int S, int W, int K, int NS, float tau, int M,
+           PageMap pm) {
   constexpr int V = Vec<T>::N;
   extern __shared__ __align__(16) unsigned char sm_raw[];
   const int kstr = d + V;                                     // padded row (elements), 16-byte multiple
@@ -328,14 +358,18 @@ k_dec_attn(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
   float* ps = qs + G * d;                                     // [G][SP], zero past the split
   __shared__ float hm[8], hl[8];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int bg = blockIdx.x, s = blockIdx.y;
+  const int bgm = blockIdx.x, s = blockIdx.y;      // (sequence, KV group, query), split
+  const int m = bgm % M, bg = bgm / M;
   const int b = bg / Hkv, g = bg % Hkv;
-  const long long hbase = (long long)b * Hq + (long long)g * G;
+  auto hrow = [&](int r) { return ((long long)b * Hq + (long long)g * G + r) * M + m; };
   // loads that do not need the sequence length go first: the query rows and,
   // for a chunk split, its chunk id (slots past the selection hold -1)
-  for (int t = tid; t < G * d; t += AT_NT) qs[t] = Elt<T>::ld(q + hbase * d + t);
-  const int csel = (s < K) ? sel[(long long)bg * K + s] : -1;
-  const long long i = clamp_len(seqlen[b], N) - 1;
+  for (int t = tid; t < G * d; t += AT_NT) {
+    const int r = t / d;
+    qs[t] = Elt<T>::ld(q + hrow(r) * d + (t - r * d));
+  }
+  const int csel = (s < K) ? sel[(long long)bgm * K + s] : -1;
+  const long long i = dec_pos(seqlen[b], N, M, m);
   long long j0 = 0;
   int jn = 0;
   if (s < K) {
@@ -347,7 +381,7 @@ k_dec_attn(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
   if (jn == 0) {               // empty split: weight 0 in the combine, zero partial
     for (int t = tid; t < G * (d + 2); t += AT_NT) {
       const int r = t / (d + 2), e = t - r * (d + 2);
-      part[((hbase + r) * NS + s) * (long long)(d + 2) + e] = (e == 0) ? -INFINITY : 0.0f;
+      part[(hrow(r) * NS + s) * (long long)(d + 2) + e] = (e == 0) ? -INFINITY : 0.0f;
     }
     return;
   }
@@ -427,7 +461,7 @@ k_dec_attn(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
         }
       }
     }
-    float* pp = part + ((hbase + r) * NS + s) * (long long)(d + 2);
+    float* pp = part + (hrow(r) * NS + s) * (long long)(d + 2);
     pp[2 + e] = a0;
     pp[3 + e] = a1;
     if (e == 0) { pp[0] = hm[r]; pp[1] = hl[r]; }
@@ -441,11 +475,11 @@ template <typename T>
 __global__ void __launch_bounds__(256)
 k_dec_combine(const float* __restrict__ part, const float* __restrict__ slog,
               const int32_t* __restrict__ seqlen, T* __restrict__ out, int Hq, int G, int N, int d,
-              int S, int W, int K, int NS, int nwin) {
+              int S, int W, int K, int NS, int nwin, int M) {
   extern __shared__ float wsplit[];          // [NS] weight of each split's unnormalised o
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int b = bh / Hq;
-  const long long i = clamp_len(seqlen[b], N) - 1;
+  const int bh = blockIdx.x, tid = threadIdx.x;   // ((b * Hq + h) * M + m)
+  const int b = bh / (Hq * M), m = bh % M;
+  const long long i = dec_pos(seqlen[b], N, M, m);
   const int n = n_cand(i, W, S);
   const int kk = min(K, n);
   const float* pb = part + (long long)bh * NS * (d + 2);
@@ -487,6 +521,17 @@ k_dec_combine(const float* __restrict__ part, const float* __restrict__ slog,
   }
 }
 
+template <typename T, bool PAGED, int MT>
+void launch_score(const HilsShape& s, const void* qr, const int32_t* seqlen, const void* ksum,
+                  const float* bsum, float* scores, float* lsep, unsigned nsb, PageMap pm,
+                  hipStream_t st) {
+  const unsigned nz = (unsigned)((s.M + MT - 1) / MT);
+  { HilsProfScope ps_("k_dec_score", st);
+    hipLaunchKernelGGL((k_dec_score<T, PAGED, MT>), dim3(s.B * s.Hq, nsb, nz), dim3(256), 0, st,
+                       (const T*)qr, (const T*)ksum, bsum, seqlen, scores, lsep, s.Hq, s.nC, s.nmax,
+                       (int)nsb, s.N, s.d, s.S, s.W, (float)s.tau, s.M, pm); }
+}
+
 template <typename T, bool PAGED>
 void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const void* k, const void* v,
                      const int32_t* seqlen, const void* ksum, const float* bsum, void* out,
@@ -499,21 +544,22 @@ void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const vo
   const size_t ashm = 2 * (size_t)s.S * (s.d + 16 / esz) * esz + (size_t)s.G * s.d * 4 +
                       (size_t)s.G * ((s.S + 3) & ~3) * 4;
   const size_t cshm = (size_t)NS * 4;
-  if (nsb > 0)
-    { HilsProfScope ps_("k_dec_score", st); hipLaunchKernelGGL((k_dec_score<T, PAGED>), dim3(s.B * s.Hq, nsb), dim3(256), 0, st,
-                       (const T*)qr, (const T*)ksum, bsum, seqlen, scores, lsep, s.Hq,
-                       s.nC, s.nmax, (int)nsb, s.N, s.d, s.S, s.W, tau, pm); }
+  if (nsb > 0) {
+    if (s.M == 1) launch_score<T, PAGED, 1>(s, qr, seqlen, ksum, bsum, scores, lsep, nsb, pm, st);
+    else if (s.M == 2) launch_score<T, PAGED, 2>(s, qr, seqlen, ksum, bsum, scores, lsep, nsb, pm, st);
+    else launch_score<T, PAGED, 4>(s, qr, seqlen, ksum, bsum, scores, lsep, nsb, pm, st);
+  }
   const size_t sshm = (size_t)4 * (size_t)min(s.nmax > 0 ? s.nmax : 1, SEL_LDS_KEYS);
   hipFuncSetAttribute((const void*)k_dec_select, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sshm);
-  { HilsProfScope ps_("k_dec_select", st); hipLaunchKernelGGL(k_dec_select, dim3(s.B * s.Hkv), dim3(SEL_NT), sshm, st, scores, lsep, seqlen,
+  { HilsProfScope ps_("k_dec_select", st); hipLaunchKernelGGL(k_dec_select, dim3(s.B * s.Hkv * s.M), dim3(SEL_NT), sshm, st, scores, lsep, seqlen,
                      keys, sel, slog, s.Hq, s.Hkv, s.G, s.nmax > 0 ? s.nmax : 1, (int)nsb, s.N, s.S,
-                     s.W, s.K); }
+                     s.W, s.K, s.M); }
   hipFuncSetAttribute((const void*)k_dec_attn<T, PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
-  { HilsProfScope ps_("k_dec_attn", st); hipLaunchKernelGGL((k_dec_attn<T, PAGED>), dim3(s.B * s.Hkv, NS), dim3(AT_NT), ashm, st,
+  { HilsProfScope ps_("k_dec_attn", st); hipLaunchKernelGGL((k_dec_attn<T, PAGED>), dim3(s.B * s.Hkv * s.M, NS), dim3(AT_NT), ashm, st,
                      (const T*)q, (const T*)k, (const T*)v, seqlen, sel, part,
-                     s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, NS, tau, pm); }
-  { HilsProfScope ps_("k_dec_combine", st); hipLaunchKernelGGL(k_dec_combine<T>, dim3(s.B * s.Hq), dim3(256), cshm, st, part, slog,
-                     seqlen, (T*)out, s.Hq, s.G, s.N, s.d, s.S, s.W, s.K, NS, s.nwin); }
+                     s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, NS, tau, s.M, pm); }
+  { HilsProfScope ps_("k_dec_combine", st); hipLaunchKernelGGL(k_dec_combine<T>, dim3(s.B * s.Hq * s.M), dim3(256), cshm, st, part, slog,
+                     seqlen, (T*)out, s.Hq, s.G, s.N, s.d, s.S, s.W, s.K, NS, s.nwin, s.M); }
 }
 
 }  // namespace

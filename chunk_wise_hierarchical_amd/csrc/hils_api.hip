@@ -115,12 +115,13 @@ DecodeLayout decode_layout(const HilsShape& s) {
   DecodeLayout L{};
   const size_t nm = (size_t)(s.nmax > 0 ? s.nmax : 1);
   size_t off = 0;
-  L.scores = off; off += align_up((size_t)s.B * s.Hq * nm * 4);
-  L.keys = off;   off += align_up((size_t)s.B * s.Hkv * nm * 4);
-  L.slog = off;   off += align_up((size_t)s.B * s.Hq * s.K * 4);
-  L.sel = off;    off += align_up((size_t)s.B * s.Hkv * s.K * 4);
-  L.part = off;   off += align_up((size_t)s.B * s.Hq * (s.K + s.nwin) * (s.d + 2) * 4);
-  L.lsep = off;   off += align_up((size_t)s.B * s.Hq * ((nm + HILS_DEC_SCORE_ROWS - 1) / HILS_DEC_SCORE_ROWS) * 8);
+  const size_t BM = (size_t)s.B * s.M;          // (sequence, query) rows
+  L.scores = off; off += align_up(BM * s.Hq * nm * 4);
+  L.keys = off;   off += align_up(BM * s.Hkv * nm * 4);
+  L.slog = off;   off += align_up(BM * s.Hq * s.K * 4);
+  L.sel = off;    off += align_up(BM * s.Hkv * s.K * 4);
+  L.part = off;   off += align_up(BM * s.Hq * (s.K + s.nwin) * (s.d + 2) * 4);
+  L.lsep = off;   off += align_up(BM * s.Hq * ((nm + HILS_DEC_SCORE_ROWS - 1) / HILS_DEC_SCORE_ROWS) * 8);
   L.total = off;
   return L;
 }
@@ -300,6 +301,43 @@ hils_status hils_decode(const hils_cfg* cfg, const void* q, const void* q_route,
   hils_status r = make_shape(cfg, s);
   if (r != HILS_OK) return r;
   if (s.mode == HILS_SCORE_EXACT) return HILS_E_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !seqlen || !out) return HILS_E_ARG;
+  if (s.nmax > 0 && (!k_sum || !b_sum)) return HILS_E_ARG;
+  const void* ptrs[] = {q, q_route, k_cache, v_cache, seqlen, k_sum, b_sum, out, sel, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return HILS_E_ARG;
+  if (s.d % (s.dtype == HILS_BF16 ? 8 : 4) != 0) return HILS_E_UNSUPPORTED;
+  const DecodeLayout L = decode_layout(s);
+  if (ws_bytes < L.total || (L.total > 0 && !ws)) return HILS_E_WORKSPACE;
+  char* w = static_cast<char*>(ws);
+  int32_t* sl = sel ? sel : (int32_t*)(w + L.sel);
+  const void* qr = q_route ? q_route : q;
+  return hip_status(hils_launch_decode(s, q, qr, k_cache, v_cache, seqlen, k_sum, b_sum, out, sl,
+                                       (float*)(w + L.scores), (uint32_t*)(w + L.keys),
+                                       (float*)(w + L.slog), (float*)(w + L.part),
+                                       (float*)(w + L.lsep), nullptr, 0, 0, (hipStream_t)stream));
+}
+
+size_t hils_decode_multi_workspace_bytes(const hils_cfg* cfg, int32_t M) {
+  HilsShape s;
+  if (make_shape(cfg, s) != HILS_OK || M < 1 || M > HILS_MAX_DECODE_QUERIES) return 0;
+  s.M = M;
+  return decode_layout(s).total;
+}
+
+hils_status hils_decode_multi(const hils_cfg* cfg, int32_t M, const void* q, const void* q_route,
+                              const void* k_cache, const void* v_cache, const int32_t* seqlen,
+                              const void* k_sum, const float* b_sum, void* out, int32_t* sel,
+                              void* ws, size_t ws_bytes, void* stream) {
+  HilsShape s;
+  hils_status r = make_shape(cfg, s);
+  if (r != HILS_OK) return r;
+  if (M < 1 || M > s.N) return HILS_E_ARG;
+  if (M > HILS_MAX_DECODE_QUERIES) return HILS_E_UNSUPPORTED;
+  if (s.mode == HILS_SCORE_EXACT) return HILS_E_UNSUPPORTED;
+  s.M = M;
+  if ((long long)s.B * s.Hkv * M >= (1LL << 31) || (long long)s.B * s.Hq * M >= (1LL << 31))
+    return HILS_E_UNSUPPORTED;
   if (!q || !k_cache || !v_cache || !seqlen || !out) return HILS_E_ARG;
   if (s.nmax > 0 && (!k_sum || !b_sum)) return HILS_E_ARG;
   const void* ptrs[] = {q, q_route, k_cache, v_cache, seqlen, k_sum, b_sum, out, sel, ws};

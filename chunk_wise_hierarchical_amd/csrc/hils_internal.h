@@ -12,6 +12,7 @@ struct HilsShape {
   int nmax;    // |C_{N-1}|: most candidate chunks of any position
   int nwin;    // max number of S-token tiles a window spans
   double tau;  // logit scale
+  int M = 1;   // decode: new tokens (queries) per sequence
 };
 
 // Kernel timing (hils_profile_enable): records a HIP event pair around each launch.

@@ -134,6 +134,25 @@ hils_status hils_decode(const hils_cfg* cfg, const void* q, const void* q_route,
                         const void* k_sum, const float* b_sum, void* out, int32_t* sel,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Multi-query decode: M new tokens of each sequence (draft or verification
+ * tokens, 1 <= M <= HILS_MAX_DECODE_QUERIES) are already in the cache at
+ * positions T_b - M .. T_b - 1 (T_b = seqlen[b] >= M), and query m is the
+ * query of the token at position T_b - M + m.  Each query is the prefill row
+ * at its own position (section 3; causal among the new tokens: its window ends
+ * at its own position, and its candidate chunks are the complete chunks
+ * before its window).  Layouts:
+ *   q, q_route, out : [B][Hq][M][d];   sel (optional) : [B][Hkv][M][K].
+ * k_sum/b_sum as for hils_decode.  The chunk-summary read, the dominant
+ * traffic, is shared by up to 4 queries of a sequence.  A position below 0
+ * (seqlen < M) is evaluated at position 0.  M = 1 is hils_decode.  Workspace:
+ * hils_decode_multi_workspace_bytes(cfg, M) (0 for an invalid cfg or M). */
+#define HILS_MAX_DECODE_QUERIES 16
+size_t hils_decode_multi_workspace_bytes(const hils_cfg* cfg, int32_t M);
+hils_status hils_decode_multi(const hils_cfg* cfg, int32_t M, const void* q, const void* q_route,
+                              const void* k_cache, const void* v_cache, const int32_t* seqlen,
+                              const void* k_sum, const float* b_sum, void* out, int32_t* sel,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* Paged KV cache with one chunk per page (the pages' serving setup, section
  * 7.1: KV page size equal to the chunk size S).  Physical page p holds
  *   k_pages, v_pages : [num_pages][Hkv][S][d]   the S tokens of one chunk,

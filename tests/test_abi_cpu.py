@@ -129,6 +129,28 @@ def test_paged_entry_points_reject_bad_arguments(L):
     assert L.hils_summarize_paged(ctypes.byref(c), p, p, p, 0, 40, p, p, None) == _lib.HILS_OK
 
 
+def test_multi_decode_arguments_and_workspace(L):
+    p = ctypes.c_void_p(0x10000)
+    c = _cfg(N=1024)
+    ws = ctypes.c_size_t(1 << 30)
+
+    def call(M, cfg=c, wsb=ws, seqlen=p):
+        return L.hils_decode_multi(ctypes.byref(cfg), M, p, None, p, p, seqlen, p, p, p, None, p,
+                                   wsb, None)
+    assert call(0) == _lib.HILS_E_ARG
+    assert call(17) == _lib.HILS_E_UNSUPPORTED
+    assert call(4, seqlen=None) == _lib.HILS_E_ARG
+    assert call(4, cfg=_cfg(N=1024, mode=2)) == _lib.HILS_E_UNSUPPORTED
+    assert call(4, wsb=ctypes.c_size_t(16)) == _lib.HILS_E_WORKSPACE
+    # the per-row buffers of an M-token block are those of B*M single decodes
+    one = L.hils_decode_multi_workspace_bytes(ctypes.byref(c), 1)
+    assert one == L.hils_workspace_bytes(ctypes.byref(c), 1)
+    four = L.hils_decode_multi_workspace_bytes(ctypes.byref(c), 4)
+    assert four == L.hils_workspace_bytes(ctypes.byref(_cfg(N=1024, B=4 * c.B)), 1)
+    assert L.hils_decode_multi_workspace_bytes(ctypes.byref(c), 0) == 0
+    assert L.hils_decode_multi_workspace_bytes(ctypes.byref(c), 17) == 0
+
+
 def test_product_path_does_not_touch_the_oracle():
     for dirpath, _, files in os.walk(PKG):
         for f in files:
