@@ -169,12 +169,15 @@ k_pair_scatter(const int32_t* __restrict__ sel, uint32_t* __restrict__ cur,
 // ---------------------------------------------------------------------------
 // window attention + fusion weights
 
+// One workgroup per 128/G consecutive queries of one (batch, KV group): 128
+// MFMA rows, each wavefront owning two 16-row blocks, so every K / V^T
+// fragment a wavefront reads from LDS feeds two MFMAs.
 template <int G>
 __global__ void __launch_bounds__(NT, 2)
 k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
            const bf16_t* __restrict__ vt, float* __restrict__ swa, float* __restrict__ lz,
            int Hq, int Hkv, int N, int W, int nCc, float tau2, int i0, int qs, int nqb) {
-  constexpr int QA = 64 / G;
+  constexpr int QA = 128 / G;
   extern __shared__ __align__(16) unsigned char sm[];
   bf16_t* ktile = reinterpret_cast<bf16_t*>(sm);
   bf16_t* vtile = reinterpret_cast<bf16_t*>(sm + KT_BYTES);
@@ -190,18 +193,25 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const long long hb = b * Hq + (long long)g * G;
   const long long kvbase = bg;
 
-  const int colr = 16 * w + (lane & 15);
-  const int qa = colr / G, h = colr % G;
+  // row block rb of this wavefront: rows 32 w + 16 rb + (lane & 15) = (query qa, head h)
+  const int h = (lane & 15) % G;
   const int lq = lane >> 4;
-  const bool vcol = qa < qcount;
-  const int iq = ib0 + qa;
-  bf16x8_t bq[4];
+  // positions fit 32 bits here (the fast path caps N at 2^20)
+  bool vcol[2];
+  int iq[2], wlo[2];
+  bf16x8_t bq[2][4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    if (vcol) bq[ks] = ld_bf16x8(q + ((hb + h) * N + iq) * (long long)D + 32 * ks + 8 * lq);
-    else bq[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+  for (int rb = 0; rb < 2; ++rb) {
+    const int qa = (32 * w + 16 * rb + (lane & 15)) / G;
+    vcol[rb] = qa < qcount;
+    iq[rb] = ib0 + qa;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (vcol[rb]) bq[rb][ks] = ld_bf16x8(q + ((hb + h) * N + iq[rb]) * (long long)D + 32 * ks + 8 * lq);
+      else bq[rb][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+    }
+    wlo[rb] = vcol[rb] ? (int)window_start(iq[rb], W, S) : 0;
   }
-  const long long wlo = vcol ? window_start(iq, W, S) : 0;
 
   // rows past N read row N-1 (masked); V^T is zero there
   auto load_chunk = [&](uint4* r, int c) {
@@ -229,103 +239,110 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       st_u4(vtile + row * VSTR + part * 8, r[4 + p]);
     }
   };
-  f32x4_t acc[8];
+  f32x4_t acc[2][8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) acc[dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.0f;
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[rb][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
 
   auto window_tile = [&](int c) {
-    f32x4_t s[4];
+    f32x4_t s[2][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const int mm = lane & 15;
       const int key = 32 * (kt >> 1) + 8 * (mm >> 2) + 4 * (kt & 1) + (mm & 3);
-      f32x4_t a4 = {0.f, 0.f, 0.f, 0.f};
+      s[0][kt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      s[1][kt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        a4 = mfma16(ld_bf16x8(ktile + key * KSTR + kswz(key, 4 * ks + lq) * 8), bq[ks], a4);
-      s[kt] = a4;
-    }
-    float x[16];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const long long j = (long long)c * S + 32 * (kt >> 1) + 8 * lq + 4 * (kt & 1) + e;
-        const bool ok = vcol && j >= wlo && j <= iq;
-        const float v2 = ok ? s[kt][e] * tau2 : -INFINITY;
-        x[kt * 4 + e] = v2;
-        mt = fmaxf(mt, v2);
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8_t kf = ld_bf16x8(ktile + key * KSTR + kswz(key, 4 * ks + lq) * 8);
+        s[0][kt] = mfma16(kf, bq[0][ks], s[0][kt]);
+        s[1][kt] = mfma16(kf, bq[1][ks], s[1][kt]);
       }
-    mt = max_x32(max_x16(mt));
-    const float mnew = fmaxf(m, mt);
-    float p[16];
-    float ps = 0.0f;
-    float scale = 1.0f;
-    if (mnew == -INFINITY) {
-#pragma unroll
-      for (int t = 0; t < 16; ++t) p[t] = 0.0f;
-    } else {
-      scale = fast_exp2(m - mnew);
-#pragma unroll
-      for (int t = 0; t < 16; ++t) { p[t] = fast_exp2(x[t] - mnew); ps += p[t]; }
     }
-    ps = sum_x32(sum_x16(ps));
-    l = l * scale + ps;
-    m = mnew;
+    bf16x8_t pb[2][2];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[dt] *= scale;
-    bf16x8_t pb[2];
+    for (int rb = 0; rb < 2; ++rb) {
+      float x[16];
+      float mt = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const float* pp = p + 8 * kb;
-      const uint4 u = make_uint4(pack_bf16x2(pp[0], pp[1]), pack_bf16x2(pp[2], pp[3]),
-                                 pack_bf16x2(pp[4], pp[5]), pack_bf16x2(pp[6], pp[7]));
-      pb[kb] = __builtin_bit_cast(bf16x8_t, u);
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = c * S + 32 * (kt >> 1) + 8 * lq + 4 * (kt & 1) + e;
+          const bool ok = vcol[rb] && j >= wlo[rb] && j <= iq[rb];
+          const float v2 = ok ? s[rb][kt][e] * tau2 : -INFINITY;
+          x[kt * 4 + e] = v2;
+          mt = fmaxf(mt, v2);
+        }
+      mt = max_x32(max_x16(mt));
+      const float mnew = fmaxf(m[rb], mt);
+      float p[16];
+      float ps = 0.0f;
+      float scale = 1.0f;
+      if (mnew == -INFINITY) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) p[t] = 0.0f;
+      } else {
+        scale = fast_exp2(m[rb] - mnew);
+#pragma unroll
+        for (int t = 0; t < 16; ++t) { p[t] = fast_exp2(x[t] - mnew); ps += p[t]; }
+      }
+      ps = sum_x32(sum_x16(ps));
+      l[rb] = l[rb] * scale + ps;
+      m[rb] = mnew;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[rb][dt] *= scale;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float* pp = p + 8 * kb;
+        const uint4 u = make_uint4(pack_bf16x2(pp[0], pp[1]), pack_bf16x2(pp[2], pp[3]),
+                                   pack_bf16x2(pp[4], pp[5]), pack_bf16x2(pp[6], pp[7]));
+        pb[rb][kb] = __builtin_bit_cast(bf16x8_t, u);
+      }
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        acc[dt] = mfma16(ld_bf16x8(vtile + (16 * dt + (lane & 15)) * VSTR + 32 * kb + 8 * lq),
-                         pb[kb], acc[dt]);
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t vf = ld_bf16x8(vtile + (16 * dt + (lane & 15)) * VSTR + 32 * kb + 8 * lq);
+        acc[0][dt] = mfma16(vf, pb[0][kb], acc[0][dt]);
+        acc[1][dt] = mfma16(vf, pb[1][kb], acc[1][dt]);
+      }
   };
 
   const int cw_lo = (int)(window_start(ib0, W, S) / S);
   const int cw_hi = (ib0 + qcount - 1) / S;
   const int nw = cw_hi - cw_lo + 1;
-  uint4 ra[8], rb[8];
-  auto step = [&](int idx, uint4* nxt, uint4* far) {
-    load_chunk(far, cw_lo + min(idx + 2, nw - 1));
-    window_tile(cw_lo + idx);
-    __syncthreads();
-    store_chunk(nxt);
-    __syncthreads();
-  };
+  // one register buffer: tile idx + 1 is loaded while tile idx is scored
+  uint4 ra[8];
   load_chunk(ra, cw_lo);
-  load_chunk(rb, cw_lo + min(1, nw - 1));
   store_chunk(ra);
   __syncthreads();
-  int idx = 0;
-  for (; idx + 1 < nw; idx += 2) {
-    step(idx, rb, ra);
-    step(idx + 1, ra, rb);
+  for (int idx = 0; idx < nw; ++idx) {
+    load_chunk(ra, cw_lo + min(idx + 1, nw - 1));
+    window_tile(cw_lo + idx);
+    __syncthreads();
+    store_chunk(ra);             // past the last tile: rewrites the last tile, unused
+    __syncthreads();
   }
-  if (idx < nw) step(idx, rb, ra);
 
   // normalised window output and its log-mass (base 2)
-  if (vcol) {
-    const long long row = (long long)bg * qs + (iq - i0);
-    const float il = 1.0f / l;
-    float* sp = swa + (row * G + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const float4 o = make_float4(acc[dt][0] * il, acc[dt][1] * il, acc[dt][2] * il,
-                                   acc[dt][3] * il);
-      *reinterpret_cast<float4*>(sp + 16 * dt + 4 * lq) = o;
+  for (int rb = 0; rb < 2; ++rb) {
+    if (vcol[rb]) {
+      const long long row = (long long)bg * qs + (iq[rb] - i0);
+      const float il = 1.0f / l[rb];
+      float* sp = swa + (row * G + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const float4 o = make_float4(acc[rb][dt][0] * il, acc[rb][dt][1] * il, acc[rb][dt][2] * il,
+                                     acc[rb][dt][3] * il);
+        *reinterpret_cast<float4*>(sp + 16 * dt + 4 * lq) = o;
+      }
+      if (lq == 0) lz[row * G + h] = m[rb] + log2f(l[rb]);
     }
-    if (lq == 0) lz[row * G + h] = m + log2f(l);
   }
 }
 
@@ -624,7 +641,7 @@ template <int G>
 hipError_t launch_pairs(const HilsShape& s, const void* q, const void* qr, const void* k,
                         const void* vt, const void* ksum, const float* bsum, const int32_t* sel,
                         void* out, const HilsPairBufs& pb, hipStream_t st) {
-  constexpr int QA = 64 / G;
+  constexpr int QA = 128 / G;   // queries per window workgroup
   constexpr int TQ = 64 / G;
   const int F = s.B * s.Hkv * s.nC;
   const float tau2 = (float)(s.tau * 1.4426950408889634);
