@@ -88,6 +88,22 @@ __device__ __forceinline__ float xshfl_f(float v, int stride) {
 __device__ __forceinline__ uint64_t xshfl_u64(uint64_t v, int stride) {
   return ((uint64_t)xshfl((uint32_t)(v >> 32), stride) << 32) | xshfl((uint32_t)v, stride);
 }
+// maximum / sum over all 64 lanes (xor butterfly: every lane gets the same value)
+__device__ __forceinline__ float wmax64(float v) {
+  v = fmaxf(v, xshfl_f(v, 1));
+  v = fmaxf(v, xshfl_f(v, 2));
+  v = fmaxf(v, xshfl_f(v, 4));
+  v = fmaxf(v, xshfl_f(v, 8));
+  return max_x32(max_x16(v));
+}
+__device__ __forceinline__ float wsum64(float v) {
+  v += xshfl_f(v, 1);
+  v += xshfl_f(v, 2);
+  v += xshfl_f(v, 4);
+  v += xshfl_f(v, 8);
+  return sum_x32(sum_x16(v));
+}
+
 // value of lane 63 - l (= l ^ 63)
 __device__ __forceinline__ uint32_t lane_reverse(uint32_t v) {
   const uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);   // l ^ 15

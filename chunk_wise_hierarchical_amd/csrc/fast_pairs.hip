@@ -37,6 +37,7 @@ constexpr int KSTR = D;       // K tile row stride (elements); 16-byte parts XOR
 constexpr int VSTR = S + 8;   // V^T tile row stride (elements)
 constexpr int PQ = 512;       // queries per list-building workgroup
 constexpr int RQ = 16;        // queries per reduce workgroup
+constexpr int RU = 8;         // partial rows in flight per reduce thread
 constexpr int PTPW = HILS_PAIR_TPW;   // tiles per pair-attention workgroup
 
 __device__ __forceinline__ int kswz(int r, int p) { return p ^ (((r >> 1) & 12) | (r & 3)); }
@@ -577,25 +578,24 @@ k_pair_reduce(const float* __restrict__ swa, const float* __restrict__ lz,
     if (qi < qs) wk[it * (K + 1) + K] = lz[((long long)bg * qs + qi) * G + h];
   }
   __syncthreads();
-  // alpha = softmax over {s_hat_c} U {log Z_swa}, one thread per (query, head)
-  for (int it = tid; it < RQ * G; it += NT) {
-    const int qq = it / G;
-    const int qi = q0 + qq;
-    if (qi >= qs) continue;
-    const int kk = min(K, n_cand((long long)i0 + qi, W, S));
-    float* wr = wk + it * (K + 1);
-    const float lzv = wr[K];
-    float M2 = lzv;
-    for (int kx = 0; kx < kk; ++kx) M2 = fmaxf(M2, wr[kx]);
-    float Z = fast_exp2(lzv - M2);
-    for (int kx = 0; kx < kk; ++kx) {
-      const float e = fast_exp2(wr[kx] - M2);
-      wr[kx] = e;
-      Z += e;
+  // alpha = softmax over {s_hat_c} U {log Z_swa}: one wavefront per (query,
+  // head) row at a time, lane = slot (K <= 64 on this path)
+  {
+    const int lane = tid & 63, wv = tid >> 6;
+    for (int it = wv; it < RQ * G; it += NT / 64) {
+      const int qi = q0 + it / G;
+      if (qi >= qs) break;
+      const int kk = min(K, n_cand((long long)i0 + qi, W, S));
+      float* wr = wk + it * (K + 1);
+      const float lzv = wr[K];
+      const float x = (lane < kk) ? wr[lane] : -INFINITY;
+      const float M2 = fmaxf(wmax64(x), lzv);
+      const float e = (lane < kk) ? fast_exp2(x - M2) : 0.0f;
+      const float es = fast_exp2(lzv - M2);
+      const float invZ = 1.0f / (wsum64(e) + es);
+      if (lane < kk) wr[lane] = e * invZ;
+      if (lane == 0) wr[K] = es * invZ;
     }
-    const float invZ = 1.0f / Z;
-    for (int kx = 0; kx < kk; ++kx) wr[kx] *= invZ;
-    wr[K] = fast_exp2(lzv - M2) * invZ;
   }
   __syncthreads();
   const int sub = tid / TPQ, e2 = tid - sub * TPQ;
@@ -623,12 +623,12 @@ k_pair_reduce(const float* __restrict__ swa, const float* __restrict__ lz,
       }
     };
     int kx = 0;
-    for (; kx + 8 <= kk; kx += 8) {
-      uint4 uv[8];
+    for (; kx + RU <= kk; kx += RU) {      // RU slot loads in flight
+      uint4 uv[RU];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) uv[t] = ld_u4(pp + (long long)(kx + t) * G * D);
+      for (int t = 0; t < RU; ++t) uv[t] = ld_u4(pp + (long long)(kx + t) * G * D);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) add(wr[kx + t], uv[t]);
+      for (int t = 0; t < RU; ++t) add(wr[kx + t], uv[t]);
     }
     for (; kx < kk; ++kx) add(wr[kx], ld_u4(pp + (long long)kx * G * D));
     bf16_t* op = out + (((long long)b * Hq + (long long)g * G + h) * N + i) * D;
