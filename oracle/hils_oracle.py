@@ -41,7 +41,7 @@ import numpy as np
 
 __all__ = [
     "bf16_round", "f32_round", "store_round", "window_left", "n_candidates",
-    "ref_summarize", "ref_chunk_scores", "ref_exact_logz", "ref_group_scores", "ref_decode_multi",
+    "ref_summarize", "ref_chunk_scores", "ref_exact_logz", "ref_group_scores", "ref_decode_multi", "ref_backward",
     "ref_select", "ref_row", "ref_prefill_rows", "ref_decode",
     "ref_full_causal", "ref_naive_bsa", "ref_overlap", "ref_brute_force_mass_topk",
 ]
@@ -434,6 +434,116 @@ def ref_decode_multi(q, k_cache, v_cache, seqlen, lm, S, W, K, q_route=None, sca
                 sels[g], gaps[g], shats[g] = r["sel"], r["gap"], r["s_hat"]
             results[(b, m)] = dict(out=out, sel=sels, gap=gaps, s_hat=shats, n=n)
     return results
+
+
+def ref_backward(q, k, v, lm, dout, S, W, K, q_route=None, scale=None, sel=None,
+                 mode="surrogate", store="bf16"):
+    """Gradients of L = sum(dout * out) for the HiLS prefill of every position.
+
+    The top-K selection is a discrete choice and is held fixed (given as `sel`
+    [B,Hkv,N,K], -1 padded, or computed by the forward); every other step of
+    section 3 is differentiated exactly:
+      out = sum_c alpha_c o_c + alpha_w o_w, alpha = softmax({s_hat_c} U {log Z_swa});
+      o_c = softmax_j(tau q.k_j) V over chunk c;  o_w, log Z_swa over the window;
+      s_hat_c = tau q_hat.k'_c + b'_c  (section 3 routing equation);
+      k'_c = sum_j pi_j k_j, b'_c = -sum_j pi_j log pi_j, pi = softmax_j(tau q'_c.k_j)
+      (Proposition 3.1);  'landmark_key': k'_c = q'_c, b'_c = 0;
+      'mean_pool': k'_c = mean_j k_j, b'_c = ln S.
+    The stored (rounded per `store`) summaries enter s_hat as in the forward;
+    their rounding is not differentiated.  Returns dict(dq, dk, dv, dlm,
+    dq_route (None without q_route), sel).
+    """
+    q, k, v, lm, dout, q_route = map(_arr, (q, k, v, lm, dout, q_route))
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    nC = N // S
+    tau = (1.0 / math.sqrt(d)) if scale is None else float(scale)
+    qr = q if q_route is None else q_route
+    q64, k64, v64, lm64, do64, qr64 = (x.astype(np.float64) for x in (q, k, v, lm, dout, qr))
+    ks, bs = ref_summarize(k, lm, S, tau, mode=mode, store=store)
+    if sel is None:
+        res = ref_prefill_rows(q, k, v, lm, [(b, i) for b in range(B) for i in range(N)], S, W,
+                               K, q_route=q_route, scale=scale, mode=mode, store=store,
+                               summaries=(ks, bs))
+        sel = -np.ones((B, Hkv, N, K), dtype=np.int64)
+        for (b, i), r in res.items():
+            for g in range(Hkv):
+                sel[b, g, i, :len(r["sel"][g])] = r["sel"][g]
+    sel = np.asarray(sel)
+    dq, dqr = np.zeros_like(q64), np.zeros_like(q64)
+    dk, dv = np.zeros_like(k64), np.zeros_like(v64)
+    dks, dbs = np.zeros((B, Hq, nC, d)), np.zeros((B, Hq, nC))
+    for b in range(B):
+        for g in range(Hkv):
+            for i in range(N):
+                w0 = _window_start(i, W, S)
+                chunks = [int(c) for c in sel[b, g, i] if c >= 0]
+                kw, vw = k64[b, g, w0:i + 1], v64[b, g, w0:i + 1]
+                for r in range(G):
+                    h = g * G + r
+                    qi, qh, go = q64[b, h, i], qr64[b, h, i], do64[b, h, i]
+                    sw = tau * (kw @ qi)
+                    lzw = _lse(sw)
+                    pw = np.exp(sw - lzw)
+                    ow = pw @ vw
+                    pcs, ocs, lam = [], [], []
+                    for c in chunks:
+                        kc, vc = k64[b, g, c * S:(c + 1) * S], v64[b, g, c * S:(c + 1) * S]
+                        sc = tau * (kc @ qi)
+                        pc = np.exp(sc - _lse(sc))
+                        pcs.append(pc)
+                        ocs.append(pc @ vc)
+                        lam.append(tau * (qh @ ks[b, h, c]) + bs[b, h, c])
+                    logits = np.array(lam + [lzw])
+                    alpha = np.exp(logits - _lse(logits))
+                    out = sum(alpha[t] * ocs[t] for t in range(len(chunks))) + alpha[-1] * ow
+                    gbar = go @ out
+                    gw = go @ ow
+                    dlzw = alpha[-1] * (gw - gbar)
+                    # window: through o_w and log Z_swa
+                    dsw = alpha[-1] * pw * (vw @ go - gw) + dlzw * pw
+                    dq[b, h, i] += tau * (dsw @ kw)
+                    dk[b, g, w0:i + 1] += tau * np.outer(dsw, qi)
+                    dv[b, g, w0:i + 1] += alpha[-1] * np.outer(pw, go)
+                    dqh = np.zeros(d)
+                    for t, c in enumerate(chunks):
+                        kc, vc = k64[b, g, c * S:(c + 1) * S], v64[b, g, c * S:(c + 1) * S]
+                        gc = go @ ocs[t]
+                        dlam = alpha[t] * (gc - gbar)
+                        ds = alpha[t] * pcs[t] * (vc @ go - gc)
+                        dq[b, h, i] += tau * (ds @ kc)
+                        dk[b, g, c * S:(c + 1) * S] += tau * np.outer(ds, qi)
+                        dv[b, g, c * S:(c + 1) * S] += alpha[t] * np.outer(pcs[t], go)
+                        dqh += tau * dlam * ks[b, h, c]
+                        dks[b, h, c] += tau * dlam * qh
+                        dbs[b, h, c] += dlam
+                    if q_route is None:
+                        dq[b, h, i] += dqh
+                    else:
+                        dqr[b, h, i] += dqh
+    # summaries (Proposition 3.1 and the mode variants)
+    dlm = np.zeros_like(lm64)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for c in range(nC):
+                kc = k64[b, g, c * S:(c + 1) * S]
+                if mode == "landmark_key":
+                    dlm[b, h, c] = dks[b, h, c]
+                    continue
+                if mode == "mean_pool":
+                    dk[b, g, c * S:(c + 1) * S] += dks[b, h, c] / S
+                    continue
+                t = tau * (kc @ lm64[b, h, c])
+                logpi = t - _lse(t)
+                pi = np.exp(logpi)
+                dpi = kc @ dks[b, h, c] + dbs[b, h, c] * (-logpi - 1.0)
+                dt = pi * (dpi - pi @ dpi)
+                dlm[b, h, c] = tau * (dt @ kc)
+                dk[b, g, c * S:(c + 1) * S] += tau * np.outer(dt, lm64[b, h, c]) + np.outer(pi, dks[b, h, c])
+    return dict(dq=dq, dk=dk, dv=dv, dlm=dlm, dq_route=(dqr if q_route is not None else None),
+                sel=sel)
 
 
 # ---------------------------------------------------------------------------

@@ -369,6 +369,78 @@ def test_decode_multi_rows_are_causal_prefill_rows():
     assert np.abs(dec2[(0, M - 1)]["out"] - dec[(0, M - 1)]["out"]).max() > 1e-3
 
 
+def _hils_loss(x, dout, S, W, K, sel, mode, q_route=None):
+    """sum(dout * out) of every prefill row with the selection held at `sel`."""
+    B, Hq, N, d = x["q"].shape
+    Hkv = x["k"].shape[1]
+    rows = [(0, i) for i in range(N)]
+    forced = {(0, g, i): [int(c) for c in sel[0, g, i] if c >= 0] for g in range(Hkv) for i in range(N)}
+    res = O.ref_prefill_rows(x["q"], x["k"], x["v"], x["lm"], rows, S, W, K, q_route=q_route,
+                             mode=mode, store="f64", forced_sel=forced)
+    return sum(float(np.sum(dout[0, :, i] * res[(0, i)]["out"])) for i in range(N))
+
+
+@pytest.mark.parametrize("mode,route", [("surrogate", False), ("surrogate", True),
+                                        ("landmark_key", False), ("mean_pool", False)])
+def test_backward_matches_finite_differences(mode, route):
+    """The oracle's gradients (selection held fixed) equal central finite
+    differences of sum(dout * out) along random directions, for q, the routing
+    query, k, v and the landmark queries."""
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, N, d, S, W, K = 1, 4, 2, 160, 8, 16, 32, 3
+    x = {"q": rng.standard_normal((B, Hq, N, d)), "k": rng.standard_normal((B, Hkv, N, d)),
+         "v": rng.standard_normal((B, Hkv, N, d)),
+         "lm": rng.standard_normal((B, Hq, N // S, d))}
+    qr = rng.standard_normal((B, Hq, N, d)) if route else None
+    dout = rng.standard_normal((B, Hq, N, d))
+    gr = O.ref_backward(x["q"], x["k"], x["v"], x["lm"], dout, S, W, K, q_route=qr, mode=mode,
+                        store="f64")
+    sel = gr["sel"]
+    assert (sel[..., 0] >= 0).sum() > 0 and (sel[..., K - 1] >= 0).sum() > 0
+    names = [("q", "dq"), ("k", "dk"), ("v", "dv")]
+    if mode != "mean_pool":
+        names.append(("lm", "dlm"))
+    eps = 1e-5
+    for name, gname in names + ([("q_route", "dq_route")] if route else []):
+        u = rng.standard_normal(x[name].shape if name != "q_route" else qr.shape)
+        def loss(sgn):
+            y = dict(x)
+            r2 = qr
+            if name == "q_route":
+                r2 = qr + sgn * eps * u
+            else:
+                y[name] = x[name] + sgn * eps * u
+            return _hils_loss(y, dout, S, W, K, sel, mode, q_route=r2)
+        fd = (loss(1) - loss(-1)) / (2 * eps)
+        an = float(np.sum(gr[gname] * u))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (mode, name, fd, an)
+
+
+def test_backward_window_only_is_causal_attention_gradient():
+    """With the window covering every position (no candidate chunks) HiLS is
+    causal softmax attention; its gradients equal torch autograd of the
+    textbook formula (float64, CPU)."""
+    import torch
+    rng = np.random.default_rng(3)
+    B, Hq, Hkv, N, d, S = 1, 4, 2, 48, 8, 8
+    q, k, v = (rng.standard_normal(sh) for sh in ((B, Hq, N, d), (B, Hkv, N, d), (B, Hkv, N, d)))
+    lm = rng.standard_normal((B, Hq, N // S, d))
+    dout = rng.standard_normal((B, Hq, N, d))
+    gr = O.ref_backward(q, k, v, lm, dout, S, N + S, 2, store="f64")
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    G = Hq // Hkv
+    kk = tk.repeat_interleave(G, dim=1)
+    vv = tv.repeat_interleave(G, dim=1)
+    s = (tq @ kk.transpose(-1, -2)) / math.sqrt(d)
+    s = s.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+    out = torch.softmax(s, dim=-1) @ vv
+    (out * torch.tensor(dout)).sum().backward()
+    np.testing.assert_allclose(gr["dq"], tq.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(gr["dk"], tk.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(gr["dv"], tv.grad.numpy(), atol=1e-10)
+    assert np.abs(gr["dlm"]).max() == 0.0
+
+
 def test_mean_pool_is_surrogate_at_zero_landmark_query():
     """Mean pooling (section 2.2 equation) equals the Proposition 3.1 summary of
     a zero landmark query: uniform weights give the mean key and entropy ln S."""
