@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP32_VALU_TFLOPS = 157.3   # MI355X fp32 vector (256 CUs at 2.4 GHz)
 
 
 def _geometry(N, W, S):
@@ -322,6 +323,56 @@ def multi_decode_bench(torch, hils, _lib, xd, wd, ks, bs, M, steps, log):
             "tokens_per_s": B * M * 1000.0 / ms, "kernels": kt}
 
 
+def backward_bench(torch, hils, _lib, wb, steps, log):
+    """Prefill backward (selection held fixed) on a training-length workload:
+    forward once for the selection, then time the backward."""
+    import synth
+    xb = synth.make_prefill_inputs(wb, device="cuda")
+    sel = torch.empty((wb.B, wb.Hkv, wb.N, wb.K), dtype=torch.int32, device="cuda")
+    ks = torch.empty((wb.B, wb.Hq, wb.N // wb.S, wb.d), dtype=xb["q"].dtype, device="cuda")
+    bs = torch.empty((wb.B, wb.Hq, wb.N // wb.S), dtype=torch.float32, device="cuda")
+    hils.prefill(xb["q"], xb["k"], xb["v"], xb["lm"], wb.S, wb.W, wb.K, sel=sel, summaries=(ks, bs))
+    g = torch.Generator(device="cuda").manual_seed(9)
+    dout = torch.randn(xb["q"].shape, generator=g, device="cuda").to(xb["q"].dtype)
+    cfg = hils.make_cfg(wb.B, wb.N, wb.Hq, wb.Hkv, wb.d, wb.S, wb.W, wb.K, xb["q"].dtype)
+    ws = torch.empty(_lib.lib().hils_prefill_backward_workspace_bytes(ctypes.byref(cfg)),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        return hils.prefill_backward(xb["q"], xb["k"], xb["v"], xb["lm"], dout, sel, wb.S, wb.W,
+                                     wb.K, summaries=(ks, bs), ws=ws)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    _lib.profile_enable(True)
+    _lib.profile_read()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kt = _kernel_table(_lib.profile_read(), steps)
+    _lib.profile_enable(False)
+    # algorithmic FLOPs: per attended (query, head, token) the five products of an
+    # attention backward (logit and dout.v recompute, dq, dk, dv): 10 d
+    n, win = _geometry(wb.N, wb.W, wb.S)
+    att = float((np.minimum(wb.K, n) * wb.S + win).sum()) * wb.Hq * wb.B
+    flops = 10.0 * wb.d * att
+    achieved = flops / (ms * 1e-3) / 1e12
+    log(f"backward {wb.name}: {ms:.2f} ms/step; kernels {json.dumps(kt)}")
+    del xb, sel, ks, bs, dout, ws
+    return {"workload": wb.name, "ms_per_step": ms, "tokens_per_s": wb.B * wb.N / (ms * 1e-3),
+            "config": {"B": wb.B, "N": wb.N, "Hq": wb.Hq, "Hkv": wb.Hkv, "d": wb.d, "S": wb.S,
+                       "W": wb.W, "K": wb.K},
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
+                         "algorithmic_flops_per_step": flops},
+            "kernels": kt}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -332,6 +383,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--backward-workload", default="prefill_8k",
+                    help="workload of the backward measurement ('' skips it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB copy first (counter scale for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -474,6 +527,13 @@ def main():
             dec["cpu_baseline"] = cpu_baseline_decode(xd, wd)
         del xd, ks, bs, outd, wsd
 
+    bwd = None
+    if args.backward_workload:
+        import synth
+        torch.cuda.empty_cache()
+        bwd = backward_bench(torch, hils, _lib, synth.get_workload(args.backward_workload),
+                             args.steps, log)
+
     line = {
         "metric": "prefill tokens/s and decode steps/s at 512K ctx; % of MFMA/HBM roofline",
         "value": w.B * w.N / (prefill_ms * 1e-3),
@@ -498,6 +558,7 @@ def main():
         "cpu_baseline": cpu_pre,
         "kernels": kern,
         "decode": dec,
+        "backward": bwd,
     }
     print(json.dumps(line), flush=True)
 

@@ -20,7 +20,8 @@ HILS_MAX_DECODE_QUERIES = 16
 
 EXPORTED = ("hils_workspace_bytes", "hils_summarize", "hils_prefill", "hils_decode",
             "hils_summarize_paged", "hils_decode_paged", "hils_decode_multi_workspace_bytes",
-            "hils_decode_multi", "hils_strerror", "hils_abi_version", "hils_profile_enable", "hils_profile_read")
+            "hils_decode_multi", "hils_prefill_backward_workspace_bytes", "hils_prefill_backward",
+            "hils_strerror", "hils_abi_version", "hils_profile_enable", "hils_profile_read")
 
 
 class HilsCfg(ctypes.Structure):
@@ -67,6 +68,10 @@ def lib() -> ctypes.CDLL:
         L.hils_decode_multi_workspace_bytes.restype = sz
         L.hils_decode_multi.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.hils_decode_multi.restype = ctypes.c_int
+        L.hils_prefill_backward_workspace_bytes.argtypes = [cfgp]
+        L.hils_prefill_backward_workspace_bytes.restype = sz
+        L.hils_prefill_backward.argtypes = [cfgp] + [vp] * 14 + [vp, sz, vp]
+        L.hils_prefill_backward.restype = ctypes.c_int
         L.hils_strerror.argtypes = [ctypes.c_int]
         L.hils_strerror.restype = ctypes.c_char_p
         L.hils_abi_version.argtypes = []

@@ -175,6 +175,42 @@ def decode_multi(q, k_cache, v_cache, seqlen, k_sum, b_sum, S, W, K, q_route=Non
     return out
 
 
+def prefill_backward(q, k, v, lm, dout, sel, S, W, K, q_route=None, mode="surrogate", scale=0.0,
+                     summaries=None, ws=None):
+    """Gradients of sum(dout * prefill(...)) with the forward's selection `sel`
+    [B,Hkv,N,K] held fixed.  Returns a dict of fp32 tensors dq, dk, dv, dlm
+    (None in mean_pool mode) and dq_route (None without q_route)."""
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("lm", lm), ("dout", dout), ("q_route", q_route)):
+        _check_tensor(t, name, q.dtype, dev)
+    _check_tensor(sel, "sel", torch.int32, dev)
+    ks = bs = None
+    if summaries is not None:
+        ks, bs = summaries
+        _check_tensor(ks, "k_sum", q.dtype, dev)
+        _check_tensor(bs, "b_sum", torch.float32, dev)
+    cfg = make_cfg(B, N, Hq, Hkv, d, S, W, K, q.dtype, mode, scale)
+    need = _lib.lib().hils_prefill_backward_workspace_bytes(ctypes.byref(cfg))
+    if need == 0:
+        raise ValueError("prefill_backward: unsupported configuration")
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty(q.shape, **f32)
+    dk = torch.empty(k.shape, **f32)
+    dv = torch.empty(v.shape, **f32)
+    dqr = torch.empty(q.shape, **f32) if q_route is not None else None
+    dlm = torch.empty((B, Hq, N // S, d), **f32) if (mode != "mean_pool" and N // S > 0) else None
+    st = _lib.lib().hils_prefill_backward(ctypes.byref(cfg), _ptr(q), _ptr(q_route), _ptr(k), _ptr(v),
+                                          _ptr(lm), _ptr(dout), _ptr(sel), _ptr(ks), _ptr(bs),
+                                          _ptr(dq), _ptr(dqr), _ptr(dk), _ptr(dv), _ptr(dlm),
+                                          _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(dev))
+    check(st, "hils_prefill_backward")
+    return dict(dq=dq, dk=dk, dv=dv, dlm=dlm, dq_route=dqr)
+
+
 def summarize_paged(k_pages, lm_pages, pages, S, N, out=None, mode="surrogate", scale=0.0):
     """Summaries of the pages listed in `pages` (int32 device tensor) of a paged
     cache: k_pages [P,Hkv,S,d], lm_pages [P,Hq,d].  Returns (k_sum_pages [P,Hq,d],

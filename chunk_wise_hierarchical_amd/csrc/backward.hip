@@ -1,0 +1,640 @@
+// HiLS prefill backward with the top-K selection held fixed.
+//
+// "Hierarchical Sparse Attention Done Right", section 3: out = sum_c alpha_c
+// o_c + alpha_w o_w with alpha = softmax({s_hat_c} U {log Z_swa}); o_c and o_w
+// are S-key and window softmax attentions; s_hat_c = tau q_hat.k'_c + b'_c;
+// k'_c, b'_c come from the Proposition 3.1 summary softmax of the landmark
+// query q'_c over the chunk's keys.  For L = sum(dout * out) and one (query,
+// head), with g_t = dout.o_t and gbar = dout.out:
+//   d s_hat_t   = alpha_t (g_t - gbar)        d log Z_swa = alpha_w (g_w - gbar)
+//   chunk t:  ds_j = alpha_t p_j (dout.v_j - g_t)
+//   window:   ds_j = alpha_w p_j (dout.v_j - g_w) + (d log Z_swa) p_j
+//   dq += tau sum_j ds_j k_j;  dk_j += tau ds_j q;  dv_j += alpha p_j dout
+//   dq_hat += tau sum_t (d s_hat_t) k'_t;  dk'_t += tau (d s_hat_t) q_hat;  db'_t += d s_hat_t
+// and through the summary softmax pi = softmax(tau q'.k_j):
+//   dpi_j = k_j.dk' + db' (-log pi_j - 1);  dt_j = pi_j (dpi_j - sum pi dpi)
+//   dq' = tau sum_j dt_j k_j;  dk_j += tau dt_j q' + pi_j dk'.
+//
+// Three kernels, no atomics, deterministic:
+//   k_bwd_lists — per (batch, KV group): for every chunk, the (query, slot)
+//                 pairs that selected it, in query order (stable counting sort);
+//   k_bwd_rows  — per (batch, KV group, query): recompute the row's softmax
+//                 statistics, write dq (and dq_route) and per-pair / window
+//                 statistics (alpha, log-normaliser, g, d s_hat);
+//   k_bwd_cols  — per (batch, KV group, chunk): accumulate dk, dv of the
+//                 chunk's tokens over the queries that selected the chunk and
+//                 the queries whose window holds it, then back-propagate the
+//                 chunk's summaries into dlm and dk.
+#include "hils_device.h"
+#include "hils_internal.h"
+#include "hils_bwd.h"
+
+namespace {
+
+constexpr int BT = 256;
+
+// 16-byte vector access to a row of T (8 bf16 or 4 fp32 elements)
+template <typename T> struct V16;
+template <> struct V16<bf16_t> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void ld(const bf16_t* p, float* o) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      o[2 * t] = __uint_as_float(w[t] << 16);
+      o[2 * t + 1] = __uint_as_float(w[t] & 0xffff0000u);
+    }
+  }
+};
+template <> struct V16<float> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void ld(const float* p, float* o) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    o[0] = u.x; o[1] = u.y; o[2] = u.z; o[3] = u.w;
+  }
+};
+
+// a (fp32, LDS) . row (T, global), d % V16<T>::N == 0
+template <typename T>
+__device__ __forceinline__ float dot_row(const float* a, const T* row, int d) {
+  constexpr int VN = V16<T>::N;
+  float acc = 0.0f;
+  for (int e = 0; e < d; e += VN) {
+    float x[VN];
+    V16<T>::ld(row + e, x);
+#pragma unroll
+    for (int u = 0; u < VN; ++u) acc = fmaf(a[e + u], x[u], acc);
+  }
+  return acc;
+}
+
+// n (a multiple of V16<T>::N, at most 16) elements of a row into registers
+template <typename T>
+__device__ __forceinline__ void load_slice16(const T* p, int n, float* o) {
+  constexpr int VN = V16<T>::N;
+#pragma unroll
+  for (int u = 0; u < 16; u += VN) {
+    if (u < n) V16<T>::ld(p + u, o + u);
+    else {
+#pragma unroll
+      for (int t = 0; t < VN; ++t) o[u + t] = 0.0f;
+    }
+  }
+}
+
+// n (a multiple of V16<T>::N, at most 32) elements of a row into registers
+template <typename T>
+__device__ __forceinline__ void load_slice(const T* p, int n, float* o) {
+  constexpr int VN = V16<T>::N;
+#pragma unroll
+  for (int u = 0; u < 32; u += VN) {
+    if (u < n) V16<T>::ld(p + u, o + u);
+    else {
+#pragma unroll
+      for (int t = 0; t < VN; ++t) o[u + t] = 0.0f;
+    }
+  }
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max_f(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float m = red[0];
+  for (int u = 1; u < (int)(blockDim.x >> 6); ++u) m = fmaxf(m, red[u]);
+  return m;
+}
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum_f(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.0f;
+  for (int u = 0; u < (int)(blockDim.x >> 6); ++u) s += red[u];
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// inverse selection lists: for each chunk c of (b, g), entries (i << 8 | slot)
+// at off[c] .. off[c+1], in increasing query order
+
+__global__ void __launch_bounds__(1024)
+k_bwd_lists(const int32_t* __restrict__ sel, uint32_t* __restrict__ off, uint32_t* __restrict__ ent,
+            int N, int K, int nC) {
+  extern __shared__ uint32_t cur[];          // [nC] counts, then cursors
+  __shared__ uint32_t wtot[16];
+  const int bg = blockIdx.x, tid = threadIdx.x;
+  const int32_t* sg = sel + (long long)bg * N * K;
+  uint32_t* og = off + (long long)bg * (nC + 1);
+  uint32_t* eg = ent + (long long)bg * N * K;
+  for (int c = tid; c < nC; c += 1024) cur[c] = 0;
+  __syncthreads();
+  for (long long t = tid; t < (long long)N * K; t += 1024) {
+    const int c = sg[t];
+    if (c >= 0 && c < nC) atomicAdd(&cur[c], 1u);
+  }
+  __syncthreads();
+  // exclusive scan of the counts in chunks of 1024
+  uint32_t carry = 0;
+  for (int base = 0; base < nC; base += 1024) {
+    const int c = base + tid;
+    const uint32_t v = (c < nC) ? cur[c] : 0u;
+    uint32_t x = v;
+    const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const uint32_t y = __shfl_up(x, m, 64);
+      if (lane >= m) x += y;
+    }
+    if (lane == 63) wtot[w] = x;
+    __syncthreads();
+    uint32_t before = carry;
+    for (int u = 0; u < w; ++u) before += wtot[u];
+    uint32_t all = carry;
+    for (int u = 0; u < 16; ++u) all += wtot[u];
+    __syncthreads();
+    if (c < nC) {
+      const uint32_t e = before + x - v;
+      cur[c] = e;
+      og[c] = e;
+    }
+    carry = all;
+    __syncthreads();
+  }
+  if (tid == 0) og[nC] = carry;
+  __syncthreads();
+  // stable scatter in query order by one wavefront (its LDS atomics are
+  // processed in issue order; a query's slots hold distinct chunks)
+  if (tid < 64) {
+    for (int i = 0; i < N; ++i) {
+      for (int s2 = tid; s2 < K; s2 += 64) {
+        const int c = sg[(long long)i * K + s2];
+        if (c >= 0 && c < nC) {
+          const uint32_t pos = atomicAdd(&cur[c], 1u);
+          eg[pos] = ((uint32_t)i << 8) | (uint32_t)s2;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// per query row: statistics and dq
+
+template <typename T>
+__global__ void __launch_bounds__(BT)
+k_bwd_rows(const T* __restrict__ q, const T* __restrict__ qr, const T* __restrict__ k,
+           const T* __restrict__ v, const T* __restrict__ ksum, const float* __restrict__ bsum,
+           const T* __restrict__ dout, const int32_t* __restrict__ sel, float* __restrict__ dq,
+           float* __restrict__ dqr, float* __restrict__ pstat, float* __restrict__ wstat, int Hq,
+           int Hkv, int G, int N, int d, int S, int W, int K, int nC, float tau, int route_sep) {
+  extern __shared__ __align__(16) float smr[];
+  const int tid = threadIdx.x;
+  const long long row = blockIdx.x;                  // (b, g, i)
+  const int i = (int)(row % N);
+  const long long bg = row / N;
+  const int g = (int)(bg % Hkv);
+  const long long b = bg / Hkv;
+  const long long hb = b * Hq + (long long)g * G;    // first query head of the group
+  const int w0 = (int)window_start(i, W, S);
+  const int L = i - w0 + 1;
+  const int Lp = (L + 3) & ~3;
+  float* qs = smr;                                   // [G][d]
+  float* qh = qs + G * d;                            // [G][d]
+  float* go = qh + G * d;                            // [G][d]
+  float* acc = go + G * d;                           // [G][d] dq accumulator
+  float* wp = acc + G * d;                           // [G][Lp] window probabilities
+  float* wu = wp + G * Lp;                           // [G][Lp] dout.v_j on the window
+  float* cs = wu + G * Lp;                           // [G][S]  chunk p_j (u_j - g_t)
+  float* cu = cs + G * S;                            // [G][S]
+  float* st = cu + G * S;                            // [K][G][4] alpha, lse, g, dlam per slot
+  float* sw = st + K * G * 4;                        // [G][4]
+  float* red = sw + G * 4;                           // [4]
+  __shared__ int ssel[128];
+  __shared__ int skk;
+
+  for (int t = tid; t < G * d; t += BT) {
+    const int r = t / d, e = t - r * d;
+    const long long o = ((hb + r) * N + i) * (long long)d + e;
+    qs[t] = Elt<T>::ld(q + o);
+    qh[t] = Elt<T>::ld(qr + o);
+    go[t] = Elt<T>::ld(dout + o);
+    acc[t] = 0.0f;
+  }
+  if (tid == 0) {
+    int kk = 0;
+    for (int t = 0; t < K; ++t) {
+      const int c = sel[row * K + t];
+      if (c >= 0 && c < nC) ssel[kk++] = c;
+    }
+    skk = kk;
+  }
+  __syncthreads();
+  const int kk = skk;
+  const T* kb = k + bg * (long long)N * d;
+  const T* vb = v + bg * (long long)N * d;
+
+  // chunk scores s_hat_t (routing query) per (slot, head)
+  for (int t = tid; t < kk * G; t += BT) {
+    const int s2 = t / G, r = t - s2 * G, c = ssel[s2];
+    const T* kp = ksum + ((hb + r) * nC + c) * (long long)d;
+    const float a = dot_row<T>(qh + r * d, kp, d);
+    st[(s2 * G + r) * 4 + 0] = fmaf(tau, a, bsum[(hb + r) * nC + c]);
+  }
+  // window logits and dout.v_j
+  for (int t = tid; t < G * L; t += BT) {
+    const int r = t / L, j = t - r * L;
+    const T* kr = kb + (long long)(w0 + j) * d;
+    const T* vr = vb + (long long)(w0 + j) * d;
+    wp[r * Lp + j] = tau * dot_row<T>(qs + r * d, kr, d);
+    wu[r * Lp + j] = dot_row<T>(go + r * d, vr, d);
+  }
+  __syncthreads();
+  // per head: window log-mass, probabilities, g_w; fusion weights
+  for (int r = 0; r < G; ++r) {
+    float m = -INFINITY;
+    for (int j = tid; j < L; j += BT) m = fmaxf(m, wp[r * Lp + j]);
+    m = block_max(m, red);
+    float z = 0.0f;
+    for (int j = tid; j < L; j += BT) z += __expf(wp[r * Lp + j] - m);
+    z = block_sum(z, red);
+    const float lse = m + __logf(z);
+    float gw = 0.0f;
+    for (int j = tid; j < L; j += BT) {
+      const float p = __expf(wp[r * Lp + j] - lse);
+      wp[r * Lp + j] = p;
+      gw = fmaf(p, wu[r * Lp + j], gw);
+    }
+    gw = block_sum(gw, red);
+    if (tid == 0) {
+      float M = lse;
+      for (int s2 = 0; s2 < kk; ++s2) M = fmaxf(M, st[(s2 * G + r) * 4]);
+      float Z = __expf(lse - M);
+      for (int s2 = 0; s2 < kk; ++s2) Z += __expf(st[(s2 * G + r) * 4] - M);
+      for (int s2 = 0; s2 < kk; ++s2) st[(s2 * G + r) * 4] = __expf(st[(s2 * G + r) * 4] - M) / Z;
+      sw[r * 4 + 0] = __expf(lse - M) / Z;
+      sw[r * 4 + 1] = lse;
+      sw[r * 4 + 2] = gw;
+    }
+    __syncthreads();
+  }
+  // selected chunks: p, dout.v_j, g_t; dq += tau alpha_t sum_j p_j (u_j - g_t) k_j
+  for (int s2 = 0; s2 < kk; ++s2) {
+    const int c = ssel[s2];
+    const T* kc = kb + (long long)c * S * d;
+    const T* vc = vb + (long long)c * S * d;
+    for (int t = tid; t < G * S; t += BT) {
+      const int r = t / S, j = t - r * S;
+      cs[t] = tau * dot_row<T>(qs + r * d, kc + (long long)j * d, d);
+      cu[t] = dot_row<T>(go + r * d, vc + (long long)j * d, d);
+    }
+    __syncthreads();
+    for (int r = 0; r < G; ++r) {
+      float m = -INFINITY;
+      for (int j = tid; j < S; j += BT) m = fmaxf(m, cs[r * S + j]);
+      m = block_max(m, red);
+      float z = 0.0f;
+      for (int j = tid; j < S; j += BT) z += __expf(cs[r * S + j] - m);
+      z = block_sum(z, red);
+      const float lse = m + __logf(z);
+      float gt = 0.0f;
+      for (int j = tid; j < S; j += BT) gt = fmaf(__expf(cs[r * S + j] - lse), cu[r * S + j], gt);
+      gt = block_sum(gt, red);
+      for (int j = tid; j < S; j += BT) {
+        const float p = __expf(cs[r * S + j] - lse);
+        cs[r * S + j] = p * (cu[r * S + j] - gt);
+      }
+      if (tid == 0) {
+        st[(s2 * G + r) * 4 + 1] = lse;
+        st[(s2 * G + r) * 4 + 2] = gt;
+      }
+      __syncthreads();
+    }
+    for (int t = tid; t < G * d; t += BT) {
+      const int r = t / d, e = t - r * d;
+      float a = 0.0f;
+      for (int j = 0; j < S; ++j) a = fmaf(cs[r * S + j], Elt<T>::ld(kc + (long long)j * d + e), a);
+      acc[t] = fmaf(tau * st[(s2 * G + r) * 4], a, acc[t]);
+    }
+    __syncthreads();
+  }
+  // gbar, d s_hat, window gradient
+  if (tid < G) {
+    const int r = tid;
+    float gbar = sw[r * 4] * sw[r * 4 + 2];
+    for (int s2 = 0; s2 < kk; ++s2) gbar = fmaf(st[(s2 * G + r) * 4], st[(s2 * G + r) * 4 + 2], gbar);
+    for (int s2 = 0; s2 < kk; ++s2)
+      st[(s2 * G + r) * 4 + 3] = st[(s2 * G + r) * 4] * (st[(s2 * G + r) * 4 + 2] - gbar);
+    sw[r * 4 + 3] = sw[r * 4] * (sw[r * 4 + 2] - gbar);
+  }
+  __syncthreads();
+  for (int t = tid; t < G * L; t += BT) {
+    const int r = t / L, j = t - r * L;
+    const float p = wp[r * Lp + j];
+    wu[r * Lp + j] = sw[r * 4] * p * (wu[r * Lp + j] - sw[r * 4 + 2]) + sw[r * 4 + 3] * p;
+  }
+  __syncthreads();
+  for (int t = tid; t < G * d; t += BT) {
+    const int r = t / d, e = t - r * d;
+    float a = 0.0f;
+    for (int j = 0; j < L; ++j) a = fmaf(wu[r * Lp + j], Elt<T>::ld(kb + (long long)(w0 + j) * d + e), a);
+    float dqv = fmaf(tau, a, acc[t]);
+    // routing query: tau sum_t d s_hat_t k'_t
+    float dh = 0.0f;
+    for (int s2 = 0; s2 < kk; ++s2)
+      dh = fmaf(st[(s2 * G + r) * 4 + 3], Elt<T>::ld(ksum + ((hb + r) * nC + ssel[s2]) * (long long)d + e), dh);
+    dh *= tau;
+    const long long o = ((hb + r) * N + i) * (long long)d + e;
+    if (route_sep) {
+      dq[o] = dqv;
+      dqr[o] = dh;
+    } else {
+      dq[o] = dqv + dh;
+    }
+  }
+  // statistics for the column pass
+  for (int t = tid; t < K * G * 4; t += BT) {
+    const int s2 = t / (G * 4);
+    pstat[row * K * G * 4 + t] = (s2 < kk) ? st[t] : 0.0f;
+  }
+  for (int t = tid; t < G * 4; t += BT) {
+    const int r = t / 4, f = t - r * 4;
+    wstat[((hb + r) * N + i) * 4 + f] = sw[t];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// per chunk: dk, dv of its tokens; summary backward
+//
+// 512 threads: thread (token jt = tid / 8, eighth qd = tid % 8) owns d/8
+// elements of the token's k, v, dk, dv.  Contributions (query, head) are
+// described in LDS in batches (query, head, alpha, log-normaliser, g, and the
+// window term), and the next contribution's q and dout slices are loaded while
+// the current one is applied.
+
+constexpr int CT = 512;
+constexpr int CBATCH = 512;                          // contributions described per batch
+constexpr int CE = 16;                               // elements per thread (d <= 128)
+
+template <typename T>
+__global__ void __launch_bounds__(CT)
+k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restrict__ k,
+           const T* __restrict__ v, const T* __restrict__ lm, const T* __restrict__ dout,
+           const uint32_t* __restrict__ off, const uint32_t* __restrict__ ent,
+           const float* __restrict__ pstat, const float* __restrict__ wstat, float* __restrict__ dk,
+           float* __restrict__ dv, float* __restrict__ dlm, int Hq, int Hkv, int G, int N, int d,
+           int S, int W, int K, int nC, int nCc, float tau, int mode) {
+  extern __shared__ __align__(16) float smc[];
+  const int tid = threadIdx.x;
+  const long long blk = blockIdx.x;                  // (b, g, c)
+  const int c = (int)(blk % nCc);
+  const long long bg = blk / nCc;
+  const int g = (int)(bg % Hkv);
+  const long long b = bg / Hkv;
+  const long long hb = b * Hq + (long long)g * G;
+  const int j0 = c * S;
+  const int jn = min(S, N - j0);                     // tokens of this chunk
+  const int DQ = d / 8;                              // elements per thread
+  const int jt = tid >> 3, qd = tid & 7;
+  const bool act = jt < jn;
+  const int e0 = qd * DQ;
+  float* dks = smc;                                  // [G][d] dk' of the chunk
+  float* dbs = dks + G * d;                          // [G]
+  float* tmp = dbs + G;                              // [S][d] reduction scratch
+  float* red = tmp + S * d;                          // [8]
+  int* di = reinterpret_cast<int*>(red + 8);         // [CBATCH] query << 4 | head, window flag << 31
+  float* dsx = reinterpret_cast<float*>(di + CBATCH);   // [CBATCH][4] alpha, lse, g, window term
+  const T* kb = k + (bg * (long long)N + j0) * d;
+  const T* vb = v + (bg * (long long)N + j0) * d;
+
+  float kj[CE], vj[CE], dkj[CE], dvj[CE];
+  const int jr = act ? jt : 0;                       // inactive tokens read row 0, zeroed
+  load_slice16<T>(kb + (long long)jr * d + e0, DQ, kj);
+  load_slice16<T>(vb + (long long)jr * d + e0, DQ, vj);
+#pragma unroll
+  for (int u = 0; u < CE; ++u) {
+    if (!act) { kj[u] = 0.0f; vj[u] = 0.0f; }
+    dkj[u] = 0.0f;
+    dvj[u] = 0.0f;
+  }
+  for (int t = tid; t < G * d + G; t += CT) dks[t] = 0.0f;
+
+  const bool summ = c < nC;
+  const uint32_t p0 = summ ? off[bg * (nC + 1) + c] : 0u;
+  const uint32_t p1 = summ ? off[bg * (nC + 1) + c + 1] : 0u;
+  const long long nsel = (long long)(p1 - p0) * G;                 // (pair, head) contributions
+  const int i1 = min(N, (c + 1) * S + W - 1);
+  const long long nwin = (long long)(i1 - j0) * G;                // window (query, head)
+  const uint32_t* eg = ent + bg * (long long)N * K;
+
+  for (long long base = 0; base < nsel + nwin; base += CBATCH) {
+    const int nb = (int)min((long long)CBATCH, nsel + nwin - base);
+    __syncthreads();                                 // previous batch consumed
+    for (int t = tid; t < nb; t += CT) {
+      const long long idx = base + t;
+      if (idx < nsel) {
+        const uint32_t e = eg[p0 + idx / G];
+        const int r = (int)(idx % G), i = (int)(e >> 8), s2 = (int)(e & 255u);
+        const float* ps = pstat + (((bg * N + i) * (long long)K + s2) * G + r) * 4;
+        di[t] = (i << 4) | r;
+        dsx[t * 4 + 0] = ps[0];
+        dsx[t * 4 + 1] = ps[1];
+        dsx[t * 4 + 2] = ps[2];
+        dsx[t * 4 + 3] = ps[3];                      // d s_hat (for dk', db')
+      } else {
+        const long long widx = idx - nsel;
+        const int i = j0 + (int)(widx / G), r = (int)(widx % G);
+        const float* ws = wstat + ((hb + r) * N + i) * 4;
+        di[t] = (int)(0x80000000u | ((uint32_t)i << 4) | (uint32_t)r);
+        dsx[t * 4 + 0] = ws[0];
+        dsx[t * 4 + 1] = ws[1];
+        dsx[t * 4 + 2] = ws[2];
+        dsx[t * 4 + 3] = ws[3];                      // d log Z_swa
+      }
+    }
+    __syncthreads();
+    // software pipeline: q and dout slices of contribution u + 1 load while u is applied
+    float qa[CE], da[CE], qb2[CE], db2[CE];
+    auto fetch = [&](int u, float* qv, float* dv2) {
+      const int dd = di[u];
+      const int i = (dd >> 4) & 0x7ffffff, r = dd & 15;
+      const long long o = ((hb + r) * N + i) * (long long)d + e0;
+      load_slice16<T>(q + o, DQ, qv);
+      load_slice16<T>(dout + o, DQ, dv2);
+    };
+    auto apply = [&](int u, const float* qv, const float* dv2) {
+      const int dd = di[u];
+      const bool window = dd < 0;
+      const int i = (dd >> 4) & 0x7ffffff, r = dd & 15;
+      float a = 0.0f, u2 = 0.0f;
+#pragma unroll
+      for (int x = 0; x < CE; ++x) {
+        a = fmaf(qv[x], kj[x], a);
+        u2 = fmaf(dv2[x], vj[x], u2);
+      }
+      // the 8 lanes of a token hold its 8 slices
+      a += __shfl_xor(a, 1, 64);
+      a += __shfl_xor(a, 2, 64);
+      a += __shfl_xor(a, 4, 64);
+      u2 += __shfl_xor(u2, 1, 64);
+      u2 += __shfl_xor(u2, 2, 64);
+      u2 += __shfl_xor(u2, 4, 64);
+      const float alpha = dsx[u * 4], lse = dsx[u * 4 + 1], gq = dsx[u * 4 + 2], xt = dsx[u * 4 + 3];
+      const int j = j0 + jt;
+      bool ok = act;
+      if (window) ok = ok && j <= i && j >= (int)window_start(i, W, S);
+      const float pp = ok ? __expf(tau * a - lse) : 0.0f;
+      const float ds = alpha * pp * (u2 - gq) + (window ? xt * pp : 0.0f);
+      const float ap = alpha * pp;
+#pragma unroll
+      for (int x = 0; x < CE; ++x) {
+        dkj[x] = fmaf(tau * ds, qv[x], dkj[x]);
+        dvj[x] = fmaf(ap, dv2[x], dvj[x]);
+      }
+      // dk' += tau d s_hat q_hat, db' += d s_hat: threads of token r own head r
+      if (!window && jt == r) {
+        float hv[CE];
+        load_slice16<T>(qr + ((hb + r) * N + i) * (long long)d + e0, DQ, hv);
+#pragma unroll
+        for (int x = 0; x < CE; ++x)
+          if (x < DQ) dks[r * d + e0 + x] = fmaf(tau * xt, hv[x], dks[r * d + e0 + x]);
+        if (qd == 0) dbs[r] += xt;
+      }
+    };
+    if (nb > 0) fetch(0, qa, da);
+    int u = 0;
+    for (; u + 1 < nb; u += 2) {
+      fetch(u + 1, qb2, db2);
+      apply(u, qa, da);
+      if (u + 2 < nb) fetch(u + 2, qa, da);
+      apply(u + 1, qb2, db2);
+    }
+    if (u < nb) apply(u, qa, da);
+  }
+  __syncthreads();
+  // summaries of the chunk (one per query head of the group)
+  if (summ) {
+    for (int r = 0; r < G; ++r) {
+      const long long ho = ((hb + r) * nC + c) * (long long)d;
+      if (mode == 1) {                       // landmark key: k' = q', b' = 0
+        for (int e = tid; e < d; e += CT) dlm[ho + e] = dks[r * d + e];
+        continue;
+      }
+      if (mode == 3) {                       // mean pooling: k' = mean of the keys
+#pragma unroll
+        for (int x = 0; x < CE; ++x)
+          if (x < DQ) dkj[x] = fmaf(1.0f / (float)S, dks[r * d + e0 + x], dkj[x]);
+        continue;
+      }
+      float lv[CE];
+      load_slice16<T>(lm + ho + e0, DQ, lv);
+      float a = 0.0f, dp = 0.0f;
+#pragma unroll
+      for (int x = 0; x < CE; ++x) {
+        a = fmaf(lv[x], kj[x], a);
+        dp = fmaf(x < DQ ? dks[r * d + e0 + x] : 0.0f, kj[x], dp);
+      }
+      a += __shfl_xor(a, 1, 64);
+      a += __shfl_xor(a, 2, 64);
+      a += __shfl_xor(a, 4, 64);
+      dp += __shfl_xor(dp, 1, 64);
+      dp += __shfl_xor(dp, 2, 64);
+      dp += __shfl_xor(dp, 4, 64);
+      const float t = act ? tau * a : -INFINITY;
+      const float m = block_max((qd == 0) ? t : -INFINITY, red);
+      const float z = block_sum((qd == 0 && act) ? __expf(t - m) : 0.0f, red);
+      const float lpi = t - (m + __logf(z));
+      const float pi = act ? __expf(lpi) : 0.0f;
+      const float dpi = act ? dp + dbs[r] * (-lpi - 1.0f) : 0.0f;
+      const float spd = block_sum((qd == 0) ? pi * dpi : 0.0f, red);
+      const float dt = pi * (dpi - spd);
+      // dlm = tau sum_j dt_j k_j (column sums over the chunk's tokens)
+      if (act) {
+#pragma unroll
+        for (int x = 0; x < CE; ++x)
+          if (x < DQ) tmp[jt * d + e0 + x] = dt * kj[x];
+      }
+      __syncthreads();
+      for (int e = tid; e < d; e += CT) {
+        float sum = 0.0f;
+        for (int j = 0; j < jn; ++j) sum += tmp[j * d + e];
+        dlm[ho + e] = tau * sum;
+      }
+#pragma unroll
+      for (int x = 0; x < CE; ++x)
+        if (x < DQ) dkj[x] = fmaf(tau * dt, lv[x], fmaf(pi, dks[r * d + e0 + x], dkj[x]));
+      __syncthreads();
+    }
+  }
+  if (act) {
+    float* dko = dk + (bg * (long long)N + j0 + jt) * d + e0;
+    float* dvo = dv + (bg * (long long)N + j0 + jt) * d + e0;
+#pragma unroll
+    for (int x = 0; x < CE; ++x) {
+      if (x < DQ) {
+        dko[x] = dkj[x];
+        dvo[x] = dvj[x];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+size_t hils_bwd_rows_lds(const HilsShape& s) {
+  const int L = s.W + s.S - 1;
+  const int Lp = (L + 3) & ~3;
+  return sizeof(float) * ((size_t)4 * s.G * s.d + 2 * (size_t)s.G * Lp + 2 * (size_t)s.G * s.S +
+                          (size_t)s.K * s.G * 4 + (size_t)s.G * 4 + 4);
+}
+
+hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* qr, const void* k,
+                                const void* v, const void* lm, const void* dout, const int32_t* sel,
+                                const void* ksum, const float* bsum, float* dq, float* dqr,
+                                float* dk, float* dv, float* dlm, const HilsBwdBufs& wb,
+                                hipStream_t st) {
+  const float tau = (float)s.tau;
+  const size_t lshm = sizeof(uint32_t) * (size_t)(s.nC > 0 ? s.nC : 1);
+  hipFuncSetAttribute((const void*)k_bwd_lists, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lshm);
+  { HilsProfScope ps_("k_bwd_lists", st);
+    hipLaunchKernelGGL(k_bwd_lists, dim3((unsigned)(s.B * s.Hkv)), dim3(1024), lshm, st, sel,
+                       wb.off, wb.ent, s.N, s.K, s.nC); }
+  const size_t rshm = hils_bwd_rows_lds(s);
+  const size_t cshm = sizeof(float) * ((size_t)s.G * s.d + s.G + (size_t)s.S * s.d + 8) +
+                      (size_t)CBATCH * (sizeof(int) + 4 * sizeof(float));
+  const int sep = dqr != nullptr;
+  if (s.dtype == 0) {
+    hipFuncSetAttribute((const void*)k_bwd_rows<bf16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rshm);
+    hipFuncSetAttribute((const void*)k_bwd_cols<bf16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)cshm);
+    { HilsProfScope ps_("k_bwd_rows", st);
+      hipLaunchKernelGGL(k_bwd_rows<bf16_t>, dim3((unsigned)((long long)s.B * s.Hkv * s.N)), dim3(BT), rshm, st,
+                         (const bf16_t*)q, (const bf16_t*)qr, (const bf16_t*)k, (const bf16_t*)v,
+                         (const bf16_t*)ksum, bsum, (const bf16_t*)dout, sel, dq, dqr, wb.pstat,
+                         wb.wstat, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, tau, sep); }
+    { HilsProfScope ps_("k_bwd_cols", st);
+      hipLaunchKernelGGL(k_bwd_cols<bf16_t>, dim3((unsigned)((long long)s.B * s.Hkv * s.nCc)), dim3(CT), cshm, st,
+                         (const bf16_t*)q, (const bf16_t*)qr, (const bf16_t*)k, (const bf16_t*)v,
+                         (const bf16_t*)lm, (const bf16_t*)dout, wb.off, wb.ent, wb.pstat, wb.wstat,
+                         dk, dv, dlm, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, s.nCc, tau,
+                         s.mode); }
+  } else {
+    hipFuncSetAttribute((const void*)k_bwd_rows<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rshm);
+    hipFuncSetAttribute((const void*)k_bwd_cols<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)cshm);
+    { HilsProfScope ps_("k_bwd_rows", st);
+      hipLaunchKernelGGL(k_bwd_rows<float>, dim3((unsigned)((long long)s.B * s.Hkv * s.N)), dim3(BT), rshm, st,
+                         (const float*)q, (const float*)qr, (const float*)k, (const float*)v,
+                         (const float*)ksum, bsum, (const float*)dout, sel, dq, dqr, wb.pstat,
+                         wb.wstat, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, tau, sep); }
+    { HilsProfScope ps_("k_bwd_cols", st);
+      hipLaunchKernelGGL(k_bwd_cols<float>, dim3((unsigned)((long long)s.B * s.Hkv * s.nCc)), dim3(CT), cshm, st,
+                         (const float*)q, (const float*)qr, (const float*)k, (const float*)v,
+                         (const float*)lm, (const float*)dout, wb.off, wb.ent, wb.pstat, wb.wstat,
+                         dk, dv, dlm, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, s.nCc, tau,
+                         s.mode); }
+  }
+  return hipGetLastError();
+}

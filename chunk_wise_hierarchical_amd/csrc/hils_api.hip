@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "../../include/hils.h"
+#include "hils_bwd.h"
 #include "hils_internal.h"
 
 namespace {
@@ -124,6 +125,37 @@ DecodeLayout decode_layout(const HilsShape& s) {
   L.lsep = off;   off += align_up(BM * s.Hq * ((nm + HILS_DEC_SCORE_ROWS - 1) / HILS_DEC_SCORE_ROWS) * 8);
   L.total = off;
   return L;
+}
+
+struct BwdLayout {
+  size_t ks, bs, off, ent, pstat, wstat, total;
+};
+BwdLayout bwd_layout(const HilsShape& s) {
+  BwdLayout L{};
+  const size_t BG = (size_t)s.B * s.Hkv;
+  size_t off = 0;
+  L.ks = off;    off += align_up((size_t)s.B * s.Hq * s.nC * s.d * (s.dtype == HILS_BF16 ? 2 : 4));
+  L.bs = off;    off += align_up((size_t)s.B * s.Hq * s.nC * 4);
+  L.off = off;   off += align_up(BG * (s.nC + 1) * 4);
+  L.ent = off;   off += align_up(BG * s.N * s.K * 4);
+  L.pstat = off; off += align_up(BG * s.N * s.K * s.G * 16);
+  L.wstat = off; off += align_up((size_t)s.B * s.Hq * s.N * 16);
+  L.total = off;
+  return L;
+}
+
+// shapes the backward kernels take
+hils_status bwd_supported(const HilsShape& s) {
+  if (s.mode == HILS_SCORE_EXACT) return HILS_E_UNSUPPORTED;
+  // per-thread quarter rows are read with 16-byte vectors
+  if (s.d > 128 || s.d % (s.dtype == HILS_BF16 ? 32 : 16) != 0) return HILS_E_UNSUPPORTED;
+  if (s.S > 64 || s.G > 8 || s.K > 128) return HILS_E_UNSUPPORTED;
+  if (s.N >= (1 << 24)) return HILS_E_UNSUPPORTED;
+  if ((long long)s.B * s.Hkv * s.N * s.K >= (1LL << 31)) return HILS_E_UNSUPPORTED;
+  if ((long long)s.B * s.Hkv * s.N >= (1LL << 31)) return HILS_E_UNSUPPORTED;
+  if (hils_bwd_rows_lds(s) > 160 * 1024) return HILS_E_UNSUPPORTED;
+  if ((size_t)s.nC * 4 > 160 * 1024) return HILS_E_UNSUPPORTED;
+  return HILS_OK;
 }
 
 inline hils_status hip_status(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_E_HIP; }
@@ -353,6 +385,48 @@ hils_status hils_decode_multi(const hils_cfg* cfg, int32_t M, const void* q, con
                                        (float*)(w + L.scores), (uint32_t*)(w + L.keys),
                                        (float*)(w + L.slog), (float*)(w + L.part),
                                        (float*)(w + L.lsep), nullptr, 0, 0, (hipStream_t)stream));
+}
+
+size_t hils_prefill_backward_workspace_bytes(const hils_cfg* cfg) {
+  HilsShape s;
+  if (make_shape(cfg, s) != HILS_OK || bwd_supported(s) != HILS_OK) return 0;
+  return bwd_layout(s).total;
+}
+
+hils_status hils_prefill_backward(const hils_cfg* cfg, const void* q, const void* q_route,
+                                  const void* k, const void* v, const void* lm_q, const void* dout,
+                                  const int32_t* sel, const void* k_sum, const float* b_sum,
+                                  float* dq, float* dq_route, float* dk, float* dv, float* dlm,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  HilsShape s;
+  hils_status r = make_shape(cfg, s);
+  if (r != HILS_OK) return r;
+  r = bwd_supported(s);
+  if (r != HILS_OK) return r;
+  const bool need_lm = s.mode != HILS_SCORE_MEAN_POOL;
+  if (!q || !k || !v || !dout || !sel || !dq || !dk || !dv) return HILS_E_ARG;
+  if (s.nC > 0 && need_lm && (!lm_q || !dlm)) return HILS_E_ARG;
+  if ((q_route == nullptr) != (dq_route == nullptr)) return HILS_E_ARG;
+  if ((k_sum == nullptr) != (b_sum == nullptr)) return HILS_E_ARG;
+  const void* ptrs[] = {q, q_route, k, v, lm_q, dout, sel, k_sum, b_sum, dq, dq_route, dk, dv, dlm, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return HILS_E_ARG;
+  const BwdLayout L = bwd_layout(s);
+  if (ws_bytes < L.total || !ws) return HILS_E_WORKSPACE;
+  char* w = static_cast<char*>(ws);
+  hipStream_t st = (hipStream_t)stream;
+  const void* ks = k_sum;
+  const float* bs = b_sum;
+  if (!k_sum && s.nC > 0) {
+    hipError_t e = hils_launch_summarize(s, k, lm_q, 0, s.nC, w + L.ks, (float*)(w + L.bs), st);
+    if (e != hipSuccess) return HILS_E_HIP;
+    ks = w + L.ks;
+    bs = (const float*)(w + L.bs);
+  }
+  HilsBwdBufs wb{(uint32_t*)(w + L.off), (uint32_t*)(w + L.ent), (float*)(w + L.pstat),
+                 (float*)(w + L.wstat)};
+  return hip_status(hils_launch_backward(s, q, q_route ? q_route : q, k, v, lm_q, dout, sel, ks, bs,
+                                         dq, dq_route, dk, dv, dlm, wb, st));
 }
 
 hils_status hils_summarize_paged(const hils_cfg* cfg, const void* k_pages, const void* lm_pages,

@@ -180,6 +180,32 @@ hils_status hils_decode_paged(const hils_cfg* cfg, const void* q, const void* q_
                               const void* k_sum_pages, const float* b_sum_pages, void* out,
                               int32_t* sel, void* ws, size_t ws_bytes, void* stream);
 
+/* Prefill backward (training through HiLS attention).  Gradients of
+ * L = sum(dout * out) of hils_prefill, with the top-K selection held fixed (the
+ * forward's sel [B][Hkv][N][K]; a hard choice has no gradient) and every other
+ * step differentiated (section 3): the chunk-level fusion softmax into the
+ * chunk scores and the window log-mass, the chunk and window softmaxes into
+ * q, k, v, the routing equation into q_route (or q), k'_c and b'_c, and the
+ * Proposition 3.1 summary softmax into the landmark queries and k (modes
+ * LANDMARK_KEY: dlm = dk'; MEAN_POOL: dk += dk'/S, no dlm; EXACT unsupported).
+ *   dout            : [B][Hq][N][d], dtype;
+ *   k_sum, b_sum    : the forward's summaries, or both NULL to recompute them;
+ *   dq, dk, dv      : fp32 outputs shaped like q, k, v (fully written);
+ *   dq_route        : fp32 [B][Hq][N][d] iff q_route is given (the token query
+ *                     then gets only the attention part);
+ *   dlm             : fp32 [B][Hq][N/S][d] (may be NULL in MEAN_POOL mode).
+ * The kernels use no atomics, so results are deterministic.  Supports d <= 128
+ * (a multiple of 32 for bf16, of 16 for fp32), S <= 64, G <= 8, K <= 128 and
+ * windows whose G head rows of logits fit in LDS (otherwise
+ * HILS_E_UNSUPPORTED, and hils_prefill_backward_workspace_bytes returns 0).
+ */
+size_t hils_prefill_backward_workspace_bytes(const hils_cfg* cfg);
+hils_status hils_prefill_backward(const hils_cfg* cfg, const void* q, const void* q_route,
+                                  const void* k, const void* v, const void* lm_q, const void* dout,
+                                  const int32_t* sel, const void* k_sum, const float* b_sum,
+                                  float* dq, float* dq_route, float* dk, float* dv, float* dlm,
+                                  void* ws, size_t ws_bytes, void* stream);
+
 const char* hils_strerror(hils_status status);
 int hils_abi_version(void);
 
