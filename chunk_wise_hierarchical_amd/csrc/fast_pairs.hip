@@ -32,6 +32,18 @@ using namespace fastp;
 
 namespace {
 
+// Streaming (non-temporal) access for the per-pair outputs, which are written
+// once and read once: they should not displace cached query rows and K/V.
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void st_u4_nt(void* p, uint4 v) {
+  nt_u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<nt_u32x4*>(p));
+}
+__device__ __forceinline__ uint4 ld_u4_nt(const void* p) {
+  nt_u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
+
 constexpr int NT = 256;
 constexpr int KSTR = D;       // K tile row stride (elements); 16-byte parts XOR-swizzled per row
 constexpr int VSTR = S + 8;   // V^T tile row stride (elements)
@@ -530,9 +542,9 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
                                     pack_bf16x2(acc[2 * j][2], acc[2 * j][3]),
                                     pack_bf16x2(acc[2 * j + 1][0], acc[2 * j + 1][1]),
                                     pack_bf16x2(acc[2 * j + 1][2], acc[2 * j + 1][3]));
-        st_u4(op + 8 * (4 * j + lq), uu);
+        st_u4_nt(op + 8 * (4 * j + lq), uu);
       }
-      if (lq == 0) lamb[prow * G + h] = lam;
+      if (lq == 0) __builtin_nontemporal_store(lam, lamb + prow * G + h);
     }
     e0 = e1;
     e1 = e2;
@@ -626,11 +638,11 @@ k_pair_reduce(const float* __restrict__ swa, const float* __restrict__ lz,
     for (; kx + RU <= kk; kx += RU) {      // RU slot loads in flight
       uint4 uv[RU];
 #pragma unroll
-      for (int t = 0; t < RU; ++t) uv[t] = ld_u4(pp + (long long)(kx + t) * G * D);
+      for (int t = 0; t < RU; ++t) uv[t] = ld_u4_nt(pp + (long long)(kx + t) * G * D);
 #pragma unroll
       for (int t = 0; t < RU; ++t) add(wr[kx + t], uv[t]);
     }
-    for (; kx < kk; ++kx) add(wr[kx], ld_u4(pp + (long long)kx * G * D));
+    for (; kx < kk; ++kx) add(wr[kx], ld_u4_nt(pp + (long long)kx * G * D));
     bf16_t* op = out + (((long long)b * Hq + (long long)g * G + h) * N + i) * D;
     *reinterpret_cast<uint2*>(op + d0) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
     *reinterpret_cast<uint2*>(op + d0 + 16) = make_uint2(pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7]));
