@@ -10,20 +10,23 @@
 // wavefront computes a 32-chunk x 32-query score tile of one head with
 // v_mfma_f32_32x32x16_bf16 (A = k' rows, B = q_hat).  Scores are kept in
 // base-2 units (scaled by log2 e), which preserves their order.
-//   pass 0: per (query, head) online log-sum-exp over C_i (G > 1), and the four
+//   pass 0: per (query, head) online log-sum-exp over C_i (G > 1), and the three
 //           largest scores seen in each of the lane's 16 register slots.  The
-//           K-th largest of a (query, head)'s 128 tracked scores is a lower
+//           K-th largest of a (query, head)'s 96 tracked scores is a lower
 //           bound bound_h on its K-th best score; T = max_h (bound_h - L_h) is
 //           then a lower bound on the K-th best group score, because the >= K
 //           chunks reaching bound_h all have a group score >= bound_h - L_h.
 //   pass 1: group score g = max_h (s_h - L_h) (cross-head max through LDS);
-//           chunks scoring above the query's current K-th best key (initially
-//           T) go to an LDS staging list, which is merged into the query's
-//           sorted top-K list (wavefront bitonic sort of the staged keys and
-//           one bitonic merge) when it could overflow.
+//           chunks whose score reaches the query's current K-th best (initially
+//           T; a float compare) go to an LDS staging list, which is merged into
+//           the query's sorted top-K list (wavefront bitonic sort of the staged
+//           keys and one bitonic merge) before a step whose keys would not fit.
+// The MFMA accumulator starts at b'_c / scale, so scores come out in units of
+// 1 / (scale log2 e) with the bias already added.
 // Keys are 64-bit: (order-preserving bits of g) << 32 | (~chunk id), so ties
 // rank the lower chunk id first and every key is unique.  The selected ids
 // are written ascending, -1 padded.
+#include <cfloat>
 #include <type_traits>
 
 #include "fast_common.h"
@@ -48,11 +51,11 @@ struct Geo {
   static constexpr int QW = QB / 4;       // queries per wavefront in the selection layout
   static constexpr int LQ = 64 / QW;      // lanes per query
   static constexpr int CL = CT / LQ;      // chunks per lane per tile (selection layout)
-  // staging slots per query; one selection step (one chunk per lane) adds at
-  // most LQ keys, so a query merges once more than STG - LQ are waiting.  G = 1
-  // keeps a smaller area so two workgroups still fit one CU's LDS.
-  static constexpr int STG = (G == 1) ? 48 : 56;
-  static constexpr int STG_MERGE = STG - LQ;
+  // staging slots per query.  One selection step adds at most LQ * CL = 32
+  // keys to a query, which merges its staged keys first when they would not
+  // fit.  G = 4 keeps 56 so that two workgroups fit one CU's LDS.
+  static constexpr int STG = (G == 1) ? 64 : 56;
+  static_assert(LQ * CL <= STG, "one step must fit an empty staging area");
 };
 
 // [0, 64 KB) is also the scratch of the tracked scores between the passes
@@ -178,20 +181,20 @@ template <int G>
 __global__ void __launch_bounds__(NT, 2)
 k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
              const float* __restrict__ bsum, int32_t* __restrict__ sel, int Hq, int Hkv, int N,
-             int W, int K, int nC, float tau2, int nqb) {
+             int W, int K, int nC, float tau2, float bscale, int nqb) {
   using GE = Geo<G>;
   constexpr int QB = GE::QB, QW = GE::QW, LQ = GE::LQ, CL = GE::CL;
-  constexpr int STG = GE::STG, STG_MERGE = GE::STG_MERGE;
+  constexpr int STG = GE::STG;
   extern __shared__ __align__(16) unsigned char sm[];
   const Lds<G> L(K);
   bf16_t* ktile = reinterpret_cast<bf16_t*>(sm + L.ktile);   // [G][CT][16 parts], part ^= c & 15
-  float* btile = reinterpret_cast<float*>(sm + L.btile);     // [G][CT]  (b' * log2 e)
+  float* btile = reinterpret_cast<float*>(sm + L.btile);     // [G][CT]  b' * log2 e / tau2
   float* xb = reinterpret_cast<float*>(sm + L.xb);           // [G][QB][XROW]
   float* tq = reinterpret_cast<float*>(sm + L.tq);           // [G][QB] log-sum-exp (base 2)
   float* tk = reinterpret_cast<float*>(sm + L.tk);           // [G][QB] K-th tracked score
   float* trk = reinterpret_cast<float*>(sm + L.ktile);       // [G*QB][TRK] between the passes
   uint64_t* lst = reinterpret_cast<uint64_t*>(sm + L.lst);   // [QB][K]
-  uint64_t* stg = reinterpret_cast<uint64_t*>(sm + L.stg);   // [QB][STG]
+  uint2* stg = reinterpret_cast<uint2*>(sm + L.stg);         // [QB][STG] (score bits, chunk id)
   uint32_t* cnt_lst = reinterpret_cast<uint32_t*>(sm + L.cnt);
   uint64_t* thr = reinterpret_cast<uint64_t*>(sm + L.thr);
   float* thf = reinterpret_cast<float*>(sm + L.thf);        // [QB] thr as a float (prefilter)
@@ -280,14 +283,18 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
       const int h = piece / (CT * 16), c = (piece / 16) % CT, part = piece % 16;
       st_u4(ktile + ((size_t)h * CT + c) * D + ((part ^ (c & 15)) * 8), pre[p]);
     }
-    if (tid < G * CT) btile[tid] = bpre * LOG2E;
+    if (tid < G * CT) btile[tid] = bpre * bscale;
   };
 
   // merge query q's ns staged keys into its sorted top-K list (whole wavefront)
   auto merge = [&](int q, int ns) {
     const int nl = (int)cnt_lst[q];
     const uint64_t a = (lane < nl) ? lst[(size_t)q * K + lane] : 0ull;
-    uint64_t sb = (lane < ns) ? stg[(size_t)q * STG + lane] : 0ull;
+    uint64_t sb = 0ull;
+    if (lane < ns) {
+      const uint2 e = stg[(size_t)q * STG + lane];
+      sb = ((uint64_t)f32_order_key(__uint_as_float(e.x)) << 32) | (uint64_t)(0xffffffffu - e.y);
+    }
     sb = sort64_desc(sb, lane);
     const uint64_t v = merge_top64(a, sb, lane);
     const int tot = min(K, nl + ns);
@@ -308,28 +315,29 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   };
 
-  // scores of tile t for this lane (base 2): x[i] <-> chunk 32t + 8(i>>2) + 4*half + (i&3)
+  // scores of tile t for this lane in accumulator units (score = tau2 * x, base
+  // 2): x[i] <-> chunk 32t + 8(i>>2) + 4*half + (i&3).  The accumulator starts
+  // at b' / tau2 of its chunk, so the bias costs no vector instruction.
   const int n_lo = n_cand(i0, W, S);                 // every query of the block has >= n_lo
-  // ainit seeds the accumulator (every value of a lane belongs to one query):
-  // pass 1 starts it at -L / scale, which folds the head's log-sum-exp into
-  // the score without a separate subtraction
-  auto tile_scores = [&](int t, float* x, const f32x16_t& aseed) {
+  auto tile_scores = [&](int t, float* x) {
     const bf16_t* kb = ktile + ((size_t)hw * CT + col) * D;
     bf16x8_t a[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) a[ks] = ld_bf16x8(kb + (((2 * ks + half) ^ (col & 15)) * 8));
-    f32x16_t acc = mfma32(a[0], bq[0], aseed);
-#pragma unroll
-    for (int ks = 1; ks < 8; ++ks) acc = mfma32(a[ks], bq[ks], acc);
     const float* bt = btile + (size_t)hw * CT;
+    f32x16_t acc;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       const float4 b4 = *reinterpret_cast<const float4*>(bt + 8 * gq + 4 * half);
-      x[4 * gq + 0] = fmaf(acc[4 * gq + 0], tau2, b4.x);
-      x[4 * gq + 1] = fmaf(acc[4 * gq + 1], tau2, b4.y);
-      x[4 * gq + 2] = fmaf(acc[4 * gq + 2], tau2, b4.z);
-      x[4 * gq + 3] = fmaf(acc[4 * gq + 3], tau2, b4.w);
+      acc[4 * gq + 0] = b4.x;
+      acc[4 * gq + 1] = b4.y;
+      acc[4 * gq + 2] = b4.z;
+      acc[4 * gq + 3] = b4.w;
     }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) acc = mfma32(a[ks], bq[ks], acc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = acc[i];
     if (CT * t + CT > n_lo) {                        // tile crosses some query's candidate range
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -345,51 +353,52 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   auto run_pass = [&](auto pass_tag) {
     constexpr int pass = decltype(pass_tag)::value;
     float m = -INFINITY, ssum = 0.0f;
-    float t0[16], t1[16], t2[16], t3[16];  // top 4 per register slot, descending (pass 0)
+    float t0[16], t1[16], t2[16];  // top 3 per register slot, descending (pass 0)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { t0[i] = -INFINITY; t1[i] = -INFINITY; t2[i] = -INFINITY; t3[i] = -INFINITY; }
+    for (int i = 0; i < 16; ++i) { t0[i] = -INFINITY; t1[i] = -INFINITY; t2[i] = -INFINITY; }
     load_tile(0, preA, bpreA);
     store_tile(preA, bpreA);
     __syncthreads();
     load_tile(min(1, ntiles - 1), preA, bpreA);
-    // pass 1 accumulator seed: -L / scale (L = +inf/-inf only for rows without
+    // pass 1 subtracts the head's log-sum-exp (L = -inf only for rows without
     // candidates, whose scores are all masked)
-    const float ainit = (pass == 1 && G > 1) ? -L2 / tau2 : 0.0f;
-    f32x16_t aseed;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) aseed[i] = ainit;
+    const float nL = (L2 > -INFINITY) ? -L2 : 0.0f;
     // one tile step: cur holds tile t + 1 (stored to LDS during the step), nxt
     // receives tile t + 2
     auto step = [&](int t, const uint4 (&cur)[PPT], float bcur, uint4 (&nxt)[PPT], float& bnxt) {
       load_tile(min(t + 2, ntiles - 1), nxt, bnxt);
       float x[16];
-      tile_scores(t, x, aseed);
+      tile_scores(t, x);
       if constexpr (pass == 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          // insert x into t0 >= t1 >= t2 >= t3: each new entry is the median of
-          // its old neighbours above and below and x
-          t3[i] = __builtin_amdgcn_fmed3f(t2[i], t3[i], x[i]);
+          // insert x into t0 >= t1 >= t2: each new entry is the median of its
+          // old neighbours above and below and x
           t2[i] = __builtin_amdgcn_fmed3f(t1[i], t2[i], x[i]);
           t1[i] = __builtin_amdgcn_fmed3f(t0[i], t1[i], x[i]);
           t0[i] = fmaxf(t0[i], x[i]);
         }
         if (G > 1) {
+          // online log-sum-exp; m is the running maximum in accumulator units
           float mt = x[0];
 #pragma unroll
           for (int i = 1; i < 16; ++i) mt = fmaxf(mt, x[i]);
-          if (mt > m) { ssum = (m == -INFINITY) ? 0.0f : ssum * fast_exp2(m - mt); m = mt; }
+          if (mt > m) { ssum = (m == -INFINITY) ? 0.0f : ssum * fast_exp2((m - mt) * tau2); m = mt; }
           if (m != -INFINITY) {
+            const float mneg = -m * tau2;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) ssum += fast_exp2(x[i] - m);
+            for (int i = 0; i < 16; ++i) ssum += fast_exp2(fmaf(x[i], tau2, mneg));
           }
         }
         __syncthreads();
         store_tile(cur, bcur);   // past the last tile: rewrites the last tile, unused
         __syncthreads();
       } else {
-        // group scores: x already holds s_h - L_h; the heads of a group meet in LDS
+        // group scores: s_h - L_h (base 2); the heads of a group meet in LDS.
+        // G = 1 keeps accumulator units, which order the chunks the same way.
         if (G > 1) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = fmaf(x[i], tau2, nL);
           const int xrow = hw * QB + 32 * qw + col;
           float* xr = xb + (size_t)xrow * XROW;
 #pragma unroll
@@ -420,35 +429,56 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
           for (int i = 0; i < CL; ++i) gs[i] = x[i];
           cid0 = CT * t;
         }
-        // filter against the query's current K-th best key (float prefilter, then
-        // the exact 64-bit key) and stage the survivors.  A query's staging
-        // slots are handed out within its lane group by ballot ranks, and its
-        // count lives in a register of every lane of the group.
-        const float tf = thf[qsel];
-        const uint64_t th = thr[qsel];
-        int off = nstg;
-        const bool leader = (G == 1) ? (half == 0) : (lane % LQ == 0);
+        // filter: stage the chunks whose group score reaches the query's current
+        // bound (a float compare: a chunk tied with the K-th key may be staged,
+        // and the merge drops it).  Masked chunks (-inf) never pass.
+        const float tf = fmaxf(thf[qsel], -FLT_MAX);
+        bool pj[CL];
+        int c = 0;
 #pragma unroll
         for (int j = 0; j < CL; ++j) {
-          const int cid = (G == 1) ? (cid0 + 8 * (j >> 2) + 4 * half + (j & 3)) : (cid0 + j);
-          const uint64_t key = ((uint64_t)f32_order_key(gs[j]) << 32) |
-                               (uint64_t)(0xffffffffu - (uint32_t)cid);
-          const bool pass_j = gs[j] != -INFINITY && gs[j] >= tf && key > th;
-          const uint64_t m = __ballot(pass_j) & gmask;
-          if (pass_j)
-            stg[(size_t)qsel * STG + off + lanes_below(m)] = key;
-          off += __popcll(m);
-          // merge the queries whose next step could overflow their staging
-          unsigned long long need = __ballot(leader && off > STG_MERGE);
-          while (need) {
-            const int l = __ffsll((long long)need) - 1;
-            need &= need - 1;
-            const int q = (G == 1) ? (32 * w + l) : (w * QW + l / LQ);
-            merge(q, __builtin_amdgcn_readlane(off, l));
-            if (qsel == q) off = 0;
+          pj[j] = gs[j] >= tf;
+          c += pj[j] ? 1 : 0;
+        }
+        // this lane's slots: prefix of c over the query's lane group (xor
+        // butterfly: lane l ^ s holds the total of the sibling block), and the
+        // group's total
+        int incl = c, tot = c;
+        if (G == 1) {
+          const int p = (int)xshfl((uint32_t)tot, 32);
+          incl += half ? p : 0;
+          tot += p;
+        } else {
+#pragma unroll
+          for (int sh = 1; sh < LQ; sh <<= 1) {
+            const int p = (int)xshfl((uint32_t)tot, sh);
+            incl += (lane & sh) ? p : 0;
+            tot += p;
           }
         }
-        nstg = off;
+        // merge the queries whose staged keys and this step's would not fit
+        const bool leader = (G == 1) ? (half == 0) : (lane % LQ == 0);
+        unsigned long long need = __ballot(leader && nstg + tot > STG);
+        while (need) {
+          const int l = __ffsll((long long)need) - 1;
+          need &= need - 1;
+          const int q = (G == 1) ? (32 * w + l) : (w * QW + l / LQ);
+          merge(q, __builtin_amdgcn_readlane(nstg, l));
+          if (qsel == q) nstg = 0;
+        }
+        if (c > 0) {
+          uint2* sq = stg + (size_t)qsel * STG;
+          int pos = nstg + incl - c;
+#pragma unroll
+          for (int j = 0; j < CL; ++j) {
+            const int cid = (G == 1) ? (cid0 + 8 * (j >> 2) + 4 * half + (j & 3)) : (cid0 + j);
+            if (pj[j]) {
+              sq[pos] = make_uint2(__float_as_uint(gs[j]), (uint32_t)cid);
+              ++pos;
+            }
+          }
+        }
+        nstg += tot;
         __syncthreads();         // next k' tile visible; exchange reads done
       }
     };
@@ -466,15 +496,16 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
         tr[0] = t0[i];
         tr[16] = t1[i];
         tr[32] = t2[i];
-        tr[48] = t3[i];
+        tr[48] = -INFINITY;
       }
       if (G > 1) {
         const float m2 = __shfl_xor(m, 32, 64), s2 = __shfl_xor(ssum, 32, 64);
         const float M = fmaxf(m, m2);
         float s = 0.0f;
         if (M != -INFINITY)
-          s = (m == -INFINITY ? 0.0f : ssum * fast_exp2(m - M)) + (m2 == -INFINITY ? 0.0f : s2 * fast_exp2(m2 - M));
-        L2 = M + log2f(s);
+          s = (m == -INFINITY ? 0.0f : ssum * fast_exp2((m - M) * tau2)) +
+              (m2 == -INFINITY ? 0.0f : s2 * fast_exp2((m2 - M) * tau2));
+        L2 = M * tau2 + log2f(s);
       }
       if (half == 0) tq[pr] = L2;
       __syncthreads();
@@ -491,10 +522,10 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
         float T = -INFINITY;
         for (int h = 0; h < G; ++h) {
           const float kh = tk[(size_t)h * QB + t];
-          if (kh != -INFINITY) T = fmaxf(T, (G > 1) ? kh - tq[(size_t)h * QB + t] : kh);
+          if (kh != -INFINITY) T = fmaxf(T, (G > 1) ? kh * tau2 - tq[(size_t)h * QB + t] : kh);
         }
-        // pass 1 computes s_h - L_h with L folded into the accumulator, which
-        // rounds differently from pass 0: lower the bound by a margin far
+        // pass 1 computes s_h - L_h as one fma of the accumulator, which rounds
+        // differently from the product above: lower the bound by a margin far
         // above that rounding so no chunk at the bound is lost
         const float Tm = (T == -INFINITY) ? -INFINITY : T - (1e-3f + 1e-6f * fabsf(T));
         thr[t] = (Tm == -INFINITY) ? 0ull : ((uint64_t)f32_order_key(Tm) << 32);
@@ -529,9 +560,10 @@ hipError_t launch_score(const HilsShape& s, const void* qr, const void* ksum, co
   auto f = k_score_fast<G>;
   hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
   const float tau2 = (float)(s.tau * 1.4426950408889634);
+  const float bscale = (float)(1.0 / s.tau);   // b' log2 e / tau2
   { HilsProfScope ps_("k_score_fast", st); hipLaunchKernelGGL(f, dim3((unsigned)((long long)s.B * s.Hkv * nqb)), dim3(NT), L.total, st,
                      (const bf16_t*)qr, (const bf16_t*)ksum, bsum, sel, s.Hq, s.Hkv, s.N, s.W, s.K,
-                     s.nC, tau2, nqb); }
+                     s.nC, tau2, bscale, nqb); }
   return hipGetLastError();
 }
 
