@@ -11,11 +11,11 @@
 // v_mfma_f32_32x32x16_bf16 (A = k' rows, B = q_hat).  Scores are kept in
 // base-2 units (scaled by log2 e), which preserves their order.
 //   pass 0: per (query, head) online log-sum-exp over C_i (G > 1), and the three
-//           largest scores seen in each of the lane's 16 register slots.  The
-//           K-th largest of a (query, head)'s 96 tracked scores is a lower
-//           bound bound_h on its K-th best score; T = max_h (bound_h - L_h) is
-//           then a lower bound on the K-th best group score, because the >= K
-//           chunks reaching bound_h all have a group score >= bound_h - L_h.
+//           largest scores seen in each of the lane's 16 register slots.  Per
+//           slot and rank r, u = max_h (r-th best of head h - L_h) is reached by
+//           the group scores of r + 1 distinct chunks of the slot; the K-th
+//           largest u of a query (96 per query) is then a lower bound T on its
+//           K-th best group score.
 //   pass 1: group score g = max_h (s_h - L_h) (cross-head max through LDS);
 //           chunks whose score reaches the query's current K-th best (initially
 //           T; a float compare) go to an LDS staging list, which is merged into
@@ -38,7 +38,7 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int CT = 32;         // chunks per tile
-constexpr int TRK = 128;       // pass-0 tracked scores per (query, head): top 4 of 32 slots
+constexpr int TRK = 128;       // pass-0 tracked scores per (query, head): 32 slots x ranks 0-2 (rank 3 unused)
 constexpr int XROW = CT;       // row of the cross-head exchange buffer (floats); its 16-byte
                                // pieces are XOR-swizzled by the row's low 3 bits
 // buffer descriptor word 3 for raw (unformatted, stride 0) loads on gfx9-family
@@ -191,7 +191,7 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   float* btile = reinterpret_cast<float*>(sm + L.btile);     // [G][CT]  b' * log2 e / tau2
   float* xb = reinterpret_cast<float*>(sm + L.xb);           // [G][QB][XROW]
   float* tq = reinterpret_cast<float*>(sm + L.tq);           // [G][QB] log-sum-exp (base 2)
-  float* tk = reinterpret_cast<float*>(sm + L.tk);           // [G][QB] K-th tracked score
+  float* tk = reinterpret_cast<float*>(sm + L.tk);           // [QB] bound T of the query
   float* trk = reinterpret_cast<float*>(sm + L.ktile);       // [G*QB][TRK] between the passes
   uint64_t* lst = reinterpret_cast<uint64_t*>(sm + L.lst);   // [QB][K]
   uint2* stg = reinterpret_cast<uint2*>(sm + L.stg);         // [QB][STG] (score bits, chunk id)
@@ -487,8 +487,7 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
       if (t + 1 < ntiles) step(t + 1, preB, bpreB, preA, bpreA);
     }
     if constexpr (pass == 0) {
-      // per (query, head): log-sum-exp, and the K-th largest of the 128 tracked
-      // scores (a lower bound on the head's K-th best score)
+      // per (query, head): log-sum-exp and the tracked scores, by slot and rank
       const int pr = hw * QB + 32 * qw + col;        // (head, query) pair of this lane
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -509,21 +508,36 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
       }
       if (half == 0) tq[pr] = L2;
       __syncthreads();
-      for (int j = 0; j < (G * QB) / 4; ++j) {
-        const int p = w * ((G * QB) / 4) + j;
-        const float va = sort64_desc_f(trk[(size_t)p * TRK + lane], lane);
-        const float vb = sort64_desc_f(trk[(size_t)p * TRK + 64 + lane], lane);
-        const float v = merge_top64_f(va, vb, lane);
+      // bound T of a query: every head tracks, in each register slot (a fixed
+      // set of chunk positions, the same for all heads), its three best scores,
+      // which belong to three distinct chunks.  u(slot, r) = max_h (t_r,h - L_h)
+      // is thus reached by the group scores of at least r + 1 distinct chunks of
+      // the slot, and slots share no chunk: at least K distinct chunks reach the
+      // K-th largest u of the query, which bounds its K-th best group score.
+      for (int j = 0; j < QB / 4; ++j) {
+        const int q = w * (QB / 4) + j;
+        float ua = -INFINITY, ub = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float* tr = trk + (size_t)(h * QB + q) * TRK;
+          const float lh = tq[(size_t)h * QB + q];
+          const float va = tr[lane], vb = tr[64 + lane];
+          if (G > 1) {
+            // a finite tracked score implies candidates, hence a finite L
+            if (va != -INFINITY) ua = fmaxf(ua, va * tau2 - lh);
+            if (vb != -INFINITY) ub = fmaxf(ub, vb * tau2 - lh);
+          } else {
+            ua = va;
+            ub = vb;
+          }
+        }
+        const float v = merge_top64_f(sort64_desc_f(ua, lane), sort64_desc_f(ub, lane), lane);
         const float kth = __shfl(v, K - 1, 64);
-        if (lane == 0) tk[p] = kth;
+        if (lane == 0) tk[q] = kth;
       }
       __syncthreads();
       for (int t = tid; t < QB; t += NT) {
-        float T = -INFINITY;
-        for (int h = 0; h < G; ++h) {
-          const float kh = tk[(size_t)h * QB + t];
-          if (kh != -INFINITY) T = fmaxf(T, (G > 1) ? kh * tau2 - tq[(size_t)h * QB + t] : kh);
-        }
+        const float T = tk[t];
         // pass 1 computes s_h - L_h as one fma of the accumulator, which rounds
         // differently from the product above: lower the bound by a margin far
         // above that rounding so no chunk at the bound is lost
