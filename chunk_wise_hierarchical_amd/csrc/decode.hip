@@ -25,6 +25,13 @@ __device__ __forceinline__ long long dec_pos(int32_t seqlen, int cap, int M, int
   return i < 0 ? 0 : i;
 }
 
+// streaming 16-byte load (non-temporal): the summary cache is read once per
+// step and should not evict the K/V tiles and scores the later kernels reuse
+typedef unsigned int ntu4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt_u4(const void* p) {
+  const ntu4_t w = __builtin_nontemporal_load(reinterpret_cast<const ntu4_t*>(p));
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
 template <typename T> struct Vec;
 template <> struct Vec<bf16_t> {
   static constexpr int N = 8;   // 16 bytes
@@ -76,13 +83,15 @@ k_dec_score(const T* __restrict__ qr, const T* __restrict__ ksum, const float* _
   constexpr int MAXT = 256 / (16 * V) > 0 ? 256 / (16 * V) : 1;
   constexpr int R = 16;
   __shared__ float red_m[4][MT], red_s[4][MT];
-  const long long bh = blockIdx.x;
+  // grid x: 256-row block (fastest, so neighbouring workgroups stream adjacent
+  // rows of one head), grid y: (sequence, head)
+  const long long bh = blockIdx.y;
   const int b = (int)(bh / Hq);
-  const int c0 = blockIdx.y * SC_CPB;
+  const int c0 = blockIdx.x * SC_CPB;
   // queries m0 .. m0 + mc - 1 of the sequence share every summary row read
   const int m0 = blockIdx.z * MT, mc = min(MT, M - m0);
   const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15, lane = tid & 63, wv = tid >> 6;
-  auto lpart = [&](int mm) { return lsep + ((bh * M + m0 + mm) * nsb + blockIdx.y) * 2; };
+  auto lpart = [&](int mm) { return lsep + ((bh * M + m0 + mm) * nsb + blockIdx.x) * 2; };
   // Contiguous cache: the summary rows are read before the sequence length is
   // known (rows are clamped to the batch's longest candidate range, which the
   // cache always holds), so the loads overlap the length lookup; rows past
@@ -122,7 +131,7 @@ k_dec_score(const T* __restrict__ qr, const T* __restrict__ ksum, const float* _
 #pragma unroll
       for (int u = 0; u < R; ++u) {
         const int c = min(r0 + u, cmax);
-        raw[u] = *reinterpret_cast<const uint4*>(ksum + krow(c) + e);
+        raw[u] = ld_nt_u4(ksum + krow(c) + e);
       }
 #pragma unroll
       for (int u = 0; u < R; ++u) {
@@ -527,7 +536,7 @@ void launch_score(const HilsShape& s, const void* qr, const int32_t* seqlen, con
                   hipStream_t st) {
   const unsigned nz = (unsigned)((s.M + MT - 1) / MT);
   { HilsProfScope ps_("k_dec_score", st);
-    hipLaunchKernelGGL((k_dec_score<T, PAGED, MT>), dim3(s.B * s.Hq, nsb, nz), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_dec_score<T, PAGED, MT>), dim3(nsb, s.B * s.Hq, nz), dim3(256), 0, st,
                        (const T*)qr, (const T*)ksum, bsum, seqlen, scores, lsep, s.Hq, s.nC, s.nmax,
                        (int)nsb, s.N, s.d, s.S, s.W, (float)s.tau, s.M, pm); }
 }

@@ -344,6 +344,7 @@ hils_status hils_decode(const hils_cfg* cfg, const void* q, const void* q_route,
   char* w = static_cast<char*>(ws);
   int32_t* sl = sel ? sel : (int32_t*)(w + L.sel);
   const void* qr = q_route ? q_route : q;
+  if ((long long)s.B * s.Hq > HILS_DEC_MAX_ROWS_Y) return HILS_E_UNSUPPORTED;
   return hip_status(hils_launch_decode(s, q, qr, k_cache, v_cache, seqlen, k_sum, b_sum, out, sl,
                                        (float*)(w + L.scores), (uint32_t*)(w + L.keys),
                                        (float*)(w + L.slog), (float*)(w + L.part),
@@ -381,6 +382,7 @@ hils_status hils_decode_multi(const hils_cfg* cfg, int32_t M, const void* q, con
   char* w = static_cast<char*>(ws);
   int32_t* sl = sel ? sel : (int32_t*)(w + L.sel);
   const void* qr = q_route ? q_route : q;
+  if ((long long)s.B * s.Hq > HILS_DEC_MAX_ROWS_Y) return HILS_E_UNSUPPORTED;
   return hip_status(hils_launch_decode(s, q, qr, k_cache, v_cache, seqlen, k_sum, b_sum, out, sl,
                                        (float*)(w + L.scores), (uint32_t*)(w + L.keys),
                                        (float*)(w + L.slog), (float*)(w + L.part),
@@ -472,6 +474,7 @@ hils_status hils_decode_paged(const hils_cfg* cfg, const void* q, const void* q_
   char* w = static_cast<char*>(ws);
   int32_t* sl = sel ? sel : (int32_t*)(w + L.sel);
   const void* qr = q_route ? q_route : q;
+  if ((long long)s.B * s.Hq > HILS_DEC_MAX_ROWS_Y) return HILS_E_UNSUPPORTED;
   return hip_status(hils_launch_decode(s, q, qr, k_pages, v_pages, seqlen, k_sum_pages, b_sum_pages,
                                        out, sl, (float*)(w + L.scores), (uint32_t*)(w + L.keys),
                                        (float*)(w + L.slog), (float*)(w + L.part),

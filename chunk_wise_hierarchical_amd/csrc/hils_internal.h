@@ -78,6 +78,8 @@ hipError_t hils_launch_summarize_paged(const HilsShape& s, const void* k_pages, 
 
 // chunk rows per decode scoring workgroup (one (max, sum exp) partial each)
 constexpr int HILS_DEC_SCORE_ROWS = 256;
+// the decode scoring grid puts (sequence, query head) on grid dimension y
+constexpr long long HILS_DEC_MAX_ROWS_Y = 65535;
 
 // maximum candidates the generic select kernel keeps in LDS
 constexpr int HILS_GENERIC_NMAX = 8192;

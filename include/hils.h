@@ -128,7 +128,9 @@ hils_status hils_prefill(const hils_cfg* cfg, const void* q, const void* q_route
  * cache at position T_b - 1 (T_b = seqlen[b], 1 <= T_b <= N, device int32[B]),
  * and the query q[b,:,0,:] is that token's query.  k_sum/b_sum hold the
  * summaries of every complete chunk (from hils_summarize); only chunks
- * c < |C_{T_b-1}| are read.  out: [B][Hq][1][d]; sel optional [B][Hkv][K]. */
+ * c < |C_{T_b-1}| are read.  out: [B][Hq][1][d]; sel optional [B][Hkv][K].
+ * B * Hq above 65535 returns HILS_E_UNSUPPORTED (also for the multi-query and
+ * paged decode below). */
 hils_status hils_decode(const hils_cfg* cfg, const void* q, const void* q_route,
                         const void* k_cache, const void* v_cache, const int32_t* seqlen,
                         const void* k_sum, const float* b_sum, void* out, int32_t* sel,

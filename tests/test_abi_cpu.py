@@ -151,6 +151,20 @@ def test_multi_decode_arguments_and_workspace(L):
     assert L.hils_decode_multi_workspace_bytes(ctypes.byref(c), 17) == 0
 
 
+def test_decode_rejects_batches_beyond_the_scoring_grid(L):
+    # the decode scoring grid holds (sequence, query head) in its y dimension:
+    # B * Hq = 8192 * 8 is one past its limit of 65535
+    p = ctypes.c_void_p(0x10000)
+    c = _cfg(N=1024, B=8192, Hq=8, Hkv=2)
+    ws = ctypes.c_size_t(L.hils_workspace_bytes(ctypes.byref(c), 1))
+    assert ws.value > 0
+    args = (p, None, p, p, p, p, p, p, None, p, ws, None)
+    assert L.hils_decode(ctypes.byref(c), *args) == _lib.HILS_E_UNSUPPORTED
+    assert L.hils_decode_multi(ctypes.byref(c), 1, *args) == _lib.HILS_E_UNSUPPORTED
+    assert L.hils_decode_paged(ctypes.byref(c), p, None, p, p, 16, p, 16, p, p, p, p, None, p, ws,
+                               None) == _lib.HILS_E_UNSUPPORTED
+
+
 def test_product_path_does_not_touch_the_oracle():
     for dirpath, _, files in os.walk(PKG):
         for f in files:
