@@ -25,6 +25,8 @@
 //      out = alpha_swa o_swa + sum_c alpha_c o_c, in slot order (deterministic;
 //      the order of pairs inside a bucket never changes a result, since MFMA
 //      rows are independent).
+#include <type_traits>
+
 #include "fast_common.h"
 #include "hils_internal.h"
 
@@ -257,9 +259,15 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[rb][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  // running row maximum in raw score units (logit = tau2 * raw, base 2) and
+  // this lane's part of the row's exp sum (the four lanes of a row add up at
+  // the end)
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
 
-  auto window_tile = [&](int c) {
+  // full: the tile lies inside the window of every row of the workgroup, so
+  // no score needs a mask
+  auto window_tile = [&](int c, auto full_tag) {
+    constexpr bool full = decltype(full_tag)::value;
     f32x4_t s[2][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -275,6 +283,7 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       }
     }
     bf16x8_t pb[2][2];
+    float scale[2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       float x[16];
@@ -283,30 +292,30 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int j = c * S + 32 * (kt >> 1) + 8 * lq + 4 * (kt & 1) + e;
-          const bool ok = vcol[rb] && j >= wlo[rb] && j <= iq[rb];
-          const float v2 = ok ? s[rb][kt][e] * tau2 : -INFINITY;
-          x[kt * 4 + e] = v2;
-          mt = fmaxf(mt, v2);
+          float v = s[rb][kt][e];
+          if constexpr (!full) {
+            const int j = c * S + 32 * (kt >> 1) + 8 * lq + 4 * (kt & 1) + e;
+            v = (vcol[rb] && j >= wlo[rb] && j <= iq[rb]) ? v : -INFINITY;
+          }
+          x[kt * 4 + e] = v;
+          mt = fmaxf(mt, v);
         }
       mt = max_x32(max_x16(mt));
       const float mnew = fmaxf(m[rb], mt);
       float p[16];
       float ps = 0.0f;
-      float scale = 1.0f;
+      scale[rb] = 1.0f;
       if (mnew == -INFINITY) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) p[t] = 0.0f;
       } else {
-        scale = fast_exp2(m[rb] - mnew);
+        if (mnew != m[rb]) scale[rb] = fast_exp2((m[rb] - mnew) * tau2);
+        const float mneg = -mnew * tau2;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) { p[t] = fast_exp2(x[t] - mnew); ps += p[t]; }
+        for (int t = 0; t < 16; ++t) { p[t] = fast_exp2(fmaf(x[t], tau2, mneg)); ps += p[t]; }
       }
-      ps = sum_x32(sum_x16(ps));
-      l[rb] = l[rb] * scale + ps;
+      l[rb] = l[rb] * scale[rb] + ps;
       m[rb] = mnew;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[rb][dt] *= scale;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const float* pp = p + 8 * kb;
@@ -314,6 +323,13 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                    pack_bf16x2(pp[4], pp[5]), pack_bf16x2(pp[6], pp[7]));
         pb[rb][kb] = __builtin_bit_cast(bf16x8_t, u);
       }
+    }
+    // rescale the outputs only when some row's maximum moved
+    if (__ballot(scale[0] != 1.0f || scale[1] != 1.0f)) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[rb][dt] *= scale[rb];
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
@@ -328,14 +344,19 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const int cw_lo = (int)(window_start(ib0, W, S) / S);
   const int cw_hi = (ib0 + qcount - 1) / S;
   const int nw = cw_hi - cw_lo + 1;
+  // tiles [full_lo, full_hi] lie inside every row's window [window_start(i), i]
+  const long long full_lo = (window_start(ib0 + qcount - 1, W, S) + S - 1) / S;
+  const long long full_hi = (ib0 + 1) / S - 1;
   // one register buffer: tile idx + 1 is loaded while tile idx is scored
   uint4 ra[8];
   load_chunk(ra, cw_lo);
   store_chunk(ra);
   __syncthreads();
   for (int idx = 0; idx < nw; ++idx) {
+    const int c = cw_lo + idx;
     load_chunk(ra, cw_lo + min(idx + 1, nw - 1));
-    window_tile(cw_lo + idx);
+    if (qcount == QA && c >= full_lo && c <= full_hi) window_tile(c, std::true_type{});
+    else window_tile(c, std::false_type{});
     __syncthreads();
     store_chunk(ra);             // past the last tile: rewrites the last tile, unused
     __syncthreads();
@@ -344,9 +365,10 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // normalised window output and its log-mass (base 2)
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
+    const float lr = sum_x32(sum_x16(l[rb]));      // the row's four lanes
     if (vcol[rb]) {
       const long long row = (long long)bg * qs + (iq[rb] - i0);
-      const float il = 1.0f / l[rb];
+      const float il = 1.0f / lr;
       float* sp = swa + (row * G + h) * D;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
@@ -354,7 +376,7 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                      acc[rb][dt][3] * il);
         *reinterpret_cast<float4*>(sp + 16 * dt + 4 * lq) = o;
       }
-      if (lq == 0) lz[row * G + h] = m[rb] + log2f(l[rb]);
+      if (lq == 0) lz[row * G + h] = m[rb] * tau2 + log2f(lr);
     }
   }
 }
