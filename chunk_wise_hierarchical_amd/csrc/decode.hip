@@ -13,7 +13,9 @@
 //                      S-token window tile, partial (max, sum, unnormalised o);
 //   4. k_dec_combine — window partials merged in the log domain, then the
 //                      chunk-level softmax over {s_hat_c} U {log Z_swa}.
-#include "hils_device.h"
+#include <type_traits>
+
+#include "fast_common.h"
 #include "hils_internal.h"
 
 namespace {
@@ -477,6 +479,160 @@ k_dec_attn(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
   }
 }
 
+// Specialised split attention for bf16, d = 128, S = 64, G <= 4 (same
+// partials as k_dec_attn).  Every K and V load of the split is issued at the
+// start, straight into registers:
+//   logits: wave w takes elements [32w, 32w + 32) of key row j = lane and
+//           forms its partial dot with each head's query (broadcast LDS
+//           reads); the four partials meet in LDS and wave h takes head h's
+//           softmax over the keys;
+//   output: wave w takes keys [16w, 16w + 16), lane = (8-element slice e8 =
+//           lane % 16, 4 keys 16w + 4 (lane / 16) + u); the four key groups of
+//           a wave are summed with row swaps, the four waves in LDS.
+// Rows past the split's last token are read at that token (their weight is
+// 0), so every load stays inside the split's written rows.
+constexpr int DA_D = 128, DA_S = 64;
+
+template <bool PAGED, int G>
+__global__ void __launch_bounds__(AT_NT)
+k_dec_attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                const bf16_t* __restrict__ v, const int32_t* __restrict__ seqlen,
+                const int32_t* __restrict__ sel, float* __restrict__ part, int Hq, int Hkv, int N,
+                int W, int K, int NS, float tau, int M, PageMap pm) {
+  constexpr int D = DA_D, S = DA_S;
+  __shared__ __align__(16) float qs[G][D];
+  __shared__ __align__(16) float dp[4][G][S];     // partial dots by element quarter
+  __shared__ __align__(16) float ps[G][S];        // softmax weights
+  __shared__ __align__(16) float red[4][G][D];    // output partials by key quarter
+  __shared__ float hm[G], hl[G];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int bgm = blockIdx.x, s = blockIdx.y;
+  const int m = bgm % M, bg = bgm / M;
+  const int b = bg / Hkv, g = bg % Hkv;
+  auto hrow = [&](int r) { return ((long long)b * Hq + (long long)g * G + r) * M + m; };
+  for (int t = tid; t < G * D; t += AT_NT) {
+    const int r = t / D;
+    qs[r][t - r * D] = bf16_to_f32(q[hrow(r) * D + (t - r * D)]);
+  }
+  const int csel = (s < K) ? sel[(long long)bgm * K + s] : -1;
+  const long long i = dec_pos(seqlen[b], N, M, m);
+  long long j0 = 0;
+  int jn = 0;
+  if (s < K) {
+    if (csel >= 0) { j0 = (long long)csel * S; jn = S; }
+  } else {
+    j0 = window_start(i, W, S) + (long long)(s - K) * S;
+    if (j0 <= i) jn = (int)min((long long)S, i - j0 + 1);
+  }
+  if (jn == 0) {
+    for (int t = tid; t < G * (D + 2); t += AT_NT) {
+      const int r = t / (D + 2), e = t - r * (D + 2);
+      part[(hrow(r) * NS + s) * (long long)(D + 2) + e] = (e == 0) ? -INFINITY : 0.0f;
+    }
+    return;
+  }
+  const long long kvoff = PAGED ? (pm.page(b, j0 / S) * Hkv + g) * (long long)S * D
+                                : ((b * (long long)Hkv + g) * N + j0) * D;
+  const bf16_t* kg = k + kvoff;
+  const bf16_t* vg = v + kvoff;
+  // logit loads: key row min(lane, jn - 1), elements [32 wv, 32 wv + 32)
+  uint4 kx[4];
+  {
+    const bf16_t* kr = kg + (long long)min(lane, jn - 1) * D + 32 * wv;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kx[u] = *reinterpret_cast<const uint4*>(kr + 8 * u);
+  }
+  // output loads: keys 16 wv + 4 kq + u, elements [8 e8, 8 e8 + 8)
+  const int e8 = lane & 15, kq = lane >> 4;
+  const int jb = 16 * wv + 4 * kq;
+  uint4 vx[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    vx[u] = *reinterpret_cast<const uint4*>(vg + (long long)min(jb + u, jn - 1) * D + 8 * e8);
+  __syncthreads();                                // qs
+  {
+    float kf[32];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t w4[4] = {kx[u].x, kx[u].y, kx[u].z, kx[u].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        kf[8 * u + 2 * t] = __uint_as_float(w4[t] << 16);
+        kf[8 * u + 2 * t + 1] = __uint_as_float(w4[t] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      const float* qq = &qs[r][32 * wv];
+      float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 32; e += 8) {
+        const float4 qa = *reinterpret_cast<const float4*>(qq + e);
+        const float4 qb = *reinterpret_cast<const float4*>(qq + e + 4);
+        a0 = fmaf(qa.x, kf[e], a0);
+        a1 = fmaf(qa.y, kf[e + 1], a1);
+        a0 = fmaf(qa.z, kf[e + 2], a0);
+        a1 = fmaf(qa.w, kf[e + 3], a1);
+        a0 = fmaf(qb.x, kf[e + 4], a0);
+        a1 = fmaf(qb.y, kf[e + 5], a1);
+        a0 = fmaf(qb.z, kf[e + 6], a0);
+        a1 = fmaf(qb.w, kf[e + 7], a1);
+      }
+      dp[wv][r][lane] = a0 + a1;
+    }
+  }
+  __syncthreads();                                // dp
+  if (wv < G) {
+    const int r = wv;
+    const float dot = (dp[0][r][lane] + dp[1][r][lane]) + (dp[2][r][lane] + dp[3][r][lane]);
+    const float x = (lane < jn) ? tau * dot : -INFINITY;
+    const float mx = wave_max_f(x);
+    const float p = (lane < jn) ? __expf(x - mx) : 0.0f;
+    const float l = wave_sum_f(p);
+    ps[r][lane] = p;
+    if (lane == 0) { hm[r] = mx; hl[r] = l; }
+  }
+  __syncthreads();                                // ps, hm, hl
+  {
+    float vf[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t w4[4] = {vx[u].x, vx[u].y, vx[u].z, vx[u].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        vf[u][2 * t] = __uint_as_float(w4[t] << 16);
+        vf[u][2 * t + 1] = __uint_as_float(w4[t] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < G; ++r) {
+      const float4 p4 = *reinterpret_cast<const float4*>(&ps[r][jb]);
+      const float pu[4] = {p4.x, p4.y, p4.z, p4.w};
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float a = pu[0] * vf[0][e];
+        a = fmaf(pu[1], vf[1][e], a);
+        a = fmaf(pu[2], vf[2][e], a);
+        a = fmaf(pu[3], vf[3][e], a);
+        // the wave's four key groups (lanes l, l ^ 16, l ^ 32, l ^ 48)
+        o[e] = fastp::sum_x32(fastp::sum_x16(a));
+      }
+      if (kq == 0) {
+        *reinterpret_cast<float4*>(&red[wv][r][8 * e8]) = make_float4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<float4*>(&red[wv][r][8 * e8 + 4]) = make_float4(o[4], o[5], o[6], o[7]);
+      }
+    }
+  }
+  __syncthreads();                                // red
+  for (int t = tid; t < G * D; t += AT_NT) {
+    const int r = t / D, e = t - r * D;
+    float* pp = part + (hrow(r) * NS + s) * (long long)(D + 2);
+    pp[2 + e] = (red[0][r][e] + red[1][r][e]) + (red[2][r][e] + red[3][r][e]);
+    if (e == 0) { pp[0] = hm[r]; pp[1] = hl[r]; }
+  }
+}
+
 // Per (sequence, query head): merge the window tiles in the log domain, take
 // the chunk-level softmax over {s_hat_c} U {log Z_swa}, and form the output as
 // one weighted sum of the split partials.  Wave 0 computes the split weights.
@@ -563,10 +719,28 @@ void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const vo
   { HilsProfScope ps_("k_dec_select", st); hipLaunchKernelGGL(k_dec_select, dim3(s.B * s.Hkv * s.M), dim3(SEL_NT), sshm, st, scores, lsep, seqlen,
                      keys, sel, slog, s.Hq, s.Hkv, s.G, s.nmax > 0 ? s.nmax : 1, (int)nsb, s.N, s.S,
                      s.W, s.K, s.M); }
-  hipFuncSetAttribute((const void*)k_dec_attn<T, PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
-  { HilsProfScope ps_("k_dec_attn", st); hipLaunchKernelGGL((k_dec_attn<T, PAGED>), dim3(s.B * s.Hkv * s.M, NS), dim3(AT_NT), ashm, st,
-                     (const T*)q, (const T*)k, (const T*)v, seqlen, sel, part,
-                     s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, NS, tau, s.M, pm); }
+  const dim3 agrid(s.B * s.Hkv * s.M, NS);
+  if (std::is_same<T, bf16_t>::value && s.d == DA_D && s.S == DA_S && (s.G == 1 || s.G == 2 || s.G == 4)) {
+    const bf16_t* qb = (const bf16_t*)q;
+    const bf16_t* kb = (const bf16_t*)k;
+    const bf16_t* vb = (const bf16_t*)v;
+    HilsProfScope ps_("k_dec_attn", st);
+    if (s.G == 1)
+      hipLaunchKernelGGL((k_dec_attn_bf16<PAGED, 1>), agrid, dim3(AT_NT), 0, st, qb, kb, vb, seqlen, sel,
+                         part, s.Hq, s.Hkv, s.N, s.W, s.K, NS, tau, s.M, pm);
+    else if (s.G == 2)
+      hipLaunchKernelGGL((k_dec_attn_bf16<PAGED, 2>), agrid, dim3(AT_NT), 0, st, qb, kb, vb, seqlen, sel,
+                         part, s.Hq, s.Hkv, s.N, s.W, s.K, NS, tau, s.M, pm);
+    else
+      hipLaunchKernelGGL((k_dec_attn_bf16<PAGED, 4>), agrid, dim3(AT_NT), 0, st, qb, kb, vb, seqlen, sel,
+                         part, s.Hq, s.Hkv, s.N, s.W, s.K, NS, tau, s.M, pm);
+  } else {
+    hipFuncSetAttribute((const void*)k_dec_attn<T, PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
+    HilsProfScope ps_("k_dec_attn", st);
+    hipLaunchKernelGGL((k_dec_attn<T, PAGED>), agrid, dim3(AT_NT), ashm, st,
+                       (const T*)q, (const T*)k, (const T*)v, seqlen, sel, part,
+                       s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, NS, tau, s.M, pm);
+  }
   { HilsProfScope ps_("k_dec_combine", st); hipLaunchKernelGGL(k_dec_combine<T>, dim3(s.B * s.Hq * s.M), dim3(256), cshm, st, part, slog,
                      seqlen, (T*)out, s.Hq, s.G, s.N, s.d, s.S, s.W, s.K, NS, s.nwin, s.M); }
 }

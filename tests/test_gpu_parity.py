@@ -330,6 +330,8 @@ def test_decode_mha_and_wide_groups():
     # G = 1 ranks raw scores; G = 8 is the widest group the kernels take
     w = synth.get_workload("decode_512k", N=8192, B=2, Hq=8, Hkv=8, K=16, W=512)
     _decode_case(w, [8192, 4097], label="G=1")
+    w = synth.get_workload("decode_512k", N=8192, B=2, Hq=4, Hkv=2, K=16, W=512)
+    _decode_case(w, [8192, 5000], label="G=2")
     w = synth.get_workload("decode_512k", N=8192, B=2, Hq=16, Hkv=2, K=16, W=512)
     _decode_case(w, [8192, 6001], label="G=8")
     # chunk size that is not a multiple of 4, window not a multiple of the chunk
