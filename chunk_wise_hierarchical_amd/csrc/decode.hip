@@ -193,22 +193,6 @@ k_dec_score(const T* __restrict__ qr, const T* __restrict__ ksum, const float* _
 constexpr int SEL_NT = 1024;
 constexpr int SEL_NW = SEL_NT / 64;
 
-__device__ __forceinline__ int sel_excl_scan(int flag, int* wsum, int& pos) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const unsigned long long bal = __ballot(flag);
-  const int inwave = __popcll(bal & ((1ull << lane) - 1ull));
-  if (lane == 0) wsum[w] = __popcll(bal);
-  __syncthreads();
-  int before = 0, total = 0;
-  for (int u = 0; u < SEL_NW; ++u) {
-    if (u < w) before += wsum[u];
-    total += wsum[u];
-  }
-  pos = before + inwave;
-  __syncthreads();
-  return total;
-}
-
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
   const float M = fmaxf(m, m2);
   if (M == -INFINITY) { m = M; s = 0.0f; return; }
@@ -301,12 +285,14 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
       uint32_t h4[4], s4 = 0;
 #pragma unroll
       for (int u = 3; u >= 0; --u) { s4 += hist[tid * 4 + u]; h4[u] = s4; }
-      // totals of all higher lanes (uniform loop: every lane takes part in every shuffle)
-      uint32_t above = 0;
-      for (int l2 = 0; l2 < 64; ++l2) {
-        const uint32_t y = __shfl(s4, l2, 64);
-        if (l2 > tid) above += y;
+      // totals of all higher lanes: inclusive suffix scan over the wave
+      uint32_t suf = s4;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_down(suf, o, 64);
+        if (tid + o < 64) suf += y;
       }
+      const uint32_t above = suf - s4;
       const int need = sh_need;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -327,22 +313,61 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
   const uint32_t thr = prefix;
   const int need_eq = sh_need;   // how many keys equal to thr to take (lowest chunk ids)
 
-  int running = 0, eq_seen = 0;
-  for (int base = 0; base < n; base += SEL_NT) {
-    const int c = base + tid;
-    const uint32_t key = (c < n) ? ky[c] : 0u;
-    const int eq = (c < n) && (key == thr);
-    int eqpos;
-    const int eqtot = sel_excl_scan(eq, wsum, eqpos);
-    const int f = (c < n) && (key > thr || (eq && eq_seen + eqpos < need_eq));
-    int pos;
-    const int tot = sel_excl_scan(f, wsum, pos);
-    if (f) {
-      so[running + pos] = c;
-      for (int r = 0; r < G; ++r) slog[hrow(r) * K + running + pos] = scores[hrow(r) * nmax + c];
+  // compaction in ascending chunk order: thread t owns chunks [8t, 8t + 8) of
+  // each round of 8 * SEL_NT; one block scan of its (greater, equal) counts
+  // gives where its selected chunks go.  Keys equal to thr are taken lowest
+  // chunk id first, need_eq of them.
+  constexpr int CPT = 8;
+  int taken_all = 0, eq_all = 0;
+  for (int base = 0; base < n; base += CPT * SEL_NT) {
+    const int c0 = base + CPT * tid;
+    uint32_t kv[CPT];
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      kv[u] = (c0 + u < n) ? ky[c0 + u] : 0u;
+      const bool in = c0 + u < n;
+      ngt += (in && kv[u] > thr) ? 1 : 0;
+      neq += (in && kv[u] == thr) ? 1 : 0;
     }
-    running += tot;
-    eq_seen += eqtot;
+    // inclusive scan of the packed counts (greater in the low 16 bits)
+    const uint32_t mine = (uint32_t)ngt | ((uint32_t)neq << 16);
+    uint32_t inc = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) wsum[wv] = (int)inc;
+    __syncthreads();
+    uint32_t before = inc - mine, total = 0;
+    for (int u = 0; u < SEL_NW; ++u) {
+      const uint32_t t = (uint32_t)wsum[u];
+      if (u < wv) before += t;
+      total += t;
+    }
+    __syncthreads();                       // wsum is rewritten next round
+    const int gt_before = (int)(before & 0xffffu), eq_before = eq_all + (int)(before >> 16);
+    // taken before this thread: earlier rounds, then this round's greater keys
+    // and equal keys before it
+    int pos = taken_all + gt_before + min(eq_before, need_eq) - min(eq_all, need_eq);
+    int eqi = eq_before;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c = c0 + u;
+      if (c < n) {
+        bool take = kv[u] > thr;
+        if (kv[u] == thr) take = eqi++ < need_eq;
+        if (take) {
+          so[pos] = c;
+          for (int r = 0; r < G; ++r) slog[hrow(r) * K + pos] = scores[hrow(r) * nmax + c];
+          ++pos;
+        }
+      }
+    }
+    const int gt_tot = (int)(total & 0xffffu), eq_tot = (int)(total >> 16);
+    taken_all += gt_tot + min(eq_all + eq_tot, need_eq) - min(eq_all, need_eq);
+    eq_all += eq_tot;
   }
 }
 
