@@ -83,7 +83,7 @@ KERNEL_SOURCES = {
     "k_pair_attn": ["fast_pairs.hip", "fast_common.h", "hils_device.h", "hils_internal.h"],
     "k_pair_reduce": ["fast_pairs.hip", "fast_common.h", "hils_device.h", "hils_internal.h"],
     "k_win_fast": ["fast_pairs.hip", "fast_common.h", "hils_device.h", "hils_internal.h"],
-    "k_dec_score": ["decode.hip", "hils_device.h", "hils_internal.h"],
+    "k_dec_score": ["decode.hip", "fast_common.h", "hils_device.h", "hils_internal.h"],
 }
 
 

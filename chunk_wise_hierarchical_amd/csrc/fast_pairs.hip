@@ -34,13 +34,12 @@ using namespace fastp;
 
 namespace {
 
-// Streaming (non-temporal) access for the per-pair outputs, which are written
-// once and read once: they should not displace cached query rows and K/V.
+// Streaming (non-temporal) access to the per-pair outputs, which are written
+// once and read once.  The bf16 partial rows are stored normally (whole
+// lines, which L2 combines before writing back), the scattered 4-byte
+// fusion logits and the reduction's reads non-temporally, so that neither
+// displaces cached query rows and K/V.
 typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void st_u4_nt(void* p, uint4 v) {
-  nt_u32x4 w = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(w, reinterpret_cast<nt_u32x4*>(p));
-}
 __device__ __forceinline__ uint4 ld_u4_nt(const void* p) {
   nt_u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
   return make_uint4(w.x, w.y, w.z, w.w);
@@ -564,7 +563,7 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
                                     pack_bf16x2(acc[2 * j][2], acc[2 * j][3]),
                                     pack_bf16x2(acc[2 * j + 1][0], acc[2 * j + 1][1]),
                                     pack_bf16x2(acc[2 * j + 1][2], acc[2 * j + 1][3]));
-        st_u4_nt(op + 8 * (4 * j + lq), uu);
+        st_u4(op + 8 * (4 * j + lq), uu);
       }
       if (lq == 0) __builtin_nontemporal_store(lam, lamb + prow * G + h);
     }
