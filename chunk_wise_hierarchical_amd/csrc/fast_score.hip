@@ -36,7 +36,6 @@ using namespace fastp;
 
 namespace {
 
-constexpr int NT = 256;
 constexpr int CT = 32;         // chunks per tile
 constexpr int TRK = 128;       // pass-0 tracked scores per (query, head): 32 slots x ranks 0-2 (rank 3 unused)
 constexpr int XROW = CT;       // row of the cross-head exchange buffer (floats); its 16-byte
@@ -45,17 +44,25 @@ constexpr int XROW = CT;       // row of the cross-head exchange buffer (floats)
 // parts: 32-bit data format, so num_records counts bytes
 constexpr int BUF_RSRC_WORD3 = 0x00020000;
 
+// Workgroup geometry.  Every wavefront scores 32 queries of one head; a
+// workgroup of NW wavefronts covers QB = 32 NW / G queries with all G heads.
+// The k' tile each step loads and stores to LDS serves the whole workgroup,
+// so G = 4 takes 8 wavefronts (64 queries, one workgroup per CU) to halve that
+// traffic per query; G = 1 and 2 keep 4 (their lists would not fit otherwise).
 template <int G>
 struct Geo {
-  static constexpr int QB = 32 * 4 / G;   // queries per workgroup
-  static constexpr int QW = QB / 4;       // queries per wavefront in the selection layout
+  static constexpr int NW = (G == 4) ? 8 : 4;
+  static constexpr int NT = 64 * NW;      // threads
+  static constexpr int QB = 32 * NW / G;  // queries per workgroup
+  static constexpr int QW = QB / NW;      // queries per wavefront in the selection layout
   static constexpr int LQ = 64 / QW;      // lanes per query
   static constexpr int CL = CT / LQ;      // chunks per lane per tile (selection layout)
   // staging slots per query.  One selection step adds at most LQ * CL = 32
   // keys to a query, which merges its staged keys first when they would not
-  // fit.  G = 4 keeps 56 so that two workgroups fit one CU's LDS.
-  static constexpr int STG = (G == 1) ? 64 : 56;
-  static_assert(LQ * CL <= STG, "one step must fit an empty staging area");
+  // fit; a merge takes at most 64.  G = 2 keeps 56 to fit one CU's LDS.
+  static constexpr int STG = (G == 2) ? 56 : 64;
+  static_assert(LQ * CL <= STG && STG <= 64, "staging area");
+  static_assert(QW % 8 == 0, "merge rounds take 8 queries");
 };
 
 // [0, 64 KB) is also the scratch of the tracked scores between the passes
@@ -63,7 +70,7 @@ struct Geo {
 // possibly stg, which are idle then.  tq and everything after it start past it.
 template <int G>
 struct Lds {
-  size_t ktile, btile, xb, lst, stg, tq, thf, tk, cnt, thr, total;
+  size_t ktile, btile, xb, lst, stg, tq, thf, tk, cnt, total;
   __host__ __device__ Lds(int K) {
     size_t o = 0;
     ktile = o; o += (size_t)G * CT * D * 2;            // swizzled, no padding
@@ -84,9 +91,7 @@ struct Lds {
     } else {
       tk = o;  o += (size_t)G * Geo<G>::QB * 4;
     }
-    cnt = o;   o += (size_t)Geo<G>::QB * 2 * 4;
-    o = (o + 15) & ~(size_t)15;
-    thr = o;   o += (size_t)Geo<G>::QB * 8;
+    cnt = o;   o += (size_t)Geo<G>::QB * 4;
     total = o;
   }
 };
@@ -102,38 +107,62 @@ __device__ __forceinline__ void* uniform_ptr(const void* p) {
   return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
 }
 
-// number of set bits of m below this lane
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+// The 64 keys of one query held by its 8 lanes (lg = lane & 7) x 8
+// registers: the key of rank 8 lg + r sits in register r.  In the bitonic
+// networks below, strides 8, 16 and 32 pair lane lg with lane lg ^ 1, 2, 4 of
+// the group (DPP); strides 1, 2 and 4 pair registers of one lane.
+__device__ __forceinline__ uint64_t mirror8_u64(uint64_t v) {     // lane lg ^ 7 of the group
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, 0x141, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), 0x141, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
 }
 
-// wavefront-wide bitonic sort of 64 keys (1 per lane), descending
-__device__ __forceinline__ uint64_t sort64_desc(uint64_t v, int lane) {
+// one stage (block size k, stride j) of the descending bitonic network
+template <int k, int j>
+__device__ __forceinline__ void bitonic_stage8(uint64_t (&v)[8], int lg) {
+  if constexpr (j >= 8) {
+    constexpr int ls = j / 8;
+    const bool lower = (lg & ls) == 0;
+    const bool desc = (k >= 64) || ((8 * lg) & k) == 0;
+    const bool keepmax = lower == desc;
 #pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
+    for (int r = 0; r < 8; ++r) {
+      const uint64_t p = xshfl_u64(v[r], ls);
+      v[r] = keepmax ? umax64(v[r], p) : umin64(v[r], p);
+    }
+  } else {
 #pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint64_t p = xshfl_u64(v, stride);
-      const bool lower = (lane & stride) == 0;
-      const bool desc = (lane & size) == 0 || size == 64;
-      v = (lower == desc) ? umax64(v, p) : umin64(v, p);
+    for (int r = 0; r < 8; ++r) {
+      if ((r & j) == 0) {
+        const bool desc = (k >= 64) || ((8 * lg + r) & k) == 0;
+        const uint64_t hi = umax64(v[r], v[r | j]), lo = umin64(v[r], v[r | j]);
+        v[r] = desc ? hi : lo;
+        v[r | j] = desc ? lo : hi;
+      }
     }
   }
-  return v;
 }
 
-// a, b descending across the wavefront -> the 64 largest of a U b, descending
-__device__ __forceinline__ uint64_t merge_top64(uint64_t a, uint64_t b, int lane) {
-  const uint32_t lo = lane_reverse((uint32_t)b);
-  const uint32_t hi = lane_reverse((uint32_t)(b >> 32));
-  const uint64_t br = ((uint64_t)hi << 32) | lo;          // b reversed: ascending
-  uint64_t v = umax64(a, br);                              // top half of the bitonic sequence
+template <int k, int j>
+__device__ __forceinline__ void bitonic_block8(uint64_t (&v)[8], int lg) {
+  bitonic_stage8<k, j>(v, lg);
+  if constexpr (j > 1) bitonic_block8<k, j / 2>(v, lg);
+}
+
+template <int k>
+__device__ __forceinline__ void bitonic_sort8(uint64_t (&v)[8], int lg) {
+  if constexpr (k > 2) bitonic_sort8<k / 2>(v, lg);
+  bitonic_block8<k, k / 2>(v, lg);
+}
+
+// sort the 64 keys of each 8-lane group descending
+__device__ __forceinline__ void sort8x8_desc(uint64_t (&v)[8], int lg) { bitonic_sort8<64>(v, lg); }
+
+// a, b descending -> a = the 64 largest of a U b, descending
+__device__ __forceinline__ void merge8x8_top(uint64_t (&a)[8], const uint64_t (&b)[8], int lg) {
 #pragma unroll
-  for (int stride = 32; stride > 0; stride >>= 1) {
-    const uint64_t p = xshfl_u64(v, stride);
-    v = ((lane & stride) == 0) ? umax64(v, p) : umin64(v, p);
-  }
-  return v;
+  for (int r = 0; r < 8; ++r) a[r] = umax64(a[r], mirror8_u64(b[7 - r]));   // b reversed
+  bitonic_block8<64, 32>(a, lg);
 }
 
 // wavefront-wide bitonic sort of 64 floats (1 per lane), descending
@@ -162,29 +191,14 @@ __device__ __forceinline__ float merge_top64_f(float a, float b, int lane) {
   return v;
 }
 
-// wavefront-wide bitonic sort of 64 ints (1 per lane), ascending
-__device__ __forceinline__ int sort64_asc(int v, int lane) {
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int p = (int)xshfl((uint32_t)v, stride);
-      const bool lower = (lane & stride) == 0;
-      const bool asc = (lane & size) == 0;
-      v = (lower == asc) ? min(v, p) : max(v, p);
-    }
-  }
-  return v;
-}
-
 template <int G>
-__global__ void __launch_bounds__(NT, 2)
+__global__ void __launch_bounds__(Geo<G>::NT, 2)
 k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
              const float* __restrict__ bsum, int32_t* __restrict__ sel, int Hq, int Hkv, int N,
              int W, int K, int nC, float tau2, float bscale, int nqb) {
   using GE = Geo<G>;
   constexpr int QB = GE::QB, QW = GE::QW, LQ = GE::LQ, CL = GE::CL;
-  constexpr int STG = GE::STG;
+  constexpr int STG = GE::STG, NT = GE::NT, NW = GE::NW;
   extern __shared__ __align__(16) unsigned char sm[];
   const Lds<G> L(K);
   bf16_t* ktile = reinterpret_cast<bf16_t*>(sm + L.ktile);   // [G][CT][16 parts], part ^= c & 15
@@ -196,8 +210,7 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   uint64_t* lst = reinterpret_cast<uint64_t*>(sm + L.lst);   // [QB][K]
   uint2* stg = reinterpret_cast<uint2*>(sm + L.stg);         // [QB][STG] (score bits, chunk id)
   uint32_t* cnt_lst = reinterpret_cast<uint32_t*>(sm + L.cnt);
-  uint64_t* thr = reinterpret_cast<uint64_t*>(sm + L.thr);
-  float* thf = reinterpret_cast<float*>(sm + L.thf);        // [QB] thr as a float (prefilter)
+  float* thf = reinterpret_cast<float*>(sm + L.thf);        // [QB] staging bound (K-th key's score)
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int blk = blockIdx.x;
@@ -216,7 +229,6 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     for (int t = tid; t < (i_last - i0 + 1) * K; t += NT) selg[(long long)i0 * K + t] = -1;
     return;
   }
-  for (int t = tid; t < QB; t += NT) cnt_lst[t] = 0;
 
   // MFMA layout: wavefront -> (head hw, 32-query column block qw); lane -> query column
   const int hw = w % G, qw = w / G;
@@ -230,33 +242,32 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     else bq[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
   }
 
-  // selection layout: lane -> (query qsel, CL chunks of the tile); gmask is
-  // the lane group of qsel and nstg that query's staged-key count
+  // selection layout: lane -> (query qsel, CL chunks of the tile); nstg is
+  // that query's staged-key count, held by every lane of its group
   const int qsel = (G == 1) ? (32 * w + col) : (w * QW + lane / LQ);
   const int cbase = (G == 1) ? 0 : CL * (lane % LQ);
-  const uint64_t gmask = (G == 1) ? ((1ull << col) | (1ull << (col + 32)))
-                                  : (((1ull << LQ) - 1) << (LQ * (lane / LQ)));
   int nstg = 0;
 
   // tile staging through registers into a single XOR-swizzled LDS tile.  The
   // loads are unconditional and kept raw until the store, so they stay in
   // flight while earlier tiles are scored.
-  constexpr int PPT = 2 * G;               // 16-byte pieces per thread per tile
-  // piece p of this thread: head p/2, chunk c0 (+16 for odd p) of the tile,
+  constexpr int PPT = G * CT * 16 / NT;    // 16-byte pieces per thread per tile
+  static_assert(PPT * NT == G * CT * 16, "pieces split evenly over the threads");
+  // piece tid + NT p of the tile: row (tid + NT p) / 16 = head * CT + chunk,
   // 16-byte part tid % 16.  The loads go through buffer descriptors whose base
   // is the tile's first row and whose range ends at the group's last k' row:
   // the per-thread offsets never change, and rows past the range read zero
   // (past chunk nC - 1 a row reads another head's chunk or zero; those scores
   // are masked by the candidate range).
-  static_assert(NT == 256 && CT == 32, "piece layout assumes 256 threads and 32-chunk tiles");
-  const int c0 = tid >> 4;
   const char* kgrp = reinterpret_cast<const char*>(ksum + hb * nC * (long long)D);
   const char* bgrp = reinterpret_cast<const char*>(bsum + hb * nC);
   uint32_t voff[PPT];
 #pragma unroll
-  for (int p = 0; p < PPT; ++p)
-    voff[p] = ((uint32_t)(p >> 1) * (uint32_t)nC + (uint32_t)(c0 + 16 * (p & 1))) * (uint32_t)(D * 2) +
+  for (int p = 0; p < PPT; ++p) {
+    const int row = (tid + NT * p) / 16;
+    voff[p] = ((uint32_t)(row / CT) * (uint32_t)nC + (uint32_t)(row % CT)) * (uint32_t)(D * 2) +
               (uint32_t)(tid & 15) * 16u;
+  }
   const uint32_t boff = ((uint32_t)((tid / CT) % G) * (uint32_t)nC + (uint32_t)(tid % CT)) * 4u;
   const int grows = G * nC;                // k' rows of the group
   // two register buffers: the loads of tile t + 2 are issued while tile t is
@@ -286,32 +297,47 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     if (tid < G * CT) btile[tid] = bpre * bscale;
   };
 
-  // merge query q's ns staged keys into its sorted top-K list (whole wavefront)
-  auto merge = [&](int q, int ns) {
-    const int nl = (int)cnt_lst[q];
-    const uint64_t a = (lane < nl) ? lst[(size_t)q * K + lane] : 0ull;
-    uint64_t sb = 0ull;
-    if (lane < ns) {
-      const uint2 e = stg[(size_t)q * STG + lane];
-      sb = ((uint64_t)f32_order_key(__uint_as_float(e.x)) << 32) | (uint64_t)(0xffffffffu - e.y);
-    }
-    sb = sort64_desc(sb, lane);
-    const uint64_t v = merge_top64(a, sb, lane);
-    const int tot = min(K, nl + ns);
-    const uint32_t klo = __builtin_amdgcn_readlane((uint32_t)v, K - 1);
-    const uint32_t khi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), K - 1);
-    if (lane < K) lst[(size_t)q * K + lane] = (lane < tot) ? v : 0ull;
-    if (lane == 0) {
-      cnt_lst[q] = tot;
-      if (tot >= K) {
-        const uint64_t nt = umax64(thr[q], ((uint64_t)khi << 32) | klo);
-        thr[q] = nt;
-        thf[q] = order_key_f32((uint32_t)(nt >> 32));
+  // merge the staged keys of every query of this wavefront into its sorted
+  // top-K list: each query in one 8-lane group (QW / 8 rounds), keys of rank
+  // 8 lg + r in register r.  Staged counts pass through cnt_lst (the staging
+  // lane groups need not be the merge groups).  An empty list slot holds 0,
+  // which is below every key.
+  auto merge_wave = [&](int ns_mine, bool leader) __attribute__((always_inline)) {
+    if (leader) cnt_lst[qsel] = (uint32_t)ns_mine;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const int lg = lane & 7;
+#pragma unroll 1
+    for (int rd = 0; rd < QW / 8; ++rd) {
+      const int q = w * QW + 8 * rd + (lane >> 3);
+      const int ns = (int)cnt_lst[q];
+      uint64_t a[8], b[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int i = 8 * lg + r;
+        a[r] = (i < K) ? lst[(size_t)q * K + i] : 0ull;
+        b[r] = 0ull;
+        if (i < ns) {
+          const uint2 e = stg[(size_t)q * STG + i];
+          b[r] = ((uint64_t)f32_order_key(__uint_as_float(e.x)) << 32) | (uint64_t)(0xffffffffu - e.y);
+        }
       }
+      sort8x8_desc(b, lg);
+      merge8x8_top(a, b, lg);
+      uint64_t kth = 0ull;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int i = 8 * lg + r;
+        if (i < K) lst[(size_t)q * K + i] = a[r];
+        kth = (r == ((K - 1) & 7)) ? a[r] : kth;
+      }
+      // key of rank K - 1 (0 while the list holds fewer than K keys)
+      const int src = (lane & ~7) | ((K - 1) >> 3);
+      const uint32_t khi = (uint32_t)__shfl((int)(uint32_t)(kth >> 32), src, 64);
+      const uint32_t klo = (uint32_t)__shfl((int)(uint32_t)kth, src, 64);
+      if (lg == 0 && (khi | klo) != 0u) thf[q] = fmaxf(thf[q], order_key_f32(khi));
     }
-    // other lanes of this wavefront read the list, the counts and the
-    // threshold next: acquire-release keeps the compiler from answering those
-    // reads with values it holds from before lane 0's writes
+    // the lanes read the lists and bounds next: acquire-release keeps the
+    // compiler from answering those reads with values from before the writes
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   };
 
@@ -458,13 +484,9 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
         }
         // merge the queries whose staged keys and this step's would not fit
         const bool leader = (G == 1) ? (half == 0) : (lane % LQ == 0);
-        unsigned long long need = __ballot(leader && nstg + tot > STG);
-        while (need) {
-          const int l = __ffsll((long long)need) - 1;
-          need &= need - 1;
-          const int q = (G == 1) ? (32 * w + l) : (w * QW + l / LQ);
-          merge(q, __builtin_amdgcn_readlane(nstg, l));
-          if (qsel == q) nstg = 0;
+        if (__ballot(leader && nstg + tot > STG)) {   // some query's keys would not fit
+          merge_wave(nstg, leader);
+          nstg = 0;
         }
         if (c > 0) {
           uint2* sq = stg + (size_t)qsel * STG;
@@ -514,8 +536,8 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
       // is thus reached by the group scores of at least r + 1 distinct chunks of
       // the slot, and slots share no chunk: at least K distinct chunks reach the
       // K-th largest u of the query, which bounds its K-th best group score.
-      for (int j = 0; j < QB / 4; ++j) {
-        const int q = w * (QB / 4) + j;
+      for (int j = 0; j < QB / NW; ++j) {
+        const int q = w * (QB / NW) + j;
         float ua = -INFINITY, ub = -INFINITY;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -536,13 +558,13 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
         if (lane == 0) tk[q] = kth;
       }
       __syncthreads();
+      for (int t = tid; t < QB * K; t += NT) lst[t] = 0ull;   // pass-0 scratch read above
       for (int t = tid; t < QB; t += NT) {
         const float T = tk[t];
         // pass 1 computes s_h - L_h as one fma of the accumulator, which rounds
         // differently from the product above: lower the bound by a margin far
         // above that rounding so no chunk at the bound is lost
         const float Tm = (T == -INFINITY) ? -INFINITY : T - (1e-3f + 1e-6f * fabsf(T));
-        thr[t] = (Tm == -INFINITY) ? 0ull : ((uint64_t)f32_order_key(Tm) << 32);
         thf[t] = Tm;
       }
       __syncthreads();
@@ -551,24 +573,39 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   run_pass(std::integral_constant<int, 0>{});
   run_pass(std::integral_constant<int, 1>{});
 
-  // final merge, ascending ids, write the selection
-  for (int qq = 0; qq < QW; ++qq) {
-    const int q = w * QW + qq;
-    const int ns = __builtin_amdgcn_readlane(nstg, (G == 1) ? qq : qq * LQ);
-    if (ns > 0) merge(q, ns);
-    const int tot = (int)cnt_lst[q];
-    const uint64_t e = (lane < tot) ? lst[(size_t)q * K + lane] : 0ull;
-    int id = (lane < tot) ? (int)(0xffffffffu - (uint32_t)e) : 0x7fffffff;
-    id = sort64_asc(id, lane);
-    const int i = i0 + q;
-    if (i < N && lane < K) selg[(long long)i * K + lane] = (lane < tot) ? id : -1;
+  // final merge, then each query's ids ascending (sorting (1 << 32 | ~id)
+  // descending; empty slots, 0, go last) and the selection row
+  merge_wave(nstg, (G == 1) ? (half == 0) : (lane % LQ == 0));
+  {
+    const int lg = lane & 7;
+#pragma unroll 1
+    for (int rd = 0; rd < QW / 8; ++rd) {
+      const int q = w * QW + 8 * rd + (lane >> 3);
+      uint64_t x[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int i = 8 * lg + r;
+        const uint64_t e = (i < K) ? lst[(size_t)q * K + i] : 0ull;
+        x[r] = e ? ((1ull << 32) | (uint64_t)(uint32_t)e) : 0ull;
+      }
+      sort8x8_desc(x, lg);
+      const int i = i0 + q;
+      if (i < N) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int rank = 8 * lg + r;
+          if (rank < K)
+            selg[(long long)i * K + rank] = (x[r] >> 32) ? (int)(0xffffffffu - (uint32_t)x[r]) : -1;
+        }
+      }
+    }
   }
 }
 
 template <int G>
 hipError_t launch_score(const HilsShape& s, const void* qr, const void* ksum, const float* bsum,
                         int32_t* sel, hipStream_t st) {
-  const int QB = Geo<G>::QB;
+  const int QB = Geo<G>::QB, NT = Geo<G>::NT;
   const int nqb = (s.N + QB - 1) / QB;
   const Lds<G> L(s.K);
   auto f = k_score_fast<G>;
