@@ -40,9 +40,12 @@ constexpr int CT = 32;         // chunks per tile
 constexpr int TRK = 128;       // pass-0 tracked scores per (query, head): 32 slots x ranks 0-2 (rank 3 unused)
 constexpr int XROW = CT;       // row of the cross-head exchange buffer (floats); its 16-byte
                                // pieces are XOR-swizzled by the row's low 3 bits
-// buffer descriptor word 3 for raw (unformatted, stride 0) loads on gfx9-family
-// parts: 32-bit data format, so num_records counts bytes
-constexpr int BUF_RSRC_WORD3 = 0x00020000;
+// k' in MFMA fragment order: per (query head, 32-chunk tile) FRAGS fragments of
+// 64 lanes x 16 bytes.  Fragment ks < 8 holds the A operand of k-step ks
+// (lane l: chunk 32t + l % 32, elements 16 ks + 8 (l / 32) .. + 7); fragment
+// 8 holds b' / scale split into three bf16 terms (lanes 0-31, elements 0-2),
+// which an MFMA against a constant operand of ones adds exactly.
+constexpr int FRAGS = 9;
 
 // Workgroup geometry.  Every wavefront scores 32 queries of one head; a
 // workgroup of NW wavefronts covers QB = 32 NW / G queries with all G heads.
@@ -65,18 +68,16 @@ struct Geo {
   static_assert(QW % 8 == 0, "merge rounds take 8 queries");
 };
 
-// [0, 64 KB) is also the scratch of the tracked scores between the passes
-// (G*QB = 128 (query, head) pairs x TRK floats); it covers ktile, xb, lst and
-// possibly stg, which are idle then.  tq and everything after it start past it.
+// The tracked scores of pass 0 (G*QB (query, head) pairs x TRK floats) are
+// written at offset 0 once the pass's loop is done; they cover the exchange
+// buffers, the lists and possibly the staging area, idle then.  tq and
+// everything after it start past them.
 template <int G>
 struct Lds {
-  size_t ktile, btile, xb, lst, stg, tq, thf, tk, cnt, total;
+  size_t xb, lst, stg, tq, thf, tk, cnt, total;
   __host__ __device__ Lds(int K) {
     size_t o = 0;
-    ktile = o; o += (size_t)G * CT * D * 2;            // swizzled, no padding
-    btile = o; o += (size_t)G * CT * 4;
-    xb = o;    o += (G > 1) ? (size_t)G * Geo<G>::QB * XROW * 4 : 0;
-    o = (o + 15) & ~(size_t)15;
+    xb = o;    o += (G > 1) ? (size_t)2 * G * Geo<G>::QB * XROW * 4 : 0;   // two buffers
     lst = o;   o += (size_t)Geo<G>::QB * K * 8;
     stg = o;   o += (size_t)Geo<G>::QB * Geo<G>::STG * 8;
     const size_t scratch = (size_t)G * Geo<G>::QB * TRK * 4;
@@ -98,14 +99,6 @@ struct Lds {
 
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a > b ? b : a; }
-
-// a wavefront-uniform pointer, held in scalar registers
-__device__ __forceinline__ void* uniform_ptr(const void* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-}
 
 // The 64 keys of one query held by its 8 lanes (lg = lane & 7) x 8
 // registers: the key of rank 8 lg + r sits in register r.  In the bitonic
@@ -193,20 +186,18 @@ __device__ __forceinline__ float merge_top64_f(float a, float b, int lane) {
 
 template <int G>
 __global__ void __launch_bounds__(Geo<G>::NT, 2)
-k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
-             const float* __restrict__ bsum, int32_t* __restrict__ sel, int Hq, int Hkv, int N,
-             int W, int K, int nC, float tau2, float bscale, int nqb) {
+k_score_fast(const bf16_t* __restrict__ qr, const uint4* __restrict__ frag,
+             int32_t* __restrict__ sel, int Hq, int Hkv, int N, int W, int K, int ntg, float tau2,
+             int nqb) {
   using GE = Geo<G>;
   constexpr int QB = GE::QB, QW = GE::QW, LQ = GE::LQ, CL = GE::CL;
   constexpr int STG = GE::STG, NT = GE::NT, NW = GE::NW;
   extern __shared__ __align__(16) unsigned char sm[];
   const Lds<G> L(K);
-  bf16_t* ktile = reinterpret_cast<bf16_t*>(sm + L.ktile);   // [G][CT][16 parts], part ^= c & 15
-  float* btile = reinterpret_cast<float*>(sm + L.btile);     // [G][CT]  b' * log2 e / tau2
-  float* xb = reinterpret_cast<float*>(sm + L.xb);           // [G][QB][XROW]
+  float* xb = reinterpret_cast<float*>(sm + L.xb);           // [2][G][QB][XROW]
   float* tq = reinterpret_cast<float*>(sm + L.tq);           // [G][QB] log-sum-exp (base 2)
   float* tk = reinterpret_cast<float*>(sm + L.tk);           // [QB] bound T of the query
-  float* trk = reinterpret_cast<float*>(sm + L.ktile);       // [G*QB][TRK] between the passes
+  float* trk = reinterpret_cast<float*>(sm);                 // [G*QB][TRK] between the passes
   uint64_t* lst = reinterpret_cast<uint64_t*>(sm + L.lst);   // [QB][K]
   uint2* stg = reinterpret_cast<uint2*>(sm + L.stg);         // [QB][STG] (score bits, chunk id)
   uint32_t* cnt_lst = reinterpret_cast<uint32_t*>(sm + L.cnt);
@@ -248,54 +239,18 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   const int cbase = (G == 1) ? 0 : CL * (lane % LQ);
   int nstg = 0;
 
-  // tile staging through registers into a single XOR-swizzled LDS tile.  The
-  // loads are unconditional and kept raw until the store, so they stay in
-  // flight while earlier tiles are scored.
-  constexpr int PPT = G * CT * 16 / NT;    // 16-byte pieces per thread per tile
-  static_assert(PPT * NT == G * CT * 16, "pieces split evenly over the threads");
-  // piece tid + NT p of the tile: row (tid + NT p) / 16 = head * CT + chunk,
-  // 16-byte part tid % 16.  The loads go through buffer descriptors whose base
-  // is the tile's first row and whose range ends at the group's last k' row:
-  // the per-thread offsets never change, and rows past the range read zero
-  // (past chunk nC - 1 a row reads another head's chunk or zero; those scores
-  // are masked by the candidate range).
-  const char* kgrp = reinterpret_cast<const char*>(ksum + hb * nC * (long long)D);
-  const char* bgrp = reinterpret_cast<const char*>(bsum + hb * nC);
-  uint32_t voff[PPT];
+  // this wavefront's k' fragments: coalesced 16-byte loads straight into the
+  // MFMA operand registers (no LDS staging, no barrier)
+  const uint4* fh = frag + ((hb + hw) * (long long)ntg) * (FRAGS * 64) + lane;
+  auto load_frag = [&](int t, uint4 (&f)[FRAGS]) {
+    const uint4* p = fh + (long long)t * (FRAGS * 64);
 #pragma unroll
-  for (int p = 0; p < PPT; ++p) {
-    const int row = (tid + NT * p) / 16;
-    voff[p] = ((uint32_t)(row / CT) * (uint32_t)nC + (uint32_t)(row % CT)) * (uint32_t)(D * 2) +
-              (uint32_t)(tid & 15) * 16u;
-  }
-  const uint32_t boff = ((uint32_t)((tid / CT) % G) * (uint32_t)nC + (uint32_t)(tid % CT)) * 4u;
-  const int grows = G * nC;                // k' rows of the group
-  // two register buffers: the loads of tile t + 2 are issued while tile t is
-  // scored and tile t + 1 waits in the other buffer for its LDS store, so each
-  // load has two tile steps to arrive
-  uint4 preA[PPT], preB[PPT];
-  float bpreA = 0.0f, bpreB = 0.0f;
-  auto load_tile = [&](int t, uint4 (&pre)[PPT], float& bpre) {
-    const int r0 = __builtin_amdgcn_readfirstlane(CT * t);
-    const int left = max(grows - r0, 0);
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(kgrp + (size_t)r0 * (D * 2)), 0, left * (D * 2), BUF_RSRC_WORD3);
-    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-        uniform_ptr(bgrp + (size_t)r0 * 4), 0, left * 4, BUF_RSRC_WORD3);
-#pragma unroll
-    for (int p = 0; p < PPT; ++p)
-      pre[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)voff[p], 0, 0));
-    bpre = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(br, (int)boff, 0, 0));
+    for (int ks = 0; ks < FRAGS; ++ks) f[ks] = p[ks * 64];
   };
-  auto store_tile = [&](const uint4 (&pre)[PPT], float bpre) {
-#pragma unroll
-    for (int p = 0; p < PPT; ++p) {
-      const int piece = tid + NT * p;
-      const int h = piece / (CT * 16), c = (piece / 16) % CT, part = piece % 16;
-      st_u4(ktile + ((size_t)h * CT + c) * D + ((part ^ (c & 15)) * 8), pre[p]);
-    }
-    if (tid < G * CT) btile[tid] = bpre * bscale;
-  };
+  // B operand of the bias fragment: ones at k = 0, 1, 2 (lanes 0-31)
+  const uint32_t one2 = 0x3F803F80u;                  // two bf16 1.0
+  const bf16x8_t bones = __builtin_bit_cast(
+      bf16x8_t, half ? make_uint4(0u, 0u, 0u, 0u) : make_uint4(one2, one2 & 0xFFFFu, 0u, 0u));
 
   // merge the staged keys of every query of this wavefront into its sorted
   // top-K list: each query in one 8-lane group (QW / 8 rounds), keys of rank
@@ -342,26 +297,16 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   };
 
   // scores of tile t for this lane in accumulator units (score = tau2 * x, base
-  // 2): x[i] <-> chunk 32t + 8(i>>2) + 4*half + (i&3).  The accumulator starts
-  // at b' / tau2 of its chunk, so the bias costs no vector instruction.
+  // 2): x[i] <-> chunk 32t + 8(i>>2) + 4*half + (i&3).  The ninth MFMA adds the
+  // bias b' / tau2 of each chunk.
   const int n_lo = n_cand(i0, W, S);                 // every query of the block has >= n_lo
-  auto tile_scores = [&](int t, float* x) {
-    const bf16_t* kb = ktile + ((size_t)hw * CT + col) * D;
-    bf16x8_t a[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) a[ks] = ld_bf16x8(kb + (((2 * ks + half) ^ (col & 15)) * 8));
-    const float* bt = btile + (size_t)hw * CT;
+  auto tile_scores = [&](const uint4 (&f)[FRAGS], int t, float* x) {
     f32x16_t acc;
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const float4 b4 = *reinterpret_cast<const float4*>(bt + 8 * gq + 4 * half);
-      acc[4 * gq + 0] = b4.x;
-      acc[4 * gq + 1] = b4.y;
-      acc[4 * gq + 2] = b4.z;
-      acc[4 * gq + 3] = b4.w;
-    }
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) acc = mfma32(a[ks], bq[ks], acc);
+    for (int ks = 0; ks < 8; ++ks) acc = mfma32(__builtin_bit_cast(bf16x8_t, f[ks]), bq[ks], acc);
+    acc = mfma32(__builtin_bit_cast(bf16x8_t, f[8]), bones, acc);
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = acc[i];
     if (CT * t + CT > n_lo) {                        // tile crosses some query's candidate range
@@ -382,19 +327,17 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     float t0[16], t1[16], t2[16];  // top 3 per register slot, descending (pass 0)
 #pragma unroll
     for (int i = 0; i < 16; ++i) { t0[i] = -INFINITY; t1[i] = -INFINITY; t2[i] = -INFINITY; }
-    load_tile(0, preA, bpreA);
-    store_tile(preA, bpreA);
-    __syncthreads();
-    load_tile(min(1, ntiles - 1), preA, bpreA);
+    uint4 fA[FRAGS], fB[FRAGS];
+    load_frag(0, fA);
     // pass 1 subtracts the head's log-sum-exp (L = -inf only for rows without
     // candidates, whose scores are all masked)
     const float nL = (L2 > -INFINITY) ? -L2 : 0.0f;
-    // one tile step: cur holds tile t + 1 (stored to LDS during the step), nxt
-    // receives tile t + 2
-    auto step = [&](int t, const uint4 (&cur)[PPT], float bcur, uint4 (&nxt)[PPT], float& bnxt) {
-      load_tile(min(t + 2, ntiles - 1), nxt, bnxt);
+    // one tile step: cur holds the fragments of tile t, nxt receives tile t + 1
+    // (past the last tile: the last again, unused)
+    auto step = [&](int t, const uint4 (&cur)[FRAGS], uint4 (&nxt)[FRAGS]) {
+      load_frag(min(t + 1, ntiles - 1), nxt);
       float x[16];
-      tile_scores(t, x);
+      tile_scores(cur, t, x);
       if constexpr (pass == 0) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -416,35 +359,35 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
             for (int i = 0; i < 16; ++i) ssum += fast_exp2(fmaf(x[i], tau2, mneg));
           }
         }
-        __syncthreads();
-        store_tile(cur, bcur);   // past the last tile: rewrites the last tile, unused
-        __syncthreads();
       } else {
-        // group scores: s_h - L_h (base 2); the heads of a group meet in LDS.
-        // G = 1 keeps accumulator units, which order the chunks the same way.
+        // group scores: s_h - L_h (base 2); the heads of a group meet in LDS,
+        // in one of two exchange buffers by step parity (a wavefront writes
+        // buffer t & 1 only after every wavefront passed the barrier of step
+        // t - 1, so after their reads of step t - 2).  G = 1 keeps accumulator
+        // units, which order the chunks the same way, and exchanges nothing.
+        float* xbt = xb + (size_t)(t & 1) * G * QB * XROW;
         if (G > 1) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) x[i] = fmaf(x[i], tau2, nL);
           const int xrow = hw * QB + 32 * qw + col;
-          float* xr = xb + (size_t)xrow * XROW;
+          float* xr = xbt + (size_t)xrow * XROW;
 #pragma unroll
           for (int gq = 0; gq < 4; ++gq)
             *reinterpret_cast<float4*>(xr + 4 * ((2 * gq + half) ^ (xrow & 7))) =
                 make_float4(x[4 * gq], x[4 * gq + 1], x[4 * gq + 2], x[4 * gq + 3]);
         }
-        __syncthreads();         // exchange written; every wave is done reading the k' tile
-        store_tile(cur, bcur);   // next tile (past the last: rewrites the last, unused)
+        if (G > 1) __syncthreads();                      // exchange written
         float gs[CL];
         int cid0;
         if (G > 1) {
 #pragma unroll
           for (int j4 = 0; j4 < CL; j4 += 4) {
             const int piece = (cbase + j4) >> 2;
-            float4 mx = *reinterpret_cast<const float4*>(xb + (size_t)qsel * XROW + 4 * (piece ^ (qsel & 7)));
+            float4 mx = *reinterpret_cast<const float4*>(xbt + (size_t)qsel * XROW + 4 * (piece ^ (qsel & 7)));
 #pragma unroll
             for (int h = 1; h < G; ++h) {
               const int xrow = h * QB + qsel;
-              const float4 y = *reinterpret_cast<const float4*>(xb + (size_t)xrow * XROW + 4 * (piece ^ (xrow & 7)));
+              const float4 y = *reinterpret_cast<const float4*>(xbt + (size_t)xrow * XROW + 4 * (piece ^ (xrow & 7)));
               mx = make_float4(fmaxf(mx.x, y.x), fmaxf(mx.y, y.y), fmaxf(mx.z, y.z), fmaxf(mx.w, y.w));
             }
             gs[j4] = mx.x; gs[j4 + 1] = mx.y; gs[j4 + 2] = mx.z; gs[j4 + 3] = mx.w;
@@ -501,12 +444,11 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
           }
         }
         nstg += tot;
-        __syncthreads();         // next k' tile visible; exchange reads done
       }
     };
     for (int t = 0; t < ntiles; t += 2) {
-      step(t, preA, bpreA, preB, bpreB);
-      if (t + 1 < ntiles) step(t + 1, preB, bpreB, preA, bpreA);
+      step(t, fA, fB);
+      if (t + 1 < ntiles) step(t + 1, fB, fA);
     }
     if constexpr (pass == 0) {
       // per (query, head): log-sum-exp and the tracked scores, by slot and rank
@@ -602,21 +544,54 @@ k_score_fast(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   }
 }
 
+// k' and b' of every (sequence, query head) in MFMA fragment order (FRAGS per
+// 32-chunk tile); chunks past nC are zero.  One thread per 16-byte piece.
+// The bias term b' / tau2 is split as hi + mid + lo with each term a bf16
+// (the sum equals the fp32 value to within its last bit).
+__global__ void __launch_bounds__(256)
+k_score_frag(const bf16_t* __restrict__ ksum, const float* __restrict__ bsum, uint4* __restrict__ frag,
+             int nC, int ntg, float bscale, long long total) {
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= total) return;
+  const int lane = (int)(gid & 63);
+  const long long fi = gid >> 6;
+  const int ks = (int)(fi % FRAGS);
+  const long long rt = fi / FRAGS;
+  const int t = (int)(rt % ntg);
+  const long long row = rt / ntg;                    // sequence * Hq + head
+  const int c = CT * t + (lane & 31), half = lane >> 5;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (c < nC) {
+    if (ks < 8) {
+      v = *reinterpret_cast<const uint4*>(ksum + (row * nC + c) * (long long)D + 16 * ks + 8 * half);
+    } else if (half == 0) {
+      const float bv = bsum[row * nC + c] * bscale;
+      const float hi = (float)(__bf16)bv;
+      const float r1 = bv - hi;
+      const float mid = (float)(__bf16)r1;
+      const float lo = (float)(__bf16)(r1 - mid);
+      v.x = pack_bf16x2(hi, mid);
+      v.y = pack_bf16x2(lo, 0.0f);
+    }
+  }
+  frag[gid] = v;
+}
+
 template <int G>
-hipError_t launch_score(const HilsShape& s, const void* qr, const void* ksum, const float* bsum,
-                        int32_t* sel, hipStream_t st) {
+hipError_t launch_score(const HilsShape& s, const void* qr, const uint4* frag, int ntg, int32_t* sel,
+                        hipStream_t st) {
   const int QB = Geo<G>::QB, NT = Geo<G>::NT;
   const int nqb = (s.N + QB - 1) / QB;
   const Lds<G> L(s.K);
   auto f = k_score_fast<G>;
   hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
   const float tau2 = (float)(s.tau * 1.4426950408889634);
-  const float bscale = (float)(1.0 / s.tau);   // b' log2 e / tau2
   { HilsProfScope ps_("k_score_fast", st); hipLaunchKernelGGL(f, dim3((unsigned)((long long)s.B * s.Hkv * nqb)), dim3(NT), L.total, st,
-                     (const bf16_t*)qr, (const bf16_t*)ksum, bsum, sel, s.Hq, s.Hkv, s.N, s.W, s.K,
-                     s.nC, tau2, bscale, nqb); }
+                     (const bf16_t*)qr, frag, sel, s.Hq, s.Hkv, s.N, s.W, s.K, ntg, tau2, nqb); }
   return hipGetLastError();
 }
+
+int frag_tiles(const HilsShape& s) { return (s.nC + CT - 1) / CT; }
 
 }  // namespace
 
@@ -629,12 +604,24 @@ size_t hils_fast_score_lds(int G, int K) {
   return 0;
 }
 
+size_t hils_score_frag_bytes(const HilsShape& s) {
+  return (size_t)s.B * s.Hq * frag_tiles(s) * FRAGS * 64 * 16;
+}
+
 hipError_t hils_launch_score_fast(const HilsShape& s, const void* qr, const void* ksum,
-                                  const float* bsum, int32_t* sel, hipStream_t st) {
+                                  const float* bsum, void* frag, int32_t* sel, hipStream_t st) {
+  const int ntg = frag_tiles(s);
+  if (ntg > 0) {
+    const long long total = (long long)s.B * s.Hq * ntg * FRAGS * 64;
+    HilsProfScope ps_("k_score_frag", st);
+    hipLaunchKernelGGL(k_score_frag, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                       (const bf16_t*)ksum, bsum, (uint4*)frag, s.nC, ntg, (float)(1.0 / s.tau), total);
+  }
+  const uint4* fr = (const uint4*)frag;
   switch (s.G) {
-    case 1: return launch_score<1>(s, qr, ksum, bsum, sel, st);
-    case 2: return launch_score<2>(s, qr, ksum, bsum, sel, st);
-    case 4: return launch_score<4>(s, qr, ksum, bsum, sel, st);
+    case 1: return launch_score<1>(s, qr, fr, ntg, sel, st);
+    case 2: return launch_score<2>(s, qr, fr, ntg, sel, st);
+    case 4: return launch_score<4>(s, qr, fr, ntg, sel, st);
   }
   return hipErrorInvalidValue;
 }

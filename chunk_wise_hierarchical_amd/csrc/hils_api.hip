@@ -67,14 +67,14 @@ inline bool pair_path(const HilsShape& s, uint32_t flags, bool fast) {
 }
 
 struct PrefillLayout {
-  size_t ks, bs, sel, slog, vt, total;
+  size_t ks, bs, sel, slog, vt, kf, total;
   // per-chunk bucket path
   size_t cnt, loff, toff, cur, tot, tinfo, list, lam, swa, lz, part;
   int qs_max;
 };
 // generic path: summaries, selection, fusion logits; fast path: summaries,
-// selection and the per-chunk transposed V (fusion logits are recomputed in
-// the attention kernel)
+// selection, the per-chunk transposed V and k' in MFMA fragment order (fusion
+// logits are recomputed in the attention kernel)
 PrefillLayout prefill_layout(const HilsShape& s, bool fast, bool pairs) {
   PrefillLayout L{};
   size_t off = 0;
@@ -84,6 +84,7 @@ PrefillLayout prefill_layout(const HilsShape& s, bool fast, bool pairs) {
   if (fast) {
     L.slog = 0;
     L.vt = off; off += align_up((size_t)s.B * s.Hkv * s.nCc * s.d * s.S * 2);
+    L.kf = off; off += align_up(hils_score_frag_bytes(s));
     if (pairs) {
       const int qs = s.N < HILS_PAIR_SLICE ? s.N : HILS_PAIR_SLICE;
       const size_t F = (size_t)s.B * s.Hkv * s.nC;
@@ -300,7 +301,7 @@ hils_status hils_prefill(const hils_cfg* cfg, const void* q, const void* q_route
     void* vt = (void*)(w + L.vt);
     e = hils_launch_vt(s, v, vt, st);
     if (e != hipSuccess) return HILS_E_HIP;
-    e = hils_launch_score_fast(s, qr, ks, bs, sl, st);
+    e = hils_launch_score_fast(s, qr, ks, bs, w + L.kf, sl, st);
     if (e != hipSuccess) return HILS_E_HIP;
     if (!pairs) return hip_status(hils_launch_attn_fast(s, q, qr, k, vt, ks, bs, sl, out, st));
     HilsPairBufs pb{};

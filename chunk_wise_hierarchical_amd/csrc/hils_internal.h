@@ -36,8 +36,10 @@ hipError_t hils_launch_attn_generic(const HilsShape& s, const void* q, const voi
 
 // fast path (bf16, d = 128, S = 64, G in {1,2,4}, K <= 64): fast_score.hip, fast_attn.hip
 hipError_t hils_launch_vt(const HilsShape& s, const void* v, void* vt, hipStream_t st);
+// frag: workspace of hils_score_frag_bytes(s) for k' in MFMA fragment order
 hipError_t hils_launch_score_fast(const HilsShape& s, const void* qr, const void* ksum,
-                                  const float* bsum, int32_t* sel, hipStream_t st);
+                                  const float* bsum, void* frag, int32_t* sel, hipStream_t st);
+size_t hils_score_frag_bytes(const HilsShape& s);
 hipError_t hils_launch_attn_fast(const HilsShape& s, const void* q, const void* qr, const void* k,
                                  const void* vt, const void* ksum, const float* bsum,
                                  const int32_t* sel, void* out, hipStream_t st);
