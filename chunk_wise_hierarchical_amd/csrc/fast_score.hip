@@ -48,13 +48,13 @@ constexpr int XROW = CT;       // row of the cross-head exchange buffer (floats)
 constexpr int FRAGS = 9;
 
 // Workgroup geometry.  Every wavefront scores 32 queries of one head; a
-// workgroup of NW wavefronts covers QB = 32 NW / G queries with all G heads.
-// The k' tile each step loads and stores to LDS serves the whole workgroup,
-// so G = 4 takes 8 wavefronts (64 queries, one workgroup per CU) to halve that
-// traffic per query; G = 1 and 2 keep 4 (their lists would not fit otherwise).
+// workgroup of NW = 4 wavefronts covers QB = 32 NW / G queries with all G
+// heads (the heads of a query meet in the workgroup's LDS exchange).  Each
+// wavefront loads its own k' fragments, so a larger workgroup would only
+// lengthen the exchange barrier (8 wavefronts measured slower).
 template <int G>
 struct Geo {
-  static constexpr int NW = (G == 4) ? 8 : 4;
+  static constexpr int NW = 4;
   static constexpr int NT = 64 * NW;      // threads
   static constexpr int QB = 32 * NW / G;  // queries per workgroup
   static constexpr int QW = QB / NW;      // queries per wavefront in the selection layout
