@@ -368,6 +368,214 @@ k_bwd_rows(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
 }
 
 // ---------------------------------------------------------------------------
+// per query row, all attended keys at once (used when their logits fit LDS):
+// the same statistics and dq as k_bwd_rows, with the work spread so that no
+// phase waits on a block-wide reduction per chunk:
+//   1. every attended key's logit and dout.v (chunk keys in slot order, then
+//      the window), one (key, head) per thread;
+//   2. softmax statistics, one wavefront per (slot, head) and per window head;
+//   3. fusion weights per head; 4. each key's dq weight;
+//   5. dq = sum over keys of weight x k_j: thread (head, 16-byte group, key
+//      subset) with vector loads of the key rows, subsets summed in LDS.
+template <typename T>
+__global__ void __launch_bounds__(BT)
+k_bwd_rows2(const T* __restrict__ q, const T* __restrict__ qr, const T* __restrict__ k,
+            const T* __restrict__ v, const T* __restrict__ ksum, const float* __restrict__ bsum,
+            const T* __restrict__ dout, const int32_t* __restrict__ sel, float* __restrict__ dq,
+            float* __restrict__ dqr, float* __restrict__ pstat, float* __restrict__ wstat, int Hq,
+            int Hkv, int G, int N, int d, int S, int W, int K, int nC, float tau, int route_sep) {
+  extern __shared__ __align__(16) float smr[];
+  constexpr int VN = V16<T>::N;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const long long row = blockIdx.x;                  // (b, g, i)
+  const int i = (int)(row % N);
+  const long long bg = row / N;
+  const int g = (int)(bg % Hkv);
+  const long long b = bg / Hkv;
+  const long long hb = b * Hq + (long long)g * G;
+  const int w0 = (int)window_start(i, W, S);
+  const int L = i - w0 + 1;
+  const int LW = W + S - 1;                          // longest window
+  const int NCK = K * S;                             // chunk key columns
+  const int RL = NCK + ((LW + 3) & ~3);              // columns per head
+  float* qs = smr;                                   // [G][d]
+  float* qh = qs + G * d;                            // [G][d]
+  float* go = qh + G * d;                            // [G][d]
+  float* lw = go + G * d;                            // [G][RL] logits -> weights
+  float* du = lw + G * RL;                           // [G][RL] dout.v_j
+  float* st = du + G * RL;                           // [K][G][4] alpha, lse, g, d s_hat
+  float* sw = st + K * G * 4;                        // [G][4] alpha_w, lse_w, g_w, d log Z
+  float* dqp = sw + G * 4;                           // [BT * VN] dq partials by key subset
+  __shared__ int ssel[128];
+  __shared__ int skk;
+
+  for (int t = tid; t < G * d; t += BT) {
+    const int r = t / d, e = t - r * d;
+    const long long o = ((hb + r) * N + i) * (long long)d + e;
+    qs[t] = Elt<T>::ld(q + o);
+    qh[t] = Elt<T>::ld(qr + o);
+    go[t] = Elt<T>::ld(dout + o);
+  }
+  if (tid == 0) {
+    int kk = 0;
+    for (int t = 0; t < K; ++t) {
+      const int c = sel[row * K + t];
+      if (c >= 0 && c < nC) ssel[kk++] = c;
+    }
+    skk = kk;
+  }
+  __syncthreads();
+  const int kk = skk;
+  const int nk = kk * S + L;                         // attended keys
+  const T* kb = k + bg * (long long)N * d;
+  const T* vb = v + bg * (long long)N * d;
+  // key f: chunk key (slot f / S, offset f % S) or window key f - kk S
+  auto key_pos = [&](int f) -> long long {
+    return (f < kk * S) ? (long long)ssel[f / S] * S + (f % S) : (long long)(w0 + f - kk * S);
+  };
+  auto key_col = [&](int f) { return (f < kk * S) ? f : NCK + (f - kk * S); };
+
+  // 1. chunk scores s_hat (routing query) and every key's logit and dout.v
+  for (int t = tid; t < kk * G; t += BT) {
+    const int s2 = t / G, r = t - s2 * G, c = ssel[s2];
+    const T* kp = ksum + ((hb + r) * nC + c) * (long long)d;
+    st[(s2 * G + r) * 4 + 0] = fmaf(tau, dot_row<T>(qh + r * d, kp, d), bsum[(hb + r) * nC + c]);
+  }
+  for (int t = tid; t < nk * G; t += BT) {
+    const int f = t / G, r = t - f * G;
+    const long long pos = key_pos(f);
+    const int col = key_col(f);
+    lw[r * RL + col] = tau * dot_row<T>(qs + r * d, kb + pos * d, d);
+    du[r * RL + col] = dot_row<T>(go + r * d, vb + pos * d, d);
+  }
+  __syncthreads();
+  // 2. softmax statistics: items 0 .. G-1 are the window heads, then (slot, head)
+  for (int it = wv; it < G + kk * G; it += BT / 64) {
+    if (it < G) {
+      const int r = it;
+      float* x = lw + r * RL + NCK;
+      const float* u = du + r * RL + NCK;
+      float m = -INFINITY;
+      for (int j = lane; j < L; j += 64) m = fmaxf(m, x[j]);
+      m = wave_max_f(m);
+      float z = 0.0f;
+      for (int j = lane; j < L; j += 64) z += __expf(x[j] - m);
+      z = wave_sum_f(z);
+      const float lse = m + __logf(z);
+      float gw = 0.0f;
+      for (int j = lane; j < L; j += 64) {
+        const float p = __expf(x[j] - lse);
+        x[j] = p;
+        gw = fmaf(p, u[j], gw);
+      }
+      gw = wave_sum_f(gw);
+      if (lane == 0) { sw[r * 4 + 1] = lse; sw[r * 4 + 2] = gw; }
+    } else {
+      const int s2 = (it - G) / G, r = (it - G) - s2 * G;
+      float* x = lw + r * RL + s2 * S;
+      const float* u = du + r * RL + s2 * S;
+      const float xv = (lane < S) ? x[lane] : -INFINITY;
+      const float m = wave_max_f(xv);
+      const float z = wave_sum_f((lane < S) ? __expf(xv - m) : 0.0f);
+      const float lse = m + __logf(z);
+      const float p = (lane < S) ? __expf(xv - lse) : 0.0f;
+      const float uv = (lane < S) ? u[lane] : 0.0f;
+      const float gt = wave_sum_f(p * uv);
+      if (lane < S) x[lane] = p * (uv - gt);
+      if (lane == 0) { st[(s2 * G + r) * 4 + 1] = lse; st[(s2 * G + r) * 4 + 2] = gt; }
+    }
+  }
+  __syncthreads();
+  // 3. fusion weights, gbar, d s_hat and d log Z_swa per head
+  if (tid < G) {
+    const int r = tid;
+    const float lse = sw[r * 4 + 1];
+    float M = lse;
+    for (int s2 = 0; s2 < kk; ++s2) M = fmaxf(M, st[(s2 * G + r) * 4]);
+    float Z = __expf(lse - M);
+    for (int s2 = 0; s2 < kk; ++s2) Z += __expf(st[(s2 * G + r) * 4] - M);
+    for (int s2 = 0; s2 < kk; ++s2) st[(s2 * G + r) * 4] = __expf(st[(s2 * G + r) * 4] - M) / Z;
+    sw[r * 4 + 0] = __expf(lse - M) / Z;
+    float gbar = sw[r * 4] * sw[r * 4 + 2];
+    for (int s2 = 0; s2 < kk; ++s2) gbar = fmaf(st[(s2 * G + r) * 4], st[(s2 * G + r) * 4 + 2], gbar);
+    for (int s2 = 0; s2 < kk; ++s2)
+      st[(s2 * G + r) * 4 + 3] = st[(s2 * G + r) * 4] * (st[(s2 * G + r) * 4 + 2] - gbar);
+    sw[r * 4 + 3] = sw[r * 4] * (sw[r * 4 + 2] - gbar);
+  }
+  __syncthreads();
+  // 4. dq weight of every key: tau alpha_t p_j (u_j - g_t) on a chunk,
+  //    tau (alpha_w p_j (u_j - g_w) + d log Z_swa p_j) on the window
+  for (int t = tid; t < nk * G; t += BT) {
+    const int f = t / G, r = t - f * G;
+    const int col = key_col(f);
+    float* x = lw + r * RL + col;
+    if (f < kk * S) {
+      *x = tau * st[((f / S) * G + r) * 4] * *x;
+    } else {
+      const float p = *x;
+      *x = tau * (sw[r * 4] * p * (du[r * RL + col] - sw[r * 4 + 2]) + sw[r * 4 + 3] * p);
+    }
+  }
+  __syncthreads();
+  // 5. dq: thread (head r, 16-byte group eg, key subset sub)
+  const int ngh = d / VN, ngr = G * ngh, nsub = BT / ngr;
+  {
+    const int grp = tid % ngr, sub = tid / ngr;
+    const int r = grp / ngh, eg = grp - r * ngh;
+    float a[VN];
+#pragma unroll
+    for (int u = 0; u < VN; ++u) a[u] = 0.0f;
+    if (sub < nsub) {
+      for (int f = sub; f < nk; f += nsub) {
+        const float wgt = lw[r * RL + key_col(f)];
+        float kv[VN];
+        V16<T>::ld(kb + key_pos(f) * d + eg * VN, kv);
+#pragma unroll
+        for (int u = 0; u < VN; ++u) a[u] = fmaf(wgt, kv[u], a[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VN; ++u) dqp[tid * VN + u] = a[u];
+  }
+  __syncthreads();
+  for (int t = tid; t < G * d; t += BT) {
+    const int r = t / d, e = t - r * d;
+    const int grp = r * ngh + e / VN, u = e % VN;
+    float dqv = 0.0f;
+    for (int sub = 0; sub < nsub; ++sub) dqv += dqp[(sub * ngr + grp) * VN + u];
+    // routing query: tau sum_t d s_hat_t k'_t
+    float dh = 0.0f;
+    for (int s2 = 0; s2 < kk; ++s2)
+      dh = fmaf(st[(s2 * G + r) * 4 + 3], Elt<T>::ld(ksum + ((hb + r) * nC + ssel[s2]) * (long long)d + e), dh);
+    dh *= tau;
+    const long long o = ((hb + r) * N + i) * (long long)d + e;
+    if (route_sep) {
+      dq[o] = dqv;
+      dqr[o] = dh;
+    } else {
+      dq[o] = dqv + dh;
+    }
+  }
+  // statistics for the column pass (window probabilities are recomputed there)
+  for (int t = tid; t < K * G * 4; t += BT) {
+    const int s2 = t / (G * 4);
+    pstat[row * K * G * 4 + t] = (s2 < kk) ? st[t] : 0.0f;
+  }
+  for (int t = tid; t < G * 4; t += BT) {
+    const int r = t / 4, f = t - r * 4;
+    wstat[((hb + r) * N + i) * 4 + f] = sw[t];
+  }
+}
+
+size_t bwd_rows2_lds(const HilsShape& s) {
+  const int LW = s.W + s.S - 1;
+  const size_t RL = (size_t)s.K * s.S + ((LW + 3) & ~3);
+  const int vn = (s.dtype == 0) ? 8 : 4;
+  return sizeof(float) * (3 * (size_t)s.G * s.d + 2 * (size_t)s.G * RL + (size_t)s.K * s.G * 4 +
+                          (size_t)s.G * 4 + (size_t)BT * vn);
+}
+
+// ---------------------------------------------------------------------------
 // per chunk: dk, dv of its tokens; summary backward
 //
 // 512 threads: thread (token jt = tid / 8, eighth qd = tid % 8) owns d/8
@@ -603,15 +811,18 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
   { HilsProfScope ps_("k_bwd_lists", st);
     hipLaunchKernelGGL(k_bwd_lists, dim3((unsigned)(s.B * s.Hkv)), dim3(1024), lshm, st, sel,
                        wb.off, wb.ent, s.N, s.K, s.nC); }
-  const size_t rshm = hils_bwd_rows_lds(s);
+  // the all-keys row kernel when every attended key's logit fits 64 KB of LDS
+  const bool all_keys = bwd_rows2_lds(s) <= 65536;
+  const size_t rshm = all_keys ? bwd_rows2_lds(s) : hils_bwd_rows_lds(s);
   const size_t cshm = sizeof(float) * ((size_t)s.G * s.d + s.G + (size_t)s.S * s.d + 8) +
                       (size_t)CBATCH * (sizeof(int) + 4 * sizeof(float));
   const int sep = dqr != nullptr;
   if (s.dtype == 0) {
-    hipFuncSetAttribute((const void*)k_bwd_rows<bf16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rshm);
+    auto fr = all_keys ? k_bwd_rows2<bf16_t> : k_bwd_rows<bf16_t>;
+    hipFuncSetAttribute((const void*)fr, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rshm);
     hipFuncSetAttribute((const void*)k_bwd_cols<bf16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)cshm);
     { HilsProfScope ps_("k_bwd_rows", st);
-      hipLaunchKernelGGL(k_bwd_rows<bf16_t>, dim3((unsigned)((long long)s.B * s.Hkv * s.N)), dim3(BT), rshm, st,
+      hipLaunchKernelGGL(fr, dim3((unsigned)((long long)s.B * s.Hkv * s.N)), dim3(BT), rshm, st,
                          (const bf16_t*)q, (const bf16_t*)qr, (const bf16_t*)k, (const bf16_t*)v,
                          (const bf16_t*)ksum, bsum, (const bf16_t*)dout, sel, dq, dqr, wb.pstat,
                          wb.wstat, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, tau, sep); }
@@ -622,10 +833,11 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
                          dk, dv, dlm, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, s.nCc, tau,
                          s.mode); }
   } else {
-    hipFuncSetAttribute((const void*)k_bwd_rows<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rshm);
+    auto fr = all_keys ? k_bwd_rows2<float> : k_bwd_rows<float>;
+    hipFuncSetAttribute((const void*)fr, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rshm);
     hipFuncSetAttribute((const void*)k_bwd_cols<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)cshm);
     { HilsProfScope ps_("k_bwd_rows", st);
-      hipLaunchKernelGGL(k_bwd_rows<float>, dim3((unsigned)((long long)s.B * s.Hkv * s.N)), dim3(BT), rshm, st,
+      hipLaunchKernelGGL(fr, dim3((unsigned)((long long)s.B * s.Hkv * s.N)), dim3(BT), rshm, st,
                          (const float*)q, (const float*)qr, (const float*)k, (const float*)v,
                          (const float*)ksum, bsum, (const float*)dout, sel, dq, dqr, wb.pstat,
                          wb.wstat, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, tau, sep); }

@@ -69,6 +69,13 @@ def test_backward_bf16_gqa_ragged():
     _case(w, label="bf16 GQA ragged")
 
 
+def test_backward_many_selected_keys():
+    # G = 4 and K = 32 chunks of 64: the keys a row attends do not fit the
+    # all-keys row kernel's LDS budget, so the chunk-at-a-time row kernel runs
+    w = synth.get_workload("prefill_64k", N=2500, Hq=8, Hkv=2, W=128, K=32, regime="iid")
+    _case(w, label="bf16 GQA K=32")
+
+
 def test_backward_summary_modes():
     w = synth.get_workload("prefill_64k", N=520, Hq=4, Hkv=2, d=64, S=32, W=96, K=3, regime="iid",
                            dtype="f32")
