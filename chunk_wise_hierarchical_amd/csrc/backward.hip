@@ -587,6 +587,18 @@ size_t bwd_rows2_lds(const HilsShape& s) {
 constexpr int CT = 512;
 constexpr int CBATCH = 512;                          // contributions described per batch
 constexpr int CE = 16;                               // elements per thread (d <= 128)
+// contributions whose q, dout and routing-query rows are staged in LDS
+// together (two buffers): 48 KB for d = 128 in either precision
+template <typename T> struct ColStage { static constexpr int NB = (sizeof(T) == 2) ? 32 : 16; };
+
+// bytes of the column kernel's staging area (also the summary backward's
+// scratch of S x d floats, used after the contributions)
+template <typename T>
+__host__ __device__ inline size_t col_stage_bytes(int d, int S) {
+  const size_t st = (size_t)2 * 3 * ColStage<T>::NB * d * sizeof(T);
+  const size_t sc = (size_t)S * d * sizeof(float);
+  return ((st > sc ? st : sc) + 15) & ~(size_t)15;
+}
 
 template <typename T>
 __global__ void __launch_bounds__(CT)
@@ -610,10 +622,14 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
   const int jt = tid >> 3, qd = tid & 7;
   const bool act = jt < jn;
   const int e0 = qd * DQ;
-  float* dks = smc;                                  // [G][d] dk' of the chunk
+  constexpr int NB = ColStage<T>::NB;
+  // staging: [2 buffers][q, dout, routing query][NB][d] T; after the
+  // contributions the same bytes hold the [S][d] float reduction scratch
+  T* stg = reinterpret_cast<T*>(smc);
+  float* tmp = smc;
+  float* dks = reinterpret_cast<float*>(reinterpret_cast<char*>(smc) + col_stage_bytes<T>(d, S));
   float* dbs = dks + G * d;                          // [G]
-  float* tmp = dbs + G;                              // [S][d] reduction scratch
-  float* red = tmp + S * d;                          // [8]
+  float* red = dbs + G;                              // [8]
   int* di = reinterpret_cast<int*>(red + 8);         // [CBATCH] query << 4 | head, window flag << 31
   float* dsx = reinterpret_cast<float*>(di + CBATCH);   // [CBATCH][4] alpha, lse, g, window term
   const T* kb = k + (bg * (long long)N + j0) * d;
@@ -665,16 +681,39 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
       }
     }
     __syncthreads();
-    // software pipeline: q and dout slices of contribution u + 1 load while u is applied
-    float qa[CE], da[CE], qb2[CE], db2[CE];
-    auto fetch = [&](int u, float* qv, float* dv2) {
-      const int dd = di[u];
-      const int i = (dd >> 4) & 0x7ffffff, r = dd & 15;
-      const long long o = ((hb + r) * N + i) * (long long)d + e0;
-      load_slice16<T>(q + o, DQ, qv);
-      load_slice16<T>(dout + o, DQ, dv2);
+    // the rows of sub-batch sb (NB contributions) are loaded into registers
+    // while sub-batch sb - 1 is applied from LDS, then stored to the other
+    // buffer.  Thread tid takes 16-byte piece tid % prow of contribution
+    // tid / prow from each of the three rows (NB * prow <= CT: d <= 128).
+    constexpr int VE = 16 / (int)sizeof(T);          // elements per 16-byte piece
+    const int prow = d / VE;                         // pieces per row
+    const int sul = tid / prow, spart = tid - sul * prow;
+    const bool stager = sul < NB;
+    uint4 pv0 = make_uint4(0u, 0u, 0u, 0u), pv1 = pv0, pv2 = pv0;
+    auto stage_load = [&](int sb) __attribute__((always_inline)) {
+      const int u = sb * NB + sul;
+      if (stager && u < nb) {
+        const int dd = di[u];
+        const int i = (dd >> 4) & 0x7ffffff, r = dd & 15;
+        const long long o = ((hb + r) * N + i) * (long long)d + spart * VE;
+        pv0 = *reinterpret_cast<const uint4*>(q + o);
+        pv1 = *reinterpret_cast<const uint4*>(dout + o);
+        pv2 = *reinterpret_cast<const uint4*>(qr + o);
+      }
     };
-    auto apply = [&](int u, const float* qv, const float* dv2) {
+    auto stage_store = [&](int buf) __attribute__((always_inline)) {
+      if (stager) {
+        T* base = stg + ((size_t)buf * 3 * NB + sul) * d + spart * VE;
+        *reinterpret_cast<uint4*>(base) = pv0;
+        *reinterpret_cast<uint4*>(base + (size_t)NB * d) = pv1;
+        *reinterpret_cast<uint4*>(base + (size_t)2 * NB * d) = pv2;
+      }
+    };
+    auto apply = [&](int u, int buf) __attribute__((always_inline)) {
+      const int ul = u % NB;
+      float qv[CE], dv2[CE];
+      load_slice16<T>(stg + (((size_t)buf * 3 + 0) * NB + ul) * d + e0, DQ, qv);
+      load_slice16<T>(stg + (((size_t)buf * 3 + 1) * NB + ul) * d + e0, DQ, dv2);
       const int dd = di[u];
       const bool window = dd < 0;
       const int i = (dd >> 4) & 0x7ffffff, r = dd & 15;
@@ -706,22 +745,26 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
       // dk' += tau d s_hat q_hat, db' += d s_hat: threads of token r own head r
       if (!window && jt == r) {
         float hv[CE];
-        load_slice16<T>(qr + ((hb + r) * N + i) * (long long)d + e0, DQ, hv);
+        load_slice16<T>(stg + (((size_t)buf * 3 + 2) * NB + ul) * d + e0, DQ, hv);
 #pragma unroll
         for (int x = 0; x < CE; ++x)
           if (x < DQ) dks[r * d + e0 + x] = fmaf(tau * xt, hv[x], dks[r * d + e0 + x]);
         if (qd == 0) dbs[r] += xt;
       }
     };
-    if (nb > 0) fetch(0, qa, da);
-    int u = 0;
-    for (; u + 1 < nb; u += 2) {
-      fetch(u + 1, qb2, db2);
-      apply(u, qa, da);
-      if (u + 2 < nb) fetch(u + 2, qa, da);
-      apply(u + 1, qb2, db2);
+    const int nsb = (nb + NB - 1) / NB;
+    stage_load(0);
+    stage_store(0);
+    __syncthreads();
+    for (int sb = 0; sb < nsb; ++sb) {
+      if (sb + 1 < nsb) stage_load(sb + 1);
+      const int ue = min(nb, (sb + 1) * NB);
+      for (int u = sb * NB; u < ue; ++u) apply(u, sb & 1);
+      // buffer (sb + 1) & 1 was last read in sub-batch sb - 1, before the
+      // barrier that ended it
+      if (sb + 1 < nsb) stage_store((sb + 1) & 1);
+      __syncthreads();
     }
-    if (u < nb) apply(u, qa, da);
   }
   __syncthreads();
   // summaries of the chunk (one per query head of the group)
@@ -814,7 +857,8 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
   // the all-keys row kernel when every attended key's logit fits 64 KB of LDS
   const bool all_keys = bwd_rows2_lds(s) <= 65536;
   const size_t rshm = all_keys ? bwd_rows2_lds(s) : hils_bwd_rows_lds(s);
-  const size_t cshm = sizeof(float) * ((size_t)s.G * s.d + s.G + (size_t)s.S * s.d + 8) +
+  const size_t cshm = (s.dtype == 0 ? col_stage_bytes<bf16_t>(s.d, s.S) : col_stage_bytes<float>(s.d, s.S)) +
+                      sizeof(float) * ((size_t)s.G * s.d + s.G + 8) +
                       (size_t)CBATCH * (sizeof(int) + 4 * sizeof(float));
   const int sep = dqr != nullptr;
   if (s.dtype == 0) {

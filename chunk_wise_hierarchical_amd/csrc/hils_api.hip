@@ -148,8 +148,9 @@ BwdLayout bwd_layout(const HilsShape& s) {
 // shapes the backward kernels take
 hils_status bwd_supported(const HilsShape& s) {
   if (s.mode == HILS_SCORE_EXACT) return HILS_E_UNSUPPORTED;
-  // per-thread quarter rows are read with 16-byte vectors
-  if (s.d > 128 || s.d % (s.dtype == HILS_BF16 ? 32 : 16) != 0) return HILS_E_UNSUPPORTED;
+  // the column pass gives each thread d / 8 elements of a row, read as whole
+  // 16-byte vectors (8 bf16 or 4 fp32 elements)
+  if (s.d > 128 || s.d % (s.dtype == HILS_BF16 ? 64 : 32) != 0) return HILS_E_UNSUPPORTED;
   if (s.S > 64 || s.G > 8 || s.K > 128) return HILS_E_UNSUPPORTED;
   if (s.N >= (1 << 24)) return HILS_E_UNSUPPORTED;
   if ((long long)s.B * s.Hkv * s.N * s.K >= (1LL << 31)) return HILS_E_UNSUPPORTED;

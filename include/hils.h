@@ -197,7 +197,7 @@ hils_status hils_decode_paged(const hils_cfg* cfg, const void* q, const void* q_
  *                     then gets only the attention part);
  *   dlm             : fp32 [B][Hq][N/S][d] (may be NULL in MEAN_POOL mode).
  * The kernels use no atomics, so results are deterministic.  Supports d <= 128
- * (a multiple of 32 for bf16, of 16 for fp32), S <= 64, G <= 8, K <= 128 and
+ * (a multiple of 64 for bf16, of 32 for fp32), S <= 64, G <= 8, K <= 128 and
  * windows whose G head rows of logits fit in LDS (otherwise
  * HILS_E_UNSUPPORTED, and hils_prefill_backward_workspace_bytes returns 0).
  */

@@ -153,6 +153,15 @@ def test_multi_decode_arguments_and_workspace(L):
     assert L.hils_decode_multi_workspace_bytes(ctypes.byref(c), 17) == 0
 
 
+def test_backward_head_dim_granularity(L):
+    # the column pass reads each thread's d / 8 elements as whole 16-byte vectors
+    ok = L.hils_prefill_backward_workspace_bytes
+    assert ok(ctypes.byref(_cfg(d=128))) > 0 and ok(ctypes.byref(_cfg(d=64))) > 0
+    assert ok(ctypes.byref(_cfg(d=32))) == 0                       # bf16: d % 64
+    assert ok(ctypes.byref(_cfg(d=32, dtype=1))) > 0               # fp32: d % 32
+    assert ok(ctypes.byref(_cfg(d=16, dtype=1))) == 0
+
+
 def test_decode_rejects_batches_beyond_the_scoring_grid(L):
     # the decode scoring grid holds (sequence, query head) in its y dimension:
     # B * Hq = 8192 * 8 is one past its limit of 65535
