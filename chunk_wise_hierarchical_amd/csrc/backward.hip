@@ -25,7 +25,7 @@
 //                 chunk's tokens over the queries that selected the chunk and
 //                 the queries whose window holds it, then back-propagate the
 //                 chunk's summaries into dlm and dk.
-#include "hils_device.h"
+#include "fast_common.h"
 #include "hils_internal.h"
 #include "hils_bwd.h"
 
@@ -723,13 +723,13 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
         a = fmaf(qv[x], kj[x], a);
         u2 = fmaf(dv2[x], vj[x], u2);
       }
-      // the 8 lanes of a token hold its 8 slices
-      a += __shfl_xor(a, 1, 64);
-      a += __shfl_xor(a, 2, 64);
-      a += __shfl_xor(a, 4, 64);
-      u2 += __shfl_xor(u2, 1, 64);
-      u2 += __shfl_xor(u2, 2, 64);
-      u2 += __shfl_xor(u2, 4, 64);
+      // the 8 lanes of a token hold its 8 slices (DPP, within one row)
+      a += fastp::xshfl_f(a, 1);
+      u2 += fastp::xshfl_f(u2, 1);
+      a += fastp::xshfl_f(a, 2);
+      u2 += fastp::xshfl_f(u2, 2);
+      a += fastp::xshfl_f(a, 4);
+      u2 += fastp::xshfl_f(u2, 4);
       const float alpha = dsx[u * 4], lse = dsx[u * 4 + 1], gq = dsx[u * 4 + 2], xt = dsx[u * 4 + 3];
       const int j = j0 + jt;
       bool ok = act;
