@@ -383,6 +383,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--union", action="store_true",
+                    help="prefill attention by query block over the union of its chunks "
+                         "instead of the default per-chunk buckets")
     ap.add_argument("--backward-workload", default="prefill_8k",
                     help="workload of the backward measurement ('' skips it)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -414,11 +417,12 @@ def main():
     x = synth.make_prefill_inputs(w, device=dev)
     out = torch.empty_like(x["q"])
     sel = torch.empty((w.B, w.Hkv, w.N, w.K), dtype=torch.int32, device=dev)
-    cfg = hils.make_cfg(w.B, w.N, w.Hq, w.Hkv, w.d, w.S, w.W, w.K, x["q"].dtype)
+    cfg = hils.make_cfg(w.B, w.N, w.Hq, w.Hkv, w.d, w.S, w.W, w.K, x["q"].dtype, union=args.union)
     ws = torch.empty(max(1, hils.workspace_bytes(cfg, False)), dtype=torch.uint8, device=dev)
 
     def step():
-        hils.prefill(x["q"], x["k"], x["v"], x["lm"], w.S, w.W, w.K, out=out, sel=sel, ws=ws)
+        hils.prefill(x["q"], x["k"], x["v"], x["lm"], w.S, w.W, w.K, out=out, sel=sel, ws=ws,
+                     union=args.union)
 
     for _ in range(args.warmup):
         step()
@@ -549,6 +553,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
                    "S": w.S, "W": w.W, "K": w.K, "regime": w.regime,
+                   "attention": "query-block unions" if args.union else "chunk buckets",
                    "chunk_overlap_M16": sel_cpu_overlap},
         "useful_tflops_total": total_tflops,
         "algorithmic_tflop": {"scoring": score_f / 1e12, "summaries": summ_f / 1e12,
