@@ -35,14 +35,17 @@ using namespace fastp;
 namespace {
 
 // Streaming (non-temporal) access to the per-pair outputs, which are written
-// once and read once.  The bf16 partial rows are stored normally (whole
-// lines, which L2 combines before writing back), the scattered 4-byte
-// fusion logits and the reduction's reads non-temporally, so that neither
-// displaces cached query rows and K/V.
+// once and read once: the bf16 partial rows (whole 128-byte lines per store
+// instruction), the scattered 4-byte fusion logits and the reduction's reads,
+// so that none of them displaces cached query rows and K/V.
 typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_u4_nt(const void* p) {
   nt_u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
   return make_uint4(w.x, w.y, w.z, w.w);
+}
+__device__ __forceinline__ void st_u4_nt(void* p, uint4 v) {
+  const nt_u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<nt_u32x4*>(p));
 }
 
 constexpr int NT = 256;
@@ -52,6 +55,7 @@ constexpr int PQ = 512;       // queries per list-building workgroup
 constexpr int RQ = 16;        // queries per reduce workgroup
 constexpr int RU = 8;         // partial rows in flight per reduce thread
 constexpr int PTPW = HILS_PAIR_TPW;   // tiles per pair-attention workgroup
+constexpr int OSTR = 17;      // output patch row stride (16-byte pieces; one of padding)
 
 __device__ __forceinline__ int kswz(int r, int p) { return p ^ (((r >> 1) & 12) | (r & 3)); }
 
@@ -397,6 +401,7 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
   bf16_t* kstile = reinterpret_cast<bf16_t*>(sm + KT_BYTES + VT_BYTES);   // [G][D] k'_c
   __shared__ float bst[G];
   __shared__ uint2 tl[PTPW];
+  __shared__ uint4 ostg[4 * 16 * OSTR];   // per wavefront: 16 output rows
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint32_t T = tot[1];
   const uint32_t t0 = (uint32_t)blockIdx.x * PTPW;
@@ -552,20 +557,35 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
         acc[dt] = mfma16(ld_bf16x8(vtile + (16 * dt + (lane & 15)) * VSTR + 32 * kb + 8 * lq),
                          pb[kb], acc[dt]);
     }
-    if (valid) {
-      // stored in the MFMA output order: 16-byte piece 4j + lq holds elements
-      // 32j + 4lq + {0..3} and 32j + 16 + 4lq + {0..3}, so each lane writes
-      // 16 bytes and the 4 lanes of a row write 64 contiguous bytes
-      bf16_t* op = part + (prow * G + h) * D;
+    {
+      // Each lane holds a 64-byte slice of its row (piece 4j + lq holds
+      // elements 32j + 4lq + {0..3} and 32j + 16 + 4lq + {0..3}).  The rows go
+      // through the wavefront's LDS patch so that every store instruction
+      // writes whole 128-byte lines: 8 lanes per line, two rows per 8-lane
+      // group.  Whole-line non-temporal stores neither split lines nor push
+      // reused query rows and K/V out of the caches.
+      uint4* ow = ostg + w * (16 * OSTR);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint4 uu = make_uint4(pack_bf16x2(acc[2 * j][0], acc[2 * j][1]),
                                     pack_bf16x2(acc[2 * j][2], acc[2 * j][3]),
                                     pack_bf16x2(acc[2 * j + 1][0], acc[2 * j + 1][1]),
                                     pack_bf16x2(acc[2 * j + 1][2], acc[2 * j + 1][3]));
-        st_u4(op + 8 * (4 * j + lq), uu);
+        ow[(lane & 15) * OSTR + 4 * j + lq] = uu;
       }
-      if (lq == 0) __builtin_nontemporal_store(lam, lamb + prow * G + h);
+      if (valid && lq == 0) __builtin_nontemporal_store(lam, lamb + prow * G + h);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const int rp = lane >> 3, sl = lane & 7;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 2 * rp + (i >> 1);                  // row of this store
+        const uint32_t er = (uint32_t)__shfl((int)e0, rr);  // its list entry
+        const int cr = 16 * w + rr, jrr = cr / G, hr = cr % G;
+        const long long pr = ((long long)bg * qs + (int)(er >> 7)) * K + (int)(er & 127u);
+        const uint4 uu = ow[rr * OSTR + 8 * (i & 1) + sl];
+        if (jrr < mcount) st_u4_nt(part + (pr * G + hr) * D + 8 * (8 * (i & 1) + sl), uu);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // patch reads before the next tile's writes
     }
     e0 = e1;
     e1 = e2;
