@@ -55,6 +55,7 @@ constexpr int PQ = 512;       // queries per list-building workgroup
 constexpr int RQ = 16;        // queries per reduce workgroup
 constexpr int RU = 8;         // partial rows in flight per reduce thread
 constexpr int PTPW = HILS_PAIR_TPW;   // tiles per pair-attention workgroup
+constexpr int KSS = D + 8;    // k'_c row stride in LDS (elements)
 constexpr int OSTR = 17;      // output patch row stride (16-byte pieces; one of padding)
 
 __device__ __forceinline__ int kswz(int r, int p) { return p ^ (((r >> 1) & 12) | (r & 3)); }
@@ -398,7 +399,7 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
   extern __shared__ __align__(16) unsigned char sm[];
   bf16_t* ktile = reinterpret_cast<bf16_t*>(sm);
   bf16_t* vtile = reinterpret_cast<bf16_t*>(sm + KT_BYTES);
-  bf16_t* kstile = reinterpret_cast<bf16_t*>(sm + KT_BYTES + VT_BYTES);   // [G][D] k'_c
+  bf16_t* kstile = reinterpret_cast<bf16_t*>(sm + KT_BYTES + VT_BYTES);   // [G + 1][KSS] k'_c, zero row
   __shared__ float bst[G];
   __shared__ uint2 tl[PTPW];
   __shared__ uint4 ostg[4 * 16 * OSTR];   // per wavefront: 16 output rows
@@ -408,6 +409,7 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
   if (t0 >= T) return;
   const int nt = (int)min((uint32_t)PTPW, T - t0);
   if (tid < nt) tl[tid] = tinfo[t0 + tid];
+  if (tid < 16) st_u4(kstile + G * KSS + tid * 8, make_uint4(0, 0, 0, 0));
   __syncthreads();
   const int colr = 16 * w + (lane & 15);
   const int jr = colr / G, h = colr % G;
@@ -441,6 +443,9 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
     load_q(qr, qrow(e1, 1), br1);
   }
   int cur = -1;
+  // A operand of the fusion logits: rows 0..G-1 the group's k'_c, the other
+  // rows read the zero row G
+  const bf16_t* kar = kstile + min(lane & 15, G) * KSS + 8 * lq;
   for (int u = 0; u < nt; ++u) {
     const uint2 ti = tl[u];
     const int f = (int)(ti.x >> 7), mcount = (int)(ti.x & 127u);
@@ -480,7 +485,7 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
         const int piece = tid + NT * p, row = piece / 8, pt = piece % 8;
         st_u4(vtile + row * VSTR + pt * 8, r[4 + p]);
       }
-      if (tid < G * 16) st_u4(kstile + tid * 8, rk);
+      if (tid < G * 16) st_u4(kstile + (tid / 16) * KSS + (tid % 16) * 8, rk);
       if (tid < G) bst[tid] = rb;
       __syncthreads();
       cur = f;
@@ -489,24 +494,17 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
     const int qi = (int)(e0 >> 7), kx = (int)(e0 & 127u);
     const long long prow = ((long long)bg * qs + qi) * K + kx;   // pair index
 
-    // fusion logit of the row (base 2): the 4 lanes of a row each hold 32 of
-    // its 128 query elements
+    // fusion logit of the row (base 2) on the matrix cores: output element
+    // (h', row) of k'·q^T is the dot product of head h' with the row's query,
+    // and the row's own head h < 4 sits in element h of its lq = 0 lane
     float lam;
     {
       const bf16x8_t* src = QR ? br0 : bq0;
-      float dp = 0.0f;
+      f32x4_t a5 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 a = __builtin_bit_cast(uint4, src[ks]);
-        const uint4 kb = ld_u4(kstile + h * D + 32 * ks + 8 * lq);
-        const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {kb.x, kb.y, kb.z, kb.w};
-#pragma unroll
-        for (int t2 = 0; t2 < 4; ++t2) {
-          dp = fmaf(__uint_as_float(av[t2] << 16), __uint_as_float(bv[t2] << 16), dp);
-          dp = fmaf(__uint_as_float(av[t2] & 0xffff0000u), __uint_as_float(bv[t2] & 0xffff0000u), dp);
-        }
-      }
-      dp = sum_x32(sum_x16(dp));
+      for (int ks = 0; ks < 4; ++ks) a5 = mfma16(ld_bf16x8(kar + 32 * ks), src[ks], a5);
+      const float d01 = (h & 1) ? a5[1] : a5[0], d23 = (h & 1) ? a5[3] : a5[2];
+      const float dp = (h & 2) ? d23 : d01;
       lam = fmaf(dp, tau2, bst[h] * LOG2E);
     }
 
@@ -521,23 +519,25 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
         a4 = mfma16(ld_bf16x8(ktile + key * KSTR + kswz(key, 4 * ks + lq) * 8), bq0[ks], a4);
       s4[kt] = a4;
     }
-    float mt = -INFINITY;
+    // every key of a selected chunk is visible: no mask.  The maximum is taken
+    // on the raw products (the scale is positive) and scaled once.
+    float mr = s4[0][0];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s4[kt][e] * tau2);
-    mt = max_x32(max_x16(mt));
+      for (int e = 0; e < 4; ++e) mr = fmaxf(mr, s4[kt][e]);
+    const float nmt = -max_x32(max_x16(mr)) * tau2;
     float p[16];
     float ps = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        p[kt * 4 + e] = fast_exp2(s4[kt][e] * tau2 - mt);
+        p[kt * 4 + e] = fast_exp2(fmaf(s4[kt][e], tau2, nmt));
         ps += p[kt * 4 + e];
       }
     ps = sum_x32(sum_x16(ps));
-    const float coef = 1.0f / ps;
+    const float coef = __builtin_amdgcn_rcpf(ps);   // ps >= 1; the weights are rounded to bf16
     bf16x8_t pb[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -577,13 +577,17 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       const int rp = lane >> 3, sl = lane & 7;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rr = 2 * rp + (i >> 1);                  // row of this store
+      for (int i = 0; i < 2; ++i) {
+        const int rr = 2 * rp + i;                          // row of these two stores
         const uint32_t er = (uint32_t)__shfl((int)e0, rr);  // its list entry
         const int cr = 16 * w + rr, jrr = cr / G, hr = cr % G;
         const long long pr = ((long long)bg * qs + (int)(er >> 7)) * K + (int)(er & 127u);
-        const uint4 uu = ow[rr * OSTR + 8 * (i & 1) + sl];
-        if (jrr < mcount) st_u4_nt(part + (pr * G + hr) * D + 8 * (8 * (i & 1) + sl), uu);
+        const uint4 u0 = ow[rr * OSTR + sl], u1 = ow[rr * OSTR + 8 + sl];
+        if (jrr < mcount) {
+          bf16_t* dst = part + (pr * G + hr) * D + 8 * sl;
+          st_u4_nt(dst, u0);
+          st_u4_nt(dst + 64, u1);
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // patch reads before the next tile's writes
     }
@@ -700,7 +704,7 @@ hipError_t launch_pairs(const HilsShape& s, const void* q, const void* qr, const
   const float tau2 = (float)(s.tau * 1.4426950408889634);
   const size_t hshm = (size_t)(s.nC > 0 ? s.nC : 1) * 4;
   const size_t wshm = KT_BYTES + VT_BYTES;
-  const size_t ashm = KT_BYTES + VT_BYTES + (size_t)G * D * 2;
+  const size_t ashm = KT_BYTES + VT_BYTES + (size_t)(G + 1) * KSS * 2;
   const size_t rshm = (size_t)RQ * G * (s.K + 1) * 4;
   hipFuncSetAttribute((const void*)k_pair_count, hipFuncAttributeMaxDynamicSharedMemorySize, (int)hshm);
   hipFuncSetAttribute((const void*)k_pair_scatter, hipFuncAttributeMaxDynamicSharedMemorySize, (int)hshm);
