@@ -13,7 +13,7 @@
 // chunk's K/V for almost every query.  Here the pairs of a slice of queries are
 // bucketed by chunk instead, so each chunk's K/V is staged in LDS once per
 // slice and every pair that selected it is computed against it:
-//   1. k_pair_count / k_pair_scan / k_pair_tiles / k_pair_scatter: counting
+//   1. k_pair_count / k_pair_bsum / k_pair_scan / k_pair_tiles / k_pair_scatter: counting
 //      sort of the slice's (query, slot) pairs by (KV group, chunk), cut into
 //      tiles of 64/G pairs (64 MFMA rows with the G heads of a group);
 //   2. k_win_fast: window attention (online softmax over the window tiles);
@@ -55,6 +55,7 @@ constexpr int PQ = 512;       // queries per list-building workgroup
 constexpr int RQ = 16;        // queries per reduce workgroup
 constexpr int RU = 8;         // partial rows in flight per reduce thread
 constexpr int PTPW = HILS_PAIR_TPW;   // tiles per pair-attention workgroup
+constexpr int SB = HILS_PAIR_SB;      // buckets per scan workgroup
 constexpr int KSS = D + 8;    // k'_c row stride in LDS (elements)
 constexpr int OSTR = 17;      // output patch row stride (16-byte pieces; one of padding)
 
@@ -102,41 +103,81 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v, int lane) {
   return v;
 }
 
-// one workgroup: exclusive prefix sums over f = bg*nC + c of the bucket sizes
-// (list offsets, also the scatter cursors) and of their tile counts;
-// tot[0] = pairs, tot[1] = tiles
-__global__ void __launch_bounds__(1024)
-k_pair_scan(const uint32_t* __restrict__ cnt, uint32_t* __restrict__ loff,
+// per scan workgroup (SB buckets): number of pairs and of tiles
+__global__ void __launch_bounds__(NT)
+k_pair_bsum(const uint32_t* __restrict__ cnt, uint32_t* __restrict__ bsa,
+            uint32_t* __restrict__ bsb, int F, int TQ) {
+  __shared__ uint32_t sa, sb;
+  if (threadIdx.x == 0) { sa = 0; sb = 0; }
+  __syncthreads();
+  const long long f0 = (long long)blockIdx.x * SB;
+  uint32_t a = 0, b = 0;
+  for (int t = threadIdx.x; t < SB; t += NT) {
+    const long long f = f0 + t;
+    if (f < F) {
+      const uint32_t n = cnt[f];
+      a += n;
+      b += (n + (uint32_t)TQ - 1u) / (uint32_t)TQ;
+    }
+  }
+  atomicAdd(&sa, a);
+  atomicAdd(&sb, b);
+  __syncthreads();
+  if (threadIdx.x == 0) { bsa[blockIdx.x] = sa; bsb[blockIdx.x] = sb; }
+}
+
+// exclusive prefix sums over the buckets f = bg * nC + c of the bucket
+// sizes (list offsets, also the scatter cursors) and of their tile counts;
+// each workgroup adds up the totals of the workgroups before it, then scans
+// its SB buckets, 16 consecutive ones per thread.  The last workgroup writes
+// tot[0] = pairs, tot[1] = tiles.
+__global__ void __launch_bounds__(NT)
+k_pair_scan(const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ bsa,
+            const uint32_t* __restrict__ bsb, uint32_t* __restrict__ loff,
             uint32_t* __restrict__ toff, uint32_t* __restrict__ cur, uint32_t* __restrict__ tot,
             int F, int TQ) {
-  __shared__ uint32_t wa[16], wb[16];
+  static_assert(SB == 16 * NT, "16 buckets per thread");
+  __shared__ uint32_t wa[NT / 64], wb[NT / 64], ba, bb;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  uint32_t run_a = 0, run_b = 0;
-  for (int base = 0; base < F; base += 1024) {
-    const int f = base + tid;
-    const uint32_t a = (f < F) ? cnt[f] : 0u;
-    const uint32_t b = (a + (uint32_t)TQ - 1u) / (uint32_t)TQ;
-    const uint32_t ia = wave_incl_scan_u32(a, lane), ib = wave_incl_scan_u32(b, lane);
-    if (lane == 63) { wa[w] = ia; wb[w] = ib; }
-    __syncthreads();
-    uint32_t pa = 0, pb = 0, ta = 0, tb = 0;
-    for (int u = 0; u < 16; ++u) {
-      const uint32_t x = wa[u], y = wb[u];
-      if (u < w) { pa += x; pb += y; }
-      ta += x;
-      tb += y;
-    }
-    if (f < F) {
-      const uint32_t la = run_a + pa + ia - a;
-      loff[f] = la;
-      cur[f] = la;
-      toff[f] = run_b + pb + ib - b;
-    }
-    run_a += ta;
-    run_b += tb;
-    __syncthreads();
+  if (tid == 0) { ba = 0; bb = 0; }
+  __syncthreads();
+  {
+    uint32_t a = 0, b = 0;
+    for (int i = tid; i < (int)blockIdx.x; i += NT) { a += bsa[i]; b += bsb[i]; }
+    atomicAdd(&ba, a);
+    atomicAdd(&bb, b);
   }
-  if (tid == 0) { tot[0] = run_a; tot[1] = run_b; }
+  const long long f0 = (long long)blockIdx.x * SB + 16 * tid;
+  uint32_t na[16], ta = 0, tb = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    na[e] = (f0 + e < F) ? cnt[f0 + e] : 0u;
+    ta += na[e];
+    tb += (na[e] + (uint32_t)TQ - 1u) / (uint32_t)TQ;
+  }
+  const uint32_t ia = wave_incl_scan_u32(ta, lane), ib = wave_incl_scan_u32(tb, lane);
+  if (lane == 63) { wa[w] = ia; wb[w] = ib; }
+  __syncthreads();
+  uint32_t pa = ba, pb = bb, sa = 0, sb2 = 0;
+#pragma unroll
+  for (int u = 0; u < NT / 64; ++u) {
+    if (u < w) { pa += wa[u]; pb += wb[u]; }
+    sa += wa[u];
+    sb2 += wb[u];
+  }
+  pa += ia - ta;
+  pb += ib - tb;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    if (f0 + e < F) {
+      loff[f0 + e] = pa;
+      cur[f0 + e] = pa;
+      toff[f0 + e] = pb;
+    }
+    pa += na[e];
+    pb += (na[e] + (uint32_t)TQ - 1u) / (uint32_t)TQ;
+  }
+  if (blockIdx.x == gridDim.x - 1 && tid == 0) { tot[0] = ba + sa; tot[1] = bb + sb2; }
 }
 
 // tile t of bucket f: {f << 7 | pairs in the tile, first list position}
@@ -714,6 +755,7 @@ hipError_t launch_pairs(const HilsShape& s, const void* q, const void* qr, const
   hipFuncSetAttribute((const void*)k_pair_reduce<G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rshm);
   const bf16_t* qb = (const bf16_t*)q;
   const bf16_t* qrb = (qr == q) ? nullptr : (const bf16_t*)qr;
+  const int nsb = (F + SB - 1) / SB;        // scan workgroups
   for (int i0 = 0; i0 < s.N; i0 += pb.qs_max) {
     const int qs = min(pb.qs_max, s.N - i0);
     const int nqb = (qs + QA - 1) / QA;
@@ -723,8 +765,10 @@ hipError_t launch_pairs(const HilsShape& s, const void* q, const void* qr, const
                            pb.cnt, (long long)F, 0u);
         hipLaunchKernelGGL(k_pair_count, dim3(s.B * s.Hkv, (qs + PQ - 1) / PQ), dim3(NT), hshm, st,
                            sel, pb.cnt, s.N, s.K, s.nC, i0, qs);
-        hipLaunchKernelGGL(k_pair_scan, dim3(1), dim3(1024), 0, st, pb.cnt, pb.loff, pb.toff, pb.cur,
-                           pb.tot, F, TQ);
+        hipLaunchKernelGGL(k_pair_bsum, dim3(nsb), dim3(NT), 0, st, pb.cnt, pb.bsum, pb.bsum + nsb,
+                           F, TQ);
+        hipLaunchKernelGGL(k_pair_scan, dim3(nsb), dim3(NT), 0, st, pb.cnt, pb.bsum, pb.bsum + nsb,
+                           pb.loff, pb.toff, pb.cur, pb.tot, F, TQ);
         hipLaunchKernelGGL(k_pair_tiles, dim3((F + NT - 1) / NT), dim3(NT), 0, st, pb.cnt, pb.loff,
                            pb.toff, pb.tinfo, F, TQ);
         hipLaunchKernelGGL(k_pair_scatter, dim3(s.B * s.Hkv, (qs + PQ - 1) / PQ), dim3(NT), hshm, st,

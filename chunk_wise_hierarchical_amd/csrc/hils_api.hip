@@ -69,7 +69,7 @@ inline bool pair_path(const HilsShape& s, uint32_t flags, bool fast) {
 struct PrefillLayout {
   size_t ks, bs, sel, slog, vt, kf, total;
   // per-chunk bucket path
-  size_t cnt, loff, toff, cur, tot, tinfo, list, lam, swa, lz, part;
+  size_t cnt, loff, toff, cur, tot, bsum, tinfo, list, lam, swa, lz, part;
   int qs_max;
 };
 // generic path: summaries, selection, fusion logits; fast path: summaries,
@@ -95,6 +95,7 @@ PrefillLayout prefill_layout(const HilsShape& s, bool fast, bool pairs) {
       L.toff = off;  off += align_up(F * 4);
       L.cur = off;   off += align_up(F * 4);
       L.tot = off;   off += align_up(16);
+      L.bsum = off;  off += align_up((F + HILS_PAIR_SB - 1) / HILS_PAIR_SB * 8);
       L.tinfo = off; off += align_up((size_t)hils_pair_tiles_max(s, qs) * 8);
       L.list = off;  off += align_up(P * 4);
       L.lam = off;   off += align_up(P * s.G * 4);
@@ -311,6 +312,7 @@ hils_status hils_prefill(const hils_cfg* cfg, const void* q, const void* q_route
     pb.toff = (uint32_t*)(w + L.toff);
     pb.cur = (uint32_t*)(w + L.cur);
     pb.tot = (uint32_t*)(w + L.tot);
+    pb.bsum = (uint32_t*)(w + L.bsum);
     pb.tinfo = (uint2*)(w + L.tinfo);
     pb.list = (uint32_t*)(w + L.list);
     pb.lam = (float*)(w + L.lam);

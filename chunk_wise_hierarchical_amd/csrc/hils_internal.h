@@ -49,6 +49,7 @@ size_t hils_fast_score_lds(int G, int K);
 // one slice of at most qs_max queries (workspace):
 struct HilsPairBufs {
   uint32_t *cnt, *loff, *toff, *cur, *tot;  // [B*Hkv*nC] x4, [4]
+  uint32_t* bsum;                           // [2 * ceil(B*Hkv*nC / HILS_PAIR_SB)]
   uint2* tinfo;                             // [hils_pair_tiles_max]
   uint32_t* list;                           // [B*Hkv*qs_max*K]
   float* lam;                               // [B*Hkv*qs_max*K*G] fusion logits (base 2)
@@ -59,6 +60,7 @@ struct HilsPairBufs {
 };
 constexpr int HILS_PAIR_SLICE = 32768;      // queries per slice
 constexpr int HILS_PAIR_TPW = 16;           // tiles per attention workgroup
+constexpr int HILS_PAIR_SB = 4096;          // buckets per scan workgroup
 long long hils_pair_tiles_max(const HilsShape& s, int qs);
 hipError_t hils_launch_attn_pairs(const HilsShape& s, const void* q, const void* qr, const void* k,
                                   const void* vt, const void* ksum, const float* bsum,

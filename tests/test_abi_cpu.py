@@ -60,11 +60,11 @@ def test_workspace_bytes(L):
         + (1 * 8 * 1 * 9 * 1024)
     assert base <= n <= base + 5 * 256
     # default per-chunk buckets add, for one slice of 1024 queries (G=4, 16 pairs a tile):
-    # 4 bucket arrays, totals, tile table, pair list, pair fusion logits, fp32 window output
-    # and log-mass, bf16 per-chunk outputs
+    # 4 bucket arrays, totals, scan-block totals, tile table, pair list, pair fusion
+    # logits, fp32 window output and log-mass, bf16 per-chunk outputs
     n = L.hils_workspace_bytes(ctypes.byref(_cfg()), 0)
     F, P = 2 * 16, 2 * 1024 * 8
-    want = base + 4 * F * 4 + 16 + (P // 16 + F) * 8 + P * 4 + P * 4 * 4 + 2 * 1024 * 4 * 128 * 4 \
+    want = base + 4 * F * 4 + 16 + 8 + (P // 16 + F) * 8 + P * 4 + P * 4 * 4 + 2 * 1024 * 4 * 128 * 4 \
         + 2 * 1024 * 4 * 4 + P * 4 * 128 * 2
     assert want <= n <= want + 16 * 256
     assert L.hils_workspace_bytes(ctypes.byref(_cfg()), 1) > 0
