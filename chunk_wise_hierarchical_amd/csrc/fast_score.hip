@@ -300,10 +300,10 @@ k_score_fast(const bf16_t* __restrict__ qr, const uint4* __restrict__ frag,
   // 2): x[i] <-> chunk 32t + 8(i>>2) + 4*half + (i&3).  The ninth MFMA adds the
   // bias b' / tau2 of each chunk.
   const int n_lo = n_cand(i0, W, S);                 // every query of the block has >= n_lo
-  auto tile_scores = [&](const uint4 (&f)[FRAGS], int t, float* x) {
+  auto tile_scores = [&](const uint4 (&f)[FRAGS], int t, float* x, float a0) {
     f32x16_t acc;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    for (int i = 0; i < 16; ++i) acc[i] = a0;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) acc = mfma32(__builtin_bit_cast(bf16x8_t, f[ks]), bq[ks], acc);
     acc = mfma32(__builtin_bit_cast(bf16x8_t, f[8]), bones, acc);
@@ -332,43 +332,53 @@ k_score_fast(const bf16_t* __restrict__ qr, const uint4* __restrict__ frag,
     // pass 1 subtracts the head's log-sum-exp (L = -inf only for rows without
     // candidates, whose scores are all masked)
     const float nL = (L2 > -INFINITY) ? -L2 : 0.0f;
-    // one tile step: cur holds the fragments of tile t, nxt receives tile t + 1
-    // (past the last tile: the last again, unused)
+    // pass 0 takes the tiles in pairs: every register slot's trackers absorb
+    // the larger of the pair's two scores (one chunk's score, so a slot's
+    // tracked entries still belong to distinct chunks), and the log-sum-exp
+    // takes both tiles against one running maximum
+    auto absorb2 = [&](const float* xa, const float* xc) __attribute__((always_inline)) {
+      float hi[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        hi[i] = fmaxf(xa[i], xc[i]);
+        // insert hi into t0 >= t1 >= t2: each new entry is the median of its
+        // old neighbours above and below and hi
+        t2[i] = __builtin_amdgcn_fmed3f(t1[i], t2[i], hi[i]);
+        t1[i] = __builtin_amdgcn_fmed3f(t0[i], t1[i], hi[i]);
+        t0[i] = fmaxf(t0[i], hi[i]);
+      }
+      if (G > 1) {
+        // online log-sum-exp; m is the running maximum in accumulator units
+        float mt = hi[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mt = fmaxf(mt, hi[i]);
+        if (mt > m) { ssum = (m == -INFINITY) ? 0.0f : ssum * fast_exp2((m - mt) * tau2); m = mt; }
+        if (m != -INFINITY) {
+          const float mneg = -m * tau2;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            ssum += fast_exp2(fmaf(xa[i], tau2, mneg)) + fast_exp2(fmaf(xc[i], tau2, mneg));
+        }
+      }
+    };
+    // pass 1 starts the accumulators at -L / tau2, so its scores come out as
+    // (s_h - L_h) / tau2: group scores in accumulator units
+    const float a1 = (pass == 1 && G > 1) ? nL / tau2 : 0.0f;
+    // one tile step of pass 1: cur holds the fragments of tile t, nxt receives
+    // tile t + 1 (past the last tile: the last again, unused)
     auto step = [&](int t, const uint4 (&cur)[FRAGS], uint4 (&nxt)[FRAGS]) {
       load_frag(min(t + 1, ntiles - 1), nxt);
       float x[16];
-      tile_scores(cur, t, x);
+      tile_scores(cur, t, x, a1);
       if constexpr (pass == 0) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          // insert x into t0 >= t1 >= t2: each new entry is the median of its
-          // old neighbours above and below and x
-          t2[i] = __builtin_amdgcn_fmed3f(t1[i], t2[i], x[i]);
-          t1[i] = __builtin_amdgcn_fmed3f(t0[i], t1[i], x[i]);
-          t0[i] = fmaxf(t0[i], x[i]);
-        }
-        if (G > 1) {
-          // online log-sum-exp; m is the running maximum in accumulator units
-          float mt = x[0];
-#pragma unroll
-          for (int i = 1; i < 16; ++i) mt = fmaxf(mt, x[i]);
-          if (mt > m) { ssum = (m == -INFINITY) ? 0.0f : ssum * fast_exp2((m - mt) * tau2); m = mt; }
-          if (m != -INFINITY) {
-            const float mneg = -m * tau2;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) ssum += fast_exp2(fmaf(x[i], tau2, mneg));
-          }
-        }
       } else {
-        // group scores: s_h - L_h (base 2); the heads of a group meet in LDS,
-        // in one of two exchange buffers by step parity (a wavefront writes
+        // group scores (s_h - L_h) / tau2, in accumulator units, which order
+        // the chunks as s_h - L_h does; the heads of a group meet in LDS, in
+        // one of two exchange buffers by step parity (a wavefront writes
         // buffer t & 1 only after every wavefront passed the barrier of step
-        // t - 1, so after their reads of step t - 2).  G = 1 keeps accumulator
-        // units, which order the chunks the same way, and exchanges nothing.
+        // t - 1, so after their reads of step t - 2).  G = 1 exchanges nothing.
         float* xbt = xb + (size_t)(t & 1) * G * QB * XROW;
         if (G > 1) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) x[i] = fmaf(x[i], tau2, nL);
           const int xrow = hw * QB + 32 * qw + col;
           float* xr = xbt + (size_t)xrow * XROW;
 #pragma unroll
@@ -446,9 +456,25 @@ k_score_fast(const bf16_t* __restrict__ qr, const uint4* __restrict__ frag,
         nstg += tot;
       }
     };
-    for (int t = 0; t < ntiles; t += 2) {
-      step(t, fA, fB);
-      if (t + 1 < ntiles) step(t + 1, fB, fA);
+    if constexpr (pass == 0) {
+      for (int t = 0; t < ntiles; t += 2) {
+        float xa[16], xc[16];
+        load_frag(min(t + 1, ntiles - 1), fB);
+        tile_scores(fA, t, xa, 0.0f);
+        if (t + 1 < ntiles) {
+          load_frag(min(t + 2, ntiles - 1), fA);
+          tile_scores(fB, t + 1, xc, 0.0f);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xc[i] = -INFINITY;
+        }
+        absorb2(xa, xc);
+      }
+    } else {
+      for (int t = 0; t < ntiles; t += 2) {
+        step(t, fA, fB);
+        if (t + 1 < ntiles) step(t + 1, fB, fA);
+      }
     }
     if constexpr (pass == 0) {
       // per (query, head): log-sum-exp and the tracked scores, by slot and rank
@@ -503,11 +529,12 @@ k_score_fast(const bf16_t* __restrict__ qr, const uint4* __restrict__ frag,
       for (int t = tid; t < QB * K; t += NT) lst[t] = 0ull;   // pass-0 scratch read above
       for (int t = tid; t < QB; t += NT) {
         const float T = tk[t];
-        // pass 1 computes s_h - L_h as one fma of the accumulator, which rounds
-        // differently from the product above: lower the bound by a margin far
-        // above that rounding so no chunk at the bound is lost
+        // pass 1 accumulates s_h - L_h in accumulator units (scores / tau2),
+        // which rounds differently from the product above: lower the bound by
+        // a margin far above that rounding so no chunk at the bound is lost,
+        // then convert it to those units
         const float Tm = (T == -INFINITY) ? -INFINITY : T - (1e-3f + 1e-6f * fabsf(T));
-        thf[t] = Tm;
+        thf[t] = (G > 1) ? Tm / tau2 : Tm;
       }
       __syncthreads();
     }
