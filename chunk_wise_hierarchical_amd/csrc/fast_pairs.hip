@@ -180,18 +180,23 @@ k_pair_scan(const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ bsa,
   if (blockIdx.x == gridDim.x - 1 && tid == 0) { tot[0] = ba + sa; tot[1] = bb + sb2; }
 }
 
-// tile t of bucket f: {f << 7 | pairs in the tile, first list position}
+// tile t (one thread per tile): {f << 7 | pairs in the tile, first list
+// position}, f the bucket holding it = the last bucket whose first tile is
+// <= t (buckets without pairs share their first tile with the next one)
 __global__ void __launch_bounds__(NT)
 k_pair_tiles(const uint32_t* __restrict__ cnt, const uint32_t* __restrict__ loff,
-             const uint32_t* __restrict__ toff, uint2* __restrict__ tinfo, int F, int TQ) {
-  const int f = blockIdx.x * NT + threadIdx.x;
-  if (f >= F) return;
-  const uint32_t n = cnt[f], t0 = toff[f], l0 = loff[f];
-  const uint32_t nt = (n + (uint32_t)TQ - 1u) / (uint32_t)TQ;
-  for (uint32_t u = 0; u < nt; ++u) {
-    const uint32_t m = min((uint32_t)TQ, n - u * (uint32_t)TQ);
-    tinfo[t0 + u] = make_uint2(((uint32_t)f << 7) | m, l0 + u * (uint32_t)TQ);
+             const uint32_t* __restrict__ toff, const uint32_t* __restrict__ tot,
+             uint2* __restrict__ tinfo, int F, int TQ) {
+  const uint32_t t = (uint32_t)blockIdx.x * NT + threadIdx.x;
+  if (t >= tot[1]) return;
+  int lo = 0, hi = F;   // toff[lo] <= t < toff[hi] (toff[F] read as +inf)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (toff[mid] <= t) lo = mid; else hi = mid;
   }
+  const uint32_t u = t - toff[lo], n = cnt[lo];
+  const uint32_t m = min((uint32_t)TQ, n - u * (uint32_t)TQ);
+  tinfo[t] = make_uint2(((uint32_t)lo << 7) | m, loff[lo] + u * (uint32_t)TQ);
 }
 
 // list entries (local query << 7 | slot), bucketed by chunk; the order inside
@@ -663,12 +668,14 @@ k_pair_reduce(const float* __restrict__ swa, const float* __restrict__ lz,
   const int b = bg / Hkv, g = bg - b * Hkv;
   const int tid = threadIdx.x;
   const int q0 = blockIdx.y * RQ;
-  // fusion logits of the workgroup's queries into LDS (independent loads)
-  for (int it = tid; it < RQ * G * K; it += NT) {
-    const int kx = it % K, qh = it / K, qq = qh / G, h = qh - qq * G;
+  // fusion logits of the workgroup's queries into LDS: they are contiguous in
+  // memory ([query][slot][head]), so consecutive threads read consecutive words
+  const float* lb = lamb + ((long long)bg * qs + q0) * K * G;
+  for (int it = tid; it < RQ * K * G; it += NT) {
+    const int h = it % G, r = it / G, kx = r % K, qq = r / K;
     const int qi = q0 + qq;
     if (qi < qs && kx < min(K, n_cand((long long)i0 + qi, W, S)))
-      wk[qh * (K + 1) + kx] = lamb[((((long long)bg * qs + qi) * K + kx) * G) + h];
+      wk[(qq * G + h) * (K + 1) + kx] = lb[it];
   }
   for (int it = tid; it < RQ * G; it += NT) {
     const int qq = it / G, h = it - qq * G;
@@ -769,8 +776,8 @@ hipError_t launch_pairs(const HilsShape& s, const void* q, const void* qr, const
                            F, TQ);
         hipLaunchKernelGGL(k_pair_scan, dim3(nsb), dim3(NT), 0, st, pb.cnt, pb.bsum, pb.bsum + nsb,
                            pb.loff, pb.toff, pb.cur, pb.tot, F, TQ);
-        hipLaunchKernelGGL(k_pair_tiles, dim3((F + NT - 1) / NT), dim3(NT), 0, st, pb.cnt, pb.loff,
-                           pb.toff, pb.tinfo, F, TQ);
+        hipLaunchKernelGGL(k_pair_tiles, dim3((unsigned)((hils_pair_tiles_max(s, qs) + NT - 1) / NT)),
+                           dim3(NT), 0, st, pb.cnt, pb.loff, pb.toff, pb.tot, pb.tinfo, F, TQ);
         hipLaunchKernelGGL(k_pair_scatter, dim3(s.B * s.Hkv, (qs + PQ - 1) / PQ), dim3(NT), hshm, st,
                            sel, pb.cur, pb.list, s.N, s.K, s.nC, i0, qs); }
     }
