@@ -189,6 +189,14 @@ def test_prefill_pairs_across_slices():
                   label="two slices")
 
 
+def test_prefill_pairs_many_buckets():
+    # 2 x 8 x 312 = 4992 (KV group, chunk) buckets: the bucket prefix sums span
+    # two scan workgroups (4096 buckets each), the second one partial
+    w = synth.get_workload("prefill_64k", N=20000, B=2, W=1024, K=32)
+    assert w.B * w.Hkv * (w.N // w.S) == 4992
+    _prefill_case(w, rows=sample_rows(w, 120, include=[19999]), label="4992 buckets")
+
+
 def test_union_and_pairs_agree():
     w = synth.get_workload("prefill_64k", N=4096, W=512, K=16)
     x = _gpu_inputs(w)
