@@ -309,10 +309,11 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[rb][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  // running row maximum in raw score units (logit = tau2 * raw, base 2) and
-  // this lane's part of the row's exp sum (the four lanes of a row add up at
-  // the end)
+  // running row reference in raw score units (logit = tau2 * raw, base 2) and
+  // this lane's part of the row's exp sum relative to it (the four lanes of a
+  // row add up at the end)
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
+  const float mslack = 8.0f / tau2;
 
   // full: the tile lies inside the window of every row of the workgroup, so
   // no score needs a mask
@@ -351,19 +352,17 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           mt = fmaxf(mt, v);
         }
       mt = max_x32(max_x16(mt));
-      const float mnew = fmaxf(m[rb], mt);
+      // the row's reference m moves only when the tile's maximum passes it by
+      // more than 8 in base-2 logit units (always on the first finite tile):
+      // the weights stay below 2^8, and the outputs are rescaled rarely.  A
+      // row without a finite score yet keeps m = -inf and weights 0.
+      const float mnew = (mt > m[rb] + mslack) ? mt : m[rb];
+      scale[rb] = (mnew == m[rb]) ? 1.0f : fast_exp2((m[rb] - mnew) * tau2);
+      const float mneg = (mnew == -INFINITY) ? 0.0f : -mnew * tau2;
       float p[16];
       float ps = 0.0f;
-      scale[rb] = 1.0f;
-      if (mnew == -INFINITY) {
 #pragma unroll
-        for (int t = 0; t < 16; ++t) p[t] = 0.0f;
-      } else {
-        if (mnew != m[rb]) scale[rb] = fast_exp2((m[rb] - mnew) * tau2);
-        const float mneg = -mnew * tau2;
-#pragma unroll
-        for (int t = 0; t < 16; ++t) { p[t] = fast_exp2(fmaf(x[t], tau2, mneg)); ps += p[t]; }
-      }
+      for (int t = 0; t < 16; ++t) { p[t] = fast_exp2(fmaf(x[t], tau2, mneg)); ps += p[t]; }
       l[rb] = l[rb] * scale[rb] + ps;
       m[rb] = mnew;
 #pragma unroll
@@ -374,7 +373,7 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         pb[rb][kb] = __builtin_bit_cast(bf16x8_t, u);
       }
     }
-    // rescale the outputs only when some row's maximum moved
+    // rescale the outputs only when some row's reference moved
     if (__ballot(scale[0] != 1.0f || scale[1] != 1.0f)) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
