@@ -296,23 +296,24 @@ k_attn_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
         mt = fmaxf(mt, v2);
       }
     mt = max_x32(max_x16(mt));
-    const float mnew = fmaxf(m, mt);
+    // the reference m moves only when the tile's maximum passes it by more
+    // than 8 (base-2 logits; always on the first finite tile), so weights
+    // stay below 2^8 and the outputs are rescaled rarely; a row without a
+    // finite score yet keeps m = -inf and weights 0
+    const float mnew = (mt > m + 8.0f) ? mt : m;
+    const float scale = (mnew == m) ? 1.0f : fast_exp2(m - mnew);   // 0 when m = -inf
+    const float mref = (mnew == -INFINITY) ? 0.0f : mnew;
     float p[16];
     float ps = 0.0f;
-    float scale = 1.0f;
-    if (mnew == -INFINITY) {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) p[t] = 0.0f;
-    } else {
-      scale = fast_exp2(m - mnew);       // 0 when m = -inf
-#pragma unroll
-      for (int t = 0; t < 16; ++t) { p[t] = fast_exp2(x[t] - mnew); ps += p[t]; }
-    }
+    for (int t = 0; t < 16; ++t) { p[t] = fast_exp2(x[t] - mref); ps += p[t]; }
     ps = sum_x32(sum_x16(ps));
     l = l * scale + ps;
     m = mnew;
+    if (__ballot(scale != 1.0f)) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[dt] *= scale;
+      for (int dt = 0; dt < 8; ++dt) acc[dt] *= scale;
+    }
     float pk[16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
