@@ -82,9 +82,9 @@ def _plan_structure(w: Workload, seed: int, ncand: int):
                 if h % 3 == 1:
                     plan.append((b, h, [(rint(nC), rint(w.S))]))
                 elif h % 3 == 2:
-                    m = 2 + rint(7)                       # 2..8 chunks
+                    m = 2 + rint(7)                       # 2..8 chunks (fewer if nC < m)
                     chunks = torch.randperm(nC, generator=g)[:m].tolist()
-                    plan.append((b, h, [(chunks[rint(m)], rint(w.S)) for _ in range(8)]))
+                    plan.append((b, h, [(chunks[rint(len(chunks))], rint(w.S)) for _ in range(8)]))
         elif w.regime == "needle_chunk":
             c = rint(nC)
             for h in range(w.Hq):

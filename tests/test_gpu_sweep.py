@@ -1,0 +1,77 @@
+"""GPU parity over a seeded sweep of shapes: the HIP library against the fp64
+oracle on configurations drawn at random from the supported space (fast MFMA
+path and generic kernels, bf16 and fp32, every head-structure regime, ragged
+lengths, windows shorter and longer than the sequence, K from 1 to 64).
+
+The draws are fixed by the seed, so every run checks the same cases; each case
+prints its shape before it runs.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests.parity_util import sample_rows
+from tests.test_gpu_parity import _decode_case, _prefill_case
+
+pytestmark = pytest.mark.gpu
+
+REGIMES = ["iid", "mod3", "half_peaked4", "depth10", "needle_chunk"]
+
+
+def _prefill_draws(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        fast = c % 2 == 0
+        if fast:                          # shapes the MFMA path takes
+            d, S, dtype = 128, 64, "bf16"
+            G = int(rng.choice([1, 2, 4]))
+        else:                             # generic kernels
+            d = int(rng.choice([32, 64, 96]))
+            S = int(rng.choice([16, 32, 48]))
+            dtype = str(rng.choice(["bf16", "f32"]))
+            G = int(rng.choice([1, 2, 3, 8]))
+        Hkv = int(rng.choice([1, 2]))
+        N = int(rng.integers(S, 40 * S))
+        W = int(rng.integers(1, 12 * S))
+        K = int(rng.integers(1, 65 if fast else 33))
+        regime = REGIMES[int(rng.integers(0, 4))]
+        out.append(dict(B=int(rng.integers(1, 3)), N=N, Hq=G * Hkv, Hkv=Hkv, d=d, S=S, W=W,
+                        K=K, dtype=dtype, regime=regime, seed=int(rng.integers(0, 1 << 30)),
+                        scaled=bool(rng.integers(0, 2)), q_route=bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _prefill_draws(24, seed=20261203),
+                         ids=lambda c: f"N{c['N']}_G{c['Hq'] // c['Hkv']}_d{c['d']}_S{c['S']}_"
+                                       f"W{c['W']}_K{c['K']}_{c['dtype']}")
+def test_prefill_sweep(case):
+    c = dict(case)
+    q_route = c.pop("q_route")
+    w = synth.get_workload("prefill_64k", **c)
+    _prefill_case(w, rows=sample_rows(w, 120, seed=c["seed"] % 1000), q_route=q_route,
+                  label="sweep")
+
+
+def _decode_draws(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        G = int(rng.choice([1, 2, 4]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        B = int(rng.integers(1, 5))
+        N = int(rng.integers(512, 6000))
+        out.append(dict(B=B, N=N, Hq=G * Hkv, Hkv=Hkv, W=int(rng.integers(1, 1200)),
+                        K=int(rng.integers(1, 65)), regime=REGIMES[int(rng.integers(0, 5))],
+                        seed=int(rng.integers(0, 1 << 30)),
+                        seqlen=[int(x) for x in rng.integers(1, N + 1, size=B)]))
+    return out
+
+
+@pytest.mark.parametrize("case", _decode_draws(12, seed=20261204),
+                         ids=lambda c: f"B{c['B']}_T{c['N']}_G{c['Hq'] // c['Hkv']}_W{c['W']}_K{c['K']}")
+def test_decode_sweep(case):
+    c = dict(case)
+    seqlen = c.pop("seqlen")
+    w = synth.get_workload("decode_512k", **c)
+    _decode_case(w, seqlen, label="sweep")
