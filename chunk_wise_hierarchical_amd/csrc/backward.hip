@@ -797,12 +797,16 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
       dp += __shfl_xor(dp, 4, 64);
       const float t = act ? tau * a : -INFINITY;
       const float m = block_max((qd == 0) ? t : -INFINITY, red);
-      const float z = block_sum((qd == 0 && act) ? __expf(t - m) : 0.0f, red);
-      const float lpi = t - (m + __logf(z));
-      const float pi = act ? __expf(lpi) : 0.0f;
+      const float z = block_sum((qd == 0 && act) ? expf(t - m) : 0.0f, red);
+      const float lpi = t - (m + logf(z));
+      const float pi = act ? expf(lpi) : 0.0f;
       const float dpi = act ? dp + dbs[r] * (-lpi - 1.0f) : 0.0f;
-      const float spd = block_sum((qd == 0) ? pi * dpi : 0.0f, red);
-      const float dt = pi * (dpi - spd);
+      // dt = pi (dpi - sum pi dpi), centred on the dpi of a largest-weight
+      // token (any reference gives the same value since sum pi = 1): the
+      // differences stay small where pi is peaked, instead of cancelling
+      const float rc = block_max((qd == 0 && act && t == m) ? dpi : -INFINITY, red);
+      const float spd = block_sum((qd == 0) ? pi * (dpi - rc) : 0.0f, red);
+      const float dt = pi * ((dpi - rc) - spd);
       // dlm = tau sum_j dt_j k_j (column sums over the chunk's tokens)
       if (act) {
 #pragma unroll

@@ -75,3 +75,58 @@ def test_decode_sweep(case):
     seqlen = c.pop("seqlen")
     w = synth.get_workload("decode_512k", **c)
     _decode_case(w, seqlen, label="sweep")
+
+
+def _backward_draws(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        dtype = "bf16" if c % 2 == 0 else "f32"
+        d = int(rng.choice([64, 128])) if dtype == "bf16" else int(rng.choice([32, 64, 96, 128]))
+        S = int(rng.choice([16, 32, 64]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.choice([1, 2]))
+        out.append(dict(B=int(rng.integers(1, 3)), N=int(rng.integers(S, 24 * S)), Hq=G * Hkv,
+                        Hkv=Hkv, d=d, S=S, W=int(rng.integers(1, 8 * S)),
+                        K=int(rng.integers(1, 17)), dtype=dtype, regime=REGIMES[int(rng.integers(0, 4))],
+                        seed=int(rng.integers(0, 1 << 30)), scaled=bool(rng.integers(0, 2)),
+                        q_route=bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _backward_draws(10, seed=20261205),
+                         ids=lambda c: f"N{c['N']}_G{c['Hq'] // c['Hkv']}_d{c['d']}_S{c['S']}_"
+                                       f"W{c['W']}_K{c['K']}_{c['dtype']}")
+def test_backward_sweep(case):
+    from tests.test_gpu_backward import _case as backward_case
+    c = dict(case)
+    q_route = c.pop("q_route")
+    w = synth.get_workload("prefill_64k", **c)
+    backward_case(w, q_route=q_route, label="sweep", seed=c["seed"] % 1000)
+
+
+def _multi_draws(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.choice([1, 2]))
+        B = int(rng.integers(1, 4))
+        N = int(rng.integers(256, 5000))
+        M = int(rng.integers(1, 17))
+        out.append(dict(B=B, N=N, Hq=G * Hkv, Hkv=Hkv, W=int(rng.integers(1, 1200)),
+                        K=int(rng.integers(1, 65)), regime=REGIMES[int(rng.integers(0, 5))],
+                        seed=int(rng.integers(0, 1 << 30)), M=M,
+                        seqlen=[int(x) for x in rng.integers(M, N + 1, size=B)]))
+    return out
+
+
+@pytest.mark.parametrize("case", _multi_draws(8, seed=20261206),
+                         ids=lambda c: f"B{c['B']}_T{c['N']}_G{c['Hq'] // c['Hkv']}_M{c['M']}_"
+                                       f"W{c['W']}_K{c['K']}")
+def test_multi_decode_sweep(case):
+    from tests.test_gpu_multi_decode import _multi_case
+    c = dict(case)
+    seqlen, M = c.pop("seqlen"), c.pop("M")
+    w = synth.get_workload("decode_512k", **c)
+    _multi_case(w, M, seqlen, label="sweep")
