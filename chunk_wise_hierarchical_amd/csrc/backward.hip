@@ -107,6 +107,26 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   for (int u = 1; u < (int)(blockDim.x >> 6); ++u) m = fmaxf(m, red[u]);
   return m;
 }
+__device__ __forceinline__ double block_max_d(double v, double* red) {
+  v = wave_max_d(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  double m = red[0];
+  for (int u = 1; u < (int)(blockDim.x >> 6); ++u) m = fmax(m, red[u]);
+  return m;
+}
+__device__ __forceinline__ double block_sum_d(double v, double* red) {
+  v = wave_sum_d(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  double s = 0.0;
+  for (int u = 0; u < (int)(blockDim.x >> 6); ++u) s += red[u];
+  return s;
+}
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum_f(v);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -592,11 +612,12 @@ constexpr int CE = 16;                               // elements per thread (d <
 template <typename T> struct ColStage { static constexpr int NB = (sizeof(T) == 2) ? 32 : 16; };
 
 // bytes of the column kernel's staging area (also the summary backward's
-// scratch of S x d floats, used after the contributions)
+// scratch of one d-row of doubles per wavefront, used after the contributions)
 template <typename T>
 __host__ __device__ inline size_t col_stage_bytes(int d, int S) {
+  (void)S;
   const size_t st = (size_t)2 * 3 * ColStage<T>::NB * d * sizeof(T);
-  const size_t sc = (size_t)S * d * sizeof(float);
+  const size_t sc = (size_t)(CT / 64) * d * sizeof(double);
   return ((st > sc ? st : sc) + 15) & ~(size_t)15;
 }
 
@@ -624,12 +645,16 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
   const int e0 = qd * DQ;
   constexpr int NB = ColStage<T>::NB;
   // staging: [2 buffers][q, dout, routing query][NB][d] T; after the
-  // contributions the same bytes hold the [S][d] float reduction scratch
+  // contributions the same bytes hold the [CT / 64][d] double column sums.
+  // dk' and db' of the chunk's summaries accumulate in double: their
+  // contributions (one per selecting query and head) cancel, and the
+  // summary backward below subtracts nearly equal terms.
   T* stg = reinterpret_cast<T*>(smc);
-  float* tmp = smc;
-  float* dks = reinterpret_cast<float*>(reinterpret_cast<char*>(smc) + col_stage_bytes<T>(d, S));
-  float* dbs = dks + G * d;                          // [G]
-  float* red = dbs + G;                              // [8]
+  double* tmp = reinterpret_cast<double*>(smc);
+  double* dks = reinterpret_cast<double*>(reinterpret_cast<char*>(smc) + col_stage_bytes<T>(d, S));
+  double* dbs = dks + G * d;                         // [G]
+  double* redd = dbs + G;                            // [8]
+  float* red = reinterpret_cast<float*>(redd + 8);   // [8]
   int* di = reinterpret_cast<int*>(red + 8);         // [CBATCH] query << 4 | head, window flag << 31
   float* dsx = reinterpret_cast<float*>(di + CBATCH);   // [CBATCH][4] alpha, lse, g, window term
   const T* kb = k + (bg * (long long)N + j0) * d;
@@ -645,7 +670,7 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
     dkj[u] = 0.0f;
     dvj[u] = 0.0f;
   }
-  for (int t = tid; t < G * d + G; t += CT) dks[t] = 0.0f;
+  for (int t = tid; t < G * d + G; t += CT) dks[t] = 0.0;
 
   const bool summ = c < nC;
   const uint32_t p0 = summ ? off[bg * (nC + 1) + c] : 0u;
@@ -748,8 +773,8 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
         load_slice16<T>(stg + (((size_t)buf * 3 + 2) * NB + ul) * d + e0, DQ, hv);
 #pragma unroll
         for (int x = 0; x < CE; ++x)
-          if (x < DQ) dks[r * d + e0 + x] = fmaf(tau * xt, hv[x], dks[r * d + e0 + x]);
-        if (qd == 0) dbs[r] += xt;
+          if (x < DQ) dks[r * d + e0 + x] = fma((double)tau * xt, (double)hv[x], dks[r * d + e0 + x]);
+        if (qd == 0) dbs[r] += (double)xt;
       }
     };
     const int nsb = (nb + NB - 1) / NB;
@@ -772,22 +797,23 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
     for (int r = 0; r < G; ++r) {
       const long long ho = ((hb + r) * nC + c) * (long long)d;
       if (mode == 1) {                       // landmark key: k' = q', b' = 0
-        for (int e = tid; e < d; e += CT) dlm[ho + e] = dks[r * d + e];
+        for (int e = tid; e < d; e += CT) dlm[ho + e] = (float)dks[r * d + e];
         continue;
       }
       if (mode == 3) {                       // mean pooling: k' = mean of the keys
 #pragma unroll
         for (int x = 0; x < CE; ++x)
-          if (x < DQ) dkj[x] = fmaf(1.0f / (float)S, dks[r * d + e0 + x], dkj[x]);
+          if (x < DQ) dkj[x] = fmaf(1.0f / (float)S, (float)dks[r * d + e0 + x], dkj[x]);
         continue;
       }
       float lv[CE];
       load_slice16<T>(lm + ho + e0, DQ, lv);
-      float a = 0.0f, dp = 0.0f;
+      // the summary softmax and its backward in double (see dks above)
+      double a = 0.0, dp = 0.0;
 #pragma unroll
       for (int x = 0; x < CE; ++x) {
-        a = fmaf(lv[x], kj[x], a);
-        dp = fmaf(x < DQ ? dks[r * d + e0 + x] : 0.0f, kj[x], dp);
+        a = fma((double)lv[x], (double)kj[x], a);
+        dp = fma(x < DQ ? dks[r * d + e0 + x] : 0.0, (double)kj[x], dp);
       }
       a += __shfl_xor(a, 1, 64);
       a += __shfl_xor(a, 2, 64);
@@ -795,33 +821,42 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
       dp += __shfl_xor(dp, 1, 64);
       dp += __shfl_xor(dp, 2, 64);
       dp += __shfl_xor(dp, 4, 64);
-      const float t = act ? tau * a : -INFINITY;
-      const float m = block_max((qd == 0) ? t : -INFINITY, red);
-      const float z = block_sum((qd == 0 && act) ? expf(t - m) : 0.0f, red);
-      const float lpi = t - (m + logf(z));
-      const float pi = act ? expf(lpi) : 0.0f;
-      const float dpi = act ? dp + dbs[r] * (-lpi - 1.0f) : 0.0f;
+      const double t = act ? (double)tau * a : -INFINITY;
+      const double m = block_max_d((qd == 0) ? t : -INFINITY, redd);
+      const double z = block_sum_d((qd == 0 && act) ? exp(t - m) : 0.0, redd);
+      const double lpi = t - (m + log(z));
+      const double pi = act ? exp(lpi) : 0.0;
+      const double dpi = act ? dp + dbs[r] * (-lpi - 1.0) : 0.0;
       // dt = pi (dpi - sum pi dpi), centred on the dpi of a largest-weight
       // token (any reference gives the same value since sum pi = 1): the
       // differences stay small where pi is peaked, instead of cancelling
-      const float rc = block_max((qd == 0 && act && t == m) ? dpi : -INFINITY, red);
-      const float spd = block_sum((qd == 0) ? pi * (dpi - rc) : 0.0f, red);
-      const float dt = pi * ((dpi - rc) - spd);
-      // dlm = tau sum_j dt_j k_j (column sums over the chunk's tokens)
-      if (act) {
+      const double rc = block_max_d((qd == 0 && act && t == m) ? dpi : -INFINITY, redd);
+      const double spd = block_sum_d((qd == 0) ? pi * (dpi - rc) : 0.0, redd);
+      const double dt = pi * ((dpi - rc) - spd);
+      // dlm = tau sum_j dt_j k_j: column sums over the chunk's tokens, first
+      // over the 8 tokens of a wavefront (lanes 8, 16 and 32 apart share an
+      // element slice), then over the wavefronts in LDS
+      {
+        const int wv = tid >> 6, ln = tid & 63;
 #pragma unroll
-        for (int x = 0; x < CE; ++x)
-          if (x < DQ) tmp[jt * d + e0 + x] = dt * kj[x];
+        for (int x = 0; x < CE; ++x) {
+          double v = (act && x < DQ) ? dt * (double)kj[x] : 0.0;
+          v += __shfl_xor(v, 8, 64);
+          v += __shfl_xor(v, 16, 64);
+          v += __shfl_xor(v, 32, 64);
+          if (ln < 8 && x < DQ) tmp[wv * d + e0 + x] = v;
+        }
       }
       __syncthreads();
       for (int e = tid; e < d; e += CT) {
-        float sum = 0.0f;
-        for (int j = 0; j < jn; ++j) sum += tmp[j * d + e];
-        dlm[ho + e] = tau * sum;
+        double sum = 0.0;
+        for (int u = 0; u < CT / 64; ++u) sum += tmp[u * d + e];
+        dlm[ho + e] = (float)((double)tau * sum);
       }
 #pragma unroll
       for (int x = 0; x < CE; ++x)
-        if (x < DQ) dkj[x] = fmaf(tau * dt, lv[x], fmaf(pi, dks[r * d + e0 + x], dkj[x]));
+        if (x < DQ)
+          dkj[x] += (float)((double)tau * dt * (double)lv[x] + pi * dks[r * d + e0 + x]);
       __syncthreads();
     }
   }
@@ -862,7 +897,7 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
   const bool all_keys = bwd_rows2_lds(s) <= 65536;
   const size_t rshm = all_keys ? bwd_rows2_lds(s) : hils_bwd_rows_lds(s);
   const size_t cshm = (s.dtype == 0 ? col_stage_bytes<bf16_t>(s.d, s.S) : col_stage_bytes<float>(s.d, s.S)) +
-                      sizeof(float) * ((size_t)s.G * s.d + s.G + 8) +
+                      sizeof(double) * ((size_t)s.G * s.d + s.G + 8) + sizeof(float) * 8 +
                       (size_t)CBATCH * (sizeof(int) + 4 * sizeof(float));
   const int sep = dqr != nullptr;
   if (s.dtype == 0) {
