@@ -113,6 +113,8 @@ def _apply_structure(w, plan, dirs, q, k, lm, lam):
         lm[b, h] = (lm[b, h].float() + a * u).to(lm.dtype)
         for (c, off) in needles:
             t = c * w.S + off
+            if t >= k.shape[2]:      # a sequence shorter than one chunk: nothing to plant
+                continue
             k[b, h // G, t] = (k[b, h // G, t].float() + coef * u).to(k.dtype)
 
 
