@@ -130,3 +130,62 @@ def test_multi_decode_sweep(case):
     seqlen, M = c.pop("seqlen"), c.pop("M")
     w = synth.get_workload("decode_512k", **c)
     _multi_case(w, M, seqlen, label="sweep")
+
+
+def _long_draws(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        G = int(rng.choice([1, 2, 4]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        out.append(dict(N=int(rng.integers(3000, 20000)), Hq=G * Hkv, Hkv=Hkv,
+                        W=int(rng.integers(64, 3000)), K=int(rng.integers(1, 65)),
+                        regime=REGIMES[int(rng.integers(0, 4))], seed=int(rng.integers(0, 1 << 30)),
+                        scaled=bool(rng.integers(0, 2)), union=bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _long_draws(6, seed=20261207),
+                         ids=lambda c: f"N{c['N']}_G{c['Hq'] // c['Hkv']}_W{c['W']}_K{c['K']}_"
+                                       f"{'union' if c['union'] else 'buckets'}")
+def test_prefill_long_sweep(case):
+    # several score tiles, window tiles and (for the buckets) pair tiles per
+    # query block, on both attention organisations
+    c = dict(case)
+    union = c.pop("union")
+    w = synth.get_workload("prefill_64k", **c)
+    _prefill_case(w, rows=sample_rows(w, 40, seed=c["seed"] % 1000), union=union, label="sweep")
+
+
+def _paged_draws(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for c in range(n):
+        G = int(rng.choice([1, 2, 4, 8]))
+        Hkv = int(rng.choice([1, 2]))
+        B = int(rng.integers(1, 4))
+        N = int(rng.integers(2, 80)) * 64
+        out.append(dict(B=B, N=N, Hq=G * Hkv, Hkv=Hkv, W=int(rng.integers(1, 2000)),
+                        K=int(rng.integers(1, 65)), regime=REGIMES[int(rng.integers(0, 5))],
+                        seed=int(rng.integers(0, 1 << 30)),
+                        lens=[int(x) for x in rng.integers(1, N + 1, size=B)]))
+    return out
+
+
+@pytest.mark.parametrize("case", _paged_draws(8, seed=20261208),
+                         ids=lambda c: f"B{c['B']}_T{c['N']}_G{c['Hq'] // c['Hkv']}_W{c['W']}_K{c['K']}")
+def test_paged_decode_sweep(case):
+    # decode over randomly placed pages equals decode over the contiguous
+    # cache (selection and output, bit for bit)
+    import torch
+    import chunk_wise_hierarchical_amd as hils
+    from tests.test_gpu_paged import _case as paged_case
+    c = dict(case)
+    lens = c.pop("lens")
+    w = synth.get_workload("decode_512k", **c)
+    x, seqlen, (ks, bs, out_c, sel_c), (table, kp, vp, ksp, bsp) = paged_case(w, lens)
+    sel_p = torch.empty_like(sel_c)
+    out_p = hils.decode_paged(x["q"], kp, vp, table, seqlen, ksp, bsp, w.S, w.W, w.K, sel=sel_p)
+    torch.cuda.synchronize()
+    assert torch.equal(sel_p, sel_c)
+    assert torch.equal(out_p, out_c)
