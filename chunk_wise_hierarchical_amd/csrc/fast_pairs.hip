@@ -356,7 +356,7 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       // more than 8 in base-2 logit units (always on the first finite tile):
       // the weights stay below 2^8, and the outputs are rescaled rarely.  A
       // row without a finite score yet keeps m = -inf and weights 0.
-      const float mnew = (mt > m[rb] + mslack) ? mt : m[rb];
+      const float mnew = (m[rb] == -INFINITY || mt > m[rb] + mslack) ? mt : m[rb];
       scale[rb] = (mnew == m[rb]) ? 1.0f : fast_exp2((m[rb] - mnew) * tau2);
       const float mneg = (mnew == -INFINITY) ? 0.0f : -mnew * tau2;
       float p[16];
