@@ -137,6 +137,32 @@ def _kernel_table(records, steps):
     return {k: {"ms_per_step": v[0] / steps, "calls": v[1], "avg_ms": v[0] / v[1]} for k, v in agg.items()}
 
 
+def pair_path_bytes(sel, w, launches):
+    """Algorithmic HBM bytes per prefill of the chunk-bucket path's pair
+    attention and reduction, from the selection sel [B,Hkv,N,K] (-1 padded).
+    Pair attention, per (query, KV group, selected chunk) pair: the G gathered
+    query rows and the G bf16 per-chunk output rows (G*d*2 B each), G fp32
+    fusion logits and the 4-byte list entry; per (slice, KV group, chunk)
+    bucket: the chunk's K and V^T (S*d*2 B each), k' (G*d*2 B) and b' (G*4 B).
+    Reduction, per pair: the G output rows and logits read back; per (query,
+    head): the fp32 window output and log-mass read, the bf16 output written."""
+    import torch
+    B, Hkv, N, K = sel.shape
+    G, d, S = w.G, w.d, w.S
+    nC = max(N // S, 1)
+    qs = -(-N // int(round(launches)))
+    pairs, buckets = 0, 0
+    bgi = torch.arange(B * Hkv, device=sel.device, dtype=torch.int64).view(B, Hkv, 1, 1)
+    for i0 in range(0, N, qs):
+        s = sel[:, :, i0:i0 + qs]
+        v = s >= 0
+        pairs += int(v.sum())
+        buckets += int(torch.unique((bgi * nC + s.long())[v]).numel())
+    attn = pairs * (2 * G * d * 2 + G * 4 + 4) + buckets * (2 * S * d * 2 + G * d * 2 + G * 4)
+    red = pairs * G * (d * 2 + 4) + B * Hkv * N * G * (d * 4 + 4 + d * 2)
+    return float(attn), float(red)
+
+
 def _overlap(sel, K, M=16, blocks=64):
     """Normalised chunk overlap of M adjacent queries (section 7.2) over the
     last `blocks` full blocks of KV group 0 (rows with at least K candidates)."""
@@ -461,8 +487,26 @@ def main():
                 "algorithmic_flops_per_launch": per_launch, "launches_per_step": launches}
 
     rooflines = {k2: roofline(k2) for k2 in kern if k2 in step_flops}
+    # the bucket path's pair attention and reduction are bound by HBM: their
+    # algorithmic bytes per launch against the HBM peak
+    hbm_rooflines = {}
+    if "k_pair_attn" in kern:
+        attn_b, red_b = pair_path_bytes(sel, w, kern["k_pair_attn"]["calls"] / args.steps)
+        for kname, step_bytes in (("k_pair_attn", attn_b), ("k_pair_reduce", red_b)):
+            if kname not in kern:
+                continue
+            launches = kern[kname]["calls"] / args.steps
+            per_launch = step_bytes / launches
+            achieved = per_launch / (kern[kname]["avg_ms"] * 1e-3) / 1e9
+            hbm_rooflines[kname] = {"kernel": kname, "bound": "hbm", "achieved": achieved,
+                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": achieved / PEAK_HBM_GBS,
+                                    "traffic": counter_traffic(kname, w.name),
+                                    "algorithmic_bytes_per_launch": per_launch,
+                                    "launches_per_step": launches}
     dom = max(kern, key=lambda k2: kern[k2]["ms_per_step"])
-    roof = rooflines.get(dom) or max(rooflines.values(), key=lambda r: kern[r["kernel"]]["ms_per_step"])
+    roof = (hbm_rooflines.get(dom) or rooflines.get(dom)
+            or max(rooflines.values(), key=lambda r: kern[r["kernel"]]["ms_per_step"]))
     total_tflops = (score_f + summ_f + attn_f) / (prefill_ms * 1e-3) / 1e12
 
     cpu_pre = None
@@ -560,6 +604,7 @@ def main():
                               "attention": attn_f / 1e12},
         "roofline": roof,
         "kernel_rooflines": rooflines,
+        "hbm_rooflines": hbm_rooflines,
         "cpu_baseline": cpu_pre,
         "kernels": kern,
         "decode": dec,
