@@ -86,6 +86,92 @@ def test_hand_example_d1():
         assert r["n"] == fx["expected_n_candidates"][str(i)]
 
 
+# --- hand-derived example at the default scale 1/sqrt(d) (d = 4) -----------
+
+_LOGS = {"0": 0.0, "ln2": math.log(2), "ln3": math.log(3), "ln6": math.log(6)}
+
+
+def _d4_example():
+    """tests/golden/hand_example_d4_default_scale.json: q = (2,0,0,0) at every
+    position, keys (x_j,0,0,0), values (j,1,-j,0), landmark queries (2,0,0,0)."""
+    fx = json.load(open(os.path.join(GOLD, "hand_example_d4_default_scale.json")))
+    x = np.array([_LOGS[s] for s in fx["setup"]["k_first_component"]])
+    N, d = x.shape[0], 4
+    j = np.arange(N, dtype=np.float64)
+    q = np.zeros((1, 1, N, d))
+    q[0, 0, :, 0] = 2.0
+    k = np.zeros((1, 1, N, d))
+    k[0, 0, :, 0] = x
+    v = np.zeros((1, 1, N, d))
+    v[0, 0, :, 0], v[0, 0, :, 1], v[0, 0, :, 2] = j, 1.0, -j
+    lm = np.zeros((1, 1, N // 2, d))
+    lm[0, 0, :, 0] = 2.0
+    return fx, q, k, v, lm
+
+
+def test_hand_example_default_scale_summaries_and_scores():
+    # Proposition 3.1 summaries and the routing scores at scale 1/sqrt(d) = 1/2,
+    # through ref_summarize's default scale and ref_chunk_scores itself
+    fx, q, k, v, lm = _d4_example()
+    ln2, ln3, ln6 = math.log(2), math.log(3), math.log(6)
+    ks, bs = O.ref_summarize(k, lm, 2, store="f64")
+    np.testing.assert_allclose(ks[0, 0, :, 0], [0.0, ln2, ln3, ln3 / 3 + 2 * ln6 / 3, 0.0],
+                               rtol=0, atol=1e-14)
+    assert np.all(ks[0, 0, :, 1:] == 0.0)
+    np.testing.assert_allclose(bs[0, 0], [ln2, ln2, ln2, ln3 - 2 * ln2 / 3, ln2], rtol=0,
+                               atol=1e-14)
+    s = O.ref_chunk_scores(q[0, :, 9], ks[0], bs[0], 4, 1 / math.sqrt(4))
+    np.testing.assert_allclose(s[0], [ln2, math.log(4), ln6, math.log(9)], rtol=0, atol=1e-14)
+
+
+def test_hand_example_default_scale_outputs():
+    fx, q, k, v, lm = _d4_example()
+    res = O.ref_prefill_rows(q, k, v, lm, [(0, i) for i in range(10)], S=2, W=2, K=1,
+                             store="f64")
+    for i in range(10):
+        num, den = fx["expected_out_surrogate"][str(i)]
+        o = res[(0, i)]["out"][0]
+        np.testing.assert_allclose(o, [num / den, 1.0, -num / den, 0.0], rtol=0, atol=1e-12,
+                                   err_msg=f"row {i}")
+        assert res[(0, i)]["sel"][0].tolist() == fx["expected_sel_surrogate"][str(i)], i
+
+
+def test_hand_example_landmark_key_mode():
+    # ablation 'w/o Prop. 3.1' (section 5.3, Table 5): the landmark row is the
+    # routing key as it is and the entropy bias is absent (b' = 0), which the
+    # fusion weight against the window fixes (b' = ln S would give other outputs)
+    fx, q, k, v, _ = _d4_example()
+    lm = np.zeros((1, 1, 5, 4))
+    lm[0, 0, 0, 0] = math.log(5)
+    ks, bs = O.ref_summarize(k, lm, 2, mode="landmark_key", store="f64")
+    np.testing.assert_array_equal(ks, lm)
+    assert np.all(bs == 0.0)
+    rows = [(0, int(i)) for i in fx["expected_out_landmark_key"]]
+    res = O.ref_prefill_rows(q, k, v, lm, rows, S=2, W=2, K=1, mode="landmark_key", store="f64")
+    for (_, i) in rows:
+        num, den = fx["expected_out_landmark_key"][str(i)]
+        np.testing.assert_allclose(res[(0, i)]["out"][0], [num / den, 1.0, -num / den, 0.0],
+                                   rtol=0, atol=1e-12, err_msg=f"row {i}")
+        assert res[(0, i)]["sel"][0].tolist() == fx["expected_sel_landmark_key"][str(i)], i
+
+
+def test_surrogate_tangent_point_through_chunk_scores():
+    # Proposition 3.1: the routing score equals the exact chunk log-mass when the
+    # routing query is the chunk's landmark query, at the default scale 1/sqrt(d);
+    # everywhere else it stays below it (convexity of log-sum-exp)
+    rng = np.random.default_rng(11)
+    S, d, n = 64, 128, 6
+    tau = 1 / math.sqrt(d)
+    k = rng.standard_normal((1, 1, n * S, d))
+    lm = rng.standard_normal((1, 2, n, d)) * 3.0
+    ks, bs = O.ref_summarize(k, lm, S, store="f64")
+    for c in range(n):
+        s = O.ref_chunk_scores(lm[0, :, c], ks[0], bs[0], n, tau)
+        logz = O.ref_exact_logz(lm[0, :, c], k[0, 0], n, S, tau)
+        np.testing.assert_allclose(s[:, c], logz[:, c], rtol=0, atol=1e-11)
+        assert np.all(s <= logz + 1e-11)
+
+
 # --- P1: exact masses with K >= |C_i| reproduce full causal attention ------
 
 def test_exact_mode_full_k_equals_full_causal():
