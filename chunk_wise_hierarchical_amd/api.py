@@ -21,6 +21,19 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(t, name, shape):
+    """Exact shape check (the C ABI takes bare pointers, so a mis-shaped tensor
+    would be read or written out of bounds on the device)."""
+    if t is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _dims(t, name, ndim):
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
 def _check_tensor(t, name, dtype=None, device=None):
     if t is None:
         return
@@ -69,8 +82,17 @@ def prefill(q, k, v, lm, S, W, K, q_route=None, mode="surrogate", scale=0.0, out
     summaries (optional) (k_sum [B,Hq,N//S,d], b_sum [B,Hq,N//S] fp32) receive the
     chunk summaries.  Returns out [B,Hq,N,d].
     """
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
+    B, Hq, N, d = _dims(q, "q", 4)
+    Hkv = _dims(k, "k", 4)[1]
+    nC = N // S if S > 0 else 0
+    ks = bs = None
+    if summaries is not None:
+        ks, bs = summaries
+    for name, t, shape in (("k", k, (B, Hkv, N, d)), ("v", v, (B, Hkv, N, d)),
+                           ("lm", lm, (B, Hq, nC, d)), ("q_route", q_route, (B, Hq, N, d)),
+                           ("out", out, (B, Hq, N, d)), ("sel", sel, (B, Hkv, N, K)),
+                           ("k_sum", ks, (B, Hq, nC, d)), ("b_sum", bs, (B, Hq, nC))):
+        _expect(t, name, shape)
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("lm", lm), ("q_route", q_route)):
         _check_tensor(t, name, q.dtype, dev)
@@ -78,9 +100,7 @@ def prefill(q, k, v, lm, S, W, K, q_route=None, mode="surrogate", scale=0.0, out
         out = torch.empty_like(q)
     _check_tensor(out, "out", q.dtype, dev)
     _check_tensor(sel, "sel", torch.int32, dev)
-    ks = bs = None
     if summaries is not None:
-        ks, bs = summaries
         _check_tensor(ks, "k_sum", q.dtype, dev)
         _check_tensor(bs, "b_sum", torch.float32, dev)
     cfg = make_cfg(B, N, Hq, Hkv, d, S, W, K, q.dtype, mode, scale, generic, union)
@@ -95,13 +115,17 @@ def prefill(q, k, v, lm, S, W, K, q_route=None, mode="surrogate", scale=0.0, out
 def summarize(k, lm, S, c0=0, c1=None, out=None, mode="surrogate", scale=0.0, Hq=None):
     """Chunk summaries for chunks [c0, c1): returns (k_sum [B,Hq,N//S,d], b_sum [B,Hq,N//S]).
     In "mean_pool" mode lm may be None (then pass Hq)."""
-    B, Hkv, N, d = k.shape
+    B, Hkv, N, d = _dims(k, "k", 4)
     if Hq is None:
         if lm is None:
             raise ValueError("summarize: Hq is required when lm is None")
-        Hq = lm.shape[1]
-    nC = N // S
+        Hq = _dims(lm, "lm", 4)[1]
+    nC = N // S if S > 0 else 0
     c1 = nC if c1 is None else c1
+    _expect(lm, "lm", (B, Hq, nC, d))
+    if out is not None:
+        _expect(out[0], "k_sum", (B, Hq, nC, d))
+        _expect(out[1], "b_sum", (B, Hq, nC))
     dev = k.device
     _check_tensor(k, "k", None, dev)
     _check_tensor(lm, "lm", k.dtype, dev)
@@ -122,8 +146,16 @@ def decode(q, k_cache, v_cache, seqlen, k_sum, b_sum, S, W, K, q_route=None, mod
            scale=0.0, out=None, sel=None, ws=None):
     """HiLS single-step decode. q [B,Hq,1,d]; caches [B,Hkv,T,d]; seqlen [B] int32 (device);
     k_sum [B,Hq,T//S,d], b_sum [B,Hq,T//S].  Returns out [B,Hq,1,d]."""
-    B, Hq, _, d = q.shape
-    Hkv, T = k_cache.shape[1], k_cache.shape[2]
+    B, Hq, one, d = _dims(q, "q", 4)
+    if one != 1:
+        raise ValueError(f"decode takes one query per sequence: q has shape {tuple(q.shape)}")
+    Hkv, T = _dims(k_cache, "k_cache", 4)[1:3]
+    nC = T // S if S > 0 else 0
+    for name, t, shape in (("k_cache", k_cache, (B, Hkv, T, d)), ("v_cache", v_cache, (B, Hkv, T, d)),
+                           ("seqlen", seqlen, (B,)), ("k_sum", k_sum, (B, Hq, nC, d)),
+                           ("b_sum", b_sum, (B, Hq, nC)), ("q_route", q_route, (B, Hq, 1, d)),
+                           ("out", out, (B, Hq, 1, d)), ("sel", sel, (B, Hkv, K))):
+        _expect(t, name, shape)
     dev = q.device
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_sum", k_sum),
                     ("q_route", q_route)):
@@ -149,8 +181,14 @@ def decode_multi(q, k_cache, v_cache, seqlen, k_sum, b_sum, S, W, K, q_route=Non
     seqlen[b] - M + m); caches [B,Hkv,T,d]; seqlen [B] int32 (device);
     k_sum [B,Hq,T//S,d], b_sum [B,Hq,T//S].  Returns out [B,Hq,M,d]; sel, if
     given, [B,Hkv,M,K] int32 receives the selected chunk ids."""
-    B, Hq, M, d = q.shape
-    Hkv, T = k_cache.shape[1], k_cache.shape[2]
+    B, Hq, M, d = _dims(q, "q", 4)
+    Hkv, T = _dims(k_cache, "k_cache", 4)[1:3]
+    nC = T // S if S > 0 else 0
+    for name, t, shape in (("k_cache", k_cache, (B, Hkv, T, d)), ("v_cache", v_cache, (B, Hkv, T, d)),
+                           ("seqlen", seqlen, (B,)), ("k_sum", k_sum, (B, Hq, nC, d)),
+                           ("b_sum", b_sum, (B, Hq, nC)), ("q_route", q_route, (B, Hq, M, d)),
+                           ("out", out, (B, Hq, M, d)), ("sel", sel, (B, Hkv, M, K))):
+        _expect(t, name, shape)
     dev = q.device
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_sum", k_sum),
                     ("q_route", q_route)):
@@ -180,8 +218,16 @@ def prefill_backward(q, k, v, lm, dout, sel, S, W, K, q_route=None, mode="surrog
     """Gradients of sum(dout * prefill(...)) with the forward's selection `sel`
     [B,Hkv,N,K] held fixed.  Returns a dict of fp32 tensors dq, dk, dv, dlm
     (None in mean_pool mode) and dq_route (None without q_route)."""
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
+    B, Hq, N, d = _dims(q, "q", 4)
+    Hkv = _dims(k, "k", 4)[1]
+    nC = N // S if S > 0 else 0
+    for name, t, shape in (("k", k, (B, Hkv, N, d)), ("v", v, (B, Hkv, N, d)),
+                           ("lm", lm, (B, Hq, nC, d)), ("dout", dout, (B, Hq, N, d)),
+                           ("q_route", q_route, (B, Hq, N, d)), ("sel", sel, (B, Hkv, N, K))):
+        _expect(t, name, shape)
+    if summaries is not None:
+        _expect(summaries[0], "k_sum", (B, Hq, nC, d))
+        _expect(summaries[1], "b_sum", (B, Hq, nC))
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("lm", lm), ("dout", dout), ("q_route", q_route)):
         _check_tensor(t, name, q.dtype, dev)
@@ -215,12 +261,17 @@ def summarize_paged(k_pages, lm_pages, pages, S, N, out=None, mode="surrogate", 
     """Summaries of the pages listed in `pages` (int32 device tensor) of a paged
     cache: k_pages [P,Hkv,S,d], lm_pages [P,Hq,d].  Returns (k_sum_pages [P,Hq,d],
     b_sum_pages [P,Hq]); `out` reuses existing page-summary tensors."""
-    P, Hkv, S_, d = k_pages.shape
+    P, Hkv, S_, d = _dims(k_pages, "k_pages", 4)
     if lm_pages is None:
         raise ValueError("summarize_paged: lm_pages is required (it sets Hq)")
-    Hq = lm_pages.shape[1]
+    Hq = _dims(lm_pages, "lm_pages", 3)[1]
     if S_ != S:
         raise ValueError(f"k_pages page size {S_} != S={S}")
+    _expect(lm_pages, "lm_pages", (P, Hq, d))
+    _dims(pages, "pages", 1)
+    if out is not None:
+        _expect(out[0], "k_sum_pages", (P, Hq, d))
+        _expect(out[1], "b_sum_pages", (P, Hq))
     dev = k_pages.device
     _check_tensor(k_pages, "k_pages", None, dev)
     _check_tensor(lm_pages, "lm_pages", k_pages.dtype, dev)
@@ -244,9 +295,17 @@ def decode_paged(q, k_pages, v_pages, page_table, seqlen, k_sum_pages, b_sum_pag
     """HiLS single-step decode over a paged cache (one chunk per page).
     q [B,Hq,1,d]; k_pages/v_pages [P,Hkv,S,d]; page_table [B,max_pages] int32;
     seqlen [B] int32; k_sum_pages [P,Hq,d]; b_sum_pages [P,Hq].  Returns out."""
-    B, Hq, _, d = q.shape
-    P, Hkv = k_pages.shape[0], k_pages.shape[1]
-    maxp = page_table.shape[1]
+    B, Hq, one, d = _dims(q, "q", 4)
+    if one != 1:
+        raise ValueError(f"decode takes one query per sequence: q has shape {tuple(q.shape)}")
+    P, Hkv = _dims(k_pages, "k_pages", 4)[:2]
+    maxp = _dims(page_table, "page_table", 2)[1]
+    for name, t, shape in (("k_pages", k_pages, (P, Hkv, S, d)), ("v_pages", v_pages, (P, Hkv, S, d)),
+                           ("page_table", page_table, (B, maxp)), ("seqlen", seqlen, (B,)),
+                           ("k_sum_pages", k_sum_pages, (P, Hq, d)),
+                           ("b_sum_pages", b_sum_pages, (P, Hq)), ("q_route", q_route, (B, Hq, 1, d)),
+                           ("out", out, (B, Hq, 1, d)), ("sel", sel, (B, Hkv, K))):
+        _expect(t, name, shape)
     dev = q.device
     for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages),
                     ("k_sum_pages", k_sum_pages), ("q_route", q_route)):

@@ -182,3 +182,50 @@ def test_product_path_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 txt = open(os.path.join(dirpath, f), errors="ignore").read()
                 assert "oracle" not in txt.lower(), f"{f} mentions the oracle"
+
+
+def test_wrappers_reject_mis_shaped_tensors():
+    """The torch wrappers check every tensor's exact shape against (B, Hq, Hkv,
+    N, d, S, K) before anything reaches the C ABI, which takes bare pointers."""
+    import torch
+    import chunk_wise_hierarchical_amd as hils
+
+    B, Hq, Hkv, N, d, S, W, K = 1, 4, 2, 256, 16, 32, 64, 4
+    bf = dict(dtype=torch.bfloat16)
+    q = torch.zeros(B, Hq, N, d, **bf)
+    k = torch.zeros(B, Hkv, N, d, **bf)
+    v = torch.zeros(B, Hkv, N, d, **bf)
+    lm = torch.zeros(B, Hq, N // S, d, **bf)
+
+    def bad(fn, *a, **kw):
+        with pytest.raises(ValueError, match="shape|dimensions"):
+            fn(*a, **kw)
+
+    bad(hils.prefill, q, k, v, lm, S, W, K, sel=torch.zeros(B, Hkv, N, K - 1, dtype=torch.int32))
+    bad(hils.prefill, q, k[:, :, :N - 1].contiguous(), v, lm, S, W, K)
+    bad(hils.prefill, q, k, v, lm[:, :, :N // S - 1].contiguous(), S, W, K)
+    bad(hils.prefill, q, k, v, lm, S, W, K, out=torch.zeros(B, Hq, N, d + 8, **bf))
+    bad(hils.prefill, q, k, v, lm, S, W, K,
+        summaries=(torch.zeros(B, Hq, N // S + 1, d, **bf), torch.zeros(B, Hq, N // S + 1)))
+    bad(hils.summarize, k, lm[:, :, :3].contiguous(), S)
+    qd = torch.zeros(B, Hq, 1, d, **bf)
+    ks = torch.zeros(B, Hq, N // S, d, **bf)
+    bs = torch.zeros(B, Hq, N // S)
+    sl = torch.full((B,), N, dtype=torch.int32)
+    bad(hils.decode, qd, k, v, sl, ks[:, :, :2].contiguous(), bs, S, W, K)
+    bad(hils.decode, qd, k, v, torch.full((B + 1,), N, dtype=torch.int32), ks, bs, S, W, K)
+    bad(hils.decode, qd, k, v, sl, ks, bs, S, W, K, sel=torch.zeros(B, Hkv, K - 1, dtype=torch.int32))
+    bad(hils.decode, torch.zeros(B, Hq, 2, d, **bf), k, v, sl, ks, bs, S, W, K)
+    bad(hils.decode_multi, torch.zeros(B, Hq, 3, d, **bf), k, v, sl, ks, bs, S, W, K,
+        sel=torch.zeros(B, Hkv, 2, K, dtype=torch.int32))
+    bad(hils.prefill_backward, q, k, v, lm, torch.zeros(B, Hq, N - 1, d, **bf),
+        torch.zeros(B, Hkv, N, K, dtype=torch.int32), S, W, K)
+    P = 8
+    kp = torch.zeros(P, Hkv, S, d, **bf)
+    bad(hils.summarize_paged, kp, torch.zeros(P + 1, Hq, d, **bf),
+        torch.zeros(P, dtype=torch.int32), S, N)
+    bad(hils.decode_paged, qd, kp, kp, torch.zeros(B + 1, N // S, dtype=torch.int32), sl,
+        torch.zeros(P, Hq, d, **bf), torch.zeros(P, Hq), S, W, K)
+    # well-shaped host tensors get past the shape checks and stop at the device check
+    with pytest.raises(ValueError, match="GPU tensor"):
+        hils.prefill(q, k, v, lm, S, W, K)
