@@ -5,8 +5,12 @@ A step is one HiLS prefill of the prefill workload (summaries, scoring and
 top-K, window + selected-chunk attention, fusion); the decode workload's
 single-step decode is timed in the same run and reported under "decode".
 Inputs are seeded synthetic tensors (synth/) already resident in HBM when the
-timed region starts.  Per-kernel durations come from HIP events the library
-records on its own stream (hils_profile_enable) inside the timed region.
+timed region starts.  Headline times are taken with the library's kernel
+timing off; a second timed pass with it on (HIP events the library records
+around each kernel on the kernel's own stream, hils_profile_enable) gives the
+per-kernel table and the rooflines.  After the headline prefill and decode
+workloads, further workloads are timed the same way ("more_workloads": the
+64K GQA and 8K MHA prefills and the 4M-token decode by default).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_512k]
                     [--decode-workload decode_512k] [--decode-steps 50] [--no-cpu]
@@ -36,7 +40,9 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-PEAK_FP32_VALU_TFLOPS = 157.3   # MI355X fp32 vector (256 CUs at 2.4 GHz)
+# fp32 vector peak without packed-fp32 instructions (which this build turns off):
+# 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP (FMA) x 2.4 GHz = 78.6 TFLOP/s
+PEAK_FP32_VALU_TFLOPS = 78.6
 
 
 def _geometry(N, W, S):
@@ -128,6 +134,29 @@ def calibrate_copy(torch, dev, log):
     del a, b
 
 
+def timed(torch, _lib, fn, steps, profile):
+    """Mean ms per call of fn over `steps` calls between two HIP events on the
+    current stream.  With profile=True the library also brackets every kernel
+    with HIP events (hils_profile_enable) and the per-kernel table is returned;
+    the headline numbers come from runs with profile=False."""
+    torch.cuda.synchronize()
+    if profile:
+        _lib.profile_enable(True)
+        _lib.profile_read()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kt = None
+    if profile:
+        kt = _kernel_table(_lib.profile_read(), steps)
+        _lib.profile_enable(False)
+    return ms, kt
+
+
 def _kernel_table(records, steps):
     agg = {}
     for name, ms in records:
@@ -198,11 +227,13 @@ def cpu_baseline_prefill(x, w, rows=4096):
                            store=w.dtype, summaries=summ)
         t2 = time.perf_counter()
     t_full = w.Hkv * w.B * ((t1 - t0) + (t2 - t1) * w.N / rows)
-    return {"value": w.B * w.N / t_full, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": w.B * w.N / t_full, "unit": "tokens/s", "cores": 1,
+            "host_cores": os.cpu_count(), "kind": "oracle",
             "sample": (f"KV group 0 of {w.Hkv}: summaries of all {w.N // w.S} chunks "
                        f"({t1 - t0:.1f} s) + {rows} query rows spread over the sequence "
                        f"({t2 - t1:.1f} s); full prefill extrapolated = {w.Hkv * w.B} groups x "
-                       f"(summaries + rows x {w.N}/{rows}) = {t_full:.0f} s; NumPy float64, 1 BLAS thread")}
+                       f"(summaries + rows x {w.N}/{rows}) = {t_full:.0f} s; NumPy float64, 1 BLAS thread "
+                       f"(host has {os.cpu_count()} cores)")}
 
 
 def cpu_baseline_decode(xd, wd, nseq=8):
@@ -234,12 +265,14 @@ def cpu_baseline_decode(xd, wd, nseq=8):
                                    summaries=summ)
                 ts += time.perf_counter() - t0
     t_step = ts * wd.B / nseq
-    return {"value": 1.0 / t_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+    return {"value": 1.0 / t_step, "unit": "steps/s", "cores": 1,
+            "host_cores": os.cpu_count(), "kind": "oracle",
             "sample": (f"all {wd.Hkv} KV groups of sequences 0..{nseq - 1}: {ts:.2f} s for their "
                        f"single-token steps over {n}-chunk summary caches (the caches, "
                        f"{tsum:.1f} s, built by the oracle beforehand and not timed, as on the "
                        f"GPU); step time extrapolated x {wd.B}/{nseq} sequences = {t_step:.2f} s; "
-                       f"NumPy float64, 1 BLAS thread")}
+                       f"NumPy float64, 1 BLAS thread "
+                       f"(host has {os.cpu_count()} cores)")}
 
 
 def paged_decode_bench(torch, hils, _lib, xd, wd, ks, bs, steps, log):
@@ -331,18 +364,8 @@ def multi_decode_bench(torch, hils, _lib, xd, wd, ks, bs, M, steps, log):
 
     for _ in range(3):
         step()
-    torch.cuda.synchronize()
-    _lib.profile_enable(True)
-    _lib.profile_read()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    kt = _kernel_table(_lib.profile_read(), steps)
-    _lib.profile_enable(False)
+    ms, _ = timed(torch, _lib, step, steps, profile=False)
+    _, kt = timed(torch, _lib, step, steps, profile=True)
     log(f"decode block of {M} tokens {ms:.3f} ms/step; kernels {json.dumps(kt)}")
     del ws, out, sel, qm
     return {"M": M, "ms_per_step": ms, "steps_per_s": 1000.0 / ms,
@@ -370,18 +393,8 @@ def backward_bench(torch, hils, _lib, wb, steps, log):
 
     for _ in range(2):
         step()
-    torch.cuda.synchronize()
-    _lib.profile_enable(True)
-    _lib.profile_read()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    kt = _kernel_table(_lib.profile_read(), steps)
-    _lib.profile_enable(False)
+    ms, _ = timed(torch, _lib, step, steps, profile=False)
+    _, kt = timed(torch, _lib, step, steps, profile=True)
     # algorithmic FLOPs: per attended (query, head, token) the five products of an
     # attention backward (logit and dout.v recompute, dq, dk, dv): 10 d
     n, win = _geometry(wb.N, wb.W, wb.S)
@@ -399,6 +412,144 @@ def backward_bench(torch, hils, _lib, wb, steps, log):
             "kernels": kt}
 
 
+def prefill_bench(torch, hils, _lib, w, steps, warmup, union, log, want_sel=False):
+    """One workload's prefill: the headline time with the library's kernel
+    timing off, then a second timed pass with it on for the per-kernel table
+    and the rooflines.  Rooflines are useful (algorithmic) FLOPs against the
+    bf16 MFMA peak: per kernel (FLOPs per launch over the kernel's average
+    launch time) and for the whole step."""
+    dev = torch.device("cuda:0")
+    log(f"prefill inputs {w.name}: B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} d={w.d} S={w.S} "
+        f"W={w.W} K={w.K}")
+    x = synth_inputs(w, dev)
+    out = torch.empty_like(x["q"])
+    sel = torch.empty((w.B, w.Hkv, w.N, w.K), dtype=torch.int32, device=dev)
+    cfg = hils.make_cfg(w.B, w.N, w.Hq, w.Hkv, w.d, w.S, w.W, w.K, x["q"].dtype, union=union)
+    ws = torch.empty(max(1, hils.workspace_bytes(cfg, False)), dtype=torch.uint8, device=dev)
+
+    def step():
+        hils.prefill(x["q"], x["k"], x["v"], x["lm"], w.S, w.W, w.K, out=out, sel=sel, ws=ws,
+                     union=union)
+
+    for _ in range(warmup):
+        step()
+    ms, _ = timed(torch, _lib, step, steps, profile=False)
+    ms_prof, kern = timed(torch, _lib, step, steps, profile=True)
+    log(f"prefill {w.name} {ms:.3f} ms/step ({ms_prof:.3f} with kernel timing); "
+        f"kernels {json.dumps(kern)}")
+    score_f, summ_f, attn_f = prefill_work(w)
+    win_f, sel_f = window_work(w)
+    # algorithmic FLOPs per step of the contraction kernels; per launch is that
+    # over the launches per step (the bucket-path kernels run once per slice)
+    step_flops = {"k_attn_fast": attn_f, "k_attn_generic": attn_f, "k_score_fast": score_f,
+                  "k_select_generic": score_f, "k_summarize": summ_f, "k_win_fast": win_f,
+                  "k_pair_attn": sel_f}
+
+    def roofline(kname):
+        launches = kern[kname]["calls"] / steps
+        per_launch = step_flops[kname] / launches
+        achieved = per_launch / (kern[kname]["avg_ms"] * 1e-3) / 1e12
+        return {"kernel": kname, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": counter_traffic(kname, w.name),
+                "algorithmic_flops_per_launch": per_launch, "launches_per_step": launches}
+
+    rooflines = {k2: roofline(k2) for k2 in kern if k2 in step_flops}
+    # design-traffic diagnostic: the bucket path's pair attention and reduction
+    # move per-pair gathers and partial rows, counted from the selection
+    hbm_rooflines = {}
+    if "k_pair_attn" in kern:
+        attn_b, red_b = pair_path_bytes(sel, w, kern["k_pair_attn"]["calls"] / steps)
+        for kname, step_bytes in (("k_pair_attn", attn_b), ("k_pair_reduce", red_b)):
+            if kname not in kern:
+                continue
+            launches = kern[kname]["calls"] / steps
+            per_launch = step_bytes / launches
+            achieved = per_launch / (kern[kname]["avg_ms"] * 1e-3) / 1e9
+            hbm_rooflines[kname] = {"kernel": kname, "bound": "hbm", "achieved": achieved,
+                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": achieved / PEAK_HBM_GBS,
+                                    "traffic": counter_traffic(kname, w.name),
+                                    "design_bytes_per_launch": per_launch,
+                                    "launches_per_step": launches}
+    # the dominant kernel among those doing the method's contractions
+    dom = max(rooflines, key=lambda k2: kern[k2]["ms_per_step"])
+    total_flops = score_f + summ_f + attn_f
+    step_tflops = total_flops / (ms * 1e-3) / 1e12
+    rec = {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.N / (ms * 1e-3),
+           "ms_per_step_with_kernel_timing": ms_prof,
+           "config": {"workload": w.name, "B": w.B, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
+                      "S": w.S, "W": w.W, "K": w.K, "regime": w.regime,
+                      "attention": "query-block unions" if union else "chunk buckets"},
+           "algorithmic_tflop": {"scoring": score_f / 1e12, "summaries": summ_f / 1e12,
+                                 "attention": attn_f / 1e12},
+           "roofline": rooflines[dom],
+           "step_roofline": {"bound": "mfma", "achieved": step_tflops, "peak": PEAK_BF16_TFLOPS,
+                             "unit": "TFLOP/s", "frac": step_tflops / PEAK_BF16_TFLOPS,
+                             "algorithmic_flops_per_step": total_flops},
+           "kernel_rooflines": rooflines, "design_traffic_hbm": hbm_rooflines, "kernels": kern}
+    if w.N >= 16 * 64:
+        rec["config"]["chunk_overlap_M16"] = _overlap(sel, w.K)
+    del out, ws
+    if not want_sel:
+        del sel, x
+        torch.cuda.empty_cache()
+        return rec, None, None
+    return rec, x, sel
+
+
+def synth_inputs(w, dev):
+    import synth
+    return synth.make_prefill_inputs(w, device=dev)
+
+
+def decode_bench(torch, hils, _lib, wd, steps, warmup, log, keep=False):
+    """Single-step decode of every sequence of the workload (the cache is full,
+    T = capacity), headline time with kernel timing off, then the kernel table."""
+    import synth
+    dev = torch.device("cuda:0")
+    log(f"decode inputs {wd.name}: B={wd.B} T={wd.N} Hq={wd.Hq} Hkv={wd.Hkv} W={wd.W} K={wd.K}")
+    xd = synth.make_decode_inputs(wd, device=dev)
+    ks, bs = hils.summarize(xd["k"], xd["lm"], wd.S)
+    outd = torch.empty_like(xd["q"])
+    cfgd = hils.make_cfg(wd.B, wd.N, wd.Hq, wd.Hkv, wd.d, wd.S, wd.W, wd.K, xd["q"].dtype)
+    wsd = torch.empty(max(1, hils.workspace_bytes(cfgd, True)), dtype=torch.uint8, device=dev)
+
+    def dstep():
+        hils.decode(xd["q"], xd["k"], xd["v"], xd["seqlen"], ks, bs, wd.S, wd.W, wd.K,
+                    out=outd, ws=wsd)
+
+    for _ in range(max(3, warmup)):
+        dstep()
+    dec_ms, _ = timed(torch, _lib, dstep, steps, profile=False)
+    ms_prof, dk = timed(torch, _lib, dstep, steps, profile=True)
+    log(f"decode {wd.name} {dec_ms:.4f} ms/step ({ms_prof:.4f} with kernel timing); "
+        f"kernels {json.dumps(dk)}")
+    step_bytes, score_bytes = decode_work(wd, wd.N)
+    sc = dk.get("k_dec_score")
+    dach = score_bytes / (sc["avg_ms"] * 1e-3) / 1e9 if sc else None
+    step_gbs = step_bytes / (dec_ms * 1e-3) / 1e9
+    rec = {"workload": wd.name, "metric": "decode steps/s", "value": 1000.0 / dec_ms,
+           "unit": "steps/s", "ms_per_step": dec_ms, "tokens_per_s": wd.B * 1000.0 / dec_ms,
+           "ms_per_step_with_kernel_timing": ms_prof,
+           "config": {"workload": wd.name, "B": wd.B, "T": wd.N, "Hq": wd.Hq, "Hkv": wd.Hkv,
+                      "d": wd.d, "S": wd.S, "W": wd.W, "K": wd.K},
+           "step_roofline": {"bound": "hbm", "achieved": step_gbs, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": step_gbs / PEAK_HBM_GBS,
+                             "algorithmic_bytes_per_step": step_bytes},
+           "roofline": {"kernel": "k_dec_score", "bound": "hbm", "achieved": dach,
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": (dach / PEAK_HBM_GBS) if dach else None,
+                        "traffic": counter_traffic("k_dec_score", wd.name),
+                        "algorithmic_bytes_per_launch": score_bytes},
+           "kernels": dk}
+    if keep:
+        return rec, (xd, ks, bs)
+    del xd, ks, bs, outd, wsd
+    torch.cuda.empty_cache()
+    return rec, None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -407,6 +558,10 @@ def main():
     ap.add_argument("--workload", default="prefill_512k")
     ap.add_argument("--decode-workload", default="decode_512k")
     ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--more-prefill", default="prefill_64k,prefill_8k",
+                    help="further prefill workloads timed after the headline one ('' skips)")
+    ap.add_argument("--more-decode", default="decode_4m",
+                    help="further decode workloads timed after the headline one ('' skips)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--union", action="store_true",
@@ -437,133 +592,30 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(torch, dev, log)
 
-    # ---------------- prefill ----------------
+    # ---------------- prefill (headline workload) ----------------
     w = synth.get_workload(args.workload)
-    log(f"prefill inputs {w.name}: B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} d={w.d} S={w.S} W={w.W} K={w.K}")
-    x = synth.make_prefill_inputs(w, device=dev)
-    out = torch.empty_like(x["q"])
-    sel = torch.empty((w.B, w.Hkv, w.N, w.K), dtype=torch.int32, device=dev)
-    cfg = hils.make_cfg(w.B, w.N, w.Hq, w.Hkv, w.d, w.S, w.W, w.K, x["q"].dtype, union=args.union)
-    ws = torch.empty(max(1, hils.workspace_bytes(cfg, False)), dtype=torch.uint8, device=dev)
-
-    def step():
-        hils.prefill(x["q"], x["k"], x["v"], x["lm"], w.S, w.W, w.K, out=out, sel=sel, ws=ws,
-                     union=args.union)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log("prefill warm")
-    _lib.profile_enable(True)
-    _lib.profile_read()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    prefill_ms = e0.elapsed_time(e1) / args.steps
-    kern = _kernel_table(_lib.profile_read(), args.steps)
-    _lib.profile_enable(False)
-    log(f"prefill {prefill_ms:.2f} ms/step; kernels {json.dumps(kern)}")
-    overlap = _overlap(sel, w.K)
-
-    score_f, summ_f, attn_f = prefill_work(w)
-    win_f, sel_f = window_work(w)
-    # algorithmic FLOPs per step of the contraction kernels; per launch is that
-    # over the launches per step (the bucket-path kernels run once per slice)
-    step_flops = {"k_attn_fast": attn_f, "k_attn_generic": attn_f, "k_score_fast": score_f,
-                  "k_select_generic": score_f, "k_summarize": summ_f, "k_win_fast": win_f,
-                  "k_pair_attn": sel_f}
-
-    def roofline(kname):
-        launches = kern[kname]["calls"] / args.steps
-        per_launch = step_flops[kname] / launches
-        achieved = per_launch / (kern[kname]["avg_ms"] * 1e-3) / 1e12
-        return {"kernel": kname, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": counter_traffic(kname, w.name),
-                "algorithmic_flops_per_launch": per_launch, "launches_per_step": launches}
-
-    rooflines = {k2: roofline(k2) for k2 in kern if k2 in step_flops}
-    # the bucket path's pair attention and reduction are bound by HBM: their
-    # algorithmic bytes per launch against the HBM peak
-    hbm_rooflines = {}
-    if "k_pair_attn" in kern:
-        attn_b, red_b = pair_path_bytes(sel, w, kern["k_pair_attn"]["calls"] / args.steps)
-        for kname, step_bytes in (("k_pair_attn", attn_b), ("k_pair_reduce", red_b)):
-            if kname not in kern:
-                continue
-            launches = kern[kname]["calls"] / args.steps
-            per_launch = step_bytes / launches
-            achieved = per_launch / (kern[kname]["avg_ms"] * 1e-3) / 1e9
-            hbm_rooflines[kname] = {"kernel": kname, "bound": "hbm", "achieved": achieved,
-                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                    "frac": achieved / PEAK_HBM_GBS,
-                                    "traffic": counter_traffic(kname, w.name),
-                                    "algorithmic_bytes_per_launch": per_launch,
-                                    "launches_per_step": launches}
-    dom = max(kern, key=lambda k2: kern[k2]["ms_per_step"])
-    roof = (hbm_rooflines.get(dom) or rooflines.get(dom)
-            or max(rooflines.values(), key=lambda r: kern[r["kernel"]]["ms_per_step"]))
-    total_tflops = (score_f + summ_f + attn_f) / (prefill_ms * 1e-3) / 1e12
-
+    pre, x, sel = prefill_bench(torch, hils, _lib, w, args.steps, args.warmup, args.union, log,
+                                want_sel=not args.no_cpu)
     cpu_pre = None
     if not args.no_cpu:
         log("oracle baseline (prefill sample)")
         cpu_pre = cpu_baseline_prefill(x, w)
-    del x, out, ws
-    sel_cpu_overlap = overlap
-    del sel
+    del x, sel
     torch.cuda.empty_cache()
+
+    more = {}
+    for name in [n for n in args.more_prefill.split(",") if n]:
+        wm = synth.get_workload(name)
+        more[name], _, _ = prefill_bench(torch, hils, _lib, wm, max(args.steps, 10),
+                                         args.warmup, args.union, log)
 
     # ---------------- decode ----------------
     dec = None
     if not args.no_decode:
         wd = synth.get_workload(args.decode_workload)
-        log(f"decode inputs {wd.name}: B={wd.B} T={wd.N} Hq={wd.Hq} Hkv={wd.Hkv} W={wd.W} K={wd.K}")
-        xd = synth.make_decode_inputs(wd, device=dev)
-        ks, bs = hils.summarize(xd["k"], xd["lm"], wd.S)
-        outd = torch.empty_like(xd["q"])
-        cfgd = hils.make_cfg(wd.B, wd.N, wd.Hq, wd.Hkv, wd.d, wd.S, wd.W, wd.K, xd["q"].dtype)
-        wsd = torch.empty(max(1, hils.workspace_bytes(cfgd, True)), dtype=torch.uint8, device=dev)
-
-        def dstep():
-            hils.decode(xd["q"], xd["k"], xd["v"], xd["seqlen"], ks, bs, wd.S, wd.W, wd.K,
-                        out=outd, ws=wsd)
-
-        for _ in range(max(3, args.warmup)):
-            dstep()
-        torch.cuda.synchronize()
-        _lib.profile_enable(True)
-        _lib.profile_read()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(args.decode_steps):
-            dstep()
-        e1.record()
-        torch.cuda.synchronize()
-        dec_ms = e0.elapsed_time(e1) / args.decode_steps
-        dk = _kernel_table(_lib.profile_read(), args.decode_steps)
-        _lib.profile_enable(False)
-        log(f"decode {dec_ms:.3f} ms/step; kernels {json.dumps(dk)}")
-        step_bytes, score_bytes = decode_work(wd, wd.N)
-        sc = dk.get("k_dec_score")
-        dach = score_bytes / (sc["avg_ms"] * 1e-3) / 1e9 if sc else None
-        dec = {"workload": wd.name, "metric": "decode steps/s", "value": 1000.0 / dec_ms,
-               "unit": "steps/s", "ms_per_step": dec_ms, "tokens_per_s": wd.B * 1000.0 / dec_ms,
-               "config": {"workload": wd.name, "B": wd.B, "T": wd.N, "Hq": wd.Hq, "Hkv": wd.Hkv,
-                          "d": wd.d, "S": wd.S, "W": wd.W, "K": wd.K},
-               "step_hbm_gbs": step_bytes / (dec_ms * 1e-3) / 1e9,
-               "step_frac_hbm": step_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-               "algorithmic_bytes_per_step": step_bytes,
-               "roofline": {"kernel": "k_dec_score", "bound": "hbm", "achieved": dach,
-                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                            "frac": (dach / PEAK_HBM_GBS) if dach else None,
-                            "traffic": counter_traffic("k_dec_score", wd.name),
-                            "algorithmic_bytes_per_launch": score_bytes},
-               "kernels": dk}
+        dec, kept = decode_bench(torch, hils, _lib, wd, args.decode_steps, args.warmup, log,
+                                 keep=True)
+        xd, ks, bs = kept
         # the same step over a paged cache (one chunk per page, pages randomly
         # placed), eagerly and replayed from a captured HIP graph
         dec["paged"] = paged_decode_bench(torch, hils, _lib, xd, wd, ks, bs, args.decode_steps, log)
@@ -573,41 +625,42 @@ def main():
         if not args.no_cpu:
             log("oracle baseline (decode sample)")
             dec["cpu_baseline"] = cpu_baseline_decode(xd, wd)
-        del xd, ks, bs, outd, wsd
+        del xd, ks, bs, kept
+        torch.cuda.empty_cache()
+        for name in [n for n in args.more_decode.split(",") if n]:
+            more[name], _ = decode_bench(torch, hils, _lib, synth.get_workload(name),
+                                         args.decode_steps, args.warmup, log)
 
     bwd = None
     if args.backward_workload:
-        import synth
         torch.cuda.empty_cache()
         bwd = backward_bench(torch, hils, _lib, synth.get_workload(args.backward_workload),
                              args.steps, log)
 
     line = {
         "metric": "prefill tokens/s and decode steps/s at 512K ctx; % of MFMA/HBM roofline",
-        "value": w.B * w.N / (prefill_ms * 1e-3),
+        "value": pre["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": prefill_ms,
+        "ms_per_step": pre["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
-                   "S": w.S, "W": w.W, "K": w.K, "regime": w.regime,
-                   "attention": "query-block unions" if args.union else "chunk buckets",
-                   "chunk_overlap_M16": sel_cpu_overlap},
-        "useful_tflops_total": total_tflops,
-        "algorithmic_tflop": {"scoring": score_f / 1e12, "summaries": summ_f / 1e12,
-                              "attention": attn_f / 1e12},
-        "roofline": roof,
-        "kernel_rooflines": rooflines,
-        "hbm_rooflines": hbm_rooflines,
+        "config": pre["config"],
+        "roofline": pre["roofline"],
+        "step_roofline": pre["step_roofline"],
+        "algorithmic_tflop": pre["algorithmic_tflop"],
+        "kernel_rooflines": pre["kernel_rooflines"],
+        "design_traffic_hbm": pre["design_traffic_hbm"],
         "cpu_baseline": cpu_pre,
-        "kernels": kern,
+        "kernels": pre["kernels"],
+        "ms_per_step_with_kernel_timing": pre["ms_per_step_with_kernel_timing"],
         "decode": dec,
+        "more_workloads": more,
         "backward": bwd,
     }
     print(json.dumps(line), flush=True)
