@@ -21,7 +21,9 @@ HILS_MAX_DECODE_QUERIES = 16
 EXPORTED = ("hils_workspace_bytes", "hils_summarize", "hils_prefill", "hils_decode",
             "hils_summarize_paged", "hils_decode_paged", "hils_decode_multi_workspace_bytes",
             "hils_decode_multi", "hils_prefill_backward_workspace_bytes", "hils_prefill_backward",
-            "hils_strerror", "hils_abi_version", "hils_profile_enable", "hils_profile_read")
+            "hils_strerror", "hils_abi_version", "hils_profile_enable", "hils_profile_read",
+            "hils_decode_noalloc")
+HILS_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class HilsCfg(ctypes.Structure):
@@ -59,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.hils_prefill.restype = ctypes.c_int
         L.hils_decode.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.hils_decode.restype = ctypes.c_int
+        L.hils_decode_noalloc.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.hils_decode_noalloc.restype = ctypes.c_int
         L.hils_summarize_paged.argtypes = [cfgp, vp, vp, vp, i32, i32, vp, vp, vp]
         L.hils_summarize_paged.restype = ctypes.c_int
         L.hils_decode_paged.argtypes = [cfgp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp,

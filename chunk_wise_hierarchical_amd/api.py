@@ -175,6 +175,39 @@ def decode(q, k_cache, v_cache, seqlen, k_sum, b_sum, S, W, K, q_route=None, mod
     return out
 
 
+def decode_noalloc(q, k_cache, v_cache, seqlen, k_sum, b_sum, S, W, K, q_route=None,
+                   mode="surrogate", scale=0.0, out=None, sel=None):
+    """hils_decode_noalloc: the single-step decode with the library's own
+    per-GPU scratch instead of a workspace (no device allocation in the call
+    when `out` is given).  Same arguments and result as decode() without ws."""
+    B, Hq, one, d = _dims(q, "q", 4)
+    if one != 1:
+        raise ValueError(f"decode takes one query per sequence: q has shape {tuple(q.shape)}")
+    Hkv, T = _dims(k_cache, "k_cache", 4)[1:3]
+    nC = T // S if S > 0 else 0
+    for name, t, shape in (("k_cache", k_cache, (B, Hkv, T, d)), ("v_cache", v_cache, (B, Hkv, T, d)),
+                           ("seqlen", seqlen, (B,)), ("k_sum", k_sum, (B, Hq, nC, d)),
+                           ("b_sum", b_sum, (B, Hq, nC)), ("q_route", q_route, (B, Hq, 1, d)),
+                           ("out", out, (B, Hq, 1, d)), ("sel", sel, (B, Hkv, K))):
+        _expect(t, name, shape)
+    dev = q.device
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("k_sum", k_sum),
+                    ("q_route", q_route)):
+        _check_tensor(t, name, q.dtype, dev)
+    _check_tensor(seqlen, "seqlen", torch.int32, dev)
+    _check_tensor(b_sum, "b_sum", torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor(out, "out", q.dtype, dev)
+    _check_tensor(sel, "sel", torch.int32, dev)
+    cfg = make_cfg(B, T, Hq, Hkv, d, S, W, K, q.dtype, mode, scale)
+    st = _lib.lib().hils_decode_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(q_route), _ptr(k_cache),
+                                        _ptr(v_cache), _ptr(seqlen), _ptr(k_sum), _ptr(b_sum),
+                                        _ptr(out), _ptr(sel), _stream(dev))
+    check(st, "hils_decode_noalloc")
+    return out
+
+
 def decode_multi(q, k_cache, v_cache, seqlen, k_sum, b_sum, S, W, K, q_route=None,
                  mode="surrogate", scale=0.0, out=None, sel=None, ws=None):
     """HiLS decode of M new tokens per sequence. q [B,Hq,M,d] (token m at position

@@ -163,6 +163,18 @@ hils_status bwd_supported(const HilsShape& s) {
 
 inline hils_status hip_status(hipError_t e) { return e == hipSuccess ? HILS_OK : HILS_E_HIP; }
 
+// ---- scratch of the allocation-free decode entry point --------------------
+// Device addresses of `scratch` (defined below, outside this namespace), one
+// per device: each GPU holds its own copy of the array at its own address,
+// which only hipGetSymbolAddress with that device current can tell.  In host
+// code the array's name is a host-side stand-in and is never passed to a
+// kernel or a copy.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hils_status scratch_ptr_current_device(void** out);
+
 // ---- kernel timing record ------------------------------------------------
 struct ProfRec {
   const char* name;
@@ -184,6 +196,25 @@ hipEvent_t prof_event() {
   return e;
 }
 
+}  // namespace
+
+// Scratch of hils_decode_noalloc: file scope, 256-byte aligned, the size the
+// header states; zero-initialised once at load and never freed.
+static __device__ __align__(256) unsigned char scratch[HILS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+hils_status scratch_ptr_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HILS_E_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HILS_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HILS_OK;
+}
 }  // namespace
 
 HilsProfScope::HilsProfScope(const char* name, hipStream_t s) : slot(-1), st(s) {
@@ -353,6 +384,26 @@ hils_status hils_decode(const hils_cfg* cfg, const void* q, const void* q_route,
                                        (float*)(w + L.scores), (uint32_t*)(w + L.keys),
                                        (float*)(w + L.slog), (float*)(w + L.part),
                                        (float*)(w + L.lsep), nullptr, 0, 0, (hipStream_t)stream));
+}
+
+hils_status hils_decode_noalloc(const hils_cfg* cfg, const void* q, const void* q_route,
+                                const void* k_cache, const void* v_cache, const int32_t* seqlen,
+                                const void* k_sum, const float* b_sum, void* out, int32_t* sel,
+                                void* stream) {
+  HilsShape s;
+  hils_status r = make_shape(cfg, s);
+  if (r != HILS_OK) return r;
+  if (s.mode == HILS_SCORE_EXACT) return HILS_E_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !seqlen || !out) return HILS_E_ARG;
+  // the scratch must hold this configuration's decode workspace
+  const size_t need = decode_layout(s).total;
+  if (need > HILS_NOALLOC_SCRATCH_BYTES) return HILS_E_WORKSPACE;
+  void* ws = nullptr;
+  r = scratch_ptr_current_device(&ws);
+  if (r != HILS_OK) return r;
+  // the regular entry point validates the rest and enqueues the same kernels
+  return hils_decode(cfg, q, q_route, k_cache, v_cache, seqlen, k_sum, b_sum, out, sel, ws,
+                     HILS_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t hils_decode_multi_workspace_bytes(const hils_cfg* cfg, int32_t M) {

@@ -136,6 +136,26 @@ hils_status hils_decode(const hils_cfg* cfg, const void* q, const void* q_route,
                         const void* k_sum, const float* b_sum, void* out, int32_t* sel,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Allocation-free single-step decode, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, result and errors
+ * as hils_decode without ws/ws_bytes; the scratch comes from a buffer of
+ * HILS_NOALLOC_SCRATCH_BYTES that the library keeps in device memory, one per
+ * GPU it runs on (held until the process ends; its address is looked up once
+ * per device, on the first call with that device current).  The call
+ * allocates nothing.  Configurations whose decode workspace
+ * (hils_workspace_bytes(cfg, 1)) exceeds HILS_NOALLOC_SCRATCH_BYTES return
+ * HILS_E_WORKSPACE before anything is enqueued.  Every call on one GPU shares
+ * that GPU's buffer: calls that overlap in time on one GPU (different streams
+ * or host threads without ordering between them) race and give undefined
+ * results; calls on one stream are ordered and safe.  The buffer keeps the
+ * last call's contents; the decode kernels need no zeroed scratch. */
+#define HILS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hils_status hils_decode_noalloc(const hils_cfg* cfg, const void* q, const void* q_route,
+                                const void* k_cache, const void* v_cache, const int32_t* seqlen,
+                                const void* k_sum, const float* b_sum, void* out, int32_t* sel,
+                                void* stream);
+
 /* Multi-query decode: M new tokens of each sequence (draft or verification
  * tokens, 1 <= M <= HILS_MAX_DECODE_QUERIES) are already in the cache at
  * positions T_b - M .. T_b - 1 (T_b = seqlen[b] >= M), and query m is the

@@ -229,3 +229,15 @@ def test_wrappers_reject_mis_shaped_tensors():
     # well-shaped host tensors get past the shape checks and stop at the device check
     with pytest.raises(ValueError, match="GPU tensor"):
         hils.prefill(q, k, v, lm, S, W, K)
+
+
+def test_decode_noalloc_refuses_oversized_workspace_before_any_launch(L):
+    """The allocation-free decode checks its scratch size before it looks up
+    the device buffer or enqueues anything (so this runs without a GPU)."""
+    c = _cfg(B=16, N=1 << 22, Hq=32, Hkv=8, W=2048, K=64)
+    assert L.hils_workspace_bytes(ctypes.byref(c), 1) > _lib.HILS_NOALLOC_SCRATCH_BYTES
+    p = ctypes.c_void_p(4096)          # never dereferenced: the call returns first
+    st = L.hils_decode_noalloc(ctypes.byref(c), p, None, p, p, p, p, p, p, None, None)
+    assert st == _lib.HILS_E_WORKSPACE
+    bad = _cfg(Hq=7, Hkv=2)
+    assert L.hils_decode_noalloc(ctypes.byref(bad), p, None, p, p, p, p, p, p, None, None) == _lib.HILS_E_ARG
