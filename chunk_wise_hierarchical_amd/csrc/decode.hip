@@ -200,13 +200,24 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   m = M;
 }
 
-constexpr int SEL_LDS_KEYS = 24576;   // keys kept in LDS (96 KB) when the candidate set fits
+constexpr int SEL_LDS_KEYS = HILS_DEC_SEL_LDS_KEYS;   // keys kept in LDS (96 KB) when they fit
 
+// Exact top-K of the group scores, ties to the lower chunk id.  A query with
+// at most `span` candidates takes one workgroup (SEL_WHOLE).  A longer
+// candidate list is cut into P partitions of `span` chunks: SEL_PART finds
+// each partition's own top-K (the global top-K is contained in the union of
+// the partitions' top-K lists under the same order) and writes it as
+// (key, chunk id) in ascending chunk order, and SEL_MERGE selects the top-K
+// of those P * K candidates; the merged list is in ascending chunk order too,
+// so both paths take tied keys lowest chunk id first.
+enum { SEL_WHOLE = 0, SEL_PART = 1, SEL_MERGE = 2 };
+
+template <int PH>
 __global__ void __launch_bounds__(SEL_NT)
 k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
-             const int32_t* __restrict__ seqlen, uint32_t* __restrict__ keys,
+             const int32_t* __restrict__ seqlen, uint32_t* __restrict__ keys, uint2* __restrict__ cand,
              int32_t* __restrict__ sel, float* __restrict__ slog, int Hq, int Hkv, int G, int nmax,
-             int nsb, int N, int S, int W, int K, int M) {
+             int nsb, int N, int S, int W, int K, int M, int span, int P) {
   extern __shared__ uint32_t sel_keys_lds[];
   __shared__ uint32_t hist[256];
   __shared__ float Lh[8];
@@ -215,6 +226,7 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bgm = blockIdx.x;                 // (sequence, KV group, query)
+  const int part = (PH == SEL_PART) ? (int)blockIdx.y : 0;
   const int m = bgm % M, bg = bgm / M;
   const int b = bg / Hkv, g = bg % Hkv;
   const int n = n_cand(dec_pos(seqlen[b], N, M, m), W, S);
@@ -222,61 +234,82 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
   // per-head rows of this query: ((b * Hq + g * G + r) * M + m)
   auto hrow = [&](int r) { return ((long long)b * Hq + (long long)g * G + r) * M + m; };
   int32_t* so = sel + (long long)bgm * K;
-  for (int t = tid; t < K; t += SEL_NT) if (t >= kk) so[t] = -1;
-  for (int t = tid; t < G * K; t += SEL_NT) {
-    const int r = t / K, kx = t % K;
-    if (kx >= kk) slog[hrow(r) * K + kx] = 0.0f;
-  }
-  if (n == 0) return;
-  uint32_t* ky = (n <= SEL_LDS_KEYS) ? sel_keys_lds : keys + (long long)bgm * nmax;
-
-  if (G > 1) {
-    // per-head log-sum-exp from the scoring workgroups' (max, sum exp) partials
-    for (int r = wv; r < G; r += SEL_NW) {
-      const float* lp = lsep + hrow(r) * nsb * 2;
-      float m = -INFINITY, s = 0.0f;
-      for (int t = lane; t < nsb; t += 64) lse_merge(m, s, lp[2 * t], lp[2 * t + 1]);
-#pragma unroll
-      for (int msk = 32; msk >= 1; msk >>= 1) {
-        const float m2 = __shfl_xor(m, msk, 64), s2 = __shfl_xor(s, msk, 64);
-        lse_merge(m, s, m2, s2);
-      }
-      if (lane == 0) Lh[r] = m + __logf(s);
+  uint2* co = cand + ((long long)bgm * P + part) * K;   // this partition's candidate slots
+  // the candidate range of this workgroup: chunks [c0, c0 + cnt) (SEL_MERGE:
+  // the P * K candidate slots)
+  const int c0 = (PH == SEL_PART) ? part * span : 0;
+  const int cnt = (PH == SEL_WHOLE) ? n : (PH == SEL_PART) ? max(0, min(n - c0, span)) : P * K;
+  const int kl = (PH == SEL_PART) ? min(K, cnt) : kk;   // keys this workgroup selects
+  if (PH != SEL_PART) {
+    for (int t = tid; t < K; t += SEL_NT) if (t >= kk) so[t] = -1;
+    for (int t = tid; t < G * K; t += SEL_NT) {
+      const int r = t / K, kx = t % K;
+      if (kx >= kk) slog[hrow(r) * K + kx] = 0.0f;
     }
-    __syncthreads();
+  } else {
+    for (int t = tid; t < K; t += SEL_NT) if (t >= kl) co[t] = make_uint2(0u, 0xffffffffu);
   }
-  constexpr int KU = 4;
-  for (int base = 0; base < n; base += KU * SEL_NT) {
-    float gs[KU];
+  if (kk == 0 || kl == 0) return;
+  uint32_t* ky = (cnt <= SEL_LDS_KEYS) ? sel_keys_lds : keys + (long long)bgm * nmax + c0;
+  // SEL_MERGE: candidate chunk ids next to their keys in LDS (cnt <= 8192)
+  int32_t* cid = reinterpret_cast<int32_t*>(sel_keys_lds) + cnt;
+
+  if (PH == SEL_MERGE) {
+    const uint2* ci = cand + (long long)bgm * P * K;
+    for (int t = tid; t < cnt; t += SEL_NT) {
+      const uint2 e = ci[t];
+      ky[t] = e.x;                           // empty slots hold key 0, below every score
+      cid[t] = (int32_t)e.y;
+    }
+  } else {
+    if (G > 1) {
+      // per-head log-sum-exp from the scoring workgroups' (max, sum exp) partials
+      for (int r = wv; r < G; r += SEL_NW) {
+        const float* lp = lsep + hrow(r) * nsb * 2;
+        float m = -INFINITY, s = 0.0f;
+        for (int t = lane; t < nsb; t += 64) lse_merge(m, s, lp[2 * t], lp[2 * t + 1]);
 #pragma unroll
-    for (int u = 0; u < KU; ++u) gs[u] = -INFINITY;
-    for (int r = 0; r < G; ++r) {
-      const float* sr = scores + hrow(r) * nmax;
-      const float lr = (G == 1) ? 0.0f : Lh[r];
-      float x[KU];
+        for (int msk = 32; msk >= 1; msk >>= 1) {
+          const float m2 = __shfl_xor(m, msk, 64), s2 = __shfl_xor(s, msk, 64);
+          lse_merge(m, s, m2, s2);
+        }
+        if (lane == 0) Lh[r] = m + __logf(s);
+      }
+      __syncthreads();
+    }
+    constexpr int KU = 4;
+    for (int base = 0; base < cnt; base += KU * SEL_NT) {
+      float gs[KU];
+#pragma unroll
+      for (int u = 0; u < KU; ++u) gs[u] = -INFINITY;
+      for (int r = 0; r < G; ++r) {
+        const float* sr = scores + hrow(r) * nmax + c0;
+        const float lr = (G == 1) ? 0.0f : Lh[r];
+        float x[KU];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+          const int c = base + u * SEL_NT + tid;
+          x[u] = (c < cnt) ? sr[c] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < KU; ++u) gs[u] = fmaxf(gs[u], x[u] - lr);
+      }
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
         const int c = base + u * SEL_NT + tid;
-        x[u] = (c < n) ? sr[c] : -INFINITY;
+        if (c < cnt) ky[c] = f32_order_key(gs[u]);
       }
-#pragma unroll
-      for (int u = 0; u < KU; ++u) gs[u] = fmaxf(gs[u], x[u] - lr);
-    }
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int c = base + u * SEL_NT + tid;
-      if (c < n) ky[c] = f32_order_key(gs[u]);
     }
   }
-  if (tid == 0) sh_need = kk;
+  if (tid == 0) sh_need = kl;
   __syncthreads();
 
-  // MSD radix select of the kk-th largest 32-bit key
+  // MSD radix select of the kl-th largest 32-bit key
   uint32_t prefix = 0, pmask = 0;
   for (int p = 3; p >= 0; --p) {
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int c = tid; c < n; c += SEL_NT) {
+    for (int c = tid; c < cnt; c += SEL_NT) {
       const uint32_t key = ky[c];
       if ((key & pmask) == prefix) atomicAdd(&hist[(key >> (8 * p)) & 255u], 1u);
     }
@@ -311,22 +344,22 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
     __syncthreads();
   }
   const uint32_t thr = prefix;
-  const int need_eq = sh_need;   // how many keys equal to thr to take (lowest chunk ids)
+  const int need_eq = sh_need;   // how many keys equal to thr to take (lowest positions)
 
-  // compaction in ascending chunk order: thread t owns chunks [8t, 8t + 8) of
-  // each round of 8 * SEL_NT; one block scan of its (greater, equal) counts
-  // gives where its selected chunks go.  Keys equal to thr are taken lowest
-  // chunk id first, need_eq of them.
+  // compaction in ascending position order: thread t owns positions [8t, 8t + 8)
+  // of each round of 8 * SEL_NT; one block scan of its (greater, equal) counts
+  // gives where its selected entries go.  Keys equal to thr are taken lowest
+  // position (= lowest chunk id) first, need_eq of them.
   constexpr int CPT = 8;
   int taken_all = 0, eq_all = 0;
-  for (int base = 0; base < n; base += CPT * SEL_NT) {
-    const int c0 = base + CPT * tid;
+  for (int base = 0; base < cnt; base += CPT * SEL_NT) {
+    const int q0 = base + CPT * tid;
     uint32_t kv[CPT];
     int ngt = 0, neq = 0;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      kv[u] = (c0 + u < n) ? ky[c0 + u] : 0u;
-      const bool in = c0 + u < n;
+      kv[u] = (q0 + u < cnt) ? ky[q0 + u] : 0u;
+      const bool in = q0 + u < cnt;
       ngt += (in && kv[u] > thr) ? 1 : 0;
       neq += (in && kv[u] == thr) ? 1 : 0;
     }
@@ -354,13 +387,18 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
     int eqi = eq_before;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int c = c0 + u;
-      if (c < n) {
+      const int t = q0 + u;
+      if (t < cnt) {
         bool take = kv[u] > thr;
         if (kv[u] == thr) take = eqi++ < need_eq;
         if (take) {
-          so[pos] = c;
-          for (int r = 0; r < G; ++r) slog[hrow(r) * K + pos] = scores[hrow(r) * nmax + c];
+          if (PH == SEL_PART) {
+            co[pos] = make_uint2(kv[u], (uint32_t)(c0 + t));
+          } else {
+            const int c = (PH == SEL_MERGE) ? cid[t] : t;
+            so[pos] = c;
+            for (int r = 0; r < G; ++r) slog[hrow(r) * K + pos] = scores[hrow(r) * nmax + c];
+          }
           ++pos;
         }
       }
@@ -725,8 +763,8 @@ void launch_score(const HilsShape& s, const void* qr, const int32_t* seqlen, con
 template <typename T, bool PAGED>
 void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const void* k, const void* v,
                      const int32_t* seqlen, const void* ksum, const float* bsum, void* out,
-                     int32_t* sel, float* scores, uint32_t* keys, float* slog, float* part,
-                     float* lsep, PageMap pm, hipStream_t st) {
+                     int32_t* sel, float* scores, uint32_t* keys, uint2* cand, float* slog,
+                     float* part, float* lsep, PageMap pm, hipStream_t st) {
   const int NS = s.K + s.nwin;
   const float tau = (float)s.tau;
   const unsigned nsb = (unsigned)((s.nmax + SC_CPB - 1) / SC_CPB);
@@ -739,11 +777,30 @@ void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const vo
     else if (s.M == 2) launch_score<T, PAGED, 2>(s, qr, seqlen, ksum, bsum, scores, lsep, nsb, pm, st);
     else launch_score<T, PAGED, 4>(s, qr, seqlen, ksum, bsum, scores, lsep, nsb, pm, st);
   }
-  const size_t sshm = (size_t)4 * (size_t)min(s.nmax > 0 ? s.nmax : 1, SEL_LDS_KEYS);
-  hipFuncSetAttribute((const void*)k_dec_select, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sshm);
-  { HilsProfScope ps_("k_dec_select", st); hipLaunchKernelGGL(k_dec_select, dim3(s.B * s.Hkv * s.M), dim3(SEL_NT), sshm, st, scores, lsep, seqlen,
-                     keys, sel, slog, s.Hq, s.Hkv, s.G, s.nmax > 0 ? s.nmax : 1, (int)nsb, s.N, s.S,
-                     s.W, s.K, s.M); }
+  int P = 1, span = 1;
+  hils_dec_select_split(s, P, span);
+  const int nm = s.nmax > 0 ? s.nmax : 1;
+  const unsigned rows = (unsigned)(s.B * s.Hkv * s.M);
+  if (P == 1) {
+    const size_t sshm = (size_t)4 * (size_t)min(nm, SEL_LDS_KEYS);
+    hipFuncSetAttribute((const void*)k_dec_select<SEL_WHOLE>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sshm);
+    HilsProfScope ps_("k_dec_select", st);
+    hipLaunchKernelGGL(k_dec_select<SEL_WHOLE>, dim3(rows), dim3(SEL_NT), sshm, st, scores, lsep,
+                       seqlen, keys, cand, sel, slog, s.Hq, s.Hkv, s.G, nm, (int)nsb, s.N, s.S, s.W,
+                       s.K, s.M, nm, 1);
+  } else {
+    const size_t pshm = (size_t)4 * (size_t)min(span, SEL_LDS_KEYS);
+    const size_t mshm = (size_t)8 * (size_t)P * s.K;          // keys and chunk ids
+    hipFuncSetAttribute((const void*)k_dec_select<SEL_PART>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pshm);
+    hipFuncSetAttribute((const void*)k_dec_select<SEL_MERGE>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)mshm);
+    HilsProfScope ps_("k_dec_select", st);
+    hipLaunchKernelGGL(k_dec_select<SEL_PART>, dim3(rows, P), dim3(SEL_NT), pshm, st, scores, lsep,
+                       seqlen, keys, cand, sel, slog, s.Hq, s.Hkv, s.G, nm, (int)nsb, s.N, s.S, s.W,
+                       s.K, s.M, span, P);
+    hipLaunchKernelGGL(k_dec_select<SEL_MERGE>, dim3(rows), dim3(SEL_NT), mshm, st, scores, lsep,
+                       seqlen, keys, cand, sel, slog, s.Hq, s.Hkv, s.G, nm, (int)nsb, s.N, s.S, s.W,
+                       s.K, s.M, span, P);
+  }
   const dim3 agrid(s.B * s.Hkv * s.M, NS);
   if (std::is_same<T, bf16_t>::value && s.d == DA_D && s.S == DA_S && (s.G == 1 || s.G == 2 || s.G == 4)) {
     const bf16_t* qb = (const bf16_t*)q;
@@ -775,17 +832,17 @@ void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const vo
 hipError_t hils_launch_decode(const HilsShape& s, const void* q, const void* qr, const void* k,
                               const void* v, const int32_t* seqlen, const void* ksum,
                               const float* bsum, void* out, int32_t* sel, float* scores,
-                              uint32_t* keys, float* slog, float* part, float* lsep,
-                              const int32_t* page_table, int max_pages, int num_pages,
+                              uint32_t* keys, uint2* cand, float* slog, float* part,
+                              float* lsep, const int32_t* page_table, int max_pages, int num_pages,
                               hipStream_t st) {
   const PageMap pm{page_table, max_pages, num_pages};
   const bool paged = page_table != nullptr;
   if (s.dtype == 0) {
-    if (paged) launch_decode_t<bf16_t, true>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, slog, part, lsep, pm, st);
-    else launch_decode_t<bf16_t, false>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, slog, part, lsep, pm, st);
+    if (paged) launch_decode_t<bf16_t, true>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, cand, slog, part, lsep, pm, st);
+    else launch_decode_t<bf16_t, false>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, cand, slog, part, lsep, pm, st);
   } else {
-    if (paged) launch_decode_t<float, true>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, slog, part, lsep, pm, st);
-    else launch_decode_t<float, false>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, slog, part, lsep, pm, st);
+    if (paged) launch_decode_t<float, true>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, cand, slog, part, lsep, pm, st);
+    else launch_decode_t<float, false>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, cand, slog, part, lsep, pm, st);
   }
   return hipGetLastError();
 }

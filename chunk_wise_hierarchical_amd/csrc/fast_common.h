@@ -104,6 +104,22 @@ __device__ __forceinline__ float wsum64(float v) {
   return sum_x32(sum_x16(v));
 }
 
+// Workgroups are handed to the 8 XCDs (each with its own L2) round-robin by
+// workgroup id.  xcd_work maps workgroup blk of a grid of at least
+// NXCD * ceil(nwork / NXCD) workgroups to a work index such that XCD x takes
+// the contiguous range [x * per, (x + 1) * per), per = ceil(nwork / NXCD), in
+// order: neighbouring work items, which share data through L2, run on one
+// XCD.  Workgroups without a work item get -1.
+constexpr int NXCD = 8;
+__device__ __forceinline__ long long xcd_work(long long blk, long long nwork) {
+  const long long per = (nwork + NXCD - 1) / NXCD;
+  const long long j = blk / NXCD;
+  if (j >= per) return -1;
+  const long long L = (blk % NXCD) * per + j;
+  return L < nwork ? L : -1;
+}
+inline long long xcd_grid(long long nwork) { return NXCD * ((nwork + NXCD - 1) / NXCD); }
+
 // value of lane 63 - l (= l ^ 63)
 __device__ __forceinline__ uint32_t lane_reverse(uint32_t v) {
   const uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);   // l ^ 15

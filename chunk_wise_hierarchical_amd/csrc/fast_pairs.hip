@@ -241,15 +241,18 @@ template <int G>
 __global__ void __launch_bounds__(NT, 2)
 k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
            const bf16_t* __restrict__ vt, float* __restrict__ swa, float* __restrict__ lz,
-           int Hq, int Hkv, int N, int W, int nCc, float tau2, int i0, int qs, int nqb) {
+           int Hq, int Hkv, int N, int W, int nCc, float tau2, int i0, int qs, int nqb, int nbg) {
   constexpr int QA = 128 / G;
   extern __shared__ __align__(16) unsigned char sm[];
   bf16_t* ktile = reinterpret_cast<bf16_t*>(sm);
   bf16_t* vtile = reinterpret_cast<bf16_t*>(sm + KT_BYTES);
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int blk = blockIdx.x;
-  const int qb = nqb - 1 - (blk % nqb);
+  // consecutive query blocks, whose windows overlap, run on one XCD
+  const long long wk = xcd_work(blockIdx.x, (long long)nbg * nqb);
+  if (wk < 0) return;
+  const int blk = (int)wk;
+  const int qb = blk % nqb;
   const int bg = blk / nqb;
   const int g = bg % Hkv;
   const long long b = bg / Hkv;
@@ -781,9 +784,9 @@ hipError_t launch_pairs(const HilsShape& s, const void* q, const void* qr, const
                            sel, pb.cur, pb.list, s.N, s.K, s.nC, i0, qs); }
     }
     { HilsProfScope ps_("k_win_fast", st);
-      hipLaunchKernelGGL(k_win_fast<G>, dim3((unsigned)(s.B * s.Hkv * nqb)), dim3(NT), wshm, st, qb,
-                         (const bf16_t*)k, (const bf16_t*)vt, pb.swa, pb.lz, s.Hq, s.Hkv, s.N, s.W,
-                         s.nCc, tau2, i0, qs, nqb); }
+      hipLaunchKernelGGL(k_win_fast<G>, dim3((unsigned)xcd_grid((long long)s.B * s.Hkv * nqb)),
+                         dim3(NT), wshm, st, qb, (const bf16_t*)k, (const bf16_t*)vt, pb.swa, pb.lz,
+                         s.Hq, s.Hkv, s.N, s.W, s.nCc, tau2, i0, qs, nqb, s.B * s.Hkv); }
     if (F > 0) {
       const long long tmax = hils_pair_tiles_max(s, qs);
       const unsigned grid = (unsigned)((tmax + PTPW - 1) / PTPW);

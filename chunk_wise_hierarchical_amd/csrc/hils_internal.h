@@ -73,9 +73,35 @@ constexpr int HILS_FAST_NCMAX = 16384;   // chunk ids the fast attention bitmap 
 hipError_t hils_launch_decode(const HilsShape& s, const void* q, const void* qr, const void* k,
                               const void* v, const int32_t* seqlen, const void* ksum,
                               const float* bsum, void* out, int32_t* sel, float* scores,
-                              uint32_t* keys, float* slog, float* part, float* lsep,
+                              uint32_t* keys, uint2* cand, float* slog, float* part, float* lsep,
                               const int32_t* page_table, int max_pages, int num_pages,
                               hipStream_t st);
+// Decode selection: one workgroup per (sequence, KV group, query) takes the
+// whole candidate list when there are enough such rows to fill the chip and
+// the list's keys fit in LDS.  Otherwise P partitions of `span` chunks each
+// find their own top-K, then one merge of the P * K candidates; the merge
+// keeps its P * K keys and ids in LDS, so P * K stays within
+// HILS_DEC_MERGE_MAX.
+constexpr int HILS_DEC_SEL_SPAN = 4096;
+constexpr int HILS_DEC_MERGE_MAX = 8192;
+constexpr int HILS_DEC_SEL_ROWS_WHOLE = 128;
+constexpr int HILS_DEC_SEL_LDS_KEYS = 24576;
+inline void hils_dec_select_split(const HilsShape& s, int& P, int& span) {
+  const long long nm = s.nmax > 0 ? s.nmax : 1;
+  const long long rows = (long long)s.B * s.Hkv * s.M;
+  if (rows >= HILS_DEC_SEL_ROWS_WHOLE && nm <= HILS_DEC_SEL_LDS_KEYS) {
+    P = 1;
+    span = (int)nm;
+    return;
+  }
+  span = HILS_DEC_SEL_SPAN;
+  P = (int)((nm + span - 1) / span);
+  if (P > 1 && (long long)P * s.K > HILS_DEC_MERGE_MAX) {
+    const long long pmax = HILS_DEC_MERGE_MAX / s.K;             // >= 64 (K <= 128)
+    span = (int)(((nm + pmax - 1) / pmax + 1023) / 1024 * 1024);
+    P = (int)((nm + span - 1) / span);
+  }
+}
 hipError_t hils_launch_summarize_paged(const HilsShape& s, const void* k_pages, const void* lm_pages,
                                        const int32_t* pages, int npages_listed, int num_pages,
                                        void* ksum_pages, float* bsum_pages, hipStream_t st);

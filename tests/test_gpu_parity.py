@@ -447,3 +447,12 @@ def test_decode_candidates_beyond_lds():
     # more candidate chunks than the selection kernel keeps in LDS (24576)
     w = synth.get_workload("decode_512k", N=409600, B=1, Hq=2, Hkv=1, d=64, S=16, W=256, K=8)
     _decode_case(w, [409600], label="n > 24576")
+
+
+def test_decode_partitioned_selection():
+    # 299999 candidate chunks, K = 128: the selection runs as partitions of
+    # 5120 chunks (the 128-key lists of at most 64 partitions fit one merge),
+    # then one merge; a shorter sequence takes fewer partitions
+    w = synth.get_workload("decode_512k", N=300000, B=2, Hq=2, Hkv=1, d=32, S=1, W=1, K=128,
+                           regime="iid")
+    _decode_case(w, [300000, 7000], label="partitioned selection")
