@@ -87,8 +87,7 @@ KERNEL_SOURCES = {
     "k_attn_fast": ["fast_attn.hip", "fast_common.h", "hils_device.h"],
     "k_score_fast": ["fast_score.hip", "fast_common.h", "hils_device.h"],
     "k_pair_attn": ["fast_pairs.hip", "fast_common.h", "hils_device.h", "hils_internal.h"],
-    "k_pair_reduce": ["fast_pairs.hip", "fast_common.h", "hils_device.h", "hils_internal.h"],
-    "k_win_fast": ["fast_pairs.hip", "fast_common.h", "hils_device.h", "hils_internal.h"],
+    "k_win_fuse": ["fast_pairs.hip", "fast_common.h", "hils_device.h", "hils_internal.h"],
     "k_dec_score": ["decode.hip", "fast_common.h", "hils_device.h", "hils_internal.h"],
 }
 
@@ -167,14 +166,15 @@ def _kernel_table(records, steps):
 
 
 def pair_path_bytes(sel, w, launches):
-    """Algorithmic HBM bytes per prefill of the chunk-bucket path's pair
-    attention and reduction, from the selection sel [B,Hkv,N,K] (-1 padded).
-    Pair attention, per (query, KV group, selected chunk) pair: the G gathered
-    query rows and the G bf16 per-chunk output rows (G*d*2 B each), G fp32
-    fusion logits and the 4-byte list entry; per (slice, KV group, chunk)
-    bucket: the chunk's K and V^T (S*d*2 B each), k' (G*d*2 B) and b' (G*4 B).
-    Reduction, per pair: the G output rows and logits read back; per (query,
-    head): the fp32 window output and log-mass read, the bf16 output written."""
+    """Design-traffic bytes per prefill of the chunk-bucket path's pair
+    attention and fused window + fusion kernel, from the selection sel
+    [B,Hkv,N,K] (-1 padded).  Pair attention, per (query, KV group, selected
+    chunk) pair: the G gathered query rows and the G bf16 per-chunk output rows
+    (G*d*2 B each), G fp32 fusion logits and the 4-byte list entry; per
+    (slice, KV group, chunk) bucket: the chunk's K and V^T (S*d*2 B each), k'
+    (G*d*2 B) and b' (G*4 B).  Window + fusion, per pair: the G output rows and
+    logits read back; per (query, head): its query row read and the bf16
+    output written (the window's K/V tiles are shared through L2)."""
     import torch
     B, Hkv, N, K = sel.shape
     G, d, S = w.G, w.d, w.S
@@ -188,7 +188,7 @@ def pair_path_bytes(sel, w, launches):
         pairs += int(v.sum())
         buckets += int(torch.unique((bgi * nC + s.long())[v]).numel())
     attn = pairs * (2 * G * d * 2 + G * 4 + 4) + buckets * (2 * S * d * 2 + G * d * 2 + G * 4)
-    red = pairs * G * (d * 2 + 4) + B * Hkv * N * G * (d * 4 + 4 + d * 2)
+    red = pairs * G * (d * 2 + 4) + B * Hkv * N * G * (d * 2 + d * 2)
     return float(attn), float(red)
 
 
@@ -442,7 +442,7 @@ def prefill_bench(torch, hils, _lib, w, steps, warmup, union, log, want_sel=Fals
     # algorithmic FLOPs per step of the contraction kernels; per launch is that
     # over the launches per step (the bucket-path kernels run once per slice)
     step_flops = {"k_attn_fast": attn_f, "k_attn_generic": attn_f, "k_score_fast": score_f,
-                  "k_select_generic": score_f, "k_summarize": summ_f, "k_win_fast": win_f,
+                  "k_select_generic": score_f, "k_summarize": summ_f, "k_win_fuse": win_f,
                   "k_pair_attn": sel_f}
 
     def roofline(kname):
@@ -460,7 +460,7 @@ def prefill_bench(torch, hils, _lib, w, steps, warmup, union, log, want_sel=Fals
     hbm_rooflines = {}
     if "k_pair_attn" in kern:
         attn_b, red_b = pair_path_bytes(sel, w, kern["k_pair_attn"]["calls"] / steps)
-        for kname, step_bytes in (("k_pair_attn", attn_b), ("k_pair_reduce", red_b)):
+        for kname, step_bytes in (("k_pair_attn", attn_b), ("k_win_fuse", red_b)):
             if kname not in kern:
                 continue
             launches = kern[kname]["calls"] / steps

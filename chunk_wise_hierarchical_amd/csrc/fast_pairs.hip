@@ -16,15 +16,16 @@
 //   1. k_pair_count / k_pair_bsum / k_pair_scan / k_pair_tiles / k_pair_scatter: counting
 //      sort of the slice's (query, slot) pairs by (KV group, chunk), cut into
 //      tiles of 64/G pairs (64 MFMA rows with the G heads of a group);
-//   2. k_win_fast: window attention (online softmax over the window tiles);
-//      writes o_swa (normalised, fp32) and log Z_swa;
-//   3. k_pair_attn: per tile, gather the 64 query rows, form the fusion logit
+//   2. k_pair_attn: per tile, gather the 64 query rows, form the fusion logit
 //      s_hat = scale q_hat.k'_c + b'_c of each row, S^T = K Q^T and
 //      O^T = V^T P^T on MFMA; writes o_c (normalised, bf16) and s_hat per pair;
-//   4. k_pair_reduce: alpha = softmax over {s_hat_c} U {log Z_swa} and
+//   3. k_win_fuse: window attention (online softmax over the window tiles),
+//      then alpha = softmax over {s_hat_c} U {log Z_swa} and
 //      out = alpha_swa o_swa + sum_c alpha_c o_c, in slot order (deterministic;
 //      the order of pairs inside a bucket never changes a result, since MFMA
-//      rows are independent).
+//      rows are independent).  The window's compute overlaps the per-chunk
+//      outputs' reads across the workgroups of a CU.
+#include <algorithm>
 #include <type_traits>
 
 #include "fast_common.h"
@@ -52,8 +53,6 @@ constexpr int NT = 256;
 constexpr int KSTR = D;       // K tile row stride (elements); 16-byte parts XOR-swizzled per row
 constexpr int VSTR = S + 8;   // V^T tile row stride (elements)
 constexpr int PQ = 512;       // queries per list-building workgroup
-constexpr int RQ = 16;        // queries per reduce workgroup
-constexpr int RU = 8;         // partial rows in flight per reduce thread
 constexpr int PTPW = HILS_PAIR_TPW;   // tiles per pair-attention workgroup
 constexpr int SB = HILS_PAIR_SB;      // buckets per scan workgroup
 constexpr int KSS = D + 8;    // k'_c row stride in LDS (elements)
@@ -239,9 +238,10 @@ k_pair_scatter(const int32_t* __restrict__ sel, uint32_t* __restrict__ cur,
 // fragment a wavefront reads from LDS feeds two MFMAs.
 template <int G>
 __global__ void __launch_bounds__(NT, 2)
-k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-           const bf16_t* __restrict__ vt, float* __restrict__ swa, float* __restrict__ lz,
-           int Hq, int Hkv, int N, int W, int nCc, float tau2, int i0, int qs, int nqb, int nbg) {
+k_win_fuse(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+           const bf16_t* __restrict__ vt, const float* __restrict__ lamb,
+           const bf16_t* __restrict__ part, bf16_t* __restrict__ out, int Hq, int Hkv, int N,
+           int W, int K, int nCc, float tau2, int i0, int qs, int nqb, int nbg) {
   constexpr int QA = 128 / G;
   extern __shared__ __align__(16) unsigned char sm[];
   bf16_t* ktile = reinterpret_cast<bf16_t*>(sm);
@@ -393,6 +393,114 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       }
   };
 
+  // Chunk-level fusion (section 3, hierarchical softmax): each row (query,
+  // head) mixes its window output with the per-chunk outputs o_c the pair
+  // kernel stored for its selected chunks: alpha = softmax over {s_hat_c} U
+  // {log Z_swa} (base 2 throughout), out = alpha_swa o_swa + sum_c alpha_c o_c.
+  // The chunk part is accumulated first against the row's largest chunk
+  // logit m_c: P = sum_c 2^(s_hat_c - m_c) o_c (slot order) and
+  // E = sum_c 2^(s_hat_c - m_c); with M = max(m_c, log Z_swa) the output is
+  //   (2^(m_c - M) P + 2^(log Z_swa - M) o_swa) / (2^(m_c - M) E + 2^(log Z_swa - M)).
+  // So the chunk part does not wait for the window: workgroups of odd work
+  // index take row block 0's chunk part before their window tiles, even ones
+  // after, which keeps the per-chunk output reads of some workgroups of a CU
+  // running while others compute their window.  A row's four lanes (lq)
+  // share its weights through this wavefront's part of the LDS, free outside
+  // the tile loop.
+  float* al = reinterpret_cast<float*>(sm) + (size_t)w * 32 * (K + 1);
+  // chunk part of row block rb into pa (with its m_c and E)
+  auto chunk_part = [&](int rb, float (&pa)[8][4], float& pmx, float& pse) __attribute__((always_inline)) {
+    const int kk = vcol[rb] ? min(K, n_cand(iq[rb], W, S)) : 0;
+    const long long qrow = (long long)bg * qs + (iq[rb] - i0);
+    float* ar = al + (16 * rb + (lane & 15)) * (K + 1);
+    const float* lrow = lamb + qrow * K * G + h;    // slot kx at lrow[kx * G]
+    float mx = -INFINITY;
+    for (int kx = lq; kx < kk; kx += 4) {
+      const float x = lrow[(long long)kx * G];
+      ar[kx] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = max_x32(max_x16(mx));
+    float se = 0.0f;
+    for (int kx = lq; kx < kk; kx += 4) {
+      const float e = fast_exp2(ar[kx] - mx);
+      ar[kx] = e;
+      se += e;
+    }
+    pse = sum_x32(sum_x16(se));
+    pmx = mx;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // the row's weights, from its four lanes
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pa[dt][e] = 0.0f;
+    // piece 4j + lq of a stored row (16 bytes at element 8 (4j + lq)) holds
+    // the elements 32j + 4lq + {0..3} (acc block 2j) and 32j + 16 + 4lq +
+    // {0..3} (block 2j + 1) of this lane
+    const bf16_t* pp = part + (qrow * K * G + h) * D + 8 * lq;
+    constexpr int RU = 8;                 // slots whose pieces are in flight together
+    for (int kx = 0; kx < kk; kx += RU) {
+      uint4 u[RU][4];
+#pragma unroll
+      for (int t = 0; t < RU; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)   // a slot past kk reads slot kk - 1 again, unused
+          u[t][jj] = ld_u4(pp + (long long)min(kx + t, kk - 1) * G * D + 32 * jj);
+#pragma unroll
+      for (int t = 0; t < RU; ++t) {
+        if (kx + t < kk) {
+          const float wt = ar[kx + t];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const uint32_t uv[4] = {u[t][jj].x, u[t][jj].y, u[t][jj].z, u[t][jj].w};
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+              pa[2 * jj][2 * t2] = fmaf(wt, __uint_as_float(uv[t2] << 16), pa[2 * jj][2 * t2]);
+              pa[2 * jj][2 * t2 + 1] =
+                  fmaf(wt, __uint_as_float(uv[t2] & 0xffff0000u), pa[2 * jj][2 * t2 + 1]);
+              pa[2 * jj + 1][2 * t2] = fmaf(wt, __uint_as_float(uv[2 + t2] << 16), pa[2 * jj + 1][2 * t2]);
+              pa[2 * jj + 1][2 * t2 + 1] =
+                  fmaf(wt, __uint_as_float(uv[2 + t2] & 0xffff0000u), pa[2 * jj + 1][2 * t2 + 1]);
+            }
+          }
+        }
+      }
+    }
+  };
+  // the output rows of block rb: window state (m, l, acc) with the chunk part
+  auto finish = [&](int rb, const float (&pa)[8][4], float pmx, float pse) __attribute__((always_inline)) {
+    const float lr = sum_x32(sum_x16(l[rb]));      // the row's four lanes
+    if (!vcol[rb]) return;
+    // every valid row has its own position in the window: lr >= 1
+    const float lzr = m[rb] * tau2 + log2f(lr);
+    const float M2 = fmaxf(pmx, lzr);
+    const float sc = fast_exp2(pmx - M2);          // 0 without selected chunks (pmx = -inf)
+    const float es = fast_exp2(lzr - M2);
+    const float iz = 1.0f / (sc * pse + es);
+    const float cw = sc * iz, ww = es * iz / lr;
+    bf16_t* op = out + ((hb + h) * N + iq[rb]) * (long long)D + 4 * lq;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = fmaf(cw, pa[dt][e], ww * acc[rb][dt][e]);
+      *reinterpret_cast<uint2*>(op + 16 * dt) =
+          make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+    }
+  };
+  // row block 0's chunk part of a part-first workgroup waits in LDS (past the
+  // tiles), lane-interleaved 16-byte pieces: the tile loop needs the registers
+  const bool part_first = (wk & 1) != 0;
+  float4* p0s = reinterpret_cast<float4*>(sm + KT_BYTES + VT_BYTES) + (size_t)w * 8 * 64 + lane;
+  float m0 = -INFINITY, e0 = 0.0f;
+  if (part_first) {
+    float pa[8][4];
+    chunk_part(0, pa, m0, e0);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) p0s[dt * 64] = make_float4(pa[dt][0], pa[dt][1], pa[dt][2], pa[dt][3]);
+    __syncthreads();             // the LDS weights are read; the tile loop takes that LDS
+  }
+
   const int cw_lo = (int)(window_start(ib0, W, S) / S);
   const int cw_hi = (ib0 + qcount - 1) / S;
   const int nw = cw_hi - cw_lo + 1;
@@ -413,23 +521,23 @@ k_win_fast(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     store_chunk(ra);             // past the last tile: rewrites the last tile, unused
     __syncthreads();
   }
-
-  // normalised window output and its log-mass (base 2)
+  if (part_first) {
+    float pa[8][4];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const float lr = sum_x32(sum_x16(l[rb]));      // the row's four lanes
-    if (vcol[rb]) {
-      const long long row = (long long)bg * qs + (iq[rb] - i0);
-      const float il = 1.0f / lr;
-      float* sp = swa + (row * G + h) * D;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const float4 o = make_float4(acc[rb][dt][0] * il, acc[rb][dt][1] * il, acc[rb][dt][2] * il,
-                                     acc[rb][dt][3] * il);
-        *reinterpret_cast<float4*>(sp + 16 * dt + 4 * lq) = o;
-      }
-      if (lq == 0) lz[row * G + h] = m[rb] * tau2 + log2f(lr);
+    for (int dt = 0; dt < 8; ++dt) {
+      const float4 v = p0s[dt * 64];
+      pa[dt][0] = v.x; pa[dt][1] = v.y; pa[dt][2] = v.z; pa[dt][3] = v.w;
     }
+    finish(0, pa, m0, e0);
+  } else {
+    float pa[8][4], pm, pe;
+    chunk_part(0, pa, pm, pe);
+    finish(0, pa, pm, pe);
+  }
+  {
+    float pa[8][4], pm, pe;
+    chunk_part(1, pa, pm, pe);
+    finish(1, pa, pm, pe);
   }
 }
 
@@ -654,96 +762,6 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
   }
 }
 
-// ---------------------------------------------------------------------------
-// out = alpha_swa o_swa + sum_k alpha_k o_k, slot order
-
-template <int G>
-__global__ void __launch_bounds__(NT)
-k_pair_reduce(const float* __restrict__ swa, const float* __restrict__ lz,
-              const float* __restrict__ lamb, const bf16_t* __restrict__ part,
-              bf16_t* __restrict__ out, int Hq, int Hkv, int N, int W, int K, int i0, int qs) {
-  constexpr int EV = D / 8;                     // 16-byte vectors of a head row
-  constexpr int TPQ = G * EV;                   // threads of one query
-  constexpr int QPP = NT / TPQ;                 // queries per pass
-  extern __shared__ float wk[];                 // [RQ*G][K+1]: alpha_c per slot, alpha_swa last
-  const int bg = blockIdx.x;
-  const int b = bg / Hkv, g = bg - b * Hkv;
-  const int tid = threadIdx.x;
-  const int q0 = blockIdx.y * RQ;
-  // fusion logits of the workgroup's queries into LDS: they are contiguous in
-  // memory ([query][slot][head]), so consecutive threads read consecutive words
-  const float* lb = lamb + ((long long)bg * qs + q0) * K * G;
-  for (int it = tid; it < RQ * K * G; it += NT) {
-    const int h = it % G, r = it / G, kx = r % K, qq = r / K;
-    const int qi = q0 + qq;
-    if (qi < qs && kx < min(K, n_cand((long long)i0 + qi, W, S)))
-      wk[(qq * G + h) * (K + 1) + kx] = lb[it];
-  }
-  for (int it = tid; it < RQ * G; it += NT) {
-    const int qq = it / G, h = it - qq * G;
-    const int qi = q0 + qq;
-    if (qi < qs) wk[it * (K + 1) + K] = lz[((long long)bg * qs + qi) * G + h];
-  }
-  __syncthreads();
-  // alpha = softmax over {s_hat_c} U {log Z_swa}: one wavefront per (query,
-  // head) row at a time, lane = slot (K <= 64 on this path)
-  {
-    const int lane = tid & 63, wv = tid >> 6;
-    for (int it = wv; it < RQ * G; it += NT / 64) {
-      const int qi = q0 + it / G;
-      if (qi >= qs) break;
-      const int kk = min(K, n_cand((long long)i0 + qi, W, S));
-      float* wr = wk + it * (K + 1);
-      const float lzv = wr[K];
-      const float x = (lane < kk) ? wr[lane] : -INFINITY;
-      const float M2 = fmaxf(wmax64(x), lzv);
-      const float e = (lane < kk) ? fast_exp2(x - M2) : 0.0f;
-      const float es = fast_exp2(lzv - M2);
-      const float invZ = 1.0f / (wsum64(e) + es);
-      if (lane < kk) wr[lane] = e * invZ;
-      if (lane == 0) wr[K] = es * invZ;
-    }
-  }
-  __syncthreads();
-  const int sub = tid / TPQ, e2 = tid - sub * TPQ;
-  const int h = e2 / EV, pv = e2 - h * EV;            // 16-byte piece of the stored order
-  const int d0 = 32 * (pv >> 2) + 4 * (pv & 3);       // its elements: d0 + {0..3}, d0 + 16 + {0..3}
-  for (int qq = sub; qq < RQ; qq += QPP) {
-    const int qi = q0 + qq;
-    if (qi >= qs) break;
-    const long long i = (long long)i0 + qi;
-    const int kk = min(K, n_cand(i, W, S));
-    const long long row = (long long)bg * qs + qi;
-    const float* wr = wk + (qq * G + h) * (K + 1);
-    const float* sp = swa + (row * G + h) * D;
-    const float4 s0 = *reinterpret_cast<const float4*>(sp + d0);
-    const float4 s1 = *reinterpret_cast<const float4*>(sp + d0 + 16);
-    const float ws = wr[K];
-    float a[8] = {ws * s0.x, ws * s0.y, ws * s0.z, ws * s0.w, ws * s1.x, ws * s1.y, ws * s1.z, ws * s1.w};
-    const bf16_t* pp = part + (row * K * G + h) * D + 8 * pv;
-    auto add = [&](float wt, uint4 u) {
-      const uint32_t uv[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        a[2 * t] = fmaf(wt, __uint_as_float(uv[t] << 16), a[2 * t]);
-        a[2 * t + 1] = fmaf(wt, __uint_as_float(uv[t] & 0xffff0000u), a[2 * t + 1]);
-      }
-    };
-    int kx = 0;
-    for (; kx + RU <= kk; kx += RU) {      // RU slot loads in flight
-      uint4 uv[RU];
-#pragma unroll
-      for (int t = 0; t < RU; ++t) uv[t] = ld_u4_nt(pp + (long long)(kx + t) * G * D);
-#pragma unroll
-      for (int t = 0; t < RU; ++t) add(wr[kx + t], uv[t]);
-    }
-    for (; kx < kk; ++kx) add(wr[kx], ld_u4_nt(pp + (long long)kx * G * D));
-    bf16_t* op = out + (((long long)b * Hq + (long long)g * G + h) * N + i) * D;
-    *reinterpret_cast<uint2*>(op + d0) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
-    *reinterpret_cast<uint2*>(op + d0 + 16) = make_uint2(pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7]));
-  }
-}
-
 template <int G>
 hipError_t launch_pairs(const HilsShape& s, const void* q, const void* qr, const void* k,
                         const void* vt, const void* ksum, const float* bsum, const int32_t* sel,
@@ -753,15 +771,16 @@ hipError_t launch_pairs(const HilsShape& s, const void* q, const void* qr, const
   const int F = s.B * s.Hkv * s.nC;
   const float tau2 = (float)(s.tau * 1.4426950408889634);
   const size_t hshm = (size_t)(s.nC > 0 ? s.nC : 1) * 4;
-  const size_t wshm = KT_BYTES + VT_BYTES;
+  // window tiles during the tile loop (per wavefront 32 rows of fusion weights
+  // outside it), then the part-first workgroups' row block 0 chunk parts
+  const size_t wshm = std::max(KT_BYTES + VT_BYTES, (size_t)4 * 32 * (s.K + 1) * 4) +
+                      (size_t)4 * 8 * 64 * 16;
   const size_t ashm = KT_BYTES + VT_BYTES + (size_t)(G + 1) * KSS * 2;
-  const size_t rshm = (size_t)RQ * G * (s.K + 1) * 4;
   hipFuncSetAttribute((const void*)k_pair_count, hipFuncAttributeMaxDynamicSharedMemorySize, (int)hshm);
   hipFuncSetAttribute((const void*)k_pair_scatter, hipFuncAttributeMaxDynamicSharedMemorySize, (int)hshm);
-  hipFuncSetAttribute((const void*)k_win_fast<G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)wshm);
+  hipFuncSetAttribute((const void*)k_win_fuse<G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)wshm);
   hipFuncSetAttribute((const void*)k_pair_attn<G, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
   hipFuncSetAttribute((const void*)k_pair_attn<G, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
-  hipFuncSetAttribute((const void*)k_pair_reduce<G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rshm);
   const bf16_t* qb = (const bf16_t*)q;
   const bf16_t* qrb = (qr == q) ? nullptr : (const bf16_t*)qr;
   const int nsb = (F + SB - 1) / SB;        // scan workgroups
@@ -783,10 +802,6 @@ hipError_t launch_pairs(const HilsShape& s, const void* q, const void* qr, const
         hipLaunchKernelGGL(k_pair_scatter, dim3(s.B * s.Hkv, (qs + PQ - 1) / PQ), dim3(NT), hshm, st,
                            sel, pb.cur, pb.list, s.N, s.K, s.nC, i0, qs); }
     }
-    { HilsProfScope ps_("k_win_fast", st);
-      hipLaunchKernelGGL(k_win_fast<G>, dim3((unsigned)xcd_grid((long long)s.B * s.Hkv * nqb)),
-                         dim3(NT), wshm, st, qb, (const bf16_t*)k, (const bf16_t*)vt, pb.swa, pb.lz,
-                         s.Hq, s.Hkv, s.N, s.W, s.nCc, tau2, i0, qs, nqb, s.B * s.Hkv); }
     if (F > 0) {
       const long long tmax = hils_pair_tiles_max(s, qs);
       const unsigned grid = (unsigned)((tmax + PTPW - 1) / PTPW);
@@ -797,10 +812,12 @@ hipError_t launch_pairs(const HilsShape& s, const void* q, const void* qr, const
                            pb.tinfo, pb.tot, pb.lam, (bf16_t*)pb.part, s.Hq, s.Hkv, s.N, s.K, s.nC,
                            s.nCc, tau2, i0, qs); }
     }
-    { HilsProfScope ps_("k_pair_reduce", st);
-      hipLaunchKernelGGL(k_pair_reduce<G>, dim3(s.B * s.Hkv, (qs + RQ - 1) / RQ), dim3(NT), rshm, st,
-                         pb.swa, pb.lz, pb.lam, (const bf16_t*)pb.part, (bf16_t*)out, s.Hq, s.Hkv,
-                         s.N, s.W, s.K, i0, qs); }
+    // window attention, then the fusion with the slice's per-chunk outputs
+    { HilsProfScope ps_("k_win_fuse", st);
+      hipLaunchKernelGGL(k_win_fuse<G>, dim3((unsigned)xcd_grid((long long)s.B * s.Hkv * nqb)),
+                         dim3(NT), wshm, st, qb, (const bf16_t*)k, (const bf16_t*)vt, pb.lam,
+                         (const bf16_t*)pb.part, (bf16_t*)out, s.Hq, s.Hkv, s.N, s.W, s.K, s.nCc,
+                         tau2, i0, qs, nqb, s.B * s.Hkv); }
   }
   return hipGetLastError();
 }

@@ -69,7 +69,7 @@ inline bool pair_path(const HilsShape& s, uint32_t flags, bool fast) {
 struct PrefillLayout {
   size_t ks, bs, sel, slog, vt, kf, total;
   // per-chunk bucket path
-  size_t cnt, loff, toff, cur, tot, bsum, tinfo, list, lam, swa, lz, part;
+  size_t cnt, loff, toff, cur, tot, bsum, tinfo, list, lam, part;
   int qs_max;
 };
 // generic path: summaries, selection, fusion logits; fast path: summaries,
@@ -99,8 +99,6 @@ PrefillLayout prefill_layout(const HilsShape& s, bool fast, bool pairs) {
       L.tinfo = off; off += align_up((size_t)hils_pair_tiles_max(s, qs) * 8);
       L.list = off;  off += align_up(P * 4);
       L.lam = off;   off += align_up(P * s.G * 4);
-      L.swa = off;   off += align_up((size_t)s.B * s.Hkv * qs * s.G * s.d * 4);
-      L.lz = off;    off += align_up((size_t)s.B * s.Hkv * qs * s.G * 4);
       L.part = off;  off += align_up(P * s.G * s.d * 2);
     }
   } else {
@@ -350,8 +348,6 @@ hils_status hils_prefill(const hils_cfg* cfg, const void* q, const void* q_route
     pb.tinfo = (uint2*)(w + L.tinfo);
     pb.list = (uint32_t*)(w + L.list);
     pb.lam = (float*)(w + L.lam);
-    pb.swa = (float*)(w + L.swa);
-    pb.lz = (float*)(w + L.lz);
     pb.part = (uint16_t*)(w + L.part);
     pb.qs_max = L.qs_max;
     return hip_status(hils_launch_attn_pairs(s, q, qr, k, vt, ks, bs, sl, out, pb, st));

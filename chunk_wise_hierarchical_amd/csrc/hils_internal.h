@@ -53,8 +53,6 @@ struct HilsPairBufs {
   uint2* tinfo;                             // [hils_pair_tiles_max]
   uint32_t* list;                           // [B*Hkv*qs_max*K]
   float* lam;                               // [B*Hkv*qs_max*K*G] fusion logits (base 2)
-  float* swa;                               // [B*Hkv*qs_max*G*d] normalised window output
-  float* lz;                                // [B*Hkv*qs_max*G] window log-mass (base 2)
   uint16_t* part;                           // [B*Hkv*qs_max*K*G*d] bf16 per-chunk outputs
   int qs_max;
 };
