@@ -133,22 +133,33 @@ def calibrate_copy(torch, dev, log):
     del a, b
 
 
-def timed(torch, _lib, fn, steps, profile):
-    """Mean ms per call of fn over `steps` calls between two HIP events on the
-    current stream.  With profile=True the library also brackets every kernel
-    with HIP events (hils_profile_enable) and the per-kernel table is returned;
-    the headline numbers come from runs with profile=False."""
+def timed(torch, _lib, fn, steps, profile, group=16):
+    """Mean ms per call of fn over `steps` calls, timed between HIP events on
+    the current stream in groups of at most `group` calls with the host
+    synchronised between groups (the time between a group's two events is
+    device time: the host enqueues far faster than the device runs).  Longer
+    unsynchronised runs of short steps fill the runtime's command queue and
+    then time the host's waits instead.  With profile=True the library also
+    brackets every kernel with HIP events (hils_profile_enable) and the
+    per-kernel table is returned; the headline numbers come from runs with
+    profile=False."""
     torch.cuda.synchronize()
     if profile:
         _lib.profile_enable(True)
         _lib.profile_read()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    total = 0.0
+    done = 0
+    while done < steps:
+        n = min(group, steps - done)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1)
+        done += n
+    ms = total / steps
     kt = None
     if profile:
         kt = _kernel_table(_lib.profile_read(), steps)
@@ -315,25 +326,14 @@ def paged_decode_bench(torch, hils, _lib, xd, wd, ks, bs, steps, log):
             step()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1) / steps
+    eager_ms, _ = timed(torch, _lib, step, steps, profile=False)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
     torch.cuda.synchronize()
     graph.replay()
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(steps):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    graph_ms = e0.elapsed_time(e1) / steps
+    graph_ms, _ = timed(torch, _lib, graph.replay, steps, profile=False)
     log(f"paged decode {eager_ms:.3f} ms/step eager, {graph_ms:.3f} ms/step graph replay "
         f"({P} pages; page summaries identical to contiguous: {same})")
     del kp, vp, lmp, ksp, bsp, ws, graph
@@ -342,14 +342,18 @@ def paged_decode_bench(torch, hils, _lib, xd, wd, ks, bs, steps, log):
             "page_summaries_identical": same}
 
 
-def multi_decode_bench(torch, hils, _lib, xd, wd, ks, bs, M, steps, log):
+def multi_decode_bench(torch, hils, _lib, xd, wd, ks, bs, M, steps, log, corr=0.0):
     """Decode of a block of M new tokens per sequence (the cache already holds
     them; token m at position T - M + m).  The per-step summary read is shared
     by the block's tokens, so tokens/s should grow with M at nearly the
-    single-step cost."""
+    single-step cost.  The block's earlier queries are seeded normals; with
+    corr > 0 they share that fraction of their variance with the last token's
+    query (adjacent positions route to overlapping chunks, section 7.2)."""
     B, Hq, _, d = xd["q"].shape
     g = torch.Generator(device="cpu").manual_seed(17)
-    qm = (torch.randn((B, Hq, M, d), generator=g)).to(xd["q"].dtype).to(xd["q"].device)
+    noise = torch.randn((B, Hq, M, d), generator=g).to(xd["q"].device)
+    last = xd["q"][:, :, 0:1].float()
+    qm = (noise * math.sqrt(1.0 - corr) + last * math.sqrt(corr)).to(xd["q"].dtype)
     qm[:, :, M - 1] = xd["q"][:, :, 0]
     qm = qm.contiguous()
     out = torch.empty_like(qm)
@@ -366,10 +370,15 @@ def multi_decode_bench(torch, hils, _lib, xd, wd, ks, bs, M, steps, log):
         step()
     ms, _ = timed(torch, _lib, step, steps, profile=False)
     _, kt = timed(torch, _lib, step, steps, profile=True)
-    log(f"decode block of {M} tokens {ms:.3f} ms/step; kernels {json.dumps(kt)}")
+    s_np = sel.cpu().numpy()
+    union = float(np.mean([len(set(s_np[b, gg].ravel().tolist()) - {-1})
+                           for b in range(B) for gg in range(wd.Hkv)]))
+    log(f"decode block of {M} tokens (query correlation {corr}) {ms:.3f} ms/step; distinct chunks "
+        f"per (sequence, KV group) {union:.1f}; kernels {json.dumps(kt)}")
     del ws, out, sel, qm
-    return {"M": M, "ms_per_step": ms, "steps_per_s": 1000.0 / ms,
-            "tokens_per_s": B * M * 1000.0 / ms, "kernels": kt}
+    return {"M": M, "query_correlation": corr, "ms_per_step": ms, "steps_per_s": 1000.0 / ms,
+            "tokens_per_s": B * M * 1000.0 / ms, "distinct_chunks_per_group": union,
+            "kernels": kt}
 
 
 def backward_bench(torch, hils, _lib, wb, steps, log):
@@ -622,6 +631,8 @@ def main():
         # a block of 4 new tokens per sequence (draft / verification tokens)
         dec["multi_token"] = multi_decode_bench(torch, hils, _lib, xd, wd, ks, bs, 4,
                                                 args.decode_steps, log)
+        dec["multi_token_correlated"] = multi_decode_bench(torch, hils, _lib, xd, wd, ks, bs, 4,
+                                                           args.decode_steps, log, corr=0.9)
         if not args.no_cpu:
             log("oracle baseline (decode sample)")
             dec["cpu_baseline"] = cpu_baseline_decode(xd, wd)

@@ -889,7 +889,7 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
                                 hipStream_t st) {
   const float tau = (float)s.tau;
   const size_t lshm = sizeof(uint32_t) * (size_t)(s.nC > 0 ? s.nC : 1);
-  hipFuncSetAttribute((const void*)k_bwd_lists, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lshm);
+  hils_allow_lds((const void*)k_bwd_lists, lshm);
   { HilsProfScope ps_("k_bwd_lists", st);
     hipLaunchKernelGGL(k_bwd_lists, dim3((unsigned)(s.B * s.Hkv)), dim3(1024), lshm, st, sel,
                        wb.off, wb.ent, s.N, s.K, s.nC); }
@@ -902,8 +902,8 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
   const int sep = dqr != nullptr;
   if (s.dtype == 0) {
     auto fr = all_keys ? k_bwd_rows2<bf16_t> : k_bwd_rows<bf16_t>;
-    hipFuncSetAttribute((const void*)fr, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rshm);
-    hipFuncSetAttribute((const void*)k_bwd_cols<bf16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)cshm);
+    hils_allow_lds((const void*)fr, rshm);
+    hils_allow_lds((const void*)k_bwd_cols<bf16_t>, cshm);
     { HilsProfScope ps_("k_bwd_rows", st);
       hipLaunchKernelGGL(fr, dim3((unsigned)((long long)s.B * s.Hkv * s.N)), dim3(BT), rshm, st,
                          (const bf16_t*)q, (const bf16_t*)qr, (const bf16_t*)k, (const bf16_t*)v,
@@ -917,8 +917,8 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
                          s.mode); }
   } else {
     auto fr = all_keys ? k_bwd_rows2<float> : k_bwd_rows<float>;
-    hipFuncSetAttribute((const void*)fr, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rshm);
-    hipFuncSetAttribute((const void*)k_bwd_cols<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)cshm);
+    hils_allow_lds((const void*)fr, rshm);
+    hils_allow_lds((const void*)k_bwd_cols<float>, cshm);
     { HilsProfScope ps_("k_bwd_rows", st);
       hipLaunchKernelGGL(fr, dim3((unsigned)((long long)s.B * s.Hkv * s.N)), dim3(BT), rshm, st,
                          (const float*)q, (const float*)qr, (const float*)k, (const float*)v,

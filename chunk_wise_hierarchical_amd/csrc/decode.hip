@@ -783,7 +783,7 @@ void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const vo
   const unsigned rows = (unsigned)(s.B * s.Hkv * s.M);
   if (P == 1) {
     const size_t sshm = (size_t)4 * (size_t)min(nm, SEL_LDS_KEYS);
-    hipFuncSetAttribute((const void*)k_dec_select<SEL_WHOLE>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sshm);
+    hils_allow_lds((const void*)k_dec_select<SEL_WHOLE>, sshm);
     HilsProfScope ps_("k_dec_select", st);
     hipLaunchKernelGGL(k_dec_select<SEL_WHOLE>, dim3(rows), dim3(SEL_NT), sshm, st, scores, lsep,
                        seqlen, keys, cand, sel, slog, s.Hq, s.Hkv, s.G, nm, (int)nsb, s.N, s.S, s.W,
@@ -791,8 +791,8 @@ void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const vo
   } else {
     const size_t pshm = (size_t)4 * (size_t)min(span, SEL_LDS_KEYS);
     const size_t mshm = (size_t)8 * (size_t)P * s.K;          // keys and chunk ids
-    hipFuncSetAttribute((const void*)k_dec_select<SEL_PART>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)pshm);
-    hipFuncSetAttribute((const void*)k_dec_select<SEL_MERGE>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)mshm);
+    hils_allow_lds((const void*)k_dec_select<SEL_PART>, pshm);
+    hils_allow_lds((const void*)k_dec_select<SEL_MERGE>, mshm);
     HilsProfScope ps_("k_dec_select", st);
     hipLaunchKernelGGL(k_dec_select<SEL_PART>, dim3(rows, P), dim3(SEL_NT), pshm, st, scores, lsep,
                        seqlen, keys, cand, sel, slog, s.Hq, s.Hkv, s.G, nm, (int)nsb, s.N, s.S, s.W,
@@ -802,7 +802,9 @@ void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const vo
                        s.K, s.M, span, P);
   }
   const dim3 agrid(s.B * s.Hkv * s.M, NS);
-  if (std::is_same<T, bf16_t>::value && s.d == DA_D && s.S == DA_S && (s.G == 1 || s.G == 2 || s.G == 4)) {
+  const bool fast_bf16 = std::is_same<T, bf16_t>::value && s.d == DA_D && s.S == DA_S &&
+                         (s.G == 1 || s.G == 2 || s.G == 4);
+  if (fast_bf16) {
     const bf16_t* qb = (const bf16_t*)q;
     const bf16_t* kb = (const bf16_t*)k;
     const bf16_t* vb = (const bf16_t*)v;
@@ -817,7 +819,7 @@ void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const vo
       hipLaunchKernelGGL((k_dec_attn_bf16<PAGED, 4>), agrid, dim3(AT_NT), 0, st, qb, kb, vb, seqlen, sel,
                          part, s.Hq, s.Hkv, s.N, s.W, s.K, NS, tau, s.M, pm);
   } else {
-    hipFuncSetAttribute((const void*)k_dec_attn<T, PAGED>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
+    hils_allow_lds((const void*)k_dec_attn<T, PAGED>, ashm);
     HilsProfScope ps_("k_dec_attn", st);
     hipLaunchKernelGGL((k_dec_attn<T, PAGED>), agrid, dim3(AT_NT), ashm, st,
                        (const T*)q, (const T*)k, (const T*)v, seqlen, sel, part,

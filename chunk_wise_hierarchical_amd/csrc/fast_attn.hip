@@ -421,7 +421,7 @@ hipError_t launch_attn(const HilsShape& s, const void* q, const void* qr, const 
   const int nqb = (s.N + QA - 1) / QA;
   const ALds L(QA, s.K);
   auto f = k_attn_fast<G>;
-  hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
+  hils_allow_lds((const void*)f, L.total);
   const float tau2 = (float)(s.tau * 1.4426950408889634);
   { HilsProfScope ps_("k_attn_fast", st); hipLaunchKernelGGL(f, dim3((unsigned)((long long)s.B * s.Hkv * nqb)), dim3(NT), L.total, st,
                      (const bf16_t*)q, (const bf16_t*)qr, (const bf16_t*)k, (const bf16_t*)vt,

@@ -776,11 +776,11 @@ hipError_t launch_pairs(const HilsShape& s, const void* q, const void* qr, const
   const size_t wshm = std::max(KT_BYTES + VT_BYTES, (size_t)4 * 32 * (s.K + 1) * 4) +
                       (size_t)4 * 8 * 64 * 16;
   const size_t ashm = KT_BYTES + VT_BYTES + (size_t)(G + 1) * KSS * 2;
-  hipFuncSetAttribute((const void*)k_pair_count, hipFuncAttributeMaxDynamicSharedMemorySize, (int)hshm);
-  hipFuncSetAttribute((const void*)k_pair_scatter, hipFuncAttributeMaxDynamicSharedMemorySize, (int)hshm);
-  hipFuncSetAttribute((const void*)k_win_fuse<G>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)wshm);
-  hipFuncSetAttribute((const void*)k_pair_attn<G, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
-  hipFuncSetAttribute((const void*)k_pair_attn<G, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ashm);
+  hils_allow_lds((const void*)k_pair_count, hshm);
+  hils_allow_lds((const void*)k_pair_scatter, hshm);
+  hils_allow_lds((const void*)k_win_fuse<G>, wshm);
+  hils_allow_lds((const void*)k_pair_attn<G, false>, ashm);
+  hils_allow_lds((const void*)k_pair_attn<G, true>, ashm);
   const bf16_t* qb = (const bf16_t*)q;
   const bf16_t* qrb = (qr == q) ? nullptr : (const bf16_t*)qr;
   const int nsb = (F + SB - 1) / SB;        // scan workgroups

@@ -611,7 +611,7 @@ hipError_t launch_score(const HilsShape& s, const void* qr, const uint4* frag, i
   const int nqb = (s.N + QB - 1) / QB;
   const Lds<G> L(s.K);
   auto f = k_score_fast<G>;
-  hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)L.total);
+  hils_allow_lds((const void*)f, L.total);
   const float tau2 = (float)(s.tau * 1.4426950408889634);
   { HilsProfScope ps_("k_score_fast", st); hipLaunchKernelGGL(f, dim3((unsigned)((long long)s.B * s.Hkv * nqb)), dim3(NT), L.total, st,
                      (const bf16_t*)qr, frag, sel, s.Hq, s.Hkv, s.N, s.W, s.K, ntg, tau2, nqb); }

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <map>
 #include <mutex>
 #include <vector>
 
@@ -217,6 +218,21 @@ hils_status scratch_ptr_current_device(void** out) {
   return HILS_OK;
 }
 }  // namespace
+
+namespace {
+std::mutex g_lds_mu;
+std::map<std::pair<const void*, int>, size_t> g_lds_set;   // (kernel, device) -> bytes allowed
+}  // namespace
+
+void hils_allow_lds(const void* kernel, size_t bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  std::lock_guard<std::mutex> lk(g_lds_mu);
+  size_t& have = g_lds_set[std::make_pair(kernel, dev)];
+  if (bytes <= have) return;
+  if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess)
+    have = bytes;
+}
 
 HilsProfScope::HilsProfScope(const char* name, hipStream_t s) : slot(-1), st(s) {
   if (!g_prof_on.load(std::memory_order_relaxed)) return;

@@ -15,6 +15,12 @@ struct HilsShape {
   int M = 1;   // decode: new tokens (queries) per sequence
 };
 
+// Lets `kernel` launch with up to `bytes` of dynamic LDS on the current
+// device.  The attribute is set only when a launch needs more than was set
+// before (per kernel and device); setting it on every launch has stalled the
+// host's enqueueing.
+void hils_allow_lds(const void* kernel, size_t bytes);
+
 // Kernel timing (hils_profile_enable): records a HIP event pair around each launch.
 struct HilsProfScope {
   HilsProfScope(const char* name, hipStream_t st);

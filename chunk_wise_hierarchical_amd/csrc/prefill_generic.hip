@@ -358,13 +358,13 @@ hipError_t hils_launch_select_generic(const HilsShape& s, const void* qr, const 
   const size_t shm = (((size_t)s.G * s.d * 4 + 15) & ~(size_t)15) + (size_t)8 * (s.nmax > 0 ? s.nmax : 1);
   if (s.dtype == 0) {
     auto f = k_select_generic<bf16_t>;
-    hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    hils_allow_lds((const void*)f, shm);
     { HilsProfScope ps_("k_select_generic", st); hipLaunchKernelGGL(f, dim3((unsigned)nblk), dim3(NT), shm, st, (const bf16_t*)qr,
                        (const bf16_t*)k, (const bf16_t*)ksum, bsum, sel, slog, s.Hq, s.Hkv, s.G, s.N,
                        s.d, s.S, s.W, s.K, s.nC, (float)s.tau, exact); }
   } else {
     auto f = k_select_generic<float>;
-    hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    hils_allow_lds((const void*)f, shm);
     { HilsProfScope ps_("k_select_generic", st); hipLaunchKernelGGL(f, dim3((unsigned)nblk), dim3(NT), shm, st, (const float*)qr,
                        (const float*)k, (const float*)ksum, bsum, sel, slog, s.Hq, s.Hkv, s.G, s.N,
                        s.d, s.S, s.W, s.K, s.nC, (float)s.tau, exact); }
@@ -378,13 +378,13 @@ hipError_t hils_launch_attn_generic(const HilsShape& s, const void* q, const voi
   const size_t shm = (size_t)s.G * s.d * 4 + (size_t)s.G * NT * 4;
   if (s.dtype == 0) {
     auto f = k_attn_generic<bf16_t>;
-    hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    hils_allow_lds((const void*)f, shm);
     { HilsProfScope ps_("k_attn_generic", st); hipLaunchKernelGGL(f, dim3((unsigned)nblk), dim3(NT), shm, st, (const bf16_t*)q,
                        (const bf16_t*)k, (const bf16_t*)v, sel, slog, (bf16_t*)out, s.Hq, s.Hkv,
                        s.G, s.N, s.d, s.S, s.W, s.K, (float)s.tau); }
   } else {
     auto f = k_attn_generic<float>;
-    hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    hils_allow_lds((const void*)f, shm);
     { HilsProfScope ps_("k_attn_generic", st); hipLaunchKernelGGL(f, dim3((unsigned)nblk), dim3(NT), shm, st, (const float*)q,
                        (const float*)k, (const float*)v, sel, slog, (float*)out, s.Hq, s.Hkv,
                        s.G, s.N, s.d, s.S, s.W, s.K, (float)s.tau); }
