@@ -133,21 +133,24 @@ def calibrate_copy(torch, dev, log):
     del a, b
 
 
-def timed(torch, _lib, fn, steps, profile, group=16):
-    """Mean ms per call of fn over `steps` calls, timed between HIP events on
-    the current stream in groups of at most `group` calls with the host
+def timed(torch, _lib, fn, steps, profile, group=16, median=False):
+    """ms per call of fn over `steps` calls, timed between HIP events on the
+    current stream in groups of at most `group` calls with the host
     synchronised between groups (the time between a group's two events is
-    device time: the host enqueues far faster than the device runs).  Longer
-    unsynchronised runs of short steps fill the runtime's command queue and
-    then time the host's waits instead.  With profile=True the library also
-    brackets every kernel with HIP events (hils_profile_enable) and the
-    per-kernel table is returned; the headline numbers come from runs with
-    profile=False."""
+    device time: the host enqueues far faster than the device runs).  The
+    result is the mean over all calls, or with median=True the median of the
+    groups' per-call times: sub-millisecond steps are exposed to rare stalls of
+    the host's enqueueing (tens of ms, seen in kernel traces as gaps inside an
+    otherwise back-to-back group), which the median of short groups ignores.
+    With profile=True the library also brackets every kernel with HIP events
+    (hils_profile_enable) and the per-kernel table is returned; the headline
+    numbers come from runs with profile=False."""
     torch.cuda.synchronize()
     if profile:
         _lib.profile_enable(True)
         _lib.profile_read()
     total = 0.0
+    per_group = []
     done = 0
     while done < steps:
         n = min(group, steps - done)
@@ -157,9 +160,11 @@ def timed(torch, _lib, fn, steps, profile, group=16):
             fn()
         e1.record()
         torch.cuda.synchronize()
-        total += e0.elapsed_time(e1)
+        t = e0.elapsed_time(e1)
+        total += t
+        per_group.append(t / n)
         done += n
-    ms = total / steps
+    ms = float(np.median(per_group)) if median else total / steps
     kt = None
     if profile:
         kt = _kernel_table(_lib.profile_read(), steps)
@@ -326,14 +331,14 @@ def paged_decode_bench(torch, hils, _lib, xd, wd, ks, bs, steps, log):
             step()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    eager_ms, _ = timed(torch, _lib, step, steps, profile=False)
+    eager_ms, _ = timed(torch, _lib, step, steps, profile=False, group=8, median=True)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
     torch.cuda.synchronize()
     graph.replay()
     torch.cuda.synchronize()
-    graph_ms, _ = timed(torch, _lib, graph.replay, steps, profile=False)
+    graph_ms, _ = timed(torch, _lib, graph.replay, steps, profile=False, group=8, median=True)
     log(f"paged decode {eager_ms:.3f} ms/step eager, {graph_ms:.3f} ms/step graph replay "
         f"({P} pages; page summaries identical to contiguous: {same})")
     del kp, vp, lmp, ksp, bsp, ws, graph
@@ -368,7 +373,7 @@ def multi_decode_bench(torch, hils, _lib, xd, wd, ks, bs, M, steps, log, corr=0.
 
     for _ in range(3):
         step()
-    ms, _ = timed(torch, _lib, step, steps, profile=False)
+    ms, _ = timed(torch, _lib, step, steps, profile=False, group=8, median=True)
     _, kt = timed(torch, _lib, step, steps, profile=True)
     s_np = sel.cpu().numpy()
     union = float(np.mean([len(set(s_np[b, gg].ravel().tolist()) - {-1})
@@ -530,7 +535,7 @@ def decode_bench(torch, hils, _lib, wd, steps, warmup, log, keep=False):
 
     for _ in range(max(3, warmup)):
         dstep()
-    dec_ms, _ = timed(torch, _lib, dstep, steps, profile=False)
+    dec_ms, _ = timed(torch, _lib, dstep, steps, profile=False, group=8, median=True)
     ms_prof, dk = timed(torch, _lib, dstep, steps, profile=True)
     log(f"decode {wd.name} {dec_ms:.4f} ms/step ({ms_prof:.4f} with kernel timing); "
         f"kernels {json.dumps(dk)}")
