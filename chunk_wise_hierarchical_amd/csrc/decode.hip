@@ -56,6 +56,8 @@ template <> struct Vec<float> {
 };
 
 constexpr int SC_CPB = HILS_DEC_SCORE_ROWS;   // chunks per scoring workgroup: 16 groups x 16 rows
+constexpr int AT_NT = 256;                    // threads of a split-attention workgroup
+constexpr int DA_D = 128, DA_S = 64;          // shape of the specialised bf16 split attention
 
 // Scores of 256 consecutive chunk rows of one (sequence, query head): a
 // 16-lane group owns 16 consecutive rows and reads each row with 16-byte loads
@@ -75,16 +77,46 @@ struct PageMap {
   }
 };
 
-template <typename T, bool PAGED, int MT>
+template <bool PAGED, int G>
+__device__ __forceinline__ void dec_split_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                               const bf16_t* __restrict__ v, const int32_t* __restrict__ seqlen,
+                                               const int32_t* __restrict__ sel, float* __restrict__ part,
+                                               int Hq, int Hkv, int N, int W, int K, int NS, float tau,
+                                               int M, PageMap pm, int bgm, int s);
+
+// The window tiles of a single-token step do not depend on the selection, so
+// with WG > 0 (bf16, d = 128, S = 64, G = WG heads per KV group) the scoring
+// grid carries them: workgroups x >= nsb of row y = (sequence, head h) run
+// window splits h % WG + WG j of that head's KV group, interleaved with the
+// scoring workgroups so that their loads share the scoring pass's time.
+struct WinArgs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  float* part;
+  int Hkv, K, NS, nwin;
+};
+
+template <typename T, bool PAGED, int MT, int WG>
 __global__ void __launch_bounds__(256)
 k_dec_score(const T* __restrict__ qr, const T* __restrict__ ksum, const float* __restrict__ bsum,
             const int32_t* __restrict__ seqlen, float* __restrict__ scores, float* __restrict__ lsep,
             int Hq, int nC, int nmax, int nsb, int N, int d, int S, int W, float tau, int M,
-            PageMap pm) {
+            PageMap pm, WinArgs wa) {
   constexpr int V = Vec<T>::N;
   constexpr int MAXT = 256 / (16 * V) > 0 ? 256 / (16 * V) : 1;
   constexpr int R = 16;
   __shared__ float red_m[4][MT], red_s[4][MT];
+  if constexpr (WG > 0) {
+    if ((int)blockIdx.x >= nsb) {
+      const int bq = (int)(blockIdx.y / Hq), hq = (int)(blockIdx.y % Hq);
+      const int w = hq % WG + WG * ((int)blockIdx.x - nsb);
+      if (w < wa.nwin)
+        dec_split_bf16<PAGED, WG>(wa.q, wa.k, wa.v, seqlen, nullptr, wa.part, Hq, wa.Hkv, N, W, wa.K,
+                                  wa.NS, tau, 1, pm, bq * wa.Hkv + hq / WG, wa.K + w);
+      return;
+    }
+  }
   // grid x: 256-row block (fastest, so neighbouring workgroups stream adjacent
   // rows of one head), grid y: (sequence, head)
   const long long bh = blockIdx.y;
@@ -409,8 +441,6 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
   }
 }
 
-constexpr int AT_NT = 256;
-
 // One workgroup per (sequence, KV group, split): a split is one selected chunk
 // or one S-token window tile (S <= 64, G <= 8, checked on the host).  The K and
 // V rows of the split are staged in LDS with 16-byte loads; thread (head, key)
@@ -554,14 +584,14 @@ k_dec_attn(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
 //           a wave are summed with row swaps, the four waves in LDS.
 // Rows past the split's last token are read at that token (their weight is
 // 0), so every load stays inside the split's written rows.
-constexpr int DA_D = 128, DA_S = 64;
-
+// split s of query row bgm = (sequence, KV group, query), by a workgroup of
+// AT_NT threads
 template <bool PAGED, int G>
-__global__ void __launch_bounds__(AT_NT)
-k_dec_attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                const bf16_t* __restrict__ v, const int32_t* __restrict__ seqlen,
-                const int32_t* __restrict__ sel, float* __restrict__ part, int Hq, int Hkv, int N,
-                int W, int K, int NS, float tau, int M, PageMap pm) {
+__device__ __forceinline__ void dec_split_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                               const bf16_t* __restrict__ v, const int32_t* __restrict__ seqlen,
+                                               const int32_t* __restrict__ sel, float* __restrict__ part,
+                                               int Hq, int Hkv, int N, int W, int K, int NS, float tau,
+                                               int M, PageMap pm, int bgm, int s) {
   constexpr int D = DA_D, S = DA_S;
   __shared__ __align__(16) float qs[G][D];
   __shared__ __align__(16) float dp[4][G][S];     // partial dots by element quarter
@@ -569,7 +599,6 @@ k_dec_attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   __shared__ __align__(16) float red[4][G][D];    // output partials by key quarter
   __shared__ float hm[G], hl[G];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int bgm = blockIdx.x, s = blockIdx.y;
   const int m = bgm % M, bg = bgm / M;
   const int b = bg / Hkv, g = bg % Hkv;
   auto hrow = [&](int r) { return ((long long)b * Hq + (long long)g * G + r) * M + m; };
@@ -696,6 +725,17 @@ k_dec_attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   }
 }
 
+// grid (sequence x KV group x query, split)
+template <bool PAGED, int G>
+__global__ void __launch_bounds__(AT_NT)
+k_dec_attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                const bf16_t* __restrict__ v, const int32_t* __restrict__ seqlen,
+                const int32_t* __restrict__ sel, float* __restrict__ part, int Hq, int Hkv, int N,
+                int W, int K, int NS, float tau, int M, PageMap pm) {
+  dec_split_bf16<PAGED, G>(q, k, v, seqlen, sel, part, Hq, Hkv, N, W, K, NS, tau, M, pm,
+                           (int)blockIdx.x, (int)blockIdx.y);
+}
+
 // Per (sequence, query head): merge the window tiles in the log domain, take
 // the chunk-level softmax over {s_hat_c} U {log Z_swa}, and form the output as
 // one weighted sum of the split partials.  Wave 0 computes the split weights.
@@ -749,15 +789,16 @@ k_dec_combine(const float* __restrict__ part, const float* __restrict__ slog,
   }
 }
 
-template <typename T, bool PAGED, int MT>
+template <typename T, bool PAGED, int MT, int WG = 0>
 void launch_score(const HilsShape& s, const void* qr, const int32_t* seqlen, const void* ksum,
                   const float* bsum, float* scores, float* lsep, unsigned nsb, PageMap pm,
-                  hipStream_t st) {
+                  hipStream_t st, WinArgs wa = WinArgs{}) {
   const unsigned nz = (unsigned)((s.M + MT - 1) / MT);
+  const unsigned nwx = WG > 0 ? (unsigned)((wa.nwin + WG - 1) / WG) : 0u;
   { HilsProfScope ps_("k_dec_score", st);
-    hipLaunchKernelGGL((k_dec_score<T, PAGED, MT>), dim3(nsb, s.B * s.Hq, nz), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_dec_score<T, PAGED, MT, WG>), dim3(nsb + nwx, s.B * s.Hq, nz), dim3(256), 0, st,
                        (const T*)qr, (const T*)ksum, bsum, seqlen, scores, lsep, s.Hq, s.nC, s.nmax,
-                       (int)nsb, s.N, s.d, s.S, s.W, (float)s.tau, s.M, pm); }
+                       (int)nsb, s.N, s.d, s.S, s.W, (float)s.tau, s.M, pm, wa); }
 }
 
 template <typename T, bool PAGED>
@@ -772,7 +813,18 @@ void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const vo
   const size_t ashm = 2 * (size_t)s.S * (s.d + 16 / esz) * esz + (size_t)s.G * s.d * 4 +
                       (size_t)s.G * ((s.S + 3) & ~3) * 4;
   const size_t cshm = (size_t)NS * 4;
-  if (nsb > 0) {
+  const bool fast_bf16 = std::is_same<T, bf16_t>::value && s.d == DA_D && s.S == DA_S &&
+                         (s.G == 1 || s.G == 2 || s.G == 4);
+  // single-token bf16 steps take their window splits inside the scoring launch
+  const bool win_in_score = fast_bf16 && s.M == 1;
+  if (win_in_score) {
+    if constexpr (std::is_same<T, bf16_t>::value) {
+      const WinArgs wa{(const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, part, s.Hkv, s.K, NS, s.nwin};
+      if (s.G == 1) launch_score<T, PAGED, 1, 1>(s, qr, seqlen, ksum, bsum, scores, lsep, nsb, pm, st, wa);
+      else if (s.G == 2) launch_score<T, PAGED, 1, 2>(s, qr, seqlen, ksum, bsum, scores, lsep, nsb, pm, st, wa);
+      else launch_score<T, PAGED, 1, 4>(s, qr, seqlen, ksum, bsum, scores, lsep, nsb, pm, st, wa);
+    }
+  } else if (nsb > 0) {
     if (s.M == 1) launch_score<T, PAGED, 1>(s, qr, seqlen, ksum, bsum, scores, lsep, nsb, pm, st);
     else if (s.M == 2) launch_score<T, PAGED, 2>(s, qr, seqlen, ksum, bsum, scores, lsep, nsb, pm, st);
     else launch_score<T, PAGED, 4>(s, qr, seqlen, ksum, bsum, scores, lsep, nsb, pm, st);
@@ -801,9 +853,7 @@ void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const vo
                        seqlen, keys, cand, sel, slog, s.Hq, s.Hkv, s.G, nm, (int)nsb, s.N, s.S, s.W,
                        s.K, s.M, span, P);
   }
-  const dim3 agrid(s.B * s.Hkv * s.M, NS);
-  const bool fast_bf16 = std::is_same<T, bf16_t>::value && s.d == DA_D && s.S == DA_S &&
-                         (s.G == 1 || s.G == 2 || s.G == 4);
+  const dim3 agrid(s.B * s.Hkv * s.M, win_in_score ? s.K : NS);
   if (fast_bf16) {
     const bf16_t* qb = (const bf16_t*)q;
     const bf16_t* kb = (const bf16_t*)k;
