@@ -20,6 +20,17 @@
 
 namespace {
 
+using fastp::fast_exp2;
+using fastp::ld_bf16x8;
+using fastp::LN2;
+using fastp::LOG2E;
+using fastp::max_x16;
+using fastp::max_x32;
+using fastp::mfma16;
+using fastp::pack_bf16x2;
+using fastp::sum_x16;
+using fastp::sum_x32;
+
 // position of query m of a block of M new tokens of a sequence whose length is
 // seqlen (clamped into the cache; a position below 0 is evaluated at 0)
 __device__ __forceinline__ long long dec_pos(int32_t seqlen, int cap, int M, int m) {
@@ -572,18 +583,146 @@ k_dec_attn(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict
   }
 }
 
-// Specialised split attention for bf16, d = 128, S = 64, G <= 4 (same
-// partials as k_dec_attn).  Every K and V load of the split is issued at the
-// start, straight into registers:
-//   logits: wave w takes elements [32w, 32w + 32) of key row j = lane and
-//           forms its partial dot with each head's query (broadcast LDS
-//           reads); the four partials meet in LDS and wave h takes head h's
-//           softmax over the keys;
-//   output: wave w takes keys [16w, 16w + 16), lane = (8-element slice e8 =
-//           lane % 16, 4 keys 16w + 4 (lane / 16) + u); the four key groups of
-//           a wave are summed with row swaps, the four waves in LDS.
-// Rows past the split's last token are read at that token (their weight is
-// 0), so every load stays inside the split's written rows.
+// Split attention on the matrix cores for bf16, d = 128, S = 64 (same
+// partials as k_dec_attn): up to 16 query rows (the G heads of a query, or the
+// heads of several tokens of a block) against one S-token tile, as
+// S^T = K Q^T and O^T = V^T P^T with v_mfma_f32_16x16x32_bf16 (lane l, i =
+// l % 16, g = l / 16: A operand A[i][8g..8g+7], B operand B[8g..8g+7][i],
+// result D[4g + r][i]).  Wave w scores 16 keys: A-operand row i stands for key
+// kperm(w, i) = 32 (w / 2) + 8 (i / 4) + 4 (w % 2) + i % 4, so that the four
+// waves' results put keys 32 kb + 8g .. 32 kb + 8g + 7 of every row in lane
+// group g, which is the B operand of O^T's k-block kb as stored.  V^T is
+// staged in LDS (the cache holds V row-major); wave w forms output elements
+// 32w .. 32w + 31.  Softmax statistics meet in LDS (two barriers).
+constexpr int VTS = DA_S + 4;   // V^T row stride (bf16): 8-byte aligned rows, banks spread
+constexpr int PTS = DA_S + 8;   // P row stride (bf16): 16-byte aligned rows
+
+struct MfLds {
+  uint16_t vt[DA_D][VTS];       // V^T of the tile, zero past its valid keys
+  uint16_t pt[16][PTS];         // P (row = query row), bf16
+  float mx[4][16], sm[4][16];   // per-wave row maxima and exp sums
+};
+
+__device__ __forceinline__ int kperm(int w, int i) {
+  return 32 * (w >> 1) + 8 * (i >> 2) + 4 * (w & 1) + (i & 3);
+}
+
+// this wave's K A operand (keys kperm(w, i), rows past jmax - 1 read row jmax - 1)
+__device__ __forceinline__ void mf_load_k(const bf16_t* __restrict__ kg, int jmax, uint4 (&ka)[4]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int key = min(kperm(w, lane & 15), jmax - 1);
+  const bf16_t* kr = kg + (long long)key * DA_D + 8 * (lane >> 4);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) ka[ks] = *reinterpret_cast<const uint4*>(kr + 32 * ks);
+}
+
+// V tile (jmax valid rows) into L.vt, transposed; rows past jmax are zero and
+// are not read.  Lane (e8 = l % 16, kq = l / 16) of wave w loads keys
+// 16 w + 4 kq + u, elements 8 e8 .. 8 e8 + 7 (whole rows per instruction).
+__device__ __forceinline__ void mf_stage_v(MfLds& L, const bf16_t* __restrict__ vg, int jmax) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e8 = lane & 15, kq = lane >> 4;
+  uint4 x[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int key = 16 * w + 4 * kq + u;
+    x[u] = (key < jmax) ? *reinterpret_cast<const uint4*>(vg + (long long)key * DA_D + 8 * e8)
+                        : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int key = 16 * w + 4 * kq + u;
+    const uint32_t wd[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      L.vt[8 * e8 + 2 * t][key] = (uint16_t)(wd[t] & 0xffffu);
+      L.vt[8 * e8 + 2 * t + 1][key] = (uint16_t)(wd[t] >> 16);
+    }
+  }
+}
+
+// the empty partial (weight 0) of split s for rows hrow0 + r * hstep
+template <int G>
+__device__ __forceinline__ void split_empty(float* __restrict__ part, long long hrow0, int hstep, int NS, int s) {
+  for (int t = threadIdx.x; t < G * (DA_D + 2); t += AT_NT) {
+    const int r = t / (DA_D + 2), e = t - r * (DA_D + 2);
+    part[((hrow0 + (long long)r * hstep) * NS + s) * (long long)(DA_D + 2) + e] = (e == 0) ? -INFINITY : 0.0f;
+  }
+}
+
+// One pass over up to 16 rows; every thread calls it with the data of row
+// j = lane % 16: its query's B operand (mf_load_q), ok (row exists), hrow (its
+// partial row), slot (its split) and jn (its valid keys, >= 1).  L.vt must hold the tile (a
+// barrier after staging); a pass after the first (first = false) waits for
+// the previous pass's LDS readers.
+__device__ __forceinline__ void mf_load_q(const bf16_t* __restrict__ q, bool ok, long long hrow, bf16x8_t (&qb)[4]) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qb[ks] = ok ? ld_bf16x8(q + hrow * DA_D + 32 * ks + 8 * g)
+                : __builtin_bit_cast(bf16x8_t, make_uint4(0u, 0u, 0u, 0u));
+}
+
+__device__ __forceinline__ void mf_rows(MfLds& L, const bf16x8_t (&qb)[4], float* __restrict__ part,
+                                        int NS, float tau2, const uint4 (&ka)[4], bool ok,
+                                        long long hrow, int slot, int jn, bool first) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) sc = mfma16(__builtin_bit_cast(bf16x8_t, ka[ks]), qb[ks], sc);
+  // sc[r]: row j, key kb0 + r (base-2 logits after scaling)
+  const int kb0 = 32 * (w >> 1) + 8 * g + 4 * (w & 1);
+  float x[4];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    x[r] = (kb0 + r < jn) ? sc[r] * tau2 : -INFINITY;
+    mloc = fmaxf(mloc, x[r]);
+  }
+  mloc = max_x32(max_x16(mloc));
+  if (!first) __syncthreads();                   // the previous pass's readers
+  if (g == 0) L.mx[w][j] = mloc;
+  __syncthreads();                                // mx
+  const float Mj = fmaxf(fmaxf(L.mx[0][j], L.mx[1][j]), fmaxf(L.mx[2][j], L.mx[3][j]));
+  float p[4];
+  float ps = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    p[r] = (x[r] == -INFINITY) ? 0.0f : fast_exp2(x[r] - Mj);
+    ps += p[r];
+  }
+  ps = sum_x32(sum_x16(ps));
+  if (g == 0) L.sm[w][j] = ps;
+  *reinterpret_cast<uint2*>(&L.pt[j][kb0]) = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+  __syncthreads();                                // pt, sm
+  bf16x8_t pb[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) pb[kb] = ld_bf16x8(reinterpret_cast<const bf16_t*>(&L.pt[j][32 * kb + 8 * g]));
+  float* pp = part + (hrow * NS + slot) * (long long)(DA_D + 2);
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int dt = 2 * w + h2;
+    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint16_t* vr = &L.vt[16 * dt + j][32 * kb + 8 * g];
+      const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vr + 4);
+      o = mfma16(__builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y)), pb[kb], o);
+    }
+    // o[r] = O^T[16 dt + 4g + r][row j], unnormalised
+    if (ok) {
+      *reinterpret_cast<float2*>(pp + 2 + 16 * dt + 4 * g) = make_float2(o[0], o[1]);
+      *reinterpret_cast<float2*>(pp + 2 + 16 * dt + 4 * g + 2) = make_float2(o[2], o[3]);
+    }
+  }
+  if (ok && w == 0 && g == 0) {
+    pp[0] = Mj * LN2;                             // natural-log units, as the combine takes them
+    pp[1] = (L.sm[0][j] + L.sm[1][j]) + (L.sm[2][j] + L.sm[3][j]);
+  }
+}
+
 // split s of query row bgm = (sequence, KV group, query), by a workgroup of
 // AT_NT threads
 template <bool PAGED, int G>
@@ -593,19 +732,10 @@ __device__ __forceinline__ void dec_split_bf16(const bf16_t* __restrict__ q, con
                                                int Hq, int Hkv, int N, int W, int K, int NS, float tau,
                                                int M, PageMap pm, int bgm, int s) {
   constexpr int D = DA_D, S = DA_S;
-  __shared__ __align__(16) float qs[G][D];
-  __shared__ __align__(16) float dp[4][G][S];     // partial dots by element quarter
-  __shared__ __align__(16) float ps[G][S];        // softmax weights
-  __shared__ __align__(16) float red[4][G][D];    // output partials by key quarter
-  __shared__ float hm[G], hl[G];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ __align__(16) MfLds L;
   const int m = bgm % M, bg = bgm / M;
   const int b = bg / Hkv, g = bg % Hkv;
-  auto hrow = [&](int r) { return ((long long)b * Hq + (long long)g * G + r) * M + m; };
-  for (int t = tid; t < G * D; t += AT_NT) {
-    const int r = t / D;
-    qs[r][t - r * D] = bf16_to_f32(q[hrow(r) * D + (t - r * D)]);
-  }
+  const long long hrow0 = ((long long)b * Hq + (long long)g * G) * M + m;   // row r: hrow0 + r M
   const int csel = (s < K) ? sel[(long long)bgm * K + s] : -1;
   const long long i = dec_pos(seqlen[b], N, M, m);
   long long j0 = 0;
@@ -617,112 +747,20 @@ __device__ __forceinline__ void dec_split_bf16(const bf16_t* __restrict__ q, con
     if (j0 <= i) jn = (int)min((long long)S, i - j0 + 1);
   }
   if (jn == 0) {
-    for (int t = tid; t < G * (D + 2); t += AT_NT) {
-      const int r = t / (D + 2), e = t - r * (D + 2);
-      part[(hrow(r) * NS + s) * (long long)(D + 2) + e] = (e == 0) ? -INFINITY : 0.0f;
-    }
+    split_empty<G>(part, hrow0, M, NS, s);
     return;
   }
   const long long kvoff = PAGED ? (pm.page(b, j0 / S) * Hkv + g) * (long long)S * D
                                 : ((b * (long long)Hkv + g) * N + j0) * D;
-  const bf16_t* kg = k + kvoff;
-  const bf16_t* vg = v + kvoff;
-  // logit loads: key row min(lane, jn - 1), elements [32 wv, 32 wv + 32)
-  uint4 kx[4];
-  {
-    const bf16_t* kr = kg + (long long)min(lane, jn - 1) * D + 32 * wv;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) kx[u] = *reinterpret_cast<const uint4*>(kr + 8 * u);
-  }
-  // output loads: keys 16 wv + 4 kq + u, elements [8 e8, 8 e8 + 8)
-  const int e8 = lane & 15, kq = lane >> 4;
-  const int jb = 16 * wv + 4 * kq;
-  uint4 vx[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    vx[u] = *reinterpret_cast<const uint4*>(vg + (long long)min(jb + u, jn - 1) * D + 8 * e8);
-  __syncthreads();                                // qs
-  {
-    float kf[32];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t w4[4] = {kx[u].x, kx[u].y, kx[u].z, kx[u].w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        kf[8 * u + 2 * t] = __uint_as_float(w4[t] << 16);
-        kf[8 * u + 2 * t + 1] = __uint_as_float(w4[t] & 0xffff0000u);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < G; ++r) {
-      const float* qq = &qs[r][32 * wv];
-      float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 32; e += 8) {
-        const float4 qa = *reinterpret_cast<const float4*>(qq + e);
-        const float4 qb = *reinterpret_cast<const float4*>(qq + e + 4);
-        a0 = fmaf(qa.x, kf[e], a0);
-        a1 = fmaf(qa.y, kf[e + 1], a1);
-        a0 = fmaf(qa.z, kf[e + 2], a0);
-        a1 = fmaf(qa.w, kf[e + 3], a1);
-        a0 = fmaf(qb.x, kf[e + 4], a0);
-        a1 = fmaf(qb.y, kf[e + 5], a1);
-        a0 = fmaf(qb.z, kf[e + 6], a0);
-        a1 = fmaf(qb.w, kf[e + 7], a1);
-      }
-      dp[wv][r][lane] = a0 + a1;
-    }
-  }
-  __syncthreads();                                // dp
-  if (wv < G) {
-    const int r = wv;
-    const float dot = (dp[0][r][lane] + dp[1][r][lane]) + (dp[2][r][lane] + dp[3][r][lane]);
-    const float x = (lane < jn) ? tau * dot : -INFINITY;
-    const float mx = wave_max_f(x);
-    const float p = (lane < jn) ? __expf(x - mx) : 0.0f;
-    const float l = wave_sum_f(p);
-    ps[r][lane] = p;
-    if (lane == 0) { hm[r] = mx; hl[r] = l; }
-  }
-  __syncthreads();                                // ps, hm, hl
-  {
-    float vf[4][8];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t w4[4] = {vx[u].x, vx[u].y, vx[u].z, vx[u].w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        vf[u][2 * t] = __uint_as_float(w4[t] << 16);
-        vf[u][2 * t + 1] = __uint_as_float(w4[t] & 0xffff0000u);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < G; ++r) {
-      const float4 p4 = *reinterpret_cast<const float4*>(&ps[r][jb]);
-      const float pu[4] = {p4.x, p4.y, p4.z, p4.w};
-      float o[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float a = pu[0] * vf[0][e];
-        a = fmaf(pu[1], vf[1][e], a);
-        a = fmaf(pu[2], vf[2][e], a);
-        a = fmaf(pu[3], vf[3][e], a);
-        // the wave's four key groups (lanes l, l ^ 16, l ^ 32, l ^ 48)
-        o[e] = fastp::sum_x32(fastp::sum_x16(a));
-      }
-      if (kq == 0) {
-        *reinterpret_cast<float4*>(&red[wv][r][8 * e8]) = make_float4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<float4*>(&red[wv][r][8 * e8 + 4]) = make_float4(o[4], o[5], o[6], o[7]);
-      }
-    }
-  }
-  __syncthreads();                                // red
-  for (int t = tid; t < G * D; t += AT_NT) {
-    const int r = t / D, e = t - r * D;
-    float* pp = part + (hrow(r) * NS + s) * (long long)(D + 2);
-    pp[2 + e] = (red[0][r][e] + red[1][r][e]) + (red[2][r][e] + red[3][r][e]);
-    if (e == 0) { pp[0] = hm[r]; pp[1] = hl[r]; }
-  }
+  const int r = threadIdx.x & 15;
+  const long long hrow = hrow0 + (long long)min(r, G - 1) * M;
+  bf16x8_t qb[4];
+  mf_load_q(q, r < G, hrow, qb);
+  uint4 ka[4];
+  mf_load_k(k + kvoff, jn, ka);
+  mf_stage_v(L, v + kvoff, jn);
+  __syncthreads();                                // vt
+  mf_rows(L, qb, part, NS, tau * LOG2E, ka, r < G, hrow, s, jn, true);
 }
 
 // grid (sequence x KV group x query, split)
@@ -734,6 +772,180 @@ k_dec_attn_bf16(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 int W, int K, int NS, float tau, int M, PageMap pm) {
   dec_split_bf16<PAGED, G>(q, k, v, seqlen, sel, part, Hq, Hkv, N, W, K, NS, tau, M, pm,
                            (int)blockIdx.x, (int)blockIdx.y);
+}
+
+// Multi-token blocks (M > 1), bf16, d = 128, S = 64: the block's tokens share
+// most of their window tiles and, when their queries are alike, many selected
+// chunks (section 4.2: a query block loads the union of its chunks once;
+// section 7.2: chunk overlap of adjacent queries).  One workgroup per
+// (sequence, KV group, union element) loads a tile once and attends it for
+// every token of the block that uses it, writing the same split partials as
+// the per-token kernel (the combine is unchanged):
+//   y < M K:  the y-th smallest distinct chunk id of the block's M selections
+//             (k_dec_union lists them; workgroups past the union's size have
+//             none), for each token that selected it at its own slot; the
+//             workgroup also writes the empty partial of slot (y / K, y % K)
+//             when that token selected fewer chunks;
+//   y >= M K: window tile ws_0 / S + (y - M K), ws_0 = the first token's window
+//             start, for each token whose window holds it (tokens differ only
+//             in where their windows start and end); the workgroup also writes
+//             the empty partial of window slot y - M K of tokens whose
+//             windows span fewer tiles.
+constexpr int UN_IDS = HILS_DEC_UNION_IDS;       // M K ids held in LDS
+constexpr int UN_WORDS = HILS_DEC_UNION_CHUNKS / 32;   // bitmap words over chunk ids
+
+__device__ __forceinline__ int lower_bound_i32(const int* a, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Per (sequence, KV group) of a multi-token block: the union of the tokens'
+// selections in ascending chunk order (a bitmap over chunk ids, then one block
+// scan of its set-bit counts) and each token's slot of every union element.
+// Layout of `uni`: per (sequence, KV group) the union's size and its M K ids;
+// then per (sequence, KV group, union element, token) one signed byte.
+__global__ void __launch_bounds__(AT_NT)
+k_dec_union(const int32_t* __restrict__ sel, const int32_t* __restrict__ seqlen, int32_t* __restrict__ uni,
+            int Hkv, int N, int W, int S, int K, int M, int nC) {
+  __shared__ uint32_t bits[UN_WORDS];
+  __shared__ int ids[UN_IDS], uu[UN_IDS];
+  __shared__ int wtot[AT_NT / 64];
+  __shared__ int kkm[HILS_MAX_DECODE_QUERIES];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int bg = blockIdx.x, nbg = gridDim.x, b = bg / Hkv;
+  const int mk = M * K;
+  int32_t* ub = uni + (long long)bg * (mk + 1);
+  int8_t* us = reinterpret_cast<int8_t*>(uni + (long long)nbg * (mk + 1)) + (long long)bg * mk * M;
+  const int nw = (nC + 31) >> 5;
+  for (int t = tid; t < nw; t += AT_NT) bits[t] = 0u;
+  if (tid < M) kkm[tid] = min(K, n_cand(dec_pos(seqlen[b], N, M, tid), W, S));
+  __syncthreads();
+  for (int e = tid; e < mk; e += AT_NT) {
+    const int m = e / K, kx = e - m * K;
+    const int c = (kx < kkm[m]) ? sel[((long long)bg * M + m) * K + kx] : -1;
+    ids[e] = c;
+    if (c >= 0 && c < nC) atomicOr(&bits[c >> 5], 1u << (c & 31));
+  }
+  __syncthreads();
+  // each thread takes a contiguous run of words; its set bits go to the union
+  // after those of the runs before it
+  const int per = (nw + AT_NT - 1) / AT_NT;
+  const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
+  int cnt = 0;
+  for (int t = w0; t < w1; ++t) cnt += __popc(bits[t]);
+  int inc = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int up = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += up;
+  }
+  if (lane == 63) wtot[wv] = inc;
+  __syncthreads();
+  int pos = inc - cnt, total = 0;
+  for (int u = 0; u < AT_NT / 64; ++u) {
+    if (u < wv) pos += wtot[u];
+    total += wtot[u];
+  }
+  for (int t = w0; t < w1; ++t) {
+    uint32_t x = bits[t];
+    while (x) {
+      const int c = t * 32 + __ffs(x) - 1;
+      uu[pos] = c;
+      ub[1 + pos] = c;
+      ++pos;
+      x &= x - 1u;
+    }
+  }
+  if (tid == 0) ub[0] = total;
+  for (int e = total + tid; e < mk; e += AT_NT) ub[1 + e] = -1;   // no chunk past the union
+  __syncthreads();
+  for (int e = tid; e < total * M; e += AT_NT) {
+    const int u = e / M, m = e - u * M;
+    const int c = uu[u], n = kkm[m];
+    const int p = lower_bound_i32(ids + m * K, n, c);
+    us[e] = (int8_t)((p < n && ids[m * K + p] == c) ? p : -1);
+  }
+}
+
+template <bool PAGED, int G>
+__global__ void __launch_bounds__(AT_NT)
+k_dec_attn_union(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                 const bf16_t* __restrict__ v, const int32_t* __restrict__ seqlen,
+                 const int32_t* __restrict__ uni, float* __restrict__ part, int Hq, int Hkv, int N,
+                 int W, int K, int NS, int nwin, float tau, int M, PageMap pm) {
+  constexpr int D = DA_D, S = DA_S;
+  __shared__ __align__(16) MfLds L;
+  __shared__ int tsl[HILS_MAX_DECODE_QUERIES], tjn[HILS_MAX_DECODE_QUERIES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int bg = blockIdx.x, y = blockIdx.y;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const long long hbase = ((long long)b * Hq + (long long)g * G) * M;   // row (r, m): hbase + r M + m
+  const int mk = M * K;
+  const int sl = seqlen[b];
+  long long j0;
+  int jmax;
+  if (y < mk) {
+    // the chunk (-1 past the union) and, by thread m < M, token m's slot of
+    // it: neither depends on the other, so both loads go out together
+    const int c = uni[(long long)bg * (mk + 1) + 1 + y];
+    const int8_t* us = reinterpret_cast<const int8_t*>(uni + (long long)gridDim.x * (mk + 1)) +
+                       ((long long)bg * mk + y) * M;
+    const int myslot = (tid < M) ? (int)us[tid] : -1;
+    const int mu = y / K, su = y - mu * K;
+    if (su >= min(K, n_cand(dec_pos(sl, N, M, mu), W, S))) split_empty<G>(part, hbase + mu, M, NS, su);
+    if (c < 0) return;
+    j0 = (long long)c * S;
+    jmax = S;
+    if (tid < M) { tsl[tid] = myslot; tjn[tid] = S; }
+  } else {
+    const int vt = y - mk;
+    const long long i0 = dec_pos(sl, N, M, 0), iM = dec_pos(sl, N, M, M - 1);
+    j0 = window_start(i0, W, S) + (long long)vt * S;   // tile start
+    for (int m = 0; m < M; ++m) {                // window slots past a token's tiles
+      const long long im = dec_pos(sl, N, M, m);
+      const int cntm = (int)(im / S - window_start(im, W, S) / S) + 1;
+      if (vt < nwin && vt >= cntm) split_empty<G>(part, hbase + m, M, NS, K + vt);
+    }
+    if (j0 > iM) return;
+    jmax = (int)min((long long)S, iM - j0 + 1);
+    if (tid < M) {                               // tokens whose windows hold the tile
+      const long long im = dec_pos(sl, N, M, tid);
+      const long long wsm = window_start(im, W, S);
+      const bool in = j0 >= wsm && j0 <= im;
+      tsl[tid] = in ? K + (int)((j0 - wsm) / S) : -1;
+      tjn[tid] = in ? (int)min((long long)S, im - j0 + 1) : 0;
+    }
+  }
+  const long long kvoff = PAGED ? (pm.page(b, j0 / S) * Hkv + g) * (long long)S * D
+                                : ((b * (long long)Hkv + g) * N + j0) * D;
+  uint4 ka[4];
+  mf_load_k(k + kvoff, jmax, ka);
+  mf_stage_v(L, v + kvoff, jmax);
+  __syncthreads();                                // vt, tsl, tjn
+  // rows (n-th token using the tile, head r) in passes of 16: row idx = G n + r
+  int ntok = 0;
+  for (int m = 0; m < M; ++m) ntok += (tsl[m] >= 0) ? 1 : 0;
+  const int nrow = G * ntok;
+  const float tau2 = tau * LOG2E;
+  for (int base = 0; base < nrow; base += 16) {
+    const int idx = base + (lane & 15);
+    const bool ok = idx < nrow;
+    const int n = ok ? idx / G : 0, r = ok ? idx % G : 0;
+    int m = 0;
+    for (int seen = -1; m < M; ++m) {            // the n-th token with a slot
+      seen += (tsl[m] >= 0) ? 1 : 0;
+      if (seen == n) break;
+    }
+    m = min(m, M - 1);
+    const long long hrow = hbase + (long long)r * M + m;
+    bf16x8_t qb[4];
+    mf_load_q(q, ok, hrow, qb);
+    mf_rows(L, qb, part, NS, tau2, ka, ok, hrow, tsl[m], tjn[m], base == 0);
+  }
 }
 
 // Per (sequence, query head): merge the window tiles in the log domain, take
@@ -804,8 +1016,8 @@ void launch_score(const HilsShape& s, const void* qr, const int32_t* seqlen, con
 template <typename T, bool PAGED>
 void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const void* k, const void* v,
                      const int32_t* seqlen, const void* ksum, const float* bsum, void* out,
-                     int32_t* sel, float* scores, uint32_t* keys, uint2* cand, float* slog,
-                     float* part, float* lsep, PageMap pm, hipStream_t st) {
+                     int32_t* sel, float* scores, uint32_t* keys, uint2* cand, int32_t* uni,
+                     float* slog, float* part, float* lsep, PageMap pm, hipStream_t st) {
   const int NS = s.K + s.nwin;
   const float tau = (float)s.tau;
   const unsigned nsb = (unsigned)((s.nmax + SC_CPB - 1) / SC_CPB);
@@ -854,7 +1066,27 @@ void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const vo
                        s.K, s.M, span, P);
   }
   const dim3 agrid(s.B * s.Hkv * s.M, win_in_score ? s.K : NS);
-  if (fast_bf16) {
+  if (hils_dec_union(s)) {
+    if constexpr (std::is_same<T, bf16_t>::value) {
+      { HilsProfScope ps_("k_dec_union", st);
+        hipLaunchKernelGGL(k_dec_union, dim3(s.B * s.Hkv), dim3(AT_NT), 0, st, sel, seqlen, uni, s.Hkv, s.N,
+                           s.W, s.S, s.K, s.M, s.nC); }
+      const dim3 ugrid(s.B * s.Hkv, s.M * s.K + s.nwin + 1);
+      const bf16_t* qb = (const bf16_t*)q;
+      const bf16_t* kb = (const bf16_t*)k;
+      const bf16_t* vb = (const bf16_t*)v;
+      HilsProfScope ps_("k_dec_attn", st);
+      if (s.G == 1)
+        hipLaunchKernelGGL((k_dec_attn_union<PAGED, 1>), ugrid, dim3(AT_NT), 0, st, qb, kb, vb, seqlen,
+                           uni, part, s.Hq, s.Hkv, s.N, s.W, s.K, NS, s.nwin, tau, s.M, pm);
+      else if (s.G == 2)
+        hipLaunchKernelGGL((k_dec_attn_union<PAGED, 2>), ugrid, dim3(AT_NT), 0, st, qb, kb, vb, seqlen,
+                           uni, part, s.Hq, s.Hkv, s.N, s.W, s.K, NS, s.nwin, tau, s.M, pm);
+      else
+        hipLaunchKernelGGL((k_dec_attn_union<PAGED, 4>), ugrid, dim3(AT_NT), 0, st, qb, kb, vb, seqlen,
+                           uni, part, s.Hq, s.Hkv, s.N, s.W, s.K, NS, s.nwin, tau, s.M, pm);
+    }
+  } else if (fast_bf16) {
     const bf16_t* qb = (const bf16_t*)q;
     const bf16_t* kb = (const bf16_t*)k;
     const bf16_t* vb = (const bf16_t*)v;
@@ -884,17 +1116,17 @@ void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const vo
 hipError_t hils_launch_decode(const HilsShape& s, const void* q, const void* qr, const void* k,
                               const void* v, const int32_t* seqlen, const void* ksum,
                               const float* bsum, void* out, int32_t* sel, float* scores,
-                              uint32_t* keys, uint2* cand, float* slog, float* part,
+                              uint32_t* keys, uint2* cand, int32_t* uni, float* slog, float* part,
                               float* lsep, const int32_t* page_table, int max_pages, int num_pages,
                               hipStream_t st) {
   const PageMap pm{page_table, max_pages, num_pages};
   const bool paged = page_table != nullptr;
   if (s.dtype == 0) {
-    if (paged) launch_decode_t<bf16_t, true>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, cand, slog, part, lsep, pm, st);
-    else launch_decode_t<bf16_t, false>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, cand, slog, part, lsep, pm, st);
+    if (paged) launch_decode_t<bf16_t, true>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, cand, uni, slog, part, lsep, pm, st);
+    else launch_decode_t<bf16_t, false>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, cand, uni, slog, part, lsep, pm, st);
   } else {
-    if (paged) launch_decode_t<float, true>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, cand, slog, part, lsep, pm, st);
-    else launch_decode_t<float, false>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, cand, slog, part, lsep, pm, st);
+    if (paged) launch_decode_t<float, true>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, cand, uni, slog, part, lsep, pm, st);
+    else launch_decode_t<float, false>(s, q, qr, k, v, seqlen, ksum, bsum, out, sel, scores, keys, cand, uni, slog, part, lsep, pm, st);
   }
   return hipGetLastError();
 }

@@ -111,7 +111,7 @@ PrefillLayout prefill_layout(const HilsShape& s, bool fast, bool pairs) {
 }
 
 struct DecodeLayout {
-  size_t scores, keys, cand, slog, sel, part, lsep, total;
+  size_t scores, keys, cand, uni, slog, sel, part, lsep, total;
 };
 DecodeLayout decode_layout(const HilsShape& s) {
   DecodeLayout L{};
@@ -123,6 +123,7 @@ DecodeLayout decode_layout(const HilsShape& s) {
   int P = 1, span = 1;
   hils_dec_select_split(s, P, span);
   L.cand = off;   off += align_up(P > 1 ? BM * s.Hkv * (size_t)P * s.K * 8 : 8);
+  L.uni = off;    off += align_up(hils_dec_union_bytes(s));
   L.slog = off;   off += align_up(BM * s.Hq * s.K * 4);
   L.sel = off;    off += align_up(BM * s.Hkv * s.K * 4);
   L.part = off;   off += align_up(BM * s.Hq * (s.K + s.nwin) * (s.d + 2) * 4);
@@ -397,7 +398,8 @@ hils_status hils_decode(const hils_cfg* cfg, const void* q, const void* q_route,
   if ((long long)s.B * s.Hq > HILS_DEC_MAX_ROWS_Y) return HILS_E_UNSUPPORTED;
   return hip_status(hils_launch_decode(s, q, qr, k_cache, v_cache, seqlen, k_sum, b_sum, out, sl,
                                        (float*)(w + L.scores), (uint32_t*)(w + L.keys),
-                                       (uint2*)(w + L.cand), (float*)(w + L.slog), (float*)(w + L.part),
+                                       (uint2*)(w + L.cand), (int32_t*)(w + L.uni),
+                                       (float*)(w + L.slog), (float*)(w + L.part),
                                        (float*)(w + L.lsep), nullptr, 0, 0, (hipStream_t)stream));
 }
 
@@ -455,7 +457,8 @@ hils_status hils_decode_multi(const hils_cfg* cfg, int32_t M, const void* q, con
   if ((long long)s.B * s.Hq > HILS_DEC_MAX_ROWS_Y) return HILS_E_UNSUPPORTED;
   return hip_status(hils_launch_decode(s, q, qr, k_cache, v_cache, seqlen, k_sum, b_sum, out, sl,
                                        (float*)(w + L.scores), (uint32_t*)(w + L.keys),
-                                       (uint2*)(w + L.cand), (float*)(w + L.slog), (float*)(w + L.part),
+                                       (uint2*)(w + L.cand), (int32_t*)(w + L.uni),
+                                       (float*)(w + L.slog), (float*)(w + L.part),
                                        (float*)(w + L.lsep), nullptr, 0, 0, (hipStream_t)stream));
 }
 
@@ -547,7 +550,8 @@ hils_status hils_decode_paged(const hils_cfg* cfg, const void* q, const void* q_
   if ((long long)s.B * s.Hq > HILS_DEC_MAX_ROWS_Y) return HILS_E_UNSUPPORTED;
   return hip_status(hils_launch_decode(s, q, qr, k_pages, v_pages, seqlen, k_sum_pages, b_sum_pages,
                                        out, sl, (float*)(w + L.scores), (uint32_t*)(w + L.keys),
-                                       (uint2*)(w + L.cand), (float*)(w + L.slog), (float*)(w + L.part),
+                                       (uint2*)(w + L.cand), (int32_t*)(w + L.uni),
+                                       (float*)(w + L.slog), (float*)(w + L.part),
                                        (float*)(w + L.lsep), page_table, max_pages, num_pages,
                                        (hipStream_t)stream));
 }

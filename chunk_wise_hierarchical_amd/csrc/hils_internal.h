@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "hils.h"
+
 struct HilsShape {
   int B, N, Hq, Hkv, G, d, S, W, K;
   int dtype;   // 0 bf16, 1 fp32
@@ -77,7 +79,8 @@ constexpr int HILS_FAST_NCMAX = 16384;   // chunk ids the fast attention bitmap 
 hipError_t hils_launch_decode(const HilsShape& s, const void* q, const void* qr, const void* k,
                               const void* v, const int32_t* seqlen, const void* ksum,
                               const float* bsum, void* out, int32_t* sel, float* scores,
-                              uint32_t* keys, uint2* cand, float* slog, float* part, float* lsep,
+                              uint32_t* keys, uint2* cand, int32_t* uni, float* slog, float* part,
+                              float* lsep,
                               const int32_t* page_table, int max_pages, int num_pages,
                               hipStream_t st);
 // Decode selection: one workgroup per (sequence, KV group, query) takes the
@@ -90,6 +93,23 @@ constexpr int HILS_DEC_SEL_SPAN = 4096;
 constexpr int HILS_DEC_MERGE_MAX = 8192;
 constexpr int HILS_DEC_SEL_ROWS_WHOLE = 128;
 constexpr int HILS_DEC_SEL_LDS_KEYS = 24576;
+// Multi-token blocks take the union attention when M K <= HILS_DEC_UNION_IDS
+// and the cache has at most HILS_DEC_UNION_CHUNKS chunks (an LDS bitmap over
+// chunk ids); other blocks attend token by token.
+constexpr int HILS_DEC_UNION_IDS = HILS_MAX_DECODE_QUERIES * 64;
+constexpr int HILS_DEC_UNION_CHUNKS = 65536;
+inline bool hils_dec_union(const HilsShape& s) {
+  return s.dtype == 0 && s.d == 128 && s.S == 64 && (s.G == 1 || s.G == 2 || s.G == 4) && s.M > 1 &&
+         s.M * s.K <= HILS_DEC_UNION_IDS && s.nC <= HILS_DEC_UNION_CHUNKS;
+}
+// per (sequence, KV group): the union's size and its ids ascending (M K + 1
+// ints), then per union element and token the token's slot of that chunk (M K
+// x M bytes, -1 where the token did not select it)
+inline size_t hils_dec_union_bytes(const HilsShape& s) {
+  if (!hils_dec_union(s)) return 8;
+  const size_t bg = (size_t)s.B * s.Hkv, mk = (size_t)s.M * s.K;
+  return bg * (mk + 1) * 4 + bg * mk * s.M;
+}
 inline void hils_dec_select_split(const HilsShape& s, int& P, int& span) {
   const long long nm = s.nmax > 0 ? s.nmax : 1;
   const long long rows = (long long)s.B * s.Hkv * s.M;

@@ -143,11 +143,19 @@ def test_multi_decode_arguments_and_workspace(L):
     assert call(4, seqlen=None) == _lib.HILS_E_ARG
     assert call(4, cfg=_cfg(N=1024, mode=2)) == _lib.HILS_E_UNSUPPORTED
     assert call(4, wsb=ctypes.c_size_t(16)) == _lib.HILS_E_WORKSPACE
-    # the per-row buffers of an M-token block are those of B*M single decodes
+    # the per-row buffers of an M-token block are those of B*M single decodes,
+    # plus (bf16, d=128, S=64) the block's chunk union per (sequence, KV group):
+    # its size and M*K ids, and a slot byte per (union element, token)
     one = L.hils_decode_multi_workspace_bytes(ctypes.byref(c), 1)
     assert one == L.hils_workspace_bytes(ctypes.byref(c), 1)
     four = L.hils_decode_multi_workspace_bytes(ctypes.byref(c), 4)
-    assert four == L.hils_workspace_bytes(ctypes.byref(_cfg(N=1024, B=4 * c.B)), 1)
+    bg, mk = c.B * c.Hkv, 4 * c.K
+    align = lambda x: (x + 255) // 256 * 256
+    union = align(bg * (mk + 1) * 4 + bg * mk * 4) - align(8)
+    assert four == L.hils_workspace_bytes(ctypes.byref(_cfg(N=1024, B=4 * c.B)), 1) + union
+    c32 = _cfg(N=1024, dtype=1)                    # fp32 blocks attend token by token
+    assert (L.hils_decode_multi_workspace_bytes(ctypes.byref(c32), 4)
+            == L.hils_workspace_bytes(ctypes.byref(_cfg(N=1024, B=4, dtype=1)), 1))
     assert L.hils_decode_multi_workspace_bytes(ctypes.byref(c), 0) == 0
     assert L.hils_decode_multi_workspace_bytes(ctypes.byref(c), 17) == 0
 
