@@ -434,10 +434,12 @@ k_win_fuse(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) pa[dt][e] = 0.0f;
-    // piece 4j + lq of a stored row (16 bytes at element 8 (4j + lq)) holds
-    // the elements 32j + 4lq + {0..3} (acc block 2j) and 32j + 16 + 4lq +
-    // {0..3} (block 2j + 1) of this lane
-    const bf16_t* pp = part + (qrow * K * G + h) * D + 8 * lq;
+    // piece 4j + lq of head h's row (16 bytes at element 32 (G j + h) + 8 lq
+    // of the pair's block) holds the elements 32j + 4lq + {0..3} (acc block
+    // 2j) and 32j + 16 + 4lq + {0..3} (block 2j + 1) of this lane; for G > 1
+    // one load instruction reads whole 128-byte lines (the 4 lq lanes of two
+    // heads), non-temporal
+    const bf16_t* pp = part + qrow * K * G * D + 32 * h + 8 * lq;
     constexpr int RU = 8;                 // slots whose pieces are in flight together
     for (int kx = 0; kx < kk; kx += RU) {
       uint4 u[RU][4];
@@ -445,7 +447,10 @@ k_win_fuse(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       for (int t = 0; t < RU; ++t)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)   // a slot past kk reads slot kk - 1 again, unused
-          u[t][jj] = ld_u4(pp + (long long)min(kx + t, kk - 1) * G * D + 32 * jj);
+          {  // G = 1 reads half lines per instruction: cached, so the line's other half hits
+            const bf16_t* src = pp + (long long)min(kx + t, kk - 1) * G * D + 32 * G * jj;
+            u[t][jj] = (G == 1) ? ld_u4(src) : ld_u4_nt(src);
+          }
 #pragma unroll
       for (int t = 0; t < RU; ++t) {
         if (kx + t < kk) {
@@ -731,19 +736,32 @@ k_pair_attn(const bf16_t* __restrict__ q, const bf16_t* __restrict__ qr,
       }
       if (valid && lq == 0) __builtin_nontemporal_store(lam, lamb + prow * G + h);
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      const int rp = lane >> 3, sl = lane & 7;
+      // Stored layout of a pair's G rows (G D elements): piece 4j + lq of
+      // head h at element 32 (G j + h) + 8 lq, so that the pieces 4j .. 4j + 3
+      // of two neighbouring heads fill one 128-byte line (G = 1: the row in
+      // order).  Line ln of this wavefront's 16 rows: 8 lanes, 16 bytes each.
+      const int sl = lane & 7;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int rr = 2 * rp + i;                          // row of these two stores
-        const uint32_t er = (uint32_t)__shfl((int)e0, rr);  // its list entry
-        const int cr = 16 * w + rr, jrr = cr / G, hr = cr % G;
-        const long long pr = ((long long)bg * qs + (int)(er >> 7)) * K + (int)(er & 127u);
-        const uint4 u0 = ow[rr * OSTR + sl], u1 = ow[rr * OSTR + 8 + sl];
-        if (jrr < mcount) {
-          bf16_t* dst = part + (pr * G + hr) * D + 8 * sl;
-          st_u4_nt(dst, u0);
-          st_u4_nt(dst + 64, u1);
+      for (int i = 0; i < 4; ++i) {
+        const int ln = 8 * i + (lane >> 3);
+        int rr, pc, eo;                                     // patch row, piece, element offset
+        if constexpr (G == 1) {
+          rr = ln >> 1;
+          pc = 8 * (ln & 1) + sl;
+          eo = 64 * (ln & 1) + 8 * sl;
+        } else {
+          const int pw = ln / (2 * G), rem = ln % (2 * G);
+          const int jj = rem / (G / 2), hp = rem % (G / 2);
+          rr = pw * G + 2 * hp + (sl >> 2);
+          pc = 4 * jj + (sl & 3);
+          eo = 32 * (G * jj + 2 * hp) + 8 * sl;
         }
+        const int rp0 = rr - rr % G;                        // first row of the pair
+        const uint32_t er = (uint32_t)__shfl((int)e0, rp0); // its list entry
+        const int jrr = (16 * w + rp0) / G;
+        const long long pr = ((long long)bg * qs + (int)(er >> 7)) * K + (int)(er & 127u);
+        const uint4 u = ow[rr * OSTR + pc];
+        if (jrr < mcount) st_u4_nt(part + pr * G * D + eo, u);
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // patch reads before the next tile's writes
     }
