@@ -72,13 +72,17 @@ def window_work(w):
 
 def decode_work(w, T):
     """Algorithmic HBM bytes of one decode step (all sequences at length T), and the
-    bytes of the summary-scoring kernel alone (k', b' read, scores written)."""
+    bytes of the scoring launch (k', b' read, scores written; for bf16 d=128 S=64
+    single-token steps it also carries the window tiles' K and V)."""
     n, win = _geometry(T, w.W, w.S)
     n, win = int(n[-1]), int(win[-1])
     e = 2 if w.dtype == "bf16" else 4
+    win_bytes = w.Hkv * win * w.d * e * 2
     per_seq = (w.Hq * n * (w.d * e + 4) + w.Hkv * min(w.K, n) * w.S * w.d * e * 2
-               + w.Hkv * win * w.d * e * 2 + 2 * w.Hq * w.d * e)
+               + win_bytes + 2 * w.Hq * w.d * e)
     score_bytes = w.B * w.Hq * n * (w.d * e + 4 + 4)
+    if w.dtype == "bf16" and w.d == 128 and w.S == 64 and w.G in (1, 2, 4):
+        score_bytes += w.B * win_bytes
     return per_seq * w.B, score_bytes
 
 
