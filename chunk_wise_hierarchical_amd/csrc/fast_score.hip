@@ -323,6 +323,15 @@ k_score_fast(const bf16_t* __restrict__ qr, const uint4* __restrict__ frag,
   // pass 0's trackers live
   auto run_pass = [&](auto pass_tag) {
     constexpr int pass = decltype(pass_tag)::value;
+    // One head (G = 1) needs no log-sum-exp, and with at most four tiles of
+    // candidates staging every chunk costs at most two merges, less than the
+    // bound: pass 0 is skipped and the staging bound is -inf.
+    if (pass == 0 && G == 1 && ntiles <= 4) {
+      for (int t = tid; t < QB * K; t += NT) lst[t] = 0ull;
+      for (int t = tid; t < QB; t += NT) thf[t] = -INFINITY;
+      __syncthreads();
+      return;
+    }
     float m = -INFINITY, ssum = 0.0f;
     float t0[16], t1[16], t2[16];  // top 3 per register slot, descending (pass 0)
 #pragma unroll
