@@ -25,7 +25,7 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def _inputs(w, M, seqlen, q_route=False, seed=11):
+def _inputs(w, M, seqlen, q_route=False, seed=11, corr=0.0):
     gen_dev = "cpu" if w.B * w.Hkv * w.N * w.d <= (1 << 26) else "cuda"
     x = synth.make_decode_inputs(w, device=gen_dev, seqlen=seqlen, with_q_route=q_route)
     x = {k: v.cuda() for k, v in x.items()}
@@ -33,7 +33,10 @@ def _inputs(w, M, seqlen, q_route=False, seed=11):
     # structure) for the last token, seeded normals of the same scale before it
     g = torch.Generator(device="cpu").manual_seed(seed)
     f = (1.0 / w.d ** 0.5) if w.scaled else 1.0
-    qm = (torch.randn((w.B, w.Hq, M, w.d), generator=g) * f).to(x["q"].dtype).cuda()
+    qm = (torch.randn((w.B, w.Hq, M, w.d), generator=g) * f).cuda()
+    if corr > 0.0:                 # the block's queries share most of their direction
+        qm = qm * (1.0 - corr) ** 0.5 + x["q"][:, :, 0:1].float() * corr ** 0.5
+    qm = qm.to(x["q"].dtype)
     qm[:, :, M - 1] = x["q"][:, :, 0]
     x["qm"] = qm.contiguous()
     if q_route:
@@ -42,10 +45,10 @@ def _inputs(w, M, seqlen, q_route=False, seed=11):
     return x
 
 
-def _multi_case(w, M, seqlen, label="", q_route=False, mode="surrogate", seqs=None):
+def _multi_case(w, M, seqlen, label="", q_route=False, mode="surrogate", seqs=None, corr=0.0):
     _say(f"[decode_multi] {label} {w.name} B={w.B} T={w.N} Hq={w.Hq} Hkv={w.Hkv} d={w.d} "
          f"S={w.S} W={w.W} K={w.K} M={M} seqlen={seqlen[:4]} dtype={w.dtype} mode={mode}")
-    x = _inputs(w, M, seqlen, q_route)
+    x = _inputs(w, M, seqlen, q_route, corr=corr)
     ks, bs = hils.summarize(x["k"], x["lm"], w.S, mode=mode)
     sel = torch.empty((w.B, w.Hkv, M, w.K), dtype=torch.int32, device="cuda")
     out = hils.decode_multi(x["qm"], x["k"], x["v"], x["seqlen"], ks, bs, w.S, w.W, w.K,
@@ -124,6 +127,18 @@ def test_multi_decode_max_block_short_sequence_and_mean_pool():
     # a sequence shorter than the block: positions below 0 are evaluated at 0
     _multi_case(w, 4, [2048, 2], label="seqlen < M")
     _multi_case(w, 3, [2048, 999], label="mean_pool", mode="mean_pool")
+
+
+def test_multi_decode_union_at_its_limits():
+    # bf16, d=128, S=64 blocks take the union attention (one load per distinct
+    # chunk or window tile of the block): M*K at its limit of 1024 ids, G = 2,
+    # a sequence shorter than the block (positions clamp at 0) and one whose
+    # tokens straddle a chunk boundary; then G = 1 with correlated queries, so
+    # that many chunks are shared by several tokens
+    w = synth.get_workload("decode_512k", N=8192, B=3, Hq=8, Hkv=4, K=64, W=512)
+    _multi_case(w, 16, [8192, 5000 + 70, 9], label="M=16 K=64 G=2")
+    w = synth.get_workload("decode_512k", N=8192, B=2, Hq=4, Hkv=4, K=32, W=1024)
+    _multi_case(w, 8, [8192, 6400 + 3], label="M=8 G=1", corr=0.9)
 
 
 def test_multi_decode_one_token_is_decode():
