@@ -671,6 +671,14 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
     dvj[u] = 0.0f;
   }
   for (int t = tid; t < G * d + G; t += CT) dks[t] = 0.0;
+  // dk' and db' of the chunk's summaries: thread t takes element ea = t % 128
+  // of the selecting contributions u with u % 4 == t / 128 (every wavefront a
+  // quarter of them), in registers; the four quarters meet in dks / dbs after
+  // the contributions
+  const int ea = tid & 127, eq4 = tid >> 7;
+  double dka[8], dba[8];
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) { dka[rr] = 0.0; dba[rr] = 0.0; }
 
   const bool summ = c < nC;
   const uint32_t p0 = summ ? off[bg * (nC + 1) + c] : 0u;
@@ -767,14 +775,17 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
         dkj[x] = fmaf(tau * ds, qv[x], dkj[x]);
         dvj[x] = fmaf(ap, dv2[x], dvj[x]);
       }
-      // dk' += tau d s_hat q_hat, db' += d s_hat: threads of token r own head r
-      if (!window && jt == r) {
-        float hv[CE];
-        load_slice16<T>(stg + (((size_t)buf * 3 + 2) * NB + ul) * d + e0, DQ, hv);
+      // dk' += tau d s_hat q_hat, db' += d s_hat (see dka above)
+      if (!window && (u & 3) == eq4 && ea < d) {
+        const double hv = (double)Elt<T>::ld(stg + (((size_t)buf * 3 + 2) * NB + ul) * d + ea);
+        const double txt = (double)tau * (double)xt;
 #pragma unroll
-        for (int x = 0; x < CE; ++x)
-          if (x < DQ) dks[r * d + e0 + x] = fma((double)tau * xt, (double)hv[x], dks[r * d + e0 + x]);
-        if (qd == 0) dbs[r] += (double)xt;
+        for (int rr = 0; rr < 8; ++rr) {
+          if (rr == r) {
+            dka[rr] = fma(txt, hv, dka[rr]);
+            dba[rr] += (double)xt;
+          }
+        }
       }
     };
     const int nsb = (nb + NB - 1) / NB;
@@ -792,6 +803,18 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
     }
   }
   __syncthreads();
+  for (int p4 = 0; p4 < 4; ++p4) {                   // the quarters of dk', db', in order
+    if (eq4 == p4 && ea < d) {
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        if (rr < G) {
+          dks[rr * d + ea] += dka[rr];
+          if (ea == 0) dbs[rr] += dba[rr];
+        }
+      }
+    }
+    __syncthreads();
+  }
   // summaries of the chunk (one per query head of the group)
   if (summ) {
     for (int r = 0; r < G; ++r) {
