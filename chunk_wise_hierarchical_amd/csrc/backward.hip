@@ -461,12 +461,39 @@ k_bwd_rows2(const T* __restrict__ q, const T* __restrict__ qr, const T* __restri
     const T* kp = ksum + ((hb + r) * nC + c) * (long long)d;
     st[(s2 * G + r) * 4 + 0] = fmaf(tau, dot_row<T>(qh + r * d, kp, d), bsum[(hb + r) * nC + c]);
   }
-  for (int t = tid; t < nk * G; t += BT) {
-    const int f = t / G, r = t - f * G;
-    const long long pos = key_pos(f);
-    const int col = key_col(f);
-    lw[r * RL + col] = tau * dot_row<T>(qs + r * d, kb + pos * d, d);
-    du[r * RL + col] = dot_row<T>(go + r * d, vb + pos * d, d);
+  // four lanes per (key, head): each load instruction reads 64 contiguous bytes
+  // of a key row (the quad's four 16-byte pieces), the quad's partial dots
+  // meet by DPP
+  {
+    const int l4 = tid & 3;
+    for (int t = tid >> 2; t < nk * G; t += BT / 4) {
+      const int f = t / G, r = t - f * G;
+      const long long pos = key_pos(f);
+      const T* kr = kb + pos * d;
+      const T* vr = vb + pos * d;
+      const float* qq = qs + r * d;
+      const float* gg = go + r * d;
+      float a = 0.0f, u2 = 0.0f;
+      for (int e = VN * l4; e < d; e += 4 * VN) {
+        float kv[VN], vv[VN];
+        V16<T>::ld(kr + e, kv);
+        V16<T>::ld(vr + e, vv);
+#pragma unroll
+        for (int u = 0; u < VN; ++u) {
+          a = fmaf(qq[e + u], kv[u], a);
+          u2 = fmaf(gg[e + u], vv[u], u2);
+        }
+      }
+      a += fastp::xshfl_f(a, 1);
+      u2 += fastp::xshfl_f(u2, 1);
+      a += fastp::xshfl_f(a, 2);
+      u2 += fastp::xshfl_f(u2, 2);
+      if (l4 == 0) {
+        const int col = key_col(f);
+        lw[r * RL + col] = tau * a;
+        du[r * RL + col] = u2;
+      }
+    }
   }
   __syncthreads();
   // 2. softmax statistics: items 0 .. G-1 are the window heads, then (slot, head)
