@@ -658,9 +658,15 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
            int S, int W, int K, int nC, int nCc, float tau, int mode) {
   extern __shared__ __align__(16) float smc[];
   const int tid = threadIdx.x;
-  const long long blk = blockIdx.x;                  // (b, g, c)
-  const int c = (int)(blk % nCc);
-  const long long bg = blk / nCc;
+  // chunk-major order (c, b, g): a chunk's work (its selections) depends on
+  // its position and on the routing, and neighbouring chunks of one sequence
+  // tend to be alike; consecutive workgroups take one chunk of every sequence
+  // and KV group, so heavy chunks spread over the chip instead of arriving
+  // together on a few CUs.
+  const long long blk = blockIdx.x;
+  const long long nbg = gridDim.x / nCc;             // B * Hkv
+  const int c = (int)(blk / nbg);
+  const long long bg = blk % nbg;
   const int g = (int)(bg % Hkv);
   const long long b = bg / Hkv;
   const long long hb = b * Hq + (long long)g * G;
@@ -684,6 +690,8 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
   float* red = reinterpret_cast<float*>(redd + 8);   // [8]
   int* di = reinterpret_cast<int*>(red + 8);         // [CBATCH] query << 4 | head, window flag << 31
   float* dsx = reinterpret_cast<float*>(di + CBATCH);   // [CBATCH][4] alpha, lse, g, window term
+  int* dwl = reinterpret_cast<int*>(dsx + 4 * CBATCH);  // [CBATCH] window contributions: first
+                                                         // token of the window, minus j0
   const T* kb = k + (bg * (long long)N + j0) * d;
   const T* vb = v + (bg * (long long)N + j0) * d;
 
@@ -734,6 +742,7 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
         const int i = j0 + (int)(widx / G), r = (int)(widx % G);
         const float* ws = wstat + ((hb + r) * N + i) * 4;
         di[t] = (int)(0x80000000u | ((uint32_t)i << 4) | (uint32_t)r);
+        dwl[t] = (int)(window_start(i, W, S) - j0);
         dsx[t * 4 + 0] = ws[0];
         dsx[t * 4 + 1] = ws[1];
         dsx[t * 4 + 2] = ws[2];
@@ -793,7 +802,7 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
       const float alpha = dsx[u * 4], lse = dsx[u * 4 + 1], gq = dsx[u * 4 + 2], xt = dsx[u * 4 + 3];
       const int j = j0 + jt;
       bool ok = act;
-      if (window) ok = ok && j <= i && j >= (int)window_start(i, W, S);
+      if (window) ok = ok && j <= i && jt >= dwl[u];
       const float pp = ok ? __expf(tau * a - lse) : 0.0f;
       const float ds = alpha * pp * (u2 - gq) + (window ? xt * pp : 0.0f);
       const float ap = alpha * pp;
@@ -948,7 +957,7 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
   const size_t rshm = all_keys ? bwd_rows2_lds(s) : hils_bwd_rows_lds(s);
   const size_t cshm = (s.dtype == 0 ? col_stage_bytes<bf16_t>(s.d, s.S) : col_stage_bytes<float>(s.d, s.S)) +
                       sizeof(double) * ((size_t)s.G * s.d + s.G + 8) + sizeof(float) * 8 +
-                      (size_t)CBATCH * (sizeof(int) + 4 * sizeof(float));
+                      (size_t)CBATCH * (2 * sizeof(int) + 4 * sizeof(float));
   const int sep = dqr != nullptr;
   if (s.dtype == 0) {
     auto fr = all_keys ? k_bwd_rows2<bf16_t> : k_bwd_rows<bf16_t>;
