@@ -648,7 +648,7 @@ __host__ __device__ inline size_t col_stage_bytes(int d, int S) {
   return ((st > sc ? st : sc) + 15) & ~(size_t)15;
 }
 
-template <typename T>
+template <typename T, bool SUMONLY>
 __global__ void __launch_bounds__(CT)
 k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restrict__ k,
            const T* __restrict__ v, const T* __restrict__ lm, const T* __restrict__ dout,
@@ -720,7 +720,9 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
   const uint32_t p1 = summ ? off[bg * (nC + 1) + c + 1] : 0u;
   const long long nsel = (long long)(p1 - p0) * G;                 // (pair, head) contributions
   const int i1 = min(N, (c + 1) * S + W - 1);
-  const long long nwin = (long long)(i1 - j0) * G;                // window (query, head)
+  // summaries only (dk, dv of the contributions come from the matrix-core
+  // column pass): the selecting contributions' d s_hat and q_hat alone
+  const long long nwin = SUMONLY ? 0 : (long long)(i1 - j0) * G;  // window (query, head)
   const uint32_t* eg = ent + bg * (long long)N * K;
 
   for (long long base = 0; base < nsel + nwin; base += CBATCH) {
@@ -765,8 +767,10 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
         const int dd = di[u];
         const int i = (dd >> 4) & 0x7ffffff, r = dd & 15;
         const long long o = ((hb + r) * N + i) * (long long)d + spart * VE;
-        pv0 = *reinterpret_cast<const uint4*>(q + o);
-        pv1 = *reinterpret_cast<const uint4*>(dout + o);
+        if (!SUMONLY) {
+          pv0 = *reinterpret_cast<const uint4*>(q + o);
+          pv1 = *reinterpret_cast<const uint4*>(dout + o);
+        }
         pv2 = *reinterpret_cast<const uint4*>(qr + o);
       }
     };
@@ -780,6 +784,21 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
     };
     auto apply = [&](int u, int buf) __attribute__((always_inline)) {
       const int ul = u % NB;
+      if (SUMONLY) {
+        if ((u & 3) == eq4 && ea < d) {
+          const int r = di[u] & 15;
+          const double hv = (double)Elt<T>::ld(stg + (((size_t)buf * 3 + 2) * NB + ul) * d + ea);
+          const double xt = (double)dsx[u * 4 + 3];
+#pragma unroll
+          for (int rr = 0; rr < 8; ++rr) {
+            if (rr == r) {
+              dka[rr] = fma((double)tau * xt, hv, dka[rr]);
+              dba[rr] += xt;
+            }
+          }
+        }
+        return;
+      }
       float qv[CE], dv2[CE];
       load_slice16<T>(stg + (((size_t)buf * 3 + 0) * NB + ul) * d + e0, DQ, qv);
       load_slice16<T>(stg + (((size_t)buf * 3 + 1) * NB + ul) * d + e0, DQ, dv2);
@@ -919,6 +938,15 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
       __syncthreads();
     }
   }
+  if (SUMONLY) {                             // add the summaries' share to dk
+    if (act && mode != 1) {
+      float* dko = dk + (bg * (long long)N + j0 + jt) * d + e0;
+#pragma unroll
+      for (int x = 0; x < CE; ++x)
+        if (x < DQ) dko[x] += dkj[x];
+    }
+    return;
+  }
   if (act) {
     float* dko = dk + (bg * (long long)N + j0 + jt) * d + e0;
     float* dvo = dv + (bg * (long long)N + j0 + jt) * d + e0;
@@ -962,14 +990,27 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
   if (s.dtype == 0) {
     auto fr = all_keys ? k_bwd_rows2<bf16_t> : k_bwd_rows<bf16_t>;
     hils_allow_lds((const void*)fr, rshm);
-    hils_allow_lds((const void*)k_bwd_cols<bf16_t>, cshm);
     { HilsProfScope ps_("k_bwd_rows", st);
       hipLaunchKernelGGL(fr, dim3((unsigned)((long long)s.B * s.Hkv * s.N)), dim3(BT), rshm, st,
                          (const bf16_t*)q, (const bf16_t*)qr, (const bf16_t*)k, (const bf16_t*)v,
                          (const bf16_t*)ksum, bsum, (const bf16_t*)dout, sel, dq, dqr, wb.pstat,
                          wb.wstat, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, tau, sep); }
+    if (hils_bwd_cols_mf_ok(s)) {
+      // dk, dv on the matrix cores, then the summaries' share of dk and dlm
+      hipError_t e = hils_launch_bwd_cols_mf(s, q, k, v, dout, wb, dk, dv, st);
+      if (e != hipSuccess || s.nC <= 0) return e;
+      hils_allow_lds((const void*)k_bwd_cols<bf16_t, true>, cshm);
+      HilsProfScope ps_("k_bwd_summ", st);
+      hipLaunchKernelGGL((k_bwd_cols<bf16_t, true>), dim3((unsigned)((long long)s.B * s.Hkv * s.nC)), dim3(CT),
+                         cshm, st, (const bf16_t*)q, (const bf16_t*)qr, (const bf16_t*)k,
+                         (const bf16_t*)v, (const bf16_t*)lm, (const bf16_t*)dout, wb.off, wb.ent,
+                         wb.pstat, wb.wstat, dk, dv, dlm, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K,
+                         s.nC, s.nC, tau, s.mode);
+      return hipGetLastError();
+    }
+    hils_allow_lds((const void*)k_bwd_cols<bf16_t, false>, cshm);
     { HilsProfScope ps_("k_bwd_cols", st);
-      hipLaunchKernelGGL(k_bwd_cols<bf16_t>, dim3((unsigned)((long long)s.B * s.Hkv * s.nCc)), dim3(CT), cshm, st,
+      hipLaunchKernelGGL((k_bwd_cols<bf16_t, false>), dim3((unsigned)((long long)s.B * s.Hkv * s.nCc)), dim3(CT), cshm, st,
                          (const bf16_t*)q, (const bf16_t*)qr, (const bf16_t*)k, (const bf16_t*)v,
                          (const bf16_t*)lm, (const bf16_t*)dout, wb.off, wb.ent, wb.pstat, wb.wstat,
                          dk, dv, dlm, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, s.nCc, tau,
@@ -977,14 +1018,14 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
   } else {
     auto fr = all_keys ? k_bwd_rows2<float> : k_bwd_rows<float>;
     hils_allow_lds((const void*)fr, rshm);
-    hils_allow_lds((const void*)k_bwd_cols<float>, cshm);
+    hils_allow_lds((const void*)k_bwd_cols<float, false>, cshm);
     { HilsProfScope ps_("k_bwd_rows", st);
       hipLaunchKernelGGL(fr, dim3((unsigned)((long long)s.B * s.Hkv * s.N)), dim3(BT), rshm, st,
                          (const float*)q, (const float*)qr, (const float*)k, (const float*)v,
                          (const float*)ksum, bsum, (const float*)dout, sel, dq, dqr, wb.pstat,
                          wb.wstat, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, tau, sep); }
     { HilsProfScope ps_("k_bwd_cols", st);
-      hipLaunchKernelGGL(k_bwd_cols<float>, dim3((unsigned)((long long)s.B * s.Hkv * s.nCc)), dim3(CT), cshm, st,
+      hipLaunchKernelGGL((k_bwd_cols<float, false>), dim3((unsigned)((long long)s.B * s.Hkv * s.nCc)), dim3(CT), cshm, st,
                          (const float*)q, (const float*)qr, (const float*)k, (const float*)v,
                          (const float*)lm, (const float*)dout, wb.off, wb.ent, wb.pstat, wb.wstat,
                          dk, dv, dlm, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, s.nCc, tau,

@@ -20,3 +20,11 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
                                 const void* ksum, const float* bsum, float* dq, float* dqr,
                                 float* dk, float* dv, float* dlm, const HilsBwdBufs& wb,
                                 hipStream_t st);
+
+// Column pass on the matrix cores (backward_mf.hip): dk, dv of every chunk's
+// tokens for bf16 inputs with d in {64, 128} and S a multiple of 16 (<= 64);
+// the summaries' share of dk and dlm is added afterwards by the summary pass.
+bool hils_bwd_cols_mf_ok(const HilsShape& s);
+hipError_t hils_launch_bwd_cols_mf(const HilsShape& s, const void* q, const void* k, const void* v,
+                                   const void* dout, const HilsBwdBufs& wb, float* dk, float* dv,
+                                   hipStream_t st);

@@ -83,6 +83,21 @@ def test_backward_summary_modes():
     _case(w, mode="mean_pool", label="mean_pool")
 
 
+def test_backward_matrix_core_columns_all_modes():
+    # bf16 with d = 128 and S = 64 (and d = 64, S = 32): dk and dv come from the
+    # matrix-core column pass, the summaries' share of dk and dlm from the
+    # summary pass; routing query, landmark key and mean pool; a sequence
+    # shorter than one chunk (window only, no summaries)
+    w = synth.get_workload("prefill_64k", N=700, Hq=4, Hkv=2, W=100, K=4, regime="iid")
+    _case(w, q_route=True, label="mf q_route")
+    _case(w, mode="landmark_key", label="mf landmark_key")
+    _case(w, mode="mean_pool", label="mf mean_pool")
+    w = synth.get_workload("prefill_64k", N=333, Hq=8, Hkv=1, d=64, S=32, W=40, K=6, regime="depth10")
+    _case(w, label="mf d64 S32 G8")
+    w = synth.get_workload("prefill_64k", N=50, Hq=2, Hkv=1, W=30, K=2)
+    _case(w, label="mf N < S")
+
+
 def test_backward_deterministic():
     w = synth.get_workload("prefill_64k", N=700, Hq=4, Hkv=1, d=64, S=32, W=64, K=4, regime="iid")
     gr, (x, dout, sel) = _case(w, label="determinism")
