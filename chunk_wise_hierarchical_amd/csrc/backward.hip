@@ -235,6 +235,7 @@ k_bwd_rows(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
   float* sw = st + K * G * 4;                        // [G][4]
   float* red = sw + G * 4;                           // [4]
   __shared__ int ssel[128];
+  __shared__ int sorg[128];                          // slot of each valid selection
   __shared__ int skk;
 
   for (int t = tid; t < G * d; t += BT) {
@@ -249,7 +250,10 @@ k_bwd_rows(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
     int kk = 0;
     for (int t = 0; t < K; ++t) {
       const int c = sel[row * K + t];
-      if (c >= 0 && c < nC) ssel[kk++] = c;
+      if (c >= 0 && c < nC) {
+        sorg[kk] = t;
+        ssel[kk++] = c;
+      }
     }
     skk = kk;
   }
@@ -376,10 +380,11 @@ k_bwd_rows(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
       dq[o] = dqv + dh;
     }
   }
-  // statistics for the column pass
-  for (int t = tid; t < K * G * 4; t += BT) {
+  // statistics for the column pass, per selection slot (the column pass finds
+  // a pair's statistics by its slot)
+  for (int t = tid; t < kk * G * 4; t += BT) {
     const int s2 = t / (G * 4);
-    pstat[row * K * G * 4 + t] = (s2 < kk) ? st[t] : 0.0f;
+    pstat[(row * K + sorg[s2]) * G * 4 + (t - s2 * G * 4)] = st[t];
   }
   for (int t = tid; t < G * 4; t += BT) {
     const int r = t / 4, f = t - r * 4;
@@ -427,6 +432,7 @@ k_bwd_rows2(const T* __restrict__ q, const T* __restrict__ qr, const T* __restri
   float* sw = st + K * G * 4;                        // [G][4] alpha_w, lse_w, g_w, d log Z
   float* dqp = sw + G * 4;                           // [BT * VN] dq partials by key subset
   __shared__ int ssel[128];
+  __shared__ int sorg[128];                          // slot of each valid selection
   __shared__ int skk;
 
   for (int t = tid; t < G * d; t += BT) {
@@ -440,7 +446,10 @@ k_bwd_rows2(const T* __restrict__ q, const T* __restrict__ qr, const T* __restri
     int kk = 0;
     for (int t = 0; t < K; ++t) {
       const int c = sel[row * K + t];
-      if (c >= 0 && c < nC) ssel[kk++] = c;
+      if (c >= 0 && c < nC) {
+        sorg[kk] = t;
+        ssel[kk++] = c;
+      }
     }
     skk = kk;
   }
@@ -603,10 +612,12 @@ k_bwd_rows2(const T* __restrict__ q, const T* __restrict__ qr, const T* __restri
       dq[o] = dqv + dh;
     }
   }
-  // statistics for the column pass (window probabilities are recomputed there)
-  for (int t = tid; t < K * G * 4; t += BT) {
+  // statistics for the column pass (window probabilities are recomputed
+  // there), per selection slot (the column pass finds a pair's statistics by
+  // its slot)
+  for (int t = tid; t < kk * G * 4; t += BT) {
     const int s2 = t / (G * 4);
-    pstat[row * K * G * 4 + t] = (s2 < kk) ? st[t] : 0.0f;
+    pstat[(row * K + sorg[s2]) * G * 4 + (t - s2 * G * 4)] = st[t];
   }
   for (int t = tid; t < G * 4; t += BT) {
     const int r = t / 4, f = t - r * 4;
@@ -990,14 +1001,10 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
   if (s.dtype == 0) {
     auto fr = all_keys ? k_bwd_rows2<bf16_t> : k_bwd_rows<bf16_t>;
     hils_allow_lds((const void*)fr, rshm);
-    { HilsProfScope ps_("k_bwd_rows", st);
-      hipLaunchKernelGGL(fr, dim3((unsigned)((long long)s.B * s.Hkv * s.N)), dim3(BT), rshm, st,
-                         (const bf16_t*)q, (const bf16_t*)qr, (const bf16_t*)k, (const bf16_t*)v,
-                         (const bf16_t*)ksum, bsum, (const bf16_t*)dout, sel, dq, dqr, wb.pstat,
-                         wb.wstat, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, tau, sep); }
-    if (hils_bwd_cols_mf_ok(s)) {
-      // dk, dv on the matrix cores, then the summaries' share of dk and dlm
-      hipError_t e = hils_launch_bwd_cols_mf(s, q, k, v, dout, wb, dk, dv, st);
+    if (hils_bwd_mf_ok(s)) {
+      // matrix-core passes, then the summaries' share of dk and dlm
+      hipError_t e = hils_launch_backward_mf(s, q, qr, k, v, dout, sel, ksum, bsum, dq, dqr, dk, dv,
+                                             wb, st);
       if (e != hipSuccess || s.nC <= 0) return e;
       hils_allow_lds((const void*)k_bwd_cols<bf16_t, true>, cshm);
       HilsProfScope ps_("k_bwd_summ", st);
@@ -1008,6 +1015,11 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
                          s.nC, s.nC, tau, s.mode);
       return hipGetLastError();
     }
+    { HilsProfScope ps_("k_bwd_rows", st);
+      hipLaunchKernelGGL(fr, dim3((unsigned)((long long)s.B * s.Hkv * s.N)), dim3(BT), rshm, st,
+                         (const bf16_t*)q, (const bf16_t*)qr, (const bf16_t*)k, (const bf16_t*)v,
+                         (const bf16_t*)ksum, bsum, (const bf16_t*)dout, sel, dq, dqr, wb.pstat,
+                         wb.wstat, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, tau, sep); }
     hils_allow_lds((const void*)k_bwd_cols<bf16_t, false>, cshm);
     { HilsProfScope ps_("k_bwd_cols", st);
       hipLaunchKernelGGL((k_bwd_cols<bf16_t, false>), dim3((unsigned)((long long)s.B * s.Hkv * s.nCc)), dim3(CT), cshm, st,

@@ -1,34 +1,50 @@
-// Prefill backward, column pass on the matrix cores: dk and dv of one chunk's
-// tokens over every (query, head) that attends them, for bf16 inputs with
-// d in {64, 128} and S a multiple of 16.
+// Prefill backward on the matrix cores, for bf16 inputs with d in {64, 128}
+// and S a multiple of 16: everything that touches the attended keys runs per
+// chunk over the chunk's contributions, as MFMA tiles.
 //
 // "Hierarchical Sparse Attention Done Right", section 3 (chunk attention, the
-// sliding window and the fusion softmax).  With the row pass's statistics of
-// a contribution (query i, head h) to chunk c - the fusion weight alpha, the
+// sliding window, the routing equation and the fusion softmax).  A
+// contribution is a (query i, head h) that attends keys of chunk c: a
+// (query, slot) pair whose selection holds c, or a query whose window
+// [window_start(i), i] meets c.  For a contribution with fusion weight alpha,
 // log-normaliser lse of the softmax the chunk's keys take part in, g = dout.o
-// of that softmax's output and, for the window, d log Z_swa = E - every key j
-// of the chunk it attends gets
-//   p_j = exp(tau q.k_j - lse),  dv_j += alpha p_j dout,
-//   ds_j = alpha p_j (dout.v_j - g) + E p_j,  dk_j += tau ds_j q.
-// The contributions are the (query, slot) pairs that selected the chunk (E = 0)
-// and the queries whose window holds any of its keys (each key j counts only
-// where window_start(i) <= j <= i).
+// of that softmax's output and, for the window, E = d log Z_swa (0 for a
+// selected chunk), every key j it attends gets
+//   p_j = exp(tau q.k_j - lse),  ds_j = alpha p_j (dout.v_j - g) + E p_j,
+//   dv_j += alpha p_j dout,  dk_j += tau ds_j q,  dq += tau ds_j k_j.
 //
-// One workgroup per (chunk, sequence, KV group), 4 wavefronts; wavefront w owns
-// keys 16w .. 16w + 15 and keeps their K and V rows as MFMA operands in
-// registers.  Contributions go in tiles of 32: their q and dout rows are
-// gathered into LDS both row-major (operand of S = Q K^T and dP = dOut V^T,
-// reduced over d) and transposed (operand of dV^T = dOut^T P and
-// dK^T = Q^T dS, reduced over the tile's queries), double-buffered, the next
-// tile's rows loaded while the current one is computed.  S and dP take bf16
-// MFMA with exact products and fp32 sums; P and tau dS are fp32 and enter
-// their products as a bf16 pair hi + lo (hi = bf16(x), lo = bf16(x - hi),
-// within 2^-18 of x), two MFMAs each, so the gradients keep fp32 accuracy.
-// The MFMA output layout of S (lane l: key l % 16, queries 4 (l / 16) + r of
-// each 16-query half) is the B-operand layout of the second products once the
-// tile's query positions are permuted (position 8 g + t <-> query
-// 16 (t / 4) + 4 g + t % 4); the transposed LDS tiles store queries at those
-// positions.  No atomics: every dk, dv row is written by one workgroup.
+// Four passes (plus the selection lists before and the summaries after):
+//   k_bwd_mf<D, 0> (stats)  per chunk: lse and g of every selecting pair;
+//                           for the window, per (query, chunk) the partial
+//                           max / sum exp / sum exp dout.v over the chunk's
+//                           keys in the window;
+//   k_bwd_rowstat           per (query, head): the window's lse and g from
+//                           its partials, the routing scores s_hat, the
+//                           fusion weights and their gradients (d s_hat,
+//                           d log Z_swa), and the routing query's gradient
+//                           tau sum_t (d s_hat_t) k'_t;
+//   k_bwd_mf<D, 1> (grads)  per chunk: dk, dv of its tokens, and one dq
+//                           partial per contribution;
+//   k_bwd_dq_reduce         per (query, head): dq = sum of its partials.
+//
+// Layout of the chunk passes: one workgroup per (chunk, sequence, KV group),
+// 4 wavefronts; wavefront w owns keys 16w .. 16w + 15 and keeps their K and V
+// rows as MFMA operands in registers.  Contributions go in tiles of 32 whose
+// q and dout rows are gathered into LDS row-major (the operand of
+// S = Q K^T and dP = dOut V^T, reduced over d) and, in the gradient pass,
+// transposed (the operand of dV^T = dOut^T P and dK^T = Q^T dS, reduced over
+// the tile's queries); double-buffered, the next tile's rows load while the
+// current one is computed.  S and dP take bf16 MFMA with exact products and
+// fp32 sums.  P and tau dS are fp32 and enter their products as a bf16 pair
+// hi + lo (hi = bf16(x), lo = bf16(x - hi), within 2^-18 of x), two MFMAs
+// each, so the gradients keep fp32 accuracy.  The MFMA output layout of S
+// (lane l: key l % 16, queries 4 (l / 16) + r of each 16-query half) is the
+// B-operand layout of the second products once the tile's query positions are
+// permuted (position 8 g + t <-> query 16 (t / 4) + 4 g + t % 4); the
+// transposed tiles store queries at those positions.  dq^T = K^T dS^T takes
+// dS through LDS (key-contiguous per query) and K^T fragments built once per
+// workgroup.  No atomics: every output element is written by one workgroup
+// or wavefront, in a fixed order.
 #include "fast_common.h"
 #include "hils_internal.h"
 #include "hils_bwd.h"
@@ -38,18 +54,22 @@ namespace {
 using fastp::ld_bf16x8;
 using fastp::mfma16;
 using fastp::pack_bf16x2;
+using fastp::xshfl_f;
 
-constexpr int MT = 256;     // threads (4 wavefronts)
+constexpr int MT = 256;     // threads of the chunk passes (4 wavefronts)
 constexpr int QT = 32;      // contributions per tile
 constexpr int CB = 128;     // contributions described per batch
 
-template <int D>
+template <int D, int PASS>
 struct MfCol {
-  static constexpr int RS = D + 8;     // row-major tile: row stride (bf16), 16-byte pad
-  static constexpr int TS = QT + 8;    // transposed tile: row stride (bf16), 16-byte pad
-  // one buffer: q rows, dout rows, q^T, dout^T
-  static constexpr int TILE = 2 * QT * RS + 2 * D * TS;
-  static constexpr int NPC = QT * (D / 8) / MT;   // 16-byte pieces per thread per tensor
+  static constexpr int RS = D + 8;                 // row-major tile: row stride (bf16), 16-byte pad
+  static constexpr int TS = QT + 8;                // transposed tile: row stride (bf16), 16-byte pad
+  static constexpr int ROWS = 2 * QT * RS;         // q rows, dout rows
+  static constexpr int TILE = ROWS + (PASS ? 2 * D * TS : 0);   // + q^T, dout^T
+  static constexpr int NPC = QT * (D / 8) / MT;    // 16-byte pieces per thread and tensor
+  static constexpr int DSS = 72;                   // dS tile: row stride (bf16), 64 keys + pad
+  static constexpr int DB = D / 64;                // 16-column blocks of dq per wavefront
+  static_assert(2 * QT * DSS <= ROWS, "the dS tile overlays the row-major tiles");
 };
 
 // position of tile query q in the transposed tiles (see above)
@@ -58,34 +78,51 @@ __device__ __forceinline__ int tpos(int q) { return 8 * ((q & 15) >> 2) + 4 * (q
 __device__ __forceinline__ float bf_lo(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
 
-template <int D>
+// reductions over the 16 lanes of a row (lanes 16 g .. 16 g + 15)
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, xshfl_f(v, 1));
+  v = fmaxf(v, xshfl_f(v, 2));
+  v = fmaxf(v, xshfl_f(v, 4));
+  return fmaxf(v, xshfl_f(v, 8));
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += xshfl_f(v, 1);
+  v += xshfl_f(v, 2);
+  v += xshfl_f(v, 4);
+  return v + xshfl_f(v, 8);
+}
+
+template <int D, int PASS>
 __global__ void __launch_bounds__(MT, 2)
-k_bwd_cols_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-              const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
-              const uint32_t* __restrict__ off, const uint32_t* __restrict__ ent,
-              const float* __restrict__ pstat, const float* __restrict__ wstat,
-              float* __restrict__ dk, float* __restrict__ dv, int Hq, int Hkv, int G, int N,
-              int S, int W, int K, int nC, int nCc, float tau) {
-  using L = MfCol<D>;
+k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+         const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
+         const uint32_t* __restrict__ off, const uint32_t* __restrict__ ent,
+         float* __restrict__ pstat, const float* __restrict__ wstat, float* __restrict__ wpart,
+         float* __restrict__ dqp, float* __restrict__ dk, float* __restrict__ dv, int Hq, int Hkv,
+         int G, int N, int S, int W, int K, int nC, int nCc, int nwin, float tau) {
+  using L = MfCol<D, PASS>;
   extern __shared__ __align__(16) unsigned char smm[];
-  bf16_t* tiles = reinterpret_cast<bf16_t*>(smm);                      // [2][TILE]
-  int* did = reinterpret_cast<int*>(smm + sizeof(bf16_t) * 2 * L::TILE); // [CB] i << 4 | head
-  float4* dcf = reinterpret_cast<float4*>(did + CB);                    // [CB] alpha, lse, g, E
-  int2* dlim = reinterpret_cast<int2*>(dcf + CB);                       // [CB] attended keys lo..hi
+  bf16_t* tiles = reinterpret_cast<bf16_t*>(smm);                        // [2][TILE]
+  int* did = reinterpret_cast<int*>(smm + sizeof(bf16_t) * 2 * L::TILE);  // [CB] i << 4 | head
+  int* dslot = did + CB;                                                  // [CB] slot, K + window chunk
+  int2* dlim = reinterpret_cast<int2*>(dslot + CB);                       // [CB] attended keys lo..hi
+  float4* dcf = reinterpret_cast<float4*>(dlim + CB);   // [CB] alpha, lse, g, E; stats: [4][QT] partials
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  // chunk-major order (c, b, g), as in the VALU column pass
+  // chunk-major order (c, b, g): a chunk's work depends on its position and
+  // the routing; consecutive workgroups take one chunk of every sequence and
+  // KV group, so heavy chunks spread over the chip
   const long long nbg = gridDim.x / nCc;             // B * Hkv
   const long long blk = blockIdx.x;
   const int c = (int)(blk / nbg);
   const long long bg = blk % nbg;
-  const int gq = (int)(bg % Hkv);
-  const long long hb = (bg / Hkv) * Hq + (long long)gq * G;
+  const long long hb = (bg / Hkv) * Hq + (long long)(bg % Hkv) * G;
   const int j0 = c * S;
   const int jn = min(S, N - j0);                     // tokens of this chunk
   const int kk = 16 * wv + l16;                      // this lane's key in the MFMA layouts
   const bool kwave = 16 * wv < S;                    // the wavefront owns keys
   const bool kown = kwave && kk < jn;
+  const int NS = K + nwin;                           // dq partial slots per (query, head)
 
   bf16x8_t kf[D / 32], vf[D / 32];                   // B operand: K[kk][32 s + 8 g4 ..]
   {
@@ -97,11 +134,33 @@ k_bwd_cols_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       vf[s2] = __builtin_bit_cast(bf16x8_t, kown ? fastp::ld_u4(v + ro + 32 * s2) : z);
     }
   }
-  f32x4_t accv[D / 16], acck[D / 16];
+  // gradient pass: A operand of dq^T = K^T dS^T, K^T[16 db + l16][32 ks + 8 g4 ..]
+  // for the wavefront's dq column blocks db = DB w ..
+  bf16x8_t ktf[PASS ? L::DB : 1][2];
+  f32x4_t accv[PASS ? D / 16 : 1], acck[PASS ? D / 16 : 1];
+  if (PASS) {
+    const unsigned short* k16 = reinterpret_cast<const unsigned short*>(k);
 #pragma unroll
-  for (int b2 = 0; b2 < D / 16; ++b2) {
-    accv[b2] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    acck[b2] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int db = 0; db < L::DB; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint32_t w2[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int k0 = 32 * ks + 8 * g4 + 2 * t;
+          const long long e = (bg * (long long)N + j0) * D + 16 * (L::DB * wv + db) + l16;
+          const uint32_t lo = k0 < jn ? k16[e + (long long)k0 * D] : 0u;
+          const uint32_t hi = k0 + 1 < jn ? k16[e + (long long)(k0 + 1) * D] : 0u;
+          w2[t] = lo | (hi << 16);
+        }
+        ktf[db][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(w2[0], w2[1], w2[2], w2[3]));
+      }
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < D / 16; ++b2) {
+      accv[b2] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      acck[b2] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
   }
 
   const bool summ = c < nC;
@@ -109,7 +168,7 @@ k_bwd_cols_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const uint32_t p1 = summ ? off[bg * (nC + 1) + c + 1] : 0u;
   const long long nsel = (long long)(p1 - p0) * G;                 // (pair, head)
   const int i1 = min(N, (c + 1) * S + W - 1);
-  const long long nwin = (long long)(i1 - j0) * G;                // window (query, head)
+  const long long nwq = (long long)(i1 - j0) * G;                 // window (query, head)
   const uint32_t* eg = ent + bg * (long long)N * K;
 
   // staging: piece pc = tid + MT m of a tile: query pc % QT, 16-byte part pc / QT
@@ -123,8 +182,7 @@ k_bwd_cols_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       po[m] = pq[m];
       if (u < nb) {
         const int id = did[u];
-        const int i = (id >> 4) & 0x7ffffff, r = id & 15;
-        const long long o = ((hb + r) * N + i) * (long long)D + 8 * part;
+        const long long o = ((hb + (id & 15)) * N + (id >> 4)) * (long long)D + 8 * part;
         pq[m] = fastp::ld_u4(q + o);
         po[m] = fastp::ld_u4(dout + o);
       }
@@ -132,29 +190,29 @@ k_bwd_cols_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   };
   auto stage_store = [&](int buf) __attribute__((always_inline)) {
     bf16_t* tb = tiles + (size_t)buf * L::TILE;
-    unsigned short* tq = reinterpret_cast<unsigned short*>(tb + 2 * QT * L::RS);
-    unsigned short* to = tq + D * L::TS;
 #pragma unroll
     for (int m = 0; m < L::NPC; ++m) {
       const int pc = tid + MT * m, qq = pc % QT, part = pc / QT;
       fastp::st_u4(tb + qq * L::RS + 8 * part, pq[m]);
       fastp::st_u4(tb + (QT + qq) * L::RS + 8 * part, po[m]);
-      const int ps = tpos(qq);
-      const uint32_t wq[4] = {pq[m].x, pq[m].y, pq[m].z, pq[m].w};
-      const uint32_t wo[4] = {po[m].x, po[m].y, po[m].z, po[m].w};
+      if (PASS) {
+        unsigned short* tq = reinterpret_cast<unsigned short*>(tb + L::ROWS);
+        unsigned short* to = tq + D * L::TS;
+        const int ps = tpos(qq);
+        const uint32_t wq[4] = {pq[m].x, pq[m].y, pq[m].z, pq[m].w};
+        const uint32_t wo[4] = {po[m].x, po[m].y, po[m].z, po[m].w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = 8 * part + e;
-        tq[row * L::TS + ps] = (unsigned short)(wq[e >> 1] >> (16 * (e & 1)));
-        to[row * L::TS + ps] = (unsigned short)(wo[e >> 1] >> (16 * (e & 1)));
+        for (int e = 0; e < 8; ++e) {
+          const int row = 8 * part + e;
+          tq[row * L::TS + ps] = (unsigned short)(wq[e >> 1] >> (16 * (e & 1)));
+          to[row * L::TS + ps] = (unsigned short)(wo[e >> 1] >> (16 * (e & 1)));
+        }
       }
     }
   };
-  auto compute = [&](int tl, int buf) __attribute__((always_inline)) {
-    const bf16_t* tb = tiles + (size_t)buf * L::TILE;
-    const bf16_t* tqt = tb + 2 * QT * L::RS;
-    const bf16_t* tot = tqt + D * L::TS;
-    f32x4_t sc[2], dp[2];
+  // S and dP of the tile for this wavefront's 16 keys: sc[h][r], dp[h][r] for
+  // query 16 h + 4 g4 + r, key kk
+  auto scores = [&](const bf16_t* tb, f32x4_t* sc, f32x4_t* dp) __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       sc[h] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -167,73 +225,191 @@ k_bwd_cols_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         dp[h] = mfma16(ao, vf[s2], dp[h]);
       }
     }
-    // weights of the (query, key) pairs this lane holds: query 16 h + 4 g4 + r
-    float ap[8], ds[8];
+  };
+
+  // stats pass: per query of the tile, max / sum exp / sum exp dout.v over
+  // this wavefront's keys, combined over the wavefronts
+  auto compute_stats = [&](int tl, int buf, int nb) __attribute__((always_inline)) {
+    float4* red = dcf;                               // [4][QT]
+    if (kwave) {
+      f32x4_t sc[2], dp[2];
+      scores(tiles + (size_t)buf * L::TILE, sc, dp);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int u = tl * QT + 16 * h + 4 * g4 + r;
-        const float4 cf = dcf[u];
-        const int2 lm = dlim[u];
-        const bool ok = kown && kk >= lm.x && kk <= lm.y;
-        const float p = ok ? __expf(tau * sc[h][r] - cf.y) : 0.0f;
-        const float a = cf.x * p;
-        ap[4 * h + r] = a;
-        ds[4 * h + r] = tau * fmaf(a, dp[h][r] - cf.z, cf.w * p);
+        for (int r = 0; r < 4; ++r) {
+          const int qq = 16 * h + 4 * g4 + r;
+          const int2 lm = dlim[tl * QT + qq];
+          const bool ok = kown && kk >= lm.x && kk <= lm.y;
+          const float x = ok ? tau * sc[h][r] : -INFINITY;
+          const float m = max16(x);
+          const float e = ok ? __expf(x - m) : 0.0f;
+          const float z = sum16(e);
+          const float y = sum16(e * dp[h][r]);
+          if (l16 == 0) red[wv * QT + qq] = make_float4(m, z, y, 0.0f);
+        }
       }
     }
-    uint32_t ph[4], pl[4], dh[4], dl[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      ph[t] = pack_bf16x2(ap[2 * t], ap[2 * t + 1]);
-      pl[t] = pack_bf16x2(ap[2 * t] - bf_lo(ph[t]), ap[2 * t + 1] - bf_hi(ph[t]));
-      dh[t] = pack_bf16x2(ds[2 * t], ds[2 * t + 1]);
-      dl[t] = pack_bf16x2(ds[2 * t] - bf_lo(dh[t]), ds[2 * t + 1] - bf_hi(dh[t]));
-    }
-    const bf16x8_t bph = __builtin_bit_cast(bf16x8_t, make_uint4(ph[0], ph[1], ph[2], ph[3]));
-    const bf16x8_t bpl = __builtin_bit_cast(bf16x8_t, make_uint4(pl[0], pl[1], pl[2], pl[3]));
-    const bf16x8_t bdh = __builtin_bit_cast(bf16x8_t, make_uint4(dh[0], dh[1], dh[2], dh[3]));
-    const bf16x8_t bdl = __builtin_bit_cast(bf16x8_t, make_uint4(dl[0], dl[1], dl[2], dl[3]));
-#pragma unroll
-    for (int b2 = 0; b2 < D / 16; ++b2) {
-      const bf16x8_t ao = ld_bf16x8(tot + (16 * b2 + l16) * L::TS + 8 * g4);
-      const bf16x8_t aq = ld_bf16x8(tqt + (16 * b2 + l16) * L::TS + 8 * g4);
-      accv[b2] = mfma16(ao, bph, accv[b2]);
-      accv[b2] = mfma16(ao, bpl, accv[b2]);
-      acck[b2] = mfma16(aq, bdh, acck[b2]);
-      acck[b2] = mfma16(aq, bdl, acck[b2]);
+    __syncthreads();
+    if (tid < QT) {
+      const int u = tl * QT + tid;
+      if (u < nb) {
+        const int nkw = (S + 15) / 16;
+        float M = -INFINITY;
+        for (int w = 0; w < nkw; ++w) M = fmaxf(M, red[w * QT + tid].x);
+        float Z = 0.0f, Y = 0.0f;
+        for (int w = 0; w < nkw; ++w) {
+          const float4 p = red[w * QT + tid];
+          if (p.x > -INFINITY) {
+            const float f = __expf(p.x - M);
+            Z = fmaf(p.y, f, Z);
+            Y = fmaf(p.z, f, Y);
+          }
+        }
+        const int id = did[u], slot = dslot[u];
+        const int i = id >> 4, r = id & 15;
+        if (slot < K) {
+          float* ps = pstat + (((bg * N + i) * (long long)K + slot) * G + r) * 4;
+          ps[1] = M + __logf(Z);
+          ps[2] = Y / Z;
+        } else {
+          *reinterpret_cast<float4*>(wpart + (((hb + r) * N + i) * (long long)nwin + (slot - K)) * 4) =
+              make_float4(M, Z, Y, 0.0f);
+        }
+      }
     }
   };
 
-  for (long long base = 0; base < nsel + nwin; base += CB) {
-    const int nb = (int)min((long long)CB, nsel + nwin - base);
+  // gradient pass
+  auto compute_grads = [&](int tl, int buf, int nb) __attribute__((always_inline)) {
+    bf16_t* tb = tiles + (size_t)buf * L::TILE;
+    const bf16_t* tqt = tb + L::ROWS;
+    const bf16_t* tot = tqt + D * L::TS;
+    uint32_t ph[4], pl[4], dh[4], dl[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) { ph[t] = 0u; pl[t] = 0u; dh[t] = 0u; dl[t] = 0u; }
+    if (kwave) {
+      f32x4_t sc[2], dp[2];
+      scores(tb, sc, dp);
+      // weights of the (query, key) pairs this lane holds
+      float ap[8], ds[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int u = tl * QT + 16 * h + 4 * g4 + r;
+          const float4 cf = dcf[u];
+          const int2 lm = dlim[u];
+          const bool ok = kown && kk >= lm.x && kk <= lm.y;
+          const float p = ok ? __expf(tau * sc[h][r] - cf.y) : 0.0f;
+          const float a = cf.x * p;
+          ap[4 * h + r] = a;
+          ds[4 * h + r] = tau * fmaf(a, dp[h][r] - cf.z, cf.w * p);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        ph[t] = pack_bf16x2(ap[2 * t], ap[2 * t + 1]);
+        pl[t] = pack_bf16x2(ap[2 * t] - bf_lo(ph[t]), ap[2 * t + 1] - bf_hi(ph[t]));
+        dh[t] = pack_bf16x2(ds[2 * t], ds[2 * t + 1]);
+        dl[t] = pack_bf16x2(ds[2 * t] - bf_lo(dh[t]), ds[2 * t + 1] - bf_hi(dh[t]));
+      }
+    }
+    __syncthreads();                                 // every wavefront has read the row-major tiles
+    // dS (hi, lo) over the row-major area: [2][QT][DSS], key-contiguous
+    {
+      unsigned short* dsl = reinterpret_cast<unsigned short*>(tb);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int e = 2 * t + x, qq = 16 * (e >> 2) + 4 * g4 + (e & 3);
+          dsl[qq * L::DSS + kk] = (unsigned short)(dh[t] >> (16 * x));
+          dsl[(QT + qq) * L::DSS + kk] = (unsigned short)(dl[t] >> (16 * x));
+        }
+      }
+    }
+    if (kwave) {
+      const bf16x8_t bph = __builtin_bit_cast(bf16x8_t, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+      const bf16x8_t bpl = __builtin_bit_cast(bf16x8_t, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+      const bf16x8_t bdh = __builtin_bit_cast(bf16x8_t, make_uint4(dh[0], dh[1], dh[2], dh[3]));
+      const bf16x8_t bdl = __builtin_bit_cast(bf16x8_t, make_uint4(dl[0], dl[1], dl[2], dl[3]));
+#pragma unroll
+      for (int b2 = 0; b2 < D / 16; ++b2) {
+        const bf16x8_t ao = ld_bf16x8(tot + (16 * b2 + l16) * L::TS + 8 * g4);
+        const bf16x8_t aq = ld_bf16x8(tqt + (16 * b2 + l16) * L::TS + 8 * g4);
+        accv[b2] = mfma16(ao, bph, accv[b2]);
+        accv[b2] = mfma16(ao, bpl, accv[b2]);
+        acck[b2] = mfma16(aq, bdh, acck[b2]);
+        acck[b2] = mfma16(aq, bdl, acck[b2]);
+      }
+    }
+    __syncthreads();                                 // the dS tile is complete
+    // dq^T[16 db + 4 g4 + r][query 16 qb + l16] = sum over the chunk's keys
+    const bf16_t* dsl = tb;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int u = tl * QT + 16 * qb + l16;
+      long long prow = 0;
+      if (u < nb) {
+        const int id = did[u];
+        prow = ((hb + (id & 15)) * N + (id >> 4)) * (long long)NS + dslot[u];
+      }
+      bf16x8_t bh[2], bl[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bh[ks] = ld_bf16x8(dsl + (16 * qb + l16) * L::DSS + 32 * ks + 8 * g4);
+        bl[ks] = ld_bf16x8(dsl + (QT + 16 * qb + l16) * L::DSS + 32 * ks + 8 * g4);
+      }
+#pragma unroll
+      for (int db = 0; db < L::DB; ++db) {
+        f32x4_t a = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          a = mfma16(ktf[db][ks], bh[ks], a);
+          a = mfma16(ktf[db][ks], bl[ks], a);
+        }
+        if (u < nb)
+          *reinterpret_cast<float4*>(dqp + prow * D + 16 * (L::DB * wv + db) + 4 * g4) =
+              make_float4(a[0], a[1], a[2], a[3]);
+      }
+    }
+  };
+
+  for (long long base = 0; base < nsel + nwq; base += CB) {
+    const int nb = (int)min((long long)CB, nsel + nwq - base);
     __syncthreads();                                 // the previous batch is consumed
     for (int t = tid; t < CB; t += MT) {
       const long long idx = base + t;
-      int id = 0;
+      int id = 0, slot = 0;
       float4 cf = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       int2 lm = make_int2(1, 0);                     // no key
       if (t < nb) {
         if (idx < nsel) {
           const uint32_t e = eg[p0 + idx / G];
-          const int r = (int)(idx % G), i = (int)(e >> 8), s2 = (int)(e & 255u);
-          const float4 ps = *reinterpret_cast<const float4*>(pstat + (((bg * N + i) * (long long)K + s2) * G + r) * 4);
+          const int r = (int)(idx % G), i = (int)(e >> 8);
+          slot = (int)(e & 255u);
           id = (i << 4) | r;
-          cf = make_float4(ps.x, ps.y, ps.z, 0.0f);
           lm = make_int2(0, S);
+          if (PASS) {
+            const float4 ps = *reinterpret_cast<const float4*>(
+                pstat + (((bg * N + i) * (long long)K + slot) * G + r) * 4);
+            cf = make_float4(ps.x, ps.y, ps.z, 0.0f);
+          }
         } else {
           const long long widx = idx - nsel;
           const int i = j0 + (int)(widx / G), r = (int)(widx % G);
-          const float4 ws = *reinterpret_cast<const float4*>(wstat + ((hb + r) * N + i) * 4);
+          const int ws = (int)window_start(i, W, S);
           id = (i << 4) | r;
-          cf = ws;
-          lm = make_int2((int)(window_start(i, W, S) - j0), i - j0);
+          slot = K + (c - ws / S);
+          lm = make_int2(ws - j0, i - j0);
+          if (PASS) cf = *reinterpret_cast<const float4*>(wstat + ((hb + r) * N + i) * 4);
         }
       }
       did[t] = id;
-      dcf[t] = cf;
+      dslot[t] = slot;
       dlim[t] = lm;
+      if (PASS) dcf[t] = cf;
     }
     __syncthreads();
     const int ntl = (nb + QT - 1) / QT;
@@ -242,14 +418,15 @@ k_bwd_cols_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     __syncthreads();
     for (int tl = 0; tl < ntl; ++tl) {
       if (tl + 1 < ntl) stage_load(tl + 1, nb);
-      if (kwave) compute(tl, tl & 1);
+      if (PASS) compute_grads(tl, tl & 1, nb);
+      else compute_stats(tl, tl & 1, nb);
       // buffer (tl + 1) & 1 was last read in tile tl - 1, before the barrier
       // that ended it
       if (tl + 1 < ntl) stage_store((tl + 1) & 1);
       __syncthreads();
     }
   }
-  if (kown) {
+  if (PASS && kown) {
     const long long ro = (bg * (long long)N + j0 + kk) * D + 4 * g4;
 #pragma unroll
     for (int b2 = 0; b2 < D / 16; ++b2) {
@@ -261,39 +438,218 @@ k_bwd_cols_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   }
 }
 
+template <int D, int PASS>
+size_t mf_lds() {
+  return sizeof(bf16_t) * 2 * MfCol<D, PASS>::TILE +
+         (size_t)CB * (2 * sizeof(int) + sizeof(int2) + sizeof(float4));
+}
+
+// ---------------------------------------------------------------------------
+// per (query, head): window statistics from the partials, routing scores,
+// fusion weights and their gradients; one wavefront per row, K <= 128
+
+__global__ void __launch_bounds__(256)
+k_bwd_rowstat(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
+              const float* __restrict__ bsum, const int32_t* __restrict__ sel,
+              float* __restrict__ pstat, float* __restrict__ wstat, const float* __restrict__ wpart,
+              float* __restrict__ dqo, int Hq, int Hkv, int G, int N, int d, int S, int W, int K,
+              int nC, int nwin, long long nrows, float tau) {
+  extern __shared__ __align__(16) float smq[];       // [4][d] routing query rows
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const long long item = (long long)blockIdx.x * 4 + wv;   // (b, h, i)
+  if (item >= nrows) return;                         // whole wavefronts; no barriers below
+  const int i = (int)(item % N);
+  const long long bh = item / N;
+  const int h = (int)(bh % Hq);
+  const long long b = bh / Hq;
+  const int g = h / G, r = h - g * G;
+  const long long row = (b * Hkv + g) * N + i;       // selection row
+  float* qs = smq + wv * d;
+  for (int e = lane; e < d; e += 64) qs[e] = bf16_to_f32(qr[item * d + e]);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  // selected chunks: lanes t and t + 64
+  float sh[2], lt[2], gt[2];
+  bool vt[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int t = lane + 64 * m;
+    vt[m] = false;
+    sh[m] = -INFINITY;
+    lt[m] = 0.0f;
+    gt[m] = 0.0f;
+    if (t < K) {
+      const int c = sel[row * K + t];
+      if (c >= 0 && c < nC) {
+        vt[m] = true;
+        const bf16_t* kp = ksum + (bh * nC + c) * (long long)d;
+        float a = 0.0f;
+        for (int e = 0; e < d; e += 8) {
+          const uint4 u = fastp::ld_u4(kp + e);
+          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            a = fmaf(qs[e + 2 * x], bf_lo(w4[x]), a);
+            a = fmaf(qs[e + 2 * x + 1], bf_hi(w4[x]), a);
+          }
+        }
+        sh[m] = fmaf(tau, a, bsum[bh * nC + c]);
+        const float* ps = pstat + ((row * K + t) * G + r) * 4;
+        lt[m] = ps[1];
+        gt[m] = ps[2];
+      }
+    }
+  }
+  // the window: partials of its chunks
+  const int ws = (int)window_start(i, W, S);
+  const int nw = i / S - ws / S + 1;
+  float wm = -INFINITY, wz = 0.0f, wy = 0.0f;      // this lane's chunks, online
+  for (int w = lane; w < nw; w += 64) {
+    const float4 p = *reinterpret_cast<const float4*>(wpart + (item * nwin + w) * 4);
+    if (p.x > wm) {
+      const float f = __expf(wm - p.x);
+      wz = fmaf(wz, f, p.y);
+      wy = fmaf(wy, f, p.z);
+      wm = p.x;
+    } else if (p.x > -INFINITY) {
+      const float f = __expf(p.x - wm);
+      wz = fmaf(p.y, f, wz);
+      wy = fmaf(p.z, f, wy);
+    }
+  }
+  const float Mw = wave_max_f(wm);
+  const float fw = wm > -INFINITY ? __expf(wm - Mw) : 0.0f;
+  const float Zw = wave_sum_f(wz * fw);
+  const float Yw = wave_sum_f(wy * fw);
+  const float lse_w = Mw + __logf(Zw);
+  const float g_w = Yw / Zw;
+  // fusion softmax over {s_hat_t} U {log Z_swa}
+  const float Mf = fmaxf(wave_max_f(fmaxf(sh[0], sh[1])), lse_w);
+  float ez[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) ez[m] = vt[m] ? __expf(sh[m] - Mf) : 0.0f;
+  const float ew = __expf(lse_w - Mf);
+  const float Zf = wave_sum_f(ez[0] + ez[1]) + ew;
+  const float aw = ew / Zf;
+  float at[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) at[m] = ez[m] / Zf;
+  const float gbar = fmaf(aw, g_w, wave_sum_f(fmaf(at[0], gt[0], at[1] * gt[1])));
+  float dsh[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    dsh[m] = at[m] * (gt[m] - gbar);
+    if (vt[m])
+      *reinterpret_cast<float4*>(pstat + ((row * K + lane + 64 * m) * G + r) * 4) =
+          make_float4(at[m], lt[m], gt[m], dsh[m]);
+  }
+  if (lane == 0)
+    *reinterpret_cast<float4*>(wstat + item * 4) = make_float4(aw, lse_w, g_w, aw * (g_w - gbar));
+  // routing query: tau sum_t (d s_hat_t) k'_t; lane takes elements 2 lane, 2 lane + 1
+  float q0 = 0.0f, q1 = 0.0f;
+  const int e = 2 * lane;
+  for (int t = 0; t < K; ++t) {
+    const int c = sel[row * K + t];
+    if (c < 0 || c >= nC) continue;
+    const float x = __shfl(dsh[t >> 6], t & 63, 64);
+    if (e < d) {
+      const uint32_t kv = *reinterpret_cast<const uint32_t*>(ksum + (bh * nC + c) * (long long)d + e);
+      q0 = fmaf(x, bf_lo(kv), q0);
+      q1 = fmaf(x, bf_hi(kv), q1);
+    }
+  }
+  if (e < d) *reinterpret_cast<float2*>(dqo + item * d + e) = make_float2(tau * q0, tau * q1);
+}
+
+// per (query, head): dq = (add ? dq : 0) + the partials of its selected
+// chunks and window chunks; one wavefront per row, lane takes 2 elements
+__global__ void __launch_bounds__(256)
+k_bwd_dq_reduce(const float* __restrict__ dqp, const int32_t* __restrict__ sel, float* __restrict__ dq,
+                int Hq, int Hkv, int G, int N, int d, int S, int W, int K, int nC, int nwin,
+                long long nrows, int add) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const long long item = (long long)blockIdx.x * 4 + wv;
+  if (item >= nrows) return;
+  const int e = 2 * lane;
+  if (e >= d) return;
+  const int i = (int)(item % N);
+  const long long bh = item / N;
+  const int h = (int)(bh % Hq);
+  const long long b = bh / Hq;
+  const long long row = (b * Hkv + h / G) * N + i;
+  const float* pp = dqp + item * (long long)(K + nwin) * d + e;
+  float2 acc = add ? *reinterpret_cast<const float2*>(dq + item * d + e) : make_float2(0.0f, 0.0f);
+  for (int t = 0; t < K; ++t) {
+    const int c = sel[row * K + t];
+    if (c < 0 || c >= nC) continue;
+    const float2 x = *reinterpret_cast<const float2*>(pp + (long long)t * d);
+    acc.x += x.x;
+    acc.y += x.y;
+  }
+  const int ws = (int)window_start(i, W, S);
+  const int nw = i / S - ws / S + 1;
+  for (int w = 0; w < nw; ++w) {
+    const float2 x = *reinterpret_cast<const float2*>(pp + (long long)(K + w) * d);
+    acc.x += x.x;
+    acc.y += x.y;
+  }
+  *reinterpret_cast<float2*>(dq + item * d + e) = acc;
+}
+
 template <int D>
-size_t cols_mf_lds() {
-  return sizeof(bf16_t) * 2 * MfCol<D>::TILE + (size_t)CB * (sizeof(int) + sizeof(float4) + sizeof(int2));
+hipError_t launch_mf(const HilsShape& s, const void* q, const void* qr, const void* k, const void* v,
+                     const void* dout, const int32_t* sel, const void* ksum, const float* bsum,
+                     float* dq, float* dqr, float* dk, float* dv, const HilsBwdBufs& wb,
+                     hipStream_t st) {
+  const float tau = (float)s.tau;
+  const long long nblk = (long long)s.B * s.Hkv * s.nCc;
+  const long long nrows = (long long)s.B * s.Hq * s.N;
+  const unsigned rgrid = (unsigned)((nrows + 3) / 4);
+  const size_t sh0 = mf_lds<D, 0>(), sh1 = mf_lds<D, 1>();
+  hils_allow_lds((const void*)k_bwd_mf<D, 0>, sh0);
+  hils_allow_lds((const void*)k_bwd_mf<D, 1>, sh1);
+  { HilsProfScope ps_("k_bwd_stats", st);
+    hipLaunchKernelGGL((k_bwd_mf<D, 0>), dim3((unsigned)nblk), dim3(MT), sh0, st,
+                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout,
+                       wb.off, wb.ent, wb.pstat, wb.wstat, wb.wpart, wb.dqp, dk, dv, s.Hq, s.Hkv,
+                       s.G, s.N, s.S, s.W, s.K, s.nC, s.nCc, s.nwin, tau); }
+  // the routing query's gradient goes to dq_route, or to dq (then the
+  // partials are added to it)
+  { HilsProfScope ps_("k_bwd_rowstat", st);
+    hipLaunchKernelGGL(k_bwd_rowstat, dim3(rgrid), dim3(256), sizeof(float) * 4 * s.d, st,
+                       (const bf16_t*)qr, (const bf16_t*)ksum, bsum, sel, wb.pstat, wb.wstat,
+                       wb.wpart, dqr ? dqr : dq, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC,
+                       s.nwin, nrows, tau); }
+  { HilsProfScope ps_("k_bwd_cols", st);
+    hipLaunchKernelGGL((k_bwd_mf<D, 1>), dim3((unsigned)nblk), dim3(MT), sh1, st,
+                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout,
+                       wb.off, wb.ent, wb.pstat, wb.wstat, wb.wpart, wb.dqp, dk, dv, s.Hq, s.Hkv,
+                       s.G, s.N, s.S, s.W, s.K, s.nC, s.nCc, s.nwin, tau); }
+  { HilsProfScope ps_("k_bwd_dq", st);
+    hipLaunchKernelGGL(k_bwd_dq_reduce, dim3(rgrid), dim3(256), 0, st, wb.dqp, sel, dq, s.Hq,
+                       s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, s.nwin, nrows, dqr ? 0 : 1); }
+  return hipGetLastError();
 }
 
 }  // namespace
 
-bool hils_bwd_cols_mf_ok(const HilsShape& s) {
-  return s.dtype == 0 && (s.d == 64 || s.d == 128) && s.S % 16 == 0 && s.S <= 64 && s.G <= 16;
+bool hils_bwd_mf_ok(const HilsShape& s) {
+  return s.dtype == 0 && (s.d == 64 || s.d == 128) && s.S % 16 == 0 && s.S <= 64 && s.G <= 16 &&
+         s.K <= 128 && s.N < (1 << 24);
 }
 
-hipError_t hils_launch_bwd_cols_mf(const HilsShape& s, const void* q, const void* k, const void* v,
-                                   const void* dout, const HilsBwdBufs& wb, float* dk, float* dv,
-                                   hipStream_t st) {
-  if (!hils_bwd_cols_mf_ok(s)) return hipErrorInvalidValue;
-  const long long nblk = (long long)s.B * s.Hkv * s.nCc;
-  if (nblk <= 0) return hipSuccess;
-  const float tau = (float)s.tau;
-  HilsProfScope ps_("k_bwd_cols", st);
-  if (s.d == 128) {
-    const size_t shm = cols_mf_lds<128>();
-    hils_allow_lds((const void*)k_bwd_cols_mf<128>, shm);
-    hipLaunchKernelGGL(k_bwd_cols_mf<128>, dim3((unsigned)nblk), dim3(MT), shm, st,
-                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout,
-                       wb.off, wb.ent, wb.pstat, wb.wstat, dk, dv, s.Hq, s.Hkv, s.G, s.N, s.S, s.W,
-                       s.K, s.nC, s.nCc, tau);
-  } else {
-    const size_t shm = cols_mf_lds<64>();
-    hils_allow_lds((const void*)k_bwd_cols_mf<64>, shm);
-    hipLaunchKernelGGL(k_bwd_cols_mf<64>, dim3((unsigned)nblk), dim3(MT), shm, st,
-                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout,
-                       wb.off, wb.ent, wb.pstat, wb.wstat, dk, dv, s.Hq, s.Hkv, s.G, s.N, s.S, s.W,
-                       s.K, s.nC, s.nCc, tau);
-  }
-  return hipGetLastError();
+size_t hils_bwd_mf_wpart_bytes(const HilsShape& s) {
+  return (size_t)s.B * s.Hq * s.N * s.nwin * 16;
+}
+size_t hils_bwd_mf_dqp_bytes(const HilsShape& s) {
+  return (size_t)s.B * s.Hq * s.N * (s.K + s.nwin) * s.d * 4;
+}
+
+hipError_t hils_launch_backward_mf(const HilsShape& s, const void* q, const void* qr, const void* k,
+                                   const void* v, const void* dout, const int32_t* sel,
+                                   const void* ksum, const float* bsum, float* dq, float* dqr,
+                                   float* dk, float* dv, const HilsBwdBufs& wb, hipStream_t st) {
+  if (!hils_bwd_mf_ok(s) || !wb.wpart || !wb.dqp) return hipErrorInvalidValue;
+  if ((long long)s.B * s.Hkv * s.nCc <= 0) return hipSuccess;
+  return s.d == 128 ? launch_mf<128>(s, q, qr, k, v, dout, sel, ksum, bsum, dq, dqr, dk, dv, wb, st)
+                    : launch_mf<64>(s, q, qr, k, v, dout, sel, ksum, bsum, dq, dqr, dk, dv, wb, st);
 }

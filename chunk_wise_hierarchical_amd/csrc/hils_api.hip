@@ -133,7 +133,7 @@ DecodeLayout decode_layout(const HilsShape& s) {
 }
 
 struct BwdLayout {
-  size_t ks, bs, off, ent, pstat, wstat, total;
+  size_t ks, bs, off, ent, pstat, wstat, wpart, dqp, total;
 };
 BwdLayout bwd_layout(const HilsShape& s) {
   BwdLayout L{};
@@ -145,6 +145,9 @@ BwdLayout bwd_layout(const HilsShape& s) {
   L.ent = off;   off += align_up(BG * s.N * s.K * 4);
   L.pstat = off; off += align_up(BG * s.N * s.K * s.G * 16);
   L.wstat = off; off += align_up((size_t)s.B * s.Hq * s.N * 16);
+  const bool mf = hils_bwd_mf_ok(s);
+  L.wpart = off; off += align_up(mf ? hils_bwd_mf_wpart_bytes(s) : 0);
+  L.dqp = off;   off += align_up(mf ? hils_bwd_mf_dqp_bytes(s) : 0);
   L.total = off;
   return L;
 }
@@ -498,8 +501,10 @@ hils_status hils_prefill_backward(const hils_cfg* cfg, const void* q, const void
     ks = w + L.ks;
     bs = (const float*)(w + L.bs);
   }
+  const bool mf = hils_bwd_mf_ok(s);
   HilsBwdBufs wb{(uint32_t*)(w + L.off), (uint32_t*)(w + L.ent), (float*)(w + L.pstat),
-                 (float*)(w + L.wstat)};
+                 (float*)(w + L.wstat), mf ? (float*)(w + L.wpart) : nullptr,
+                 mf ? (float*)(w + L.dqp) : nullptr};
   return hip_status(hils_launch_backward(s, q, q_route ? q_route : q, k, v, lm_q, dout, sel, ks, bs,
                                          dq, dq_route, dk, dv, dlm, wb, st));
 }

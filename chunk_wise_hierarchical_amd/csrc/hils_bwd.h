@@ -10,6 +10,9 @@ struct HilsBwdBufs {
   uint32_t* ent;    // [B*Hkv][N*K]  pairs (query << 8 | slot), query order per chunk
   float* pstat;     // [B*Hkv*N][K][G][4] alpha, log-normaliser, g = dout.o, d s_hat
   float* wstat;     // [B*Hq*N][4]        the same for the window (d log Z_swa last)
+  // matrix-core backward only (else null):
+  float* wpart;     // [B*Hq*N][nwin][4]  window partials per chunk: max, sum exp, sum exp dout.v
+  float* dqp;       // [B*Hq*N][K + nwin][d] dq partial per selected slot and window chunk
 };
 
 // LDS bytes of the row kernel (window logits of G heads live in LDS)
@@ -21,10 +24,14 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
                                 float* dk, float* dv, float* dlm, const HilsBwdBufs& wb,
                                 hipStream_t st);
 
-// Column pass on the matrix cores (backward_mf.hip): dk, dv of every chunk's
-// tokens for bf16 inputs with d in {64, 128} and S a multiple of 16 (<= 64);
-// the summaries' share of dk and dlm is added afterwards by the summary pass.
-bool hils_bwd_cols_mf_ok(const HilsShape& s);
-hipError_t hils_launch_bwd_cols_mf(const HilsShape& s, const void* q, const void* k, const void* v,
-                                   const void* dout, const HilsBwdBufs& wb, float* dk, float* dv,
-                                   hipStream_t st);
+// Matrix-core backward (backward_mf.hip) for bf16 inputs with d in {64, 128}
+// and S a multiple of 16: per-chunk statistics, per-row fusion gradients,
+// per-chunk dk, dv and dq partials, per-row dq.  The selection lists come
+// before it and the summaries' share of dk and dlm after it.
+bool hils_bwd_mf_ok(const HilsShape& s);
+size_t hils_bwd_mf_wpart_bytes(const HilsShape& s);
+size_t hils_bwd_mf_dqp_bytes(const HilsShape& s);
+hipError_t hils_launch_backward_mf(const HilsShape& s, const void* q, const void* qr, const void* k,
+                                   const void* v, const void* dout, const int32_t* sel,
+                                   const void* ksum, const float* bsum, float* dq, float* dqr,
+                                   float* dk, float* dv, const HilsBwdBufs& wb, hipStream_t st);

@@ -30,7 +30,7 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def _case(w, mode="surrogate", q_route=False, label="", seed=21):
+def _case(w, mode="surrogate", q_route=False, label="", seed=21, reverse_slots=False):
     _say(f"[backward] {label} {w.name} B={w.B} N={w.N} Hq={w.Hq} Hkv={w.Hkv} d={w.d} S={w.S} "
          f"W={w.W} K={w.K} dtype={w.dtype} mode={mode} q_route={q_route}")
     x = {k: v.cuda() for k, v in synth.make_prefill_inputs(w, with_q_route=q_route).items()}
@@ -40,6 +40,8 @@ def _case(w, mode="surrogate", q_route=False, label="", seed=21):
     ref = O.ref_backward(xn["q"], xn["k"], xn["v"], xn["lm"], np32(dout), w.S, w.W, w.K,
                          q_route=xn.get("q_route"), mode=mode, store=w.dtype)
     sel = torch.tensor(ref["sel"], dtype=torch.int32).cuda().contiguous()
+    if reverse_slots:      # empty slots (-1) first: the gradients depend on the set only
+        sel = sel.flip(-1).contiguous()
     lm = None if mode == "mean_pool" else x["lm"]
     gr = hils.prefill_backward(x["q"], x["k"], x["v"], lm, dout, sel, w.S, w.W, w.K,
                                q_route=x.get("q_route"), mode=mode)
@@ -96,6 +98,16 @@ def test_backward_matrix_core_columns_all_modes():
     _case(w, label="mf d64 S32 G8")
     w = synth.get_workload("prefill_64k", N=50, Hq=2, Hkv=1, W=30, K=2)
     _case(w, label="mf N < S")
+
+
+def test_backward_selection_slot_order():
+    # early queries have fewer candidates than K; with the slots reversed their
+    # -1 entries come first, in both the matrix-core (bf16) and VALU (fp32) paths
+    w = synth.get_workload("prefill_64k", N=600, Hq=4, Hkv=2, W=64, K=6, regime="iid")
+    _case(w, label="bf16 reversed slots", reverse_slots=True)
+    w = synth.get_workload("prefill_64k", N=300, Hq=2, Hkv=1, d=64, S=32, W=40, K=5, regime="iid",
+                           dtype="f32")
+    _case(w, label="fp32 reversed slots", reverse_slots=True)
 
 
 def test_backward_deterministic():
