@@ -140,61 +140,86 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 // ---------------------------------------------------------------------------
 // inverse selection lists: for each chunk c of (b, g), entries (i << 8 | slot)
-// at off[c] .. off[c+1], in increasing query order
+// at off[c] .. off[c+1], in increasing query order (a stable counting sort).
+// With par set, each of the 16 wavefronts takes a contiguous sixteenth of the
+// queries: it counts its own entries per chunk ([16][nC] counters in LDS), the
+// scan over chunks turns the counts into per-wavefront cursors (wavefront w
+// starts after wavefronts 0 .. w-1 within every chunk), and the wavefronts
+// scatter their ranges in parallel.  Otherwise one wavefront scatters all
+// queries ([nC] counters).  Within a wavefront the queries go in order and a
+// query's slots hold distinct chunks, so its LDS atomics, processed in issue
+// order, keep the query order.
 
 __global__ void __launch_bounds__(1024)
 k_bwd_lists(const int32_t* __restrict__ sel, uint32_t* __restrict__ off, uint32_t* __restrict__ ent,
-            int N, int K, int nC) {
-  extern __shared__ uint32_t cur[];          // [nC] counts, then cursors
+            int N, int K, int nC, int par) {
+  extern __shared__ uint32_t cur[];          // [par ? 16 : 1][nC] counts, then cursors
   __shared__ uint32_t wtot[16];
-  const int bg = blockIdx.x, tid = threadIdx.x;
+  const int bg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nw = par ? 16 : 1;
   const int32_t* sg = sel + (long long)bg * N * K;
   uint32_t* og = off + (long long)bg * (nC + 1);
   uint32_t* eg = ent + (long long)bg * N * K;
-  for (int c = tid; c < nC; c += 1024) cur[c] = 0;
+  for (int c = tid; c < nw * nC; c += 1024) cur[c] = 0;
   __syncthreads();
-  for (long long t = tid; t < (long long)N * K; t += 1024) {
-    const int c = sg[t];
-    if (c >= 0 && c < nC) atomicAdd(&cur[c], 1u);
+  // this wavefront's query range (par)
+  const int qa = par ? (int)((long long)N * wv / 16) : 0;
+  const int qz = par ? (int)((long long)N * (wv + 1) / 16) : 0;
+  if (par) {
+    uint32_t* cw = cur + (size_t)wv * nC;
+    for (long long t = (long long)qa * K + lane; t < (long long)qz * K; t += 64) {
+      const int c = sg[t];
+      if (c >= 0 && c < nC) atomicAdd(&cw[c], 1u);
+    }
+  } else {
+    for (long long t = tid; t < (long long)N * K; t += 1024) {
+      const int c = sg[t];
+      if (c >= 0 && c < nC) atomicAdd(&cur[c], 1u);
+    }
   }
   __syncthreads();
-  // exclusive scan of the counts in chunks of 1024
+  // exclusive scan of the per-chunk totals in chunks of 1024
   uint32_t carry = 0;
   for (int base = 0; base < nC; base += 1024) {
     const int c = base + tid;
-    const uint32_t v = (c < nC) ? cur[c] : 0u;
+    uint32_t v = 0u;
+    if (c < nC)
+      for (int w = 0; w < nw; ++w) v += cur[(size_t)w * nC + c];
     uint32_t x = v;
-    const int lane = tid & 63, w = tid >> 6;
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
       const uint32_t y = __shfl_up(x, m, 64);
       if (lane >= m) x += y;
     }
-    if (lane == 63) wtot[w] = x;
+    if (lane == 63) wtot[wv] = x;
     __syncthreads();
     uint32_t before = carry;
-    for (int u = 0; u < w; ++u) before += wtot[u];
+    for (int u = 0; u < wv; ++u) before += wtot[u];
     uint32_t all = carry;
     for (int u = 0; u < 16; ++u) all += wtot[u];
     __syncthreads();
     if (c < nC) {
-      const uint32_t e = before + x - v;
-      cur[c] = e;
+      uint32_t e = before + x - v;
       og[c] = e;
+      for (int w = 0; w < nw; ++w) {         // cursor of wavefront w in chunk c
+        const uint32_t n = cur[(size_t)w * nC + c];
+        cur[(size_t)w * nC + c] = e;
+        e += n;
+      }
     }
     carry = all;
     __syncthreads();
   }
   if (tid == 0) og[nC] = carry;
   __syncthreads();
-  // stable scatter in query order by one wavefront (its LDS atomics are
-  // processed in issue order; a query's slots hold distinct chunks)
-  if (tid < 64) {
-    for (int i = 0; i < N; ++i) {
-      for (int s2 = tid; s2 < K; s2 += 64) {
+  if (par || wv == 0) {
+    uint32_t* cw = cur + (size_t)(par ? wv : 0) * nC;
+    const int i0 = par ? qa : 0, i1 = par ? qz : N;
+    for (int i = i0; i < i1; ++i) {
+      for (int s2 = lane; s2 < K; s2 += 64) {
         const int c = sg[(long long)i * K + s2];
         if (c >= 0 && c < nC) {
-          const uint32_t pos = atomicAdd(&cur[c], 1u);
+          const uint32_t pos = atomicAdd(&cw[c], 1u);
           eg[pos] = ((uint32_t)i << 8) | (uint32_t)s2;
         }
       }
@@ -651,10 +676,11 @@ template <typename T> struct ColStage { static constexpr int NB = (sizeof(T) == 
 
 // bytes of the column kernel's staging area (also the summary backward's
 // scratch of one d-row of doubles per wavefront, used after the contributions)
-template <typename T>
+// (the summary-only variant stages no rows)
+template <typename T, bool SUMONLY>
 __host__ __device__ inline size_t col_stage_bytes(int d, int S) {
   (void)S;
-  const size_t st = (size_t)2 * 3 * ColStage<T>::NB * d * sizeof(T);
+  const size_t st = SUMONLY ? 0 : (size_t)2 * 3 * ColStage<T>::NB * d * sizeof(T);
   const size_t sc = (size_t)(CT / 64) * d * sizeof(double);
   return ((st > sc ? st : sc) + 15) & ~(size_t)15;
 }
@@ -695,7 +721,7 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
   // summary backward below subtracts nearly equal terms.
   T* stg = reinterpret_cast<T*>(smc);
   double* tmp = reinterpret_cast<double*>(smc);
-  double* dks = reinterpret_cast<double*>(reinterpret_cast<char*>(smc) + col_stage_bytes<T>(d, S));
+  double* dks = reinterpret_cast<double*>(reinterpret_cast<char*>(smc) + col_stage_bytes<T, SUMONLY>(d, S));
   double* dbs = dks + G * d;                         // [G]
   double* redd = dbs + G;                            // [8]
   float* red = reinterpret_cast<float*>(redd + 8);   // [8]
@@ -725,6 +751,13 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
   double dka[8], dba[8];
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) { dka[rr] = 0.0; dba[rr] = 0.0; }
+  // summary-only variant: wavefront w takes contributions 64 w .. 64 w + 63 of
+  // each batch, lane the elements 2 lane, 2 lane + 1; the eight wavefronts'
+  // sums meet in dks / dbs in order after the contributions
+  const int wvs = tid >> 6, el = 2 * (tid & 63);
+  double sa[8][2], sb[8];
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr) { sa[rr][0] = 0.0; sa[rr][1] = 0.0; sb[rr] = 0.0; }
 
   const bool summ = c < nC;
   const uint32_t p0 = summ ? off[bg * (nC + 1) + c] : 0u;
@@ -763,6 +796,43 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
       }
     }
     __syncthreads();
+    if constexpr (SUMONLY) {
+      static_assert(sizeof(T) == 2, "the summary-only variant reads bf16 pairs");
+      const int u0 = 64 * wvs, u1 = min(nb, u0 + 64);
+      for (int ub = u0; ub < u1; ub += 8) {          // eight rows in flight
+        uint32_t rv[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int u = ub + x;
+          rv[x] = 0u;
+          if (u < u1 && el < d) {
+            const int dd = di[u];
+            rv[x] = *reinterpret_cast<const uint32_t*>(
+                qr + ((hb + (dd & 15)) * N + (dd >> 4)) * (long long)d + el);
+          }
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int u = ub + x;
+          if (u < u1) {
+            const int r = di[u] & 15;
+            const double xt = (double)dsx[u * 4 + 3];
+            const double tx = (double)tau * xt;
+            const double h0 = (double)__uint_as_float(rv[x] << 16);
+            const double h1 = (double)__uint_as_float(rv[x] & 0xffff0000u);
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) {
+              if (rr == r) {
+                sa[rr][0] = fma(tx, h0, sa[rr][0]);
+                sa[rr][1] = fma(tx, h1, sa[rr][1]);
+                sb[rr] += xt;
+              }
+            }
+          }
+        }
+      }
+      continue;
+    }
     // the rows of sub-batch sb (NB contributions) are loaded into registers
     // while sub-batch sb - 1 is applied from LDS, then stored to the other
     // buffer.  Thread tid takes 16-byte piece tid % prow of contribution
@@ -778,10 +848,8 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
         const int dd = di[u];
         const int i = (dd >> 4) & 0x7ffffff, r = dd & 15;
         const long long o = ((hb + r) * N + i) * (long long)d + spart * VE;
-        if (!SUMONLY) {
-          pv0 = *reinterpret_cast<const uint4*>(q + o);
-          pv1 = *reinterpret_cast<const uint4*>(dout + o);
-        }
+        pv0 = *reinterpret_cast<const uint4*>(q + o);
+        pv1 = *reinterpret_cast<const uint4*>(dout + o);
         pv2 = *reinterpret_cast<const uint4*>(qr + o);
       }
     };
@@ -795,21 +863,6 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
     };
     auto apply = [&](int u, int buf) __attribute__((always_inline)) {
       const int ul = u % NB;
-      if (SUMONLY) {
-        if ((u & 3) == eq4 && ea < d) {
-          const int r = di[u] & 15;
-          const double hv = (double)Elt<T>::ld(stg + (((size_t)buf * 3 + 2) * NB + ul) * d + ea);
-          const double xt = (double)dsx[u * 4 + 3];
-#pragma unroll
-          for (int rr = 0; rr < 8; ++rr) {
-            if (rr == r) {
-              dka[rr] = fma((double)tau * xt, hv, dka[rr]);
-              dba[rr] += xt;
-            }
-          }
-        }
-        return;
-      }
       float qv[CE], dv2[CE];
       load_slice16<T>(stg + (((size_t)buf * 3 + 0) * NB + ul) * d + e0, DQ, qv);
       load_slice16<T>(stg + (((size_t)buf * 3 + 1) * NB + ul) * d + e0, DQ, dv2);
@@ -869,17 +922,35 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
     }
   }
   __syncthreads();
-  for (int p4 = 0; p4 < 4; ++p4) {                   // the quarters of dk', db', in order
-    if (eq4 == p4 && ea < d) {
+  if constexpr (SUMONLY) {
+    for (int w = 0; w < CT / 64; ++w) {              // the wavefronts' sums, in order
+      if (wvs == w) {
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        if (rr < G) {
-          dks[rr * d + ea] += dka[rr];
-          if (ea == 0) dbs[rr] += dba[rr];
+        for (int rr = 0; rr < 8; ++rr) {
+          if (rr < G) {
+            if (el < d) {
+              dks[rr * d + el] += sa[rr][0];
+              dks[rr * d + el + 1] += sa[rr][1];
+            }
+            if (el == 0) dbs[rr] += sb[rr];
+          }
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
+  } else {
+    for (int p4 = 0; p4 < 4; ++p4) {                 // the quarters of dk', db', in order
+      if (eq4 == p4 && ea < d) {
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+          if (rr < G) {
+            dks[rr * d + ea] += dka[rr];
+            if (ea == 0) dbs[rr] += dba[rr];
+          }
+        }
+      }
+      __syncthreads();
+    }
   }
   // summaries of the chunk (one per query head of the group)
   if (summ) {
@@ -986,17 +1057,21 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
                                 float* dk, float* dv, float* dlm, const HilsBwdBufs& wb,
                                 hipStream_t st) {
   const float tau = (float)s.tau;
-  const size_t lshm = sizeof(uint32_t) * (size_t)(s.nC > 0 ? s.nC : 1);
+  // per-wavefront counters while they fit 128 KB of LDS
+  const int lpar = (size_t)16 * s.nC * sizeof(uint32_t) <= 128 * 1024;
+  const size_t lshm = sizeof(uint32_t) * (size_t)(lpar ? 16 : 1) * (size_t)(s.nC > 0 ? s.nC : 1);
   hils_allow_lds((const void*)k_bwd_lists, lshm);
   { HilsProfScope ps_("k_bwd_lists", st);
     hipLaunchKernelGGL(k_bwd_lists, dim3((unsigned)(s.B * s.Hkv)), dim3(1024), lshm, st, sel,
-                       wb.off, wb.ent, s.N, s.K, s.nC); }
+                       wb.off, wb.ent, s.N, s.K, s.nC, lpar); }
   // the all-keys row kernel when every attended key's logit fits 64 KB of LDS
   const bool all_keys = bwd_rows2_lds(s) <= 65536;
   const size_t rshm = all_keys ? bwd_rows2_lds(s) : hils_bwd_rows_lds(s);
-  const size_t cshm = (s.dtype == 0 ? col_stage_bytes<bf16_t>(s.d, s.S) : col_stage_bytes<float>(s.d, s.S)) +
-                      sizeof(double) * ((size_t)s.G * s.d + s.G + 8) + sizeof(float) * 8 +
-                      (size_t)CBATCH * (2 * sizeof(int) + 4 * sizeof(float));
+  const size_t ctail = sizeof(double) * ((size_t)s.G * s.d + s.G + 8) + sizeof(float) * 8 +
+                       (size_t)CBATCH * (2 * sizeof(int) + 4 * sizeof(float));
+  const size_t cshm = (s.dtype == 0 ? col_stage_bytes<bf16_t, false>(s.d, s.S)
+                                    : col_stage_bytes<float, false>(s.d, s.S)) + ctail;
+  const size_t sshm = col_stage_bytes<bf16_t, true>(s.d, s.S) + ctail;
   const int sep = dqr != nullptr;
   if (s.dtype == 0) {
     auto fr = all_keys ? k_bwd_rows2<bf16_t> : k_bwd_rows<bf16_t>;
@@ -1006,10 +1081,10 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
       hipError_t e = hils_launch_backward_mf(s, q, qr, k, v, dout, sel, ksum, bsum, dq, dqr, dk, dv,
                                              wb, st);
       if (e != hipSuccess || s.nC <= 0) return e;
-      hils_allow_lds((const void*)k_bwd_cols<bf16_t, true>, cshm);
+      hils_allow_lds((const void*)k_bwd_cols<bf16_t, true>, sshm);
       HilsProfScope ps_("k_bwd_summ", st);
       hipLaunchKernelGGL((k_bwd_cols<bf16_t, true>), dim3((unsigned)((long long)s.B * s.Hkv * s.nC)), dim3(CT),
-                         cshm, st, (const bf16_t*)q, (const bf16_t*)qr, (const bf16_t*)k,
+                         sshm, st, (const bf16_t*)q, (const bf16_t*)qr, (const bf16_t*)k,
                          (const bf16_t*)v, (const bf16_t*)lm, (const bf16_t*)dout, wb.off, wb.ent,
                          wb.pstat, wb.wstat, dk, dv, dlm, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K,
                          s.nC, s.nC, tau, s.mode);
