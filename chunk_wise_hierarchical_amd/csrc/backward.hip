@@ -685,7 +685,7 @@ __host__ __device__ inline size_t col_stage_bytes(int d, int S) {
   return ((st > sc ? st : sc) + 15) & ~(size_t)15;
 }
 
-template <typename T, bool SUMONLY>
+template <typename T, bool SUMONLY, int GT = 0>
 __global__ void __launch_bounds__(CT)
 k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restrict__ k,
            const T* __restrict__ v, const T* __restrict__ lm, const T* __restrict__ dout,
@@ -798,11 +798,13 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
     __syncthreads();
     if constexpr (SUMONLY) {
       static_assert(sizeof(T) == 2, "the summary-only variant reads bf16 pairs");
+      // sixteen rows in flight; with the group size GT fixed at compile time
+      // (u0 and ub are multiples of it) contribution ub + x has head x % GT
       const int u0 = 64 * wvs, u1 = min(nb, u0 + 64);
-      for (int ub = u0; ub < u1; ub += 8) {          // eight rows in flight
-        uint32_t rv[8];
+      for (int ub = u0; ub < u1; ub += 16) {
+        uint32_t rv[16];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
+        for (int x = 0; x < 16; ++x) {
           const int u = ub + x;
           rv[x] = 0u;
           if (u < u1 && el < d) {
@@ -812,20 +814,27 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
           }
         }
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
+        for (int x = 0; x < 16; ++x) {
           const int u = ub + x;
           if (u < u1) {
-            const int r = di[u] & 15;
             const double xt = (double)dsx[u * 4 + 3];
             const double tx = (double)tau * xt;
             const double h0 = (double)__uint_as_float(rv[x] << 16);
             const double h1 = (double)__uint_as_float(rv[x] & 0xffff0000u);
+            if constexpr (GT > 0) {
+              const int rr = x % GT;
+              sa[rr][0] = fma(tx, h0, sa[rr][0]);
+              sa[rr][1] = fma(tx, h1, sa[rr][1]);
+              sb[rr] += xt;
+            } else {
+              const int r = di[u] & 15;
 #pragma unroll
-            for (int rr = 0; rr < 8; ++rr) {
-              if (rr == r) {
-                sa[rr][0] = fma(tx, h0, sa[rr][0]);
-                sa[rr][1] = fma(tx, h1, sa[rr][1]);
-                sb[rr] += xt;
+              for (int rr = 0; rr < 8; ++rr) {
+                if (rr == r) {
+                  sa[rr][0] = fma(tx, h0, sa[rr][0]);
+                  sa[rr][1] = fma(tx, h1, sa[rr][1]);
+                  sb[rr] += xt;
+                }
               }
             }
           }
@@ -1081,9 +1090,13 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
       hipError_t e = hils_launch_backward_mf(s, q, qr, k, v, dout, sel, ksum, bsum, dq, dqr, dk, dv,
                                              wb, st);
       if (e != hipSuccess || s.nC <= 0) return e;
-      hils_allow_lds((const void*)k_bwd_cols<bf16_t, true>, sshm);
+      // the group size as a template argument where it is a power of two
+      auto fs = s.G == 1 ? k_bwd_cols<bf16_t, true, 1> : s.G == 2 ? k_bwd_cols<bf16_t, true, 2>
+              : s.G == 4 ? k_bwd_cols<bf16_t, true, 4> : s.G == 8 ? k_bwd_cols<bf16_t, true, 8>
+              : k_bwd_cols<bf16_t, true, 0>;
+      hils_allow_lds((const void*)fs, sshm);
       HilsProfScope ps_("k_bwd_summ", st);
-      hipLaunchKernelGGL((k_bwd_cols<bf16_t, true>), dim3((unsigned)((long long)s.B * s.Hkv * s.nC)), dim3(CT),
+      hipLaunchKernelGGL(fs, dim3((unsigned)((long long)s.B * s.Hkv * s.nC)), dim3(CT),
                          sshm, st, (const bf16_t*)q, (const bf16_t*)qr, (const bf16_t*)k,
                          (const bf16_t*)v, (const bf16_t*)lm, (const bf16_t*)dout, wb.off, wb.ent,
                          wb.pstat, wb.wstat, dk, dv, dlm, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K,
