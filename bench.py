@@ -414,18 +414,22 @@ def backward_bench(torch, hils, _lib, wb, steps, log):
     ms, _ = timed(torch, _lib, step, steps, profile=False)
     _, kt = timed(torch, _lib, step, steps, profile=True)
     # algorithmic FLOPs: per attended (query, head, token) the five products of an
-    # attention backward (logit and dout.v recompute, dq, dk, dv): 10 d
+    # attention backward (logit and dout.v recompute, dq, dk, dv): 10 d.  For bf16
+    # with d in {64, 128} and S a multiple of 16 all five run on the matrix cores
+    # (priced against the bf16 MFMA peak), else on the fp32 vector ALU.
     n, win = _geometry(wb.N, wb.W, wb.S)
     att = float((np.minimum(wb.K, n) * wb.S + win).sum()) * wb.Hq * wb.B
     flops = 10.0 * wb.d * att
     achieved = flops / (ms * 1e-3) / 1e12
+    on_mfma = wb.dtype == "bf16" and wb.d in (64, 128) and wb.S % 16 == 0
+    bound, peak = ("mfma", PEAK_BF16_TFLOPS) if on_mfma else ("alu", PEAK_FP32_VALU_TFLOPS)
     log(f"backward {wb.name}: {ms:.2f} ms/step; kernels {json.dumps(kt)}")
     del xb, sel, ks, bs, dout, ws
     return {"workload": wb.name, "ms_per_step": ms, "tokens_per_s": wb.B * wb.N / (ms * 1e-3),
             "config": {"B": wb.B, "N": wb.N, "Hq": wb.Hq, "Hkv": wb.Hkv, "d": wb.d, "S": wb.S,
                        "W": wb.W, "K": wb.K},
-            "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
-                         "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
+            "roofline": {"bound": bound, "achieved": achieved, "peak": peak,
+                         "unit": "TFLOP/s", "frac": achieved / peak,
                          "algorithmic_flops_per_step": flops},
             "kernels": kt}
 

@@ -35,9 +35,10 @@
 // transposed (the operand of dV^T = dOut^T P and dK^T = Q^T dS, reduced over
 // the tile's queries); double-buffered, the next tile's rows load while the
 // current one is computed.  S and dP take bf16 MFMA with exact products and
-// fp32 sums.  P and tau dS are fp32 and enter their products as a bf16 pair
-// hi + lo (hi = bf16(x), lo = bf16(x - hi), within 2^-18 of x), two MFMAs
-// each, so the gradients keep fp32 accuracy.  The MFMA output layout of S
+// fp32 sums.  P and tau dS are fp32 and enter their products as bf16 sums
+// hi + lo (hi = bf16(x), lo = bf16(x - hi), within 2^-18 of x) in dv and dk,
+// and hi + mid + lo (within 2^-27) in dq, whose error gathers over all of a
+// query's keys: one MFMA per term, so the gradients keep fp32 accuracy.  The MFMA output layout of S
 // (lane l: key l % 16, queries 4 (l / 16) + r of each 16-query half) is the
 // B-operand layout of the second products once the tile's query positions are
 // permuted (position 8 g + t <-> query 16 (t / 4) + 4 g + t % 4); the
@@ -68,8 +69,12 @@ struct MfCol {
   static constexpr int TILE = ROWS + (PASS ? 2 * D * TS : 0);   // + q^T, dout^T
   static constexpr int NPC = QT * (D / 8) / MT;    // 16-byte pieces per thread and tensor
   static constexpr int DSS = 72;                   // dS tile: row stride (bf16), 64 keys + pad
+  static constexpr int DSN = 3 * QT * DSS;         // dS tile: three bf16 planes (hi, mid, lo)
+  // the dS tile overlays the row-major tiles of the current buffer when it
+  // fits there (d = 128), else it has a region of its own after both buffers
+  static constexpr bool DS_OVER = DSN <= ROWS;
+  static constexpr int EXTRA = (PASS && !DS_OVER) ? DSN : 0;
   static constexpr int DB = D / 64;                // 16-column blocks of dq per wavefront
-  static_assert(2 * QT * DSS <= ROWS, "the dS tile overlays the row-major tiles");
 };
 
 // position of tile query q in the transposed tiles (see above)
@@ -103,7 +108,7 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   using L = MfCol<D, PASS>;
   extern __shared__ __align__(16) unsigned char smm[];
   bf16_t* tiles = reinterpret_cast<bf16_t*>(smm);                        // [2][TILE]
-  int* did = reinterpret_cast<int*>(smm + sizeof(bf16_t) * 2 * L::TILE);  // [CB] i << 4 | head
+  int* did = reinterpret_cast<int*>(smm + sizeof(bf16_t) * (2 * L::TILE + L::EXTRA));   // [CB] i << 4 | head
   int* dslot = did + CB;                                                  // [CB] slot, K + window chunk
   int2* dlim = reinterpret_cast<int2*>(dslot + CB);                       // [CB] attended keys lo..hi
   float4* dcf = reinterpret_cast<float4*>(dlim + CB);   // [CB] alpha, lse, g, E; stats: [4][QT] partials
@@ -285,9 +290,9 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     bf16_t* tb = tiles + (size_t)buf * L::TILE;
     const bf16_t* tqt = tb + L::ROWS;
     const bf16_t* tot = tqt + D * L::TS;
-    uint32_t ph[4], pl[4], dh[4], dl[4];
+    uint32_t ph[4], pl[4], dh[4], dl[4], d3[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) { ph[t] = 0u; pl[t] = 0u; dh[t] = 0u; dl[t] = 0u; }
+    for (int t = 0; t < 4; ++t) { ph[t] = 0u; pl[t] = 0u; dh[t] = 0u; dl[t] = 0u; d3[t] = 0u; }
     if (kwave) {
       f32x4_t sc[2], dp[2];
       scores(tb, sc, dp);
@@ -313,12 +318,16 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         pl[t] = pack_bf16x2(ap[2 * t] - bf_lo(ph[t]), ap[2 * t + 1] - bf_hi(ph[t]));
         dh[t] = pack_bf16x2(ds[2 * t], ds[2 * t + 1]);
         dl[t] = pack_bf16x2(ds[2 * t] - bf_lo(dh[t]), ds[2 * t + 1] - bf_hi(dh[t]));
+        // third term for dq (its error is summed over all of a query's keys)
+        d3[t] = pack_bf16x2(ds[2 * t] - bf_lo(dh[t]) - bf_lo(dl[t]),
+                            ds[2 * t + 1] - bf_hi(dh[t]) - bf_hi(dl[t]));
       }
     }
     __syncthreads();                                 // every wavefront has read the row-major tiles
-    // dS (hi, lo) over the row-major area: [2][QT][DSS], key-contiguous
+    // dS (hi, mid, lo): [3][QT][DSS], key-contiguous
+    bf16_t* dst = L::DS_OVER ? tb : tiles + 2 * L::TILE;
     {
-      unsigned short* dsl = reinterpret_cast<unsigned short*>(tb);
+      unsigned short* dsl = reinterpret_cast<unsigned short*>(dst);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -326,6 +335,7 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           const int e = 2 * t + x, qq = 16 * (e >> 2) + 4 * g4 + (e & 3);
           dsl[qq * L::DSS + kk] = (unsigned short)(dh[t] >> (16 * x));
           dsl[(QT + qq) * L::DSS + kk] = (unsigned short)(dl[t] >> (16 * x));
+          dsl[(2 * QT + qq) * L::DSS + kk] = (unsigned short)(d3[t] >> (16 * x));
         }
       }
     }
@@ -346,7 +356,7 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }
     __syncthreads();                                 // the dS tile is complete
     // dq^T[16 db + 4 g4 + r][query 16 qb + l16] = sum over the chunk's keys
-    const bf16_t* dsl = tb;
+    const bf16_t* dsl = dst;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int u = tl * QT + 16 * qb + l16;
@@ -355,11 +365,12 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         const int id = did[u];
         prow = ((hb + (id & 15)) * N + (id >> 4)) * (long long)NS + dslot[u];
       }
-      bf16x8_t bh[2], bl[2];
+      bf16x8_t bh[2], bl[2], b3[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bh[ks] = ld_bf16x8(dsl + (16 * qb + l16) * L::DSS + 32 * ks + 8 * g4);
         bl[ks] = ld_bf16x8(dsl + (QT + 16 * qb + l16) * L::DSS + 32 * ks + 8 * g4);
+        b3[ks] = ld_bf16x8(dsl + (2 * QT + 16 * qb + l16) * L::DSS + 32 * ks + 8 * g4);
       }
 #pragma unroll
       for (int db = 0; db < L::DB; ++db) {
@@ -368,6 +379,7 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         for (int ks = 0; ks < 2; ++ks) {
           a = mfma16(ktf[db][ks], bh[ks], a);
           a = mfma16(ktf[db][ks], bl[ks], a);
+          a = mfma16(ktf[db][ks], b3[ks], a);
         }
         if (u < nb)
           *reinterpret_cast<float4*>(dqp + prow * D + 16 * (L::DB * wv + db) + 4 * g4) =
@@ -440,7 +452,7 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
 template <int D, int PASS>
 size_t mf_lds() {
-  return sizeof(bf16_t) * 2 * MfCol<D, PASS>::TILE +
+  return sizeof(bf16_t) * (2 * MfCol<D, PASS>::TILE + MfCol<D, PASS>::EXTRA) +
          (size_t)CB * (2 * sizeof(int) + sizeof(int2) + sizeof(float4));
 }
 
