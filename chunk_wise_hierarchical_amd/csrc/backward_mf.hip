@@ -644,16 +644,20 @@ hipError_t launch_mf(const HilsShape& s, const void* q, const void* qr, const vo
 
 }  // namespace
 
-bool hils_bwd_mf_ok(const HilsShape& s) {
-  return s.dtype == 0 && (s.d == 64 || s.d == 128) && s.S % 16 == 0 && s.S <= 64 && s.G <= 16 &&
-         s.K <= 128 && s.N < (1 << 24);
-}
-
 size_t hils_bwd_mf_wpart_bytes(const HilsShape& s) {
   return (size_t)s.B * s.Hq * s.N * s.nwin * 16;
 }
 size_t hils_bwd_mf_dqp_bytes(const HilsShape& s) {
   return (size_t)s.B * s.Hq * s.N * (s.K + s.nwin) * s.d * 4;
+}
+
+// the dq partials grow with N (K + nwin) Hq d; past 32 GiB (about 20K query
+// rows of 32 heads at K = 64, W = 2048) the vector-ALU kernels run instead
+constexpr size_t kMaxDqPartialBytes = (size_t)32 << 30;
+
+bool hils_bwd_mf_ok(const HilsShape& s) {
+  return s.dtype == 0 && (s.d == 64 || s.d == 128) && s.S % 16 == 0 && s.S <= 64 && s.G <= 16 &&
+         s.K <= 128 && s.N < (1 << 24) && hils_bwd_mf_dqp_bytes(s) <= kMaxDqPartialBytes;
 }
 
 hipError_t hils_launch_backward_mf(const HilsShape& s, const void* q, const void* qr, const void* k,

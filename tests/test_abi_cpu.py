@@ -169,6 +169,24 @@ def test_backward_head_dim_granularity(L):
     assert ok(ctypes.byref(_cfg(d=16, dtype=1))) == 0
 
 
+def test_backward_workspace_holds_the_dq_partials(L):
+    # the matrix-core backward (bf16, d in {64, 128}, S % 16 == 0) keeps one fp32
+    # dq partial row per (query, head, selected slot or window chunk) and the
+    # window partials; fp32 inputs take the vector-ALU kernels without them
+    ok = L.hils_prefill_backward_workspace_bytes
+    c = _cfg(N=1024, W=256, K=8)
+    nwin = -(-(256 + 64 - 1) // 64)
+    parts = 1 * 8 * 1024 * (8 + nwin) * 128 * 4 + 1 * 8 * 1024 * nwin * 16
+    bf16, f32 = ok(ctypes.byref(c)), ok(ctypes.byref(_cfg(N=1024, W=256, K=8, dtype=1)))
+    assert bf16 >= parts
+    # fp32 summaries are twice the size; everything else is shared
+    assert 0 < f32 < bf16 - parts + 1 * 8 * 16 * 128 * 2 + 4096
+    # past 32 GiB of dq partials the vector-ALU kernels run, without them
+    big = _cfg(N=1 << 20, Hq=32, Hkv=8, W=2048, K=64)
+    big_parts = (1 << 20) * 32 * (64 + 33) * 128 * 4
+    assert 0 < ok(ctypes.byref(big)) < big_parts
+
+
 def test_decode_rejects_batches_beyond_the_scoring_grid(L):
     # the decode scoring grid holds (sequence, query head) in its y dimension:
     # B * Hq = 8192 * 8 is one past its limit of 65535
