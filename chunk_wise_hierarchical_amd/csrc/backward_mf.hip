@@ -26,6 +26,10 @@
 //   k_bwd_mf<D, 1> (grads)  per chunk: dk, dv of its tokens, and one dq
 //                           partial per contribution;
 //   k_bwd_dq_reduce         per (query, head): dq = sum of its partials.
+// The four run per query slice (one for most shapes) so that the partials fit
+// a bounded workspace: a chunk pass then takes the contributions whose query
+// lies in the slice, and dk, dv are written by the slice holding the chunk's
+// first token and added to by the later ones.
 //
 // Layout of the chunk passes: one workgroup per (chunk, sequence, KV group),
 // 4 wavefronts; wavefront w owns keys 16w .. 16w + 15 and keeps their K and V
@@ -46,6 +50,8 @@
 // dS through LDS (key-contiguous per query) and K^T fragments built once per
 // workgroup.  No atomics: every output element is written by one workgroup
 // or wavefront, in a fixed order.
+#include <cstdlib>
+
 #include "fast_common.h"
 #include "hils_internal.h"
 #include "hils_bwd.h"
@@ -103,8 +109,9 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
          const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
          const uint32_t* __restrict__ off, const uint32_t* __restrict__ ent,
          float* __restrict__ pstat, const float* __restrict__ wstat, float* __restrict__ wpart,
-         float* __restrict__ dqp, float* __restrict__ dk, float* __restrict__ dv, int Hq, int Hkv,
-         int G, int N, int S, int W, int K, int nC, int nCc, int nwin, float tau) {
+         float* __restrict__ dqp, float* __restrict__ dk, float* __restrict__ dv,
+         const uint32_t* __restrict__ srng, int Hq, int Hkv, int G, int N, int S, int W, int K,
+         int nC, int nCc, int nwin, int qa, int qz, int QS, float tau) {
   using L = MfCol<D, PASS>;
   extern __shared__ __align__(16) unsigned char smm[];
   bf16_t* tiles = reinterpret_cast<bf16_t*>(smm);                        // [2][TILE]
@@ -168,13 +175,20 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }
   }
 
+  // contributions of the query slice [qa, qz): the slice's part of the
+  // chunk's list (srng, or the whole list for one slice) and its window
+  // queries
   const bool summ = c < nC;
-  const uint32_t p0 = summ ? off[bg * (nC + 1) + c] : 0u;
-  const uint32_t p1 = summ ? off[bg * (nC + 1) + c + 1] : 0u;
+  const long long lc = bg * (long long)nC + c;
+  const uint32_t p0 = !summ ? 0u : srng ? srng[2 * lc] : off[bg * (nC + 1) + c];
+  const uint32_t p1 = !summ ? 0u : srng ? srng[2 * lc + 1] : off[bg * (nC + 1) + c + 1];
   const long long nsel = (long long)(p1 - p0) * G;                 // (pair, head)
-  const int i1 = min(N, (c + 1) * S + W - 1);
-  const long long nwq = (long long)(i1 - j0) * G;                 // window (query, head)
+  const int wa = max(j0, qa), wz = min(min(N, (c + 1) * S + W - 1), qz);
+  const long long nwq = (long long)max(0, wz - wa) * G;          // window (query, head)
   const uint32_t* eg = ent + bg * (long long)N * K;
+  // dk, dv: written by the slice holding the chunk's first token (its first
+  // contribution), added to by the later ones
+  const bool accum = j0 < qa;
 
   // staging: piece pc = tid + MT m of a tile: query pc % QT, 16-byte part pc / QT
   uint4 pq[L::NPC], po[L::NPC];
@@ -278,7 +292,7 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           ps[1] = M + __logf(Z);
           ps[2] = Y / Z;
         } else {
-          *reinterpret_cast<float4*>(wpart + (((hb + r) * N + i) * (long long)nwin + (slot - K)) * 4) =
+          *reinterpret_cast<float4*>(wpart + (((hb + r) * QS + (i - qa)) * (long long)nwin + (slot - K)) * 4) =
               make_float4(M, Z, Y, 0.0f);
         }
       }
@@ -363,7 +377,7 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       long long prow = 0;
       if (u < nb) {
         const int id = did[u];
-        prow = ((hb + (id & 15)) * N + (id >> 4)) * (long long)NS + dslot[u];
+        prow = ((hb + (id & 15)) * QS + ((id >> 4) - qa)) * (long long)NS + dslot[u];
       }
       bf16x8_t bh[2], bl[2], b3[2];
 #pragma unroll
@@ -410,7 +424,7 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
           }
         } else {
           const long long widx = idx - nsel;
-          const int i = j0 + (int)(widx / G), r = (int)(widx % G);
+          const int i = wa + (int)(widx / G), r = (int)(widx % G);
           const int ws = (int)window_start(i, W, S);
           id = (i << 4) | r;
           slot = K + (c - ws / S);
@@ -442,10 +456,17 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const long long ro = (bg * (long long)N + j0 + kk) * D + 4 * g4;
 #pragma unroll
     for (int b2 = 0; b2 < D / 16; ++b2) {
-      *reinterpret_cast<float4*>(dv + ro + 16 * b2) =
-          make_float4(accv[b2][0], accv[b2][1], accv[b2][2], accv[b2][3]);
-      *reinterpret_cast<float4*>(dk + ro + 16 * b2) =
-          make_float4(acck[b2][0], acck[b2][1], acck[b2][2], acck[b2][3]);
+      float4* pv = reinterpret_cast<float4*>(dv + ro + 16 * b2);
+      float4* pk = reinterpret_cast<float4*>(dk + ro + 16 * b2);
+      float4 av = make_float4(accv[b2][0], accv[b2][1], accv[b2][2], accv[b2][3]);
+      float4 ak = make_float4(acck[b2][0], acck[b2][1], acck[b2][2], acck[b2][3]);
+      if (accum) {
+        const float4 ov = *pv, ok = *pk;
+        av = make_float4(ov.x + av.x, ov.y + av.y, ov.z + av.z, ov.w + av.w);
+        ak = make_float4(ok.x + ak.x, ok.y + ak.y, ok.z + ak.z, ok.w + ak.w);
+      }
+      *pv = av;
+      *pk = ak;
     }
   }
 }
@@ -465,19 +486,21 @@ k_bwd_rowstat(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
               const float* __restrict__ bsum, const int32_t* __restrict__ sel,
               float* __restrict__ pstat, float* __restrict__ wstat, const float* __restrict__ wpart,
               float* __restrict__ dqo, int Hq, int Hkv, int G, int N, int d, int S, int W, int K,
-              int nC, int nwin, long long nrows, float tau) {
+              int nC, int nwin, int qa, int QN, int QS, long long nrows, float tau) {
   extern __shared__ __align__(16) float smq[];       // [4][d] routing query rows
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const long long item = (long long)blockIdx.x * 4 + wv;   // (b, h, i)
+  const long long item = (long long)blockIdx.x * 4 + wv;   // (b, h, i - qa), slice rows
   if (item >= nrows) return;                         // whole wavefronts; no barriers below
-  const int i = (int)(item % N);
-  const long long bh = item / N;
+  const int i = qa + (int)(item % QN);
+  const long long bh = item / QN;
   const int h = (int)(bh % Hq);
   const long long b = bh / Hq;
   const int g = h / G, r = h - g * G;
   const long long row = (b * Hkv + g) * N + i;       // selection row
+  const long long arow = bh * N + i;                 // (b, h, i)
+  const long long srow = bh * QS + (i - qa);         // its row of the slice's partials
   float* qs = smq + wv * d;
-  for (int e = lane; e < d; e += 64) qs[e] = bf16_to_f32(qr[item * d + e]);
+  for (int e = lane; e < d; e += 64) qs[e] = bf16_to_f32(qr[arow * d + e]);
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   // selected chunks: lanes t and t + 64
   float sh[2], lt[2], gt[2];
@@ -516,7 +539,7 @@ k_bwd_rowstat(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   const int nw = i / S - ws / S + 1;
   float wm = -INFINITY, wz = 0.0f, wy = 0.0f;      // this lane's chunks, online
   for (int w = lane; w < nw; w += 64) {
-    const float4 p = *reinterpret_cast<const float4*>(wpart + (item * nwin + w) * 4);
+    const float4 p = *reinterpret_cast<const float4*>(wpart + (srow * nwin + w) * 4);
     if (p.x > wm) {
       const float f = __expf(wm - p.x);
       wz = fmaf(wz, f, p.y);
@@ -555,7 +578,7 @@ k_bwd_rowstat(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
           make_float4(at[m], lt[m], gt[m], dsh[m]);
   }
   if (lane == 0)
-    *reinterpret_cast<float4*>(wstat + item * 4) = make_float4(aw, lse_w, g_w, aw * (g_w - gbar));
+    *reinterpret_cast<float4*>(wstat + arow * 4) = make_float4(aw, lse_w, g_w, aw * (g_w - gbar));
   // routing query: tau sum_t (d s_hat_t) k'_t; lane takes elements 2 lane, 2 lane + 1
   float q0 = 0.0f, q1 = 0.0f;
   const int e = 2 * lane;
@@ -569,7 +592,7 @@ k_bwd_rowstat(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
       q1 = fmaf(x, bf_hi(kv), q1);
     }
   }
-  if (e < d) *reinterpret_cast<float2*>(dqo + item * d + e) = make_float2(tau * q0, tau * q1);
+  if (e < d) *reinterpret_cast<float2*>(dqo + arow * d + e) = make_float2(tau * q0, tau * q1);
 }
 
 // per (query, head): dq = (add ? dq : 0) + the partials of its selected
@@ -577,19 +600,20 @@ k_bwd_rowstat(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
 __global__ void __launch_bounds__(256)
 k_bwd_dq_reduce(const float* __restrict__ dqp, const int32_t* __restrict__ sel, float* __restrict__ dq,
                 int Hq, int Hkv, int G, int N, int d, int S, int W, int K, int nC, int nwin,
-                long long nrows, int add) {
+                int qa, int QN, int QS, long long nrows, int add) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const long long item = (long long)blockIdx.x * 4 + wv;
   if (item >= nrows) return;
   const int e = 2 * lane;
   if (e >= d) return;
-  const int i = (int)(item % N);
-  const long long bh = item / N;
+  const int i = qa + (int)(item % QN);
+  const long long bh = item / QN;
   const int h = (int)(bh % Hq);
   const long long b = bh / Hq;
   const long long row = (b * Hkv + h / G) * N + i;
-  const float* pp = dqp + item * (long long)(K + nwin) * d + e;
-  float2 acc = add ? *reinterpret_cast<const float2*>(dq + item * d + e) : make_float2(0.0f, 0.0f);
+  const long long arow = bh * N + i;
+  const float* pp = dqp + (bh * QS + (i - qa)) * (long long)(K + nwin) * d + e;
+  float2 acc = add ? *reinterpret_cast<const float2*>(dq + arow * d + e) : make_float2(0.0f, 0.0f);
   for (int t = 0; t < K; ++t) {
     const int c = sel[row * K + t];
     if (c < 0 || c >= nC) continue;
@@ -604,7 +628,32 @@ k_bwd_dq_reduce(const float* __restrict__ dqp, const int32_t* __restrict__ sel, 
     acc.x += x.x;
     acc.y += x.y;
   }
-  *reinterpret_cast<float2*>(dq + item * d + e) = acc;
+  *reinterpret_cast<float2*>(dq + arow * d + e) = acc;
+}
+
+// per (sequence, KV group, chunk with a summary): the part of the chunk's
+// query-ordered list whose queries lie in [qa, qz) (entries are i << 8 | slot)
+__global__ void __launch_bounds__(256)
+k_bwd_slice_ranges(const uint32_t* __restrict__ off, const uint32_t* __restrict__ ent,
+                   uint32_t* __restrict__ srng, int N, int K, int nC, long long nlists, int qa,
+                   int qz) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= nlists) return;
+  const long long bg = t / nC;
+  const int c = (int)(t % nC);
+  const uint32_t* eg = ent + bg * (long long)N * K;
+  const uint32_t p0 = off[bg * (nC + 1) + c], p1 = off[bg * (nC + 1) + c + 1];
+  auto lower = [&](uint32_t key) {
+    uint32_t lo = p0, hi = p1;
+    while (lo < hi) {
+      const uint32_t mid = lo + (hi - lo) / 2;
+      if (eg[mid] < key) lo = mid + 1;
+      else hi = mid;
+    }
+    return lo;
+  };
+  srng[2 * t] = lower((uint32_t)qa << 8);
+  srng[2 * t + 1] = lower((uint32_t)qz << 8);
 }
 
 template <int D>
@@ -613,51 +662,80 @@ hipError_t launch_mf(const HilsShape& s, const void* q, const void* qr, const vo
                      float* dq, float* dqr, float* dk, float* dv, const HilsBwdBufs& wb,
                      hipStream_t st) {
   const float tau = (float)s.tau;
-  const long long nblk = (long long)s.B * s.Hkv * s.nCc;
-  const long long nrows = (long long)s.B * s.Hq * s.N;
-  const unsigned rgrid = (unsigned)((nrows + 3) / 4);
+  const int QS = hils_bwd_mf_slice(s);
   const size_t sh0 = mf_lds<D, 0>(), sh1 = mf_lds<D, 1>();
   hils_allow_lds((const void*)k_bwd_mf<D, 0>, sh0);
   hils_allow_lds((const void*)k_bwd_mf<D, 1>, sh1);
-  { HilsProfScope ps_("k_bwd_stats", st);
-    hipLaunchKernelGGL((k_bwd_mf<D, 0>), dim3((unsigned)nblk), dim3(MT), sh0, st,
-                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout,
-                       wb.off, wb.ent, wb.pstat, wb.wstat, wb.wpart, wb.dqp, dk, dv, s.Hq, s.Hkv,
-                       s.G, s.N, s.S, s.W, s.K, s.nC, s.nCc, s.nwin, tau); }
-  // the routing query's gradient goes to dq_route, or to dq (then the
-  // partials are added to it)
-  { HilsProfScope ps_("k_bwd_rowstat", st);
-    hipLaunchKernelGGL(k_bwd_rowstat, dim3(rgrid), dim3(256), sizeof(float) * 4 * s.d, st,
-                       (const bf16_t*)qr, (const bf16_t*)ksum, bsum, sel, wb.pstat, wb.wstat,
-                       wb.wpart, dqr ? dqr : dq, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC,
-                       s.nwin, nrows, tau); }
-  { HilsProfScope ps_("k_bwd_cols", st);
-    hipLaunchKernelGGL((k_bwd_mf<D, 1>), dim3((unsigned)nblk), dim3(MT), sh1, st,
-                       (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout,
-                       wb.off, wb.ent, wb.pstat, wb.wstat, wb.wpart, wb.dqp, dk, dv, s.Hq, s.Hkv,
-                       s.G, s.N, s.S, s.W, s.K, s.nC, s.nCc, s.nwin, tau); }
-  { HilsProfScope ps_("k_bwd_dq", st);
-    hipLaunchKernelGGL(k_bwd_dq_reduce, dim3(rgrid), dim3(256), 0, st, wb.dqp, sel, dq, s.Hq,
-                       s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, s.nwin, nrows, dqr ? 0 : 1); }
+  for (int qa = 0; qa < s.N; qa += QS) {
+    const int qz = min(s.N, qa + QS), QN = qz - qa;
+    const uint32_t* srng = nullptr;
+    if (QS < s.N && s.nC > 0) {
+      const long long nl = (long long)s.B * s.Hkv * s.nC;
+      HilsProfScope ps_("k_bwd_slice_ranges", st);
+      hipLaunchKernelGGL(k_bwd_slice_ranges, dim3((unsigned)((nl + 255) / 256)), dim3(256), 0, st,
+                         wb.off, wb.ent, wb.srng, s.N, s.K, s.nC, nl, qa, qz);
+      srng = wb.srng;
+    }
+    // chunks with a token before qz (the others have no contribution yet)
+    const int ncs = min(s.nCc, (qz + s.S - 1) / s.S);
+    const long long nblk = (long long)s.B * s.Hkv * ncs;
+    const long long nrows = (long long)s.B * s.Hq * QN;
+    const unsigned rgrid = (unsigned)((nrows + 3) / 4);
+    { HilsProfScope ps_("k_bwd_stats", st);
+      hipLaunchKernelGGL((k_bwd_mf<D, 0>), dim3((unsigned)nblk), dim3(MT), sh0, st,
+                         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout,
+                         wb.off, wb.ent, wb.pstat, wb.wstat, wb.wpart, wb.dqp, dk, dv, srng, s.Hq,
+                         s.Hkv, s.G, s.N, s.S, s.W, s.K, s.nC, ncs, s.nwin, qa, qz, QS, tau); }
+    // the routing query's gradient goes to dq_route, or to dq (then the
+    // partials are added to it)
+    { HilsProfScope ps_("k_bwd_rowstat", st);
+      hipLaunchKernelGGL(k_bwd_rowstat, dim3(rgrid), dim3(256), sizeof(float) * 4 * s.d, st,
+                         (const bf16_t*)qr, (const bf16_t*)ksum, bsum, sel, wb.pstat, wb.wstat,
+                         wb.wpart, dqr ? dqr : dq, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC,
+                         s.nwin, qa, QN, QS, nrows, tau); }
+    { HilsProfScope ps_("k_bwd_cols", st);
+      hipLaunchKernelGGL((k_bwd_mf<D, 1>), dim3((unsigned)nblk), dim3(MT), sh1, st,
+                         (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout,
+                         wb.off, wb.ent, wb.pstat, wb.wstat, wb.wpart, wb.dqp, dk, dv, srng, s.Hq,
+                         s.Hkv, s.G, s.N, s.S, s.W, s.K, s.nC, ncs, s.nwin, qa, qz, QS, tau); }
+    { HilsProfScope ps_("k_bwd_dq", st);
+      hipLaunchKernelGGL(k_bwd_dq_reduce, dim3(rgrid), dim3(256), 0, st, wb.dqp, sel, dq, s.Hq,
+                         s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, s.nwin, qa, QN, QS, nrows,
+                         dqr ? 0 : 1); }
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t hils_bwd_mf_wpart_bytes(const HilsShape& s) {
-  return (size_t)s.B * s.Hq * s.N * s.nwin * 16;
-}
-size_t hils_bwd_mf_dqp_bytes(const HilsShape& s) {
-  return (size_t)s.B * s.Hq * s.N * (s.K + s.nwin) * s.d * 4;
+// Queries per slice: the slice's dq and window partials stay within 4 GiB
+// (all of prefill_8k in one slice; about 2.6K query rows of 32 heads at
+// K = 64, W = 2048).  HILS_BWD_SLICE_QUERIES, when set to a positive count,
+// caps it (tests use it to run several slices at small sizes).
+int hils_bwd_mf_slice(const HilsShape& s) {
+  const size_t per_q = (size_t)s.B * s.Hq * ((size_t)(s.K + s.nwin) * s.d * 4 + (size_t)s.nwin * 16);
+  size_t qs = ((size_t)4 << 30) / (per_q ? per_q : 1);
+  if (const char* e = getenv("HILS_BWD_SLICE_QUERIES")) {
+    const long v = atol(e);
+    if (v > 0 && (size_t)v < qs) qs = (size_t)v;
+  }
+  if (qs < 1) qs = 1;
+  return qs >= (size_t)s.N ? s.N : (int)qs;
 }
 
-// the dq partials grow with N (K + nwin) Hq d; past 32 GiB (about 20K query
-// rows of 32 heads at K = 64, W = 2048) the vector-ALU kernels run instead
-constexpr size_t kMaxDqPartialBytes = (size_t)32 << 30;
+size_t hils_bwd_mf_wpart_bytes(const HilsShape& s) {
+  return (size_t)s.B * s.Hq * hils_bwd_mf_slice(s) * s.nwin * 16;
+}
+size_t hils_bwd_mf_dqp_bytes(const HilsShape& s) {
+  return (size_t)s.B * s.Hq * hils_bwd_mf_slice(s) * (s.K + s.nwin) * s.d * 4;
+}
+size_t hils_bwd_mf_srng_bytes(const HilsShape& s) {
+  return hils_bwd_mf_slice(s) < s.N ? (size_t)s.B * s.Hkv * s.nC * 8 : 0;
+}
 
 bool hils_bwd_mf_ok(const HilsShape& s) {
   return s.dtype == 0 && (s.d == 64 || s.d == 128) && s.S % 16 == 0 && s.S <= 64 && s.G <= 16 &&
-         s.K <= 128 && s.N < (1 << 24) && hils_bwd_mf_dqp_bytes(s) <= kMaxDqPartialBytes;
+         s.K <= 128 && s.N < (1 << 24);
 }
 
 hipError_t hils_launch_backward_mf(const HilsShape& s, const void* q, const void* qr, const void* k,
@@ -665,6 +743,7 @@ hipError_t hils_launch_backward_mf(const HilsShape& s, const void* q, const void
                                    const void* ksum, const float* bsum, float* dq, float* dqr,
                                    float* dk, float* dv, const HilsBwdBufs& wb, hipStream_t st) {
   if (!hils_bwd_mf_ok(s) || !wb.wpart || !wb.dqp) return hipErrorInvalidValue;
+  if (hils_bwd_mf_slice(s) < s.N && s.nC > 0 && !wb.srng) return hipErrorInvalidValue;
   if ((long long)s.B * s.Hkv * s.nCc <= 0) return hipSuccess;
   return s.d == 128 ? launch_mf<128>(s, q, qr, k, v, dout, sel, ksum, bsum, dq, dqr, dk, dv, wb, st)
                     : launch_mf<64>(s, q, qr, k, v, dout, sel, ksum, bsum, dq, dqr, dk, dv, wb, st);

@@ -133,7 +133,7 @@ DecodeLayout decode_layout(const HilsShape& s) {
 }
 
 struct BwdLayout {
-  size_t ks, bs, off, ent, pstat, wstat, wpart, dqp, total;
+  size_t ks, bs, off, ent, pstat, wstat, wpart, dqp, srng, total;
 };
 BwdLayout bwd_layout(const HilsShape& s) {
   BwdLayout L{};
@@ -148,6 +148,7 @@ BwdLayout bwd_layout(const HilsShape& s) {
   const bool mf = hils_bwd_mf_ok(s);
   L.wpart = off; off += align_up(mf ? hils_bwd_mf_wpart_bytes(s) : 0);
   L.dqp = off;   off += align_up(mf ? hils_bwd_mf_dqp_bytes(s) : 0);
+  L.srng = off;  off += align_up(mf ? hils_bwd_mf_srng_bytes(s) : 0);
   L.total = off;
   return L;
 }
@@ -504,7 +505,8 @@ hils_status hils_prefill_backward(const hils_cfg* cfg, const void* q, const void
   const bool mf = hils_bwd_mf_ok(s);
   HilsBwdBufs wb{(uint32_t*)(w + L.off), (uint32_t*)(w + L.ent), (float*)(w + L.pstat),
                  (float*)(w + L.wstat), mf ? (float*)(w + L.wpart) : nullptr,
-                 mf ? (float*)(w + L.dqp) : nullptr};
+                 mf ? (float*)(w + L.dqp) : nullptr,
+                 mf && hils_bwd_mf_srng_bytes(s) ? (uint32_t*)(w + L.srng) : nullptr};
   return hip_status(hils_launch_backward(s, q, q_route ? q_route : q, k, v, lm_q, dout, sel, ks, bs,
                                          dq, dq_route, dk, dv, dlm, wb, st));
 }

@@ -11,8 +11,10 @@ struct HilsBwdBufs {
   float* pstat;     // [B*Hkv*N][K][G][4] alpha, log-normaliser, g = dout.o, d s_hat
   float* wstat;     // [B*Hq*N][4]        the same for the window (d log Z_swa last)
   // matrix-core backward only (else null):
-  float* wpart;     // [B*Hq*N][nwin][4]  window partials per chunk: max, sum exp, sum exp dout.v
-  float* dqp;       // [B*Hq*N][K + nwin][d] dq partial per selected slot and window chunk
+  // (QS = queries per slice, hils_bwd_mf_slice)
+  float* wpart;     // [B*Hq*QS][nwin][4]  window partials per chunk: max, sum exp, sum exp dout.v
+  float* dqp;       // [B*Hq*QS][K + nwin][d] dq partial per selected slot and window chunk
+  uint32_t* srng;   // [B*Hkv*nC][2] each list's part in the slice (several slices only)
 };
 
 // LDS bytes of the row kernel (window logits of G heads live in LDS)
@@ -28,9 +30,13 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
 // and S a multiple of 16: per-chunk statistics, per-row fusion gradients,
 // per-chunk dk, dv and dq partials, per-row dq.  The selection lists come
 // before it and the summaries' share of dk and dlm after it.
+// It runs in query slices [qa, qa + QS) (one for most shapes) whose partials
+// fit 4 GiB; dk, dv accumulate over the slices.
 bool hils_bwd_mf_ok(const HilsShape& s);
+int hils_bwd_mf_slice(const HilsShape& s);
 size_t hils_bwd_mf_wpart_bytes(const HilsShape& s);
 size_t hils_bwd_mf_dqp_bytes(const HilsShape& s);
+size_t hils_bwd_mf_srng_bytes(const HilsShape& s);
 hipError_t hils_launch_backward_mf(const HilsShape& s, const void* q, const void* qr, const void* k,
                                    const void* v, const void* dout, const int32_t* sel,
                                    const void* ksum, const float* bsum, float* dq, float* dqr,

@@ -181,7 +181,7 @@ def test_backward_workspace_holds_the_dq_partials(L):
     assert bf16 >= parts
     # fp32 summaries are twice the size; everything else is shared
     assert 0 < f32 < bf16 - parts + 1 * 8 * 16 * 128 * 2 + 4096
-    # past 32 GiB of dq partials the vector-ALU kernels run, without them
+    # long sequences run in query slices whose partials fit 4 GiB
     big = _cfg(N=1 << 20, Hq=32, Hkv=8, W=2048, K=64)
     big_parts = (1 << 20) * 32 * (64 + 33) * 128 * 4
     assert 0 < ok(ctypes.byref(big)) < big_parts

@@ -113,6 +113,19 @@ def test_backward_selection_slot_order():
     _case(w, label="fp32 reversed slots", reverse_slots=True)
 
 
+def test_backward_query_slices(monkeypatch):
+    # the matrix-core backward in several query slices (at these sizes it
+    # normally takes one): slice bounds inside chunks and windows, dk and dv
+    # added up over the slices, the lists cut per slice
+    monkeypatch.setenv("HILS_BWD_SLICE_QUERIES", "300")
+    w = synth.get_workload("prefill_64k", N=1000, Hq=8, Hkv=2, W=128, K=4)
+    _case(w, q_route=True, label="4 slices of 300")
+    monkeypatch.setenv("HILS_BWD_SLICE_QUERIES", "64")
+    w = synth.get_workload("prefill_64k", N=333, Hq=4, Hkv=1, d=64, S=32, W=100, K=5,
+                           regime="depth10")
+    _case(w, label="6 slices of 64")
+
+
 def test_backward_deterministic():
     w = synth.get_workload("prefill_64k", N=700, Hq=4, Hkv=1, d=64, S=32, W=64, K=4, regime="iid")
     gr, (x, dout, sel) = _case(w, label="determinism")
