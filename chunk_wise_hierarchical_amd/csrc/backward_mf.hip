@@ -89,22 +89,8 @@ __device__ __forceinline__ int tpos(int q) { return 8 * ((q & 15) >> 2) + 4 * (q
 __device__ __forceinline__ float bf_lo(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
 
-// reductions over the 16 lanes of a row (lanes 16 g .. 16 g + 15)
-__device__ __forceinline__ float max16(float v) {
-  v = fmaxf(v, xshfl_f(v, 1));
-  v = fmaxf(v, xshfl_f(v, 2));
-  v = fmaxf(v, xshfl_f(v, 4));
-  return fmaxf(v, xshfl_f(v, 8));
-}
-__device__ __forceinline__ float sum16(float v) {
-  v += xshfl_f(v, 1);
-  v += xshfl_f(v, 2);
-  v += xshfl_f(v, 4);
-  return v + xshfl_f(v, 8);
-}
-
 template <int D, int PASS>
-__global__ void __launch_bounds__(MT, 2)
+__global__ void __launch_bounds__(MT, PASS ? 2 : 4)
 k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
          const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout,
          const uint32_t* __restrict__ off, const uint32_t* __restrict__ ent,
@@ -247,26 +233,51 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   };
 
   // stats pass: per query of the tile, max / sum exp / sum exp dout.v over
-  // this wavefront's keys, combined over the wavefronts
+  // this wavefront's keys, combined over the wavefronts.  The pass takes
+  // S^T = K Q^T and dP^T = V dOut^T (the same registers as operands in the
+  // other order): lane (g4, l16) then holds keys 16 w + 4 g4 + r of query
+  // 16 h + l16, so a query's sums over the wavefront's 16 keys are three
+  // in-lane steps and two lane swaps (16 and 32 apart)
   auto compute_stats = [&](int tl, int buf, int nb) __attribute__((always_inline)) {
     float4* red = dcf;                               // [4][QT]
     if (kwave) {
-      f32x4_t sc[2], dp[2];
-      scores(tiles + (size_t)buf * L::TILE, sc, dp);
+      const bf16_t* tb = tiles + (size_t)buf * L::TILE;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, dp = sc;
+#pragma unroll
+        for (int s2 = 0; s2 < D / 32; ++s2) {
+          const bf16x8_t aq = ld_bf16x8(tb + (16 * h + l16) * L::RS + 32 * s2 + 8 * g4);
+          const bf16x8_t ao = ld_bf16x8(tb + (QT + 16 * h + l16) * L::RS + 32 * s2 + 8 * g4);
+          sc = mfma16(kf[s2], aq, sc);
+          dp = mfma16(vf[s2], ao, dp);
+        }
+        const int qq = 16 * h + l16;
+        const int2 lm = dlim[tl * QT + qq];
+        float x[4];
+        bool ok[4];
+        float m = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int qq = 16 * h + 4 * g4 + r;
-          const int2 lm = dlim[tl * QT + qq];
-          const bool ok = kown && kk >= lm.x && kk <= lm.y;
-          const float x = ok ? tau * sc[h][r] : -INFINITY;
-          const float m = max16(x);
-          const float e = ok ? __expf(x - m) : 0.0f;
-          const float z = sum16(e);
-          const float y = sum16(e * dp[h][r]);
-          if (l16 == 0) red[wv * QT + qq] = make_float4(m, z, y, 0.0f);
+          const int key = 16 * wv + 4 * g4 + r;
+          ok[r] = key < jn && key >= lm.x && key <= lm.y;
+          x[r] = ok[r] ? tau * sc[r] : -INFINITY;
+          m = fmaxf(m, x[r]);
         }
+        m = fmaxf(m, xshfl_f(m, 16));
+        m = fmaxf(m, xshfl_f(m, 32));
+        float z = 0.0f, y = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = ok[r] ? __expf(x[r] - m) : 0.0f;
+          z += e;
+          y = fmaf(e, dp[r], y);
+        }
+        z += xshfl_f(z, 16);
+        z += xshfl_f(z, 32);
+        y += xshfl_f(y, 16);
+        y += xshfl_f(y, 32);
+        if (g4 == 0) red[wv * QT + qq] = make_float4(m, z, y, 0.0f);
       }
     }
     __syncthreads();
