@@ -34,11 +34,11 @@
 // Layout of the chunk passes: one workgroup per (chunk, sequence, KV group),
 // 4 wavefronts; wavefront w owns keys 16w .. 16w + 15 and keeps their K and V
 // rows as MFMA operands in registers.  Contributions go in tiles of 32 whose
-// q and dout rows are gathered into LDS row-major (the operand of
-// S = Q K^T and dP = dOut V^T, reduced over d) and, in the gradient pass,
-// transposed (the operand of dV^T = dOut^T P and dK^T = Q^T dS, reduced over
-// the tile's queries); double-buffered, the next tile's rows load while the
-// current one is computed.  S and dP take bf16 MFMA with exact products and
+// q and dout rows are gathered into LDS row-major, double-buffered (the next
+// tile's rows load while the current one is computed).  They are the operand
+// of S = Q K^T and dP = dOut V^T (reduced over d) as they stand, and of
+// dV^T = dOut^T P and dK^T = Q^T dS (reduced over the tile's queries) through
+// LDS transpose loads.  S and dP take bf16 MFMA with exact products and
 // fp32 sums.  P and tau dS are fp32 and enter their products as bf16 sums
 // hi + lo (hi = bf16(x), lo = bf16(x - hi), within 2^-18 of x) in dv and dk,
 // and hi + mid + lo (within 2^-27) in dq, whose error gathers over all of a
@@ -46,7 +46,7 @@
 // (lane l: key l % 16, queries 4 (l / 16) + r of each 16-query half) is the
 // B-operand layout of the second products once the tile's query positions are
 // permuted (position 8 g + t <-> query 16 (t / 4) + 4 g + t % 4); the
-// transposed tiles store queries at those positions.  dq^T = K^T dS^T takes
+// transpose loads gather the A operand in that order.  dq^T = K^T dS^T takes
 // dS through LDS (key-contiguous per query) and K^T fragments built once per
 // workgroup.  No atomics: every output element is written by one workgroup
 // or wavefront, in a fixed order.
@@ -70,21 +70,30 @@ constexpr int CB = 128;     // contributions described per batch
 template <int D, int PASS>
 struct MfCol {
   static constexpr int RS = D + 8;                 // row-major tile: row stride (bf16), 16-byte pad
-  static constexpr int TS = QT + 8;                // transposed tile: row stride (bf16), 16-byte pad
-  static constexpr int ROWS = 2 * QT * RS;         // q rows, dout rows
-  static constexpr int TILE = ROWS + (PASS ? 2 * D * TS : 0);   // + q^T, dout^T
+  static constexpr int TILE = 2 * QT * RS;         // one buffer: q rows, dout rows
   static constexpr int NPC = QT * (D / 8) / MT;    // 16-byte pieces per thread and tensor
   static constexpr int DSS = 72;                   // dS tile: row stride (bf16), 64 keys + pad
   static constexpr int DSN = 3 * QT * DSS;         // dS tile: three bf16 planes (hi, mid, lo)
-  // the dS tile overlays the row-major tiles of the current buffer when it
-  // fits there (d = 128), else it has a region of its own after both buffers
-  static constexpr bool DS_OVER = DSN <= ROWS;
-  static constexpr int EXTRA = (PASS && !DS_OVER) ? DSN : 0;
+  static constexpr int EXTRA = PASS ? DSN : 0;     // the dS tile, after both buffers
   static constexpr int DB = D / 64;                // 16-column blocks of dq per wavefront
 };
 
-// position of tile query q in the transposed tiles (see above)
-__device__ __forceinline__ int tpos(int q) { return 8 * ((q & 15) >> 2) + 4 * (q >> 4) + (q & 3); }
+// A operand of a product reduced over the tile's queries (dV^T = dOut^T P,
+// dK^T = Q^T dS) read from the row-major tile with two LDS transpose loads.
+// ds_read_b64_tr_b16 gives output lane j of a 16-lane group, element t, the
+// element j % 4 of the 4 read by lane 4 t + j / 4.  Lane 4 t + u of group g4
+// reads columns 16 b + 4 u .. + 3 of query 16 c + 4 g4 + t (call c = 0, 1),
+// so lane (g4, j) receives column 16 b + j of queries 16 c + 4 g4 + t: the
+// fragment A[16 b + j][8 g4 + 4 c + t] in the permuted query order.
+typedef short s4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4_t* lds_s4_ptr;
+__device__ __forceinline__ bf16x8_t ld_tr_frag(const bf16_t* rows, int rs, int b, int g4, int l16) {
+  const bf16_t* p = rows + (4 * g4 + (l16 >> 2)) * rs + 16 * b + 4 * (l16 & 3);
+  const s4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(p));
+  const s4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(p + 16 * rs));
+  const uint2 a = __builtin_bit_cast(uint2, lo), c = __builtin_bit_cast(uint2, hi);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, c.x, c.y));
+}
 
 __device__ __forceinline__ float bf_lo(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
@@ -200,19 +209,6 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       const int pc = tid + MT * m, qq = pc % QT, part = pc / QT;
       fastp::st_u4(tb + qq * L::RS + 8 * part, pq[m]);
       fastp::st_u4(tb + (QT + qq) * L::RS + 8 * part, po[m]);
-      if (PASS) {
-        unsigned short* tq = reinterpret_cast<unsigned short*>(tb + L::ROWS);
-        unsigned short* to = tq + D * L::TS;
-        const int ps = tpos(qq);
-        const uint32_t wq[4] = {pq[m].x, pq[m].y, pq[m].z, pq[m].w};
-        const uint32_t wo[4] = {po[m].x, po[m].y, po[m].z, po[m].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int row = 8 * part + e;
-          tq[row * L::TS + ps] = (unsigned short)(wq[e >> 1] >> (16 * (e & 1)));
-          to[row * L::TS + ps] = (unsigned short)(wo[e >> 1] >> (16 * (e & 1)));
-        }
-      }
     }
   };
   // S and dP of the tile for this wavefront's 16 keys: sc[h][r], dp[h][r] for
@@ -313,8 +309,6 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // gradient pass
   auto compute_grads = [&](int tl, int buf, int nb) __attribute__((always_inline)) {
     bf16_t* tb = tiles + (size_t)buf * L::TILE;
-    const bf16_t* tqt = tb + L::ROWS;
-    const bf16_t* tot = tqt + D * L::TS;
     uint32_t ph[4], pl[4], dh[4], dl[4], d3[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) { ph[t] = 0u; pl[t] = 0u; dh[t] = 0u; dl[t] = 0u; d3[t] = 0u; }
@@ -348,9 +342,9 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                             ds[2 * t + 1] - bf_hi(dh[t]) - bf_hi(dl[t]));
       }
     }
-    __syncthreads();                                 // every wavefront has read the row-major tiles
-    // dS (hi, mid, lo): [3][QT][DSS], key-contiguous
-    bf16_t* dst = L::DS_OVER ? tb : tiles + 2 * L::TILE;
+    // dS (hi, mid, lo): [3][QT][DSS], key-contiguous; the previous tile's dq
+    // products read it before the barrier that ended that tile
+    bf16_t* dst = tiles + 2 * L::TILE;
     {
       unsigned short* dsl = reinterpret_cast<unsigned short*>(dst);
 #pragma unroll
@@ -371,8 +365,8 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
       const bf16x8_t bdl = __builtin_bit_cast(bf16x8_t, make_uint4(dl[0], dl[1], dl[2], dl[3]));
 #pragma unroll
       for (int b2 = 0; b2 < D / 16; ++b2) {
-        const bf16x8_t ao = ld_bf16x8(tot + (16 * b2 + l16) * L::TS + 8 * g4);
-        const bf16x8_t aq = ld_bf16x8(tqt + (16 * b2 + l16) * L::TS + 8 * g4);
+        const bf16x8_t ao = ld_tr_frag(tb + QT * L::RS, L::RS, b2, g4, l16);
+        const bf16x8_t aq = ld_tr_frag(tb, L::RS, b2, g4, l16);
         accv[b2] = mfma16(ao, bph, accv[b2]);
         accv[b2] = mfma16(ao, bpl, accv[b2]);
         acck[b2] = mfma16(aq, bdh, acck[b2]);
