@@ -105,8 +105,9 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
          const uint32_t* __restrict__ off, const uint32_t* __restrict__ ent,
          float* __restrict__ pstat, const float* __restrict__ wstat, float* __restrict__ wpart,
          float* __restrict__ dqp, float* __restrict__ dk, float* __restrict__ dv,
-         const uint32_t* __restrict__ srng, int Hq, int Hkv, int G, int N, int S, int W, int K,
-         int nC, int nCc, int nwin, int qa, int qz, int QS, float tau) {
+         const uint32_t* __restrict__ srng, const uint32_t* __restrict__ order, int Hq, int Hkv,
+         int G, int N, int S, int W, int K, int nC, int nCc, int nwin, int qa, int qz, int QS,
+         float tau) {
   using L = MfCol<D, PASS>;
   extern __shared__ __align__(16) unsigned char smm[];
   bf16_t* tiles = reinterpret_cast<bf16_t*>(smm);                        // [2][TILE]
@@ -116,11 +117,9 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   float4* dcf = reinterpret_cast<float4*>(dlim + CB);   // [CB] alpha, lse, g, E; stats: [4][QT] partials
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  // chunk-major order (c, b, g): a chunk's work depends on its position and
-  // the routing; consecutive workgroups take one chunk of every sequence and
-  // KV group, so heavy chunks spread over the chip
+  // work item (c, b, g) = c (B Hkv) + b Hkv + g, taken heaviest first (order)
   const long long nbg = gridDim.x / nCc;             // B * Hkv
-  const long long blk = blockIdx.x;
+  const long long blk = order[blockIdx.x];
   const int c = (int)(blk / nbg);
   const long long bg = blk % nbg;
   const long long hb = (bg / Hkv) * Hq + (long long)(bg % Hkv) * G;
@@ -661,6 +660,44 @@ k_bwd_slice_ranges(const uint32_t* __restrict__ off, const uint32_t* __restrict_
   srng[2 * t + 1] = lower((uint32_t)qz << 8);
 }
 
+// Work items (chunk, sequence, KV group) of a slice in decreasing order of
+// their contribution counts (bucketed by powers of two), so that the chunk
+// passes start the longest workgroups first: a chunk's count depends on its
+// position and on the routing (a chunk many queries select takes several
+// times the mean).  The order changes only the schedule, not any result.
+__global__ void __launch_bounds__(1024)
+k_bwd_order(const uint32_t* __restrict__ off, const uint32_t* __restrict__ srng,
+            uint32_t* __restrict__ order, int nbg, int ncs, int nC, int G, int N, int S, int W,
+            int qa, int qz) {
+  __shared__ uint32_t hist[33], cur[33];
+  const int tid = threadIdx.x;
+  const long long n = (long long)nbg * ncs;
+  auto bucket = [&](long long t) {
+    const int c = (int)(t / nbg);
+    const long long bg = t % nbg;
+    long long w = 0;
+    if (c < nC) {
+      const long long lc = bg * nC + c;
+      w = srng ? (long long)srng[2 * lc + 1] - srng[2 * lc]
+               : (long long)off[bg * (nC + 1) + c + 1] - off[bg * (nC + 1) + c];
+    }
+    const int j0 = c * S;
+    w += max(0, min(min(N, (c + 1) * S + W - 1), qz) - max(j0, qa));
+    w *= G;
+    return w > 0 ? 64 - __clzll((unsigned long long)w) : 0;   // 0 .. 32 (w < 2^32)
+  };
+  if (tid < 33) hist[tid] = 0u;
+  __syncthreads();
+  for (long long t = tid; t < n; t += 1024) atomicAdd(&hist[min(bucket(t), 32)], 1u);
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t run = 0;
+    for (int b = 32; b >= 0; --b) { cur[b] = run; run += hist[b]; }
+  }
+  __syncthreads();
+  for (long long t = tid; t < n; t += 1024) order[atomicAdd(&cur[min(bucket(t), 32)], 1u)] = (uint32_t)t;
+}
+
 template <int D>
 hipError_t launch_mf(const HilsShape& s, const void* q, const void* qr, const void* k, const void* v,
                      const void* dout, const int32_t* sel, const void* ksum, const float* bsum,
@@ -684,13 +721,17 @@ hipError_t launch_mf(const HilsShape& s, const void* q, const void* qr, const vo
     // chunks with a token before qz (the others have no contribution yet)
     const int ncs = min(s.nCc, (qz + s.S - 1) / s.S);
     const long long nblk = (long long)s.B * s.Hkv * ncs;
+    { HilsProfScope ps_("k_bwd_order", st);
+      hipLaunchKernelGGL(k_bwd_order, dim3(1), dim3(1024), 0, st, wb.off, srng, wb.order,
+                         s.B * s.Hkv, ncs, s.nC, s.G, s.N, s.S, s.W, qa, qz); }
     const long long nrows = (long long)s.B * s.Hq * QN;
     const unsigned rgrid = (unsigned)((nrows + 3) / 4);
     { HilsProfScope ps_("k_bwd_stats", st);
       hipLaunchKernelGGL((k_bwd_mf<D, 0>), dim3((unsigned)nblk), dim3(MT), sh0, st,
                          (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout,
-                         wb.off, wb.ent, wb.pstat, wb.wstat, wb.wpart, wb.dqp, dk, dv, srng, s.Hq,
-                         s.Hkv, s.G, s.N, s.S, s.W, s.K, s.nC, ncs, s.nwin, qa, qz, QS, tau); }
+                         wb.off, wb.ent, wb.pstat, wb.wstat, wb.wpart, wb.dqp, dk, dv, srng,
+                         wb.order, s.Hq, s.Hkv, s.G, s.N, s.S, s.W, s.K, s.nC, ncs, s.nwin, qa, qz,
+                         QS, tau); }
     // the routing query's gradient goes to dq_route, or to dq (then the
     // partials are added to it)
     { HilsProfScope ps_("k_bwd_rowstat", st);
@@ -701,8 +742,9 @@ hipError_t launch_mf(const HilsShape& s, const void* q, const void* qr, const vo
     { HilsProfScope ps_("k_bwd_cols", st);
       hipLaunchKernelGGL((k_bwd_mf<D, 1>), dim3((unsigned)nblk), dim3(MT), sh1, st,
                          (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout,
-                         wb.off, wb.ent, wb.pstat, wb.wstat, wb.wpart, wb.dqp, dk, dv, srng, s.Hq,
-                         s.Hkv, s.G, s.N, s.S, s.W, s.K, s.nC, ncs, s.nwin, qa, qz, QS, tau); }
+                         wb.off, wb.ent, wb.pstat, wb.wstat, wb.wpart, wb.dqp, dk, dv, srng,
+                         wb.order, s.Hq, s.Hkv, s.G, s.N, s.S, s.W, s.K, s.nC, ncs, s.nwin, qa, qz,
+                         QS, tau); }
     { HilsProfScope ps_("k_bwd_dq", st);
       hipLaunchKernelGGL(k_bwd_dq_reduce, dim3(rgrid), dim3(256), 0, st, wb.dqp, sel, dq, s.Hq,
                          s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, s.nwin, qa, QN, QS, nrows,
@@ -734,6 +776,7 @@ size_t hils_bwd_mf_wpart_bytes(const HilsShape& s) {
 size_t hils_bwd_mf_dqp_bytes(const HilsShape& s) {
   return (size_t)s.B * s.Hq * hils_bwd_mf_slice(s) * (s.K + s.nwin) * s.d * 4;
 }
+size_t hils_bwd_mf_order_bytes(const HilsShape& s) { return (size_t)s.B * s.Hkv * s.nCc * 4; }
 size_t hils_bwd_mf_srng_bytes(const HilsShape& s) {
   return hils_bwd_mf_slice(s) < s.N ? (size_t)s.B * s.Hkv * s.nC * 8 : 0;
 }
@@ -747,7 +790,7 @@ hipError_t hils_launch_backward_mf(const HilsShape& s, const void* q, const void
                                    const void* v, const void* dout, const int32_t* sel,
                                    const void* ksum, const float* bsum, float* dq, float* dqr,
                                    float* dk, float* dv, const HilsBwdBufs& wb, hipStream_t st) {
-  if (!hils_bwd_mf_ok(s) || !wb.wpart || !wb.dqp) return hipErrorInvalidValue;
+  if (!hils_bwd_mf_ok(s) || !wb.wpart || !wb.dqp || !wb.order) return hipErrorInvalidValue;
   if (hils_bwd_mf_slice(s) < s.N && s.nC > 0 && !wb.srng) return hipErrorInvalidValue;
   if ((long long)s.B * s.Hkv * s.nCc <= 0) return hipSuccess;
   return s.d == 128 ? launch_mf<128>(s, q, qr, k, v, dout, sel, ksum, bsum, dq, dqr, dk, dv, wb, st)

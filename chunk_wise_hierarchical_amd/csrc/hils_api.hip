@@ -133,7 +133,7 @@ DecodeLayout decode_layout(const HilsShape& s) {
 }
 
 struct BwdLayout {
-  size_t ks, bs, off, ent, pstat, wstat, wpart, dqp, srng, total;
+  size_t ks, bs, off, ent, pstat, wstat, wpart, dqp, srng, order, total;
 };
 BwdLayout bwd_layout(const HilsShape& s) {
   BwdLayout L{};
@@ -149,6 +149,7 @@ BwdLayout bwd_layout(const HilsShape& s) {
   L.wpart = off; off += align_up(mf ? hils_bwd_mf_wpart_bytes(s) : 0);
   L.dqp = off;   off += align_up(mf ? hils_bwd_mf_dqp_bytes(s) : 0);
   L.srng = off;  off += align_up(mf ? hils_bwd_mf_srng_bytes(s) : 0);
+  L.order = off; off += align_up(mf ? hils_bwd_mf_order_bytes(s) : 0);
   L.total = off;
   return L;
 }
@@ -506,7 +507,8 @@ hils_status hils_prefill_backward(const hils_cfg* cfg, const void* q, const void
   HilsBwdBufs wb{(uint32_t*)(w + L.off), (uint32_t*)(w + L.ent), (float*)(w + L.pstat),
                  (float*)(w + L.wstat), mf ? (float*)(w + L.wpart) : nullptr,
                  mf ? (float*)(w + L.dqp) : nullptr,
-                 mf && hils_bwd_mf_srng_bytes(s) ? (uint32_t*)(w + L.srng) : nullptr};
+                 mf && hils_bwd_mf_srng_bytes(s) ? (uint32_t*)(w + L.srng) : nullptr,
+                 mf ? (uint32_t*)(w + L.order) : nullptr};
   return hip_status(hils_launch_backward(s, q, q_route ? q_route : q, k, v, lm_q, dout, sel, ks, bs,
                                          dq, dq_route, dk, dv, dlm, wb, st));
 }

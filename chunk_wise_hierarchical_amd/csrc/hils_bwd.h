@@ -15,6 +15,7 @@ struct HilsBwdBufs {
   float* wpart;     // [B*Hq*QS][nwin][4]  window partials per chunk: max, sum exp, sum exp dout.v
   float* dqp;       // [B*Hq*QS][K + nwin][d] dq partial per selected slot and window chunk
   uint32_t* srng;   // [B*Hkv*nC][2] each list's part in the slice (several slices only)
+  uint32_t* order;  // [B*Hkv*nCc]    the chunk passes' work items, heaviest first
 };
 
 // LDS bytes of the row kernel (window logits of G heads live in LDS)
@@ -37,6 +38,7 @@ int hils_bwd_mf_slice(const HilsShape& s);
 size_t hils_bwd_mf_wpart_bytes(const HilsShape& s);
 size_t hils_bwd_mf_dqp_bytes(const HilsShape& s);
 size_t hils_bwd_mf_srng_bytes(const HilsShape& s);
+size_t hils_bwd_mf_order_bytes(const HilsShape& s);
 hipError_t hils_launch_backward_mf(const HilsShape& s, const void* q, const void* qr, const void* k,
                                    const void* v, const void* dout, const int32_t* sel,
                                    const void* ksum, const float* bsum, float* dq, float* dqr,
