@@ -609,7 +609,7 @@ k_bwd_dq_reduce(const float* __restrict__ dqp, const int32_t* __restrict__ sel, 
   const long long item = (long long)blockIdx.x * 4 + wv;
   if (item >= nrows) return;
   const int e = 2 * lane;
-  if (e >= d) return;
+  const bool on = e < d;                             // every lane takes part in the ballots
   const int i = qa + (int)(item % QN);
   const long long bh = item / QN;
   const int h = (int)(bh % Hq);
@@ -617,22 +617,38 @@ k_bwd_dq_reduce(const float* __restrict__ dqp, const int32_t* __restrict__ sel, 
   const long long row = (b * Hkv + h / G) * N + i;
   const long long arow = bh * N + i;
   const float* pp = dqp + (bh * QS + (i - qa)) * (long long)(K + nwin) * d + e;
-  float2 acc = add ? *reinterpret_cast<const float2*>(dq + arow * d + e) : make_float2(0.0f, 0.0f);
-  for (int t = 0; t < K; ++t) {
-    const int c = sel[row * K + t];
-    if (c < 0 || c >= nC) continue;
-    const float2 x = *reinterpret_cast<const float2*>(pp + (long long)t * d);
-    acc.x += x.x;
-    acc.y += x.y;
-  }
+  float2 acc = add && on ? *reinterpret_cast<const float2*>(dq + arow * d + e) : make_float2(0.0f, 0.0f);
+  // the selected slots that hold a chunk (one ballot bit per slot, K <= 128),
+  // then the window chunks; eight partial rows in flight, added in slot order
+  const int c0 = lane < K ? sel[row * K + lane] : -1;
+  const int c1 = lane + 64 < K ? sel[row * K + lane + 64] : -1;
+  uint64_t m0 = __ballot(c0 >= 0 && c0 < nC), m1 = __ballot(c1 >= 0 && c1 < nC);
   const int ws = (int)window_start(i, W, S);
   const int nw = i / S - ws / S + 1;
-  for (int w = 0; w < nw; ++w) {
-    const float2 x = *reinterpret_cast<const float2*>(pp + (long long)(K + w) * d);
-    acc.x += x.x;
-    acc.y += x.y;
+  int wn = 0;
+  for (;;) {
+    int sl[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      int t = -1;
+      if (m0) { t = __ffsll((unsigned long long)m0) - 1; m0 &= m0 - 1; }
+      else if (m1) { t = 64 + __ffsll((unsigned long long)m1) - 1; m1 &= m1 - 1; }
+      else if (wn < nw) t = K + wn++;
+      sl[x] = t;
+    }
+    if (sl[0] < 0) break;
+    float2 v[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      v[x] = sl[x] >= 0 && on ? *reinterpret_cast<const float2*>(pp + (long long)sl[x] * d)
+                              : make_float2(0.0f, 0.0f);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      acc.x += v[x].x;
+      acc.y += v[x].y;
+    }
   }
-  *reinterpret_cast<float2*>(dq + arow * d + e) = acc;
+  if (on) *reinterpret_cast<float2*>(dq + arow * d + e) = acc;
 }
 
 // per (sequence, KV group, chunk with a summary): the part of the chunk's
