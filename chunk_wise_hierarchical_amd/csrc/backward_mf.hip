@@ -509,6 +509,7 @@ k_bwd_rowstat(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   // selected chunks: lanes t and t + 64
   float sh[2], lt[2], gt[2];
   bool vt[2];
+  int cs[2];                                         // chunk of slot lane + 64 m, -1 if none
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     const int t = lane + 64 * m;
@@ -516,9 +517,11 @@ k_bwd_rowstat(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
     sh[m] = -INFINITY;
     lt[m] = 0.0f;
     gt[m] = 0.0f;
+    cs[m] = -1;
     if (t < K) {
       const int c = sel[row * K + t];
       if (c >= 0 && c < nC) {
+        cs[m] = c;
         vt[m] = true;
         const bf16_t* kp = ksum + (bh * nC + c) * (long long)d;
         float a = 0.0f;
@@ -583,17 +586,27 @@ k_bwd_rowstat(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   }
   if (lane == 0)
     *reinterpret_cast<float4*>(wstat + arow * 4) = make_float4(aw, lse_w, g_w, aw * (g_w - gbar));
-  // routing query: tau sum_t (d s_hat_t) k'_t; lane takes elements 2 lane, 2 lane + 1
+  // routing query: tau sum_t (d s_hat_t) k'_t; lane takes elements 2 lane,
+  // 2 lane + 1; slots in order, eight k' rows in flight, the chunk ids and
+  // d s_hat from the slot lanes
   float q0 = 0.0f, q1 = 0.0f;
   const int e = 2 * lane;
-  for (int t = 0; t < K; ++t) {
-    const int c = sel[row * K + t];
-    if (c < 0 || c >= nC) continue;
-    const float x = __shfl(dsh[t >> 6], t & 63, 64);
-    if (e < d) {
-      const uint32_t kv = *reinterpret_cast<const uint32_t*>(ksum + (bh * nC + c) * (long long)d + e);
-      q0 = fmaf(x, bf_lo(kv), q0);
-      q1 = fmaf(x, bf_hi(kv), q1);
+  for (int t0 = 0; t0 < K; t0 += 8) {
+    uint32_t kv[8];
+    float xs[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int t = min(t0 + x, K - 1);
+      const int c = __shfl(t < 64 ? cs[0] : cs[1], t & 63, 64);
+      const float ds = __shfl(t < 64 ? dsh[0] : dsh[1], t & 63, 64);
+      const bool ok = t0 + x < K && c >= 0;
+      xs[x] = ok ? ds : 0.0f;
+      kv[x] = (ok && e < d) ? *reinterpret_cast<const uint32_t*>(ksum + (bh * nC + c) * (long long)d + e) : 0u;
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      q0 = fmaf(xs[x], bf_lo(kv[x]), q0);
+      q1 = fmaf(xs[x], bf_hi(kv[x]), q1);
     }
   }
   if (e < d) *reinterpret_cast<float2*>(dqo + arow * d + e) = make_float2(tau * q0, tau * q1);
