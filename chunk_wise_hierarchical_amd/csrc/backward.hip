@@ -685,8 +685,10 @@ __host__ __device__ inline size_t col_stage_bytes(int d, int S) {
   return ((st > sc ? st : sc) + 15) & ~(size_t)15;
 }
 
+// (the summary-only variant at two workgroups per CU: its row reads are
+// latency-bound, and it fits 128 registers)
 template <typename T, bool SUMONLY, int GT = 0>
-__global__ void __launch_bounds__(CT)
+__global__ void __launch_bounds__(CT, SUMONLY ? 4 : 1)
 k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restrict__ k,
            const T* __restrict__ v, const T* __restrict__ lm, const T* __restrict__ dout,
            const uint32_t* __restrict__ off, const uint32_t* __restrict__ ent,
