@@ -15,16 +15,19 @@
 //   dpi_j = k_j.dk' + db' (-log pi_j - 1);  dt_j = pi_j (dpi_j - sum pi dpi)
 //   dq' = tau sum_j dt_j k_j;  dk_j += tau dt_j q' + pi_j dk'.
 //
-// Three kernels, no atomics, deterministic:
+// Vector-ALU kernels (fp32 inputs and the shapes the matrix-core passes of
+// backward_mf.hip do not take), no floating-point atomics, deterministic:
 //   k_bwd_lists — per (batch, KV group): for every chunk, the (query, slot)
-//                 pairs that selected it, in query order (stable counting sort);
+//                 pairs that selected it, in query order (stable counting
+//                 sort; also used by the matrix-core passes);
 //   k_bwd_rows  — per (batch, KV group, query): recompute the row's softmax
 //                 statistics, write dq (and dq_route) and per-pair / window
 //                 statistics (alpha, log-normaliser, g, d s_hat);
 //   k_bwd_cols  — per (batch, KV group, chunk): accumulate dk, dv of the
 //                 chunk's tokens over the queries that selected the chunk and
 //                 the queries whose window holds it, then back-propagate the
-//                 chunk's summaries into dlm and dk.
+//                 chunk's summaries into dlm and dk.  Its summary-only form
+//                 follows the matrix-core passes.
 #include "fast_common.h"
 #include "hils_internal.h"
 #include "hils_bwd.h"

@@ -48,8 +48,9 @@
 // permuted (position 8 g + t <-> query 16 (t / 4) + 4 g + t % 4); the
 // transpose loads gather the A operand in that order.  dq^T = K^T dS^T takes
 // dS through LDS (key-contiguous per query) and K^T fragments built once per
-// workgroup.  No atomics: every output element is written by one workgroup
-// or wavefront, in a fixed order.
+// workgroup.  No floating-point atomics: every output element is written by
+// one workgroup or wavefront, in a fixed order (the integer atomics of the
+// work ordering change only the schedule).
 #include <cstdlib>
 
 #include "fast_common.h"

@@ -216,10 +216,15 @@ hils_status hils_decode_paged(const hils_cfg* cfg, const void* q, const void* q_
  *   dq_route        : fp32 [B][Hq][N][d] iff q_route is given (the token query
  *                     then gets only the attention part);
  *   dlm             : fp32 [B][Hq][N/S][d] (may be NULL in MEAN_POOL mode).
- * The kernels use no atomics, so results are deterministic.  Supports d <= 128
- * (a multiple of 64 for bf16, of 32 for fp32), S <= 64, G <= 8, K <= 128 and
- * windows whose G head rows of logits fit in LDS (otherwise
- * HILS_E_UNSUPPORTED, and hils_prefill_backward_workspace_bytes returns 0).
+ * The kernels use no floating-point atomics, so results are deterministic.
+ * Supports d <= 128 (a multiple of 64 for bf16, of 32 for fp32), S <= 64,
+ * G <= 8, K <= 128 and windows whose G head rows of logits fit in LDS
+ * (otherwise HILS_E_UNSUPPORTED, and hils_prefill_backward_workspace_bytes
+ * returns 0).  For bf16 with d in {64, 128} and S a multiple of 16 the
+ * attention products run on the matrix cores in query slices whose per-slice
+ * partials fit 4 GiB of workspace; the environment variable
+ * HILS_BWD_SLICE_QUERIES, a positive query count, caps the slice (the
+ * workspace query and the call must see the same value).
  */
 size_t hils_prefill_backward_workspace_bytes(const hils_cfg* cfg);
 hils_status hils_prefill_backward(const hils_cfg* cfg, const void* q, const void* q_route,
