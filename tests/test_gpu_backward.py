@@ -98,6 +98,10 @@ def test_backward_matrix_core_columns_all_modes():
     _case(w, label="mf d64 S32 G8")
     w = synth.get_workload("prefill_64k", N=50, Hq=2, Hkv=1, W=30, K=2)
     _case(w, label="mf N < S")
+    w = synth.get_workload("prefill_64k", N=1, Hq=2, Hkv=1, W=30, K=2)
+    _case(w, label="mf N = 1")
+    w = synth.get_workload("prefill_64k", N=65, Hq=4, Hkv=1, W=1, K=3, regime="iid")
+    _case(w, label="mf N = S + 1, W = 1")
     # a group size that is not a power of two (the summary pass's generic form)
     w = synth.get_workload("prefill_64k", N=400, Hq=6, Hkv=2, W=80, K=5, regime="half_peaked4")
     _case(w, label="mf G3")
