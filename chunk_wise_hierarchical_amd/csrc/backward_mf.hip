@@ -67,6 +67,7 @@ using fastp::xshfl_f;
 constexpr int MT = 256;     // threads of the chunk passes (4 wavefronts)
 constexpr int QT = 32;      // contributions per tile
 constexpr int CB = 128;     // contributions described per batch
+constexpr int SPLIT = 4096; // stats pass: contributions per workgroup at most (heavy chunks split)
 
 template <int D, int PASS>
 struct MfCol {
@@ -106,8 +107,9 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
          const uint32_t* __restrict__ off, const uint32_t* __restrict__ ent,
          float* __restrict__ pstat, const float* __restrict__ wstat, float* __restrict__ wpart,
          float* __restrict__ dqp, float* __restrict__ dk, float* __restrict__ dv,
-         const uint32_t* __restrict__ srng, const uint32_t* __restrict__ order, int Hq, int Hkv,
-         int G, int N, int S, int W, int K, int nC, int nCc, int nwin, int qa, int qz, int QS,
+         const uint32_t* __restrict__ srng, const uint32_t* __restrict__ order,
+         const uint2* __restrict__ sitems, const uint32_t* __restrict__ nsi, int nbgp, int Hq,
+         int Hkv, int G, int N, int S, int W, int K, int nC, int nwin, int qa, int qz, int QS,
          float tau) {
   using L = MfCol<D, PASS>;
   extern __shared__ __align__(16) unsigned char smm[];
@@ -118,9 +120,21 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   float4* dcf = reinterpret_cast<float4*>(dlim + CB);   // [CB] alpha, lse, g, E; stats: [4][QT] partials
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  // work item (c, b, g) = c (B Hkv) + b Hkv + g, taken heaviest first (order)
-  const long long nbg = gridDim.x / nCc;             // B * Hkv
-  const long long blk = order[blockIdx.x];
+  // work item (c, b, g) = c (B Hkv) + b Hkv + g.  The gradient pass takes the
+  // items heaviest first (order); the stats pass takes their parts (sitems:
+  // item, part), an item with more than SPLIT contributions cut into equal
+  // parts (its outputs are per contribution), heaviest parts first
+  const long long nbg = nbgp;                        // B * Hkv
+  long long blk;
+  int part = 0;
+  if (PASS) {
+    blk = order[blockIdx.x];
+  } else {
+    if (blockIdx.x >= nsi[0]) return;                // the grid bounds the part count
+    const uint2 it = sitems[blockIdx.x];
+    blk = it.x;
+    part = (int)it.y;
+  }
   const int c = (int)(blk / nbg);
   const long long bg = blk % nbg;
   const long long hb = (bg / Hkv) * Hq + (long long)(bg % Hkv) * G;
@@ -407,8 +421,14 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }
   };
 
-  for (long long base = 0; base < nsel + nwq; base += CB) {
-    const int nb = (int)min((long long)CB, nsel + nwq - base);
+  long long clo = 0, chi = nsel + nwq;              // this workgroup's contributions
+  if (!PASS) {
+    const long long np = max(1LL, (chi + SPLIT - 1) / SPLIT);
+    clo = chi * part / np;
+    chi = chi * (part + 1) / np;
+  }
+  for (long long base = clo; base < chi; base += CB) {
+    const int nb = (int)min((long long)CB, chi - base);
     __syncthreads();                                 // the previous batch is consumed
     for (int t = tid; t < CB; t += MT) {
       const long long idx = base + t;
@@ -694,15 +714,18 @@ k_bwd_slice_ranges(const uint32_t* __restrict__ off, const uint32_t* __restrict_
 // their contribution counts (bucketed by powers of two), so that the chunk
 // passes start the longest workgroups first: a chunk's count depends on its
 // position and on the routing (a chunk many queries select takes several
-// times the mean).  The order changes only the schedule, not any result.
+// times the mean).  For the stats pass the same, by part: an item with w
+// contributions is cut into ceil(w / SPLIT) parts (none when w = 0), listed
+// in sitems (item, part), their number in nsi[0].  The orders change only the
+// schedule, not any result.
 __global__ void __launch_bounds__(1024)
 k_bwd_order(const uint32_t* __restrict__ off, const uint32_t* __restrict__ srng,
-            uint32_t* __restrict__ order, int nbg, int ncs, int nC, int G, int N, int S, int W,
-            int qa, int qz) {
-  __shared__ uint32_t hist[33], cur[33];
+            uint32_t* __restrict__ order, uint2* __restrict__ sitems, uint32_t* __restrict__ nsi,
+            int nbg, int ncs, int nC, int G, int N, int S, int W, int qa, int qz) {
+  __shared__ uint32_t hist[33], cur[33], hist2[33], cur2[33];
   const int tid = threadIdx.x;
   const long long n = (long long)nbg * ncs;
-  auto bucket = [&](long long t) {
+  auto work = [&](long long t) {
     const int c = (int)(t / nbg);
     const long long bg = t % nbg;
     long long w = 0;
@@ -713,19 +736,47 @@ k_bwd_order(const uint32_t* __restrict__ off, const uint32_t* __restrict__ srng,
     }
     const int j0 = c * S;
     w += max(0, min(min(N, (c + 1) * S + W - 1), qz) - max(j0, qa));
-    w *= G;
-    return w > 0 ? 64 - __clzll((unsigned long long)w) : 0;   // 0 .. 32 (w < 2^32)
+    return w * G;
   };
-  if (tid < 33) hist[tid] = 0u;
+  auto bucket = [](long long w) {                    // 0 .. 32 (w < 2^32)
+    return min(w > 0 ? 64 - __clzll((unsigned long long)w) : 0, 32);
+  };
+  auto parts = [](long long w) { return (w + SPLIT - 1) / SPLIT; };
+  if (tid < 33) { hist[tid] = 0u; hist2[tid] = 0u; }
   __syncthreads();
-  for (long long t = tid; t < n; t += 1024) atomicAdd(&hist[min(bucket(t), 32)], 1u);
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t run = 0;
-    for (int b = 32; b >= 0; --b) { cur[b] = run; run += hist[b]; }
+  for (long long t = tid; t < n; t += 1024) {
+    const long long w = work(t), np = parts(w);
+    atomicAdd(&hist[bucket(w)], 1u);
+    if (np > 0) atomicAdd(&hist2[bucket((w + np - 1) / np)], (uint32_t)np);
   }
   __syncthreads();
-  for (long long t = tid; t < n; t += 1024) order[atomicAdd(&cur[min(bucket(t), 32)], 1u)] = (uint32_t)t;
+  if (tid == 0) {
+    uint32_t run = 0, run2 = 0;
+    for (int b = 32; b >= 0; --b) {
+      cur[b] = run;
+      run += hist[b];
+      cur2[b] = run2;
+      run2 += hist2[b];
+    }
+    nsi[0] = run2;
+  }
+  __syncthreads();
+  for (long long t = tid; t < n; t += 1024) {
+    const long long w = work(t), np = parts(w);
+    order[atomicAdd(&cur[bucket(w)], 1u)] = (uint32_t)t;
+    if (np > 0) {
+      const uint32_t p0 = atomicAdd(&cur2[bucket((w + np - 1) / np)], (uint32_t)np);
+      for (long long p = 0; p < np; ++p) sitems[p0 + p] = make_uint2((uint32_t)t, (uint32_t)p);
+    }
+  }
+}
+
+// upper bound of the stats pass's parts in a slice of QN queries: one per
+// item plus one per SPLIT of the most contributions the slice can have
+// (every query and head with K selected chunks and nwin window chunks)
+long long stats_parts_max(const HilsShape& s, int QN) {
+  return (long long)s.B * s.Hkv * s.nCc +
+         ((long long)s.B * s.Hq * QN * (s.K + s.nwin) + SPLIT - 1) / SPLIT;
 }
 
 template <int D>
@@ -753,15 +804,15 @@ hipError_t launch_mf(const HilsShape& s, const void* q, const void* qr, const vo
     const long long nblk = (long long)s.B * s.Hkv * ncs;
     { HilsProfScope ps_("k_bwd_order", st);
       hipLaunchKernelGGL(k_bwd_order, dim3(1), dim3(1024), 0, st, wb.off, srng, wb.order,
-                         s.B * s.Hkv, ncs, s.nC, s.G, s.N, s.S, s.W, qa, qz); }
+                         wb.sitems, wb.nsi, s.B * s.Hkv, ncs, s.nC, s.G, s.N, s.S, s.W, qa, qz); }
     const long long nrows = (long long)s.B * s.Hq * QN;
     const unsigned rgrid = (unsigned)((nrows + 3) / 4);
     { HilsProfScope ps_("k_bwd_stats", st);
-      hipLaunchKernelGGL((k_bwd_mf<D, 0>), dim3((unsigned)nblk), dim3(MT), sh0, st,
+      hipLaunchKernelGGL((k_bwd_mf<D, 0>), dim3((unsigned)stats_parts_max(s, QN)), dim3(MT), sh0, st,
                          (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout,
                          wb.off, wb.ent, wb.pstat, wb.wstat, wb.wpart, wb.dqp, dk, dv, srng,
-                         wb.order, s.Hq, s.Hkv, s.G, s.N, s.S, s.W, s.K, s.nC, ncs, s.nwin, qa, qz,
-                         QS, tau); }
+                         wb.order, wb.sitems, wb.nsi, s.B * s.Hkv, s.Hq, s.Hkv, s.G, s.N, s.S, s.W,
+                         s.K, s.nC, s.nwin, qa, qz, QS, tau); }
     // the routing query's gradient goes to dq_route, or to dq (then the
     // partials are added to it)
     { HilsProfScope ps_("k_bwd_rowstat", st);
@@ -773,8 +824,8 @@ hipError_t launch_mf(const HilsShape& s, const void* q, const void* qr, const vo
       hipLaunchKernelGGL((k_bwd_mf<D, 1>), dim3((unsigned)nblk), dim3(MT), sh1, st,
                          (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)dout,
                          wb.off, wb.ent, wb.pstat, wb.wstat, wb.wpart, wb.dqp, dk, dv, srng,
-                         wb.order, s.Hq, s.Hkv, s.G, s.N, s.S, s.W, s.K, s.nC, ncs, s.nwin, qa, qz,
-                         QS, tau); }
+                         wb.order, wb.sitems, wb.nsi, s.B * s.Hkv, s.Hq, s.Hkv, s.G, s.N, s.S, s.W,
+                         s.K, s.nC, s.nwin, qa, qz, QS, tau); }
     { HilsProfScope ps_("k_bwd_dq", st);
       hipLaunchKernelGGL(k_bwd_dq_reduce, dim3(rgrid), dim3(256), 0, st, wb.dqp, sel, dq, s.Hq,
                          s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, s.nwin, qa, QN, QS, nrows,
@@ -807,6 +858,9 @@ size_t hils_bwd_mf_dqp_bytes(const HilsShape& s) {
   return (size_t)s.B * s.Hq * hils_bwd_mf_slice(s) * (s.K + s.nwin) * s.d * 4;
 }
 size_t hils_bwd_mf_order_bytes(const HilsShape& s) { return (size_t)s.B * s.Hkv * s.nCc * 4; }
+size_t hils_bwd_mf_sitems_bytes(const HilsShape& s) {
+  return (size_t)stats_parts_max(s, hils_bwd_mf_slice(s)) * 8 + 16;   // parts, then the count
+}
 size_t hils_bwd_mf_srng_bytes(const HilsShape& s) {
   return hils_bwd_mf_slice(s) < s.N ? (size_t)s.B * s.Hkv * s.nC * 8 : 0;
 }
@@ -820,7 +874,8 @@ hipError_t hils_launch_backward_mf(const HilsShape& s, const void* q, const void
                                    const void* v, const void* dout, const int32_t* sel,
                                    const void* ksum, const float* bsum, float* dq, float* dqr,
                                    float* dk, float* dv, const HilsBwdBufs& wb, hipStream_t st) {
-  if (!hils_bwd_mf_ok(s) || !wb.wpart || !wb.dqp || !wb.order) return hipErrorInvalidValue;
+  if (!hils_bwd_mf_ok(s) || !wb.wpart || !wb.dqp || !wb.order || !wb.sitems || !wb.nsi)
+    return hipErrorInvalidValue;
   if (hils_bwd_mf_slice(s) < s.N && s.nC > 0 && !wb.srng) return hipErrorInvalidValue;
   if ((long long)s.B * s.Hkv * s.nCc <= 0) return hipSuccess;
   return s.d == 128 ? launch_mf<128>(s, q, qr, k, v, dout, sel, ksum, bsum, dq, dqr, dk, dv, wb, st)

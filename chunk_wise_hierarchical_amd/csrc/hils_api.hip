@@ -133,7 +133,7 @@ DecodeLayout decode_layout(const HilsShape& s) {
 }
 
 struct BwdLayout {
-  size_t ks, bs, off, ent, pstat, wstat, wpart, dqp, srng, order, total;
+  size_t ks, bs, off, ent, pstat, wstat, wpart, dqp, srng, order, sitems, total;
 };
 BwdLayout bwd_layout(const HilsShape& s) {
   BwdLayout L{};
@@ -150,6 +150,7 @@ BwdLayout bwd_layout(const HilsShape& s) {
   L.dqp = off;   off += align_up(mf ? hils_bwd_mf_dqp_bytes(s) : 0);
   L.srng = off;  off += align_up(mf ? hils_bwd_mf_srng_bytes(s) : 0);
   L.order = off; off += align_up(mf ? hils_bwd_mf_order_bytes(s) : 0);
+  L.sitems = off; off += align_up(mf ? hils_bwd_mf_sitems_bytes(s) : 0);
   L.total = off;
   return L;
 }
@@ -508,7 +509,9 @@ hils_status hils_prefill_backward(const hils_cfg* cfg, const void* q, const void
                  (float*)(w + L.wstat), mf ? (float*)(w + L.wpart) : nullptr,
                  mf ? (float*)(w + L.dqp) : nullptr,
                  mf && hils_bwd_mf_srng_bytes(s) ? (uint32_t*)(w + L.srng) : nullptr,
-                 mf ? (uint32_t*)(w + L.order) : nullptr};
+                 mf ? (uint32_t*)(w + L.order) : nullptr,
+                 mf ? (uint2*)(w + L.sitems) : nullptr,
+                 mf ? (uint32_t*)(w + L.sitems + hils_bwd_mf_sitems_bytes(s) - 16) : nullptr};
   return hip_status(hils_launch_backward(s, q, q_route ? q_route : q, k, v, lm_q, dout, sel, ks, bs,
                                          dq, dq_route, dk, dv, dlm, wb, st));
 }

@@ -15,7 +15,9 @@ struct HilsBwdBufs {
   float* wpart;     // [B*Hq*QS][nwin][4]  window partials per chunk: max, sum exp, sum exp dout.v
   float* dqp;       // [B*Hq*QS][K + nwin][d] dq partial per selected slot and window chunk
   uint32_t* srng;   // [B*Hkv*nC][2] each list's part in the slice (several slices only)
-  uint32_t* order;  // [B*Hkv*nCc]    the chunk passes' work items, heaviest first
+  uint32_t* order;  // [B*Hkv*nCc]    the gradient pass's work items, heaviest first
+  uint2* sitems;    // the stats pass's (item, part) entries, heaviest first
+  uint32_t* nsi;    // [1]            their number
 };
 
 // LDS bytes of the row kernel (window logits of G heads live in LDS)
@@ -39,6 +41,7 @@ size_t hils_bwd_mf_wpart_bytes(const HilsShape& s);
 size_t hils_bwd_mf_dqp_bytes(const HilsShape& s);
 size_t hils_bwd_mf_srng_bytes(const HilsShape& s);
 size_t hils_bwd_mf_order_bytes(const HilsShape& s);
+size_t hils_bwd_mf_sitems_bytes(const HilsShape& s);
 hipError_t hils_launch_backward_mf(const HilsShape& s, const void* q, const void* qr, const void* k,
                                    const void* v, const void* dout, const int32_t* sel,
                                    const void* ksum, const float* bsum, float* dq, float* dqr,
