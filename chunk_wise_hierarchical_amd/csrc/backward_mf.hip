@@ -66,7 +66,6 @@ using fastp::xshfl_f;
 
 constexpr int MT = 256;     // threads of the chunk passes (4 wavefronts)
 constexpr int QT = 32;      // contributions per tile
-constexpr int CB = 128;     // contributions described per batch
 constexpr int SPLIT = 4096; // stats pass: contributions per workgroup at most (heavy chunks split)
 
 template <int D, int PASS>
@@ -78,6 +77,12 @@ struct MfCol {
   static constexpr int DSN = 3 * QT * DSS;         // dS tile: three bf16 planes (hi, mid, lo)
   static constexpr int EXTRA = PASS ? DSN : 0;     // the dS tile, after both buffers
   static constexpr int DB = D / 64;                // 16-column blocks of dq per wavefront
+  // contributions described per batch: each batch restarts the pipeline (two
+  // dependent loads for the descriptors, then the first tile's rows), so the
+  // gradient pass takes long batches; the stats pass keeps its LDS small for
+  // occupancy
+  static constexpr int CB = PASS ? 512 : 128;
+  static_assert(CB % QT == 0 && CB >= 4 * QT, "whole tiles; the stats pass's [4][QT] sums fit dcf");
 };
 
 // A operand of a product reduced over the tile's queries (dV^T = dOut^T P,
@@ -115,9 +120,9 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   extern __shared__ __align__(16) unsigned char smm[];
   bf16_t* tiles = reinterpret_cast<bf16_t*>(smm);                        // [2][TILE]
   int* did = reinterpret_cast<int*>(smm + sizeof(bf16_t) * (2 * L::TILE + L::EXTRA));   // [CB] i << 4 | head
-  int* dslot = did + CB;                                                  // [CB] slot, K + window chunk
-  int2* dlim = reinterpret_cast<int2*>(dslot + CB);                       // [CB] attended keys lo..hi
-  float4* dcf = reinterpret_cast<float4*>(dlim + CB);   // [CB] alpha, lse, g, E; stats: [4][QT] partials
+  int* dslot = did + L::CB;                                // [CB] slot, K + window chunk
+  int2* dlim = reinterpret_cast<int2*>(dslot + L::CB);     // [CB] attended keys lo..hi
+  float4* dcf = reinterpret_cast<float4*>(dlim + L::CB);   // [CB] alpha, lse, g, E; stats: [4][QT] partials
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   // work item (c, b, g) = c (B Hkv) + b Hkv + g.  The gradient pass takes the
@@ -427,10 +432,10 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     clo = chi * part / np;
     chi = chi * (part + 1) / np;
   }
-  for (long long base = clo; base < chi; base += CB) {
-    const int nb = (int)min((long long)CB, chi - base);
+  for (long long base = clo; base < chi; base += L::CB) {
+    const int nb = (int)min((long long)L::CB, chi - base);
     __syncthreads();                                 // the previous batch is consumed
-    for (int t = tid; t < CB; t += MT) {
+    for (int t = tid; t < L::CB; t += MT) {
       const long long idx = base + t;
       int id = 0, slot = 0;
       float4 cf = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -499,7 +504,7 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 template <int D, int PASS>
 size_t mf_lds() {
   return sizeof(bf16_t) * (2 * MfCol<D, PASS>::TILE + MfCol<D, PASS>::EXTRA) +
-         (size_t)CB * (2 * sizeof(int) + sizeof(int2) + sizeof(float4));
+         (size_t)MfCol<D, PASS>::CB * (2 * sizeof(int) + sizeof(int2) + sizeof(float4));
 }
 
 // ---------------------------------------------------------------------------
