@@ -42,15 +42,17 @@
 // fp32 sums.  P and tau dS are fp32 and enter their products as bf16 sums
 // hi + lo (hi = bf16(x), lo = bf16(x - hi), within 2^-18 of x) in dv and dk,
 // and hi + mid + lo (within 2^-27) in dq, whose error gathers over all of a
-// query's keys: one MFMA per term, so the gradients keep fp32 accuracy.  The MFMA output layout of S
-// (lane l: key l % 16, queries 4 (l / 16) + r of each 16-query half) is the
-// B-operand layout of the second products once the tile's query positions are
-// permuted (position 8 g + t <-> query 16 (t / 4) + 4 g + t % 4); the
-// transpose loads gather the A operand in that order.  dq^T = K^T dS^T takes
-// dS through LDS (key-contiguous per query) and K^T fragments built once per
-// workgroup.  No floating-point atomics: every output element is written by
-// one workgroup or wavefront, in a fixed order (the integer atomics of the
-// work ordering change only the schedule).
+// query's keys: one MFMA per term, so the gradients keep fp32 accuracy.
+// In the gradient pass the MFMA output layout of S (lane l: key l % 16,
+// queries 4 (l / 16) + r of each 16-query half) is the B-operand layout of
+// the second products once the tile's query positions are permuted
+// (position 8 g + t <-> query 16 (t / 4) + 4 g + t % 4); the transpose loads
+// gather the A operand in that order.  dq^T = K^T dS^T takes dS through LDS
+// (key-contiguous per query) and K^T fragments built once per workgroup.  The
+// stats pass takes S^T instead (one query, four keys per lane), whose sums
+// over keys are short.  No floating-point atomics: every output element is
+// written by one workgroup or wavefront, in a fixed order (the integer
+// atomics of the work ordering change only the schedule).
 #include <cstdlib>
 
 #include "fast_common.h"
@@ -150,7 +152,9 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   const bool kown = kwave && kk < jn;
   const int NS = K + nwin;                           // dq partial slots per (query, head)
 
-  bf16x8_t kf[D / 32], vf[D / 32];                   // B operand: K[kk][32 s + 8 g4 ..]
+  // lane: K[kk][32 s + 8 g4 ..], V likewise; the B operand of S = Q K^T in
+  // the gradient pass, the A operand of S^T = K Q^T in the stats pass
+  bf16x8_t kf[D / 32], vf[D / 32];
   {
     const long long ro = (bg * (long long)N + j0 + (kown ? kk : 0)) * D + 8 * g4;
 #pragma unroll
