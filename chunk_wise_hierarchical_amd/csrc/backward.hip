@@ -230,6 +230,102 @@ k_bwd_lists(const int32_t* __restrict__ sel, uint32_t* __restrict__ off, uint32_
   }
 }
 
+// The same lists built by P workgroups per (batch, KV group), for long
+// sequences: sub-range r = 16 p + w (workgroup p, wavefront w) of R = 16 P
+// takes queries [N r / R, N (r + 1) / R).  k_bwd_lcount writes every
+// sub-range's per-chunk counts to cnt [B*Hkv][R][nC]; k_bwd_lscan turns them
+// into the list offsets and, in place, each sub-range's cursors (sub-range r
+// starts after sub-ranges 0 .. r-1 within every chunk); k_bwd_lscatter
+// scatters each sub-range in query order as above.  Needs 16 nC counters in
+// LDS.
+
+__global__ void __launch_bounds__(1024)
+k_bwd_lcount(const int32_t* __restrict__ sel, uint32_t* __restrict__ cnt, int N, int K, int nC,
+             int P) {
+  extern __shared__ uint32_t lc[];           // [16][nC]
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const long long bg = blockIdx.x;
+  const int R = 16 * P, r = 16 * (int)blockIdx.y + wv;
+  const int32_t* sg = sel + bg * N * (long long)K;
+  for (int t = tid; t < 16 * nC; t += 1024) lc[t] = 0u;
+  __syncthreads();
+  const long long qa = (long long)N * r / R, qz = (long long)N * (r + 1) / R;
+  uint32_t* cw = lc + (size_t)wv * nC;
+  for (long long t = qa * K + lane; t < qz * K; t += 64) {
+    const int c = sg[t];
+    if (c >= 0 && c < nC) atomicAdd(&cw[c], 1u);
+  }
+  __syncthreads();
+  uint32_t* cg = cnt + (bg * R + 16 * (long long)blockIdx.y) * nC;
+  for (int t = tid; t < 16 * nC; t += 1024) cg[t] = lc[t];
+}
+
+__global__ void __launch_bounds__(1024)
+k_bwd_lscan(uint32_t* __restrict__ cnt, uint32_t* __restrict__ off, int nC, int R) {
+  __shared__ uint32_t wtot[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const long long bg = blockIdx.x;
+  uint32_t* cg = cnt + bg * R * (long long)nC;
+  uint32_t* og = off + bg * (long long)(nC + 1);
+  uint32_t carry = 0;
+  for (int base = 0; base < nC; base += 1024) {
+    const int c = base + tid;
+    uint32_t v = 0u;
+    if (c < nC)
+      for (int r = 0; r < R; ++r) v += cg[(size_t)r * nC + c];
+    uint32_t x = v;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const uint32_t y = __shfl_up(x, m, 64);
+      if (lane >= m) x += y;
+    }
+    if (lane == 63) wtot[wv] = x;
+    __syncthreads();
+    uint32_t before = carry;
+    for (int u = 0; u < wv; ++u) before += wtot[u];
+    uint32_t all = carry;
+    for (int u = 0; u < 16; ++u) all += wtot[u];
+    __syncthreads();
+    if (c < nC) {
+      uint32_t e = before + x - v;
+      og[c] = e;
+      for (int r = 0; r < R; ++r) {          // cursor of sub-range r in chunk c
+        const uint32_t n = cg[(size_t)r * nC + c];
+        cg[(size_t)r * nC + c] = e;
+        e += n;
+      }
+    }
+    carry = all;
+    __syncthreads();
+  }
+  if (tid == 0) og[nC] = carry;
+}
+
+__global__ void __launch_bounds__(1024)
+k_bwd_lscatter(const int32_t* __restrict__ sel, const uint32_t* __restrict__ cnt,
+               uint32_t* __restrict__ ent, int N, int K, int nC, int P) {
+  extern __shared__ uint32_t lc[];           // [16][nC] cursors
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const long long bg = blockIdx.x;
+  const int R = 16 * P, r = 16 * (int)blockIdx.y + wv;
+  const int32_t* sg = sel + bg * N * (long long)K;
+  uint32_t* eg = ent + bg * N * (long long)K;
+  const uint32_t* cg = cnt + (bg * R + 16 * (long long)blockIdx.y) * nC;
+  for (int t = tid; t < 16 * nC; t += 1024) lc[t] = cg[t];
+  __syncthreads();
+  uint32_t* cw = lc + (size_t)wv * nC;
+  const int qa = (int)((long long)N * r / R), qz = (int)((long long)N * (r + 1) / R);
+  for (int i = qa; i < qz; ++i) {
+    for (int s2 = lane; s2 < K; s2 += 64) {
+      const int c = sg[(long long)i * K + s2];
+      if (c >= 0 && c < nC) {
+        const uint32_t pos = atomicAdd(&cw[c], 1u);
+        eg[pos] = ((uint32_t)i << 8) | (uint32_t)s2;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // per query row: statistics and dq
 
@@ -1058,6 +1154,19 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
 
 }  // namespace
 
+// workgroups per (sequence, KV group) of the list kernels: one per 4096
+// queries (each wavefront then scatters at most 256), at most 64, one when
+// the per-wavefront counters do not fit LDS
+int hils_bwd_list_parts(const HilsShape& s) {
+  if ((size_t)16 * s.nC * sizeof(uint32_t) > 128 * 1024 || s.nC <= 0) return 1;
+  const int p = (s.N + 4095) / 4096;
+  return p < 1 ? 1 : (p > 64 ? 64 : p);
+}
+size_t hils_bwd_list_count_bytes(const HilsShape& s) {
+  const int p = hils_bwd_list_parts(s);
+  return p > 1 ? (size_t)s.B * s.Hkv * 16 * p * s.nC * sizeof(uint32_t) : 0;
+}
+
 size_t hils_bwd_rows_lds(const HilsShape& s) {
   const int L = s.W + s.S - 1;
   const int Lp = (L + 3) & ~3;
@@ -1071,13 +1180,27 @@ hipError_t hils_launch_backward(const HilsShape& s, const void* q, const void* q
                                 float* dk, float* dv, float* dlm, const HilsBwdBufs& wb,
                                 hipStream_t st) {
   const float tau = (float)s.tau;
-  // per-wavefront counters while they fit 128 KB of LDS
+  // per-wavefront counters while they fit 128 KB of LDS; P workgroups per
+  // (sequence, KV group) when the counts buffer is there
   const int lpar = (size_t)16 * s.nC * sizeof(uint32_t) <= 128 * 1024;
   const size_t lshm = sizeof(uint32_t) * (size_t)(lpar ? 16 : 1) * (size_t)(s.nC > 0 ? s.nC : 1);
-  hils_allow_lds((const void*)k_bwd_lists, lshm);
-  { HilsProfScope ps_("k_bwd_lists", st);
+  const int lP = hils_bwd_list_parts(s);
+  if (lP > 1 && lpar && s.nC > 0 && wb.lcnt) {
+    hils_allow_lds((const void*)k_bwd_lcount, lshm);
+    hils_allow_lds((const void*)k_bwd_lscatter, lshm);
+    HilsProfScope ps_("k_bwd_lists", st);
+    hipLaunchKernelGGL(k_bwd_lcount, dim3((unsigned)(s.B * s.Hkv), (unsigned)lP), dim3(1024), lshm,
+                       st, sel, wb.lcnt, s.N, s.K, s.nC, lP);
+    hipLaunchKernelGGL(k_bwd_lscan, dim3((unsigned)(s.B * s.Hkv)), dim3(1024), 0, st, wb.lcnt,
+                       wb.off, s.nC, 16 * lP);
+    hipLaunchKernelGGL(k_bwd_lscatter, dim3((unsigned)(s.B * s.Hkv), (unsigned)lP), dim3(1024),
+                       lshm, st, sel, wb.lcnt, wb.ent, s.N, s.K, s.nC, lP);
+  } else {
+    hils_allow_lds((const void*)k_bwd_lists, lshm);
+    HilsProfScope ps_("k_bwd_lists", st);
     hipLaunchKernelGGL(k_bwd_lists, dim3((unsigned)(s.B * s.Hkv)), dim3(1024), lshm, st, sel,
-                       wb.off, wb.ent, s.N, s.K, s.nC, lpar); }
+                       wb.off, wb.ent, s.N, s.K, s.nC, lpar);
+  }
   // the all-keys row kernel when every attended key's logit fits 64 KB of LDS
   const bool all_keys = bwd_rows2_lds(s) <= 65536;
   const size_t rshm = all_keys ? bwd_rows2_lds(s) : hils_bwd_rows_lds(s);

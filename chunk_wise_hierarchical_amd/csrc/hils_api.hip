@@ -133,7 +133,7 @@ DecodeLayout decode_layout(const HilsShape& s) {
 }
 
 struct BwdLayout {
-  size_t ks, bs, off, ent, pstat, wstat, wpart, dqp, srng, order, sitems, total;
+  size_t ks, bs, off, ent, pstat, wstat, wpart, dqp, srng, order, sitems, lcnt, total;
 };
 BwdLayout bwd_layout(const HilsShape& s) {
   BwdLayout L{};
@@ -151,6 +151,7 @@ BwdLayout bwd_layout(const HilsShape& s) {
   L.srng = off;  off += align_up(mf ? hils_bwd_mf_srng_bytes(s) : 0);
   L.order = off; off += align_up(mf ? hils_bwd_mf_order_bytes(s) : 0);
   L.sitems = off; off += align_up(mf ? hils_bwd_mf_sitems_bytes(s) : 0);
+  L.lcnt = off;  off += align_up(hils_bwd_list_count_bytes(s));
   L.total = off;
   return L;
 }
@@ -511,7 +512,8 @@ hils_status hils_prefill_backward(const hils_cfg* cfg, const void* q, const void
                  mf && hils_bwd_mf_srng_bytes(s) ? (uint32_t*)(w + L.srng) : nullptr,
                  mf ? (uint32_t*)(w + L.order) : nullptr,
                  mf ? (uint2*)(w + L.sitems) : nullptr,
-                 mf ? (uint32_t*)(w + L.sitems + hils_bwd_mf_sitems_bytes(s) - 16) : nullptr};
+                 mf ? (uint32_t*)(w + L.sitems + hils_bwd_mf_sitems_bytes(s) - 16) : nullptr,
+                 hils_bwd_list_count_bytes(s) ? (uint32_t*)(w + L.lcnt) : nullptr};
   return hip_status(hils_launch_backward(s, q, q_route ? q_route : q, k, v, lm_q, dout, sel, ks, bs,
                                          dq, dq_route, dk, dv, dlm, wb, st));
 }

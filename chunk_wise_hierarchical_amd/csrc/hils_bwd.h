@@ -18,7 +18,13 @@ struct HilsBwdBufs {
   uint32_t* order;  // [B*Hkv*nCc]    the gradient pass's work items, heaviest first
   uint2* sitems;    // the stats pass's (item, part) entries, heaviest first
   uint32_t* nsi;    // [1]            their number
+  // list kernels over several workgroups per (sequence, KV group) (else null):
+  uint32_t* lcnt;   // [B*Hkv][16 P][nC] per sub-range counts, then cursors
 };
+
+// workgroups per (sequence, KV group) of the list kernels, and their counts buffer
+int hils_bwd_list_parts(const HilsShape& s);
+size_t hils_bwd_list_count_bytes(const HilsShape& s);
 
 // LDS bytes of the row kernel (window logits of G heads live in LDS)
 size_t hils_bwd_rows_lds(const HilsShape& s);

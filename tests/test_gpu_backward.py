@@ -130,6 +130,13 @@ def test_backward_query_slices(monkeypatch):
     _case(w, label="6 slices of 64")
 
 
+def test_backward_lists_over_several_workgroups():
+    # N > 4096: the selection lists are built by two workgroups per (sequence,
+    # KV group), each wavefront scattering its own sub-range of the queries
+    w = synth.get_workload("prefill_64k", N=5000, Hq=4, Hkv=2, W=128, K=4, regime="iid")
+    _case(w, label="lists over 2 workgroups")
+
+
 def test_backward_deterministic():
     w = synth.get_workload("prefill_64k", N=700, Hq=4, Hkv=1, d=64, S=32, W=64, K=4, regime="iid")
     gr, (x, dout, sel) = _case(w, label="determinism")
