@@ -437,7 +437,7 @@ def ref_decode_multi(q, k_cache, v_cache, seqlen, lm, S, W, K, q_route=None, sca
 
 
 def ref_backward(q, k, v, lm, dout, S, W, K, q_route=None, scale=None, sel=None,
-                 mode="surrogate", store="bf16"):
+                 mode="surrogate", store="bf16", rows=None):
     """Gradients of L = sum(dout * out) for the HiLS prefill of every position.
 
     The top-K selection is a discrete choice and is held fixed (given as `sel`
@@ -452,6 +452,11 @@ def ref_backward(q, k, v, lm, dout, S, W, K, q_route=None, scale=None, sel=None,
     The stored (rounded per `store`) summaries enter s_hat as in the forward;
     their rounding is not differentiated.  Returns dict(dq, dk, dv, dlm,
     dq_route (None without q_route), sel).
+
+    `rows` (a set of (b, g, i)), when given, keeps only those query rows'
+    terms: dq of a listed row is then exact, and so are dk, dv of a key (and
+    dlm of a chunk) all of whose attending rows (window and selecting) are
+    listed; everything else is partial.
     """
     q, k, v, lm, dout, q_route = map(_arr, (q, k, v, lm, dout, q_route))
     B, Hq, N, d = q.shape
@@ -477,6 +482,8 @@ def ref_backward(q, k, v, lm, dout, S, W, K, q_route=None, scale=None, sel=None,
     for b in range(B):
         for g in range(Hkv):
             for i in range(N):
+                if rows is not None and (b, g, i) not in rows:
+                    continue
                 w0 = _window_start(i, W, S)
                 chunks = [int(c) for c in sel[b, g, i] if c >= 0]
                 kw, vw = k64[b, g, w0:i + 1], v64[b, g, w0:i + 1]
@@ -544,6 +551,18 @@ def ref_backward(q, k, v, lm, dout, S, W, K, q_route=None, scale=None, sel=None,
                 dk[b, g, c * S:(c + 1) * S] += tau * np.outer(dt, lm64[b, h, c]) + np.outer(pi, dks[b, h, c])
     return dict(dq=dq, dk=dk, dv=dv, dlm=dlm, dq_route=(dqr if q_route is not None else None),
                 sel=sel)
+
+
+def ref_attending_rows(sel, b, g, j, S, W):
+    """The query rows (b, g, i) whose attention reads key j of KV group g of
+    sequence b (section 2.1 window, section 3 selection): those whose window
+    [window_start(i), i] holds j and those whose selection holds j's chunk."""
+    sel = np.asarray(sel)
+    N = sel.shape[2]
+    c = j // S
+    rows = {(b, g, i) for i in range(j, N) if _window_start(i, W, S) <= j}
+    rows |= {(b, g, int(i)) for i in np.nonzero((sel[b, g] == c).any(axis=-1))[0]}
+    return rows
 
 
 # ---------------------------------------------------------------------------

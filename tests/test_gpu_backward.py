@@ -137,6 +137,52 @@ def test_backward_lists_over_several_workgroups():
     _case(w, label="lists over 2 workgroups")
 
 
+def test_backward_full_size_sampled():
+    """prefill_8k at its full size (B=2, N=8192, 16/16 heads, W=512, K=16), the
+    launch bench.py times.  The selection is an input of the backward (held
+    fixed): a seeded random choice of min(K, |C_i|) candidate chunks per row,
+    the same for both sides.  The oracle runs only the rows attending three
+    sampled keys plus 24 sampled query rows, which makes those keys' dk, dv,
+    their chunks' dlm and those rows' dq exact (ref_backward, `rows`)."""
+    w = synth.get_workload("prefill_8k")
+    x = {k2: v2.cuda() for k2, v2 in synth.make_prefill_inputs(w).items()}
+    g0 = torch.Generator(device="cpu").manual_seed(31)
+    dout = torch.randn(x["q"].shape, generator=g0).to(x["q"].dtype).cuda()
+    B, Hkv, N, S, W, K = w.B, w.Hkv, w.N, w.S, w.W, w.K
+    nC = N // S
+    rng = np.random.default_rng(8192)
+    ncand = np.array([O.n_candidates(i, W, S) for i in range(N)])
+    keys = rng.random((B, Hkv, N, nC), dtype=np.float32)
+    keys[:, :, np.arange(nC)[None, :] >= ncand[:, None]] = np.inf
+    order = np.argsort(keys, axis=-1)[..., :K]
+    sel = np.where(np.arange(K)[None, :] < np.minimum(K, ncand)[:, None], order, -1).astype(np.int32)
+    _say(f"[backward] full-size prefill_8k, random selection ({(sel >= 0).sum()} pairs)")
+    gr = hils.prefill_backward(x["q"], x["k"], x["v"], x["lm"], dout,
+                               torch.from_numpy(sel).cuda().contiguous(), S, W, K)
+    torch.cuda.synchronize()
+    samp_keys = [(0, 0, 1000), (1, 5, 4100), (0, 15, N - 70)]
+    samp_rows = {(int(rng.integers(B)), int(rng.integers(Hkv)), int(rng.integers(N))) for _ in range(24)}
+    rows = set(samp_rows)
+    for (b, g, j) in samp_keys:
+        rows |= O.ref_attending_rows(sel, b, g, j, S, W)
+    _say(f"   oracle over {len(rows)} rows")
+    xn = {k2: np32(v2) for k2, v2 in x.items()}
+    ref = O.ref_backward(xn["q"], xn["k"], xn["v"], xn["lm"], np32(dout), S, W, K, sel=sel,
+                         store=w.dtype, rows=rows)
+    G = w.Hq // Hkv
+    pairs = {"dk": [(b, g, j) for (b, g, j) in samp_keys], "dv": [(b, g, j) for (b, g, j) in samp_keys],
+             "dlm": [(b, g * G + r, j // S) for (b, g, j) in samp_keys for r in range(G)],
+             "dq": [(b, g * G + r, i) for (b, g, i) in samp_rows for r in range(G)]}
+    errs = {}
+    for n, idx in pairs.items():
+        got = np.stack([gr[n][t].cpu().numpy().astype(np.float64) for t in idx])
+        want = np.stack([ref[n][t] for t in idx])
+        errs[n] = np.abs(got - want).max() / max(np.abs(want).max(), 1e-30)
+    _say("   relative gradient errors " + ", ".join(f"{n} {e:.3g}" for n, e in errs.items()))
+    for n, err in errs.items():
+        assert err <= TOL, f"{n}: relative error {err:.3g} > {TOL}"
+
+
 def test_backward_deterministic():
     w = synth.get_workload("prefill_64k", N=700, Hq=4, Hkv=1, d=64, S=32, W=64, K=4, regime="iid")
     gr, (x, dout, sel) = _case(w, label="determinism")

@@ -502,6 +502,34 @@ def test_backward_matches_finite_differences(mode, route):
         assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (mode, name, fd, an)
 
 
+def test_backward_row_restriction_is_exact_where_complete():
+    """With `rows` restricted to the rows attending a key (plus some query
+    rows), the key's dk, dv, its chunk's dlm and the listed rows' dq are those
+    of the unrestricted backward, term for term; a key whose attending rows
+    are left out gets a different dk."""
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, N, d, S, W, K = 1, 4, 2, 200, 8, 16, 40, 3
+    q, qr, dout = (rng.standard_normal((B, Hq, N, d)) for _ in range(3))
+    k, v = (rng.standard_normal((B, Hkv, N, d)) for _ in range(2))
+    lm = rng.standard_normal((B, Hq, N // S, d))
+    full = O.ref_backward(q, k, v, lm, dout, S, W, K, q_route=qr, store="f64")
+    sel = full["sel"]
+    g, j = 1, 37                                     # a key of chunk 2, selected by later rows
+    assert (sel[0, g] == j // S).any()
+    rows = O.ref_attending_rows(sel, 0, g, j, S, W) | {(0, 0, 150), (0, 1, 199)}
+    part = O.ref_backward(q, k, v, lm, dout, S, W, K, q_route=qr, sel=sel, store="f64", rows=rows)
+    np.testing.assert_array_equal(part["dk"][0, g, j], full["dk"][0, g, j])
+    np.testing.assert_array_equal(part["dv"][0, g, j], full["dv"][0, g, j])
+    for h in range(g * (Hq // Hkv), (g + 1) * (Hq // Hkv)):
+        np.testing.assert_array_equal(part["dlm"][0, h, j // S], full["dlm"][0, h, j // S])
+    for (b, gg, i) in [(0, 0, 150), (0, 1, 199)]:
+        for h in range(gg * (Hq // Hkv), (gg + 1) * (Hq // Hkv)):
+            np.testing.assert_array_equal(part["dq"][b, h, i], full["dq"][b, h, i])
+            np.testing.assert_array_equal(part["dq_route"][b, h, i], full["dq_route"][b, h, i])
+    # a key of the other group, whose rows are not all listed, differs
+    assert np.abs(part["dk"][0, 0, 37] - full["dk"][0, 0, 37]).max() > 1e-6
+
+
 def test_backward_window_only_is_causal_attention_gradient():
     """With the window covering every position (no candidate chunks) HiLS is
     causal softmax attention; its gradients equal torch autograd of the
