@@ -183,6 +183,17 @@ def test_backward_full_size_sampled():
         assert err <= TOL, f"{n}: relative error {err:.3g} > {TOL}"
 
 
+def test_backward_more_than_64_slots():
+    # K = 100 selected chunks of 16: slots 64.. live in a second register of
+    # the row pass and a second ballot word of the dq reduction (bf16, matrix
+    # cores); the fp32 case takes the vector-ALU kernels
+    w = synth.get_workload("prefill_64k", N=2200, Hq=2, Hkv=1, S=16, W=64, K=100, regime="iid")
+    _case(w, q_route=True, label="K = 100 bf16")
+    w = synth.get_workload("prefill_64k", N=1900, Hq=2, Hkv=2, d=64, S=16, W=48, K=100,
+                           regime="iid", dtype="f32")
+    _case(w, label="K = 100 fp32")
+
+
 def test_backward_deterministic():
     w = synth.get_workload("prefill_64k", N=700, Hq=4, Hkv=1, d=64, S=32, W=64, K=4, regime="iid")
     gr, (x, dout, sel) = _case(w, label="determinism")
