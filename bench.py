@@ -589,8 +589,9 @@ def main():
     ap.add_argument("--union", action="store_true",
                     help="prefill attention by query block over the union of its chunks "
                          "instead of the default per-chunk buckets")
-    ap.add_argument("--backward-workload", default="prefill_8k",
-                    help="workload of the backward measurement ('' skips it)")
+    ap.add_argument("--backward-workload", default="prefill_8k,prefill_64k",
+                    help="workloads of the backward measurement, comma-separated: the first "
+                         "is `backward`, the others `backward_more` ('' skips it)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB copy first (counter scale for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -655,11 +656,14 @@ def main():
             more[name], _ = decode_bench(torch, hils, _lib, synth.get_workload(name),
                                          args.decode_steps, args.warmup, log)
 
-    bwd = None
-    if args.backward_workload:
+    bwd, bwd_more = None, {}
+    for n, name in enumerate([n for n in args.backward_workload.split(",") if n]):
         torch.cuda.empty_cache()
-        bwd = backward_bench(torch, hils, _lib, synth.get_workload(args.backward_workload),
-                             args.steps, log)
+        rec = backward_bench(torch, hils, _lib, synth.get_workload(name), args.steps, log)
+        if n == 0:
+            bwd = rec
+        else:
+            bwd_more[name] = rec
 
     line = {
         "metric": "prefill tokens/s and decode steps/s at 512K ctx; % of MFMA/HBM roofline",
@@ -686,6 +690,7 @@ def main():
         "decode": dec,
         "more_workloads": more,
         "backward": bwd,
+        "backward_more": bwd_more,
     }
     print(json.dumps(line), flush=True)
 
