@@ -255,15 +255,24 @@ constexpr int SEL_LDS_KEYS = HILS_DEC_SEL_LDS_KEYS;   // keys kept in LDS (96 KB
 // so both paths take tied keys lowest chunk id first.
 enum { SEL_WHOLE = 0, SEL_PART = 1, SEL_MERGE = 2 };
 
-template <int PH>
+// The radix histogram is kept in SEL_REP copies, lane l counting into copy
+// l % SEL_REP: the keys of one query sit within a few octaves, so most of a
+// pass's keys share a digit and one shared copy would serialise their atomics.
+constexpr int SEL_REP = 32;
+
+// GT > 0: G is GT, and every head's scores of a round of 8 x SEL_NT candidates
+// are loaded together (before the log-sum-exp, whose latency they overlap).
+template <int PH, int GT>
 __global__ void __launch_bounds__(SEL_NT)
 k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
              const int32_t* __restrict__ seqlen, uint32_t* __restrict__ keys, uint2* __restrict__ cand,
-             int32_t* __restrict__ sel, float* __restrict__ slog, int Hq, int Hkv, int G, int nmax,
+             int32_t* __restrict__ sel, float* __restrict__ slog, int Hq, int Hkv, int Gr, int nmax,
              int nsb, int N, int S, int W, int K, int M, int span, int P) {
   extern __shared__ uint32_t sel_keys_lds[];
-  __shared__ uint32_t hist[256];
+  __shared__ __align__(16) uint32_t hist[256 * SEL_REP];
+  __shared__ uint32_t htot[256];
   __shared__ float Lh[8];
+  const int G = GT > 0 ? GT : Gr;
   __shared__ int wsum[SEL_NW];
   __shared__ int sh_digit, sh_need;
 
@@ -305,6 +314,21 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
       cid[t] = (int32_t)e.y;
     }
   } else {
+    constexpr int KB = 8;                       // candidates per thread and round (GT > 0)
+    constexpr int GB = GT > 0 ? GT : 1;
+    float xb[GB][KB];
+    auto load_round = [&](int base) {
+#pragma unroll
+      for (int r = 0; r < GB; ++r) {
+        const float* sr = scores + hrow(r) * nmax + c0;
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+          const int c = base + u * SEL_NT + tid;
+          xb[r][u] = (c < cnt) ? sr[c] : -INFINITY;
+        }
+      }
+    };
+    if (GT > 0) load_round(0);
     if (G > 1) {
       // per-head log-sum-exp from the scoring workgroups' (max, sum exp) partials
       for (int r = wv; r < G; r += SEL_NW) {
@@ -320,6 +344,19 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
       }
       __syncthreads();
     }
+    if constexpr (GT > 0) {
+      for (int base = 0; base < cnt; base += KB * SEL_NT) {
+        if (base > 0) load_round(base);
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+          float gs = -INFINITY;
+#pragma unroll
+          for (int r = 0; r < GB; ++r) gs = fmaxf(gs, xb[r][u] - ((GT == 1) ? 0.0f : Lh[r]));
+          const int c = base + u * SEL_NT + tid;
+          if (c < cnt) ky[c] = f32_order_key(gs);
+        }
+      }
+    } else {
     constexpr int KU = 4;
     for (int base = 0; base < cnt; base += KU * SEL_NT) {
       float gs[KU];
@@ -343,24 +380,34 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
         if (c < cnt) ky[c] = f32_order_key(gs[u]);
       }
     }
+    }
   }
   if (tid == 0) sh_need = kl;
   __syncthreads();
 
   // MSD radix select of the kl-th largest 32-bit key
   uint32_t prefix = 0, pmask = 0;
+  const uint32_t rep = (uint32_t)lane & (SEL_REP - 1);
   for (int p = 3; p >= 0; --p) {
-    if (tid < 256) hist[tid] = 0;
+    for (int t = tid; t < 64 * SEL_REP; t += SEL_NT)
+      reinterpret_cast<uint4*>(hist)[t] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
     for (int c = tid; c < cnt; c += SEL_NT) {
       const uint32_t key = ky[c];
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> (8 * p)) & 255u], 1u);
+      if ((key & pmask) == prefix) atomicAdd(&hist[((key >> (8 * p)) & 255u) * SEL_REP + rep], 1u);
+    }
+    __syncthreads();
+    if (tid < 256) {           // bin tid's total over the copies, starting at a
+      uint32_t tot = 0;        // rotated copy so that a wave's reads spread over the banks
+#pragma unroll
+      for (int j = 0; j < SEL_REP; ++j) tot += hist[tid * SEL_REP + ((j + tid) & (SEL_REP - 1))];
+      htot[tid] = tot;
     }
     __syncthreads();
     if (tid < 64) {            // one wave: suffix sums over 256 bins, 4 per lane
       uint32_t h4[4], s4 = 0;
 #pragma unroll
-      for (int u = 3; u >= 0; --u) { s4 += hist[tid * 4 + u]; h4[u] = s4; }
+      for (int u = 3; u >= 0; --u) { s4 += htot[tid * 4 + u]; h4[u] = s4; }
       // totals of all higher lanes: inclusive suffix scan over the wave
       uint32_t suf = s4;
 #pragma unroll
@@ -1045,25 +1092,28 @@ void launch_decode_t(const HilsShape& s, const void* q, const void* qr, const vo
   hils_dec_select_split(s, P, span);
   const int nm = s.nmax > 0 ? s.nmax : 1;
   const unsigned rows = (unsigned)(s.B * s.Hkv * s.M);
+  auto select = [&](auto ph, dim3 grid, size_t shm, int sp) {
+    constexpr int PH = decltype(ph)::value;
+    auto launch = [&](auto kern) {
+      hils_allow_lds((const void*)kern, shm);
+      hipLaunchKernelGGL(kern, grid, dim3(SEL_NT), shm, st, scores, lsep, seqlen, keys, cand, sel, slog,
+                         s.Hq, s.Hkv, s.G, nm, (int)nsb, s.N, s.S, s.W, s.K, s.M, sp, P);
+    };
+    if (s.G == 1) launch(k_dec_select<PH, 1>);
+    else if (s.G == 2) launch(k_dec_select<PH, 2>);
+    else if (s.G == 4) launch(k_dec_select<PH, 4>);
+    else if (s.G == 8) launch(k_dec_select<PH, 8>);
+    else launch(k_dec_select<PH, 0>);
+  };
   if (P == 1) {
-    const size_t sshm = (size_t)4 * (size_t)min(nm, SEL_LDS_KEYS);
-    hils_allow_lds((const void*)k_dec_select<SEL_WHOLE>, sshm);
     HilsProfScope ps_("k_dec_select", st);
-    hipLaunchKernelGGL(k_dec_select<SEL_WHOLE>, dim3(rows), dim3(SEL_NT), sshm, st, scores, lsep,
-                       seqlen, keys, cand, sel, slog, s.Hq, s.Hkv, s.G, nm, (int)nsb, s.N, s.S, s.W,
-                       s.K, s.M, nm, 1);
+    select(std::integral_constant<int, SEL_WHOLE>(), dim3(rows), (size_t)4 * (size_t)min(nm, SEL_LDS_KEYS), nm);
   } else {
-    const size_t pshm = (size_t)4 * (size_t)min(span, SEL_LDS_KEYS);
-    const size_t mshm = (size_t)8 * (size_t)P * s.K;          // keys and chunk ids
-    hils_allow_lds((const void*)k_dec_select<SEL_PART>, pshm);
-    hils_allow_lds((const void*)k_dec_select<SEL_MERGE>, mshm);
     HilsProfScope ps_("k_dec_select", st);
-    hipLaunchKernelGGL(k_dec_select<SEL_PART>, dim3(rows, P), dim3(SEL_NT), pshm, st, scores, lsep,
-                       seqlen, keys, cand, sel, slog, s.Hq, s.Hkv, s.G, nm, (int)nsb, s.N, s.S, s.W,
-                       s.K, s.M, span, P);
-    hipLaunchKernelGGL(k_dec_select<SEL_MERGE>, dim3(rows), dim3(SEL_NT), mshm, st, scores, lsep,
-                       seqlen, keys, cand, sel, slog, s.Hq, s.Hkv, s.G, nm, (int)nsb, s.N, s.S, s.W,
-                       s.K, s.M, span, P);
+    select(std::integral_constant<int, SEL_PART>(), dim3(rows, P), (size_t)4 * (size_t)min(span, SEL_LDS_KEYS),
+           span);
+    // keys and chunk ids of the P * K candidates
+    select(std::integral_constant<int, SEL_MERGE>(), dim3(rows), (size_t)8 * (size_t)P * s.K, span);
   }
   const dim3 agrid(s.B * s.Hkv * s.M, win_in_score ? s.K : NS);
   if (hils_dec_union(s)) {
