@@ -387,6 +387,11 @@ def test_decode_mha_and_wide_groups():
     _decode_case(w, [8192, 5000], label="G=2")
     w = synth.get_workload("decode_512k", N=8192, B=2, Hq=16, Hkv=2, K=16, W=512)
     _decode_case(w, [8192, 6001], label="G=8")
+    # group sizes the selection does not specialise on (heads taken in a loop)
+    w = synth.get_workload("decode_512k", N=8192, B=2, Hq=6, Hkv=2, K=16, W=512)
+    _decode_case(w, [8192, 6001], label="G=3")
+    w = synth.get_workload("decode_512k", N=6000, B=1, Hq=6, Hkv=1, K=100, W=300)
+    _decode_case(w, [5999], label="G=6, K=100")
     # chunk size that is not a multiple of 4, window not a multiple of the chunk
     w = synth.get_workload("decode_512k", N=4400, B=2, Hq=4, Hkv=2, S=22, W=100, K=6)
     _decode_case(w, [4400, 3333], label="S=22")
