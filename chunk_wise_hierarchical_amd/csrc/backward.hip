@@ -835,11 +835,18 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
 
   float kj[CE], vj[CE], dkj[CE], dvj[CE];
   const int jr = act ? jt : 0;                       // inactive tokens read row 0, zeroed
-  load_slice16<T>(kb + (long long)jr * d + e0, DQ, kj);
-  load_slice16<T>(vb + (long long)jr * d + e0, DQ, vj);
+  // (the summary-only variant needs K only after its contributions)
+  auto load_kv = [&]() __attribute__((always_inline)) {
+    load_slice16<T>(kb + (long long)jr * d + e0, DQ, kj);
+    if (!SUMONLY) load_slice16<T>(vb + (long long)jr * d + e0, DQ, vj);
+#pragma unroll
+    for (int u = 0; u < CE; ++u) {
+      if (!act) { kj[u] = 0.0f; vj[u] = 0.0f; }
+    }
+  };
+  if (!SUMONLY) load_kv();
 #pragma unroll
   for (int u = 0; u < CE; ++u) {
-    if (!act) { kj[u] = 0.0f; vj[u] = 0.0f; }
     dkj[u] = 0.0f;
     dvj[u] = 0.0f;
   }
@@ -859,6 +866,21 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
   double sa[8][2], sb[8];
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr) { sa[rr][0] = 0.0; sa[rr][1] = 0.0; sb[rr] = 0.0; }
+  // With GT > 0 (the summary-only variant follows the matrix-core passes, so
+  // d is 64 or 128) a row is read as PR = d / 8 pieces of 16 bytes: lane
+  // (rq, pc) = (lane / PR, lane % PR) takes elements 8 pc .. 8 pc + 7 of rows
+  // RPI j + rq (RPI = 64 / PR) of its wavefront's 64, whose head (RPI j + rq)
+  // % GT is one of NHW per lane (slot j % NHW)
+  constexpr int NHW = GT == 8 ? 2 : 1;
+  const int PR = d / 8, RPI = 64 / PR;
+  const int rq = (tid & 63) / PR, pc = (tid & 63) % PR;
+  double sw[NHW][8], sbw[NHW];
+#pragma unroll
+  for (int h2 = 0; h2 < NHW; ++h2) {
+    sbw[h2] = 0.0;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) sw[h2][x] = 0.0;
+  }
 
   const bool summ = c < nC;
   const uint32_t p0 = summ ? off[bg * (nC + 1) + c] : 0u;
@@ -902,6 +924,38 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
       // sixteen rows in flight; with the group size GT fixed at compile time
       // (u0 and ub are multiples of it) contribution ub + x has head x % GT
       const int u0 = 64 * wvs, u1 = min(nb, u0 + 64);
+      if constexpr (GT > 0) {
+        // the wavefront's 64 rows as 16-byte pieces, eight rows per lane in flight
+        for (int jh = 0; jh < PR; jh += 8) {
+          uint4 rv[8];
+#pragma unroll
+          for (int j2 = 0; j2 < 8; ++j2) {
+            const int u = u0 + RPI * (jh + j2) + rq;
+            rv[j2] = make_uint4(0u, 0u, 0u, 0u);
+            if (u < u1) {
+              const int dd = di[u];
+              rv[j2] = *reinterpret_cast<const uint4*>(qr + ((hb + (dd & 15)) * N + (dd >> 4)) * (long long)d + 8 * pc);
+            }
+          }
+#pragma unroll
+          for (int j2 = 0; j2 < 8; ++j2) {
+            const int u = u0 + RPI * (jh + j2) + rq;
+            if (u < u1) {
+              const double xt = (double)dsx[u * 4 + 3];
+              const double tx = (double)tau * xt;
+              const uint32_t w4[4] = {rv[j2].x, rv[j2].y, rv[j2].z, rv[j2].w};
+              const int h2 = j2 % NHW;               // jh is a multiple of NHW
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                sw[h2][2 * t] = fma(tx, (double)__uint_as_float(w4[t] << 16), sw[h2][2 * t]);
+                sw[h2][2 * t + 1] = fma(tx, (double)__uint_as_float(w4[t] & 0xffff0000u), sw[h2][2 * t + 1]);
+              }
+              if (pc == 0) sbw[h2] += xt;
+            }
+          }
+        }
+        continue;
+      }
       for (int ub = u0; ub < u1; ub += 16) {
         uint32_t rv[16];
 #pragma unroll
@@ -1032,7 +1086,26 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
     }
   }
   __syncthreads();
-  if constexpr (SUMONLY) {
+  if constexpr (SUMONLY && GT > 0) {
+    // the wavefronts' sums in order; within a wavefront one row group (rq) at
+    // a time, since the groups of one head share their dks elements
+    for (int w = 0; w < CT / 64; ++w) {
+      if (wvs == w) {
+        for (int t = 0; t < RPI; ++t) {
+          if (rq == t) {
+#pragma unroll
+            for (int h2 = 0; h2 < NHW; ++h2) {
+              const int hd = (RPI * h2 + rq) % GT;
+#pragma unroll
+              for (int x = 0; x < 8; ++x) dks[hd * d + 8 * pc + x] += sw[h2][x];
+              if (pc == 0) dbs[hd] += sbw[h2];
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+  } else if constexpr (SUMONLY) {
     for (int w = 0; w < CT / 64; ++w) {              // the wavefronts' sums, in order
       if (wvs == w) {
 #pragma unroll
@@ -1062,6 +1135,7 @@ k_bwd_cols(const T* __restrict__ q, const T* __restrict__ qr, const T* __restric
       __syncthreads();
     }
   }
+  if (SUMONLY) load_kv();
   // summaries of the chunk (one per query head of the group)
   if (summ) {
     for (int r = 0; r < G; ++r) {
