@@ -6,9 +6,10 @@
 // of a group, one shared top-K).
 //
 // One workgroup (4 wavefronts) owns QB = 128/G query positions of one
-// (batch, KV group).  k' tiles of 32 chunks x G heads stream through LDS; each
-// wavefront computes a 32-chunk x 32-query score tile of one head with
-// v_mfma_f32_32x32x16_bf16 (A = k' rows, B = q_hat).  Scores are kept in
+// (batch, KV group).  Each wavefront loads its head's k' tiles of 32 chunks,
+// stored beforehand in MFMA fragment order, straight into registers and
+// computes a 32-chunk x 32-query score tile with v_mfma_f32_32x32x16_bf16
+// (A = k' rows, B = q_hat).  Scores are kept in
 // base-2 units (scaled by log2 e), which preserves their order.
 //   pass 0: per (query, head) online log-sum-exp over C_i (G > 1), and the three
 //           largest scores seen in each of the lane's 16 register slots.  Per
