@@ -642,27 +642,41 @@ k_bwd_rowstat(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   if (e < d) *reinterpret_cast<float2*>(dqo + arow * d + e) = make_float2(tau * q0, tau * q1);
 }
 
+// streaming 16-byte load: the dq partials are read once
+typedef float f4nt_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_f4_nt(const float* p) {
+  const f4nt_t w = __builtin_nontemporal_load(reinterpret_cast<const f4nt_t*>(p));
+  return make_float4(w.x, w.y, w.z, w.w);
+}
+
 // per (query, head): dq = (add ? dq : 0) + the partials of its selected
-// chunks and window chunks; one wavefront per row, lane takes 2 elements
+// chunks and window chunks; one wavefront per row.  A partial row is read as
+// PR = D / 4 pieces of 16 bytes, so one load instruction covers SPI = 64 / PR
+// partial rows: lane (sub, e) = (lane / PR, 4 (lane % PR)) takes every SPI-th
+// slot of the row's slot sequence, eight of them in flight, and the SPI
+// partial sums meet by lane swaps at the end
+template <int D>
 __global__ void __launch_bounds__(256)
 k_bwd_dq_reduce(const float* __restrict__ dqp, const int32_t* __restrict__ sel, float* __restrict__ dq,
-                int Hq, int Hkv, int G, int N, int d, int S, int W, int K, int nC, int nwin,
+                int Hq, int Hkv, int G, int N, int S, int W, int K, int nC, int nwin,
                 int qa, int QN, int QS, long long nrows, int add) {
+  constexpr int PR = D / 4, SPI = 64 / PR;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const long long item = (long long)blockIdx.x * 4 + wv;
   if (item >= nrows) return;
-  const int e = 2 * lane;
-  const bool on = e < d;                             // every lane takes part in the ballots
+  const int sub = lane / PR, e = 4 * (lane % PR);
   const int i = qa + (int)(item % QN);
   const long long bh = item / QN;
   const int h = (int)(bh % Hq);
   const long long b = bh / Hq;
   const long long row = (b * Hkv + h / G) * N + i;
   const long long arow = bh * N + i;
-  const float* pp = dqp + (bh * QS + (i - qa)) * (long long)(K + nwin) * d + e;
-  float2 acc = add && on ? *reinterpret_cast<const float2*>(dq + arow * d + e) : make_float2(0.0f, 0.0f);
+  const float* pp = dqp + (bh * QS + (i - qa)) * (long long)(K + nwin) * D + e;
+  float4 acc = (add && sub == 0) ? *reinterpret_cast<const float4*>(dq + arow * D + e)
+                                 : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   // the selected slots that hold a chunk (one ballot bit per slot, K <= 128),
-  // then the window chunks; eight partial rows in flight, added in slot order
+  // then the window chunks, in this order; the sequence is the same in every
+  // lane (ballots and counters are uniform)
   const int c0 = lane < K ? sel[row * K + lane] : -1;
   const int c1 = lane + 64 < K ? sel[row * K + lane + 64] : -1;
   uint64_t m0 = __ballot(c0 >= 0 && c0 < nC), m1 = __ballot(c1 >= 0 && c1 < nC);
@@ -670,28 +684,42 @@ k_bwd_dq_reduce(const float* __restrict__ dqp, const int32_t* __restrict__ sel, 
   const int nw = i / S - ws / S + 1;
   int wn = 0;
   for (;;) {
-    int sl[8];
+    int sl[8], first = -1;
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      int t = -1;
-      if (m0) { t = __ffsll((unsigned long long)m0) - 1; m0 &= m0 - 1; }
-      else if (m1) { t = 64 + __ffsll((unsigned long long)m1) - 1; m1 &= m1 - 1; }
-      else if (wn < nw) t = K + wn++;
-      sl[x] = t;
+      int mine = -1;
+#pragma unroll
+      for (int y = 0; y < SPI; ++y) {
+        int t = -1;
+        if (m0) { t = __ffsll((unsigned long long)m0) - 1; m0 &= m0 - 1; }
+        else if (m1) { t = 64 + __ffsll((unsigned long long)m1) - 1; m1 &= m1 - 1; }
+        else if (wn < nw) t = K + wn++;
+        if (x == 0 && y == 0) first = t;
+        if (y == sub) mine = t;
+      }
+      sl[x] = mine;
     }
-    if (sl[0] < 0) break;
-    float2 v[8];
+    if (first < 0) break;
+    float4 v[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x)
-      v[x] = sl[x] >= 0 && on ? *reinterpret_cast<const float2*>(pp + (long long)sl[x] * d)
-                              : make_float2(0.0f, 0.0f);
+      v[x] = sl[x] >= 0 ? ld_f4_nt(pp + (long long)sl[x] * D) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       acc.x += v[x].x;
       acc.y += v[x].y;
+      acc.z += v[x].z;
+      acc.w += v[x].w;
     }
   }
-  if (on) *reinterpret_cast<float2*>(dq + arow * d + e) = acc;
+#pragma unroll
+  for (int msk = PR; msk < 64; msk <<= 1) {
+    acc.x += __shfl_xor(acc.x, msk, 64);
+    acc.y += __shfl_xor(acc.y, msk, 64);
+    acc.z += __shfl_xor(acc.z, msk, 64);
+    acc.w += __shfl_xor(acc.w, msk, 64);
+  }
+  if (sub == 0) *reinterpret_cast<float4*>(dq + arow * D + e) = acc;
 }
 
 // per (sequence, KV group, chunk with a summary): the part of the chunk's
@@ -836,8 +864,8 @@ hipError_t launch_mf(const HilsShape& s, const void* q, const void* qr, const vo
                          wb.order, wb.sitems, wb.nsi, s.B * s.Hkv, s.Hq, s.Hkv, s.G, s.N, s.S, s.W,
                          s.K, s.nC, s.nwin, qa, qz, QS, tau); }
     { HilsProfScope ps_("k_bwd_dq", st);
-      hipLaunchKernelGGL(k_bwd_dq_reduce, dim3(rgrid), dim3(256), 0, st, wb.dqp, sel, dq, s.Hq,
-                         s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC, s.nwin, qa, QN, QS, nrows,
+      hipLaunchKernelGGL(k_bwd_dq_reduce<D>, dim3(rgrid), dim3(256), 0, st, wb.dqp, sel, dq, s.Hq,
+                         s.Hkv, s.G, s.N, s.S, s.W, s.K, s.nC, s.nwin, qa, QN, QS, nrows,
                          dqr ? 0 : 1); }
   }
   return hipGetLastError();
