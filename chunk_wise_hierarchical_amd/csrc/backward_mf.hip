@@ -513,8 +513,15 @@ size_t mf_lds() {
 
 // ---------------------------------------------------------------------------
 // per (query, head): window statistics from the partials, routing scores,
-// fusion weights and their gradients; one wavefront per row, K <= 128
-
+// fusion weights and their gradients; one wavefront per row, K <= 128.
+// NI > 0: the k' rows of the selected slots are read once, as PR = D / 8
+// pieces of 16 bytes (lane (rr, pc) = (lane / PR, lane % PR) holds piece pc of
+// the rows of slots RPI x + rr, x < NI, RPI = 64 / PR, all in flight), and
+// serve both the routing scores (piece dot products summed over the PR lanes
+// of a row) and tau sum_t (d s_hat_t) k'_t (summed over x, then over the RPI
+// row groups).  NI = 0: one lane per slot for the scores, the k' rows read
+// again for the routing query's gradient (K > 16 RPI).
+template <int D, int NI>
 __global__ void __launch_bounds__(256)
 k_bwd_rowstat(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
               const float* __restrict__ bsum, const int32_t* __restrict__ sel,
@@ -553,22 +560,65 @@ k_bwd_rowstat(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
       if (c >= 0 && c < nC) {
         cs[m] = c;
         vt[m] = true;
-        const bf16_t* kp = ksum + (bh * nC + c) * (long long)d;
-        float a = 0.0f;
-        for (int e = 0; e < d; e += 8) {
-          const uint4 u = fastp::ld_u4(kp + e);
-          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+        if constexpr (NI == 0) {
+          const bf16_t* kp = ksum + (bh * nC + c) * (long long)d;
+          float a = 0.0f;
+          for (int e = 0; e < d; e += 8) {
+            const uint4 u = fastp::ld_u4(kp + e);
+            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            a = fmaf(qs[e + 2 * x], bf_lo(w4[x]), a);
-            a = fmaf(qs[e + 2 * x + 1], bf_hi(w4[x]), a);
+            for (int x = 0; x < 4; ++x) {
+              a = fmaf(qs[e + 2 * x], bf_lo(w4[x]), a);
+              a = fmaf(qs[e + 2 * x + 1], bf_hi(w4[x]), a);
+            }
           }
+          sh[m] = fmaf(tau, a, bsum[bh * nC + c]);
+        } else {
+          sh[m] = bsum[bh * nC + c];                 // the score is added below
         }
-        sh[m] = fmaf(tau, a, bsum[bh * nC + c]);
         const float* ps = pstat + ((row * K + t) * G + r) * 4;
         lt[m] = ps[1];
         gt[m] = ps[2];
       }
+    }
+  }
+  constexpr int PR = D / 8, RPI = 64 / PR;
+  const int rr = lane / PR, pc = lane % PR;
+  uint4 kr[NI > 0 ? NI : 1];
+  if constexpr (NI > 0) {
+    // slot RPI x + rr of this lane: its chunk from the slot lanes, its k' piece
+    float qv[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) qv[x] = qs[8 * pc + x];
+#pragma unroll
+    for (int x = 0; x < NI; ++x) {
+      const int t = RPI * x + rr;
+      const int ca = __shfl(cs[0], t & 63, 64), cb = __shfl(cs[1], t & 63, 64);
+      const int c = t < 64 ? ca : cb;
+      kr[x] = make_uint4(0u, 0u, 0u, 0u);
+      if (t < K && c >= 0) kr[x] = fastp::ld_u4(ksum + (bh * nC + c) * (long long)D + 8 * pc);
+    }
+    float a[NI];
+#pragma unroll
+    for (int x = 0; x < NI; ++x) {
+      const uint32_t w4[4] = {kr[x].x, kr[x].y, kr[x].z, kr[x].w};
+      float acc = 0.0f;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        acc = fmaf(qv[2 * y], bf_lo(w4[y]), acc);
+        acc = fmaf(qv[2 * y + 1], bf_hi(w4[y]), acc);
+      }
+#pragma unroll
+      for (int msk = 1; msk < PR; msk <<= 1) acc += fastp::xshfl_f(acc, msk);
+      a[x] = acc;
+    }
+    // slot lane + 64 m takes the sum of its row group
+#pragma unroll
+    for (int x = 0; x < NI; ++x) {
+      const float v = __shfl(a[x], PR * (lane % RPI), 64);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        if (vt[m] && (lane + 64 * m) / RPI == x) sh[m] = fmaf(tau, v, sh[m]);
     }
   }
   // the window: partials of its chunks
@@ -616,6 +666,34 @@ k_bwd_rowstat(const bf16_t* __restrict__ qr, const bf16_t* __restrict__ ksum,
   }
   if (lane == 0)
     *reinterpret_cast<float4*>(wstat + arow * 4) = make_float4(aw, lse_w, g_w, aw * (g_w - gbar));
+  if constexpr (NI > 0) {
+    // routing query: tau sum_t (d s_hat_t) k'_t from the k' pieces in registers
+    float qa8[8];
+#pragma unroll
+    for (int y = 0; y < 8; ++y) qa8[y] = 0.0f;
+#pragma unroll
+    for (int x = 0; x < NI; ++x) {
+      const int t = RPI * x + rr;
+      const float da = __shfl(dsh[0], t & 63, 64), db = __shfl(dsh[1], t & 63, 64);
+      const float w = t < K ? (t < 64 ? da : db) : 0.0f;   // empty slots: zero piece
+      const uint32_t w4[4] = {kr[x].x, kr[x].y, kr[x].z, kr[x].w};
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        qa8[2 * y] = fmaf(w, bf_lo(w4[y]), qa8[2 * y]);
+        qa8[2 * y + 1] = fmaf(w, bf_hi(w4[y]), qa8[2 * y + 1]);
+      }
+    }
+#pragma unroll
+    for (int msk = PR; msk < 64; msk <<= 1)
+#pragma unroll
+      for (int y = 0; y < 8; ++y) qa8[y] += fastp::xshfl_f(qa8[y], msk);
+    if (rr == 0) {
+      float* o = dqo + arow * D + 8 * pc;
+      *reinterpret_cast<float4*>(o) = make_float4(tau * qa8[0], tau * qa8[1], tau * qa8[2], tau * qa8[3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(tau * qa8[4], tau * qa8[5], tau * qa8[6], tau * qa8[7]);
+    }
+    return;
+  }
   // routing query: tau sum_t (d s_hat_t) k'_t; lane takes elements 2 lane,
   // 2 lane + 1; slots in order, eight k' rows in flight, the chunk ids and
   // d s_hat from the slot lanes
@@ -824,6 +902,13 @@ hipError_t launch_mf(const HilsShape& s, const void* q, const void* qr, const vo
   const float tau = (float)s.tau;
   const int QS = hils_bwd_mf_slice(s);
   const size_t sh0 = mf_lds<D, 0>(), sh1 = mf_lds<D, 1>();
+  // row pass: the selected slots' k' pieces in registers, NI rows per lane
+  // (a power of two covering K), while NI <= 16
+  constexpr int RPI = 64 / (D / 8);
+  const int need = (s.K + RPI - 1) / RPI;
+  auto rowstat = need <= 1 ? k_bwd_rowstat<D, 1> : need <= 2 ? k_bwd_rowstat<D, 2>
+               : need <= 4 ? k_bwd_rowstat<D, 4> : need <= 8 ? k_bwd_rowstat<D, 8>
+               : need <= 16 ? k_bwd_rowstat<D, 16> : k_bwd_rowstat<D, 0>;
   hils_allow_lds((const void*)k_bwd_mf<D, 0>, sh0);
   hils_allow_lds((const void*)k_bwd_mf<D, 1>, sh1);
   for (int qa = 0; qa < s.N; qa += QS) {
@@ -853,7 +938,7 @@ hipError_t launch_mf(const HilsShape& s, const void* q, const void* qr, const vo
     // the routing query's gradient goes to dq_route, or to dq (then the
     // partials are added to it)
     { HilsProfScope ps_("k_bwd_rowstat", st);
-      hipLaunchKernelGGL(k_bwd_rowstat, dim3(rgrid), dim3(256), sizeof(float) * 4 * s.d, st,
+      hipLaunchKernelGGL(rowstat, dim3(rgrid), dim3(256), sizeof(float) * 4 * s.d, st,
                          (const bf16_t*)qr, (const bf16_t*)ksum, bsum, sel, wb.pstat, wb.wstat,
                          wb.wpart, dqr ? dqr : dq, s.Hq, s.Hkv, s.G, s.N, s.d, s.S, s.W, s.K, s.nC,
                          s.nwin, qa, QN, QS, nrows, tau); }
