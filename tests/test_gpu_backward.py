@@ -192,6 +192,14 @@ def test_backward_more_than_64_slots():
     w = synth.get_workload("prefill_64k", N=1900, Hq=2, Hkv=2, d=64, S=16, W=48, K=100,
                            regime="iid", dtype="f32")
     _case(w, label="K = 100 fp32")
+    # the row pass keeps the slots' k' pieces in registers up to 16 rows per
+    # lane: K = 64 at d = 128 (4 rows per load instruction, the most it
+    # keeps) and K = 100 at d = 64 (8 rows per instruction, slots past 64)
+    w = synth.get_workload("prefill_64k", N=1500, Hq=4, Hkv=2, S=16, W=32, K=64, regime="iid")
+    _case(w, q_route=True, label="K = 64 bf16, row pieces in registers")
+    w = synth.get_workload("prefill_64k", N=2000, Hq=2, Hkv=1, d=64, S=16, W=40, K=100,
+                           regime="half_peaked4")
+    _case(w, label="K = 100 bf16 d = 64, row pieces in registers")
 
 
 def test_backward_deterministic():
