@@ -208,12 +208,13 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
   // contribution), added to by the later ones
   const bool accum = j0 < qa;
 
-  // staging: piece pc = tid + MT m of a tile: query pc % QT, 16-byte part pc / QT
+  // staging: piece pc = tid + MT m of a tile: query pc / (D / 8), 16-byte part
+  // pc % (D / 8), so that a load instruction reads whole rows
   uint4 pq[L::NPC], po[L::NPC];
   auto stage_load = [&](int tl, int nb) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < L::NPC; ++m) {
-      const int pc = tid + MT * m, qq = pc % QT, part = pc / QT;
+      const int pc = tid + MT * m, qq = pc / (D / 8), part = pc % (D / 8);
       const int u = tl * QT + qq;
       pq[m] = make_uint4(0u, 0u, 0u, 0u);
       po[m] = pq[m];
@@ -229,7 +230,7 @@ k_bwd_mf(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     bf16_t* tb = tiles + (size_t)buf * L::TILE;
 #pragma unroll
     for (int m = 0; m < L::NPC; ++m) {
-      const int pc = tid + MT * m, qq = pc % QT, part = pc / QT;
+      const int pc = tid + MT * m, qq = pc / (D / 8), part = pc % (D / 8);
       fastp::st_u4(tb + qq * L::RS + 8 * part, pq[m]);
       fastp::st_u4(tb + (QT + qq) * L::RS + 8 * part, po[m]);
     }
