@@ -98,6 +98,13 @@ struct Lds {
   }
 };
 
+typedef __attribute__((ext_vector_type(4))) short bf16x4_bits;
+// 32x32x8 bf16 MFMA on raw bf16 bits (same output layout as 32x32x16)
+__device__ __forceinline__ f32x16_t mfma32x8(uint2 a, uint2 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(bf16x4_bits, a),
+                                                  __builtin_bit_cast(bf16x4_bits, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a > b ? b : a; }
 
@@ -243,15 +250,20 @@ k_score_fast(const bf16_t* __restrict__ qr, const uint4* __restrict__ frag,
   // this wavefront's k' fragments: coalesced 16-byte loads straight into the
   // MFMA operand registers (no LDS staging, no barrier)
   const uint4* fh = frag + ((hb + hw) * (long long)ntg) * (FRAGS * 64) + lane;
+  // The bias fragment's data are its first 8 bytes in lanes 0-31: only those
+  // are read, and they enter a 32x32x8 MFMA (four k per lane: lanes 0-31 hold
+  // k = 0-3, lanes 32-63 k = 4-7, zero).
   auto load_frag = [&](int t, uint4 (&f)[FRAGS]) {
     const uint4* p = fh + (long long)t * (FRAGS * 64);
 #pragma unroll
-    for (int ks = 0; ks < FRAGS; ++ks) f[ks] = p[ks * 64];
+    for (int ks = 0; ks < FRAGS - 1; ++ks) f[ks] = p[ks * 64];
+    uint2 bb = make_uint2(0u, 0u);
+    if (half == 0) bb = *reinterpret_cast<const uint2*>(p + (FRAGS - 1) * 64);
+    f[FRAGS - 1] = make_uint4(bb.x, bb.y, 0u, 0u);
   };
-  // B operand of the bias fragment: ones at k = 0, 1, 2 (lanes 0-31)
+  // B operand of the bias MFMA: ones at k = 0, 1, 2 (lanes 0-31)
   const uint32_t one2 = 0x3F803F80u;                  // two bf16 1.0
-  const bf16x8_t bones = __builtin_bit_cast(
-      bf16x8_t, half ? make_uint4(0u, 0u, 0u, 0u) : make_uint4(one2, one2 & 0xFFFFu, 0u, 0u));
+  const uint2 bones = half ? make_uint2(0u, 0u) : make_uint2(one2, one2 & 0xFFFFu);
 
   // merge the staged keys of every query of this wavefront into its sorted
   // top-K list: each query in one 8-lane group (QW / 8 rounds), keys of rank
@@ -307,7 +319,7 @@ k_score_fast(const bf16_t* __restrict__ qr, const uint4* __restrict__ frag,
     for (int i = 0; i < 16; ++i) acc[i] = a0;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) acc = mfma32(__builtin_bit_cast(bf16x8_t, f[ks]), bq[ks], acc);
-    acc = mfma32(__builtin_bit_cast(bf16x8_t, f[8]), bones, acc);
+    acc = mfma32x8(make_uint2(f[8].x, f[8].y), bones, acc);
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = acc[i];
     if (CT * t + CT > n_lo) {                        // tile crosses some query's candidate range
@@ -471,13 +483,12 @@ k_score_fast(const bf16_t* __restrict__ qr, const uint4* __restrict__ frag,
         float xa[16], xc[16];
         load_frag(min(t + 1, ntiles - 1), fB);
         tile_scores(fA, t, xa, 0.0f);
-        if (t + 1 < ntiles) {
-          load_frag(min(t + 2, ntiles - 1), fA);
-          tile_scores(fB, t + 1, xc, 0.0f);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) xc[i] = -INFINITY;
-        }
+        load_frag(min(t + 2, ntiles - 1), fA);
+        // with ntiles odd, tile t + 1 = ntiles lies past every query's
+        // candidates and tile_scores masks all its scores to -inf (one extra
+        // MFMA chain per workgroup; a branch around it made the compiler set
+        // sixteen -inf scores on every iteration)
+        tile_scores(fB, t + 1, xc, 0.0f);
         absorb2(xa, xc);
       }
     } else {
