@@ -63,8 +63,10 @@ struct Geo {
   static constexpr int CL = CT / LQ;      // chunks per lane per tile (selection layout)
   // staging slots per query.  One selection step adds at most LQ * CL = 32
   // keys to a query, which merges its staged keys first when they would not
-  // fit; a merge takes at most 64.  G = 2 keeps 56 to fit one CU's LDS.
-  static constexpr int STG = (G == 2) ? 56 : 64;
+  // fit; a merge takes at most 64.  G = 2 keeps 56 to fit one CU's LDS;
+  // G = 1 keeps 56 so that two workgroups share a CU when K <= 16 (the
+  // workgroup's 128 queries hold K list keys and STG staged keys each).
+  static constexpr int STG = (G <= 2) ? 56 : 64;
   static_assert(LQ * CL <= STG && STG <= 64, "staging area");
   static_assert(QW % 8 == 0, "merge rounds take 8 queries");
 };
