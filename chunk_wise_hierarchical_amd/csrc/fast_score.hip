@@ -45,7 +45,8 @@ constexpr int XROW = CT;       // row of the cross-head exchange buffer (floats)
 // 64 lanes x 16 bytes.  Fragment ks < 8 holds the A operand of k-step ks
 // (lane l: chunk 32t + l % 32, elements 16 ks + 8 (l / 32) .. + 7); fragment
 // 8 holds b' / scale split into three bf16 terms (lanes 0-31, elements 0-2),
-// which an MFMA against a constant operand of ones adds exactly.
+// which a 32x32x8 MFMA against a constant operand of ones adds exactly (the
+// scoring kernel reads only those 8 bytes of lanes 0-31).
 constexpr int FRAGS = 9;
 
 // Workgroup geometry.  Every wavefront scores 32 queries of one head; a
@@ -312,8 +313,8 @@ k_score_fast(const bf16_t* __restrict__ qr, const uint4* __restrict__ frag,
   };
 
   // scores of tile t for this lane in accumulator units (score = tau2 * x, base
-  // 2): x[i] <-> chunk 32t + 8(i>>2) + 4*half + (i&3).  The ninth MFMA adds the
-  // bias b' / tau2 of each chunk.
+  // 2): x[i] <-> chunk 32t + 8(i>>2) + 4*half + (i&3).  The last MFMA of the
+  // chain (32x32x8) adds the bias b' / tau2 of each chunk.
   const int n_lo = n_cand(i0, W, S);                 // every query of the block has >= n_lo
   auto tile_scores = [&](const uint4 (&f)[FRAGS], int t, float* x, float a0) {
     f32x16_t acc;
