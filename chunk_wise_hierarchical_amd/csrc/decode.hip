@@ -275,6 +275,7 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
   const int G = GT > 0 ? GT : Gr;
   __shared__ int wsum[SEL_NW];
   __shared__ int sh_digit, sh_need;
+  __shared__ uint32_t sh_tkey;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bgm = blockIdx.x;                 // (sequence, KV group, query)
@@ -383,6 +384,126 @@ k_dec_select(const float* __restrict__ scores, const float* __restrict__ lsep,
     }
   }
   if (tid == 0) sh_need = kl;
+
+  // Bound and short path (partitioned selections: a whole-row selection
+  // measured faster with the radix passes, its bound over few blocks admitting
+  // too many keys).  Each scoring workgroup's partial holds, per head,
+  // the largest score m of its block of SC_CPB chunks (a stored score), so the
+  // chunk attaining it has group score >= m - L_h, by the same fp32
+  // subtraction as the keys.  The blocks are disjoint: when at least kk of
+  // them have a finite bound B_t = max_h (m_h,t - L_h), at least kk distinct
+  // chunks reach the kk-th largest bound T, so every chunk of the row's top kk
+  // (and of any partition's share of it) has a key >= key(T).  When at most
+  // FCAP keys reach the bound they are ranked directly (rank = keys above, or
+  // equal at a lower position), which takes the place of the radix passes and
+  // the compaction.  Merge slots with key 0 are empty.
+  constexpr int FCAP = SEL_NT;
+  float* bnd = reinterpret_cast<float*>(hist);               // [nsb] block bounds
+  uint32_t* fk = hist + SEL_NT;                              // [FCAP] candidate keys
+  int* fp = reinterpret_cast<int*>(hist + SEL_NT + FCAP);    // [FCAP] their positions
+  if (tid == 0) sh_tkey = (PH == SEL_MERGE) ? 1u : 0u;
+  if (PH == SEL_PART && nsb <= SEL_NT) {
+    if (tid < nsb) {
+      float bt = -INFINITY;
+      for (int r = 0; r < G; ++r)
+        bt = fmaxf(bt, lsep[(hrow(r) * nsb + tid) * 2] - ((G == 1) ? 0.0f : Lh[r]));
+      bnd[tid] = bt;
+    }
+    __syncthreads();
+    if (tid < nsb) {
+      const float v = bnd[tid];
+      int rank = 0;
+      for (int u = 0; u < nsb; ++u) {
+        const float x = bnd[u];
+        rank += (x > v || (x == v && u < tid)) ? 1 : 0;
+      }
+      if (v != -INFINITY && rank == kk - 1) sh_tkey = f32_order_key(v);
+    }
+  }
+  __syncthreads();
+  if (PH != SEL_WHOLE) {
+    const uint32_t tkey = sh_tkey;
+    constexpr int CPT = 8;
+    int total = 0;
+    bool fast = true;
+    for (int base = 0; base < cnt; base += CPT * SEL_NT) {
+      const int q0 = base + CPT * tid;
+      uint32_t kv[CPT];
+      int nin = 0;
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        kv[u] = (q0 + u < cnt) ? ky[q0 + u] : 0u;
+        nin += (q0 + u < cnt && kv[u] >= tkey && kv[u] != 0u) ? 1 : 0;
+      }
+      int inc = nin;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += y;
+      }
+      if (lane == 63) wsum[wv] = inc;
+      __syncthreads();
+      int before = inc - nin, rt = 0;
+      for (int u = 0; u < SEL_NW; ++u) {
+        const int t = wsum[u];
+        if (u < wv) before += t;
+        rt += t;
+      }
+      __syncthreads();                     // wsum is rewritten next round
+      if (total + rt > FCAP) { fast = false; break; }   // uniform
+      int pos = total + before;
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        if (q0 + u < cnt && kv[u] >= tkey && kv[u] != 0u) {
+          fk[pos] = kv[u];
+          fp[pos] = q0 + u;
+          ++pos;
+        }
+      }
+      total += rt;
+    }
+    if (fast) {
+      if (tid < 3 && total + tid < FCAP) fk[total + tid] = 0u;   // pad to a multiple of 4
+      __syncthreads();                     // candidates written
+      const int C = total, want = min(kl, C);
+      bool take = false;
+      uint32_t kj = 0u;
+      int pj = 0;
+      if (tid < C) {
+        kj = fk[tid];
+        pj = fp[tid];
+        // candidates are in position order; keys past C read as 0 (below every
+        // candidate), four per LDS read
+        int rank = 0;
+        for (int u = 0; u < C; u += 4) {
+          const uint4 x = *reinterpret_cast<const uint4*>(fk + u);
+          rank += (x.x > kj || (x.x == kj && u < tid)) ? 1 : 0;
+          rank += (x.y > kj || (x.y == kj && u + 1 < tid)) ? 1 : 0;
+          rank += (x.z > kj || (x.z == kj && u + 2 < tid)) ? 1 : 0;
+          rank += (x.w > kj || (x.w == kj && u + 3 < tid)) ? 1 : 0;
+        }
+        take = rank < want;
+      }
+      // output slot: selected candidates before this one, i.e. ascending position
+      const uint64_t bal = __ballot(take);
+      if (lane == 0) wsum[wv] = __popcll(bal);
+      __syncthreads();
+      int pos = __popcll(bal & ((1ull << lane) - 1ull));
+      for (int u = 0; u < wv; ++u) pos += wsum[u];
+      if (take) {
+        if (PH == SEL_PART) {
+          co[pos] = make_uint2(kj, (uint32_t)(c0 + pj));
+        } else {
+          const int c = (PH == SEL_MERGE) ? cid[pj] : pj;
+          so[pos] = c;
+          for (int r = 0; r < G; ++r) slog[hrow(r) * K + pos] = scores[hrow(r) * nmax + c];
+        }
+      }
+      if (PH == SEL_PART)
+        for (int t = want + tid; t < kl; t += SEL_NT) co[t] = make_uint2(0u, 0xffffffffu);
+      return;
+    }
+  }
   __syncthreads();
 
   // MSD radix select of the kl-th largest 32-bit key

@@ -454,6 +454,59 @@ def test_decode_candidates_beyond_lds():
     _decode_case(w, [409600], label="n > 24576")
 
 
+def test_decode_equal_scores_take_lowest_ids():
+    # Partitioned selection (two rows, 8191 candidates: two partitions of 4096,
+    # then a merge).  Sequence 0: every summary row of a head identical and
+    # b' = 0, so all candidates score alike, the bound admits every key of a
+    # partition (more than the 1024 ranked directly) and the radix passes pick
+    # each partition's lowest ids; the merge then ranks its 32 equal keys
+    # directly.  The top-K must be the K lowest chunk ids (section 3 ranking,
+    # ties to the lower id).  Sequence 1 (distinct rows) takes the ranked
+    # short path in both phases.
+    w = synth.get_workload("decode_512k", N=524288, B=2, Hq=4, Hkv=1, K=16, W=512)
+    T = w.N
+    _say(f"[decode] equal scores {w.name} B={w.B} T={T} Hq={w.Hq} Hkv={w.Hkv} K={w.K}")
+    x = synth.make_decode_inputs(w, device="cuda", seqlen=[T, T])
+    ks, bs = hils.summarize(x["k"], x["lm"], w.S)
+    ks[0] = ks[0, :, :1].expand(-1, ks.shape[2], -1).clone()
+    bs[0] = 0.0
+    sel = torch.empty((w.B, w.Hkv, w.K), dtype=torch.int32, device="cuda")
+    out = hils.decode(x["q"], x["k"], x["v"], x["seqlen"], ks, bs, w.S, w.W, w.K, sel=sel)
+    torch.cuda.synchronize()
+    n = O.n_candidates(T - 1, w.W, w.S)
+    assert n > 4096
+    gsel, gout = sel.cpu().numpy(), np32(out)
+    assert (gsel[0] == np.arange(w.K)[None, :]).all(), gsel[0]
+    t = Tally()
+    for b in range(w.B):
+        _say(f"   checking sequence {b}")
+        kb, vb = np32(x["k"][b:b + 1]), np32(x["v"][b:b + 1])
+        lb = np32(x["lm"][b:b + 1, :, :n])
+        summ = (np32(ks[b:b + 1, :, :n]).astype(np.float64), np32(bs[b:b + 1, :, :n]).astype(np.float64))
+        qq = np.broadcast_to(np32(x["q"][b:b + 1]), (1, w.Hq, T, w.d))
+        r = O.ref_prefill_rows(qq, kb, vb, lb, [(0, T - 1)], w.S, w.W, w.K, store=w.dtype,
+                               summaries=summ)[(0, T - 1)]
+        t.rows += 1
+        for g in range(w.Hkv):
+            hs = slice(g * w.G, (g + 1) * w.G)
+            if b == 0:
+                assert list(r["sel"][g]) == list(range(w.K))
+            kind = check_selection(gsel[b, g], dict(sel=r["sel"][g], gap=r["gap"][g],
+                                                    s_hat=r["s_hat"][g]), w.K)
+            rr = r
+            if kind == "exact":
+                t.exact += 1
+            else:
+                t.tie += 1
+                ids = [int(c) for c in gsel[b, g] if c >= 0]
+                rr = O.ref_prefill_rows(qq, kb, vb, lb, [(0, T - 1)], w.S, w.W, w.K, store=w.dtype,
+                                        summaries=summ, forced_sel={(0, g, T - 1): ids})[(0, T - 1)]
+                t.tie_checked += 1
+            t.add((b, g), gout[b, hs, 0], rr["out"][hs], w.dtype, f"equal-score decode b={b} g={g}")
+    _say(f"   {t}")
+    t.check_rel(w.dtype)
+
+
 def test_decode_partitioned_selection():
     # 299999 candidate chunks, K = 128: the selection runs as partitions of
     # 5120 chunks (the 128-key lists of at most 64 partitions fit one merge),
