@@ -64,7 +64,7 @@ struct HilsPairBufs {
   uint16_t* part;                           // [B*Hkv*qs_max*K*G*d] bf16 per-chunk outputs
   int qs_max;
 };
-constexpr int HILS_PAIR_SLICE = 65536;      // queries per slice
+constexpr int HILS_PAIR_SLICE = 131072;     // queries per slice
 constexpr int HILS_PAIR_TPW = 16;           // tiles per attention workgroup
 constexpr int HILS_PAIR_SB = 4096;          // buckets per scan workgroup
 long long hils_pair_tiles_max(const HilsShape& s, int qs);

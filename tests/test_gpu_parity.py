@@ -200,9 +200,9 @@ def test_prefill_fast_without_candidates():
 
 
 def test_prefill_pairs_across_slices():
-    # more queries than one bucket slice (65536), ragged last slice, q_route
-    w = synth.get_workload("prefill_64k", N=70000, Hq=4, Hkv=1, W=1024, K=32)
-    _prefill_case(w, rows=sample_rows(w, 300, include=[65535, 65536, 69999]), q_route=True,
+    # more queries than one bucket slice (131072), ragged last slice, q_route
+    w = synth.get_workload("prefill_64k", N=140000, Hq=4, Hkv=1, W=1024, K=32)
+    _prefill_case(w, rows=sample_rows(w, 300, include=[131071, 131072, 139999]), q_route=True,
                   label="two slices")
 
 
